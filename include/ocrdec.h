@@ -1,0 +1,306 @@
+/*
+ * libocrdec — decode step of an OCR vision-language decoder on AMD Instinct
+ * MI355X (gfx950), as a C ABI.
+ *
+ * The decoder is the one described in "Eseguire Unlimited-OCR su Apple
+ * Silicon con C e Metal" (section "Il decoder e il Mixture of Experts"):
+ * a DeepSeek-V2-style stack, hidden 1280, 10 heads of 128, layer 0 with a
+ * dense SwiGLU MLP and the other layers with a Mixture of Experts (64 routed
+ * experts, top-6, 2 shared experts), activations in fp16, generated tokens
+ * kept in a 128-slot ring cache after a fixed image+prompt prefix, and an
+ * argmax over the language head at the end of every step.  Weights are
+ * block-quantised (same page, section "Quantizzazione: Q8 prima, Q4 dove
+ * conviene": Q8_0, Q4_0; and "Nicolassuez/Falcon-OCR-int8-openvino",
+ * paragraph on NNCF INT8_ASYM: int8 asymmetric) and dequantised inside the
+ * kernels.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless the argument says "host".  The
+ *    caller owns every buffer; the library allocates and frees nothing and
+ *    keeps no device state between calls ("The KV cache is an INPUT, not
+ *    model state", Falcon-OCR card).
+ *  - fp16 is IEEE binary16 passed as uint16_t; fp32 is float.  Matrices are
+ *    row-major.
+ *  - Compute calls are asynchronous on `stream` (a hipStream_t, NULL = the
+ *    null stream).  The returned status covers argument validation, which is
+ *    done on the host before anything is enqueued, and launch errors.  A
+ *    non-OK status leaves all outputs untouched.
+ *  - Errors: a status code, and a per-thread message from ocrdec_last_error()
+ *    naming the bad argument (and, for workspaces, the needed and given bytes;
+ *    Unlimited-OCR page, "Memoria": requests that do not fit are rejected with
+ *    a detailed error).
+ *  - Calls are reentrant.  Concurrent calls need distinct outputs, workspaces
+ *    and caches (one lane per instance, Unlimited-OCR page, "Dall'ABI C
+ *    all'API Python").
+ *  - Rounding: fp16 stores are round-to-nearest-even from fp32; accumulation
+ *    is fp32.
+ */
+#ifndef OCRDEC_H
+#define OCRDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    OCRDEC_OK = 0,
+    OCRDEC_ERR_INVALID_ARG = 1, /* a pointer, size or shape is out of range */
+    OCRDEC_ERR_UNSUPPORTED = 2, /* valid but not implemented (format, shape) */
+    OCRDEC_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+    OCRDEC_ERR_DEVICE = 4       /* a HIP call failed */
+} ocrdec_status;
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* ocrdec_last_error(void);
+
+/* Library version string. */
+const char* ocrdec_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Weight formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Canonical (interchange) layouts, host memory, for W[n][k] (k % 32 == 0 for
+ * block formats).  Blocks run along k within a row; rows follow each other.
+ *   OCRDEC_F16      n*k fp16
+ *   OCRDEC_Q8_0     34-byte blocks: fp16 d, int8 q[32];            w = d*q
+ *   OCRDEC_Q4_0     18-byte blocks: fp16 d, uint8 b[16]; byte j holds element
+ *                   j in its low nibble and element j+16 in its high nibble;
+ *                   w = d*(q-8)
+ *   OCRDEC_U8A_G32  36-byte blocks: fp16 s, fp16 z, uint8 q[32];    w = s*(q-z)
+ * The Unlimited-OCR page names Q8_0/Q4_0 and the Falcon-OCR card INT8_ASYM
+ * with u8 weights; block size 32, the fp16 scale, (q-8)*d and the nibble
+ * order are this library's definition of those formats. */
+typedef enum { OCRDEC_F16 = 0, OCRDEC_Q8_0 = 1, OCRDEC_Q4_0 = 2, OCRDEC_U8A_G32 = 3 } ocrdec_qfmt;
+
+/* A packed weight matrix on the device (see ocrdec_pack). */
+typedef struct {
+    int32_t fmt;       /* ocrdec_qfmt */
+    int32_t n, k;      /* y[n] = sum_k W[n][k] x[k] */
+    const void* data;  /* packed bytes, 256-byte aligned, ocrdec_packed_bytes() long */
+} ocrdec_qmat;
+
+/* Host-only.  Size in bytes of the packed form of W[n][k].
+ * Errors: INVALID_ARG if n <= 0, k <= 0, k % 32 != 0, or bytes is NULL;
+ * UNSUPPORTED for an unknown fmt. */
+ocrdec_status ocrdec_packed_bytes(int32_t fmt, int32_t n, int32_t k, size_t* bytes);
+
+/* Host-only.  Canonical -> packed (both host memory; `packed` must hold
+ * ocrdec_packed_bytes()).  The packed form groups 16 output rows into a tile
+ * and cuts k into chunks (128 weights for Q4_0, 64 for Q8_0 and U8A_G32, 32 for
+ * F16); each (tile, chunk) is 1 KiB of codes laid out so that one 64-lane
+ * wavefront reads it with one 16-byte load per lane, followed by that chunk's
+ * scales.  Rows past n and columns past k are zero-filled.  The layout is an
+ * internal contract between ocrdec_pack and the kernels; only
+ * unpack(pack(w)) == w is promised.  Same errors as ocrdec_packed_bytes, plus
+ * INVALID_ARG for NULL buffers. */
+ocrdec_status ocrdec_pack(int32_t fmt, int32_t n, int32_t k, const void* canonical, void* packed);
+
+/* Host-only.  Packed -> canonical (inverse of ocrdec_pack, bit for bit). */
+ocrdec_status ocrdec_unpack(int32_t fmt, int32_t n, int32_t k, const void* packed, void* canonical);
+
+/* ------------------------------------------------------------------------ */
+/* ocrdec_gemv_q: weight-streaming GEMV / skinny GEMM                         */
+/* ------------------------------------------------------------------------ */
+
+typedef enum { OCRDEC_OUT_F32 = 0, OCRDEC_OUT_F16 = 1 } ocrdec_otype;
+
+/* y[r][j] = sum_k W[j][k] * x[r][k] for r < rows, j < W->n, with W dequantised
+ * in registers (Unlimited-OCR page, "Quantizzazione": dequantisation fused into
+ * the GEMV, no fp16 copy of the weights) and fp32 accumulation.
+ *   W     host pointer to the descriptor; W->data on the device.
+ *   x     fp16 [rows][ldx], ldx >= W->k, 16-byte aligned rows (ldx % 8 == 0).
+ *   y     [rows][ldy] fp32 (y_type OUT_F32) or fp16 (OUT_F16), ldy >= W->n.
+ *   rows  1 .. 4096 (all rows share one read of W).
+ * Errors: INVALID_ARG for NULL pointers, bad sizes or misalignment;
+ * UNSUPPORTED for an unknown format; DEVICE if the launch fails. */
+ocrdec_status ocrdec_gemv_q(const ocrdec_qmat* W, int32_t rows, const uint16_t* x, int64_t ldx,
+                            void* y, int32_t y_type, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* ocrdec_attn_decode: single-query attention over a prefix + ring KV cache  */
+/* ------------------------------------------------------------------------ */
+
+/* One decode step of attention for `rows` independent sequences.
+ *
+ * Inputs are the raw (un-rotated) projections of the new token, fp32
+ * [rows][ld_qkv] with q at column 0, k at n_heads*head_dim, v at
+ * 2*n_heads*head_dim.  The call rotates q and k (RoPE, rotate-half, theta
+ * rope_theta, over the whole head), rounds q, k, v to fp16, writes k and v
+ * into the row's cache slot, and attends:
+ *   o_h = sum_j softmax_j(scale * q_h . k_hj) v_hj   (fp32 softmax)
+ * and stores o as fp16 [rows][ld_out] (head h at column h*head_dim).
+ *
+ * Caches: k_cache, v_cache fp16 [rows][n_heads][cache_cap][head_dim],
+ * caller-owned ("The KV cache is an INPUT", Falcon-OCR card); the call writes
+ * only the new token's slot.
+ *
+ * Ring mode (ring_cap > 0), cache_cap = prefix_cap + ring_cap: row r has a
+ * fixed prefix of prefix_len[r] keys at [0, prefix_len[r]) and generated
+ * tokens in ring slots [prefix_cap, prefix_cap + ring_cap) (Unlimited-OCR
+ * page: a 128-token ring keeps decode memory bounded).  With t = gen_index[r],
+ * the new token goes to slot prefix_cap + t % ring_cap and the attended
+ * window is the prefix plus ring slots [0, min(t+1, ring_cap)) — the ring's
+ * capacity counts the new token.  RoPE position: prefix_len[r] + t.
+ *
+ * Linear mode (ring_cap == 0), cache_cap = prefix_cap: row r holds
+ * prefix_len[r] cached keys; the new token is written at index prefix_len[r]
+ * (< prefix_cap) and keys [0, prefix_len[r]] are attended.  RoPE position:
+ * prefix_len[r] - (sink ? 1 : 0).
+ *
+ * Sink (Falcon-OCR card, attention sink paragraph): if `sink` is non-NULL,
+ * sink[h] is added to the score of cache index 0, where the host has seeded
+ * a zero key and a zero value; this is the page's extra key with logit =
+ * sink and value 0 (its constant-1 query lane folded into a logit).
+ *
+ * gen_index and prefix_len are read, never written.
+ * head_dim: 64 or 128.  rows >= 1.  Workspace: ocrdec_attn_workspace_bytes.
+ * Errors: INVALID_ARG (NULL pointers, head_dim, ld_* too small, caps),
+ * WORKSPACE (too small), DEVICE. */
+typedef struct {
+    int32_t rows, n_heads, head_dim;
+    const float* qkv;          /* [rows][ld_qkv] fp32 */
+    int64_t ld_qkv;
+    uint16_t* k_cache;         /* [rows][n_heads][cache_cap][head_dim] fp16 */
+    uint16_t* v_cache;
+    int32_t prefix_cap, ring_cap;
+    const int32_t* prefix_len; /* [rows] */
+    const int32_t* gen_index;  /* [rows] (ring mode) */
+    const float* sink;         /* [n_heads] or NULL */
+    float rope_theta;
+    float scale;               /* score scale, normally 1/sqrt(head_dim) */
+    uint16_t* out;             /* [rows][ld_out] fp16 */
+    int64_t ld_out;
+} ocrdec_attn_args;
+
+ocrdec_status ocrdec_attn_workspace_bytes(const ocrdec_attn_args* a, size_t* bytes);
+ocrdec_status ocrdec_attn_decode(const ocrdec_attn_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* ocrdec_moe_layer: DeepSeek-V2-style MoE                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Weights of one MoE layer (Unlimited-OCR page, "Il decoder e il Mixture of
+ * Experts": 64 routed experts, top-6, 2 shared experts).  Each expert is a
+ * SwiGLU: a = fp16(silu(G x) * (U x)), y = D a.  The routed experts are stacked:
+ *   gate_up  [n_experts * 2 * d_ff][hidden]: expert e owns rows
+ *            [e*2*d_ff, e*2*d_ff + d_ff) (gate) and the next d_ff rows (up);
+ *   down     [n_experts * hidden][d_ff]: expert e owns rows [e*hidden, (e+1)*hidden);
+ *   sh_gate_up, sh_down: the same for the n_shared shared experts.
+ * hidden and d_ff must be multiples of 16 (a packed tile never straddles two
+ * experts).  router: [n_experts][hidden]; router_bias: fp32 [n_experts] added
+ * to the router logits before the softmax, or NULL. */
+typedef struct {
+    int32_t hidden, n_experts, top_k, n_shared, d_ff;
+    ocrdec_qmat router;
+    const float* router_bias;
+    ocrdec_qmat gate_up, down;
+    ocrdec_qmat sh_gate_up, sh_down;
+} ocrdec_moe_weights;
+
+/* Optional outputs (any pointer may be NULL):
+ *   topk_idx  int32 [rows][top_k]  chosen experts, by probability descending,
+ *                                  ties to the lower index
+ *   topk_w    fp32  [rows][top_k]  renormalised weights
+ *   counts    int32 [n_experts]    tokens per expert
+ *   offsets   int32 [n_experts+1]  exclusive scan of counts
+ *   perm      int32 [rows*top_k]   grouped position -> pair index r*top_k + j,
+ *                                  grouped by expert, then row, then rank */
+typedef struct {
+    int32_t* topk_idx;
+    float* topk_w;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+} ocrdec_moe_capture;
+
+/* out[r] = [h[r] +] sum_s shared_s(x[r]) + sum_j w_rj expert_{idx_rj}(x[r]),
+ * summed in fp32 (shared first, then ranks in order), rounded once to fp16.
+ * Routing: logits = router . x (+ bias); p = softmax(logits); the top_k
+ * experts by p (ties: lower index); w = p / sum of the chosen p.  Tokens are
+ * grouped per expert on the device (counting sort, stable by row then rank)
+ * before the expert projections, and recombined with their weights.
+ *   x            fp16 [rows][hidden] (the MoE input, already normalised)
+ *   h            fp16 [rows][hidden]: if add_residual, h += moe; else h = moe
+ *   forced_topk  int32 [rows][top_k] or NULL: use these experts (a row whose
+ *                first entry is < 0 routes itself); weights still come from
+ *                this call's probabilities
+ *   rows         1 .. 65536
+ * Errors: INVALID_ARG, UNSUPPORTED (top_k > 8, n_experts > 256), WORKSPACE, DEVICE. */
+ocrdec_status ocrdec_moe_workspace_bytes(const ocrdec_moe_weights* w, int32_t rows, size_t* bytes);
+ocrdec_status ocrdec_moe_layer(const ocrdec_moe_weights* w, int32_t rows, const uint16_t* x, uint16_t* h,
+                               int32_t add_residual, const int32_t* forced_topk,
+                               const ocrdec_moe_capture* capture, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* ocrdec_decode_step: one token for every row through the whole decoder     */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const uint16_t* attn_norm;   /* fp16 [hidden] RMSNorm gain before attention */
+    ocrdec_qmat wqkv;            /* [3*n_heads*head_dim][hidden]: q rows, k rows, v rows */
+    ocrdec_qmat wo;              /* [hidden][n_heads*head_dim] */
+    const uint16_t* ffn_norm;    /* fp16 [hidden] RMSNorm gain before the MLP/MoE */
+    int32_t is_moe;
+    int32_t dense_ff;            /* dense layers: SwiGLU width */
+    ocrdec_qmat dense_gate_up;   /* [2*dense_ff][hidden]: gate rows then up rows */
+    ocrdec_qmat dense_down;      /* [hidden][dense_ff] */
+    ocrdec_moe_weights moe;      /* MoE layers */
+    uint16_t* k_cache;           /* fp16 [rows][n_heads][prefix_cap+ring_cap][head_dim] */
+    uint16_t* v_cache;
+} ocrdec_layer;
+
+typedef struct {
+    int32_t n_layers, hidden, n_heads, head_dim, vocab;
+    float rope_theta, norm_eps;
+    const uint16_t* embed;       /* fp16 [vocab][hidden] or NULL (input from `hidden`) */
+    const uint16_t* final_norm;  /* fp16 [hidden] (needed with an LM head) */
+    ocrdec_qmat lm_head;         /* [vocab][hidden]; lm_head.data NULL = no LM head */
+    const ocrdec_layer* layers;  /* HOST array [n_layers] */
+} ocrdec_model;
+
+typedef struct {
+    int32_t rows, prefix_cap, ring_cap;   /* ring_cap > 0 */
+    const int32_t* prefix_len;            /* [rows] */
+    int32_t* gen_index;                   /* [rows]; the step adds 1 to each */
+} ocrdec_state;
+
+/* Optional per-step outputs (any pointer may be NULL):
+ *   topk_idx, topk_w  [n_moe_layers][rows][top_k] routing of every MoE layer
+ *   lm_top2           fp32 [rows][2]: the best and second-best logits */
+typedef struct {
+    int32_t* topk_idx;
+    float* topk_w;
+    float* lm_top2;
+} ocrdec_step_capture;
+
+/* One decode step (Unlimited-OCR page, "Il decoder e il Mixture of Experts"):
+ * h = embed[tok_in] (or `hidden` if tok_in is NULL); for each layer:
+ *   x = fp16(RMSNorm(h) * attn_norm); qkv = Wqkv x; attention as in
+ *   ocrdec_attn_decode (ring mode, scale 1/sqrt(head_dim)); h = fp16(h + Wo o);
+ *   x = fp16(RMSNorm(h) * ffn_norm); h = fp16(h + MLP(x)) with MLP the dense
+ *   SwiGLU or the MoE of ocrdec_moe_layer;
+ * then `hidden` (if non-NULL) receives h, and if the model has an LM head and
+ * tok_out is non-NULL: tok_out[r] = argmax_v (W_lm . fp16(RMSNorm(h) *
+ * final_norm))[v], ties to the lowest v, logits never leave the chip.
+ * Finally gen_index[r] += 1.  tok_out may alias tok_in (the step reads tok_in
+ * before it writes tok_out), so a caller can feed tokens back on the device.
+ *   forced_topk  int32 [n_moe_layers][rows][top_k] or NULL (see ocrdec_moe_layer)
+ *   rows         1 .. 32; prefix_cap + ring_cap <= 65536
+ * Workspace: ocrdec_step_workspace_bytes(m, st) bytes (it depends on rows and
+ * the cache capacity of the state).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE. */
+ocrdec_status ocrdec_step_workspace_bytes(const ocrdec_model* m, const ocrdec_state* st, size_t* bytes);
+ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_state* st, const int32_t* tok_in,
+                                 uint16_t* hidden, int32_t* tok_out, const int32_t* forced_topk,
+                                 const ocrdec_step_capture* capture, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OCRDEC_H */

@@ -1,0 +1,292 @@
+// Single-query decode attention over a fixed prefix plus a ring of generated
+// tokens ("Eseguire Unlimited-OCR su Apple Silicon con C e Metal", section "Il
+// decoder e il Mixture of Experts": a 128-token ring keeps decode memory
+// bounded), with an optional attention sink ("Nicolassuez/Falcon-OCR-int8-
+// openvino": the sink is one more key whose value is zero, seeded at cache
+// index 0).  The cache is caller-owned and only read, except for the new
+// token's slot ("The KV cache is an INPUT").
+//
+// Split-KV: workgroup (split, head, row) scores up to 64 keys of the row's
+// window, keeps them in LDS, and writes an unnormalised partial (max, sum,
+// sum of p*v); a combine kernel merges the splits with the usual
+// log-sum-exp rescaling.  Keys are streamed with one 16-byte load per lane:
+// for head_dim 128 a wavefront load covers 4 keys (16 lanes per key), for 64
+// it covers 8 keys.
+#include "attn.hpp"
+
+namespace ocrdec {
+
+namespace {
+
+constexpr int KPS = 64;  // keys per split
+
+struct Window {
+    int nkeys;     // keys attended
+    int new_ord;   // ordinal of the new token in the window
+    int new_idx;   // its cache index
+    int pos;       // its RoPE position
+    int P;         // prefix length
+};
+
+OCR_DEV Window row_window(const AttnParams& p, int r) {
+    Window w;
+    // Lengths are device data: clamp them so that no value can address memory
+    // outside the row's cache (prefix <= prefix_cap in ring mode; room for the
+    // new token in linear mode; t >= 0).
+    const int pmax = p.ring_cap > 0 ? p.prefix_cap : p.prefix_cap - 1;
+    w.P = min(max(p.prefix_len[r], 0), pmax);
+    if (p.ring_cap > 0) {
+        const int t = max(p.gen_index[r], 0);
+        const int n_ring = min(t + 1, p.ring_cap);
+        w.nkeys = w.P + n_ring;
+        w.new_ord = w.P + t % p.ring_cap;
+        w.new_idx = p.prefix_cap + t % p.ring_cap;
+        w.pos = w.P + t;
+    } else {
+        w.nkeys = w.P + 1;
+        w.new_ord = w.P;
+        w.new_idx = w.P;
+        w.pos = w.P - (p.sink ? 1 : 0);
+    }
+    return w;
+}
+
+OCR_DEV int ord_to_idx(const AttnParams& p, const Window& w, int o) {
+    if (p.ring_cap > 0 && o >= w.P) return p.prefix_cap + (o - w.P);
+    return o;
+}
+
+// RoPE (rotate-half) of lane pair (i, i + D/2) at position pos; the angle is
+// formed in double so large positions keep full precision.
+OCR_DEV void rope_pair(float x1, float x2, int i, int D, int pos, float theta, float& y1, float& y2) {
+    const double f = exp2(-(2.0 * i / D) * log2((double)theta));
+    const double a = (double)pos * f;
+    double s, c;
+    sincos(a, &s, &c);
+    const float cf = (float)c, sf = (float)s;
+    y1 = x1 * cf - x2 * sf;
+    y2 = x2 * cf + x1 * sf;
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
+    constexpr int LPK = D / 8;        // lanes per key
+    constexpr int KPL = 64 / LPK;     // keys per wavefront load
+    __shared__ float q_s[D];
+    __shared__ __align__(16) uint16_t knew_s[D];
+    __shared__ __align__(16) uint16_t vnew_s[D];
+    __shared__ float sc_s[KPS];
+    __shared__ float o_s[4][D];
+    __shared__ float red_s[8];
+
+    const int s = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Window w = row_window(p, r);
+    const int o0 = s * KPS, o1 = min(o0 + KPS, w.nkeys);
+    float* part = p.part + (((int64_t)r * p.n_heads + h) * p.n_split + s) * (D + 2);
+    if (o0 >= o1) {
+        if (tid < D) part[tid] = 0.f;
+        if (tid == 0) {
+            part[D] = -INFINITY;
+            part[D + 1] = 0.f;
+        }
+        return;
+    }
+    const bool has_new = (w.new_ord >= o0 && w.new_ord < o1);
+    const float* qkv = p.qkv + (int64_t)r * p.ld_qkv;
+    const int HD = p.n_heads * D;
+    if (tid < D / 2) {
+        const int i = tid;
+        float y1, y2;
+        rope_pair(qkv[h * D + i], qkv[h * D + i + D / 2], i, D, w.pos, p.theta, y1, y2);
+        q_s[i] = h2f(f2h(y1));
+        q_s[i + D / 2] = h2f(f2h(y2));
+        if (has_new) {
+            float k1, k2;
+            rope_pair(qkv[HD + h * D + i], qkv[HD + h * D + i + D / 2], i, D, w.pos, p.theta, k1, k2);
+            knew_s[i] = f2h(k1);
+            knew_s[i + D / 2] = f2h(k2);
+        }
+    } else if (has_new && tid >= 64 && tid < 64 + D) {
+        const int i = tid - 64;
+        vnew_s[i] = f2h(qkv[2 * HD + h * D + i]);
+    }
+    __syncthreads();
+    const int64_t head_off = ((int64_t)r * p.n_heads + h) * p.cache_cap;
+    if (has_new && tid < D) {
+        p.k_cache[(head_off + w.new_idx) * D + tid] = knew_s[tid];
+        p.v_cache[(head_off + w.new_idx) * D + tid] = vnew_s[tid];
+    }
+
+    // ---- scores: wave w takes keys o0 + w*KPL + j*4*KPL, lane group -> one key
+    const int dsub = (lane % LPK) * 8;
+    float qf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qf[i] = q_s[dsub + i];
+    for (int base = o0 + wave * KPL; base < o1; base += 4 * KPL) {
+        const int o = base + lane / LPK;
+        float dot = 0.f;
+        if (o < o1) {
+            const int ci = ord_to_idx(p, w, o);
+            uint4 kv;
+            if (ci == w.new_idx) kv = *(const uint4*)(knew_s + dsub);
+            else kv = *(const uint4*)(p.k_cache + (head_off + ci) * D + dsub);
+            half8v kh = bits_to_half8(kv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dot = fmaf(qf[i], (float)kh[i], dot);
+        }
+#pragma unroll
+        for (int off = LPK / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+        if (o < o1 && (lane % LPK) == 0) {
+            float sc = dot * p.scale;
+            if (p.sink && ord_to_idx(p, w, o) == 0) sc += p.sink[h];
+            sc_s[o - o0] = sc;
+        }
+    }
+    __syncthreads();
+    const int nk = o1 - o0;
+    // ---- max and sum over the split's scores (wave 0)
+    if (wave == 0) {
+        float m = lane < nk ? sc_s[lane] : -INFINITY;
+        m = wave_max(m);
+        float e = lane < nk ? __expf(sc_s[lane] - m) : 0.f;
+        if (lane < nk) sc_s[lane] = e;
+        float l = wave_sum(e);
+        if (lane == 0) {
+            red_s[0] = m;
+            red_s[1] = l;
+        }
+    }
+    __syncthreads();
+    // ---- p . V over the same key assignment
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int base = o0 + wave * KPL; base < o1; base += 4 * KPL) {
+        const int o = base + lane / LPK;
+        if (o < o1) {
+            const int ci = ord_to_idx(p, w, o);
+            uint4 vv;
+            if (ci == w.new_idx) vv = *(const uint4*)(vnew_s + dsub);
+            else vv = *(const uint4*)(p.v_cache + (head_off + ci) * D + dsub);
+            half8v vh = bits_to_half8(vv);
+            const float pj = sc_s[o - o0];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(pj, (float)vh[i], acc[i]);
+        }
+    }
+    // reduce over the key groups of the wavefront (lanes sharing dsub)
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], off, 64);
+    if (lane < LPK) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o_s[wave][dsub + i] = acc[i];
+    }
+    __syncthreads();
+    if (tid < D) part[tid] = o_s[0][tid] + o_s[1][tid] + o_s[2][tid] + o_s[3][tid];
+    if (tid == 0) {
+        part[D] = red_s[0];
+        part[D + 1] = red_s[1];
+    }
+}
+
+template <int D>
+__global__ void attn_combine_kernel(AttnParams p) {
+    const int h = blockIdx.x, r = blockIdx.y, d = threadIdx.x;
+    const float* part = p.part + ((int64_t)r * p.n_heads + h) * p.n_split * (D + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
+    float L = 0.f, o = 0.f;
+    for (int s = 0; s < p.n_split; ++s) {
+        const float m = part[s * (D + 2) + D];
+        if (m == -INFINITY) continue;
+        const float f = __expf(m - M);
+        L = fmaf(part[s * (D + 2) + D + 1], f, L);
+        o = fmaf(part[s * (D + 2) + d], f, o);
+    }
+    p.out[(int64_t)r * p.ld_out + h * D + d] = f2h(o / L);
+}
+
+int attn_n_split(int cache_cap) { return (cache_cap + 1 + KPS - 1) / KPS; }
+
+size_t attn_ws_bytes(int rows, int n_heads, int head_dim, int cache_cap) {
+    return align256((size_t)rows * n_heads * attn_n_split(cache_cap) * (head_dim + 2) * sizeof(float));
+}
+
+void launch_attn(const AttnParams& p, hipStream_t s) {
+    dim3 g1(p.n_split, p.n_heads, p.rows);
+    dim3 g2(p.n_heads, p.rows);
+    if (p.head_dim == 128) {
+        hipLaunchKernelGGL(attn_partial_kernel<128>, g1, dim3(256), 0, s, p);
+        hipLaunchKernelGGL(attn_combine_kernel<128>, g2, dim3(128), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(attn_partial_kernel<64>, g1, dim3(256), 0, s, p);
+        hipLaunchKernelGGL(attn_combine_kernel<64>, g2, dim3(64), 0, s, p);
+    }
+}
+
+ocrdec_status check_attn(const ocrdec_attn_args* a) {
+    OCR_CHECK_ARG(a, "args is NULL");
+    OCR_CHECK_ARG(a->rows >= 1, "rows must be >= 1");
+    OCR_CHECK_ARG(a->n_heads >= 1 && a->n_heads <= 64, "n_heads must be in [1, 64]");
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(OCRDEC_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    OCR_CHECK_ARG(a->qkv && a->k_cache && a->v_cache && a->prefix_len && a->out, "NULL pointer in args");
+    OCR_CHECK_ARG(a->ring_cap == 0 || a->gen_index, "gen_index is NULL in ring mode");
+    OCR_CHECK_ARG(a->ld_qkv >= 3LL * a->n_heads * a->head_dim, "ld_qkv too small");
+    OCR_CHECK_ARG(a->ld_out >= (int64_t)a->n_heads * a->head_dim, "ld_out too small");
+    OCR_CHECK_ARG(a->prefix_cap >= 0 && a->ring_cap >= 0 && a->prefix_cap + a->ring_cap >= 1,
+                  "prefix_cap and ring_cap must be >= 0 with a non-empty cache");
+    OCR_CHECK_ARG(((uintptr_t)a->k_cache & 15) == 0 && ((uintptr_t)a->v_cache & 15) == 0,
+                  "caches must be 16-byte aligned");
+    OCR_CHECK_ARG(a->rope_theta > 0.f, "rope_theta must be positive");
+    return OCRDEC_OK;
+}
+
+}  // namespace ocrdec
+
+using namespace ocrdec;
+
+extern "C" ocrdec_status ocrdec_attn_workspace_bytes(const ocrdec_attn_args* a, size_t* bytes) {
+    ocrdec_status st = check_attn(a);
+    if (st != OCRDEC_OK) return st;
+    OCR_CHECK_ARG(bytes, "bytes is NULL");
+    *bytes = attn_ws_bytes(a->rows, a->n_heads, a->head_dim, a->prefix_cap + a->ring_cap);
+    return OCRDEC_OK;
+}
+
+extern "C" ocrdec_status ocrdec_attn_decode(const ocrdec_attn_args* a, void* ws, size_t ws_bytes, void* stream) {
+    ocrdec_status st = check_attn(a);
+    if (st != OCRDEC_OK) return st;
+    const int cap = a->prefix_cap + a->ring_cap;
+    const size_t need = attn_ws_bytes(a->rows, a->n_heads, a->head_dim, cap);
+    if (!ws || ws_bytes < need)
+        return fail(OCRDEC_ERR_WORKSPACE, "attention workspace: need " + std::to_string(need) + " bytes, got " +
+                                              std::to_string(ws ? ws_bytes : 0));
+    AttnParams p{};
+    p.rows = a->rows;
+    p.n_heads = a->n_heads;
+    p.head_dim = a->head_dim;
+    p.qkv = a->qkv;
+    p.ld_qkv = a->ld_qkv;
+    p.k_cache = a->k_cache;
+    p.v_cache = a->v_cache;
+    p.prefix_cap = a->prefix_cap;
+    p.ring_cap = a->ring_cap;
+    p.cache_cap = cap;
+    p.prefix_len = a->prefix_len;
+    p.gen_index = a->gen_index;
+    p.sink = a->sink;
+    p.theta = a->rope_theta;
+    p.scale = a->scale;
+    p.out = a->out;
+    p.ld_out = a->ld_out;
+    p.n_split = attn_n_split(cap);
+    p.part = (float*)ws;
+    launch_attn(p, (hipStream_t)stream);
+    return launch_status("ocrdec_attn_decode");
+}

@@ -1,0 +1,30 @@
+// Host-side interface of the decode-attention kernels.
+#pragma once
+
+#include "common.hpp"
+
+namespace ocrdec {
+
+struct AttnParams {
+    int rows, n_heads, head_dim;
+    const float* qkv;
+    int64_t ld_qkv;
+    uint16_t* k_cache;
+    uint16_t* v_cache;
+    int prefix_cap, ring_cap, cache_cap;
+    const int32_t* prefix_len;
+    const int32_t* gen_index;
+    const float* sink;
+    float theta, scale;
+    uint16_t* out;
+    int64_t ld_out;
+    int n_split;
+    float* part;  // [rows][n_heads][n_split][head_dim + 2]
+};
+
+int attn_n_split(int cache_cap);
+size_t attn_ws_bytes(int rows, int n_heads, int head_dim, int cache_cap);
+void launch_attn(const AttnParams& p, hipStream_t s);
+ocrdec_status check_attn(const ocrdec_attn_args* a);
+
+}  // namespace ocrdec

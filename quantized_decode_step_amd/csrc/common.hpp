@@ -1,0 +1,181 @@
+// Shared definitions of libocrdec: status plumbing, the packed weight layout,
+// and device helpers for gfx950 (64-lane wavefronts, MFMA 16x16x32 f16).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include <string>
+
+#include "../../include/ocrdec.h"
+
+namespace ocrdec {
+
+// ---------------------------------------------------------------------------
+// Status and messages (host)
+// ---------------------------------------------------------------------------
+
+ocrdec_status fail(ocrdec_status s, const std::string& msg);
+ocrdec_status ok();
+
+#define OCR_CHECK_ARG(cond, ...)                                                   \
+    do {                                                                           \
+        if (!(cond)) return ::ocrdec::fail(OCRDEC_ERR_INVALID_ARG, __VA_ARGS__);   \
+    } while (0)
+
+#define OCR_HIP(call)                                                              \
+    do {                                                                           \
+        hipError_t e_ = (call);                                                    \
+        if (e_ != hipSuccess)                                                      \
+            return ::ocrdec::fail(OCRDEC_ERR_DEVICE,                               \
+                                  std::string(#call) + ": " + hipGetErrorString(e_)); \
+    } while (0)
+
+// Checks the launch that was just enqueued.
+ocrdec_status launch_status(const char* what);
+
+// ---------------------------------------------------------------------------
+// Packed weight layout
+//
+// W[n][k] is cut into tiles of 16 output rows and chunks of KC input columns.
+// Chunk (t, c) occupies CB bytes at offset (t * n_chunks + c) * CB:
+//   bytes [0, 1024): the codes, 16 bytes per lane of a 64-lane wavefront.
+//     Lane l serves row 16t + (l & 15) and the 8 consecutive columns
+//     8*(l >> 4) .. +7 of every 32-column block of the chunk, which is the
+//     B-operand layout of v_mfma_f32_16x16x32_f16 (column j = l & 15,
+//     k = 8*(l >> 4) + i).  Block j of the chunk sits in
+//       F16   the whole 16 bytes (8 halves), one block per chunk;
+//       Q8_0  bytes 8j..8j+7 (int8), two blocks per chunk;
+//       U8A   bytes 8j..8j+7 (uint8), two blocks per chunk;
+//       Q4_0  dword j, four blocks per chunk; element 2p at bits 4p..4p+3 and
+//             element 2p+1 at bits 16+4p..19+4p, so (dword >> 4p) & 0x000F000F
+//             is a pair of codes in the two halves of a 32-bit register.
+//   bytes [1024, CB): the scales of the 16 rows, row-major:
+//       Q8_0  row r: fp16 d[block 0], d[block 1]              (4 bytes)
+//       Q4_0  row r: fp16 d[block 0..3]                       (8 bytes)
+//       U8A   row r: fp16 s0, z0, s1, z1                      (8 bytes)
+// Rows >= n and blocks >= k/32 are zero.
+// ---------------------------------------------------------------------------
+
+struct PackGeom {
+    int sb;     // 32-column blocks per chunk
+    int kc;     // columns per chunk
+    int cb;     // bytes per chunk
+    int scb;    // scale bytes per row per chunk
+};
+
+inline bool pack_geom(int fmt, PackGeom* g) {
+    switch (fmt) {
+    case OCRDEC_F16: *g = {1, 32, 1024, 0}; return true;
+    case OCRDEC_Q8_0: *g = {2, 64, 1088, 4}; return true;
+    case OCRDEC_Q4_0: *g = {4, 128, 1152, 8}; return true;
+    case OCRDEC_U8A_G32: *g = {2, 64, 1152, 8}; return true;
+    default: return false;
+    }
+}
+
+inline int64_t n_tiles(int n) { return (n + 15) / 16; }
+inline int64_t n_chunks(int fmt, int k) {
+    PackGeom g;
+    pack_geom(fmt, &g);
+    return (k + g.kc - 1) / g.kc;
+}
+inline size_t packed_size(int fmt, int n, int k) {
+    PackGeom g;
+    pack_geom(fmt, &g);
+    size_t b = (size_t)n_tiles(n) * (size_t)n_chunks(fmt, k) * (size_t)g.cb;
+    return (b + 255) & ~(size_t)255;
+}
+
+// Validates a device matrix descriptor.
+ocrdec_status check_qmat(const ocrdec_qmat* w, const char* name);
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Bump allocator over a caller workspace.
+struct Carve {
+    char* base;
+    size_t off = 0;
+    explicit Carve(void* p) : base((char*)p) {}
+    template <class T>
+    T* take(size_t count) {
+        T* p = (T*)(base ? base + off : nullptr);
+        off += align256(count * sizeof(T));
+        return p;
+    }
+};
+
+}  // namespace ocrdec
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+typedef _Float16 f16_t;
+typedef f16_t half2v __attribute__((ext_vector_type(2)));
+typedef f16_t half8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+#define OCR_DEV __device__ __forceinline__
+
+OCR_DEV float h2f(uint16_t h) { return (float)__builtin_bit_cast(f16_t, h); }
+OCR_DEV uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (f16_t)f); }
+
+OCR_DEV float4v mfma16(half8v a, half8v b, float4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Sum over all 64 lanes (result in every lane).
+OCR_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+OCR_DEV float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+OCR_DEV half8v bits_to_half8(uint4 q) { return __builtin_bit_cast(half8v, q); }
+
+OCR_DEV half2v u32_to_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
+OCR_DEV uint32_t h2_to_u32(half2v h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Eight Q4_0 codes (one packed dword) -> the eight fp16 values q - 8 (exact).
+OCR_DEV half8v deq_q4(uint32_t dw) {
+    const half2v off = {(f16_t)1032.0f, (f16_t)1032.0f};
+    half2v p0 = u32_to_h2((dw & 0x000F000Fu) | 0x64006400u) - off;
+    half2v p1 = u32_to_h2(((dw >> 4) & 0x000F000Fu) | 0x64006400u) - off;
+    half2v p2 = u32_to_h2(((dw >> 8) & 0x000F000Fu) | 0x64006400u) - off;
+    half2v p3 = u32_to_h2(((dw >> 12) & 0x000F000Fu) | 0x64006400u) - off;
+    uint4 r = {h2_to_u32(p0), h2_to_u32(p1), h2_to_u32(p2), h2_to_u32(p3)};
+    return bits_to_half8(r);
+}
+
+// Eight int8 codes (two dwords, k order) -> fp16 q (exact).  1024 + (q ^ 0x80)
+// is built with a byte permute against 0x64 and 1152 is subtracted.
+OCR_DEV half8v deq_q8(uint32_t lo, uint32_t hi) {
+    const half2v off = {(f16_t)1152.0f, (f16_t)1152.0f};
+    uint32_t a = lo ^ 0x80808080u, b = hi ^ 0x80808080u;
+    half2v p0 = u32_to_h2(__builtin_amdgcn_perm(0x64646464u, a, 0x04010400u)) - off;
+    half2v p1 = u32_to_h2(__builtin_amdgcn_perm(0x64646464u, a, 0x04030402u)) - off;
+    half2v p2 = u32_to_h2(__builtin_amdgcn_perm(0x64646464u, b, 0x04010400u)) - off;
+    half2v p3 = u32_to_h2(__builtin_amdgcn_perm(0x64646464u, b, 0x04030402u)) - off;
+    uint4 r = {h2_to_u32(p0), h2_to_u32(p1), h2_to_u32(p2), h2_to_u32(p3)};
+    return bits_to_half8(r);
+}
+
+// Eight uint8 codes -> fp16 q (exact).
+OCR_DEV half8v deq_u8(uint32_t lo, uint32_t hi) {
+    const half2v off = {(f16_t)1024.0f, (f16_t)1024.0f};
+    half2v p0 = u32_to_h2(__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u)) - off;
+    half2v p1 = u32_to_h2(__builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u)) - off;
+    half2v p2 = u32_to_h2(__builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u)) - off;
+    half2v p3 = u32_to_h2(__builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)) - off;
+    uint4 r = {h2_to_u32(p0), h2_to_u32(p1), h2_to_u32(p2), h2_to_u32(p3)};
+    return bits_to_half8(r);
+}
+
+OCR_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }

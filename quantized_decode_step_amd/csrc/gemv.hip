@@ -1,0 +1,273 @@
+// Dense GEMV / skinny-GEMM kernels over packed weights, with the epilogues the
+// decode step needs: fp32 or fp16 store, residual add, SwiGLU pairing, and a
+// fused argmax over the output rows (language head).
+#include "gemv.hpp"
+
+namespace ocrdec {
+
+template <int FMT, int NT, int XT, int KS, int EPI>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
+    constexpr int CB = Geom<FMT>::CB;
+    __shared__ float4v red[(KS > 1) ? 4 * NT * XT * 64 : 1];
+    __shared__ float amx[(EPI == EPI_ARGMAX) ? 4 * 32 * 3 : 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = blockIdx.x * (4 / KS) + wave / KS;
+    const int ks = wave % KS;
+    const bool valid = g < p.n_groups;
+    const int ntiles = (p.n + 15) / 16;
+
+    int tidx[NT];
+    const uint8_t* tile[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        int t = (EPI == EPI_GLU) ? (i == 0 ? g : g + p.half_tiles) : g * NT + i;
+        tidx[i] = t;
+        if (!valid || t >= ntiles) t = 0;
+        tile[i] = p.w + (int64_t)t * p.nchunks * CB;
+    }
+    const int cper = (int)((p.nchunks + KS - 1) / KS);
+    const int c0 = ks * cper;
+    const int c1 = valid ? (int)min((int64_t)(c0 + cper), p.nchunks) : c0;
+    const int nblk = p.k / 32;
+
+    for (int tok0 = 0; tok0 < p.xs.rows; tok0 += 16 * XT) {
+        float4v acc[NT][XT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int xt = 0; xt < XT; ++xt) acc[i][xt] = float4v{0.f, 0.f, 0.f, 0.f};
+        kloop<FMT, NT, XT>(tile, c0, c1, p.xs, tok0, nblk, lane, acc);
+        ksplit_reduce<NT, XT, KS>(acc, red, wave, lane);
+
+        const bool owner = (ks == 0) && valid;
+        if constexpr (EPI == EPI_ARGMAX) {
+            // per token: best value, its row (lowest on ties), second-best value
+            float best[XT][4], second[XT][4];
+            int bidx[XT][4];
+#pragma unroll
+            for (int xt = 0; xt < XT; ++xt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    best[xt][v] = -INFINITY;
+                    second[xt][v] = -INFINITY;
+                    bidx[xt][v] = 0x7fffffff;
+                }
+            if (owner) {
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    const int row = tidx[i] * 16 + (lane & 15);
+                    if (row < p.n) {
+#pragma unroll
+                        for (int xt = 0; xt < XT; ++xt)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                float val = acc[i][xt][v];
+                                if (val > best[xt][v]) {
+                                    second[xt][v] = best[xt][v];
+                                    best[xt][v] = val;
+                                    bidx[xt][v] = row;
+                                } else if (val > second[xt][v]) {
+                                    second[xt][v] = val;
+                                }
+                            }
+                    }
+                }
+            }
+            // merge across the 16 lanes that share a token
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+#pragma unroll
+                for (int xt = 0; xt < XT; ++xt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float ob = __shfl_xor(best[xt][v], o, 64);
+                        float os = __shfl_xor(second[xt][v], o, 64);
+                        int oi = __shfl_xor(bidx[xt][v], o, 64);
+                        argmax_merge(best[xt][v], bidx[xt][v], second[xt][v], ob, oi, os);
+                    }
+            }
+            if ((lane & 15) == 0) {
+#pragma unroll
+                for (int xt = 0; xt < XT; ++xt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int tok = 16 * xt + 4 * (lane >> 4) + v;
+                        float* e = amx + (wave * 32 + tok) * 3;
+                        e[0] = best[xt][v];
+                        e[1] = __int_as_float(bidx[xt][v]);
+                        e[2] = second[xt][v];
+                    }
+            }
+            __syncthreads();
+            if (threadIdx.x < 16 * XT) {
+                const int tok = threadIdx.x;
+                float b = -INFINITY, s = -INFINITY;
+                int bi = 0x7fffffff;
+                for (int w = 0; w < 4; ++w) {
+                    const float* e = amx + (w * 32 + tok) * 3;
+                    argmax_merge(b, bi, s, e[0], __float_as_int(e[1]), e[2]);
+                }
+                if (tok0 + tok < p.xs.rows) {
+                    float* out = p.part + ((int64_t)blockIdx.x * p.xs.rows + tok0 + tok) * 3;
+                    out[0] = b;
+                    out[1] = __int_as_float(bi);
+                    out[2] = s;
+                }
+            }
+        } else if (owner) {
+#pragma unroll
+            for (int xt = 0; xt < XT; ++xt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int tok = tok0 + 16 * xt + 4 * (lane >> 4) + v;
+                    if (tok >= p.xs.rows) continue;
+                    if constexpr (EPI == EPI_GLU) {
+                        const int col = tidx[0] * 16 + (lane & 15);
+                        if (col < p.half_tiles * 16) {
+                            const float gv = acc[0][xt][v], uv = acc[1][xt][v];
+                            ((uint16_t*)p.y)[(int64_t)tok * p.ldy + col] = f2h(silu(gv) * uv);
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < NT; ++i) {
+                            const int row = tidx[i] * 16 + (lane & 15);
+                            if (row >= p.n) continue;
+                            const int64_t o = (int64_t)tok * p.ldy + row;
+                            if constexpr (EPI == EPI_F32) {
+                                ((float*)p.y)[o] = acc[i][xt][v];
+                            } else if constexpr (EPI == EPI_F16) {
+                                ((uint16_t*)p.y)[o] = f2h(acc[i][xt][v]);
+                            } else if constexpr (EPI == EPI_RESID) {
+                                uint16_t* h = (uint16_t*)p.y;
+                                h[o] = f2h(h2f(h[o]) + acc[i][xt][v]);
+                            }
+                        }
+                    }
+                }
+        }
+        __syncthreads();
+    }
+}
+
+namespace {
+
+template <int FMT, int NT, int XT, int KS, int EPI>
+void launch_t(const GemvParams& p, hipStream_t s) {
+    const int groups_per_wg = 4 / KS;
+    const int grid = (p.n_groups + groups_per_wg - 1) / groups_per_wg;
+    hipLaunchKernelGGL((gemv_kernel<FMT, NT, XT, KS, EPI>), dim3(grid), dim3(256), 0, s, p);
+}
+
+template <int FMT, int EPI>
+void launch_fmt(const GemvParams& p, int nt, int ks, int xt, hipStream_t s) {
+#define OCR_L(NT_, KS_, XT_)                                  \
+    if (nt == NT_ && ks == KS_ && xt == XT_) {                \
+        launch_t<FMT, NT_, XT_, KS_, EPI>(p, s);              \
+        return;                                               \
+    }
+    if constexpr (EPI == EPI_GLU) {
+        OCR_L(2, 1, 1) OCR_L(2, 1, 2) OCR_L(2, 4, 1) OCR_L(2, 4, 2)
+    } else {
+        OCR_L(1, 4, 1) OCR_L(1, 4, 2) OCR_L(4, 1, 1) OCR_L(4, 1, 2)
+    }
+#undef OCR_L
+}
+
+}  // namespace
+
+GemvPlan plan_gemv(int fmt, int n, int k, int rows, int epi) {
+    GemvPlan pl;
+    const int64_t tiles = (n + 15) / 16;
+    pl.xt = rows <= 16 ? 1 : 2;
+    if (epi == EPI_GLU) {
+        pl.nt = 2;
+        pl.groups = (int)(tiles / 2);
+        pl.ks = pl.groups >= 512 ? 1 : 4;
+    } else if (tiles >= 1024) {
+        pl.nt = 4;
+        pl.ks = 1;
+        pl.groups = (int)((tiles + 3) / 4);
+    } else {
+        pl.nt = 1;
+        pl.ks = 4;
+        pl.groups = (int)tiles;
+    }
+    pl.grid = (pl.groups + (4 / pl.ks) - 1) / (4 / pl.ks);
+    (void)fmt;
+    (void)k;
+    return pl;
+}
+
+void launch_gemv(int fmt, int epi, const GemvPlan& pl, GemvParams p, hipStream_t s) {
+    p.n_groups = pl.groups;
+#define OCR_E(E_)                                                                          \
+    case E_:                                                                               \
+        switch (fmt) {                                                                     \
+        case OCRDEC_F16: launch_fmt<OCRDEC_F16, E_>(p, pl.nt, pl.ks, pl.xt, s); break;     \
+        case OCRDEC_Q8_0: launch_fmt<OCRDEC_Q8_0, E_>(p, pl.nt, pl.ks, pl.xt, s); break;   \
+        case OCRDEC_Q4_0: launch_fmt<OCRDEC_Q4_0, E_>(p, pl.nt, pl.ks, pl.xt, s); break;   \
+        case OCRDEC_U8A_G32: launch_fmt<OCRDEC_U8A_G32, E_>(p, pl.nt, pl.ks, pl.xt, s); break; \
+        }                                                                                  \
+        break;
+    switch (epi) {
+        OCR_E(EPI_F32)
+        OCR_E(EPI_F16)
+        OCR_E(EPI_RESID)
+        OCR_E(EPI_GLU)
+        OCR_E(EPI_ARGMAX)
+    }
+#undef OCR_E
+}
+
+// Final reduction of the per-workgroup argmax partials: one thread per row.
+__global__ void argmax_final_kernel(const float* part, int n_wg, int rows, int32_t* tok_out, float* top2,
+                                    int32_t* gen_index) {
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    float b = -INFINITY, s = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int w = 0; w < n_wg; ++w) {
+        const float* e = part + ((int64_t)w * rows + r) * 3;
+        argmax_merge(b, bi, s, e[0], __float_as_int(e[1]), e[2]);
+    }
+    if (tok_out) tok_out[r] = (bi == 0x7fffffff) ? 0 : bi;
+    if (top2) {
+        top2[2 * r] = b;
+        top2[2 * r + 1] = s;
+    }
+    if (gen_index) gen_index[r] += 1;
+}
+
+void launch_argmax_final(const float* part, int n_wg, int rows, int32_t* tok_out, float* top2, int32_t* gen_index,
+                         hipStream_t s) {
+    hipLaunchKernelGGL(argmax_final_kernel, dim3((rows + 63) / 64), dim3(64), 0, s, part, n_wg, rows, tok_out, top2,
+                       gen_index);
+}
+
+}  // namespace ocrdec
+
+using namespace ocrdec;
+
+extern "C" ocrdec_status ocrdec_gemv_q(const ocrdec_qmat* W, int32_t rows, const uint16_t* x, int64_t ldx, void* y,
+                                       int32_t y_type, int64_t ldy, void* stream) {
+    ocrdec_status st = check_qmat(W, "W");
+    if (st != OCRDEC_OK) return st;
+    OCR_CHECK_ARG(rows >= 1 && rows <= 4096, "rows must be in [1, 4096]");
+    OCR_CHECK_ARG(x && y, "x and y must be non-NULL");
+    OCR_CHECK_ARG(ldx >= W->k && ldx % 8 == 0, "ldx must be >= k and a multiple of 8");
+    OCR_CHECK_ARG(((uintptr_t)x & 15) == 0, "x must be 16-byte aligned");
+    OCR_CHECK_ARG(ldy >= W->n, "ldy must be >= n");
+    OCR_CHECK_ARG(y_type == OCRDEC_OUT_F32 || y_type == OCRDEC_OUT_F16, "unknown y_type");
+    const int epi = y_type == OCRDEC_OUT_F32 ? EPI_F32 : EPI_F16;
+    GemvPlan pl = plan_gemv(W->fmt, W->n, W->k, rows, epi);
+    GemvParams p{};
+    p.w = (const uint8_t*)W->data;
+    p.n = W->n;
+    p.k = W->k;
+    p.nchunks = n_chunks(W->fmt, W->k);
+    p.xs = XDirect{x, ldx, rows};
+    p.y = y;
+    p.ldy = ldy;
+    launch_gemv(W->fmt, epi, pl, p, (hipStream_t)stream);
+    return launch_status("ocrdec_gemv_q");
+}

@@ -1,0 +1,219 @@
+// Weight-streaming GEMV / skinny GEMM core for gfx950.
+//
+// One wavefront owns a group of 16-row weight tiles and a range of k-chunks
+// of the packed layout (common.hpp).  Per 32-column block it dequantises the
+// tile's codes in registers into the B operand of v_mfma_f32_16x16x32_f16
+// (column j = weight row, exact fp16 codes), takes the activations of up to
+// 16 tokens per x-tile as the A operand, and applies the block's fp16 scale to
+// the fp32 MFMA result, so every product is exact and the accumulation is
+// fp32 ("Eseguire Unlimited-OCR su Apple Silicon con C e Metal", section
+// "Quantizzazione": dequantisation fused into the GEMV, no fp16 copy of the
+// weights).  The result layout is the MFMA D layout: lane l, register v holds
+// token 16*xt + 4*(l >> 4) + v and weight row 16*tile + (l & 15).
+#pragma once
+
+#include "common.hpp"
+
+namespace ocrdec {
+
+template <int FMT>
+struct Geom;
+template <>
+struct Geom<OCRDEC_F16> { static constexpr int SB = 1, CB = 1024, SCB = 0; };
+template <>
+struct Geom<OCRDEC_Q8_0> { static constexpr int SB = 2, CB = 1088, SCB = 4; };
+template <>
+struct Geom<OCRDEC_Q4_0> { static constexpr int SB = 4, CB = 1152, SCB = 8; };
+template <>
+struct Geom<OCRDEC_U8A_G32> { static constexpr int SB = 2, CB = 1152, SCB = 8; };
+
+// Registers of one (tile, chunk) for one lane.
+struct WRegs {
+    uint4 q;
+    uint2 s;
+};
+
+template <int FMT>
+OCR_DEV void load_wchunk(const uint8_t* chunk, int lane, WRegs& r) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(chunk + lane * 16));
+    r.q = make_uint4(v.x, v.y, v.z, v.w);
+    if constexpr (FMT == OCRDEC_Q4_0 || FMT == OCRDEC_U8A_G32) {
+        r.s = *(const uint2*)(chunk + 1024 + (lane & 15) * 8);
+    } else if constexpr (FMT == OCRDEC_Q8_0) {
+        r.s.x = *(const uint32_t*)(chunk + 1024 + (lane & 15) * 4);
+        r.s.y = 0;
+    } else {
+        r.s = make_uint2(0, 0);
+    }
+}
+
+template <int FMT>
+OCR_DEV half8v wfrag(const WRegs& r, int j) {
+    if constexpr (FMT == OCRDEC_F16) {
+        return bits_to_half8(r.q);
+    } else if constexpr (FMT == OCRDEC_Q4_0) {
+        uint32_t dw = j == 0 ? r.q.x : j == 1 ? r.q.y : j == 2 ? r.q.z : r.q.w;
+        return deq_q4(dw);
+    } else if constexpr (FMT == OCRDEC_Q8_0) {
+        return j == 0 ? deq_q8(r.q.x, r.q.y) : deq_q8(r.q.z, r.q.w);
+    } else {
+        return j == 0 ? deq_u8(r.q.x, r.q.y) : deq_u8(r.q.z, r.q.w);
+    }
+}
+
+// fp16 scale of block j for this lane's weight row.
+template <int FMT>
+OCR_DEV float wscale(const WRegs& r, int j) {
+    if constexpr (FMT == OCRDEC_Q4_0) {
+        uint32_t w = (j < 2) ? r.s.x : r.s.y;
+        return h2f((uint16_t)((j & 1) ? (w >> 16) : (w & 0xFFFF)));
+    } else if constexpr (FMT == OCRDEC_Q8_0) {
+        return h2f((uint16_t)(j ? (r.s.x >> 16) : (r.s.x & 0xFFFF)));
+    } else if constexpr (FMT == OCRDEC_U8A_G32) {
+        uint32_t w = j ? r.s.y : r.s.x;
+        return h2f((uint16_t)(w & 0xFFFF));
+    } else {
+        return 1.0f;
+    }
+}
+
+// Zero point (int8-asymmetric only).
+OCR_DEV float wzero_u8a(const WRegs& r, int j) {
+    uint32_t w = j ? r.s.y : r.s.x;
+    return h2f((uint16_t)(w >> 16));
+}
+
+// Multiply-accumulate one (tile, chunk) into acc[XT].
+// xa[j][xt]: A fragments of block j, x-tile xt; xs[j][xt]: per-token sums of
+// the block's activations (int8-asymmetric only).
+template <int FMT, int XT>
+OCR_DEV void chunk_mac(const WRegs& w, const half8v (&xa)[Geom<FMT>::SB][XT],
+                       const float4v (&xs)[Geom<FMT>::SB][XT], float4v (&acc)[XT]) {
+    constexpr int SB = Geom<FMT>::SB;
+    const float4v zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+        half8v b = wfrag<FMT>(w, j);
+        if constexpr (FMT == OCRDEC_F16) {
+#pragma unroll
+            for (int xt = 0; xt < XT; ++xt) acc[xt] = mfma16(xa[j][xt], b, acc[xt]);
+        } else if constexpr (FMT == OCRDEC_U8A_G32) {
+            const float s = wscale<FMT>(w, j), z = wzero_u8a(w, j);
+#pragma unroll
+            for (int xt = 0; xt < XT; ++xt) {
+                float4v t = mfma16(xa[j][xt], b, zero);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[xt][v] = fmaf(s, fmaf(-z, xs[j][xt][v], t[v]), acc[xt][v]);
+            }
+        } else {
+            const float d = wscale<FMT>(w, j);
+#pragma unroll
+            for (int xt = 0; xt < XT; ++xt) {
+                float4v t = mfma16(xa[j][xt], b, zero);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[xt][v] = fmaf(d, t[v], acc[xt][v]);
+            }
+        }
+    }
+}
+
+// Activation source: token i of the current x-tile set -> fp16 row pointer.
+struct XDirect {
+    const uint16_t* x;
+    int64_t ld;
+    int rows;
+    OCR_DEV const uint16_t* row(int tok) const { return tok < rows ? x + (int64_t)tok * ld : nullptr; }
+};
+
+// Gathered activations: token i -> x[map[i]] (grouped MoE rows).
+struct XGather {
+    const uint16_t* x;
+    int64_t ld;
+    const int32_t* map;
+    int rows;
+    OCR_DEV const uint16_t* row(int tok) const {
+        return tok < rows ? x + (int64_t)map[tok] * ld : nullptr;
+    }
+};
+
+// Loads the A fragments of chunk c for tokens [tok0, tok0 + 16*XT).
+template <int FMT, int XT, class XS>
+OCR_DEV void load_xfrags(const XS& xs, int tok0, int c, int nblk, int lane, half8v (&xa)[Geom<FMT>::SB][XT],
+                         float4v (&xsum)[Geom<FMT>::SB][XT]) {
+    constexpr int SB = Geom<FMT>::SB;
+#pragma unroll
+    for (int xt = 0; xt < XT; ++xt) {
+        const uint16_t* p = xs.row(tok0 + 16 * xt + (lane & 15));
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const int blk = c * SB + j;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (p && blk < nblk) v = *(const uint4*)(p + blk * 32 + 8 * (lane >> 4));
+            xa[j][xt] = bits_to_half8(v);
+        }
+    }
+    if constexpr (FMT == OCRDEC_U8A_G32) {
+        const half8v ones = {(f16_t)1, (f16_t)1, (f16_t)1, (f16_t)1, (f16_t)1, (f16_t)1, (f16_t)1, (f16_t)1};
+        const float4v zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < SB; ++j)
+#pragma unroll
+            for (int xt = 0; xt < XT; ++xt) xsum[j][xt] = mfma16(xa[j][xt], ones, zero);
+    }
+}
+
+// The k-loop of one wavefront: NT tiles (tile[i] chunk pointers) over chunks
+// [c0, c1), accumulating into acc[NT][XT].  Loads of chunk c+1 are issued
+// before the MFMAs of chunk c.
+template <int FMT, int NT, int XT, class XS>
+OCR_DEV void kloop(const uint8_t* const (&tile)[NT], int c0, int c1, const XS& xs, int tok0, int nblk, int lane,
+                   float4v (&acc)[NT][XT]) {
+    constexpr int CB = Geom<FMT>::CB;
+    constexpr int SB = Geom<FMT>::SB;
+    if (c0 >= c1) return;
+    WRegs cur[NT], nxt[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) load_wchunk<FMT>(tile[i] + (int64_t)c0 * CB, lane, cur[i]);
+    for (int c = c0; c < c1; ++c) {
+        if (c + 1 < c1) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) load_wchunk<FMT>(tile[i] + (int64_t)(c + 1) * CB, lane, nxt[i]);
+        }
+        half8v xa[SB][XT];
+        float4v xsum[SB][XT];
+        load_xfrags<FMT, XT>(xs, tok0, c, nblk, lane, xa, xsum);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) chunk_mac<FMT, XT>(cur[i], xa, xsum, acc[i]);
+        if (c + 1 < c1) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) cur[i] = nxt[i];
+        }
+    }
+}
+
+// Sums the accumulators of the KS waves that share a tile group (waves
+// g*KS .. g*KS+KS-1 of the workgroup) in a fixed order; the result is valid in
+// the first of them.  red: LDS scratch of 4 * NT * XT * 64 float4v.
+template <int NT, int XT, int KS>
+OCR_DEV void ksplit_reduce(float4v (&acc)[NT][XT], float4v* red, int wave, int lane) {
+    if constexpr (KS == 1) return;
+    const int ks = wave % KS;
+    if (ks != 0) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int xt = 0; xt < XT; ++xt) red[((wave * NT + i) * XT + xt) * 64 + lane] = acc[i][xt];
+    }
+    __syncthreads();
+    if (ks == 0) {
+        for (int o = 1; o < KS; ++o) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int xt = 0; xt < XT; ++xt) acc[i][xt] += red[(((wave + o) * NT + i) * XT + xt) * 64 + lane];
+        }
+    }
+}
+
+}  // namespace ocrdec

@@ -1,0 +1,513 @@
+// DeepSeek-V2-style MoE ("Eseguire Unlimited-OCR su Apple Silicon con C e
+// Metal", section "Il decoder e il Mixture of Experts": 64 routed experts,
+// top-6 routing, 2 shared experts; the runtime computes the routing, groups
+// the tokens per expert, runs the projections and recombines the results).
+//
+//   router GEMV (fp32 logits)
+//   -> route_group: top-k per token, then a stable counting sort of the
+//      (token, rank) pairs by expert and the list of active experts (routed
+//      experts with at least one token, then the shared experts with all
+//      tokens) — all on the device, no host read-back
+//   -> grouped gate/up GEMV with the SwiGLU in the epilogue (fp16 a per slot)
+//   -> grouped down GEMV (fp32 y per slot)
+//   -> combine: shared outputs, then the routed ones weighted by rank order,
+//      summed in fp32 and added to the residual with one fp16 rounding.
+#include "moe.hpp"
+
+namespace ocrdec {
+
+// ---------------------------------------------------------------------------
+// Routing and grouping (one workgroup of 1024 threads)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void route_group_kernel(MoeParams p) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int R = p.rows, E = p.n_experts, K = p.top_k, S = p.n_shared;
+    const int NP = R * K;
+
+    // ---- 1. top-k of every row
+    for (int r = tid; r < R; r += blockDim.x) {
+        const float* lg = p.logits + (int64_t)r * E;
+        float l_sel[8];
+        int own[8];
+        for (int j = 0; j < K; ++j) {
+            float best = -INFINITY;
+            int bi = -1;
+            for (int e = 0; e < E; ++e) {
+                bool taken = false;
+                for (int i = 0; i < j; ++i) taken |= (own[i] == e);
+                if (taken) continue;
+                float v = lg[e] + (p.bias ? p.bias[e] : 0.f);
+                if (v > best || bi < 0) {
+                    if (bi < 0 && !(v == v)) continue;  // a NaN logit never wins
+                    best = v;
+                    bi = e;
+                }
+            }
+            own[j] = bi < 0 ? 0 : bi;
+        }
+        int use[8];
+        const bool forced = p.forced && p.forced[(int64_t)r * K] >= 0;
+        for (int j = 0; j < K; ++j) {
+            const int f = forced ? p.forced[(int64_t)r * K + j] : own[j];
+            use[j] = min(max(f, 0), E - 1);  // device data: keep every index in range
+        }
+        float m = -INFINITY;
+        for (int j = 0; j < K; ++j) {
+            l_sel[j] = lg[use[j]] + (p.bias ? p.bias[use[j]] : 0.f);
+            m = fmaxf(m, l_sel[j]);
+        }
+        float den = 0.f;
+        for (int j = 0; j < K; ++j) {
+            l_sel[j] = expf(l_sel[j] - m);
+            den += l_sel[j];
+        }
+        for (int j = 0; j < K; ++j) {
+            p.idx[(int64_t)r * K + j] = use[j];
+            p.w[(int64_t)r * K + j] = l_sel[j] / den;
+            if (p.cap_idx) p.cap_idx[(int64_t)r * K + j] = own[j];
+            if (p.cap_w) p.cap_w[(int64_t)r * K + j] = l_sel[j] / den;
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. per 64-pair chunk: rank of each pair among equal experts before
+    // it in the chunk, and the chunk's histogram
+    const int nchunk = (NP + 63) / 64;
+    for (int c = wave; c < nchunk; c += nw) {
+        const int pi = c * 64 + lane;
+        const int e = pi < NP ? p.idx[pi] : -1;
+        int rank = 0;
+        for (int i = 0; i < 64; ++i) {
+            const int ei = __shfl(e, i, 64);
+            rank += (i < lane && ei == e) ? 1 : 0;
+        }
+        if (pi < NP) p.rank[pi] = rank;
+        for (int eb = 0; eb < E; eb += 64) {
+            const int me = eb + lane;
+            int cnt = 0;
+            for (int i = 0; i < 64; ++i) cnt += (__shfl(e, i, 64) == me) ? 1 : 0;
+            if (me < E) p.hist[(int64_t)c * E + me] = cnt;
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. per expert: exclusive prefix of the chunk histograms, counts
+    for (int e = tid; e < E; e += blockDim.x) {
+        int run = 0;
+        for (int c = 0; c < nchunk; ++c) {
+            const int h = p.hist[(int64_t)c * E + e];
+            p.hist[(int64_t)c * E + e] = run;
+            run += h;
+        }
+        p.counts[e] = run;
+    }
+    __syncthreads();
+    // exclusive scan of counts and the compact list of active experts (wave 0)
+    if (wave == 0) {
+        int base = 0, act = 0;
+        for (int eb = 0; eb < E; eb += 64) {
+            const int e = eb + lane;
+            const int cnt = e < E ? p.counts[e] : 0;
+            int incl = cnt, ai = cnt > 0 ? 1 : 0;
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(incl, o, 64);
+                const int ta = __shfl_up(ai, o, 64);
+                if (lane >= o) {
+                    incl += t;
+                    ai += ta;
+                }
+            }
+            const int excl = base + incl - cnt;
+            if (e < E) p.offsets[e] = excl;
+            if (e < E && cnt > 0) {
+                const int v = act + ai - 1;
+                p.virt_expert[v] = e;
+                p.virt_off[v] = excl;
+                p.virt_cnt[v] = cnt;
+            }
+            base += __shfl(incl, 63, 64);
+            act += __shfl(ai, 63, 64);
+        }
+        if (lane == 0) {
+            p.offsets[E] = base;
+            for (int s = 0; s < S; ++s) {
+                p.virt_expert[act + s] = E + s;
+                p.virt_off[act + s] = NP + s * R;
+                p.virt_cnt[act + s] = R;
+            }
+            p.n_virt[0] = act + S;
+        }
+    }
+    __syncthreads();
+
+    // ---- 4. scatter: grouped position of every pair
+    for (int pi = tid; pi < NP; pi += blockDim.x) {
+        const int e = p.idx[pi];
+        const int pos = p.offsets[e] + p.hist[(int64_t)(pi / 64) * E + e] + p.rank[pi];
+        p.perm[pos] = pi;
+        p.inv[pi] = pos;
+        p.slot_row[pos] = pi / K;
+    }
+    for (int i = tid; i < S * R; i += blockDim.x) p.slot_row[NP + i] = i % R;
+    __syncthreads();
+    if (p.cap_counts)
+        for (int e = tid; e < E; e += blockDim.x) p.cap_counts[e] = p.counts[e];
+    if (p.cap_offsets)
+        for (int e = tid; e <= E; e += blockDim.x) p.cap_offsets[e] = p.offsets[e];
+    if (p.cap_perm)
+        for (int i = tid; i < NP; i += blockDim.x) p.cap_perm[i] = p.perm[i];
+}
+
+// ---------------------------------------------------------------------------
+// Grouped expert GEMV
+//
+// Work item (virtual expert v, tile group g).  GLU mode: the gate tile g and
+// the up tile g + d_ff/16 of expert v over the tokens routed to it, SwiGLU in
+// the epilogue, fp16 a[slot][col].  DOWN mode: tile g of the down matrix over
+// the expert's slots of a, fp32 y[slot][row].
+// ---------------------------------------------------------------------------
+
+template <int FMT, int XT, int KS, bool GLU>
+__global__ __launch_bounds__(256) void grouped_kernel(GroupedParams p) {
+    constexpr int CB = Geom<FMT>::CB;
+    constexpr int NT = GLU ? 2 : 1;
+    __shared__ float4v red[(KS > 1) ? 4 * NT * XT * 64 : 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int item = blockIdx.x * (4 / KS) + wave / KS;
+    const int ks = wave % KS;
+    const int v = item / p.groups_per_expert;
+    const int g = item % p.groups_per_expert;
+    const int n_virt = p.n_virt[0];
+    const bool valid = v < n_virt && v < p.max_virt;
+    // uniform across the workgroup: every wave must reach the barriers below
+    const int e = valid ? p.virt_expert[v] : 0;
+    const int off = valid ? p.virt_off[v] : 0;
+    const int cnt = valid ? p.virt_cnt[v] : 0;
+    const uint8_t* base = (e < p.n_experts) ? p.w_routed + (int64_t)e * p.expert_bytes
+                                            : p.w_shared + (int64_t)(e - p.n_experts) * p.expert_bytes;
+    const uint8_t* tile[NT];
+    int tidx[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        tidx[i] = GLU ? (i == 0 ? g : g + p.half_tiles) : g;
+        tile[i] = base + (int64_t)tidx[i] * p.nchunks * CB;
+    }
+    const int cper = (int)((p.nchunks + KS - 1) / KS);
+    const int c0 = ks * cper;
+    const int c1 = valid ? (int)min((int64_t)(c0 + cper), p.nchunks) : c0;
+    const int nblk = p.k / 32;
+    // token passes: the workgroup loops to the largest count among its waves
+    int passes = (cnt + 16 * XT - 1) / (16 * XT);
+    for (int pass = 0;; ++pass) {
+        // all waves of the workgroup run the same number of passes
+        int my_more = pass < passes ? 1 : 0;
+        if (!__syncthreads_or(my_more)) break;
+        const int tok0 = pass * 16 * XT;
+        float4v acc[NT][XT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int xt = 0; xt < XT; ++xt) acc[i][xt] = float4v{0.f, 0.f, 0.f, 0.f};
+        const int cc1 = my_more ? c1 : c0;
+        if constexpr (GLU) {
+            XGather xs{p.x, p.ldx, p.slot_row + off, cnt};
+            kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
+        } else {
+            XDirect xs{p.x + (int64_t)off * p.ldx, p.ldx, cnt};
+            kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
+        }
+        ksplit_reduce<NT, XT, KS>(acc, red, wave, lane);
+        if (ks == 0 && my_more) {
+#pragma unroll
+            for (int xt = 0; xt < XT; ++xt)
+#pragma unroll
+                for (int vv = 0; vv < 4; ++vv) {
+                    const int tok = tok0 + 16 * xt + 4 * (lane >> 4) + vv;
+                    if (tok >= cnt) continue;
+                    const int64_t slot = off + tok;
+                    if constexpr (GLU) {
+                        const int col = tidx[0] * 16 + (lane & 15);
+                        const float gv = acc[0][xt][vv], uv = acc[1][xt][vv];
+                        ((uint16_t*)p.y)[slot * p.ldy + col] = f2h(silu(gv) * uv);
+                    } else {
+                        const int row = tidx[0] * 16 + (lane & 15);
+                        ((float*)p.y)[slot * p.ldy + row] = acc[0][xt][vv];
+                    }
+                }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Combine (+ optional RMSNorm of the updated residual): one workgroup per row
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+    __shared__ float red[8];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int K = p.top_k, R = p.rows, H = p.hidden;
+    uint16_t* h = p.h + (int64_t)r * p.ldh;
+    float ss = 0.f;
+    for (int col = tid; col < H; col += blockDim.x) {
+        float acc = 0.f;
+        for (int s = 0; s < p.n_shared; ++s) acc += p.y[((int64_t)p.np + s * R + r) * H + col];
+        for (int j = 0; j < K; ++j) acc = fmaf(p.w[r * K + j], p.y[(int64_t)p.inv[r * K + j] * H + col], acc);
+        const float hv = p.add_residual ? h2f(h[col]) + acc : acc;
+        const uint16_t hb = f2h(hv);
+        h[col] = hb;
+        const float hr = h2f(hb);
+        ss = fmaf(hr, hr, ss);
+    }
+    if (!p.norm_w) return;
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += red[i];
+    const float inv = 1.0f / sqrtf(tot / (float)H + p.eps);
+    uint16_t* x = p.x_out + (int64_t)r * p.ldx;
+    for (int col = tid; col < H; col += blockDim.x) x[col] = f2h(h2f(h[col]) * inv * h2f(p.norm_w[col]));
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+MoeWs carve_moe(void* ws, int rows, const ocrdec_moe_weights* w) {
+    Carve cv(ws);
+    MoeWs m;
+    const int NP = rows * w->top_k, E = w->n_experts, S = w->n_shared;
+    const int nslots = NP + S * rows;
+    m.logits = cv.take<float>((size_t)rows * E);
+    m.idx = cv.take<int32_t>(NP);
+    m.w = cv.take<float>(NP);
+    m.rank = cv.take<int32_t>(NP);
+    m.hist = cv.take<int32_t>((size_t)((NP + 63) / 64) * E);
+    m.counts = cv.take<int32_t>(E);
+    m.offsets = cv.take<int32_t>(E + 1);
+    m.perm = cv.take<int32_t>(NP);
+    m.inv = cv.take<int32_t>(NP);
+    m.slot_row = cv.take<int32_t>(nslots);
+    m.n_virt = cv.take<int32_t>(1);
+    m.virt_expert = cv.take<int32_t>(E + S);
+    m.virt_off = cv.take<int32_t>(E + S);
+    m.virt_cnt = cv.take<int32_t>(E + S);
+    m.a = cv.take<uint16_t>((size_t)nslots * w->d_ff);
+    m.y = cv.take<float>((size_t)nslots * w->hidden);
+    m.bytes = cv.off;
+    return m;
+}
+
+ocrdec_status check_moe(const ocrdec_moe_weights* w, int rows) {
+    OCR_CHECK_ARG(w, "weights is NULL");
+    OCR_CHECK_ARG(rows >= 1 && rows <= 65536, "rows must be in [1, 65536]");
+    OCR_CHECK_ARG(w->hidden > 0 && w->hidden % 32 == 0, "hidden must be a positive multiple of 32");
+    OCR_CHECK_ARG(w->d_ff > 0 && w->d_ff % 32 == 0, "d_ff must be a positive multiple of 32");
+    if (w->n_experts < 1 || w->n_experts > 256) return fail(OCRDEC_ERR_UNSUPPORTED, "n_experts must be in [1, 256]");
+    if (w->top_k < 1 || w->top_k > 8 || w->top_k > w->n_experts)
+        return fail(OCRDEC_ERR_UNSUPPORTED, "top_k must be in [1, min(8, n_experts)]");
+    OCR_CHECK_ARG(w->n_shared >= 0 && w->n_shared <= 8, "n_shared must be in [0, 8]");
+    ocrdec_status s;
+    if ((s = check_qmat(&w->router, "router")) != OCRDEC_OK) return s;
+    if ((s = check_qmat(&w->gate_up, "gate_up")) != OCRDEC_OK) return s;
+    if ((s = check_qmat(&w->down, "down")) != OCRDEC_OK) return s;
+    OCR_CHECK_ARG(w->router.n == w->n_experts && w->router.k == w->hidden, "router must be [n_experts][hidden]");
+    OCR_CHECK_ARG(w->gate_up.n == w->n_experts * 2 * w->d_ff && w->gate_up.k == w->hidden,
+                  "gate_up must be [n_experts*2*d_ff][hidden]");
+    OCR_CHECK_ARG(w->down.n == w->n_experts * w->hidden && w->down.k == w->d_ff, "down must be [n_experts*hidden][d_ff]");
+    if (w->n_shared > 0) {
+        if ((s = check_qmat(&w->sh_gate_up, "sh_gate_up")) != OCRDEC_OK) return s;
+        if ((s = check_qmat(&w->sh_down, "sh_down")) != OCRDEC_OK) return s;
+        OCR_CHECK_ARG(w->sh_gate_up.n == w->n_shared * 2 * w->d_ff && w->sh_gate_up.k == w->hidden,
+                      "sh_gate_up must be [n_shared*2*d_ff][hidden]");
+        OCR_CHECK_ARG(w->sh_down.n == w->n_shared * w->hidden && w->sh_down.k == w->d_ff,
+                      "sh_down must be [n_shared*hidden][d_ff]");
+        if (w->sh_gate_up.fmt != w->gate_up.fmt || w->sh_down.fmt != w->down.fmt)
+            return fail(OCRDEC_ERR_UNSUPPORTED, "shared and routed experts must use the same formats");
+    }
+    return OCRDEC_OK;
+}
+
+namespace {
+
+template <int FMT, bool GLU>
+void launch_grouped_fmt(const GroupedParams& p, int xt, int ks, int grid, hipStream_t s) {
+#define OCR_G(XT_, KS_)                                                                               \
+    if (xt == XT_ && ks == KS_) {                                                                    \
+        hipLaunchKernelGGL((grouped_kernel<FMT, XT_, KS_, GLU>), dim3(grid), dim3(256), 0, s, p);   \
+        return;                                                                                      \
+    }
+    OCR_G(1, 1) OCR_G(2, 1) OCR_G(1, 4) OCR_G(2, 4)
+#undef OCR_G
+}
+
+void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream_t s) {
+    const int xt = rows_hint <= 16 ? 1 : 2;
+    const int64_t items = (int64_t)p.max_virt * p.groups_per_expert;
+    const int ks = items >= 2048 ? 1 : 4;
+    const int grid = (int)((items + (4 / ks) - 1) / (4 / ks));
+#define OCR_F(F_)                                                                          \
+    case F_:                                                                               \
+        if (glu) launch_grouped_fmt<F_, true>(p, xt, ks, grid, s);                         \
+        else launch_grouped_fmt<F_, false>(p, xt, ks, grid, s);                            \
+        break;
+    switch (fmt) {
+        OCR_F(OCRDEC_F16)
+        OCR_F(OCRDEC_Q8_0)
+        OCR_F(OCRDEC_Q4_0)
+        OCR_F(OCRDEC_U8A_G32)
+    }
+#undef OCR_F
+}
+
+}  // namespace
+
+void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, uint16_t* h, int64_t ldh,
+                int add_residual, const int32_t* forced, const ocrdec_moe_capture* cap, int32_t* cap_idx,
+                float* cap_w, const MoeWs& m, const uint16_t* norm_w, float eps, uint16_t* x_out, int64_t ldxo,
+                hipStream_t s) {
+    const int E = w->n_experts, K = w->top_k, S = w->n_shared, F = w->d_ff, H = w->hidden;
+    const int NP = rows * K;
+    // router logits
+    {
+        GemvPlan pl = plan_gemv(w->router.fmt, E, H, rows, EPI_F32);
+        GemvParams gp{};
+        gp.w = (const uint8_t*)w->router.data;
+        gp.n = E;
+        gp.k = H;
+        gp.nchunks = n_chunks(w->router.fmt, H);
+        gp.xs = XDirect{x, ldx, rows};
+        gp.y = m.logits;
+        gp.ldy = E;
+        launch_gemv(w->router.fmt, EPI_F32, pl, gp, s);
+    }
+    // routing + grouping
+    {
+        MoeParams p{};
+        p.rows = rows;
+        p.n_experts = E;
+        p.top_k = K;
+        p.n_shared = S;
+        p.logits = m.logits;
+        p.bias = w->router_bias;
+        p.forced = forced;
+        p.idx = m.idx;
+        p.w = m.w;
+        p.rank = m.rank;
+        p.hist = m.hist;
+        p.counts = m.counts;
+        p.offsets = m.offsets;
+        p.perm = m.perm;
+        p.inv = m.inv;
+        p.slot_row = m.slot_row;
+        p.n_virt = m.n_virt;
+        p.virt_expert = m.virt_expert;
+        p.virt_off = m.virt_off;
+        p.virt_cnt = m.virt_cnt;
+        p.cap_idx = cap_idx ? cap_idx : (cap ? cap->topk_idx : nullptr);
+        p.cap_w = cap_w ? cap_w : (cap ? cap->topk_w : nullptr);
+        p.cap_counts = cap ? cap->counts : nullptr;
+        p.cap_offsets = cap ? cap->offsets : nullptr;
+        p.cap_perm = cap ? cap->perm : nullptr;
+        hipLaunchKernelGGL(route_group_kernel, dim3(1), dim3(1024), 0, s, p);
+    }
+    const int max_virt = std::min(E, NP) + S;
+    // gate/up with SwiGLU
+    {
+        GroupedParams p{};
+        p.w_routed = (const uint8_t*)w->gate_up.data;
+        p.w_shared = S ? (const uint8_t*)w->sh_gate_up.data : nullptr;
+        p.n_experts = E;
+        p.k = H;
+        p.nchunks = n_chunks(w->gate_up.fmt, H);
+        p.expert_bytes = (int64_t)(2 * F / 16) * p.nchunks * pack_cb(w->gate_up.fmt);
+        p.half_tiles = F / 16;
+        p.groups_per_expert = F / 16;
+        p.max_virt = max_virt;
+        p.n_virt = m.n_virt;
+        p.virt_expert = m.virt_expert;
+        p.virt_off = m.virt_off;
+        p.virt_cnt = m.virt_cnt;
+        p.slot_row = m.slot_row;
+        p.x = x;
+        p.ldx = ldx;
+        p.y = m.a;
+        p.ldy = F;
+        launch_grouped(w->gate_up.fmt, true, p, rows, s);
+    }
+    // down
+    {
+        GroupedParams p{};
+        p.w_routed = (const uint8_t*)w->down.data;
+        p.w_shared = S ? (const uint8_t*)w->sh_down.data : nullptr;
+        p.n_experts = E;
+        p.k = F;
+        p.nchunks = n_chunks(w->down.fmt, F);
+        p.expert_bytes = (int64_t)(H / 16) * p.nchunks * pack_cb(w->down.fmt);
+        p.half_tiles = 0;
+        p.groups_per_expert = H / 16;
+        p.max_virt = max_virt;
+        p.n_virt = m.n_virt;
+        p.virt_expert = m.virt_expert;
+        p.virt_off = m.virt_off;
+        p.virt_cnt = m.virt_cnt;
+        p.slot_row = m.slot_row;
+        p.x = m.a;
+        p.ldx = F;
+        p.y = m.y;
+        p.ldy = H;
+        launch_grouped(w->down.fmt, false, p, rows, s);
+    }
+    // combine
+    {
+        CombineParams p{};
+        p.rows = rows;
+        p.hidden = H;
+        p.top_k = K;
+        p.n_shared = S;
+        p.np = NP;
+        p.w = m.w;
+        p.inv = m.inv;
+        p.y = m.y;
+        p.h = h;
+        p.ldh = ldh;
+        p.add_residual = add_residual;
+        p.norm_w = norm_w;
+        p.eps = eps;
+        p.x_out = x_out;
+        p.ldx = ldxo;
+        hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(256), 0, s, p);
+    }
+}
+
+}  // namespace ocrdec
+
+using namespace ocrdec;
+
+extern "C" ocrdec_status ocrdec_moe_workspace_bytes(const ocrdec_moe_weights* w, int32_t rows, size_t* bytes) {
+    ocrdec_status st = check_moe(w, rows);
+    if (st != OCRDEC_OK) return st;
+    OCR_CHECK_ARG(bytes, "bytes is NULL");
+    *bytes = carve_moe(nullptr, rows, w).bytes;
+    return OCRDEC_OK;
+}
+
+extern "C" ocrdec_status ocrdec_moe_layer(const ocrdec_moe_weights* w, int32_t rows, const uint16_t* x, uint16_t* h,
+                                          int32_t add_residual, const int32_t* forced_topk,
+                                          const ocrdec_moe_capture* capture, void* ws, size_t ws_bytes,
+                                          void* stream) {
+    ocrdec_status st = check_moe(w, rows);
+    if (st != OCRDEC_OK) return st;
+    OCR_CHECK_ARG(x && h, "x and h must be non-NULL");
+    OCR_CHECK_ARG(((uintptr_t)x & 15) == 0, "x must be 16-byte aligned");
+    const size_t need = carve_moe(nullptr, rows, w).bytes;
+    if (!ws || ws_bytes < need)
+        return fail(OCRDEC_ERR_WORKSPACE, "MoE workspace: need " + std::to_string(need) + " bytes, got " +
+                                              std::to_string(ws ? ws_bytes : 0));
+    MoeWs m = carve_moe(ws, rows, w);
+    launch_moe(w, rows, x, w->hidden, h, w->hidden, add_residual, forced_topk, capture, nullptr, nullptr, m, nullptr,
+               0.f, nullptr, 0, (hipStream_t)stream);
+    return launch_status("ocrdec_moe_layer");
+}

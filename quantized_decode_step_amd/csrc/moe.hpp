@@ -1,0 +1,103 @@
+// Host-side interface of the MoE kernels (used by ocrdec_moe_layer and the step).
+#pragma once
+
+#include <algorithm>
+
+#include "gemv.hpp"
+
+namespace ocrdec {
+
+inline int pack_cb(int fmt) {
+    PackGeom g;
+    pack_geom(fmt, &g);
+    return g.cb;
+}
+
+struct MoeParams {
+    int rows, n_experts, top_k, n_shared;
+    const float* logits;
+    const float* bias;
+    const int32_t* forced;
+    int32_t* idx;
+    float* w;
+    int32_t* rank;
+    int32_t* hist;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* inv;
+    int32_t* slot_row;
+    int32_t* n_virt;
+    int32_t* virt_expert;
+    int32_t* virt_off;
+    int32_t* virt_cnt;
+    int32_t* cap_idx;
+    float* cap_w;
+    int32_t* cap_counts;
+    int32_t* cap_offsets;
+    int32_t* cap_perm;
+};
+
+struct GroupedParams {
+    const uint8_t* w_routed;
+    const uint8_t* w_shared;
+    int n_experts;
+    int k;
+    int64_t nchunks;
+    int64_t expert_bytes;
+    int half_tiles;
+    int groups_per_expert;
+    int max_virt;
+    const int32_t* n_virt;
+    const int32_t* virt_expert;
+    const int32_t* virt_off;
+    const int32_t* virt_cnt;
+    const int32_t* slot_row;
+    const uint16_t* x;
+    int64_t ldx;
+    void* y;
+    int64_t ldy;
+};
+
+struct CombineParams {
+    int rows, hidden, top_k, n_shared, np;
+    const float* w;
+    const int32_t* inv;
+    const float* y;
+    uint16_t* h;
+    int64_t ldh;
+    int add_residual;
+    const uint16_t* norm_w;  // RMSNorm gain of the next block, or NULL
+    float eps;
+    uint16_t* x_out;
+    int64_t ldx;
+};
+
+struct MoeWs {
+    float* logits;
+    int32_t* idx;
+    float* w;
+    int32_t* rank;
+    int32_t* hist;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* inv;
+    int32_t* slot_row;
+    int32_t* n_virt;
+    int32_t* virt_expert;
+    int32_t* virt_off;
+    int32_t* virt_cnt;
+    uint16_t* a;
+    float* y;
+    size_t bytes;
+};
+
+MoeWs carve_moe(void* ws, int rows, const ocrdec_moe_weights* w);
+ocrdec_status check_moe(const ocrdec_moe_weights* w, int rows);
+void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, uint16_t* h, int64_t ldh,
+                int add_residual, const int32_t* forced, const ocrdec_moe_capture* cap, int32_t* cap_idx,
+                float* cap_w, const MoeWs& m, const uint16_t* norm_w, float eps, uint16_t* x_out, int64_t ldxo,
+                hipStream_t s);
+
+}  // namespace ocrdec

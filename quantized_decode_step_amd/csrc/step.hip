@@ -1,0 +1,313 @@
+// The decode step ("Eseguire Unlimited-OCR su Apple Silicon con C e Metal",
+// section "Il decoder e il Mixture of Experts"): embedding lookup, the layer
+// stack (pre-norm attention over the prefix + ring cache, then the dense
+// SwiGLU or the MoE), the final RMSNorm and the language-head argmax, all
+// enqueued on the caller's stream with no host synchronisation, so the token
+// of one step can feed the next on the device ("How it is meant to be run",
+// Falcon-OCR card: rows of a round share one read of the weights).
+#include "attn.hpp"
+#include "moe.hpp"
+
+namespace ocrdec {
+
+namespace {
+
+constexpr int kMaxRows = 32;
+
+// x = fp16(RMSNorm(h) * gamma) of one row; the workgroup's threads stride
+// over the columns.
+OCR_DEV void norm_row(const uint16_t* h, const uint16_t* gamma, int H, float eps, uint16_t* x, float* red) {
+    const int tid = threadIdx.x;
+    float ss = 0.f;
+    for (int c = tid; c < H; c += blockDim.x) {
+        const float v = h2f(h[c]);
+        ss = fmaf(v, v, ss);
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += red[i];
+    const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+    for (int c = tid; c < H; c += blockDim.x) x[c] = f2h(h2f(h[c]) * inv * h2f(gamma[c]));
+}
+
+// h[r] = embed[tok[r]] or src[r]; x[r] = norm(h[r]).
+__global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tok, const uint16_t* embed, int vocab,
+                                                         const uint16_t* src, uint16_t* h, const uint16_t* gamma,
+                                                         int H, float eps, uint16_t* x) {
+    __shared__ float red[8];
+    const int r = blockIdx.x;
+    const uint16_t* from;
+    if (tok) {
+        int t = tok[r];
+        t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
+        from = embed + (int64_t)t * H;
+    } else {
+        from = src + (int64_t)r * H;
+    }
+    uint16_t* hr = h + (int64_t)r * H;
+    for (int c = threadIdx.x; c < H; c += blockDim.x) hr[c] = from[c];
+    __syncthreads();
+    norm_row(hr, gamma, H, eps, x + (int64_t)r * H, red);
+}
+
+__global__ __launch_bounds__(256) void norm_kernel(const uint16_t* h, const uint16_t* gamma, int H, float eps,
+                                                   uint16_t* x) {
+    __shared__ float red[8];
+    const int r = blockIdx.x;
+    norm_row(h + (int64_t)r * H, gamma, H, eps, x + (int64_t)r * H, red);
+}
+
+__global__ void copy_rows_kernel(const uint16_t* src, uint16_t* dst, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = src[i];
+}
+
+__global__ void bump_kernel(int32_t* gen_index, int rows) {
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r < rows) gen_index[r] += 1;
+}
+
+struct StepWs {
+    uint16_t* h;
+    uint16_t* x;
+    float* qkv;
+    float* attn_part;
+    uint16_t* o;
+    uint16_t* a;
+    float* lm_part;
+    MoeWs moe;
+    size_t bytes;
+};
+
+int lm_grid(const ocrdec_model* m, int rows) {
+    if (!m->lm_head.data) return 0;
+    return plan_gemv(m->lm_head.fmt, m->lm_head.n, m->lm_head.k, rows, EPI_ARGMAX).grid;
+}
+
+StepWs carve_step(void* ws, const ocrdec_model* m, int rows, int cache_cap) {
+    Carve cv(ws);
+    StepWs w;
+    const int H = m->hidden, HD = m->n_heads * m->head_dim;
+    int dense_ff = 0;
+    const ocrdec_moe_weights* moe = nullptr;
+    for (int l = 0; l < m->n_layers; ++l) {
+        if (m->layers[l].is_moe) moe = &m->layers[l].moe;
+        else dense_ff = std::max(dense_ff, m->layers[l].dense_ff);
+    }
+    w.h = cv.take<uint16_t>((size_t)rows * H);
+    w.x = cv.take<uint16_t>((size_t)rows * H);
+    w.qkv = cv.take<float>((size_t)rows * 3 * HD);
+    w.attn_part = cv.take<float>(attn_ws_bytes(rows, m->n_heads, m->head_dim, cache_cap) / sizeof(float));
+    w.o = cv.take<uint16_t>((size_t)rows * HD);
+    w.a = cv.take<uint16_t>((size_t)rows * std::max(dense_ff, 1));
+    w.lm_part = cv.take<float>((size_t)std::max(lm_grid(m, rows), 1) * rows * 3);
+    if (moe) {
+        MoeWs probe = carve_moe(nullptr, rows, moe);
+        char* base = (char*)cv.take<char>(probe.bytes);
+        w.moe = carve_moe(ws ? base : nullptr, rows, moe);
+    } else {
+        w.moe = MoeWs{};
+    }
+    w.bytes = cv.off;
+    return w;
+}
+
+ocrdec_status check_step(const ocrdec_model* m, const ocrdec_state* st) {
+    OCR_CHECK_ARG(m && st, "model and state must be non-NULL");
+    OCR_CHECK_ARG(st->rows >= 1 && st->rows <= kMaxRows, "rows must be in [1, 32]");
+    OCR_CHECK_ARG(st->ring_cap >= 1 && st->prefix_cap >= 0, "ring_cap must be >= 1 and prefix_cap >= 0");
+    OCR_CHECK_ARG(st->prefix_len && st->gen_index, "state arrays must be non-NULL");
+    OCR_CHECK_ARG(m->n_layers >= 1 && m->layers, "model needs at least one layer");
+    OCR_CHECK_ARG(m->hidden > 0 && m->hidden % 32 == 0, "hidden must be a positive multiple of 32");
+    if (m->head_dim != 64 && m->head_dim != 128) return fail(OCRDEC_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    OCR_CHECK_ARG(m->n_heads >= 1, "n_heads must be >= 1");
+    OCR_CHECK_ARG((m->n_heads * m->head_dim) % 32 == 0, "n_heads*head_dim must be a multiple of 32");
+    const int H = m->hidden, HD = m->n_heads * m->head_dim;
+    ocrdec_status s;
+    const ocrdec_moe_weights* moe0 = nullptr;
+    for (int l = 0; l < m->n_layers; ++l) {
+        const ocrdec_layer& L = m->layers[l];
+        const std::string tag = "layer " + std::to_string(l) + ": ";
+        OCR_CHECK_ARG(L.attn_norm && L.ffn_norm, tag + "norm gains must be non-NULL");
+        OCR_CHECK_ARG(L.k_cache && L.v_cache, tag + "caches must be non-NULL");
+        if ((s = check_qmat(&L.wqkv, "wqkv")) != OCRDEC_OK) return s;
+        if ((s = check_qmat(&L.wo, "wo")) != OCRDEC_OK) return s;
+        OCR_CHECK_ARG(L.wqkv.n == 3 * HD && L.wqkv.k == H, tag + "wqkv must be [3*n_heads*head_dim][hidden]");
+        OCR_CHECK_ARG(L.wo.n == H && L.wo.k == HD, tag + "wo must be [hidden][n_heads*head_dim]");
+        if (L.is_moe) {
+            if ((s = check_moe(&L.moe, st->rows)) != OCRDEC_OK) return s;
+            OCR_CHECK_ARG(L.moe.hidden == H, tag + "moe.hidden must equal hidden");
+            if (moe0) {
+                OCR_CHECK_ARG(L.moe.n_experts == moe0->n_experts && L.moe.top_k == moe0->top_k &&
+                                  L.moe.n_shared == moe0->n_shared && L.moe.d_ff == moe0->d_ff,
+                              tag + "all MoE layers must share n_experts, top_k, n_shared and d_ff");
+            }
+            moe0 = &L.moe;
+        } else {
+            if ((s = check_qmat(&L.dense_gate_up, "dense_gate_up")) != OCRDEC_OK) return s;
+            if ((s = check_qmat(&L.dense_down, "dense_down")) != OCRDEC_OK) return s;
+            OCR_CHECK_ARG(L.dense_ff > 0 && L.dense_ff % 32 == 0, tag + "dense_ff must be a positive multiple of 32");
+            OCR_CHECK_ARG(L.dense_gate_up.n == 2 * L.dense_ff && L.dense_gate_up.k == H,
+                          tag + "dense_gate_up must be [2*dense_ff][hidden]");
+            OCR_CHECK_ARG(L.dense_down.n == H && L.dense_down.k == L.dense_ff,
+                          tag + "dense_down must be [hidden][dense_ff]");
+        }
+    }
+    if (m->lm_head.data) {
+        if ((s = check_qmat(&m->lm_head, "lm_head")) != OCRDEC_OK) return s;
+        OCR_CHECK_ARG(m->lm_head.k == H && m->lm_head.n == m->vocab, "lm_head must be [vocab][hidden]");
+        OCR_CHECK_ARG(m->final_norm, "final_norm must be non-NULL with an LM head");
+    }
+    return OCRDEC_OK;
+}
+
+}  // namespace
+
+}  // namespace ocrdec
+
+using namespace ocrdec;
+
+extern "C" ocrdec_status ocrdec_step_workspace_bytes(const ocrdec_model* m, const ocrdec_state* st,
+                                                     size_t* bytes) {
+    ocrdec_status s0 = check_step(m, st);
+    if (s0 != OCRDEC_OK) return s0;
+    OCR_CHECK_ARG(bytes, "bytes is NULL");
+    OCR_CHECK_ARG(st->prefix_cap + st->ring_cap <= (1 << 16), "prefix_cap + ring_cap must be <= 65536");
+    *bytes = carve_step(nullptr, m, st->rows, st->prefix_cap + st->ring_cap).bytes;
+    return OCRDEC_OK;
+}
+
+extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_state* st, const int32_t* tok_in,
+                                            uint16_t* hidden, int32_t* tok_out, const int32_t* forced_topk,
+                                            const ocrdec_step_capture* cap, void* ws, size_t ws_bytes, void* stream) {
+    ocrdec_status s0 = check_step(m, st);
+    if (s0 != OCRDEC_OK) return s0;
+    OCR_CHECK_ARG(tok_in || hidden, "either tok_in or hidden must be given");
+    OCR_CHECK_ARG(!tok_in || m->embed, "tok_in needs an embedding table");
+    const int R = st->rows, H = m->hidden, HD = m->n_heads * m->head_dim;
+    const int cache_cap = st->prefix_cap + st->ring_cap;
+    OCR_CHECK_ARG(cache_cap <= (1 << 16), "prefix_cap + ring_cap must be <= 65536");
+    const size_t need = carve_step(nullptr, m, R, cache_cap).bytes;
+    if (!ws || ws_bytes < need)
+        return fail(OCRDEC_ERR_WORKSPACE, "step workspace: need " + std::to_string(need) + " bytes, got " +
+                                              std::to_string(ws ? ws_bytes : 0));
+    hipStream_t s = (hipStream_t)stream;
+    StepWs w = carve_step(ws, m, R, cache_cap);
+
+    hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(256), 0, s, tok_in, m->embed, m->vocab, hidden, w.h,
+                       m->layers[0].attn_norm, H, m->norm_eps, w.x);
+    int moe_l = 0;
+    for (int l = 0; l < m->n_layers; ++l) {
+        const ocrdec_layer& L = m->layers[l];
+        const uint16_t* next_norm = (l + 1 < m->n_layers) ? m->layers[l + 1].attn_norm : m->final_norm;
+        // QKV
+        {
+            GemvPlan pl = plan_gemv(L.wqkv.fmt, L.wqkv.n, H, R, EPI_F32);
+            GemvParams gp{};
+            gp.w = (const uint8_t*)L.wqkv.data;
+            gp.n = L.wqkv.n;
+            gp.k = H;
+            gp.nchunks = n_chunks(L.wqkv.fmt, H);
+            gp.xs = XDirect{w.x, H, R};
+            gp.y = w.qkv;
+            gp.ldy = 3 * HD;
+            launch_gemv(L.wqkv.fmt, EPI_F32, pl, gp, s);
+        }
+        // attention
+        {
+            AttnParams ap{};
+            ap.rows = R;
+            ap.n_heads = m->n_heads;
+            ap.head_dim = m->head_dim;
+            ap.qkv = w.qkv;
+            ap.ld_qkv = 3 * HD;
+            ap.k_cache = L.k_cache;
+            ap.v_cache = L.v_cache;
+            ap.prefix_cap = st->prefix_cap;
+            ap.ring_cap = st->ring_cap;
+            ap.cache_cap = cache_cap;
+            ap.prefix_len = st->prefix_len;
+            ap.gen_index = st->gen_index;
+            ap.sink = nullptr;
+            ap.theta = m->rope_theta;
+            ap.scale = 1.0f / sqrtf((float)m->head_dim);
+            ap.out = w.o;
+            ap.ld_out = HD;
+            ap.n_split = attn_n_split(cache_cap);
+            ap.part = w.attn_part;
+            launch_attn(ap, s);
+        }
+        // O projection + residual
+        {
+            GemvPlan pl = plan_gemv(L.wo.fmt, H, HD, R, EPI_RESID);
+            GemvParams gp{};
+            gp.w = (const uint8_t*)L.wo.data;
+            gp.n = H;
+            gp.k = HD;
+            gp.nchunks = n_chunks(L.wo.fmt, HD);
+            gp.xs = XDirect{w.o, HD, R};
+            gp.y = w.h;
+            gp.ldy = H;
+            launch_gemv(L.wo.fmt, EPI_RESID, pl, gp, s);
+        }
+        hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(256), 0, s, w.h, L.ffn_norm, H, m->norm_eps, w.x);
+        if (L.is_moe) {
+            const int K = L.moe.top_k;
+            int32_t* ci = cap && cap->topk_idx ? cap->topk_idx + (int64_t)moe_l * R * K : nullptr;
+            float* cw = cap && cap->topk_w ? cap->topk_w + (int64_t)moe_l * R * K : nullptr;
+            const int32_t* fo = forced_topk ? forced_topk + (int64_t)moe_l * R * K : nullptr;
+            launch_moe(&L.moe, R, w.x, H, w.h, H, 1, fo, nullptr, ci, cw, w.moe, next_norm, m->norm_eps, w.x, H, s);
+            ++moe_l;
+        } else {
+            const int F = L.dense_ff;
+            {
+                GemvPlan pl = plan_gemv(L.dense_gate_up.fmt, 2 * F, H, R, EPI_GLU);
+                GemvParams gp{};
+                gp.w = (const uint8_t*)L.dense_gate_up.data;
+                gp.n = 2 * F;
+                gp.k = H;
+                gp.nchunks = n_chunks(L.dense_gate_up.fmt, H);
+                gp.xs = XDirect{w.x, H, R};
+                gp.y = w.a;
+                gp.ldy = F;
+                gp.half_tiles = F / 16;
+                launch_gemv(L.dense_gate_up.fmt, EPI_GLU, pl, gp, s);
+            }
+            {
+                GemvPlan pl = plan_gemv(L.dense_down.fmt, H, F, R, EPI_RESID);
+                GemvParams gp{};
+                gp.w = (const uint8_t*)L.dense_down.data;
+                gp.n = H;
+                gp.k = F;
+                gp.nchunks = n_chunks(L.dense_down.fmt, F);
+                gp.xs = XDirect{w.a, F, R};
+                gp.y = w.h;
+                gp.ldy = H;
+                launch_gemv(L.dense_down.fmt, EPI_RESID, pl, gp, s);
+            }
+            if (next_norm) hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(256), 0, s, w.h, next_norm, H, m->norm_eps, w.x);
+        }
+    }
+    if (hidden) {
+        const int64_t n = (int64_t)R * H;
+        hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 1024)), dim3(256), 0, s,
+                           w.h, hidden, n);
+    }
+    if (m->lm_head.data && tok_out) {
+        GemvPlan pl = plan_gemv(m->lm_head.fmt, m->vocab, H, R, EPI_ARGMAX);
+        GemvParams gp{};
+        gp.w = (const uint8_t*)m->lm_head.data;
+        gp.n = m->vocab;
+        gp.k = H;
+        gp.nchunks = n_chunks(m->lm_head.fmt, H);
+        gp.xs = XDirect{w.x, H, R};
+        gp.part = w.lm_part;
+        launch_gemv(m->lm_head.fmt, EPI_ARGMAX, pl, gp, s);
+        launch_argmax_final(w.lm_part, pl.grid, R, tok_out, cap ? cap->lm_top2 : nullptr, st->gen_index, s);
+    } else {
+        hipLaunchKernelGGL(bump_kernel, dim3(1), dim3(64), 0, s, st->gen_index, R);
+    }
+    return launch_status("ocrdec_decode_step");
+}

@@ -1,0 +1,243 @@
+"""GPU parity of the C-ABI entry points against the oracle, kernel by kernel.
+
+Every case prints its name, shape and seed before it touches the GPU.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from tests.gpu_util import NEAR_TIE, assert_close, f16_tensor, from_f16_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import torch
+    assert torch.cuda.is_available()
+    import quantized_decode_step_amd as qd
+    return qd
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+# -----------------------------------------------------------------------------
+# ocrdec_gemv_q
+# -----------------------------------------------------------------------------
+
+GEMV_CASES = [
+    # (fmt, n, k, rows)
+    (synth.F16, 40, 96, 1), (synth.Q8_0, 40, 96, 3), (synth.Q4_0, 40, 160, 5), (synth.U8A_G32, 40, 96, 2),
+    (synth.Q8_0, 3840, 1280, 1), (synth.Q8_0, 3840, 1280, 24), (synth.Q4_0, 1280, 3584, 1),
+    (synth.Q4_0, 1792, 1280, 17), (synth.Q4_0, 1280, 896, 6), (synth.F16, 16200, 1280, 1),
+    (synth.F16, 16200, 1280, 12), (synth.U8A_G32, 1536, 512, 24), (synth.U8A_G32, 512, 512, 1),
+    (synth.Q8_0, 64, 1280, 32), (synth.Q4_0, 1000, 1280, 40), (synth.F16, 1280, 1280, 33),
+]
+
+
+@pytest.mark.parametrize("fmt,n,k,rows", GEMV_CASES)
+@pytest.mark.parametrize("otype", [0, 1])
+def test_gemv_q_parity(q, fmt, n, k, rows, otype):
+    import torch
+    seed = 100 + n + k + rows
+    _say("gemv_q", synth.FMT_NAMES[fmt], n, k, rows, "otype", otype, "seed", seed)
+    m = synth.random_qmat(fmt, synth.stream_id(seed, "W"), n, k, 0.02)
+    x = synth.normal_f16(synth.stream_id(seed, "x"), (rows, k))
+    dm = q.DeviceQMat(m)
+    xd = f16_tensor(x)
+    if otype == 0:
+        y = torch.full((rows, n), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        y = torch.full((rows, n), -1, dtype=torch.int16, device="cuda")
+    q.ocrdec_gemv_q(dm.desc, rows, xd, k, y, otype, n)
+    torch.cuda.synchronize()
+    ref = O.gemv_qmat(m, x.astype(np.float64))
+    got = y.cpu().numpy().astype(np.float64) if otype == 0 else from_f16_tensor(y)
+    if otype == 1:
+        ref = O.f16(ref)
+    assert_close(got, ref, "gemv %s %dx%d rows=%d" % (synth.FMT_NAMES[fmt], n, k, rows))
+
+
+def test_gemv_q_rejects_bad_args(q):
+    import torch
+    m = synth.random_qmat(synth.Q8_0, 1, 32, 64)
+    dm = q.DeviceQMat(m)
+    x = torch.zeros((2, 64), dtype=torch.int16, device="cuda")
+    y = torch.zeros((2, 32), dtype=torch.float32, device="cuda")
+    with pytest.raises(q.OcrdecError):
+        q.ocrdec_gemv_q(dm.desc, 0, x, 64, y, 0, 32)
+    with pytest.raises(q.OcrdecError):
+        q.ocrdec_gemv_q(dm.desc, 2, x, 60, y, 0, 32)
+    bad = q.QMatDesc(dm.desc.fmt, 32, 48, dm.desc.data)
+    with pytest.raises(q.OcrdecError):
+        q.ocrdec_gemv_q(bad, 2, x, 64, y, 0, 32)
+
+
+# -----------------------------------------------------------------------------
+# ocrdec_attn_decode
+# -----------------------------------------------------------------------------
+
+def _attn_case(q, rows, NH, D, prefix_cap, ring_cap, prefix_len, gen_index, sink, seed, fill="zero"):
+    import torch
+    cap = prefix_cap + ring_cap
+    rng = np.random.default_rng(seed)
+    qkv = rng.standard_normal((rows, 3 * NH * D)) * 0.7
+    qkv = qkv.astype(np.float32)
+    kc = synth.normal_f16(synth.stream_id(seed, "kc"), (rows, NH, cap, D))
+    vc = synth.normal_f16(synth.stream_id(seed, "vc"), (rows, NH, cap, D))
+    for r in range(rows):
+        valid = np.zeros(cap, bool)
+        if ring_cap:
+            valid[:prefix_len[r]] = True
+            valid[prefix_cap:prefix_cap + min(gen_index[r], ring_cap)] = True
+        else:
+            valid[:prefix_len[r]] = True
+        pad = np.float16(np.nan) if fill == "nan" else np.float16(0)
+        kc[r][:, ~valid] = pad
+        vc[r][:, ~valid] = pad
+        if sink is not None:
+            kc[r][:, 0] = 0
+            vc[r][:, 0] = 0
+    kd, vd = f16_tensor(kc), f16_tensor(vc)
+    qkv_d = torch.from_numpy(qkv).cuda()
+    pl = torch.tensor(prefix_len, dtype=torch.int32, device="cuda")
+    gi = torch.tensor(gen_index, dtype=torch.int32, device="cuda")
+    sk = torch.tensor(np.asarray(sink, np.float32), device="cuda") if sink is not None else None
+    out = torch.full((rows, NH * D), -1, dtype=torch.int16, device="cuda")
+    a = q.AttnArgs(rows, NH, D, qkv_d.data_ptr(), 3 * NH * D, kd.data_ptr(), vd.data_ptr(), prefix_cap, ring_cap,
+                   pl.data_ptr(), gi.data_ptr(), sk.data_ptr() if sk is not None else None, 10000.0,
+                   float(1 / np.sqrt(D)), out.data_ptr(), NH * D)
+    wsb = q.ocrdec_attn_workspace_bytes(a)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    q.ocrdec_attn_decode(a, ws, wsb)
+    torch.cuda.synchronize()
+    got = from_f16_tensor(out)
+    kc_after = kd.cpu().numpy().view(np.float16)
+    vc_after = vd.cpu().numpy().view(np.float16)
+    # oracle
+    for r in range(rows):
+        qq = qkv[r, :NH * D].reshape(NH, D).astype(np.float64)
+        kk = qkv[r, NH * D:2 * NH * D].reshape(NH, D).astype(np.float64)
+        vv = qkv[r, 2 * NH * D:].reshape(NH, D).astype(np.float64)
+        kcr, vcr = kc[r].copy(), vc[r].copy()
+        if ring_cap:
+            t = gen_index[r]
+            pos = prefix_len[r] + t
+            slot = prefix_cap + O.ring_slot(t, ring_cap)
+            idx = O.window(prefix_len[r], prefix_cap, t, ring_cap)
+        else:
+            pos = prefix_len[r] - (1 if sink is not None else 0)
+            slot = prefix_len[r]
+            idx = np.arange(prefix_len[r] + 1)
+        qr = O.f16(O.rope(qq, pos, 10000.0))
+        kr = O.f16(O.rope(kk, pos, 10000.0))
+        vr = O.f16(vv)
+        kcr[:, slot] = kr
+        vcr[:, slot] = vr
+        ref = np.zeros((NH, D))
+        for h in range(NH):
+            if sink is not None:
+                ref[h] = O.attention(qr[h], kcr[h, idx], vcr[h, idx], 1 / np.sqrt(D), sink=float(sink[h]),
+                                     sink_index=0)
+            else:
+                ref[h] = O.attention(qr[h], kcr[h, idx], vcr[h, idx], 1 / np.sqrt(D))
+        assert_close(got[r], O.f16(ref.reshape(-1)), "attn out row %d" % r)
+        assert_close(kc_after[r][:, slot].astype(np.float64), kr, "new k row %d" % r)
+        assert np.array_equal(vc_after[r][:, slot].astype(np.float64), vr), "new v row %d" % r
+        # nothing else in the cache changed
+        mask = np.ones(kc.shape[2], bool)
+        mask[slot] = False
+        assert np.array_equal(kc_after[r][:, mask].view(np.uint16), kc[r][:, mask].view(np.uint16))
+
+
+@pytest.mark.parametrize("rows,prefix_len,gen_index", [
+    (1, [1100], [128]), (1, [256], [0]), (3, [1100, 0, 37], [5, 300, 127]), (24, [1100] * 24, list(range(100, 124))),
+])
+def test_attn_ring_parity(q, rows, prefix_len, gen_index):
+    _say("attn ring", rows, prefix_len[:3], gen_index[:3])
+    _attn_case(q, rows, 10, 128, 1100, 128, prefix_len, gen_index, None, 7 + rows, fill="nan")
+
+
+@pytest.mark.parametrize("rows,L", [(1, 350), (6, 350), (2, 3000), (24, 3000)])
+def test_attn_sink_linear_parity(q, rows, L):
+    _say("attn sink linear", rows, L)
+    sink = O.f16(np.random.default_rng(L + rows).standard_normal(8))
+    _attn_case(q, rows, 8, 64, L + 1, 0, [L] * rows, [0] * rows, sink, 11 + rows, fill="nan")
+
+
+def test_attn_ring_small_cap_wraps(q):
+    _say("attn ring small cap")
+    _attn_case(q, 4, 2, 128, 70, 4, [0, 70, 3, 64], [0, 3, 4, 9], None, 5, fill="nan")
+
+
+# -----------------------------------------------------------------------------
+# ocrdec_moe_layer
+# -----------------------------------------------------------------------------
+
+class _Lay:
+    pass
+
+
+def _moe_case(q, rows, seed, H=1280, E=64, K=6, S=2, F=896, fmt=synth.Q8_0, bias=False, residual=True):
+    import torch
+    d = synth.Dims(hidden=H, n_experts=E, top_k=K, n_shared=S, expert_ff=F, fmt_router=synth.Q8_0,
+                   fmt_expert=fmt, fmt_shared=fmt)
+    lay = _Lay()
+    for k_, v_ in synth.make_moe_weights(d, seed, 0, with_bias=bias).items():
+        setattr(lay, k_, v_)
+    if not bias:
+        lay.router_bias = None
+    x = synth.normal_f16(synth.stream_id(seed, "x"), (rows, H))
+    h = synth.normal_f16(synth.stream_id(seed, "h"), (rows, H))
+    w, keep = q.moe_weights(lay, H, K)
+    xd, hd = f16_tensor(x), f16_tensor(h)
+    cap_idx = torch.full((rows, K), -1, dtype=torch.int32, device="cuda")
+    cap_w = torch.zeros((rows, K), dtype=torch.float32, device="cuda")
+    counts = torch.zeros(E, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.zeros(rows * K, dtype=torch.int32, device="cuda")
+    cap = q.MoeCapture(cap_idx.data_ptr(), cap_w.data_ptr(), counts.data_ptr(), offsets.data_ptr(), perm.data_ptr())
+    wsb = q.ocrdec_moe_workspace_bytes(w, rows)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    q.ocrdec_moe_layer(w, rows, xd, hd, residual, None, cap, ws, wsb)
+    torch.cuda.synchronize()
+    out, idx, wt, logits = O.moe(lay, x.astype(np.float64), K)
+    g_idx = cap_idx.cpu().numpy()
+    # routing: bit-exact except logged near-ties
+    ties = []
+    for r in range(rows):
+        if not np.array_equal(g_idx[r], idx[r]):
+            gap = O.topk_gap(logits[r], K, lay.router_bias)
+            assert gap < NEAR_TIE, "row %d routing differs with oracle gap %.3g" % (r, gap)
+            ties.append(r)
+    keep_rows = [r for r in range(rows) if r not in ties]
+    if ties:
+        print("[near-tie] routing rows", ties)
+    assert_close(cap_w.cpu().numpy()[keep_rows], wt[keep_rows], "topk weights")
+    if not ties:
+        c, o, p, _ = O.group(idx, E)
+        assert np.array_equal(counts.cpu().numpy(), c)
+        assert np.array_equal(offsets.cpu().numpy(), o)
+        assert np.array_equal(perm.cpu().numpy(), p)
+    ref = O.f16(h + out) if residual else O.f16(out)
+    got = from_f16_tensor(hd)
+    assert_close(got[keep_rows], ref[keep_rows], "moe out")
+
+
+@pytest.mark.parametrize("rows", [1, 6, 24])
+def test_moe_q8_parity(q, rows):
+    _say("moe q8", rows)
+    _moe_case(q, rows, 1002 + rows)
+
+
+def test_moe_q4_small_parity(q):
+    _say("moe q4 small")
+    _moe_case(q, 7, 77, H=256, E=16, K=4, S=1, F=128, fmt=synth.Q4_0)
+
+
+def test_moe_prefill_bias_parity(q):
+    _say("moe prefill-shaped 300 rows with bias")
+    _moe_case(q, 300, 1005, H=1280, E=64, K=6, S=2, F=896, fmt=synth.Q4_0, bias=True, residual=False)

@@ -1,0 +1,173 @@
+"""GPU parity of ocrdec_decode_step against the oracle over several steps.
+
+Protocol (teacher forcing): every step feeds both sides the oracle's tokens and
+gives the GPU the oracle's routing as forced experts, while the GPU still
+reports the experts it would have chosen itself.  Its own choices and its
+argmax tokens must equal the oracle's bit for bit, except where the oracle's
+own logit gap is below the near-tie threshold (such cases are printed).  All
+floating-point state (the final hidden state, every new cache slot, the routing
+weights) is compared at every step.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from tests.gpu_util import NEAR_TIE, assert_close, f16_tensor, from_f16_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import torch
+    assert torch.cuda.is_available()
+    import quantized_decode_step_amd as qd
+    return qd
+
+
+def small_dims(**kw):
+    d = synth.Dims(hidden=256, n_heads=2, head_dim=128, n_layers=3, n_dense=1, dense_ff=512, n_experts=16, top_k=6,
+                   n_shared=2, expert_ff=128, vocab=1000, prefix_cap=40, ring_cap=8)
+    for k_, v_ in kw.items():
+        setattr(d, k_, v_)
+    return d
+
+
+def run_steps(q, d, seed, prefix_len, gen_index, n_steps, forced=True, sample_rows=None, check_cache=True):
+    import torch
+    R = len(prefix_len)
+    print("[case] step", d.n_layers, "layers", "H", d.hidden, "V", d.vocab, "R", R, "steps", n_steps, "seed", seed,
+          flush=True)
+    model = synth.make_model(d, seed)
+    st = synth.make_state(d, seed, prefix_len, gen_index)
+    dm = q.DeviceModel(model)
+    ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+    dm.bind_caches(ds.k_cache, ds.v_cache)
+    wsb = q.ocrdec_step_workspace_bytes(dm.desc, ds.desc)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    n_moe = sum(1 for l in model.layers if l.is_moe)
+    K = d.top_k
+    cap_idx = torch.zeros((max(n_moe, 1), R, K), dtype=torch.int32, device="cuda")
+    cap_w = torch.zeros((max(n_moe, 1), R, K), dtype=torch.float32, device="cuda")
+    top2 = torch.zeros((R, 2), dtype=torch.float32, device="cuda")
+    cap = q.StepCapture(cap_idx.data_ptr(), cap_w.data_ptr(), top2.data_ptr())
+    hidden = torch.zeros((R, d.hidden), dtype=torch.int16, device="cuda")
+    tok_out = torch.full((R,), -1, dtype=torch.int32, device="cuda")
+    rows = list(range(R)) if sample_rows is None else list(sample_rows)
+    tok = synth.first_tokens(d, seed, R)
+    ost = st.copy()
+    ties = []
+    for step in range(n_steps):
+        res = O.decode_step(model, ost, tok_in=tok, rows=rows)
+        tok_in = torch.from_numpy(tok.astype(np.int32)).cuda()
+        forced_t = None
+        if forced and n_moe:
+            f = np.full((n_moe, R, K), -1, np.int32)
+            for ml in range(n_moe):
+                f[ml, rows] = res.topk_idx[ml]
+            forced_t = torch.from_numpy(f).cuda()
+        q.ocrdec_decode_step(dm.desc, ds.desc, tok_in, hidden, tok_out, forced_t, cap, ws, wsb)
+        torch.cuda.synchronize()
+        g_tok = tok_out.cpu().numpy()[rows]
+        g_hid = from_f16_tensor(hidden)[rows]
+        g_idx = cap_idx.cpu().numpy()[:, rows]
+        g_w = cap_w.cpu().numpy()[:, rows]
+        # routing decisions
+        for ml in range(n_moe):
+            for i, r in enumerate(rows):
+                if not np.array_equal(g_idx[ml, i], res.topk_idx[ml][i]):
+                    gap = res.router_gap[ml][i]
+                    assert gap < NEAR_TIE, "step %d layer %d row %d: routing differs, oracle gap %.3g" % (
+                        step, ml, r, gap)
+                    ties.append(("route", step, ml, r, gap))
+            assert_close(g_w[ml], res.topk_w[ml], "step %d moe layer %d weights" % (step, ml))
+        # tokens
+        for i, r in enumerate(rows):
+            if g_tok[i] != res.tok[i]:
+                gap = res.lm_top2[i, 0] - res.lm_top2[i, 1]
+                assert gap < NEAR_TIE, "step %d row %d: token %d vs oracle %d, oracle gap %.3g" % (
+                    step, r, g_tok[i], res.tok[i], gap)
+                ties.append(("token", step, r, gap))
+        assert_close(g_hid, res.hidden, "step %d hidden" % step)
+        if check_cache:
+            kc = ds.k_cache.cpu().numpy().view(np.float16)
+            vc = ds.v_cache.cpu().numpy().view(np.float16)
+            for l in range(d.n_layers):
+                for i, r in enumerate(rows):
+                    t = int(st.gen_index[r]) + step
+                    slot = d.prefix_cap + t % d.ring_cap
+                    assert_close(kc[l, r, :, slot].astype(np.float64), res.new_k[l][i], "step %d layer %d k" % (step, l))
+                    assert_close(vc[l, r, :, slot].astype(np.float64), res.new_v[l][i], "step %d layer %d v" % (step, l))
+        gi = ds.gen_index.cpu().numpy()
+        assert np.array_equal(gi[rows], ost.gen_index[rows])
+        nxt = tok.copy()
+        nxt[rows] = res.tok
+        tok = nxt
+    if ties:
+        print("[near-tie]", ties, flush=True)
+    return ties
+
+
+def test_step_small_forced_ragged(q):
+    d = small_dims()
+    run_steps(q, d, 501, prefix_len=[40, 0, 17, 33, 1], gen_index=[0, 5, 7, 20, 3], n_steps=12)
+
+
+def test_step_small_unforced(q):
+    d = small_dims()
+    run_steps(q, d, 502, prefix_len=[12, 40], gen_index=[6, 0], n_steps=10, forced=False)
+
+
+def test_step_small_rows_32(q):
+    d = small_dims(n_layers=2)
+    run_steps(q, d, 503, prefix_len=[(7 * i) % 41 for i in range(32)], gen_index=[3 * i for i in range(32)],
+              n_steps=3)
+
+
+def test_step_single_dense_layer_fp16(q):
+    """One dense fp16 decoder layer over 256 cached positions (no embedding or
+    LM head: the hidden state goes in and comes out)."""
+    import torch
+    d = synth.dims_dense_layer()
+    seed = 1001
+    print("[case] dense fp16 layer", flush=True)
+    model = synth.make_model(d, seed, with_embed=False, with_lm=False)
+    st = synth.make_state(d, seed, [256], [0])
+    h0 = synth.normal_f16(synth.stream_id(seed, "h0"), (1, d.hidden))
+    dm = q.DeviceModel(model)
+    ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+    dm.bind_caches(ds.k_cache, ds.v_cache)
+    wsb = q.ocrdec_step_workspace_bytes(dm.desc, ds.desc)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    hidden = f16_tensor(h0)
+    q.ocrdec_decode_step(dm.desc, ds.desc, None, hidden, None, None, None, ws, wsb)
+    torch.cuda.synchronize()
+    res = O.decode_step(model, st.copy(), hidden_in=h0.astype(np.float64), with_lm=False)
+    assert_close(from_f16_tensor(hidden), res.hidden, "dense layer hidden")
+
+
+def test_step_single_moe_layer_q8(q):
+    """One Q8_0 MoE decoder layer, prefix 1100 + a full ring (t = 128)."""
+    import torch
+    d = synth.dims_moe_layer()
+    seed = 1002
+    print("[case] moe q8 layer", flush=True)
+    model = synth.make_model(d, seed, with_embed=False, with_lm=False)
+    st = synth.make_state(d, seed, [1100], [128])
+    h0 = synth.normal_f16(synth.stream_id(seed, "h0"), (1, d.hidden))
+    dm = q.DeviceModel(model)
+    ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+    dm.bind_caches(ds.k_cache, ds.v_cache)
+    wsb = q.ocrdec_step_workspace_bytes(dm.desc, ds.desc)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    hidden = f16_tensor(h0)
+    cap_idx = torch.zeros((1, 1, d.top_k), dtype=torch.int32, device="cuda")
+    cap = q.StepCapture(cap_idx.data_ptr(), None, None)
+    q.ocrdec_decode_step(dm.desc, ds.desc, None, hidden, None, None, cap, ws, wsb)
+    torch.cuda.synchronize()
+    res = O.decode_step(model, st.copy(), hidden_in=h0.astype(np.float64), with_lm=False)
+    if not np.array_equal(cap_idx.cpu().numpy()[0, 0], res.topk_idx[0][0]):
+        assert res.router_gap[0][0] < NEAR_TIE
+        pytest.skip("near-tie routing for this seed")
+    assert_close(from_f16_tensor(hidden), res.hidden, "moe layer hidden")
