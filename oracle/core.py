@@ -5,11 +5,18 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 Numeric conventions (shared by every function below):
 
 * Arithmetic is float64.  Values the decode step stores as fp16 are rounded to
-  IEEE binary16 with round-to-nearest-even at exactly these points: the
-  residual stream ``h``; ``x`` after each RMSNorm; q, k, v after RoPE; the
-  attention output; the SwiGLU intermediate.  [UOCR] "Il decoder e il Mixture
-  of Experts": the decode loop keeps activations in fp16.  The residual being
-  fp16 too is our reading (the page names no other precision for it).
+  IEEE binary16 with round-to-nearest-even at exactly these points: ``x``
+  after each RMSNorm (the input of every projection); q, k, v after RoPE (k
+  and v are what the cache holds); the attention output; the SwiGLU
+  intermediate.  [UOCR] "Il decoder e il Mixture of Experts": the decode loop
+  keeps activations in fp16.
+* The residual stream ``h`` is not rounded to fp16 (the GPU keeps it in fp32).
+  Reading: the fp16 activations are the tensors the projections and the cache
+  consume; the running sum between blocks is kept wide, as [NCNN] 3.1 does
+  with its FP32 residual between blocks to avoid the error that repeated
+  low-precision round trips accumulate.  With an fp16 residual every layer
+  adds one-ulp rounding disagreements that no implementation can keep under
+  the comparison tolerance.
 * Expert outputs, the MoE combine, router logits and LM-head logits are not
   rounded to fp16.  Where floating point decides an integer (top-k routing,
   the LM-head argmax) the decision is taken on logits rounded to float32, the
@@ -392,7 +399,7 @@ def window(prefix_len: int, prefix_cap: int, t: int, ring_cap: int) -> np.ndarra
 class StepResult:
     def __init__(self):
         self.tok = None            # int32 [R] (or None without LM head)
-        self.hidden = None         # float64 [R][H] residual after the last layer (fp16 values)
+        self.hidden = None         # float64 [R][H] residual after the last layer
         self.final_x = None        # float64 [R][H] normalised input of the LM head (fp16 values)
         self.lm_top2 = None        # float64 [R][2] best and second logits (float32 values)
         self.topk_idx = []         # per MoE layer: int32 [R][k]
@@ -430,7 +437,7 @@ def attention_block(lay, dims, h, kc, vc, prefix_len, t, res: StepResult | None 
     for hh in range(NH):
         o[hh] = attention(q[hh], kc[hh, idx], vc[hh, idx], 1.0 / np.sqrt(D))
     o = f16(o.reshape(-1))
-    h = f16(h + gemv_qmat(lay.wo, o[None])[0])
+    h = h + gemv_qmat(lay.wo, o[None])[0]
     if res is not None:
         res.new_k[-1].append(k)
         res.new_v[-1].append(v)
@@ -442,7 +449,7 @@ def dense_mlp_block(lay, dims, h):
     """h + W_d fp16(silu(W_g x) * W_u x) with x the pre-FFN RMSNorm of h.
     [UOCR] "Il decoder e il Mixture of Experts": layer 0 uses a dense MLP."""
     x = f16(rmsnorm(h, lay.ffn_norm, dims.norm_eps))
-    return f16(h + swiglu(lay.dense_gate_up, lay.dense_down, x[None])[0])
+    return h + swiglu(lay.dense_gate_up, lay.dense_down, x[None])[0]
 
 
 def decode_step(model, state, tok_in=None, hidden_in=None, forced_topk=None,
@@ -466,9 +473,9 @@ def decode_step(model, state, tok_in=None, hidden_in=None, forced_topk=None,
     rows = list(range(R)) if rows is None else list(rows)
     res = StepResult()
     if tok_in is not None:
-        h = f16(model.embed[np.asarray(tok_in)[rows]].astype(np.float64))
+        h = model.embed[np.asarray(tok_in)[rows]].astype(np.float64)
     else:
-        h = f16(np.asarray(hidden_in, np.float64)[rows])
+        h = f32(np.asarray(hidden_in, np.float64)[rows])
     moe_l = 0
     for l, lay in enumerate(model.layers):
         res.new_k.append([])
@@ -484,7 +491,7 @@ def decode_step(model, state, tok_in=None, hidden_in=None, forced_topk=None,
             x = f16(rmsnorm(h, lay.ffn_norm, dims.norm_eps))
             forced = None if forced_topk is None else np.asarray(forced_topk[moe_l])[rows]
             out, idx, w, logits = moe(lay, x, dims.top_k, forced)
-            h = f16(h + out)
+            h = h + out
             res.topk_idx.append(idx)
             res.topk_w.append(w)
             res.router_logits.append(logits)

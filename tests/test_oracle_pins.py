@@ -498,8 +498,9 @@ def test_step_single_key_value_path():
     """Empty prefix and t = 0: the window holds only the new token, so the
     attention output is the new value.  With W_o = identity (Q8_0, d = 1),
     v-rows = 2 * identity and q/k rows zero, the attention block returns
-    fp16(h + fp16(2 * x)) where x = fp16(rmsnorm(h)); this pins that v is
-    the third chunk of the QKV output and that O adds into the residual."""
+    h + fp16(2 * x) where x = fp16(rmsnorm(h)) (the residual is not rounded);
+    this pins that v is the third chunk of the QKV output and that O adds into
+    the residual."""
     import synth
     d = _tiny_dims(n_layers=1, n_dense=1)
     m = synth.make_model(d, 22, with_embed=False, with_lm=False)
@@ -514,7 +515,7 @@ def test_step_single_key_value_path():
     h0 = O.f16(np.random.default_rng(13).standard_normal((1, H)))
     res = O.decode_step(m, st, hidden_in=h0, with_lm=False)
     x = O.f16(O.rmsnorm(h0[0], lay.attn_norm, d.norm_eps))
-    assert np.array_equal(res.hidden[0], O.f16(h0[0] + O.f16(2 * x)))
+    assert np.array_equal(res.hidden[0], h0[0] + O.f16(2 * x))
     assert np.array_equal(res.new_v[0][0].reshape(-1), O.f16(2 * x))
 
 
