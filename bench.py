@@ -1,0 +1,234 @@
+"""Benchmark of the OCR-decoder decode step on one MI355X.
+
+Workload: the 12-layer decoder (hidden 1280, 10 heads x 128, layer 0 dense
+SwiGLU 3584 in Q4_0, layers 1-11 MoE with 64 routed + 2 shared Q4_0 experts of
+896, top-6; attention and router Q8_0; fp16 embedding and LM head over 129280
+tokens), every row with a 1100-position prefix and a 128-slot ring that starts
+at generation index 100, so the ring wraps during a 64-step run.  All weights,
+caches and first tokens are seeded synthetic data (``synth``).
+
+A step is one ocrdec_decode_step call for all rows: embedding, 12 layers, final
+norm, LM head with fused argmax; the token feeds the next step on the device.
+
+Prints ONE JSON line: rows*steps/s of the timed steps, the roofline of the
+dominant kernel (the LM-head GEMV with fused argmax, timed with HIP events on
+its own stream), and the CPU oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+SEED = 1003
+T0 = 100
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--rows", type=int, default=1)
+    ap.add_argument("--sweep", default="6,12,24", help="extra row counts timed after the main run ('' for none)")
+    ap.add_argument("--no-graph", action="store_true", help="launch kernels directly instead of replaying a graph")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--lm-iters", type=int, default=50)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(dm, d, rows: int, distinct_experts_per_layer: float, avg_keys: float) -> float:
+    """Bytes the method must move per step: every weight matrix once, the
+    routed experts actually used, the KV window of every row and layer, and
+    the embedding rows."""
+    def nb(m):  # packed bytes minus padding are the block bytes
+        return {0: 2.0, 1: 34 / 32, 2: 18 / 32, 3: 36 / 32}[m.fmt] * m.n * m.k
+    tot = 0.0
+    H, F = d.hidden, d.expert_ff
+    per_expert = {2: 18 / 32, 1: 34 / 32, 0: 2.0, 3: 36 / 32}[d.fmt_expert] * 3 * F * H
+    n_moe = 0
+    for lay in dm.src_layers:
+        tot += nb(lay.wqkv) + nb(lay.wo) + 2 * 2 * H  # + the two norm gains
+        if lay.is_moe:
+            n_moe += 1
+            tot += nb(lay.router) + nb(lay.sh_gate_up) + nb(lay.sh_down)
+        else:
+            tot += nb(lay.dense_gate_up) + nb(lay.dense_down)
+    tot += n_moe * distinct_experts_per_layer * per_expert
+    tot += nb(dm.src_lm) + 2 * H + rows * 2 * H
+    tot += d.n_layers * rows * 2 * d.n_heads * d.head_dim * 2 * avg_keys
+    return tot
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU: the decode step here is single-GPU (no collectives); "
+              "use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import quantized_decode_step_amd as q
+
+    assert torch.cuda.is_available(), "no GPU visible"
+    dev = torch.device("cuda:0")
+    d = synth.dims_full()
+    t_build = time.time()
+    model = synth.make_model(d, SEED)
+    dm = q.DeviceModel(model)
+    dm.src_layers = model.layers
+    dm.src_lm = model.lm_head
+    t_build = time.time() - t_build
+
+    stream = torch.cuda.Stream()
+
+    def run_rows(R: int, steps: int, warmup: int, want_sample: bool):
+        st = synth.make_state(d, SEED, [d.prefix_cap] * R, [T0] * R)
+        ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+        dm.bind_caches(ds.k_cache, ds.v_cache)
+        wsb = q.ocrdec_step_workspace_bytes(dm.desc, ds.desc)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        tok = torch.from_numpy(synth.first_tokens(d, SEED, R)).to(dev)
+        n_moe = d.n_layers - d.n_dense
+        cap_idx = torch.zeros((n_moe, R, d.top_k), dtype=torch.int32, device=dev)
+        cap = q.StepCapture(cap_idx.data_ptr(), None, None)
+        distinct = []
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                q.ocrdec_decode_step(dm.desc, ds.desc, tok, None, tok, None, cap, ws, wsb, stream=stream)
+                stream.synchronize()
+                ci = cap_idx.cpu().numpy()
+                distinct.append(np.mean([len(np.unique(ci[l])) for l in range(n_moe)]))
+            graph = None
+            if not args.no_graph:
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=stream):
+                    q.ocrdec_decode_step(dm.desc, ds.desc, tok, None, tok, None, None, ws, wsb,
+                                         stream=torch.cuda.current_stream())
+                # the capture enqueued nothing: the state is where warmup left it
+            stream.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(steps):
+                if graph is not None:
+                    graph.replay()
+                else:
+                    q.ocrdec_decode_step(dm.desc, ds.desc, tok, None, tok, None, None, ws, wsb, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gi = ds.gen_index.cpu().numpy()
+        assert np.all(gi == T0 + warmup + steps), "generation index did not advance once per step"
+        toks = tok.cpu().numpy()
+        assert np.all((toks >= 0) & (toks < d.vocab))
+        out = {"rows": R, "ms_per_step": ms, "rows_steps_per_s": R * 1000.0 / ms,
+               "distinct_experts_per_moe_layer": float(np.mean(distinct)) if distinct else None}
+        # keys each row attends, averaged over the timed steps (prefix + ring so far, incl. the new token)
+        ts = np.arange(T0 + warmup, T0 + warmup + steps)
+        avg_keys = float(np.mean(d.prefix_cap + np.minimum(ts + 1, d.ring_cap)))
+        byt = algorithmic_bytes(dm, d, R, out["distinct_experts_per_moe_layer"] or d.top_k, avg_keys)
+        out["algorithmic_MB_per_step"] = byt / 1e6
+        out["step_GBps"] = byt / (ms * 1e-3) / 1e9
+        del graph
+        return out
+
+    main_run = run_rows(args.rows, args.steps, args.warmup, True)
+    sweep = []
+    for r in [int(x) for x in args.sweep.split(",") if x.strip()]:
+        if r != args.rows:
+            sweep.append(run_rows(r, args.steps, args.warmup, False))
+
+    # ---- roofline of the dominant kernel: the LM-head GEMV with fused argmax
+    R = args.rows
+    x = torch.from_numpy(synth.normal_f16(synth.stream_id(SEED, "lm_x"), (R, d.hidden)).view(np.int16)).to(dev)
+    tok_out = torch.zeros(R, dtype=torch.int32, device=dev)
+    lm_ws_b = q.ocrdec_lm_argmax_workspace_bytes(dm.lm_head.desc, R)
+    lm_ws = torch.zeros(lm_ws_b, dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            q.ocrdec_lm_argmax(dm.lm_head.desc, R, x, tok_out, None, lm_ws, lm_ws_b, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.lm_iters):
+            q.ocrdec_lm_argmax(dm.lm_head.desc, R, x, tok_out, None, lm_ws, lm_ws_b, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    lm_us = e0.elapsed_time(e1) * 1000.0 / args.lm_iters
+    lm_bytes = d.vocab * d.hidden * 2.0 + R * d.hidden * 2.0
+    lm_gbs = lm_bytes / (lm_us * 1e-6) / 1e9
+
+    # ---- CPU oracle baseline on a bounded sample (1 row of the same workload)
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(model, d, args.cpu_seconds)
+
+    line = {
+        "metric": "decode rows*steps/s (12-layer MoE step)",
+        "value": round(main_run["rows_steps_per_s"], 2),
+        "unit": "rows*steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_run["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded weights ~N(0,0.02) quantised Q4_0/Q8_0, caches ~N(0,1))",
+        "config": {
+            "workload": "12-layer mixed-Q4_0 MoE OCR decoder decode step: %d row(s), prefix 1100 + 128-slot ring "
+                        "from t=%d, vocab 129280, tokens fed back on device" % (args.rows, T0),
+            "rows": args.rows, "layers": d.n_layers, "hidden": d.hidden, "experts": "64 routed top-6 + 2 shared",
+            "graph": not args.no_graph,
+        },
+        "step_hbm": {"algorithmic_MB_per_step": round(main_run["algorithmic_MB_per_step"], 1),
+                     "achieved_GBps": round(main_run["step_GBps"], 1),
+                     "frac": round(main_run["step_GBps"] / HBM_PEAK_GBS, 4),
+                     "distinct_experts_per_moe_layer": main_run["distinct_experts_per_moe_layer"]},
+        "rows_sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in sweep],
+        "roofline": {"kernel": "gemv_kernel<F16,4,1,1,ARGMAX> (LM head %dx%d + fused argmax, %d row(s))"
+                               % (d.vocab, d.hidden, R),
+                     "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_us": round(lm_us, 2), "algorithmic_bytes": lm_bytes},
+        "cpu_baseline": cpu,
+        "setup_s": round(t_build, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(model, d, budget_s: float):
+    """The oracle, as it stands, on one row of the same workload: as many whole
+    steps as fit in the budget (at least one)."""
+    import synth
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    st = synth.make_state(d, SEED, [d.prefix_cap], [T0])
+    tok = synth.first_tokens(d, SEED, 1)
+    steps = 0
+    t0 = time.time()
+    while True:
+        res = O.decode_step(model, st, tok_in=tok)
+        tok = res.tok
+        steps += 1
+        if time.time() - t0 >= budget_s:
+            break
+    el = time.time() - t0
+    return {"value": round(steps / el, 4), "unit": "rows*steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": "%d step(s) of 1 row of the same 12-layer workload (prefix 1100, ring from t=%d), "
+                      "numpy float64, %.1f s" % (steps, T0, el)}
+
+
+if __name__ == "__main__":
+    main()

@@ -120,6 +120,24 @@ typedef enum { OCRDEC_OUT_F32 = 0, OCRDEC_OUT_F16 = 1 } ocrdec_otype;
 ocrdec_status ocrdec_gemv_q(const ocrdec_qmat* W, int32_t rows, const uint16_t* x, int64_t ldx,
                             void* y, int32_t y_type, int64_t ldy, void* stream);
 
+/* Language-head argmax (Unlimited-OCR page, "Il decoder e il Mixture of
+ * Experts": the decode loop ends with an argmax over the language head; the
+ * "Quantizzazione" section fuses it with the dequantising GEMV):
+ *   tok_out[r] = argmax_v sum_k W[v][k] x[r][k], ties to the lowest v,
+ * with the logits kept on chip (never written to memory).
+ *   x        fp16 [rows][W->k], already normalised
+ *   tok_out  int32 [rows]
+ *   top2     fp32 [rows][2] (best and second-best logit) or NULL
+ *   rows     1 .. 32
+ * Workspace: ocrdec_lm_argmax_workspace_bytes; it must be zero-filled before
+ * its first use, and every call leaves it zero-filled again (its last word
+ * counts the workgroups that have finished, so that the last one can merge
+ * their partial results without a second launch).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE. */
+ocrdec_status ocrdec_lm_argmax_workspace_bytes(const ocrdec_qmat* W, int32_t rows, size_t* bytes);
+ocrdec_status ocrdec_lm_argmax(const ocrdec_qmat* W, int32_t rows, const uint16_t* x, int32_t* tok_out,
+                               float* top2, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* ocrdec_attn_decode: single-query attention over a prefix + ring KV cache  */
 /* ------------------------------------------------------------------------ */
@@ -281,14 +299,19 @@ typedef struct {
 /* One decode step (Unlimited-OCR page, "Il decoder e il Mixture of Experts"):
  * h = embed[tok_in] (or `hidden` if tok_in is NULL); for each layer:
  *   x = fp16(RMSNorm(h) * attn_norm); qkv = Wqkv x; attention as in
- *   ocrdec_attn_decode (ring mode, scale 1/sqrt(head_dim)); h = fp16(h + Wo o);
- *   x = fp16(RMSNorm(h) * ffn_norm); h = fp16(h + MLP(x)) with MLP the dense
- *   SwiGLU or the MoE of ocrdec_moe_layer;
+ *   ocrdec_attn_decode (ring mode, scale 1/sqrt(head_dim)); h += Wo o;
+ *   x = fp16(RMSNorm(h) * ffn_norm); h += MLP(x) with MLP the dense SwiGLU or
+ *   the MoE of ocrdec_moe_layer;
  * then `hidden` (if non-NULL) receives h, and if the model has an LM head and
  * tok_out is non-NULL: tok_out[r] = argmax_v (W_lm . fp16(RMSNorm(h) *
  * final_norm))[v], ties to the lowest v, logits never leave the chip.
- * Finally gen_index[r] += 1.  tok_out may alias tok_in (the step reads tok_in
- * before it writes tok_out), so a caller can feed tokens back on the device.
+ * Finally gen_index[r] += 1.  The residual h is kept in fp32 between blocks
+ * (the fp16 activations are the projection inputs, the cache and the SwiGLU
+ * intermediate; the HunyuanOCR ncnn page, section 3.1, keeps an FP32 residual
+ * between blocks for the same reason: no accumulation of low-precision round
+ * trips).  tok_out may alias tok_in (the step reads tok_in before it writes
+ * tok_out), so a caller can feed tokens back on the device.
+ *   hidden       fp32 [rows][hidden]: input if tok_in is NULL; output if non-NULL
  *   forced_topk  int32 [n_moe_layers][rows][top_k] or NULL (see ocrdec_moe_layer)
  *   rows         1 .. 32; prefix_cap + ring_cap <= 65536
  * Workspace: ocrdec_step_workspace_bytes(m, st) bytes (it depends on rows and
@@ -296,7 +319,7 @@ typedef struct {
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE. */
 ocrdec_status ocrdec_step_workspace_bytes(const ocrdec_model* m, const ocrdec_state* st, size_t* bytes);
 ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_state* st, const int32_t* tok_in,
-                                 uint16_t* hidden, int32_t* tok_out, const int32_t* forced_topk,
+                                 float* hidden, int32_t* tok_out, const int32_t* forced_topk,
                                  const ocrdec_step_capture* capture, void* ws, size_t ws_bytes,
                                  void* stream);
 

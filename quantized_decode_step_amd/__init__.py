@@ -4,7 +4,7 @@ decoder on MI355X / gfx950).
 This module only marshals arguments: every step of the decode path runs in the
 HIP kernels of ``libocrdec.so``.  PyTorch supplies device memory and streams.
 Importing the module fails loudly if the library has not been built
-(``python -m quantized_decode_step_amd.build``); there is no fallback.
+(``python quantized_decode_step_amd/build.py``); there is no fallback.
 """
 from __future__ import annotations
 
@@ -21,7 +21,7 @@ OCRDEC_F16, OCRDEC_Q8_0, OCRDEC_Q4_0, OCRDEC_U8A_G32 = range(4)
 OCRDEC_OUT_F32, OCRDEC_OUT_F16 = 0, 1
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libocrdec.so is not built: run `python -m quantized_decode_step_amd.build` "
+    raise ImportError("libocrdec.so is not built: run `python quantized_decode_step_amd/build.py` "
                       "(hipcc --offload-arch=gfx950)")
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -91,19 +91,23 @@ _lib.ocrdec_packed_bytes.argtypes = [_i32, _i32, _i32, _P(_sz)]
 _lib.ocrdec_pack.argtypes = [_i32, _i32, _i32, _vp, _vp]
 _lib.ocrdec_unpack.argtypes = [_i32, _i32, _i32, _vp, _vp]
 _lib.ocrdec_gemv_q.argtypes = [_P(QMatDesc), _i32, _vp, _i64, _vp, _i32, _i64, _vp]
+_lib.ocrdec_lm_argmax_workspace_bytes.argtypes = [_P(QMatDesc), _i32, _P(_sz)]
+_lib.ocrdec_lm_argmax.argtypes = [_P(QMatDesc), _i32, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.ocrdec_attn_workspace_bytes.argtypes = [_P(AttnArgs), _P(_sz)]
 _lib.ocrdec_attn_decode.argtypes = [_P(AttnArgs), _vp, _sz, _vp]
 _lib.ocrdec_moe_workspace_bytes.argtypes = [_P(MoeWeights), _i32, _P(_sz)]
 _lib.ocrdec_moe_layer.argtypes = [_P(MoeWeights), _i32, _vp, _vp, _i32, _vp, _P(MoeCapture), _vp, _sz, _vp]
 _lib.ocrdec_step_workspace_bytes.argtypes = [_P(ModelDesc), _P(StateDesc), _P(_sz)]
 _lib.ocrdec_decode_step.argtypes = [_P(ModelDesc), _P(StateDesc), _vp, _vp, _vp, _vp, _P(StepCapture), _vp, _sz, _vp]
-for _fn in ("ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack", "ocrdec_gemv_q", "ocrdec_attn_workspace_bytes",
+for _fn in ("ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack", "ocrdec_gemv_q", "ocrdec_lm_argmax_workspace_bytes",
+            "ocrdec_lm_argmax", "ocrdec_attn_workspace_bytes",
             "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes", "ocrdec_moe_layer", "ocrdec_step_workspace_bytes",
             "ocrdec_decode_step"):
     getattr(_lib, _fn).restype = ctypes.c_int
 
 EXPORTED = ["ocrdec_last_error", "ocrdec_version", "ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack",
-            "ocrdec_gemv_q", "ocrdec_attn_workspace_bytes", "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes",
+            "ocrdec_gemv_q", "ocrdec_lm_argmax_workspace_bytes", "ocrdec_lm_argmax", "ocrdec_attn_workspace_bytes",
+            "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes",
             "ocrdec_moe_layer", "ocrdec_step_workspace_bytes", "ocrdec_decode_step"]
 
 
@@ -157,6 +161,17 @@ def ocrdec_unpack(fmt: int, n: int, k: int, packed: np.ndarray, canonical_bytes:
 
 def ocrdec_gemv_q(W: QMatDesc, rows: int, x, ldx: int, y, y_type: int, ldy: int, stream=None):
     _check(_lib.ocrdec_gemv_q(ctypes.byref(W), rows, _ptr(x), ldx, _ptr(y), y_type, ldy, _stream(stream)))
+
+
+def ocrdec_lm_argmax_workspace_bytes(W: QMatDesc, rows: int) -> int:
+    b = _sz()
+    _check(_lib.ocrdec_lm_argmax_workspace_bytes(ctypes.byref(W), rows, ctypes.byref(b)))
+    return b.value
+
+
+def ocrdec_lm_argmax(W: QMatDesc, rows: int, x, tok_out, top2=None, ws=None, ws_bytes: int = 0, stream=None):
+    _check(_lib.ocrdec_lm_argmax(ctypes.byref(W), rows, _ptr(x), _ptr(tok_out), _ptr(top2), _ptr(ws), ws_bytes,
+                                 _stream(stream)))
 
 
 def ocrdec_attn_workspace_bytes(a: AttnArgs) -> int:

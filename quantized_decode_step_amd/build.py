@@ -1,6 +1,7 @@
 """Builds libocrdec.so for gfx950 with hipcc (in-tree, next to this file).
 
-Usage: python -m quantized_decode_step_amd.build [--jobs N]
+Usage: python quantized_decode_step_amd/build.py [--jobs N]
+(run by path: importing the package needs the library this script builds)
 """
 from __future__ import annotations
 

@@ -5,6 +5,35 @@
 
 namespace ocrdec {
 
+// Last-arriving workgroup of an argmax launch: merges every workgroup's
+// (best, index, second) per token in workgroup order, writes the tokens, and
+// resets the arrival counter for the next launch.
+OCR_DEV void argmax_finish(const GemvParams& p) {
+    __shared__ int is_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) is_last = (atomicAdd(p.counter, 1) == (int)gridDim.x - 1);
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+    for (int r = threadIdx.x; r < p.xs.rows; r += blockDim.x) {
+        float b = -INFINITY, s = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int w = 0; w < (int)gridDim.x; ++w) {
+            const float* e = p.part + ((int64_t)w * p.xs.rows + r) * 3;
+            argmax_merge(b, bi, s, __builtin_nontemporal_load(e), __float_as_int(__builtin_nontemporal_load(e + 1)),
+                         __builtin_nontemporal_load(e + 2));
+        }
+        if (p.tok_out) p.tok_out[r] = (bi == 0x7fffffff) ? 0 : bi;
+        if (p.top2) {
+            p.top2[2 * r] = b;
+            p.top2[2 * r + 1] = s;
+        }
+        if (p.gen_index) p.gen_index[r] += 1;
+    }
+    if (threadIdx.x == 0) *p.counter = 0;
+}
+
 template <int FMT, int NT, int XT, int KS, int EPI>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
     constexpr int CB = Geom<FMT>::CB;
@@ -114,6 +143,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
                     out[2] = s;
                 }
             }
+            if (tok0 + 16 * XT >= p.xs.rows) argmax_finish(p);
         } else if (owner) {
 #pragma unroll
             for (int xt = 0; xt < XT; ++xt)
@@ -138,8 +168,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
                             } else if constexpr (EPI == EPI_F16) {
                                 ((uint16_t*)p.y)[o] = f2h(acc[i][xt][v]);
                             } else if constexpr (EPI == EPI_RESID) {
-                                uint16_t* h = (uint16_t*)p.y;
-                                h[o] = f2h(h2f(h[o]) + acc[i][xt][v]);
+                                float* h = (float*)p.y;
+                                h[o] = h[o] + acc[i][xt][v];
                             }
                         }
                     }
@@ -219,30 +249,7 @@ void launch_gemv(int fmt, int epi, const GemvPlan& pl, GemvParams p, hipStream_t
 #undef OCR_E
 }
 
-// Final reduction of the per-workgroup argmax partials: one thread per row.
-__global__ void argmax_final_kernel(const float* part, int n_wg, int rows, int32_t* tok_out, float* top2,
-                                    int32_t* gen_index) {
-    const int r = blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= rows) return;
-    float b = -INFINITY, s = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int w = 0; w < n_wg; ++w) {
-        const float* e = part + ((int64_t)w * rows + r) * 3;
-        argmax_merge(b, bi, s, e[0], __float_as_int(e[1]), e[2]);
-    }
-    if (tok_out) tok_out[r] = (bi == 0x7fffffff) ? 0 : bi;
-    if (top2) {
-        top2[2 * r] = b;
-        top2[2 * r + 1] = s;
-    }
-    if (gen_index) gen_index[r] += 1;
-}
-
-void launch_argmax_final(const float* part, int n_wg, int rows, int32_t* tok_out, float* top2, int32_t* gen_index,
-                         hipStream_t s) {
-    hipLaunchKernelGGL(argmax_final_kernel, dim3((rows + 63) / 64), dim3(64), 0, s, part, n_wg, rows, tok_out, top2,
-                       gen_index);
-}
+size_t argmax_ws_bytes(int grid, int rows) { return align256((size_t)grid * rows * 3 * sizeof(float)) + 256; }
 
 }  // namespace ocrdec
 
@@ -270,4 +277,40 @@ extern "C" ocrdec_status ocrdec_gemv_q(const ocrdec_qmat* W, int32_t rows, const
     p.ldy = ldy;
     launch_gemv(W->fmt, epi, pl, p, (hipStream_t)stream);
     return launch_status("ocrdec_gemv_q");
+}
+
+extern "C" ocrdec_status ocrdec_lm_argmax_workspace_bytes(const ocrdec_qmat* W, int32_t rows, size_t* bytes) {
+    ocrdec_status st = check_qmat(W, "W");
+    if (st != OCRDEC_OK) return st;
+    OCR_CHECK_ARG(rows >= 1 && rows <= 32, "rows must be in [1, 32]");
+    OCR_CHECK_ARG(bytes, "bytes is NULL");
+    GemvPlan pl = plan_gemv(W->fmt, W->n, W->k, rows, EPI_ARGMAX);
+    *bytes = argmax_ws_bytes(pl.grid, rows);
+    return OCRDEC_OK;
+}
+
+extern "C" ocrdec_status ocrdec_lm_argmax(const ocrdec_qmat* W, int32_t rows, const uint16_t* x, int32_t* tok_out,
+                                          float* top2, void* ws, size_t ws_bytes, void* stream) {
+    ocrdec_status st = check_qmat(W, "W");
+    if (st != OCRDEC_OK) return st;
+    OCR_CHECK_ARG(rows >= 1 && rows <= 32, "rows must be in [1, 32]");
+    OCR_CHECK_ARG(x && tok_out, "x and tok_out must be non-NULL");
+    OCR_CHECK_ARG(((uintptr_t)x & 15) == 0, "x must be 16-byte aligned");
+    GemvPlan pl = plan_gemv(W->fmt, W->n, W->k, rows, EPI_ARGMAX);
+    const size_t need = argmax_ws_bytes(pl.grid, rows);
+    if (!ws || ws_bytes < need)
+        return fail(OCRDEC_ERR_WORKSPACE, "argmax workspace: need " + std::to_string(need) + " bytes, got " +
+                                              std::to_string(ws ? ws_bytes : 0));
+    GemvParams p{};
+    p.w = (const uint8_t*)W->data;
+    p.n = W->n;
+    p.k = W->k;
+    p.nchunks = n_chunks(W->fmt, W->k);
+    p.xs = XDirect{x, W->k, rows};
+    p.part = (float*)ws;
+    p.counter = (int*)((char*)ws + need - 256);
+    p.tok_out = tok_out;
+    p.top2 = top2;
+    launch_gemv(W->fmt, EPI_ARGMAX, pl, p, (hipStream_t)stream);
+    return launch_status("ocrdec_lm_argmax");
 }

@@ -12,10 +12,14 @@ struct GemvParams {
     int n, k;
     int64_t nchunks;
     XDirect xs;
-    void* y;          // output (EPI_RESID: the fp16 residual, updated in place)
+    void* y;          // output (EPI_RESID: the fp32 residual, updated in place)
     int64_t ldy;
     int half_tiles;   // EPI_GLU: tiles in the gate half (= d_ff / 16)
     float* part;      // EPI_ARGMAX: [grid][rows][3] (best, index bits, second)
+    int* counter;     // EPI_ARGMAX: zero on entry; the last workgroup reduces and resets it
+    int32_t* tok_out; // EPI_ARGMAX outputs
+    float* top2;
+    int32_t* gen_index;
     int n_groups;
 };
 
@@ -25,8 +29,9 @@ struct GemvPlan {
 
 GemvPlan plan_gemv(int fmt, int n, int k, int rows, int epi);
 void launch_gemv(int fmt, int epi, const GemvPlan& pl, GemvParams p, hipStream_t s);
-void launch_argmax_final(const float* part, int n_wg, int rows, int32_t* tok_out, float* top2, int32_t* gen_index,
-                         hipStream_t s);
+// Argmax workspace: partials, then the arrival counter (must be zero before
+// the first use; every launch leaves it zero).
+size_t argmax_ws_bytes(int grid, int rows);
 
 // Merge of two (best, index, second) argmax states; ties go to the lower index.
 OCR_DEV void argmax_merge(float& b, int& bi, float& s, float ob, int oi, float os) {

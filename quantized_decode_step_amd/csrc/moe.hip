@@ -248,16 +248,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     __shared__ float red[8];
     const int r = blockIdx.x, tid = threadIdx.x;
     const int K = p.top_k, R = p.rows, H = p.hidden;
-    uint16_t* h = p.h + (int64_t)r * p.ldh;
+    uint16_t* h16 = (uint16_t*)p.h + (int64_t)r * p.ldh;
+    float* h32 = (float*)p.h + (int64_t)r * p.ldh;
     float ss = 0.f;
     for (int col = tid; col < H; col += blockDim.x) {
         float acc = 0.f;
         for (int s = 0; s < p.n_shared; ++s) acc += p.y[((int64_t)p.np + s * R + r) * H + col];
         for (int j = 0; j < K; ++j) acc = fmaf(p.w[r * K + j], p.y[(int64_t)p.inv[r * K + j] * H + col], acc);
-        const float hv = p.add_residual ? h2f(h[col]) + acc : acc;
-        const uint16_t hb = f2h(hv);
-        h[col] = hb;
-        const float hr = h2f(hb);
+        float hr;
+        if (p.h_f32) {
+            hr = p.add_residual ? h32[col] + acc : acc;
+            h32[col] = hr;
+        } else {
+            const uint16_t hb = f2h(p.add_residual ? h2f(h16[col]) + acc : acc);
+            h16[col] = hb;
+            hr = h2f(hb);
+        }
         ss = fmaf(hr, hr, ss);
     }
     if (!p.norm_w) return;
@@ -268,7 +274,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += red[i];
     const float inv = 1.0f / sqrtf(tot / (float)H + p.eps);
     uint16_t* x = p.x_out + (int64_t)r * p.ldx;
-    for (int col = tid; col < H; col += blockDim.x) x[col] = f2h(h2f(h[col]) * inv * h2f(p.norm_w[col]));
+    for (int col = tid; col < H; col += blockDim.x) {
+        const float hv = p.h_f32 ? h32[col] : h2f(h16[col]);
+        x[col] = f2h(hv * inv * h2f(p.norm_w[col]));
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -364,7 +373,7 @@ void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream
 
 }  // namespace
 
-void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, uint16_t* h, int64_t ldh,
+void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_f32, int64_t ldh,
                 int add_residual, const int32_t* forced, const ocrdec_moe_capture* cap, int32_t* cap_idx,
                 float* cap_w, const MoeWs& m, const uint16_t* norm_w, float eps, uint16_t* x_out, int64_t ldxo,
                 hipStream_t s) {
@@ -472,6 +481,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.inv = m.inv;
         p.y = m.y;
         p.h = h;
+        p.h_f32 = h_f32;
         p.ldh = ldh;
         p.add_residual = add_residual;
         p.norm_w = norm_w;
@@ -507,7 +517,7 @@ extern "C" ocrdec_status ocrdec_moe_layer(const ocrdec_moe_weights* w, int32_t r
         return fail(OCRDEC_ERR_WORKSPACE, "MoE workspace: need " + std::to_string(need) + " bytes, got " +
                                               std::to_string(ws ? ws_bytes : 0));
     MoeWs m = carve_moe(ws, rows, w);
-    launch_moe(w, rows, x, w->hidden, h, w->hidden, add_residual, forced_topk, capture, nullptr, nullptr, m, nullptr,
+    launch_moe(w, rows, x, w->hidden, h, 0, w->hidden, add_residual, forced_topk, capture, nullptr, nullptr, m, nullptr,
                0.f, nullptr, 0, (hipStream_t)stream);
     return launch_status("ocrdec_moe_layer");
 }

@@ -64,7 +64,8 @@ struct CombineParams {
     const float* w;
     const int32_t* inv;
     const float* y;
-    uint16_t* h;
+    void* h;          // fp16 (h_f32 == 0) or fp32 residual
+    int h_f32;
     int64_t ldh;
     int add_residual;
     const uint16_t* norm_w;  // RMSNorm gain of the next block, or NULL
@@ -95,7 +96,7 @@ struct MoeWs {
 
 MoeWs carve_moe(void* ws, int rows, const ocrdec_moe_weights* w);
 ocrdec_status check_moe(const ocrdec_moe_weights* w, int rows);
-void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, uint16_t* h, int64_t ldh,
+void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_f32, int64_t ldh,
                 int add_residual, const int32_t* forced, const ocrdec_moe_capture* cap, int32_t* cap_idx,
                 float* cap_w, const MoeWs& m, const uint16_t* norm_w, float eps, uint16_t* x_out, int64_t ldxo,
                 hipStream_t s);

@@ -14,13 +14,13 @@ namespace {
 
 constexpr int kMaxRows = 32;
 
-// x = fp16(RMSNorm(h) * gamma) of one row; the workgroup's threads stride
-// over the columns.
-OCR_DEV void norm_row(const uint16_t* h, const uint16_t* gamma, int H, float eps, uint16_t* x, float* red) {
+// x = fp16(RMSNorm(h) * gamma) of one row of the fp32 residual; the
+// workgroup's threads stride over the columns.
+OCR_DEV void norm_row(const float* h, const uint16_t* gamma, int H, float eps, uint16_t* x, float* red) {
     const int tid = threadIdx.x;
     float ss = 0.f;
     for (int c = tid; c < H; c += blockDim.x) {
-        const float v = h2f(h[c]);
+        const float v = h[c];
         ss = fmaf(v, v, ss);
     }
     ss = wave_sum(ss);
@@ -29,37 +29,39 @@ OCR_DEV void norm_row(const uint16_t* h, const uint16_t* gamma, int H, float eps
     float tot = 0.f;
     for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += red[i];
     const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-    for (int c = tid; c < H; c += blockDim.x) x[c] = f2h(h2f(h[c]) * inv * h2f(gamma[c]));
+    for (int c = tid; c < H; c += blockDim.x) x[c] = f2h(h[c] * inv * h2f(gamma[c]));
 }
 
-// h[r] = embed[tok[r]] or src[r]; x[r] = norm(h[r]).
+// h[r] = embed[tok[r]] (fp16 table) or src[r] (fp32); x[r] = norm(h[r]).
 __global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tok, const uint16_t* embed, int vocab,
-                                                         const uint16_t* src, uint16_t* h, const uint16_t* gamma,
-                                                         int H, float eps, uint16_t* x) {
+                                                         const float* src, float* h, const uint16_t* gamma,
+                                                         int H, float eps, uint16_t* x, int* lm_counter) {
     __shared__ float red[8];
     const int r = blockIdx.x;
-    const uint16_t* from;
+    // the language-head argmax of this step counts arriving workgroups from zero
+    if (r == 0 && threadIdx.x == 0 && lm_counter) *lm_counter = 0;
+    float* hr = h + (int64_t)r * H;
     if (tok) {
         int t = tok[r];
         t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
-        from = embed + (int64_t)t * H;
+        const uint16_t* from = embed + (int64_t)t * H;
+        for (int c = threadIdx.x; c < H; c += blockDim.x) hr[c] = h2f(from[c]);
     } else {
-        from = src + (int64_t)r * H;
+        const float* from = src + (int64_t)r * H;
+        for (int c = threadIdx.x; c < H; c += blockDim.x) hr[c] = from[c];
     }
-    uint16_t* hr = h + (int64_t)r * H;
-    for (int c = threadIdx.x; c < H; c += blockDim.x) hr[c] = from[c];
     __syncthreads();
     norm_row(hr, gamma, H, eps, x + (int64_t)r * H, red);
 }
 
-__global__ __launch_bounds__(256) void norm_kernel(const uint16_t* h, const uint16_t* gamma, int H, float eps,
+__global__ __launch_bounds__(256) void norm_kernel(const float* h, const uint16_t* gamma, int H, float eps,
                                                    uint16_t* x) {
     __shared__ float red[8];
     const int r = blockIdx.x;
     norm_row(h + (int64_t)r * H, gamma, H, eps, x + (int64_t)r * H, red);
 }
 
-__global__ void copy_rows_kernel(const uint16_t* src, uint16_t* dst, int64_t n) {
+__global__ void copy_rows_kernel(const float* src, float* dst, int64_t n) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         dst[i] = src[i];
 }
@@ -70,7 +72,7 @@ __global__ void bump_kernel(int32_t* gen_index, int rows) {
 }
 
 struct StepWs {
-    uint16_t* h;
+    float* h;
     uint16_t* x;
     float* qkv;
     float* attn_part;
@@ -96,13 +98,13 @@ StepWs carve_step(void* ws, const ocrdec_model* m, int rows, int cache_cap) {
         if (m->layers[l].is_moe) moe = &m->layers[l].moe;
         else dense_ff = std::max(dense_ff, m->layers[l].dense_ff);
     }
-    w.h = cv.take<uint16_t>((size_t)rows * H);
+    w.h = cv.take<float>((size_t)rows * H);
     w.x = cv.take<uint16_t>((size_t)rows * H);
     w.qkv = cv.take<float>((size_t)rows * 3 * HD);
     w.attn_part = cv.take<float>(attn_ws_bytes(rows, m->n_heads, m->head_dim, cache_cap) / sizeof(float));
     w.o = cv.take<uint16_t>((size_t)rows * HD);
     w.a = cv.take<uint16_t>((size_t)rows * std::max(dense_ff, 1));
-    w.lm_part = cv.take<float>((size_t)std::max(lm_grid(m, rows), 1) * rows * 3);
+    w.lm_part = cv.take<float>(argmax_ws_bytes(std::max(lm_grid(m, rows), 1), rows) / sizeof(float));
     if (moe) {
         MoeWs probe = carve_moe(nullptr, rows, moe);
         char* base = (char*)cv.take<char>(probe.bytes);
@@ -180,7 +182,7 @@ extern "C" ocrdec_status ocrdec_step_workspace_bytes(const ocrdec_model* m, cons
 }
 
 extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_state* st, const int32_t* tok_in,
-                                            uint16_t* hidden, int32_t* tok_out, const int32_t* forced_topk,
+                                            float* hidden, int32_t* tok_out, const int32_t* forced_topk,
                                             const ocrdec_step_capture* cap, void* ws, size_t ws_bytes, void* stream) {
     ocrdec_status s0 = check_step(m, st);
     if (s0 != OCRDEC_OK) return s0;
@@ -196,8 +198,13 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     hipStream_t s = (hipStream_t)stream;
     StepWs w = carve_step(ws, m, R, cache_cap);
 
+    int* lm_counter = nullptr;
+    if (m->lm_head.data) {
+        const int g = lm_grid(m, R);
+        lm_counter = (int*)((char*)w.lm_part + argmax_ws_bytes(g, R) - 256);
+    }
     hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(256), 0, s, tok_in, m->embed, m->vocab, hidden, w.h,
-                       m->layers[0].attn_norm, H, m->norm_eps, w.x);
+                       m->layers[0].attn_norm, H, m->norm_eps, w.x, lm_counter);
     int moe_l = 0;
     for (int l = 0; l < m->n_layers; ++l) {
         const ocrdec_layer& L = m->layers[l];
@@ -258,7 +265,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             int32_t* ci = cap && cap->topk_idx ? cap->topk_idx + (int64_t)moe_l * R * K : nullptr;
             float* cw = cap && cap->topk_w ? cap->topk_w + (int64_t)moe_l * R * K : nullptr;
             const int32_t* fo = forced_topk ? forced_topk + (int64_t)moe_l * R * K : nullptr;
-            launch_moe(&L.moe, R, w.x, H, w.h, H, 1, fo, nullptr, ci, cw, w.moe, next_norm, m->norm_eps, w.x, H, s);
+            launch_moe(&L.moe, R, w.x, H, w.h, 1, H, 1, fo, nullptr, ci, cw, w.moe, next_norm, m->norm_eps, w.x, H, s);
             ++moe_l;
         } else {
             const int F = L.dense_ff;
@@ -304,8 +311,11 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
         gp.nchunks = n_chunks(m->lm_head.fmt, H);
         gp.xs = XDirect{w.x, H, R};
         gp.part = w.lm_part;
+        gp.counter = (int*)((char*)w.lm_part + argmax_ws_bytes(pl.grid, R) - 256);
+        gp.tok_out = tok_out;
+        gp.top2 = cap ? cap->lm_top2 : nullptr;
+        gp.gen_index = st->gen_index;
         launch_gemv(m->lm_head.fmt, EPI_ARGMAX, pl, gp, s);
-        launch_argmax_final(w.lm_part, pl.grid, R, tok_out, cap ? cap->lm_top2 : nullptr, st->gen_index, s);
     } else {
         hipLaunchKernelGGL(bump_kernel, dim3(1), dim3(64), 0, s, st->gen_index, R);
     }

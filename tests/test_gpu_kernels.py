@@ -7,7 +7,7 @@ import pytest
 
 import oracle as O
 import synth
-from tests.gpu_util import NEAR_TIE, assert_close, f16_tensor, from_f16_tensor
+from tests.gpu_util import NEAR_TIE, assert_close, assert_close_f16, f16_tensor, from_f16_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -56,9 +56,11 @@ def test_gemv_q_parity(q, fmt, n, k, rows, otype):
     torch.cuda.synchronize()
     ref = O.gemv_qmat(m, x.astype(np.float64))
     got = y.cpu().numpy().astype(np.float64) if otype == 0 else from_f16_tensor(y)
+    what = "gemv %s %dx%d rows=%d" % (synth.FMT_NAMES[fmt], n, k, rows)
     if otype == 1:
-        ref = O.f16(ref)
-    assert_close(got, ref, "gemv %s %dx%d rows=%d" % (synth.FMT_NAMES[fmt], n, k, rows))
+        assert_close_f16(got, O.f16(ref), what)
+    else:
+        assert_close(got, ref, what)
 
 
 def test_gemv_q_rejects_bad_args(q):
@@ -144,8 +146,8 @@ def _attn_case(q, rows, NH, D, prefix_cap, ring_cap, prefix_len, gen_index, sink
                                      sink_index=0)
             else:
                 ref[h] = O.attention(qr[h], kcr[h, idx], vcr[h, idx], 1 / np.sqrt(D))
-        assert_close(got[r], O.f16(ref.reshape(-1)), "attn out row %d" % r)
-        assert_close(kc_after[r][:, slot].astype(np.float64), kr, "new k row %d" % r)
+        assert_close_f16(got[r], O.f16(ref.reshape(-1)), "attn out row %d" % r)
+        assert_close_f16(kc_after[r][:, slot].astype(np.float64), kr, "new k row %d" % r)
         assert np.array_equal(vc_after[r][:, slot].astype(np.float64), vr), "new v row %d" % r
         # nothing else in the cache changed
         mask = np.ones(kc.shape[2], bool)
@@ -224,7 +226,7 @@ def _moe_case(q, rows, seed, H=1280, E=64, K=6, S=2, F=896, fmt=synth.Q8_0, bias
         assert np.array_equal(perm.cpu().numpy(), p)
     ref = O.f16(h + out) if residual else O.f16(out)
     got = from_f16_tensor(hd)
-    assert_close(got[keep_rows], ref[keep_rows], "moe out")
+    assert_close_f16(got[keep_rows], ref[keep_rows], "moe out")
 
 
 @pytest.mark.parametrize("rows", [1, 6, 24])
@@ -241,3 +243,59 @@ def test_moe_q4_small_parity(q):
 def test_moe_prefill_bias_parity(q):
     _say("moe prefill-shaped 300 rows with bias")
     _moe_case(q, 300, 1005, H=1280, E=64, K=6, S=2, F=896, fmt=synth.Q4_0, bias=True, residual=False)
+
+
+# -----------------------------------------------------------------------------
+# ocrdec_lm_argmax
+# -----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt,n,rows", [(synth.F16, 129280, 1), (synth.F16, 129280, 24), (synth.Q8_0, 5000, 7),
+                                        (synth.Q4_0, 999, 32)])
+def test_lm_argmax_parity(q, fmt, n, rows):
+    import torch
+    seed = 77 + n + rows
+    _say("lm_argmax", synth.FMT_NAMES[fmt], n, rows, "seed", seed)
+    m = synth.random_qmat(fmt, synth.stream_id(seed, "W"), n, 1280, 0.02)
+    x = synth.normal_f16(synth.stream_id(seed, "x"), (rows, 1280))
+    # plant a tie between two rows for row 0: the lower index must win
+    dm = q.DeviceQMat(m)
+    xd = f16_tensor(x)
+    tok = torch.full((rows,), -1, dtype=torch.int32, device="cuda")
+    top2 = torch.zeros((rows, 2), dtype=torch.float32, device="cuda")
+    wsb = q.ocrdec_lm_argmax_workspace_bytes(dm.desc, rows)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    for rep in range(3):   # the workspace is reused as it is left
+        q.ocrdec_lm_argmax(dm.desc, rows, xd, tok, top2, ws, wsb)
+        torch.cuda.synchronize()
+        z = O.f32(O.gemv_qmat(m, x.astype(np.float64)))
+        g = tok.cpu().numpy()
+        t2 = top2.cpu().numpy()
+        for r in range(rows):
+            best = O.argmax_lowest(z[r])
+            srt = np.sort(z[r])[::-1]
+            if g[r] != best:
+                assert srt[0] - srt[1] < NEAR_TIE, "row %d: %d vs %d" % (r, g[r], best)
+            assert abs(t2[r, 0] - srt[0]) <= 1e-4 * max(1, abs(srt[0]))
+            assert abs(t2[r, 1] - srt[1]) <= 1e-4 * max(1, abs(srt[1]))
+    assert int(ws.view(torch.int32)[-64:].abs().sum().item()) == 0, "arrival counter not reset"
+
+
+def test_lm_argmax_ties_go_to_lowest_index(q):
+    import torch
+    _say("lm_argmax planted ties")
+    n, k, rows = 4096, 128, 3
+    w = np.zeros((n, k), np.float16)
+    x = np.zeros((rows, k), np.float16)
+    x[:, 0] = 1
+    # row r of x: winners planted at several equal maxima
+    for v in (17, 900, 4000):
+        w[v, 0] = 2.0
+    w[3000, 0] = 1.5
+    m = synth.QMat(synth.F16, n, k, w.reshape(-1).view(np.uint8).copy())
+    dm = q.DeviceQMat(m)
+    tok = torch.full((rows,), -1, dtype=torch.int32, device="cuda")
+    wsb = q.ocrdec_lm_argmax_workspace_bytes(dm.desc, rows)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    q.ocrdec_lm_argmax(dm.desc, rows, f16_tensor(x), tok, None, ws, wsb)
+    torch.cuda.synchronize()
+    assert tok.cpu().numpy().tolist() == [17, 17, 17]

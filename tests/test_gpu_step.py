@@ -13,7 +13,7 @@ import pytest
 
 import oracle as O
 import synth
-from tests.gpu_util import NEAR_TIE, assert_close, f16_tensor, from_f16_tensor
+from tests.gpu_util import NEAR_TIE, assert_close, assert_close_f16, f16_tensor, from_f16_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +52,7 @@ def run_steps(q, d, seed, prefix_len, gen_index, n_steps, forced=True, sample_ro
     cap_w = torch.zeros((max(n_moe, 1), R, K), dtype=torch.float32, device="cuda")
     top2 = torch.zeros((R, 2), dtype=torch.float32, device="cuda")
     cap = q.StepCapture(cap_idx.data_ptr(), cap_w.data_ptr(), top2.data_ptr())
-    hidden = torch.zeros((R, d.hidden), dtype=torch.int16, device="cuda")
+    hidden = torch.zeros((R, d.hidden), dtype=torch.float32, device="cuda")
     tok_out = torch.full((R,), -1, dtype=torch.int32, device="cuda")
     rows = list(range(R)) if sample_rows is None else list(sample_rows)
     tok = synth.first_tokens(d, seed, R)
@@ -70,7 +70,7 @@ def run_steps(q, d, seed, prefix_len, gen_index, n_steps, forced=True, sample_ro
         q.ocrdec_decode_step(dm.desc, ds.desc, tok_in, hidden, tok_out, forced_t, cap, ws, wsb)
         torch.cuda.synchronize()
         g_tok = tok_out.cpu().numpy()[rows]
-        g_hid = from_f16_tensor(hidden)[rows]
+        g_hid = hidden.cpu().numpy().astype(np.float64)[rows]
         g_idx = cap_idx.cpu().numpy()[:, rows]
         g_w = cap_w.cpu().numpy()[:, rows]
         # routing decisions
@@ -97,8 +97,10 @@ def run_steps(q, d, seed, prefix_len, gen_index, n_steps, forced=True, sample_ro
                 for i, r in enumerate(rows):
                     t = int(st.gen_index[r]) + step
                     slot = d.prefix_cap + t % d.ring_cap
-                    assert_close(kc[l, r, :, slot].astype(np.float64), res.new_k[l][i], "step %d layer %d k" % (step, l))
-                    assert_close(vc[l, r, :, slot].astype(np.float64), res.new_v[l][i], "step %d layer %d v" % (step, l))
+                    assert_close_f16(kc[l, r, :, slot].astype(np.float64), res.new_k[l][i],
+                                     "step %d layer %d k" % (step, l))
+                    assert_close_f16(vc[l, r, :, slot].astype(np.float64), res.new_v[l][i],
+                                     "step %d layer %d v" % (step, l))
         gi = ds.gen_index.cpu().numpy()
         assert np.array_equal(gi[rows], ost.gen_index[rows])
         nxt = tok.copy()
@@ -140,11 +142,11 @@ def test_step_single_dense_layer_fp16(q):
     dm.bind_caches(ds.k_cache, ds.v_cache)
     wsb = q.ocrdec_step_workspace_bytes(dm.desc, ds.desc)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    hidden = f16_tensor(h0)
+    hidden = torch.from_numpy(h0.astype(np.float32)).cuda()
     q.ocrdec_decode_step(dm.desc, ds.desc, None, hidden, None, None, None, ws, wsb)
     torch.cuda.synchronize()
     res = O.decode_step(model, st.copy(), hidden_in=h0.astype(np.float64), with_lm=False)
-    assert_close(from_f16_tensor(hidden), res.hidden, "dense layer hidden")
+    assert_close(hidden.cpu().numpy(), res.hidden, "dense layer hidden")
 
 
 def test_step_single_moe_layer_q8(q):
@@ -161,7 +163,7 @@ def test_step_single_moe_layer_q8(q):
     dm.bind_caches(ds.k_cache, ds.v_cache)
     wsb = q.ocrdec_step_workspace_bytes(dm.desc, ds.desc)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    hidden = f16_tensor(h0)
+    hidden = torch.from_numpy(h0.astype(np.float32)).cuda()
     cap_idx = torch.zeros((1, 1, d.top_k), dtype=torch.int32, device="cuda")
     cap = q.StepCapture(cap_idx.data_ptr(), None, None)
     q.ocrdec_decode_step(dm.desc, ds.desc, None, hidden, None, None, cap, ws, wsb)
@@ -170,4 +172,4 @@ def test_step_single_moe_layer_q8(q):
     if not np.array_equal(cap_idx.cpu().numpy()[0, 0], res.topk_idx[0][0]):
         assert res.router_gap[0][0] < NEAR_TIE
         pytest.skip("near-tie routing for this seed")
-    assert_close(from_f16_tensor(hidden), res.hidden, "moe layer hidden")
+    assert_close(hidden.cpu().numpy(), res.hidden, "moe layer hidden")
