@@ -175,7 +175,11 @@ ocrdec_status ocrdec_lm_argmax(const ocrdec_qmat* W, int32_t rows, const uint16_
  * sink and value 0 (its constant-1 query lane folded into a logit).
  *
  * gen_index and prefix_len are read, never written.
- * head_dim: 64 or 128.  rows >= 1.  Workspace: ocrdec_attn_workspace_bytes.
+ * head_dim: 64 or 128.  rows >= 1.  Workspace: ocrdec_attn_workspace_bytes;
+ * it must be zero-filled before its first use and every call leaves it
+ * zero-filled again where it matters (its tail holds per-(row, head) arrival
+ * counters: the last of a head's key splits to finish merges them, so the
+ * whole attention is one launch).
  * Errors: INVALID_ARG (NULL pointers, head_dim, ld_* too small, caps),
  * WORKSPACE (too small), DEVICE. */
 typedef struct {

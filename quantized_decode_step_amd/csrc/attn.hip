@@ -8,8 +8,9 @@
 //
 // Split-KV: workgroup (split, head, row) scores up to 64 keys of the row's
 // window, keeps them in LDS, and writes an unnormalised partial (max, sum,
-// sum of p*v); a combine kernel merges the splits with the usual
-// log-sum-exp rescaling.  Keys are streamed with one 16-byte load per lane:
+// sum of p*v); the last split of a (row, head) to finish (an arrival counter
+// in the workspace) merges the splits with the usual log-sum-exp rescaling,
+// so one launch does the whole attention.  Keys are streamed with one 16-byte load per lane:
 // for head_dim 128 a wavefront load covers 4 keys (16 lanes per key), for 64
 // it covers 8 keys.
 #include "attn.hpp"
@@ -86,14 +87,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
     const Window w = row_window(p, r);
     const int o0 = s * KPS, o1 = min(o0 + KPS, w.nkeys);
     float* part = p.part + (((int64_t)r * p.n_heads + h) * p.n_split + s) * (D + 2);
-    if (o0 >= o1) {
-        if (tid < D) part[tid] = 0.f;
-        if (tid == 0) {
-            part[D] = -INFINITY;
-            part[D + 1] = 0.f;
-        }
-        return;
-    }
+    if (o0 >= o1) return;  // beyond this row's window: not counted below
     const bool has_new = (w.new_ord >= o0 && w.new_ord < o1);
     const float* qkv = p.qkv + (int64_t)r * p.ld_qkv;
     const int HD = p.n_heads * D;
@@ -192,41 +186,68 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
         part[D] = red_s[0];
         part[D + 1] = red_s[1];
     }
-}
 
-template <int D>
-__global__ void attn_combine_kernel(AttnParams p) {
-    const int h = blockIdx.x, r = blockIdx.y, d = threadIdx.x;
-    const float* part = p.part + ((int64_t)r * p.n_heads + h) * p.n_split * (D + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
-    float L = 0.f, o = 0.f;
-    for (int s = 0; s < p.n_split; ++s) {
-        const float m = part[s * (D + 2) + D];
-        if (m == -INFINITY) continue;
-        const float f = __expf(m - M);
-        L = fmaf(part[s * (D + 2) + D + 1], f, L);
-        o = fmaf(part[s * (D + 2) + d], f, o);
+    // ---- the last split of (row, head) to finish merges all of them
+    __shared__ int is_last;
+    __shared__ float f_s[1024 + 1];
+    const int n_used = (w.nkeys + KPS - 1) / KPS;
+    int* ctr = p.counters + (int64_t)r * p.n_heads + h;
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) is_last = (atomicAdd(ctr, 1) == n_used - 1);
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+    const float* part0 = p.part + ((int64_t)r * p.n_heads + h) * p.n_split * (D + 2);
+    for (int i = tid; i < n_used; i += blockDim.x) f_s[i] = __builtin_nontemporal_load(part0 + i * (D + 2) + D);
+    __syncthreads();
+    if (wave == 0) {
+        float M = -INFINITY;
+        for (int i = lane; i < n_used; i += 64) M = fmaxf(M, f_s[i]);
+        M = wave_max(M);
+        float L = 0.f;
+        for (int i = lane; i < n_used; i += 64) {
+            const float f = __expf(f_s[i] - M);
+            L = fmaf(__builtin_nontemporal_load(part0 + i * (D + 2) + D + 1), f, L);
+            f_s[i] = f;
+        }
+        L = wave_sum(L);
+        if (lane == 0) f_s[1024] = 1.0f / L;
     }
-    p.out[(int64_t)r * p.ld_out + h * D + d] = f2h(o / L);
+    __syncthreads();
+    if (tid < D) {
+        float o = 0.f;
+        int i = 0;
+        for (; i + 4 <= n_used; i += 4) {
+            const float a0 = __builtin_nontemporal_load(part0 + (i + 0) * (D + 2) + tid);
+            const float a1 = __builtin_nontemporal_load(part0 + (i + 1) * (D + 2) + tid);
+            const float a2 = __builtin_nontemporal_load(part0 + (i + 2) * (D + 2) + tid);
+            const float a3 = __builtin_nontemporal_load(part0 + (i + 3) * (D + 2) + tid);
+            o = fmaf(a0, f_s[i], o);
+            o = fmaf(a1, f_s[i + 1], o);
+            o = fmaf(a2, f_s[i + 2], o);
+            o = fmaf(a3, f_s[i + 3], o);
+        }
+        for (; i < n_used; ++i) o = fmaf(__builtin_nontemporal_load(part0 + i * (D + 2) + tid), f_s[i], o);
+        p.out[(int64_t)r * p.ld_out + h * D + tid] = f2h(o * f_s[1024]);
+    }
+    if (tid == 0) *ctr = 0;
 }
 
-int attn_n_split(int cache_cap) { return (cache_cap + 1 + KPS - 1) / KPS; }
+int attn_n_split(int cache_cap) { return (cache_cap + KPS - 1) / KPS; }
+
+size_t attn_part_bytes(int rows, int n_heads, int head_dim, int cache_cap) {
+    return align256((size_t)rows * n_heads * attn_n_split(cache_cap) * (head_dim + 2) * sizeof(float));
+}
 
 size_t attn_ws_bytes(int rows, int n_heads, int head_dim, int cache_cap) {
-    return align256((size_t)rows * n_heads * attn_n_split(cache_cap) * (head_dim + 2) * sizeof(float));
+    return attn_part_bytes(rows, n_heads, head_dim, cache_cap) + align256((size_t)rows * n_heads * sizeof(int));
 }
 
 void launch_attn(const AttnParams& p, hipStream_t s) {
     dim3 g1(p.n_split, p.n_heads, p.rows);
-    dim3 g2(p.n_heads, p.rows);
-    if (p.head_dim == 128) {
-        hipLaunchKernelGGL(attn_partial_kernel<128>, g1, dim3(256), 0, s, p);
-        hipLaunchKernelGGL(attn_combine_kernel<128>, g2, dim3(128), 0, s, p);
-    } else {
-        hipLaunchKernelGGL(attn_partial_kernel<64>, g1, dim3(256), 0, s, p);
-        hipLaunchKernelGGL(attn_combine_kernel<64>, g2, dim3(64), 0, s, p);
-    }
+    if (p.head_dim == 128) hipLaunchKernelGGL(attn_partial_kernel<128>, g1, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(attn_partial_kernel<64>, g1, dim3(256), 0, s, p);
 }
 
 ocrdec_status check_attn(const ocrdec_attn_args* a) {
@@ -287,6 +308,7 @@ extern "C" ocrdec_status ocrdec_attn_decode(const ocrdec_attn_args* a, void* ws,
     p.ld_out = a->ld_out;
     p.n_split = attn_n_split(cap);
     p.part = (float*)ws;
+    p.counters = (int*)((char*)ws + attn_part_bytes(a->rows, a->n_heads, a->head_dim, cap));
     launch_attn(p, (hipStream_t)stream);
     return launch_status("ocrdec_attn_decode");
 }

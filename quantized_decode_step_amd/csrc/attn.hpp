@@ -19,10 +19,12 @@ struct AttnParams {
     uint16_t* out;
     int64_t ld_out;
     int n_split;
-    float* part;  // [rows][n_heads][n_split][head_dim + 2]
+    float* part;    // [rows][n_heads][n_split][head_dim + 2]
+    int* counters;  // [rows][n_heads] arrival counters: zero on entry, left zero
 };
 
 int attn_n_split(int cache_cap);
+size_t attn_part_bytes(int rows, int n_heads, int head_dim, int cache_cap);
 size_t attn_ws_bytes(int rows, int n_heads, int head_dim, int cache_cap);
 void launch_attn(const AttnParams& p, hipStream_t s);
 ocrdec_status check_attn(const ocrdec_attn_args* a);

@@ -34,6 +34,34 @@ OCR_DEV void argmax_finish(const GemvParams& p) {
     if (threadIdx.x == 0) *p.counter = 0;
 }
 
+// Last-arriving workgroup of a residual-update launch: RMSNorm of every
+// updated row into norm_out (the next block's fp16 input), then resets the
+// arrival counter.  One wavefront per row.
+OCR_DEV void resid_norm_finish(const GemvParams& p) {
+    __shared__ int is_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) is_last = (atomicAdd(p.counter, 1) == (int)gridDim.x - 1);
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const float* h = (const float*)p.y;
+    for (int r = wave; r < p.xs.rows; r += nw) {
+        const float* hr = h + (int64_t)r * p.ldy;
+        float ss = 0.f;
+        for (int c = lane; c < p.n; c += 64) {
+            const float v = __builtin_nontemporal_load(hr + c);
+            ss = fmaf(v, v, ss);
+        }
+        ss = wave_sum(ss);
+        const float inv = 1.0f / sqrtf(ss / (float)p.n + p.eps);
+        for (int c = lane; c < p.n; c += 64)
+            p.norm_out[(int64_t)r * p.n + c] = f2h(__builtin_nontemporal_load(hr + c) * inv * h2f(p.norm_w[c]));
+    }
+    if (threadIdx.x == 0) *p.counter = 0;
+}
+
 template <int FMT, int NT, int XT, int KS, int EPI>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
     constexpr int CB = Geom<FMT>::CB;
@@ -175,6 +203,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
                     }
                 }
         }
+        if constexpr (EPI == EPI_RESID) {
+            if (p.norm_w && tok0 + 16 * XT >= p.xs.rows) resid_norm_finish(p);
+        }
         __syncthreads();
     }
 }
@@ -198,7 +229,7 @@ void launch_fmt(const GemvParams& p, int nt, int ks, int xt, hipStream_t s) {
     if constexpr (EPI == EPI_GLU) {
         OCR_L(2, 1, 1) OCR_L(2, 1, 2) OCR_L(2, 4, 1) OCR_L(2, 4, 2)
     } else {
-        OCR_L(1, 4, 1) OCR_L(1, 4, 2) OCR_L(4, 1, 1) OCR_L(4, 1, 2)
+        OCR_L(1, 4, 1) OCR_L(1, 4, 2) OCR_L(1, 1, 1) OCR_L(1, 1, 2)
     }
 #undef OCR_L
 }
@@ -214,9 +245,9 @@ GemvPlan plan_gemv(int fmt, int n, int k, int rows, int epi) {
         pl.groups = (int)(tiles / 2);
         pl.ks = pl.groups >= 512 ? 1 : 4;
     } else if (tiles >= 1024) {
-        pl.nt = 4;
+        pl.nt = 1;
         pl.ks = 1;
-        pl.groups = (int)((tiles + 3) / 4);
+        pl.groups = (int)tiles;
     } else {
         pl.nt = 1;
         pl.ks = 4;

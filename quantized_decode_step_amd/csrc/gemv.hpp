@@ -16,7 +16,11 @@ struct GemvParams {
     int64_t ldy;
     int half_tiles;   // EPI_GLU: tiles in the gate half (= d_ff / 16)
     float* part;      // EPI_ARGMAX: [grid][rows][3] (best, index bits, second)
-    int* counter;     // EPI_ARGMAX: zero on entry; the last workgroup reduces and resets it
+    int* counter;     // EPI_ARGMAX, and EPI_RESID with norm_w: zero on entry; the last
+                      // workgroup to finish does the follow-up work and resets it
+    const uint16_t* norm_w;  // EPI_RESID: RMSNorm gain applied to the updated residual, or NULL
+    float eps;
+    uint16_t* norm_out;      // fp16 [rows][n] normalised residual
     int32_t* tok_out; // EPI_ARGMAX outputs
     float* top2;
     int32_t* gen_index;

@@ -27,6 +27,12 @@ struct Geom<OCRDEC_Q4_0> { static constexpr int SB = 4, CB = 1152, SCB = 8; };
 template <>
 struct Geom<OCRDEC_U8A_G32> { static constexpr int SB = 2, CB = 1152, SCB = 8; };
 
+template <int FMT>
+OCR_DEV int64_t n_chunks_dev(int k) {
+    constexpr int KC = 32 * Geom<FMT>::SB;
+    return (k + KC - 1) / KC;
+}
+
 // Registers of one (tile, chunk) for one lane.
 struct WRegs {
     uint4 q;
@@ -164,30 +170,38 @@ OCR_DEV void load_xfrags(const XS& xs, int tok0, int c, int nblk, int lane, half
 }
 
 // The k-loop of one wavefront: NT tiles (tile[i] chunk pointers) over chunks
-// [c0, c1), accumulating into acc[NT][XT].  Loads of chunk c+1 are issued
-// before the MFMAs of chunk c.
-template <int FMT, int NT, int XT, class XS>
+// [c0, c1), accumulating into acc[NT][XT].  The loads of PF chunks are kept
+// in flight: the load of chunk c+PF is issued as soon as chunk c has been
+// consumed (a register ring indexed at compile time).
+template <int FMT, int NT, int XT, class XS, int PF = 4>
 OCR_DEV void kloop(const uint8_t* const (&tile)[NT], int c0, int c1, const XS& xs, int tok0, int nblk, int lane,
                    float4v (&acc)[NT][XT]) {
     constexpr int CB = Geom<FMT>::CB;
     constexpr int SB = Geom<FMT>::SB;
     if (c0 >= c1) return;
-    WRegs cur[NT], nxt[NT];
+    WRegs buf[PF][NT];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) load_wchunk<FMT>(tile[i] + (int64_t)c0 * CB, lane, cur[i]);
-    for (int c = c0; c < c1; ++c) {
-        if (c + 1 < c1) {
+    for (int u = 0; u < PF; ++u)
+        if (c0 + u < c1) {
 #pragma unroll
-            for (int i = 0; i < NT; ++i) load_wchunk<FMT>(tile[i] + (int64_t)(c + 1) * CB, lane, nxt[i]);
+            for (int i = 0; i < NT; ++i) load_wchunk<FMT>(tile[i] + (int64_t)(c0 + u) * CB, lane, buf[u][i]);
         }
-        half8v xa[SB][XT];
-        float4v xsum[SB][XT];
-        load_xfrags<FMT, XT>(xs, tok0, c, nblk, lane, xa, xsum);
+    for (int c = c0; c < c1; c += PF) {
 #pragma unroll
-        for (int i = 0; i < NT; ++i) chunk_mac<FMT, XT>(cur[i], xa, xsum, acc[i]);
-        if (c + 1 < c1) {
+        for (int u = 0; u < PF; ++u) {
+            const int cc = c + u;
+            if (cc < c1) {
+                half8v xa[SB][XT];
+                float4v xsum[SB][XT];
+                load_xfrags<FMT, XT>(xs, tok0, cc, nblk, lane, xa, xsum);
 #pragma unroll
-            for (int i = 0; i < NT; ++i) cur[i] = nxt[i];
+                for (int i = 0; i < NT; ++i) chunk_mac<FMT, XT>(buf[u][i], xa, xsum, acc[i]);
+                if (cc + PF < c1) {
+#pragma unroll
+                    for (int i = 0; i < NT; ++i)
+                        load_wchunk<FMT>(tile[i] + (int64_t)(cc + PF) * CB, lane, buf[u][i]);
+                }
+            }
         }
     }
 }

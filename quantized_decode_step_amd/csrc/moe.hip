@@ -17,62 +17,82 @@
 namespace ocrdec {
 
 // ---------------------------------------------------------------------------
-// Routing and grouping (one workgroup of 1024 threads)
+// Routing and grouping (one workgroup of 1024 threads = 16 wavefronts)
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(1024) void route_group_kernel(MoeParams p) {
+// Top-k of the rows of `lg` ([rows][E], fp32, row stride ldl), one wavefront
+// per row: lane l holds experts l, l+64, ...; k rounds of a wave-wide argmax
+// with ties to the lower index (a NaN logit counts as -inf).  Writes the
+// experts used (forced ones if given), their renormalised weights and the
+// captures.
+OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int E = p.n_experts, K = p.top_k;
+    for (int r = wave; r < p.rows; r += nw) {
+        float v[4];
+        uint32_t taken = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = lane + 64 * j;
+            float x = -INFINITY;
+            if (e < E) {
+                x = lg[(int64_t)r * ldl + e] + (p.bias ? p.bias[e] : 0.f);
+                if (!(x == x)) x = -INFINITY;
+            }
+            v[j] = x;
+        }
+        int own = 0;  // lane j < K keeps the j-th choice
+        for (int j = 0; j < K; ++j) {
+            float bv = -INFINITY;
+            int be = 0x7fffffff;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int e = lane + 64 * jj;
+                if (e < E && !((taken >> jj) & 1) && (v[jj] > bv || be == 0x7fffffff)) {
+                    bv = v[jj];
+                    be = e;
+                }
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, 64);
+                const int oe = __shfl_xor(be, o, 64);
+                if (oe != 0x7fffffff && (be == 0x7fffffff || ov > bv || (ov == bv && oe < be))) {
+                    bv = ov;
+                    be = oe;
+                }
+            }
+            if ((be & 63) == lane) taken |= 1u << (be >> 6);
+            if (lane == j) own = be;
+        }
+        int use = own;
+        const bool forced = p.forced && p.forced[(int64_t)r * K] >= 0;
+        if (forced && lane < K) use = p.forced[(int64_t)r * K + lane];
+        use = min(max(use, 0), E - 1);  // device data: keep every index in range
+        float l = -INFINITY;
+        if (lane < K) l = lg[(int64_t)r * ldl + use] + (p.bias ? p.bias[use] : 0.f);
+        const float m = wave_max(l);
+        const float ex = lane < K ? __expf(l - m) : 0.f;
+        const float den = wave_sum(ex);
+        if (lane < K) {
+            const float w = ex / den;
+            p.idx[(int64_t)r * K + lane] = use;
+            p.w[(int64_t)r * K + lane] = w;
+            if (p.cap_idx) p.cap_idx[(int64_t)r * K + lane] = own;
+            if (p.cap_w) p.cap_w[(int64_t)r * K + lane] = w;
+        }
+    }
+}
+
+// Stable counting sort of the (row, rank) pairs by expert and the list of
+// active experts (routed experts with tokens, then the shared experts).
+OCR_DEV void group_pairs(const MoeParams& p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int R = p.rows, E = p.n_experts, K = p.top_k, S = p.n_shared;
     const int NP = R * K;
 
-    // ---- 1. top-k of every row
-    for (int r = tid; r < R; r += blockDim.x) {
-        const float* lg = p.logits + (int64_t)r * E;
-        float l_sel[8];
-        int own[8];
-        for (int j = 0; j < K; ++j) {
-            float best = -INFINITY;
-            int bi = -1;
-            for (int e = 0; e < E; ++e) {
-                bool taken = false;
-                for (int i = 0; i < j; ++i) taken |= (own[i] == e);
-                if (taken) continue;
-                float v = lg[e] + (p.bias ? p.bias[e] : 0.f);
-                if (v > best || bi < 0) {
-                    if (bi < 0 && !(v == v)) continue;  // a NaN logit never wins
-                    best = v;
-                    bi = e;
-                }
-            }
-            own[j] = bi < 0 ? 0 : bi;
-        }
-        int use[8];
-        const bool forced = p.forced && p.forced[(int64_t)r * K] >= 0;
-        for (int j = 0; j < K; ++j) {
-            const int f = forced ? p.forced[(int64_t)r * K + j] : own[j];
-            use[j] = min(max(f, 0), E - 1);  // device data: keep every index in range
-        }
-        float m = -INFINITY;
-        for (int j = 0; j < K; ++j) {
-            l_sel[j] = lg[use[j]] + (p.bias ? p.bias[use[j]] : 0.f);
-            m = fmaxf(m, l_sel[j]);
-        }
-        float den = 0.f;
-        for (int j = 0; j < K; ++j) {
-            l_sel[j] = expf(l_sel[j] - m);
-            den += l_sel[j];
-        }
-        for (int j = 0; j < K; ++j) {
-            p.idx[(int64_t)r * K + j] = use[j];
-            p.w[(int64_t)r * K + j] = l_sel[j] / den;
-            if (p.cap_idx) p.cap_idx[(int64_t)r * K + j] = own[j];
-            if (p.cap_w) p.cap_w[(int64_t)r * K + j] = l_sel[j] / den;
-        }
-    }
-    __syncthreads();
-
-    // ---- 2. per 64-pair chunk: rank of each pair among equal experts before
-    // it in the chunk, and the chunk's histogram
+    // per 64-pair chunk: rank of each pair among equal experts before it in
+    // the chunk, and the chunk's histogram
     const int nchunk = (NP + 63) / 64;
     for (int c = wave; c < nchunk; c += nw) {
         const int pi = c * 64 + lane;
@@ -92,7 +112,7 @@ __global__ __launch_bounds__(1024) void route_group_kernel(MoeParams p) {
     }
     __syncthreads();
 
-    // ---- 3. per expert: exclusive prefix of the chunk histograms, counts
+    // per expert: exclusive prefix of the chunk histograms, counts
     for (int e = tid; e < E; e += blockDim.x) {
         int run = 0;
         for (int c = 0; c < nchunk; ++c) {
@@ -141,7 +161,7 @@ __global__ __launch_bounds__(1024) void route_group_kernel(MoeParams p) {
     }
     __syncthreads();
 
-    // ---- 4. scatter: grouped position of every pair
+    // scatter: grouped position of every pair
     for (int pi = tid; pi < NP; pi += blockDim.x) {
         const int e = p.idx[pi];
         const int pos = p.offsets[e] + p.hist[(int64_t)(pi / 64) * E + e] + p.rank[pi];
@@ -157,6 +177,66 @@ __global__ __launch_bounds__(1024) void route_group_kernel(MoeParams p) {
         for (int e = tid; e <= E; e += blockDim.x) p.cap_offsets[e] = p.offsets[e];
     if (p.cap_perm)
         for (int i = tid; i < NP; i += blockDim.x) p.cap_perm[i] = p.perm[i];
+}
+
+// Routing of many rows: logits come from a separate router GEMV.
+__global__ __launch_bounds__(1024) void route_group_kernel(MoeParams p) {
+    topk_rows(p, p.logits, p.n_experts);
+    __syncthreads();
+    group_pairs(p);
+}
+
+// Routing of up to 32 rows with the router GEMV done by the same workgroup:
+// wave w computes tile w % T of the router over k-split w / T (T = E/16
+// tiles), the k-splits are summed in a fixed order in LDS, and top-k reads
+// the logits from LDS.
+template <int FMT, int XT>
+__global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const uint8_t* router, int H,
+                                                            const uint16_t* x, int64_t ldx) {
+    constexpr int CB = Geom<FMT>::CB;
+    __shared__ float4v red[2048];  // k-split partials, then the logits [32][E <= 256]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int E = p.n_experts, T = E / 16;
+    const int nks = 16 / T;
+    const int tile = wave % T, ks = wave / T;
+    const int64_t nch = n_chunks_dev<FMT>(H);
+    const int cper = (int)((nch + nks - 1) / nks);
+    const int c0 = ks * cper;
+    const int c1 = ks < nks ? (int)min((int64_t)(c0 + cper), nch) : c0;
+    float4v acc[1][XT];
+#pragma unroll
+    for (int xt = 0; xt < XT; ++xt) acc[0][xt] = float4v{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* tp[1] = {router + (int64_t)tile * nch * CB};
+    XDirect xs{x, ldx, p.rows};
+    kloop<FMT, 1, XT>(tp, c0, c1, xs, 0, H / 32, lane, acc);
+#pragma unroll
+    for (int xt = 0; xt < XT; ++xt) red[(wave * XT + xt) * 64 + lane] = acc[0][xt];
+    __syncthreads();
+    float lgv[XT][4];
+    if (wave < T) {
+#pragma unroll
+        for (int xt = 0; xt < XT; ++xt) {
+            float4v a = red[(wave * XT + xt) * 64 + lane];
+            for (int o = 1; o < nks; ++o) a += red[((wave + o * T) * XT + xt) * 64 + lane];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) lgv[xt][v] = a[v];
+        }
+    }
+    __syncthreads();
+    float* lg = (float*)red;  // [32][E] logits
+    if (wave < T) {
+#pragma unroll
+        for (int xt = 0; xt < XT; ++xt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int tok = 16 * xt + 4 * (lane >> 4) + v;
+                lg[tok * E + wave * 16 + (lane & 15)] = lgv[xt][v];
+            }
+    }
+    __syncthreads();
+    topk_rows(p, lg, E);
+    __syncthreads();
+    group_pairs(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -246,15 +326,31 @@ __global__ __launch_bounds__(256) void grouped_kernel(GroupedParams p) {
 
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     __shared__ float red[8];
+    __shared__ float w_s[8];
+    __shared__ int slot_s[16];
     const int r = blockIdx.x, tid = threadIdx.x;
-    const int K = p.top_k, R = p.rows, H = p.hidden;
+    const int K = p.top_k, R = p.rows, H = p.hidden, S = p.n_shared;
+    if (tid < K) {
+        w_s[tid] = p.w[r * K + tid];
+        slot_s[tid] = p.inv[r * K + tid];
+    } else if (tid >= 64 && tid < 64 + S) {
+        slot_s[8 + tid - 64] = p.np + (tid - 64) * R + r;
+    }
+    __syncthreads();
     uint16_t* h16 = (uint16_t*)p.h + (int64_t)r * p.ldh;
     float* h32 = (float*)p.h + (int64_t)r * p.ldh;
     float ss = 0.f;
     for (int col = tid; col < H; col += blockDim.x) {
+        float ys[8], yr[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) ys[s] = s < S ? p.y[(int64_t)slot_s[8 + s] * H + col] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) yr[j] = j < K ? p.y[(int64_t)slot_s[j] * H + col] : 0.f;
         float acc = 0.f;
-        for (int s = 0; s < p.n_shared; ++s) acc += p.y[((int64_t)p.np + s * R + r) * H + col];
-        for (int j = 0; j < K; ++j) acc = fmaf(p.w[r * K + j], p.y[(int64_t)p.inv[r * K + j] * H + col], acc);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc += ys[s];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = fmaf(j < K ? w_s[j] : 0.f, yr[j], acc);
         float hr;
         if (p.h_f32) {
             hr = p.add_residual ? h32[col] + acc : acc;
@@ -379,8 +475,49 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
                 hipStream_t s) {
     const int E = w->n_experts, K = w->top_k, S = w->n_shared, F = w->d_ff, H = w->hidden;
     const int NP = rows * K;
-    // router logits
-    {
+    MoeParams p{};
+    p.rows = rows;
+    p.n_experts = E;
+    p.top_k = K;
+    p.n_shared = S;
+    p.logits = m.logits;
+    p.bias = w->router_bias;
+    p.forced = forced;
+    p.idx = m.idx;
+    p.w = m.w;
+    p.rank = m.rank;
+    p.hist = m.hist;
+    p.counts = m.counts;
+    p.offsets = m.offsets;
+    p.perm = m.perm;
+    p.inv = m.inv;
+    p.slot_row = m.slot_row;
+    p.n_virt = m.n_virt;
+    p.virt_expert = m.virt_expert;
+    p.virt_off = m.virt_off;
+    p.virt_cnt = m.virt_cnt;
+    p.cap_idx = cap_idx ? cap_idx : (cap ? cap->topk_idx : nullptr);
+    p.cap_w = cap_w ? cap_w : (cap ? cap->topk_w : nullptr);
+    p.cap_counts = cap ? cap->counts : nullptr;
+    p.cap_offsets = cap ? cap->offsets : nullptr;
+    p.cap_perm = cap ? cap->perm : nullptr;
+    if (rows <= 32 && E % 16 == 0 && E <= 256) {
+        // router GEMV, top-k and grouping in one workgroup
+        const uint8_t* rw = (const uint8_t*)w->router.data;
+        const bool two = rows > 16;
+#define OCR_R(F_)                                                                                               \
+    case F_:                                                                                                    \
+        if (two) hipLaunchKernelGGL((route_fused_kernel<F_, 2>), dim3(1), dim3(1024), 0, s, p, rw, H, x, ldx); \
+        else hipLaunchKernelGGL((route_fused_kernel<F_, 1>), dim3(1), dim3(1024), 0, s, p, rw, H, x, ldx);     \
+        break;
+        switch (w->router.fmt) {
+            OCR_R(OCRDEC_F16)
+            OCR_R(OCRDEC_Q8_0)
+            OCR_R(OCRDEC_Q4_0)
+            OCR_R(OCRDEC_U8A_G32)
+        }
+#undef OCR_R
+    } else {
         GemvPlan pl = plan_gemv(w->router.fmt, E, H, rows, EPI_F32);
         GemvParams gp{};
         gp.w = (const uint8_t*)w->router.data;
@@ -391,35 +528,6 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         gp.y = m.logits;
         gp.ldy = E;
         launch_gemv(w->router.fmt, EPI_F32, pl, gp, s);
-    }
-    // routing + grouping
-    {
-        MoeParams p{};
-        p.rows = rows;
-        p.n_experts = E;
-        p.top_k = K;
-        p.n_shared = S;
-        p.logits = m.logits;
-        p.bias = w->router_bias;
-        p.forced = forced;
-        p.idx = m.idx;
-        p.w = m.w;
-        p.rank = m.rank;
-        p.hist = m.hist;
-        p.counts = m.counts;
-        p.offsets = m.offsets;
-        p.perm = m.perm;
-        p.inv = m.inv;
-        p.slot_row = m.slot_row;
-        p.n_virt = m.n_virt;
-        p.virt_expert = m.virt_expert;
-        p.virt_off = m.virt_off;
-        p.virt_cnt = m.virt_cnt;
-        p.cap_idx = cap_idx ? cap_idx : (cap ? cap->topk_idx : nullptr);
-        p.cap_w = cap_w ? cap_w : (cap ? cap->topk_w : nullptr);
-        p.cap_counts = cap ? cap->counts : nullptr;
-        p.cap_offsets = cap ? cap->offsets : nullptr;
-        p.cap_perm = cap ? cap->perm : nullptr;
         hipLaunchKernelGGL(route_group_kernel, dim3(1), dim3(1024), 0, s, p);
     }
     const int max_virt = std::min(E, NP) + S;

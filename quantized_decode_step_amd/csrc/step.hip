@@ -35,11 +35,13 @@ OCR_DEV void norm_row(const float* h, const uint16_t* gamma, int H, float eps, u
 // h[r] = embed[tok[r]] (fp16 table) or src[r] (fp32); x[r] = norm(h[r]).
 __global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tok, const uint16_t* embed, int vocab,
                                                          const float* src, float* h, const uint16_t* gamma,
-                                                         int H, float eps, uint16_t* x, int* lm_counter) {
+                                                         int H, float eps, uint16_t* x, int* counters,
+                                                         int n_counters) {
     __shared__ float red[8];
     const int r = blockIdx.x;
-    // the language-head argmax of this step counts arriving workgroups from zero
-    if (r == 0 && threadIdx.x == 0 && lm_counter) *lm_counter = 0;
+    // the step's single-launch reductions count arriving workgroups from zero
+    if (r == 0)
+        for (int i = threadIdx.x; i < n_counters; i += blockDim.x) counters[i] = 0;
     float* hr = h + (int64_t)r * H;
     if (tok) {
         int t = tok[r];
@@ -54,13 +56,6 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tok, con
     norm_row(hr, gamma, H, eps, x + (int64_t)r * H, red);
 }
 
-__global__ __launch_bounds__(256) void norm_kernel(const float* h, const uint16_t* gamma, int H, float eps,
-                                                   uint16_t* x) {
-    __shared__ float red[8];
-    const int r = blockIdx.x;
-    norm_row(h + (int64_t)r * H, gamma, H, eps, x + (int64_t)r * H, red);
-}
-
 __global__ void copy_rows_kernel(const float* src, float* dst, int64_t n) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         dst[i] = src[i];
@@ -71,7 +66,12 @@ __global__ void bump_kernel(int32_t* gen_index, int rows) {
     if (r < rows) gen_index[r] += 1;
 }
 
+// Arrival counters of the step's single-launch reductions.
+enum { CTR_LM = 0, CTR_NORM = 1, CTR_ATTN = 2 };
+
 struct StepWs {
+    int* counters;  // CTR_LM, CTR_NORM, then [rows][n_heads] for attention
+    int n_counters;
     float* h;
     uint16_t* x;
     float* qkv;
@@ -98,6 +98,8 @@ StepWs carve_step(void* ws, const ocrdec_model* m, int rows, int cache_cap) {
         if (m->layers[l].is_moe) moe = &m->layers[l].moe;
         else dense_ff = std::max(dense_ff, m->layers[l].dense_ff);
     }
+    w.n_counters = CTR_ATTN + rows * m->n_heads;
+    w.counters = cv.take<int>(w.n_counters);
     w.h = cv.take<float>((size_t)rows * H);
     w.x = cv.take<uint16_t>((size_t)rows * H);
     w.qkv = cv.take<float>((size_t)rows * 3 * HD);
@@ -198,13 +200,8 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     hipStream_t s = (hipStream_t)stream;
     StepWs w = carve_step(ws, m, R, cache_cap);
 
-    int* lm_counter = nullptr;
-    if (m->lm_head.data) {
-        const int g = lm_grid(m, R);
-        lm_counter = (int*)((char*)w.lm_part + argmax_ws_bytes(g, R) - 256);
-    }
     hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(256), 0, s, tok_in, m->embed, m->vocab, hidden, w.h,
-                       m->layers[0].attn_norm, H, m->norm_eps, w.x, lm_counter);
+                       m->layers[0].attn_norm, H, m->norm_eps, w.x, w.counters, w.n_counters);
     int moe_l = 0;
     for (int l = 0; l < m->n_layers; ++l) {
         const ocrdec_layer& L = m->layers[l];
@@ -244,6 +241,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             ap.ld_out = HD;
             ap.n_split = attn_n_split(cache_cap);
             ap.part = w.attn_part;
+            ap.counters = w.counters + CTR_ATTN;
             launch_attn(ap, s);
         }
         // O projection + residual
@@ -257,9 +255,12 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             gp.xs = XDirect{w.o, HD, R};
             gp.y = w.h;
             gp.ldy = H;
+            gp.norm_w = L.ffn_norm;  // the last workgroup normalises h for the MLP/MoE
+            gp.eps = m->norm_eps;
+            gp.norm_out = w.x;
+            gp.counter = w.counters + CTR_NORM;
             launch_gemv(L.wo.fmt, EPI_RESID, pl, gp, s);
         }
-        hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(256), 0, s, w.h, L.ffn_norm, H, m->norm_eps, w.x);
         if (L.is_moe) {
             const int K = L.moe.top_k;
             int32_t* ci = cap && cap->topk_idx ? cap->topk_idx + (int64_t)moe_l * R * K : nullptr;
@@ -292,9 +293,12 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                 gp.xs = XDirect{w.a, F, R};
                 gp.y = w.h;
                 gp.ldy = H;
+                gp.norm_w = next_norm;  // NULL after the last layer without an LM head
+                gp.eps = m->norm_eps;
+                gp.norm_out = w.x;
+                gp.counter = w.counters + CTR_NORM;
                 launch_gemv(L.dense_down.fmt, EPI_RESID, pl, gp, s);
             }
-            if (next_norm) hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(256), 0, s, w.h, next_norm, H, m->norm_eps, w.x);
         }
     }
     if (hidden) {
@@ -311,7 +315,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
         gp.nchunks = n_chunks(m->lm_head.fmt, H);
         gp.xs = XDirect{w.x, H, R};
         gp.part = w.lm_part;
-        gp.counter = (int*)((char*)w.lm_part + argmax_ws_bytes(pl.grid, R) - 256);
+        gp.counter = w.counters + CTR_LM;
         gp.tok_out = tok_out;
         gp.top2 = cap ? cap->lm_top2 : nullptr;
         gp.gen_index = st->gen_index;

@@ -113,9 +113,11 @@ def _attn_case(q, rows, NH, D, prefix_cap, ring_cap, prefix_len, gen_index, sink
                    pl.data_ptr(), gi.data_ptr(), sk.data_ptr() if sk is not None else None, 10000.0,
                    float(1 / np.sqrt(D)), out.data_ptr(), NH * D)
     wsb = q.ocrdec_attn_workspace_bytes(a)
-    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
     q.ocrdec_attn_decode(a, ws, wsb)
     torch.cuda.synchronize()
+    # the call leaves its arrival counters at zero, so the workspace is reusable as is
+    assert int(ws.view(torch.int32)[-(rows * NH):].abs().sum().item()) == 0
     got = from_f16_tensor(out)
     kc_after = kd.cpu().numpy().view(np.float16)
     vc_after = vd.cpu().numpy().view(np.float16)
