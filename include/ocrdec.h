@@ -129,10 +129,8 @@ ocrdec_status ocrdec_gemv_q(const ocrdec_qmat* W, int32_t rows, const uint16_t* 
  *   tok_out  int32 [rows]
  *   top2     fp32 [rows][2] (best and second-best logit) or NULL
  *   rows     1 .. 32
- * Workspace: ocrdec_lm_argmax_workspace_bytes; it must be zero-filled before
- * its first use, and every call leaves it zero-filled again (its last word
- * counts the workgroups that have finished, so that the last one can merge
- * their partial results without a second launch).
+ * Workspace: ocrdec_lm_argmax_workspace_bytes (per-workgroup partial
+ * results, merged by a second short kernel).
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE. */
 ocrdec_status ocrdec_lm_argmax_workspace_bytes(const ocrdec_qmat* W, int32_t rows, size_t* bytes);
 ocrdec_status ocrdec_lm_argmax(const ocrdec_qmat* W, int32_t rows, const uint16_t* x, int32_t* tok_out,
@@ -175,11 +173,7 @@ ocrdec_status ocrdec_lm_argmax(const ocrdec_qmat* W, int32_t rows, const uint16_
  * sink and value 0 (its constant-1 query lane folded into a logit).
  *
  * gen_index and prefix_len are read, never written.
- * head_dim: 64 or 128.  rows >= 1.  Workspace: ocrdec_attn_workspace_bytes;
- * it must be zero-filled before its first use and every call leaves it
- * zero-filled again where it matters (its tail holds per-(row, head) arrival
- * counters: the last of a head's key splits to finish merges them, so the
- * whole attention is one launch).
+ * head_dim: 64 or 128.  rows >= 1.  Workspace: ocrdec_attn_workspace_bytes.
  * Errors: INVALID_ARG (NULL pointers, head_dim, ld_* too small, caps),
  * WORKSPACE (too small), DEVICE. */
 typedef struct {

@@ -8,9 +8,10 @@
 //
 // Split-KV: workgroup (split, head, row) scores up to 64 keys of the row's
 // window, keeps them in LDS, and writes an unnormalised partial (max, sum,
-// sum of p*v); the last split of a (row, head) to finish (an arrival counter
-// in the workspace) merges the splits with the usual log-sum-exp rescaling,
-// so one launch does the whole attention.  Keys are streamed with one 16-byte load per lane:
+// sum of p*v); a combine kernel merges the splits with the usual
+// log-sum-exp rescaling.  (A last-arriving-workgroup merge inside the first
+// kernel was measured slower: device-scope fences and the arrival atomics cost
+// more than a second launch.)  Keys are streamed with one 16-byte load per lane:
 // for head_dim 128 a wavefront load covers 4 keys (16 lanes per key), for 64
 // it covers 8 keys.
 #include "attn.hpp"
@@ -57,14 +58,17 @@ OCR_DEV int ord_to_idx(const AttnParams& p, const Window& w, int o) {
     return o;
 }
 
-// RoPE (rotate-half) of lane pair (i, i + D/2) at position pos; the angle is
-// formed in double so large positions keep full precision.
+// RoPE (rotate-half) of lane pair (i, i + D/2) at position pos.  The angle
+// pos * theta^(-2i/D) is formed and reduced modulo 2*pi in double (positions
+// reach thousands of radians), then rotated with a float sincos on [-pi, pi].
 OCR_DEV void rope_pair(float x1, float x2, int i, int D, int pos, float theta, float& y1, float& y2) {
     const double f = exp2(-(2.0 * i / D) * log2((double)theta));
     const double a = (double)pos * f;
-    double s, c;
-    sincos(a, &s, &c);
-    const float cf = (float)c, sf = (float)s;
+    const double two_pi_hi = 6.283185307179586232, two_pi_lo = 2.4492935982947064e-16;
+    const double n = rint(a * 0.15915494309189535);
+    const double red = fma(-n, two_pi_lo, fma(-n, two_pi_hi, a));
+    float sf, cf;
+    sincosf((float)red, &sf, &cf);
     y1 = x1 * cf - x2 * sf;
     y2 = x2 * cf + x1 * sf;
 }
@@ -187,51 +191,60 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
         part[D + 1] = red_s[1];
     }
 
-    // ---- the last split of (row, head) to finish merges all of them
-    __shared__ int is_last;
+}
+
+// Merge of the splits of one (head, row): the max and sums of every split are
+// loaded in parallel into LDS, then each thread (one per output lane) sums the
+// rescaled partial outputs with independent loads.
+template <int D>
+__global__ __launch_bounds__(D) void attn_combine_kernel(AttnParams p) {
     __shared__ float f_s[1024 + 1];
+    __shared__ float red[2];
+    const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+    const Window w = row_window(p, r);
     const int n_used = (w.nkeys + KPS - 1) / KPS;
-    int* ctr = p.counters + (int64_t)r * p.n_heads + h;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) is_last = (atomicAdd(ctr, 1) == n_used - 1);
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
     const float* part0 = p.part + ((int64_t)r * p.n_heads + h) * p.n_split * (D + 2);
-    for (int i = tid; i < n_used; i += blockDim.x) f_s[i] = __builtin_nontemporal_load(part0 + i * (D + 2) + D);
+    for (int i = tid; i < n_used; i += D) f_s[i] = part0[i * (D + 2) + D];
     __syncthreads();
-    if (wave == 0) {
+    if (tid < 64) {
         float M = -INFINITY;
-        for (int i = lane; i < n_used; i += 64) M = fmaxf(M, f_s[i]);
+        for (int i = tid; i < n_used; i += 64) M = fmaxf(M, f_s[i]);
         M = wave_max(M);
-        float L = 0.f;
-        for (int i = lane; i < n_used; i += 64) {
-            const float f = __expf(f_s[i] - M);
-            L = fmaf(__builtin_nontemporal_load(part0 + i * (D + 2) + D + 1), f, L);
-            f_s[i] = f;
-        }
-        L = wave_sum(L);
-        if (lane == 0) f_s[1024] = 1.0f / L;
+        if (tid == 0) red[0] = M;
     }
     __syncthreads();
-    if (tid < D) {
-        float o = 0.f;
-        int i = 0;
-        for (; i + 4 <= n_used; i += 4) {
-            const float a0 = __builtin_nontemporal_load(part0 + (i + 0) * (D + 2) + tid);
-            const float a1 = __builtin_nontemporal_load(part0 + (i + 1) * (D + 2) + tid);
-            const float a2 = __builtin_nontemporal_load(part0 + (i + 2) * (D + 2) + tid);
-            const float a3 = __builtin_nontemporal_load(part0 + (i + 3) * (D + 2) + tid);
-            o = fmaf(a0, f_s[i], o);
-            o = fmaf(a1, f_s[i + 1], o);
-            o = fmaf(a2, f_s[i + 2], o);
-            o = fmaf(a3, f_s[i + 3], o);
-        }
-        for (; i < n_used; ++i) o = fmaf(__builtin_nontemporal_load(part0 + i * (D + 2) + tid), f_s[i], o);
-        p.out[(int64_t)r * p.ld_out + h * D + tid] = f2h(o * f_s[1024]);
+    const float M = red[0];
+    float Lp = 0.f;
+    for (int i = tid; i < n_used; i += D) {
+        const float f = __expf(f_s[i] - M);
+        Lp = fmaf(part0[i * (D + 2) + D + 1], f, Lp);
+        f_s[i] = f;
     }
-    if (tid == 0) *ctr = 0;
+    if (D == 64) {
+        Lp = wave_sum(Lp);
+        if (tid == 0) red[1] = Lp;
+    } else {
+        Lp = wave_sum(Lp);
+        __shared__ float l2[2];
+        if ((tid & 63) == 0) l2[tid >> 6] = Lp;
+        __syncthreads();
+        if (tid == 0) red[1] = l2[0] + l2[1];
+    }
+    __syncthreads();
+    float o = 0.f;
+    int i = 0;
+    for (; i + 4 <= n_used; i += 4) {
+        const float a0 = part0[(i + 0) * (D + 2) + tid];
+        const float a1 = part0[(i + 1) * (D + 2) + tid];
+        const float a2 = part0[(i + 2) * (D + 2) + tid];
+        const float a3 = part0[(i + 3) * (D + 2) + tid];
+        o = fmaf(a0, f_s[i], o);
+        o = fmaf(a1, f_s[i + 1], o);
+        o = fmaf(a2, f_s[i + 2], o);
+        o = fmaf(a3, f_s[i + 3], o);
+    }
+    for (; i < n_used; ++i) o = fmaf(part0[i * (D + 2) + tid], f_s[i], o);
+    p.out[(int64_t)r * p.ld_out + h * D + tid] = f2h(o / red[1]);
 }
 
 int attn_n_split(int cache_cap) { return (cache_cap + KPS - 1) / KPS; }
@@ -241,13 +254,19 @@ size_t attn_part_bytes(int rows, int n_heads, int head_dim, int cache_cap) {
 }
 
 size_t attn_ws_bytes(int rows, int n_heads, int head_dim, int cache_cap) {
-    return attn_part_bytes(rows, n_heads, head_dim, cache_cap) + align256((size_t)rows * n_heads * sizeof(int));
+    return attn_part_bytes(rows, n_heads, head_dim, cache_cap);
 }
 
 void launch_attn(const AttnParams& p, hipStream_t s) {
     dim3 g1(p.n_split, p.n_heads, p.rows);
-    if (p.head_dim == 128) hipLaunchKernelGGL(attn_partial_kernel<128>, g1, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(attn_partial_kernel<64>, g1, dim3(256), 0, s, p);
+    dim3 g2(p.n_heads, p.rows);
+    if (p.head_dim == 128) {
+        hipLaunchKernelGGL(attn_partial_kernel<128>, g1, dim3(256), 0, s, p);
+        hipLaunchKernelGGL(attn_combine_kernel<128>, g2, dim3(128), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(attn_partial_kernel<64>, g1, dim3(256), 0, s, p);
+        hipLaunchKernelGGL(attn_combine_kernel<64>, g2, dim3(64), 0, s, p);
+    }
 }
 
 ocrdec_status check_attn(const ocrdec_attn_args* a) {
@@ -308,7 +327,6 @@ extern "C" ocrdec_status ocrdec_attn_decode(const ocrdec_attn_args* a, void* ws,
     p.ld_out = a->ld_out;
     p.n_split = attn_n_split(cap);
     p.part = (float*)ws;
-    p.counters = (int*)((char*)ws + attn_part_bytes(a->rows, a->n_heads, a->head_dim, cap));
     launch_attn(p, (hipStream_t)stream);
     return launch_status("ocrdec_attn_decode");
 }

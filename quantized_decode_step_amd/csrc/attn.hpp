@@ -20,7 +20,6 @@ struct AttnParams {
     int64_t ld_out;
     int n_split;
     float* part;    // [rows][n_heads][n_split][head_dim + 2]
-    int* counters;  // [rows][n_heads] arrival counters: zero on entry, left zero
 };
 
 int attn_n_split(int cache_cap);

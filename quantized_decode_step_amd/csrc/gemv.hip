@@ -5,63 +5,6 @@
 
 namespace ocrdec {
 
-// Last-arriving workgroup of an argmax launch: merges every workgroup's
-// (best, index, second) per token in workgroup order, writes the tokens, and
-// resets the arrival counter for the next launch.
-OCR_DEV void argmax_finish(const GemvParams& p) {
-    __shared__ int is_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) is_last = (atomicAdd(p.counter, 1) == (int)gridDim.x - 1);
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    for (int r = threadIdx.x; r < p.xs.rows; r += blockDim.x) {
-        float b = -INFINITY, s = -INFINITY;
-        int bi = 0x7fffffff;
-        for (int w = 0; w < (int)gridDim.x; ++w) {
-            const float* e = p.part + ((int64_t)w * p.xs.rows + r) * 3;
-            argmax_merge(b, bi, s, __builtin_nontemporal_load(e), __float_as_int(__builtin_nontemporal_load(e + 1)),
-                         __builtin_nontemporal_load(e + 2));
-        }
-        if (p.tok_out) p.tok_out[r] = (bi == 0x7fffffff) ? 0 : bi;
-        if (p.top2) {
-            p.top2[2 * r] = b;
-            p.top2[2 * r + 1] = s;
-        }
-        if (p.gen_index) p.gen_index[r] += 1;
-    }
-    if (threadIdx.x == 0) *p.counter = 0;
-}
-
-// Last-arriving workgroup of a residual-update launch: RMSNorm of every
-// updated row into norm_out (the next block's fp16 input), then resets the
-// arrival counter.  One wavefront per row.
-OCR_DEV void resid_norm_finish(const GemvParams& p) {
-    __shared__ int is_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) is_last = (atomicAdd(p.counter, 1) == (int)gridDim.x - 1);
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    const float* h = (const float*)p.y;
-    for (int r = wave; r < p.xs.rows; r += nw) {
-        const float* hr = h + (int64_t)r * p.ldy;
-        float ss = 0.f;
-        for (int c = lane; c < p.n; c += 64) {
-            const float v = __builtin_nontemporal_load(hr + c);
-            ss = fmaf(v, v, ss);
-        }
-        ss = wave_sum(ss);
-        const float inv = 1.0f / sqrtf(ss / (float)p.n + p.eps);
-        for (int c = lane; c < p.n; c += 64)
-            p.norm_out[(int64_t)r * p.n + c] = f2h(__builtin_nontemporal_load(hr + c) * inv * h2f(p.norm_w[c]));
-    }
-    if (threadIdx.x == 0) *p.counter = 0;
-}
-
 template <int FMT, int NT, int XT, int KS, int EPI>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
     constexpr int CB = Geom<FMT>::CB;
@@ -171,7 +114,6 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
                     out[2] = s;
                 }
             }
-            if (tok0 + 16 * XT >= p.xs.rows) argmax_finish(p);
         } else if (owner) {
 #pragma unroll
             for (int xt = 0; xt < XT; ++xt)
@@ -203,9 +145,6 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
                     }
                 }
         }
-        if constexpr (EPI == EPI_RESID) {
-            if (p.norm_w && tok0 + 16 * XT >= p.xs.rows) resid_norm_finish(p);
-        }
         __syncthreads();
     }
 }
@@ -229,7 +168,7 @@ void launch_fmt(const GemvParams& p, int nt, int ks, int xt, hipStream_t s) {
     if constexpr (EPI == EPI_GLU) {
         OCR_L(2, 1, 1) OCR_L(2, 1, 2) OCR_L(2, 4, 1) OCR_L(2, 4, 2)
     } else {
-        OCR_L(1, 4, 1) OCR_L(1, 4, 2) OCR_L(1, 1, 1) OCR_L(1, 1, 2)
+        OCR_L(1, 4, 1) OCR_L(1, 4, 2) OCR_L(4, 1, 1) OCR_L(4, 1, 2)
     }
 #undef OCR_L
 }
@@ -245,9 +184,9 @@ GemvPlan plan_gemv(int fmt, int n, int k, int rows, int epi) {
         pl.groups = (int)(tiles / 2);
         pl.ks = pl.groups >= 512 ? 1 : 4;
     } else if (tiles >= 1024) {
-        pl.nt = 1;
+        pl.nt = 4;
         pl.ks = 1;
-        pl.groups = (int)tiles;
+        pl.groups = (int)((tiles + 3) / 4);
     } else {
         pl.nt = 1;
         pl.ks = 4;
@@ -280,7 +219,51 @@ void launch_gemv(int fmt, int epi, const GemvPlan& pl, GemvParams p, hipStream_t
 #undef OCR_E
 }
 
-size_t argmax_ws_bytes(int grid, int rows) { return align256((size_t)grid * rows * 3 * sizeof(float)) + 256; }
+size_t argmax_ws_bytes(int grid, int rows) { return align256((size_t)grid * rows * 3 * sizeof(float)); }
+
+// Merge of the per-workgroup (best, index, second) partials: one workgroup
+// per row, a strided pass then a tree in LDS (the merge is associative and
+// commutative, so the result does not depend on the order).
+__global__ __launch_bounds__(256) void argmax_final_kernel(const float* part, int n_wg, int rows, int32_t* tok_out,
+                                                           float* top2, int32_t* gen_index) {
+    __shared__ float sb[256], ss[256];
+    __shared__ int si[256];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    float b = -INFINITY, s = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int w = tid; w < n_wg; w += blockDim.x) {
+        const float* e = part + ((int64_t)w * rows + r) * 3;
+        argmax_merge(b, bi, s, e[0], __float_as_int(e[1]), e[2]);
+    }
+    sb[tid] = b;
+    ss[tid] = s;
+    si[tid] = bi;
+    __syncthreads();
+    for (int o = blockDim.x / 2; o > 0; o >>= 1) {
+        if (tid < o) {
+            float b2 = sb[tid], s2 = ss[tid];
+            int i2 = si[tid];
+            argmax_merge(b2, i2, s2, sb[tid + o], si[tid + o], ss[tid + o]);
+            sb[tid] = b2;
+            ss[tid] = s2;
+            si[tid] = i2;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        if (tok_out) tok_out[r] = (si[0] == 0x7fffffff) ? 0 : si[0];
+        if (top2) {
+            top2[2 * r] = sb[0];
+            top2[2 * r + 1] = ss[0];
+        }
+        if (gen_index) gen_index[r] += 1;
+    }
+}
+
+void launch_argmax_final(const float* part, int n_wg, int rows, int32_t* tok_out, float* top2, int32_t* gen_index,
+                         hipStream_t s) {
+    hipLaunchKernelGGL(argmax_final_kernel, dim3(rows), dim3(256), 0, s, part, n_wg, rows, tok_out, top2, gen_index);
+}
 
 }  // namespace ocrdec
 
@@ -339,9 +322,7 @@ extern "C" ocrdec_status ocrdec_lm_argmax(const ocrdec_qmat* W, int32_t rows, co
     p.nchunks = n_chunks(W->fmt, W->k);
     p.xs = XDirect{x, W->k, rows};
     p.part = (float*)ws;
-    p.counter = (int*)((char*)ws + need - 256);
-    p.tok_out = tok_out;
-    p.top2 = top2;
     launch_gemv(W->fmt, EPI_ARGMAX, pl, p, (hipStream_t)stream);
+    launch_argmax_final((float*)ws, pl.grid, rows, tok_out, top2, nullptr, (hipStream_t)stream);
     return launch_status("ocrdec_lm_argmax");
 }

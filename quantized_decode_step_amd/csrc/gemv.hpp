@@ -16,14 +16,6 @@ struct GemvParams {
     int64_t ldy;
     int half_tiles;   // EPI_GLU: tiles in the gate half (= d_ff / 16)
     float* part;      // EPI_ARGMAX: [grid][rows][3] (best, index bits, second)
-    int* counter;     // EPI_ARGMAX, and EPI_RESID with norm_w: zero on entry; the last
-                      // workgroup to finish does the follow-up work and resets it
-    const uint16_t* norm_w;  // EPI_RESID: RMSNorm gain applied to the updated residual, or NULL
-    float eps;
-    uint16_t* norm_out;      // fp16 [rows][n] normalised residual
-    int32_t* tok_out; // EPI_ARGMAX outputs
-    float* top2;
-    int32_t* gen_index;
     int n_groups;
 };
 
@@ -33,9 +25,9 @@ struct GemvPlan {
 
 GemvPlan plan_gemv(int fmt, int n, int k, int rows, int epi);
 void launch_gemv(int fmt, int epi, const GemvPlan& pl, GemvParams p, hipStream_t s);
-// Argmax workspace: partials, then the arrival counter (must be zero before
-// the first use; every launch leaves it zero).
 size_t argmax_ws_bytes(int grid, int rows);
+void launch_argmax_final(const float* part, int n_wg, int rows, int32_t* tok_out, float* top2, int32_t* gen_index,
+                         hipStream_t s);
 
 // Merge of two (best, index, second) argmax states; ties go to the lower index.
 OCR_DEV void argmax_merge(float& b, int& bi, float& s, float ob, int oi, float os) {

@@ -145,8 +145,7 @@ struct XGather {
 
 // Loads the A fragments of chunk c for tokens [tok0, tok0 + 16*XT).
 template <int FMT, int XT, class XS>
-OCR_DEV void load_xfrags(const XS& xs, int tok0, int c, int nblk, int lane, half8v (&xa)[Geom<FMT>::SB][XT],
-                         float4v (&xsum)[Geom<FMT>::SB][XT]) {
+OCR_DEV void load_xfrags(const XS& xs, int tok0, int c, int nblk, int lane, half8v (&xa)[Geom<FMT>::SB][XT]) {
     constexpr int SB = Geom<FMT>::SB;
 #pragma unroll
     for (int xt = 0; xt < XT; ++xt) {
@@ -159,47 +158,64 @@ OCR_DEV void load_xfrags(const XS& xs, int tok0, int c, int nblk, int lane, half
             xa[j][xt] = bits_to_half8(v);
         }
     }
+}
+
+// Per-token sums of each block's activations (int8-asymmetric only): an MFMA
+// against an all-ones B operand puts sum_k x[token][k] in every column.
+template <int FMT, int XT>
+OCR_DEV void xsums(const half8v (&xa)[Geom<FMT>::SB][XT], float4v (&xsum)[Geom<FMT>::SB][XT]) {
     if constexpr (FMT == OCRDEC_U8A_G32) {
         const half8v ones = {(f16_t)1, (f16_t)1, (f16_t)1, (f16_t)1, (f16_t)1, (f16_t)1, (f16_t)1, (f16_t)1};
         const float4v zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < SB; ++j)
+        for (int j = 0; j < Geom<FMT>::SB; ++j)
 #pragma unroll
             for (int xt = 0; xt < XT; ++xt) xsum[j][xt] = mfma16(xa[j][xt], ones, zero);
     }
 }
 
+// Prefetch depth that keeps the register ring near 96 VGPRs.
+template <int FMT, int NT, int XT>
+constexpr int kloop_depth() {
+    constexpr int regs = NT * 6 + Geom<FMT>::SB * XT * 4;
+    return regs * 4 <= 96 ? 4 : (regs * 3 <= 120 ? 3 : 2);
+}
+
 // The k-loop of one wavefront: NT tiles (tile[i] chunk pointers) over chunks
-// [c0, c1), accumulating into acc[NT][XT].  The loads of PF chunks are kept
-// in flight: the load of chunk c+PF is issued as soon as chunk c has been
-// consumed (a register ring indexed at compile time).
-template <int FMT, int NT, int XT, class XS, int PF = 4>
+// [c0, c1), accumulating into acc[NT][XT].  A register ring keeps PF chunks
+// in flight; each slot holds a chunk's weights AND its activation fragments,
+// loaded together, so waiting for the oldest slot (vector loads complete in
+// issue order) never waits for the younger prefetches.  The load of chunk
+// c+PF is issued as soon as chunk c has been consumed.
+template <int FMT, int NT, int XT, class XS, int PF = kloop_depth<FMT, NT, XT>()>
 OCR_DEV void kloop(const uint8_t* const (&tile)[NT], int c0, int c1, const XS& xs, int tok0, int nblk, int lane,
                    float4v (&acc)[NT][XT]) {
     constexpr int CB = Geom<FMT>::CB;
     constexpr int SB = Geom<FMT>::SB;
     if (c0 >= c1) return;
-    WRegs buf[PF][NT];
+    WRegs wb[PF][NT];
+    half8v xb[PF][SB][XT];
 #pragma unroll
     for (int u = 0; u < PF; ++u)
         if (c0 + u < c1) {
 #pragma unroll
-            for (int i = 0; i < NT; ++i) load_wchunk<FMT>(tile[i] + (int64_t)(c0 + u) * CB, lane, buf[u][i]);
+            for (int i = 0; i < NT; ++i) load_wchunk<FMT>(tile[i] + (int64_t)(c0 + u) * CB, lane, wb[u][i]);
+            load_xfrags<FMT, XT>(xs, tok0, c0 + u, nblk, lane, xb[u]);
         }
     for (int c = c0; c < c1; c += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
             const int cc = c + u;
             if (cc < c1) {
-                half8v xa[SB][XT];
                 float4v xsum[SB][XT];
-                load_xfrags<FMT, XT>(xs, tok0, cc, nblk, lane, xa, xsum);
+                xsums<FMT, XT>(xb[u], xsum);
 #pragma unroll
-                for (int i = 0; i < NT; ++i) chunk_mac<FMT, XT>(buf[u][i], xa, xsum, acc[i]);
+                for (int i = 0; i < NT; ++i) chunk_mac<FMT, XT>(wb[u][i], xb[u], xsum, acc[i]);
                 if (cc + PF < c1) {
 #pragma unroll
                     for (int i = 0; i < NT; ++i)
-                        load_wchunk<FMT>(tile[i] + (int64_t)(cc + PF) * CB, lane, buf[u][i]);
+                        load_wchunk<FMT>(tile[i] + (int64_t)(cc + PF) * CB, lane, wb[u][i]);
+                    load_xfrags<FMT, XT>(xs, tok0, cc + PF, nblk, lane, xb[u]);
                 }
             }
         }

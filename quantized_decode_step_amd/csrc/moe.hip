@@ -25,7 +25,7 @@ namespace ocrdec {
 // with ties to the lower index (a NaN logit counts as -inf).  Writes the
 // experts used (forced ones if given), their renormalised weights and the
 // captures.
-OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl) {
+OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl, int* idx_out) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int E = p.n_experts, K = p.top_k;
     for (int r = wave; r < p.rows; r += nw) {
@@ -76,7 +76,7 @@ OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl) {
         const float den = wave_sum(ex);
         if (lane < K) {
             const float w = ex / den;
-            p.idx[(int64_t)r * K + lane] = use;
+            idx_out[(int64_t)r * K + lane] = use;
             p.w[(int64_t)r * K + lane] = w;
             if (p.cap_idx) p.cap_idx[(int64_t)r * K + lane] = own;
             if (p.cap_w) p.cap_w[(int64_t)r * K + lane] = w;
@@ -84,9 +84,19 @@ OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl) {
     }
 }
 
+// Scratch of the grouping: LDS for decode-sized batches, the workspace
+// otherwise (generic pointers serve both).
+struct GroupScratch {
+    const int* idx;  // [NP] expert of every (row, rank) pair
+    int* rank;       // [NP]
+    int* hist;       // [nchunk][E]
+    int* counts;     // [E]
+    int* offsets;    // [E + 1]
+};
+
 // Stable counting sort of the (row, rank) pairs by expert and the list of
 // active experts (routed experts with tokens, then the shared experts).
-OCR_DEV void group_pairs(const MoeParams& p) {
+OCR_DEV void group_pairs(const MoeParams& p, const GroupScratch& g) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int R = p.rows, E = p.n_experts, K = p.top_k, S = p.n_shared;
     const int NP = R * K;
@@ -96,18 +106,18 @@ OCR_DEV void group_pairs(const MoeParams& p) {
     const int nchunk = (NP + 63) / 64;
     for (int c = wave; c < nchunk; c += nw) {
         const int pi = c * 64 + lane;
-        const int e = pi < NP ? p.idx[pi] : -1;
+        const int e = pi < NP ? g.idx[pi] : -1;
         int rank = 0;
         for (int i = 0; i < 64; ++i) {
             const int ei = __shfl(e, i, 64);
             rank += (i < lane && ei == e) ? 1 : 0;
         }
-        if (pi < NP) p.rank[pi] = rank;
+        if (pi < NP) g.rank[pi] = rank;
         for (int eb = 0; eb < E; eb += 64) {
             const int me = eb + lane;
             int cnt = 0;
             for (int i = 0; i < 64; ++i) cnt += (__shfl(e, i, 64) == me) ? 1 : 0;
-            if (me < E) p.hist[(int64_t)c * E + me] = cnt;
+            if (me < E) g.hist[(int64_t)c * E + me] = cnt;
         }
     }
     __syncthreads();
@@ -116,11 +126,11 @@ OCR_DEV void group_pairs(const MoeParams& p) {
     for (int e = tid; e < E; e += blockDim.x) {
         int run = 0;
         for (int c = 0; c < nchunk; ++c) {
-            const int h = p.hist[(int64_t)c * E + e];
-            p.hist[(int64_t)c * E + e] = run;
+            const int h = g.hist[(int64_t)c * E + e];
+            g.hist[(int64_t)c * E + e] = run;
             run += h;
         }
-        p.counts[e] = run;
+        g.counts[e] = run;
     }
     __syncthreads();
     // exclusive scan of counts and the compact list of active experts (wave 0)
@@ -128,7 +138,7 @@ OCR_DEV void group_pairs(const MoeParams& p) {
         int base = 0, act = 0;
         for (int eb = 0; eb < E; eb += 64) {
             const int e = eb + lane;
-            const int cnt = e < E ? p.counts[e] : 0;
+            const int cnt = e < E ? g.counts[e] : 0;
             int incl = cnt, ai = cnt > 0 ? 1 : 0;
             for (int o = 1; o < 64; o <<= 1) {
                 const int t = __shfl_up(incl, o, 64);
@@ -139,7 +149,7 @@ OCR_DEV void group_pairs(const MoeParams& p) {
                 }
             }
             const int excl = base + incl - cnt;
-            if (e < E) p.offsets[e] = excl;
+            if (e < E) g.offsets[e] = excl;
             if (e < E && cnt > 0) {
                 const int v = act + ai - 1;
                 p.virt_expert[v] = e;
@@ -150,7 +160,7 @@ OCR_DEV void group_pairs(const MoeParams& p) {
             act += __shfl(ai, 63, 64);
         }
         if (lane == 0) {
-            p.offsets[E] = base;
+            g.offsets[E] = base;
             for (int s = 0; s < S; ++s) {
                 p.virt_expert[act + s] = E + s;
                 p.virt_off[act + s] = NP + s * R;
@@ -163,8 +173,8 @@ OCR_DEV void group_pairs(const MoeParams& p) {
 
     // scatter: grouped position of every pair
     for (int pi = tid; pi < NP; pi += blockDim.x) {
-        const int e = p.idx[pi];
-        const int pos = p.offsets[e] + p.hist[(int64_t)(pi / 64) * E + e] + p.rank[pi];
+        const int e = g.idx[pi];
+        const int pos = g.offsets[e] + g.hist[(int64_t)(pi / 64) * E + e] + g.rank[pi];
         p.perm[pos] = pi;
         p.inv[pi] = pos;
         p.slot_row[pos] = pi / K;
@@ -172,31 +182,48 @@ OCR_DEV void group_pairs(const MoeParams& p) {
     for (int i = tid; i < S * R; i += blockDim.x) p.slot_row[NP + i] = i % R;
     __syncthreads();
     if (p.cap_counts)
-        for (int e = tid; e < E; e += blockDim.x) p.cap_counts[e] = p.counts[e];
+        for (int e = tid; e < E; e += blockDim.x) p.cap_counts[e] = g.counts[e];
     if (p.cap_offsets)
-        for (int e = tid; e <= E; e += blockDim.x) p.cap_offsets[e] = p.offsets[e];
+        for (int e = tid; e <= E; e += blockDim.x) p.cap_offsets[e] = g.offsets[e];
     if (p.cap_perm)
         for (int i = tid; i < NP; i += blockDim.x) p.cap_perm[i] = p.perm[i];
 }
 
 // Routing of many rows: logits come from a separate router GEMV.
 __global__ __launch_bounds__(1024) void route_group_kernel(MoeParams p) {
-    topk_rows(p, p.logits, p.n_experts);
+    topk_rows(p, p.logits, p.n_experts, p.idx);
     __syncthreads();
-    group_pairs(p);
+    group_pairs(p, GroupScratch{p.idx, p.rank, p.hist, p.counts, p.offsets});
 }
 
-// Routing of up to 32 rows with the router GEMV done by the same workgroup:
-// wave w computes tile w % T of the router over k-split w / T (T = E/16
-// tiles), the k-splits are summed in a fixed order in LDS, and top-k reads
-// the logits from LDS.
+// Routing of up to 32 rows in one workgroup.  Optionally it first forms the
+// MoE input x = fp16(RMSNorm(h) * gamma) from the fp32 residual (and writes
+// it for the expert kernels).  Router GEMV: wave w computes tile w % T over
+// k-split w / T (T = E/16 tiles), the k-splits are summed in a fixed order in
+// LDS; top-k reads the logits from LDS; the grouping works in LDS.
 template <int FMT, int XT>
 __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const uint8_t* router, int H,
-                                                            const uint16_t* x, int64_t ldx) {
+                                                            const uint16_t* x, int64_t ldx, const float* h_in,
+                                                            const uint16_t* norm_w, float eps, uint16_t* x_out) {
     constexpr int CB = Geom<FMT>::CB;
     __shared__ float4v red[2048];  // k-split partials, then the logits [32][E <= 256]
+    __shared__ int idx_s[256], rank_s[256], hist_s[4 * 256], counts_s[256], offsets_s[257];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = p.n_experts, T = E / 16;
+    if (norm_w) {
+        // one wavefront per row
+        for (int r = wave; r < p.rows; r += 16) {
+            const float* hr = h_in + (int64_t)r * H;
+            float ss = 0.f;
+            for (int c = lane; c < H; c += 64) ss = fmaf(hr[c], hr[c], ss);
+            ss = wave_sum(ss);
+            const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+            for (int c = lane; c < H; c += 64) x_out[(int64_t)r * ldx + c] = f2h(hr[c] * inv * h2f(norm_w[c]));
+        }
+        __threadfence_block();
+        __syncthreads();
+        x = x_out;
+    }
     const int nks = 16 / T;
     const int tile = wave % T, ks = wave / T;
     const int64_t nch = n_chunks_dev<FMT>(H);
@@ -234,9 +261,9 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
             }
     }
     __syncthreads();
-    topk_rows(p, lg, E);
+    topk_rows(p, lg, E, idx_s);
     __syncthreads();
-    group_pairs(p);
+    group_pairs(p, GroupScratch{idx_s, rank_s, hist_s, counts_s, offsets_s});
 }
 
 // ---------------------------------------------------------------------------
@@ -320,12 +347,27 @@ __global__ __launch_bounds__(256) void grouped_kernel(GroupedParams p) {
     }
 }
 
+// x = fp16(RMSNorm(h) * gamma) of one fp32 residual row per workgroup.
+__global__ __launch_bounds__(256) void moe_norm_kernel(const float* h, const uint16_t* gamma, int H, float eps,
+                                                       uint16_t* x, int64_t ldx) {
+    __shared__ float red[4];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const float* hr = h + (int64_t)r * H;
+    float ss = 0.f;
+    for (int c = tid; c < H; c += blockDim.x) ss = fmaf(hr[c], hr[c], ss);
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+    for (int c = tid; c < H; c += blockDim.x) x[(int64_t)r * ldx + c] = f2h(hr[c] * inv * h2f(gamma[c]));
+}
+
 // ---------------------------------------------------------------------------
 // Combine (+ optional RMSNorm of the updated residual): one workgroup per row
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-    __shared__ float red[8];
+__global__ __launch_bounds__(1024) void combine_kernel(CombineParams p) {
+    __shared__ float red[16];
     __shared__ float w_s[8];
     __shared__ int slot_s[16];
     const int r = blockIdx.x, tid = threadIdx.x;
@@ -472,7 +514,7 @@ void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream
 void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_f32, int64_t ldh,
                 int add_residual, const int32_t* forced, const ocrdec_moe_capture* cap, int32_t* cap_idx,
                 float* cap_w, const MoeWs& m, const uint16_t* norm_w, float eps, uint16_t* x_out, int64_t ldxo,
-                hipStream_t s) {
+                hipStream_t s, const float* h_norm, const uint16_t* norm_in, float eps_in) {
     const int E = w->n_experts, K = w->top_k, S = w->n_shared, F = w->d_ff, H = w->hidden;
     const int NP = rows * K;
     MoeParams p{};
@@ -501,14 +543,24 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     p.cap_counts = cap ? cap->counts : nullptr;
     p.cap_offsets = cap ? cap->offsets : nullptr;
     p.cap_perm = cap ? cap->perm : nullptr;
-    if (rows <= 32 && E % 16 == 0 && E <= 256) {
+    const bool small = rows <= 32 && E % 16 == 0 && E <= 256 && rows * K <= 256;
+    if (norm_in && !small) {
+        // the MoE input is the normalised residual: form it first
+        hipLaunchKernelGGL(moe_norm_kernel, dim3(rows), dim3(256), 0, s, h_norm, norm_in, H, eps_in, (uint16_t*)x,
+                           ldx);
+    }
+    if (small) {
         // router GEMV, top-k and grouping in one workgroup
         const uint8_t* rw = (const uint8_t*)w->router.data;
         const bool two = rows > 16;
 #define OCR_R(F_)                                                                                               \
     case F_:                                                                                                    \
-        if (two) hipLaunchKernelGGL((route_fused_kernel<F_, 2>), dim3(1), dim3(1024), 0, s, p, rw, H, x, ldx); \
-        else hipLaunchKernelGGL((route_fused_kernel<F_, 1>), dim3(1), dim3(1024), 0, s, p, rw, H, x, ldx);     \
+        if (two)                                                                                                \
+            hipLaunchKernelGGL((route_fused_kernel<F_, 2>), dim3(1), dim3(1024), 0, s, p, rw, H, x, ldx, h_norm,  \
+                               norm_in, eps_in, (uint16_t*)x);                                                   \
+        else                                                                                                    \
+            hipLaunchKernelGGL((route_fused_kernel<F_, 1>), dim3(1), dim3(1024), 0, s, p, rw, H, x, ldx, h_norm,  \
+                               norm_in, eps_in, (uint16_t*)x);                                                   \
         break;
         switch (w->router.fmt) {
             OCR_R(OCRDEC_F16)
@@ -596,7 +648,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.eps = eps;
         p.x_out = x_out;
         p.ldx = ldxo;
-        hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(rows <= 64 ? 1024 : 256), 0, s, p);
     }
 }
 
@@ -626,6 +678,6 @@ extern "C" ocrdec_status ocrdec_moe_layer(const ocrdec_moe_weights* w, int32_t r
                                               std::to_string(ws ? ws_bytes : 0));
     MoeWs m = carve_moe(ws, rows, w);
     launch_moe(w, rows, x, w->hidden, h, 0, w->hidden, add_residual, forced_topk, capture, nullptr, nullptr, m, nullptr,
-               0.f, nullptr, 0, (hipStream_t)stream);
+               0.f, nullptr, 0, (hipStream_t)stream, nullptr, nullptr, 0.f);
     return launch_status("ocrdec_moe_layer");
 }

@@ -99,6 +99,6 @@ ocrdec_status check_moe(const ocrdec_moe_weights* w, int rows);
 void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_f32, int64_t ldh,
                 int add_residual, const int32_t* forced, const ocrdec_moe_capture* cap, int32_t* cap_idx,
                 float* cap_w, const MoeWs& m, const uint16_t* norm_w, float eps, uint16_t* x_out, int64_t ldxo,
-                hipStream_t s);
+                hipStream_t s, const float* h_norm = nullptr, const uint16_t* norm_in = nullptr, float eps_in = 0.f);
 
 }  // namespace ocrdec

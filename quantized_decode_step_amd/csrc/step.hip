@@ -35,13 +35,9 @@ OCR_DEV void norm_row(const float* h, const uint16_t* gamma, int H, float eps, u
 // h[r] = embed[tok[r]] (fp16 table) or src[r] (fp32); x[r] = norm(h[r]).
 __global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tok, const uint16_t* embed, int vocab,
                                                          const float* src, float* h, const uint16_t* gamma,
-                                                         int H, float eps, uint16_t* x, int* counters,
-                                                         int n_counters) {
+                                                         int H, float eps, uint16_t* x) {
     __shared__ float red[8];
     const int r = blockIdx.x;
-    // the step's single-launch reductions count arriving workgroups from zero
-    if (r == 0)
-        for (int i = threadIdx.x; i < n_counters; i += blockDim.x) counters[i] = 0;
     float* hr = h + (int64_t)r * H;
     if (tok) {
         int t = tok[r];
@@ -56,6 +52,13 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tok, con
     norm_row(hr, gamma, H, eps, x + (int64_t)r * H, red);
 }
 
+__global__ __launch_bounds__(256) void norm_kernel(const float* h, const uint16_t* gamma, int H, float eps,
+                                                   uint16_t* x) {
+    __shared__ float red[8];
+    const int r = blockIdx.x;
+    norm_row(h + (int64_t)r * H, gamma, H, eps, x + (int64_t)r * H, red);
+}
+
 __global__ void copy_rows_kernel(const float* src, float* dst, int64_t n) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         dst[i] = src[i];
@@ -66,12 +69,7 @@ __global__ void bump_kernel(int32_t* gen_index, int rows) {
     if (r < rows) gen_index[r] += 1;
 }
 
-// Arrival counters of the step's single-launch reductions.
-enum { CTR_LM = 0, CTR_NORM = 1, CTR_ATTN = 2 };
-
 struct StepWs {
-    int* counters;  // CTR_LM, CTR_NORM, then [rows][n_heads] for attention
-    int n_counters;
     float* h;
     uint16_t* x;
     float* qkv;
@@ -98,8 +96,6 @@ StepWs carve_step(void* ws, const ocrdec_model* m, int rows, int cache_cap) {
         if (m->layers[l].is_moe) moe = &m->layers[l].moe;
         else dense_ff = std::max(dense_ff, m->layers[l].dense_ff);
     }
-    w.n_counters = CTR_ATTN + rows * m->n_heads;
-    w.counters = cv.take<int>(w.n_counters);
     w.h = cv.take<float>((size_t)rows * H);
     w.x = cv.take<uint16_t>((size_t)rows * H);
     w.qkv = cv.take<float>((size_t)rows * 3 * HD);
@@ -201,7 +197,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     StepWs w = carve_step(ws, m, R, cache_cap);
 
     hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(256), 0, s, tok_in, m->embed, m->vocab, hidden, w.h,
-                       m->layers[0].attn_norm, H, m->norm_eps, w.x, w.counters, w.n_counters);
+                       m->layers[0].attn_norm, H, m->norm_eps, w.x);
     int moe_l = 0;
     for (int l = 0; l < m->n_layers; ++l) {
         const ocrdec_layer& L = m->layers[l];
@@ -241,7 +237,6 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             ap.ld_out = HD;
             ap.n_split = attn_n_split(cache_cap);
             ap.part = w.attn_part;
-            ap.counters = w.counters + CTR_ATTN;
             launch_attn(ap, s);
         }
         // O projection + residual
@@ -255,10 +250,6 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             gp.xs = XDirect{w.o, HD, R};
             gp.y = w.h;
             gp.ldy = H;
-            gp.norm_w = L.ffn_norm;  // the last workgroup normalises h for the MLP/MoE
-            gp.eps = m->norm_eps;
-            gp.norm_out = w.x;
-            gp.counter = w.counters + CTR_NORM;
             launch_gemv(L.wo.fmt, EPI_RESID, pl, gp, s);
         }
         if (L.is_moe) {
@@ -266,9 +257,12 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             int32_t* ci = cap && cap->topk_idx ? cap->topk_idx + (int64_t)moe_l * R * K : nullptr;
             float* cw = cap && cap->topk_w ? cap->topk_w + (int64_t)moe_l * R * K : nullptr;
             const int32_t* fo = forced_topk ? forced_topk + (int64_t)moe_l * R * K : nullptr;
-            launch_moe(&L.moe, R, w.x, H, w.h, 1, H, 1, fo, nullptr, ci, cw, w.moe, next_norm, m->norm_eps, w.x, H, s);
+            // the routing kernel forms x = RMSNorm(h) itself
+            launch_moe(&L.moe, R, w.x, H, w.h, 1, H, 1, fo, nullptr, ci, cw, w.moe, next_norm, m->norm_eps, w.x, H, s,
+                       w.h, L.ffn_norm, m->norm_eps);
             ++moe_l;
         } else {
+            hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(256), 0, s, w.h, L.ffn_norm, H, m->norm_eps, w.x);
             const int F = L.dense_ff;
             {
                 GemvPlan pl = plan_gemv(L.dense_gate_up.fmt, 2 * F, H, R, EPI_GLU);
@@ -293,12 +287,10 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                 gp.xs = XDirect{w.a, F, R};
                 gp.y = w.h;
                 gp.ldy = H;
-                gp.norm_w = next_norm;  // NULL after the last layer without an LM head
-                gp.eps = m->norm_eps;
-                gp.norm_out = w.x;
-                gp.counter = w.counters + CTR_NORM;
                 launch_gemv(L.dense_down.fmt, EPI_RESID, pl, gp, s);
             }
+            if (next_norm)
+                hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(256), 0, s, w.h, next_norm, H, m->norm_eps, w.x);
         }
     }
     if (hidden) {
@@ -315,11 +307,8 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
         gp.nchunks = n_chunks(m->lm_head.fmt, H);
         gp.xs = XDirect{w.x, H, R};
         gp.part = w.lm_part;
-        gp.counter = w.counters + CTR_LM;
-        gp.tok_out = tok_out;
-        gp.top2 = cap ? cap->lm_top2 : nullptr;
-        gp.gen_index = st->gen_index;
         launch_gemv(m->lm_head.fmt, EPI_ARGMAX, pl, gp, s);
+        launch_argmax_final(w.lm_part, pl.grid, R, tok_out, cap ? cap->lm_top2 : nullptr, st->gen_index, s);
     } else {
         hipLaunchKernelGGL(bump_kernel, dim3(1), dim3(64), 0, s, st->gen_index, R);
     }

@@ -116,8 +116,6 @@ def _attn_case(q, rows, NH, D, prefix_cap, ring_cap, prefix_len, gen_index, sink
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
     q.ocrdec_attn_decode(a, ws, wsb)
     torch.cuda.synchronize()
-    # the call leaves its arrival counters at zero, so the workspace is reusable as is
-    assert int(ws.view(torch.int32)[-(rows * NH):].abs().sum().item()) == 0
     got = from_f16_tensor(out)
     kc_after = kd.cpu().numpy().view(np.float16)
     vc_after = vd.cpu().numpy().view(np.float16)
@@ -279,7 +277,6 @@ def test_lm_argmax_parity(q, fmt, n, rows):
                 assert srt[0] - srt[1] < NEAR_TIE, "row %d: %d vs %d" % (r, g[r], best)
             assert abs(t2[r, 0] - srt[0]) <= 1e-4 * max(1, abs(srt[0]))
             assert abs(t2[r, 1] - srt[1]) <= 1e-4 * max(1, abs(srt[1]))
-    assert int(ws.view(torch.int32)[-64:].abs().sum().item()) == 0, "arrival counter not reset"
 
 
 def test_lm_argmax_ties_go_to_lowest_index(q):
