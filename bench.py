@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--lm-iters", type=int, default=50)
+    ap.add_argument("--mode", choices=["full", "lm"], default="full",
+                    help="lm: only the LM-head argmax loop and a device copy of known size (for counter runs)")
+    ap.add_argument("--copy-mb", type=int, default=512, help="size of the calibration copy in --mode lm")
     return ap.parse_args()
 
 
@@ -79,14 +82,20 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     dev = torch.device("cuda:0")
     d = synth.dims_full()
+    stream = torch.cuda.Stream()
+    if args.mode == "lm":
+        lm = synth.random_qmat(d.fmt_lm, synth.stream_id(SEED, "lm_head"), d.vocab, d.hidden, d.w_std)
+
+        class _M:
+            lm_head = q.DeviceQMat(lm)
+        lm_only(args, _M, d, q, torch, dev, stream)
+        return
     t_build = time.time()
     model = synth.make_model(d, SEED)
     dm = q.DeviceModel(model)
     dm.src_layers = model.layers
     dm.src_lm = model.lm_head
     t_build = time.time() - t_build
-
-    stream = torch.cuda.Stream()
 
     def run_rows(R: int, steps: int, warmup: int, want_sample: bool):
         st = synth.make_state(d, SEED, [d.prefix_cap] * R, [T0] * R)
@@ -202,6 +211,34 @@ def main():
         "setup_s": round(t_build, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def lm_only(args, dm, d, q, torch, dev, stream):
+    """The LM-head argmax kernel alone, then a device-to-device copy of a known
+    size (its FETCH_SIZE/WRITE_SIZE calibrate the counters)."""
+    import synth
+    R = args.rows
+    x = torch.from_numpy(synth.normal_f16(synth.stream_id(SEED, "lm_x"), (R, d.hidden)).view(np.int16)).to(dev)
+    tok_out = torch.zeros(R, dtype=torch.int32, device=dev)
+    wsb = q.ocrdec_lm_argmax_workspace_bytes(dm.lm_head.desc, R)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q.ocrdec_lm_argmax(dm.lm_head.desc, R, x, tok_out, None, ws, wsb, stream=stream)
+        e0.record(stream)
+        for _ in range(args.lm_iters):
+            q.ocrdec_lm_argmax(dm.lm_head.desc, R, x, tok_out, None, ws, wsb, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        n = args.copy_mb * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / args.lm_iters
+    print(json.dumps({"mode": "lm", "rows": R, "lm_avg_us_incl_merge": round(us, 2),
+                      "copy_bytes": n, "copy_launches": 3}), flush=True)
 
 
 def cpu_baseline(model, d, budget_s: float):

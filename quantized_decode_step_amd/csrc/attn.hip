@@ -123,8 +123,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
     float qf[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) qf[i] = q_s[dsub + i];
-    for (int base = o0 + wave * KPL; base < o1; base += 4 * KPL) {
-        const int o = base + lane / LPK;
+    constexpr int ITER = KPS / (4 * KPL);  // key groups per wavefront; unrolled so all loads issue first
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int o = o0 + wave * KPL + it * 4 * KPL + lane / LPK;
         float dot = 0.f;
         if (o < o1) {
             const int ci = ord_to_idx(p, w, o);
@@ -162,8 +164,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int base = o0 + wave * KPL; base < o1; base += 4 * KPL) {
-        const int o = base + lane / LPK;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int o = o0 + wave * KPL + it * 4 * KPL + lane / LPK;
         if (o < o1) {
             const int ci = ord_to_idx(p, w, o);
             uint4 vv;

@@ -179,3 +179,34 @@ OCR_DEV half8v deq_u8(uint32_t lo, uint32_t hi) {
 }
 
 OCR_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// x = fp16(h / sqrt(mean(h^2) + eps) * gamma) for one fp32 row of H <= 4096
+// values (H % 4 == 0) by one wavefront: every load is issued before the
+// first use, so the row costs one memory round trip.
+OCR_DEV void wave_rmsnorm_row(const float* h, const uint16_t* gamma, int H, float eps, uint16_t* x) {
+    const int lane = threadIdx.x & 63;
+    const int n4 = H / 4;
+    float4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int c4 = lane + 64 * i;
+        v[i] = c4 < n4 ? ((const float4*)h)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int c4 = lane + 64 * i;
+        if (c4 < n4) {
+            const uint2 g = ((const uint2*)gamma)[c4];
+            const uint32_t lo = (uint32_t)f2h(v[i].x * inv * h2f((uint16_t)(g.x & 0xFFFF))) |
+                                ((uint32_t)f2h(v[i].y * inv * h2f((uint16_t)(g.x >> 16))) << 16);
+            const uint32_t hi = (uint32_t)f2h(v[i].z * inv * h2f((uint16_t)(g.y & 0xFFFF))) |
+                                ((uint32_t)f2h(v[i].w * inv * h2f((uint16_t)(g.y >> 16))) << 16);
+            ((uint2*)x)[c4] = make_uint2(lo, hi);
+        }
+    }
+}

@@ -92,33 +92,38 @@ struct GroupScratch {
     int* hist;       // [nchunk][E]
     int* counts;     // [E]
     int* offsets;    // [E + 1]
+    int* act_of;     // [E] index of an expert in the active list
 };
 
 // Stable counting sort of the (row, rank) pairs by expert and the list of
 // active experts (routed experts with tokens, then the shared experts).
+// Outputs: perm/inv, and per active expert v: virt[v] = (expert, first
+// grouped slot, token count) and vrows[v * NP + t] = the row of its token t.
 OCR_DEV void group_pairs(const MoeParams& p, const GroupScratch& g) {
+    __shared__ int n_act_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int R = p.rows, E = p.n_experts, K = p.top_k, S = p.n_shared;
     const int NP = R * K;
 
-    // per 64-pair chunk: rank of each pair among equal experts before it in
-    // the chunk, and the chunk's histogram
+    // per 64-pair chunk: rank of each pair among the equal experts before it
+    // in the chunk, and the chunk's histogram (one ballot per distinct expert)
     const int nchunk = (NP + 63) / 64;
     for (int c = wave; c < nchunk; c += nw) {
+        for (int e = lane; e < E; e += 64) g.hist[(int64_t)c * E + e] = 0;
         const int pi = c * 64 + lane;
-        const int e = pi < NP ? g.idx[pi] : -1;
+        const bool ok = pi < NP;
+        const int e = ok ? g.idx[pi] : -1;
+        unsigned long long todo = __ballot(ok);
         int rank = 0;
-        for (int i = 0; i < 64; ++i) {
-            const int ei = __shfl(e, i, 64);
-            rank += (i < lane && ei == e) ? 1 : 0;
+        while (todo) {
+            const int leader = __ffsll((long long)todo) - 1;
+            const int le = __shfl(e, leader, 64);
+            const unsigned long long m = __ballot(ok && e == le);
+            if (ok && e == le) rank = __popcll(m & ((1ull << lane) - 1ull));
+            if (lane == leader) g.hist[(int64_t)c * E + le] = __popcll(m);
+            todo &= ~m;
         }
-        if (pi < NP) g.rank[pi] = rank;
-        for (int eb = 0; eb < E; eb += 64) {
-            const int me = eb + lane;
-            int cnt = 0;
-            for (int i = 0; i < 64; ++i) cnt += (__shfl(e, i, 64) == me) ? 1 : 0;
-            if (me < E) g.hist[(int64_t)c * E + me] = cnt;
-        }
+        if (ok) g.rank[pi] = rank;
     }
     __syncthreads();
 
@@ -152,34 +157,32 @@ OCR_DEV void group_pairs(const MoeParams& p, const GroupScratch& g) {
             if (e < E) g.offsets[e] = excl;
             if (e < E && cnt > 0) {
                 const int v = act + ai - 1;
-                p.virt_expert[v] = e;
-                p.virt_off[v] = excl;
-                p.virt_cnt[v] = cnt;
+                p.virt[v] = make_int4(e, excl, cnt, 0);
+                g.act_of[e] = v;
             }
             base += __shfl(incl, 63, 64);
             act += __shfl(ai, 63, 64);
         }
         if (lane == 0) {
             g.offsets[E] = base;
-            for (int s = 0; s < S; ++s) {
-                p.virt_expert[act + s] = E + s;
-                p.virt_off[act + s] = NP + s * R;
-                p.virt_cnt[act + s] = R;
-            }
+            for (int s = 0; s < S; ++s) p.virt[act + s] = make_int4(E + s, NP + s * R, R, 0);
             p.n_virt[0] = act + S;
+            n_act_s = act;
         }
     }
     __syncthreads();
 
-    // scatter: grouped position of every pair
+    // scatter: grouped position of every pair; the row list of every expert
     for (int pi = tid; pi < NP; pi += blockDim.x) {
         const int e = g.idx[pi];
-        const int pos = g.offsets[e] + g.hist[(int64_t)(pi / 64) * E + e] + g.rank[pi];
+        const int t = g.hist[(int64_t)(pi / 64) * E + e] + g.rank[pi];
+        const int pos = g.offsets[e] + t;
         p.perm[pos] = pi;
         p.inv[pi] = pos;
-        p.slot_row[pos] = pi / K;
+        p.vrows[(int64_t)g.act_of[e] * NP + t] = pi / K;
     }
-    for (int i = tid; i < S * R; i += blockDim.x) p.slot_row[NP + i] = i % R;
+    const int act = n_act_s;
+    for (int i = tid; i < S * R; i += blockDim.x) p.vrows[(int64_t)(act + i / R) * NP + i % R] = i % R;
     __syncthreads();
     if (p.cap_counts)
         for (int e = tid; e < E; e += blockDim.x) p.cap_counts[e] = g.counts[e];
@@ -193,7 +196,7 @@ OCR_DEV void group_pairs(const MoeParams& p, const GroupScratch& g) {
 __global__ __launch_bounds__(1024) void route_group_kernel(MoeParams p) {
     topk_rows(p, p.logits, p.n_experts, p.idx);
     __syncthreads();
-    group_pairs(p, GroupScratch{p.idx, p.rank, p.hist, p.counts, p.offsets});
+    group_pairs(p, GroupScratch{p.idx, p.rank, p.hist, p.counts, p.offsets, p.act_of});
 }
 
 // Routing of up to 32 rows in one workgroup.  Optionally it first forms the
@@ -207,19 +210,11 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
                                                             const uint16_t* norm_w, float eps, uint16_t* x_out) {
     constexpr int CB = Geom<FMT>::CB;
     __shared__ float4v red[2048];  // k-split partials, then the logits [32][E <= 256]
-    __shared__ int idx_s[256], rank_s[256], hist_s[4 * 256], counts_s[256], offsets_s[257];
+    __shared__ int idx_s[256], rank_s[256], hist_s[4 * 256], counts_s[256], offsets_s[257], act_s[256];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = p.n_experts, T = E / 16;
     if (norm_w) {
-        // one wavefront per row
-        for (int r = wave; r < p.rows; r += 16) {
-            const float* hr = h_in + (int64_t)r * H;
-            float ss = 0.f;
-            for (int c = lane; c < H; c += 64) ss = fmaf(hr[c], hr[c], ss);
-            ss = wave_sum(ss);
-            const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-            for (int c = lane; c < H; c += 64) x_out[(int64_t)r * ldx + c] = f2h(hr[c] * inv * h2f(norm_w[c]));
-        }
+        for (int r = wave; r < p.rows; r += 16) wave_rmsnorm_row(h_in + (int64_t)r * H, norm_w, H, eps, x_out + (int64_t)r * ldx);
         __threadfence_block();
         __syncthreads();
         x = x_out;
@@ -263,7 +258,7 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
     __syncthreads();
     topk_rows(p, lg, E, idx_s);
     __syncthreads();
-    group_pairs(p, GroupScratch{idx_s, rank_s, hist_s, counts_s, offsets_s});
+    group_pairs(p, GroupScratch{idx_s, rank_s, hist_s, counts_s, offsets_s, act_s});
 }
 
 // ---------------------------------------------------------------------------
@@ -285,12 +280,15 @@ __global__ __launch_bounds__(256) void grouped_kernel(GroupedParams p) {
     const int ks = wave % KS;
     const int v = item / p.groups_per_expert;
     const int g = item % p.groups_per_expert;
+    // the list entry is read unconditionally (in bounds: v is clamped) so that
+    // it travels with the count in one round trip
+    const int vc = min(v, p.max_virt - 1);
     const int n_virt = p.n_virt[0];
+    const int4 ent = p.virt[vc];
     const bool valid = v < n_virt && v < p.max_virt;
-    // uniform across the workgroup: every wave must reach the barriers below
-    const int e = valid ? p.virt_expert[v] : 0;
-    const int off = valid ? p.virt_off[v] : 0;
-    const int cnt = valid ? p.virt_cnt[v] : 0;
+    const int e = valid ? ent.x : 0;
+    const int off = valid ? ent.y : 0;
+    const int cnt = valid ? ent.z : 0;
     const uint8_t* base = (e < p.n_experts) ? p.w_routed + (int64_t)e * p.expert_bytes
                                             : p.w_shared + (int64_t)(e - p.n_experts) * p.expert_bytes;
     const uint8_t* tile[NT];
@@ -318,7 +316,7 @@ __global__ __launch_bounds__(256) void grouped_kernel(GroupedParams p) {
             for (int xt = 0; xt < XT; ++xt) acc[i][xt] = float4v{0.f, 0.f, 0.f, 0.f};
         const int cc1 = my_more ? c1 : c0;
         if constexpr (GLU) {
-            XGather xs{p.x, p.ldx, p.slot_row + off, cnt};
+            XGather xs{p.x, p.ldx, p.vrows + (int64_t)vc * p.np, cnt};
             kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
         } else {
             XDirect xs{p.x + (int64_t)off * p.ldx, p.ldx, cnt};
@@ -436,11 +434,10 @@ MoeWs carve_moe(void* ws, int rows, const ocrdec_moe_weights* w) {
     m.offsets = cv.take<int32_t>(E + 1);
     m.perm = cv.take<int32_t>(NP);
     m.inv = cv.take<int32_t>(NP);
-    m.slot_row = cv.take<int32_t>(nslots);
+    m.vrows = cv.take<int32_t>((size_t)(E + S) * NP);
+    m.act_of = cv.take<int32_t>(E);
     m.n_virt = cv.take<int32_t>(1);
-    m.virt_expert = cv.take<int32_t>(E + S);
-    m.virt_off = cv.take<int32_t>(E + S);
-    m.virt_cnt = cv.take<int32_t>(E + S);
+    m.virt = cv.take<int4>(E + S);
     m.a = cv.take<uint16_t>((size_t)nslots * w->d_ff);
     m.y = cv.take<float>((size_t)nslots * w->hidden);
     m.bytes = cv.off;
@@ -450,7 +447,8 @@ MoeWs carve_moe(void* ws, int rows, const ocrdec_moe_weights* w) {
 ocrdec_status check_moe(const ocrdec_moe_weights* w, int rows) {
     OCR_CHECK_ARG(w, "weights is NULL");
     OCR_CHECK_ARG(rows >= 1 && rows <= 65536, "rows must be in [1, 65536]");
-    OCR_CHECK_ARG(w->hidden > 0 && w->hidden % 32 == 0, "hidden must be a positive multiple of 32");
+    OCR_CHECK_ARG(w->hidden > 0 && w->hidden % 32 == 0 && w->hidden <= 4096,
+                  "hidden must be a positive multiple of 32, at most 4096");
     OCR_CHECK_ARG(w->d_ff > 0 && w->d_ff % 32 == 0, "d_ff must be a positive multiple of 32");
     if (w->n_experts < 1 || w->n_experts > 256) return fail(OCRDEC_ERR_UNSUPPORTED, "n_experts must be in [1, 256]");
     if (w->top_k < 1 || w->top_k > 8 || w->top_k > w->n_experts)
@@ -533,11 +531,10 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     p.offsets = m.offsets;
     p.perm = m.perm;
     p.inv = m.inv;
-    p.slot_row = m.slot_row;
+    p.vrows = m.vrows;
+    p.act_of = m.act_of;
     p.n_virt = m.n_virt;
-    p.virt_expert = m.virt_expert;
-    p.virt_off = m.virt_off;
-    p.virt_cnt = m.virt_cnt;
+    p.virt = m.virt;
     p.cap_idx = cap_idx ? cap_idx : (cap ? cap->topk_idx : nullptr);
     p.cap_w = cap_w ? cap_w : (cap ? cap->topk_w : nullptr);
     p.cap_counts = cap ? cap->counts : nullptr;
@@ -596,10 +593,9 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.groups_per_expert = F / 16;
         p.max_virt = max_virt;
         p.n_virt = m.n_virt;
-        p.virt_expert = m.virt_expert;
-        p.virt_off = m.virt_off;
-        p.virt_cnt = m.virt_cnt;
-        p.slot_row = m.slot_row;
+        p.virt = m.virt;
+        p.vrows = m.vrows;
+        p.np = NP;
         p.x = x;
         p.ldx = ldx;
         p.y = m.a;
@@ -619,10 +615,9 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.groups_per_expert = H / 16;
         p.max_virt = max_virt;
         p.n_virt = m.n_virt;
-        p.virt_expert = m.virt_expert;
-        p.virt_off = m.virt_off;
-        p.virt_cnt = m.virt_cnt;
-        p.slot_row = m.slot_row;
+        p.virt = m.virt;
+        p.vrows = m.vrows;
+        p.np = NP;
         p.x = m.a;
         p.ldx = F;
         p.y = m.y;

@@ -26,11 +26,10 @@ struct MoeParams {
     int32_t* offsets;
     int32_t* perm;
     int32_t* inv;
-    int32_t* slot_row;
+    int32_t* vrows;    // [n_experts + n_shared][rows * top_k] rows of each active expert's tokens
+    int32_t* act_of;   // [n_experts] scratch
     int32_t* n_virt;
-    int32_t* virt_expert;
-    int32_t* virt_off;
-    int32_t* virt_cnt;
+    int4* virt;        // [n_experts + n_shared] (expert, first slot, count, -)
     int32_t* cap_idx;
     float* cap_w;
     int32_t* cap_counts;
@@ -49,10 +48,9 @@ struct GroupedParams {
     int groups_per_expert;
     int max_virt;
     const int32_t* n_virt;
-    const int32_t* virt_expert;
-    const int32_t* virt_off;
-    const int32_t* virt_cnt;
-    const int32_t* slot_row;
+    const int4* virt;
+    const int32_t* vrows;
+    int np;
     const uint16_t* x;
     int64_t ldx;
     void* y;
@@ -84,11 +82,10 @@ struct MoeWs {
     int32_t* offsets;
     int32_t* perm;
     int32_t* inv;
-    int32_t* slot_row;
+    int32_t* vrows;
+    int32_t* act_of;
     int32_t* n_virt;
-    int32_t* virt_expert;
-    int32_t* virt_off;
-    int32_t* virt_cnt;
+    int4* virt;
     uint16_t* a;
     float* y;
     size_t bytes;

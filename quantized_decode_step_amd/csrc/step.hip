@@ -14,49 +14,54 @@ namespace {
 
 constexpr int kMaxRows = 32;
 
-// x = fp16(RMSNorm(h) * gamma) of one row of the fp32 residual; the
-// workgroup's threads stride over the columns.
-OCR_DEV void norm_row(const float* h, const uint16_t* gamma, int H, float eps, uint16_t* x, float* red) {
-    const int tid = threadIdx.x;
-    float ss = 0.f;
-    for (int c = tid; c < H; c += blockDim.x) {
-        const float v = h[c];
-        ss = fmaf(v, v, ss);
-    }
-    ss = wave_sum(ss);
-    if ((tid & 63) == 0) red[tid >> 6] = ss;
-    __syncthreads();
-    float tot = 0.f;
-    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += red[i];
-    const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-    for (int c = tid; c < H; c += blockDim.x) x[c] = f2h(h[c] * inv * h2f(gamma[c]));
-}
-
 // h[r] = embed[tok[r]] (fp16 table) or src[r] (fp32); x[r] = norm(h[r]).
-__global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tok, const uint16_t* embed, int vocab,
-                                                         const float* src, float* h, const uint16_t* gamma,
-                                                         int H, float eps, uint16_t* x) {
-    __shared__ float red[8];
-    const int r = blockIdx.x;
+// One wavefront per row.
+__global__ __launch_bounds__(64) void embed_norm_kernel(const int32_t* tok, const uint16_t* embed, int vocab,
+                                                        const float* src, float* h, const uint16_t* gamma, int H,
+                                                        float eps, uint16_t* x) {
+    const int r = blockIdx.x, lane = threadIdx.x;
     float* hr = h + (int64_t)r * H;
+    const int n4 = H / 4;
     if (tok) {
         int t = tok[r];
         t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
-        const uint16_t* from = embed + (int64_t)t * H;
-        for (int c = threadIdx.x; c < H; c += blockDim.x) hr[c] = h2f(from[c]);
+        const uint2* from = (const uint2*)(embed + (int64_t)t * H);
+        uint2 e[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int c4 = lane + 64 * i;
+            e[i] = c4 < n4 ? from[c4] : make_uint2(0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int c4 = lane + 64 * i;
+            if (c4 < n4)
+                ((float4*)hr)[c4] = make_float4(h2f((uint16_t)(e[i].x & 0xFFFF)), h2f((uint16_t)(e[i].x >> 16)),
+                                                h2f((uint16_t)(e[i].y & 0xFFFF)), h2f((uint16_t)(e[i].y >> 16)));
+        }
     } else {
-        const float* from = src + (int64_t)r * H;
-        for (int c = threadIdx.x; c < H; c += blockDim.x) hr[c] = from[c];
+        const float4* from = (const float4*)(src + (int64_t)r * H);
+        float4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int c4 = lane + 64 * i;
+            v[i] = c4 < n4 ? from[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int c4 = lane + 64 * i;
+            if (c4 < n4) ((float4*)hr)[c4] = v[i];
+        }
     }
-    __syncthreads();
-    norm_row(hr, gamma, H, eps, x + (int64_t)r * H, red);
+    __threadfence_block();
+    wave_rmsnorm_row(hr, gamma, H, eps, x + (int64_t)r * H);
 }
 
-__global__ __launch_bounds__(256) void norm_kernel(const float* h, const uint16_t* gamma, int H, float eps,
-                                                   uint16_t* x) {
-    __shared__ float red[8];
+// x[r] = fp16(RMSNorm(h[r]) * gamma): one wavefront per row.
+__global__ __launch_bounds__(64) void norm_kernel(const float* h, const uint16_t* gamma, int H, float eps,
+                                                  uint16_t* x) {
     const int r = blockIdx.x;
-    norm_row(h + (int64_t)r * H, gamma, H, eps, x + (int64_t)r * H, red);
+    wave_rmsnorm_row(h + (int64_t)r * H, gamma, H, eps, x + (int64_t)r * H);
 }
 
 __global__ void copy_rows_kernel(const float* src, float* dst, int64_t n) {
@@ -120,7 +125,8 @@ ocrdec_status check_step(const ocrdec_model* m, const ocrdec_state* st) {
     OCR_CHECK_ARG(st->ring_cap >= 1 && st->prefix_cap >= 0, "ring_cap must be >= 1 and prefix_cap >= 0");
     OCR_CHECK_ARG(st->prefix_len && st->gen_index, "state arrays must be non-NULL");
     OCR_CHECK_ARG(m->n_layers >= 1 && m->layers, "model needs at least one layer");
-    OCR_CHECK_ARG(m->hidden > 0 && m->hidden % 32 == 0, "hidden must be a positive multiple of 32");
+    OCR_CHECK_ARG(m->hidden > 0 && m->hidden % 32 == 0 && m->hidden <= 4096,
+                  "hidden must be a positive multiple of 32, at most 4096");
     if (m->head_dim != 64 && m->head_dim != 128) return fail(OCRDEC_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     OCR_CHECK_ARG(m->n_heads >= 1, "n_heads must be >= 1");
     OCR_CHECK_ARG((m->n_heads * m->head_dim) % 32 == 0, "n_heads*head_dim must be a multiple of 32");
@@ -196,7 +202,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     hipStream_t s = (hipStream_t)stream;
     StepWs w = carve_step(ws, m, R, cache_cap);
 
-    hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(256), 0, s, tok_in, m->embed, m->vocab, hidden, w.h,
+    hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(64), 0, s, tok_in, m->embed, m->vocab, hidden, w.h,
                        m->layers[0].attn_norm, H, m->norm_eps, w.x);
     int moe_l = 0;
     for (int l = 0; l < m->n_layers; ++l) {
@@ -262,7 +268,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                        w.h, L.ffn_norm, m->norm_eps);
             ++moe_l;
         } else {
-            hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(256), 0, s, w.h, L.ffn_norm, H, m->norm_eps, w.x);
+            hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(64), 0, s, w.h, L.ffn_norm, H, m->norm_eps, w.x);
             const int F = L.dense_ff;
             {
                 GemvPlan pl = plan_gemv(L.dense_gate_up.fmt, 2 * F, H, R, EPI_GLU);
@@ -290,7 +296,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                 launch_gemv(L.dense_down.fmt, EPI_RESID, pl, gp, s);
             }
             if (next_norm)
-                hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(256), 0, s, w.h, next_norm, H, m->norm_eps, w.x);
+                hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(64), 0, s, w.h, next_norm, H, m->norm_eps, w.x);
         }
     }
     if (hidden) {
