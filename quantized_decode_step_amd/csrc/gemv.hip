@@ -5,9 +5,13 @@
 
 namespace ocrdec {
 
-template <int FMT, int NT, int XT, int KS, int EPI>
+// XT = 1, 2: 16 or 32 tokens per pass.  LDSX: activations staged in LDS;
+// otherwise their fragments are loaded from global memory alongside the
+// weights (for k too large to stage).
+template <int FMT, int NT, int XT, int KS, int EPI, bool LDSX>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
     constexpr int CB = Geom<FMT>::CB;
+    extern __shared__ __align__(16) uint16_t xl_dyn[];
     __shared__ float4v red[(KS > 1) ? 4 * NT * XT * 64 : 1];
     __shared__ float amx[(EPI == EPI_ARGMAX) ? 4 * 32 * 3 : 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -30,13 +34,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
     const int c1 = valid ? (int)min((int64_t)(c0 + cper), p.nchunks) : c0;
     const int nblk = p.k / 32;
 
+    const int ldl = xlds_stride(p.k);
     for (int tok0 = 0; tok0 < p.xs.rows; tok0 += 16 * XT) {
         float4v acc[NT][XT];
 #pragma unroll
         for (int i = 0; i < NT; ++i)
 #pragma unroll
             for (int xt = 0; xt < XT; ++xt) acc[i][xt] = float4v{0.f, 0.f, 0.f, 0.f};
-        kloop<FMT, NT, XT>(tile, c0, c1, p.xs, tok0, nblk, lane, acc);
+        if constexpr (LDSX) {
+            auto stage = [&]() { stage_x(p.xs, tok0, 16 * XT, p.k, xl_dyn, ldl); };
+            kloop_lds<FMT, NT, XT>(tile, c0, c1, stage, xl_dyn, ldl, p.xs.rows - tok0, nblk, lane, acc);
+        } else {
+            kloop<FMT, NT, XT>(tile, c0, c1, p.xs, tok0, nblk, lane, acc);
+        }
         ksplit_reduce<NT, XT, KS>(acc, red, wave, lane);
 
         const bool owner = (ks == 0) && valid;
@@ -151,19 +161,21 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
 
 namespace {
 
-template <int FMT, int NT, int XT, int KS, int EPI>
+template <int FMT, int NT, int XT, int KS, int EPI, bool LDSX>
 void launch_t(const GemvParams& p, hipStream_t s) {
     const int groups_per_wg = 4 / KS;
     const int grid = (p.n_groups + groups_per_wg - 1) / groups_per_wg;
-    hipLaunchKernelGGL((gemv_kernel<FMT, NT, XT, KS, EPI>), dim3(grid), dim3(256), 0, s, p);
+    const size_t lds = LDSX ? lds_x_bytes(p.k, XT) : 0;
+    hipLaunchKernelGGL((gemv_kernel<FMT, NT, XT, KS, EPI, LDSX>), dim3(grid), dim3(256), lds, s, p);
 }
 
 template <int FMT, int EPI>
-void launch_fmt(const GemvParams& p, int nt, int ks, int xt, hipStream_t s) {
-#define OCR_L(NT_, KS_, XT_)                                  \
-    if (nt == NT_ && ks == KS_ && xt == XT_) {                \
-        launch_t<FMT, NT_, XT_, KS_, EPI>(p, s);              \
-        return;                                               \
+void launch_fmt(const GemvParams& p, int nt, int ks, int xt, bool lds, hipStream_t s) {
+#define OCR_L(NT_, KS_, XT_)                                                    \
+    if (nt == NT_ && ks == KS_ && xt == XT_) {                                  \
+        if (lds) launch_t<FMT, NT_, XT_, KS_, EPI, true>(p, s);                 \
+        else launch_t<FMT, NT_, XT_, KS_, EPI, false>(p, s);                    \
+        return;                                                                 \
     }
     if constexpr (EPI == EPI_GLU) {
         OCR_L(2, 1, 1) OCR_L(2, 1, 2) OCR_L(2, 4, 1) OCR_L(2, 4, 2)
@@ -179,6 +191,7 @@ GemvPlan plan_gemv(int fmt, int n, int k, int rows, int epi) {
     GemvPlan pl;
     const int64_t tiles = (n + 15) / 16;
     pl.xt = rows <= 16 ? 1 : 2;
+    pl.lds = use_lds_x(k, pl.xt, rows);
     if (epi == EPI_GLU) {
         pl.nt = 2;
         pl.groups = (int)(tiles / 2);
@@ -203,10 +216,10 @@ void launch_gemv(int fmt, int epi, const GemvPlan& pl, GemvParams p, hipStream_t
 #define OCR_E(E_)                                                                          \
     case E_:                                                                               \
         switch (fmt) {                                                                     \
-        case OCRDEC_F16: launch_fmt<OCRDEC_F16, E_>(p, pl.nt, pl.ks, pl.xt, s); break;     \
-        case OCRDEC_Q8_0: launch_fmt<OCRDEC_Q8_0, E_>(p, pl.nt, pl.ks, pl.xt, s); break;   \
-        case OCRDEC_Q4_0: launch_fmt<OCRDEC_Q4_0, E_>(p, pl.nt, pl.ks, pl.xt, s); break;   \
-        case OCRDEC_U8A_G32: launch_fmt<OCRDEC_U8A_G32, E_>(p, pl.nt, pl.ks, pl.xt, s); break; \
+        case OCRDEC_F16: launch_fmt<OCRDEC_F16, E_>(p, pl.nt, pl.ks, pl.xt, pl.lds, s); break;     \
+        case OCRDEC_Q8_0: launch_fmt<OCRDEC_Q8_0, E_>(p, pl.nt, pl.ks, pl.xt, pl.lds, s); break;   \
+        case OCRDEC_Q4_0: launch_fmt<OCRDEC_Q4_0, E_>(p, pl.nt, pl.ks, pl.xt, pl.lds, s); break;   \
+        case OCRDEC_U8A_G32: launch_fmt<OCRDEC_U8A_G32, E_>(p, pl.nt, pl.ks, pl.xt, pl.lds, s); break; \
         }                                                                                  \
         break;
     switch (epi) {

@@ -21,6 +21,7 @@ struct GemvParams {
 
 struct GemvPlan {
     int nt, ks, xt, groups, grid;
+    bool lds;  // activations staged in LDS
 };
 
 GemvPlan plan_gemv(int fmt, int n, int k, int rows, int epi);

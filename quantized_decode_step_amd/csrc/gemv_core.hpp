@@ -222,6 +222,107 @@ OCR_DEV void kloop(const uint8_t* const (&tile)[NT], int c0, int c1, const XS& x
     }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-staged activations
+//
+// The workgroup copies the activations of 16 or 32 tokens (zero rows past the
+// token count) into LDS once per pass; every wavefront then reads its A
+// fragments from LDS, so the k-loop streams only weights from memory.  Row
+// stride ldl = k + 8 halves (16 bytes of padding shifts consecutive tokens by
+// four banks).
+// ---------------------------------------------------------------------------
+
+OCR_DEV int xlds_stride(int k) { return k + 8; }
+
+template <class XS>
+OCR_DEV void stage_x(const XS& xs, int tok0, int ntok, int k, uint16_t* xl, int ldl) {
+    // only the tokens that exist are copied; fragments of the others read as zero
+    const int nt = min(ntok, max(xs.rows - tok0, 0));
+    const int n16 = k >> 3;  // 16-byte pieces per row
+    for (int t = 0; t < nt; ++t) {
+        const uint16_t* p = xs.row(tok0 + t);
+        for (int c0 = 0; c0 < n16; c0 += 4 * (int)blockDim.x) {
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + u * (int)blockDim.x + (int)threadIdx.x;
+                v[u] = c < n16 ? *(const uint4*)(p + c * 8) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + u * (int)blockDim.x + (int)threadIdx.x;
+                if (c < n16) *(uint4*)(xl + t * ldl + c * 8) = v[u];
+            }
+        }
+    }
+}
+
+template <int FMT, int XT>
+OCR_DEV void lds_xfrags(const uint16_t* xl, int ldl, int ntok, int c, int nblk, int lane,
+                        half8v (&xa)[Geom<FMT>::SB][XT]) {
+#pragma unroll
+    for (int xt = 0; xt < XT; ++xt)
+#pragma unroll
+        for (int j = 0; j < Geom<FMT>::SB; ++j) {
+            const int blk = c * Geom<FMT>::SB + j;
+            const int tok = 16 * xt + (lane & 15);
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (blk < nblk && tok < ntok) v = *(const uint4*)(xl + tok * ldl + blk * 32 + 8 * (lane >> 4));
+            xa[j][xt] = bits_to_half8(v);
+        }
+}
+
+template <int FMT, int NT>
+constexpr int kloop_lds_depth() {
+    return NT * 6 * 6 <= 72 ? 6 : (NT * 6 * 4 <= 96 ? 4 : 3);
+}
+
+// k-loop over LDS-staged activations (16*XT tokens).  The weight ring's first
+// PF chunks are requested before the activations are staged (stage() copies
+// them into LDS; the barrier follows), so both travel in the same round trip;
+// afterwards the A fragments come from LDS and only weights stream from
+// memory.
+template <int FMT, int NT, int XT, class STAGE, int PF = kloop_lds_depth<FMT, NT>()>
+OCR_DEV void kloop_lds(const uint8_t* const (&tile)[NT], int c0, int c1, STAGE stage, const uint16_t* xl, int ldl,
+                       int ntok, int nblk, int lane, float4v (&acc)[NT][XT]) {
+    constexpr int CB = Geom<FMT>::CB;
+    constexpr int SB = Geom<FMT>::SB;
+    WRegs wb[PF][NT];
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+        if (c0 + u < c1) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) load_wchunk<FMT>(tile[i] + (int64_t)(c0 + u) * CB, lane, wb[u][i]);
+        }
+    stage();
+    __syncthreads();
+    for (int c = c0; c < c1; c += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int cc = c + u;
+            if (cc < c1) {
+                half8v xa[SB][XT];
+                float4v xsum[SB][XT];
+                lds_xfrags<FMT, XT>(xl, ldl, ntok, cc, nblk, lane, xa);
+                xsums<FMT, XT>(xa, xsum);
+#pragma unroll
+                for (int i = 0; i < NT; ++i) chunk_mac<FMT, XT>(wb[u][i], xa, xsum, acc[i]);
+                if (cc + PF < c1) {
+#pragma unroll
+                    for (int i = 0; i < NT; ++i)
+                        load_wchunk<FMT>(tile[i] + (int64_t)(cc + PF) * CB, lane, wb[u][i]);
+                }
+            }
+        }
+    }
+}
+
+// LDS bytes for 16*xt tokens of k activations.  The LDS path is used when it
+// fits in 64 KiB and there are enough tokens to pay for the staging (with 1-3
+// tokens the fragments are cheaper to load alongside the weights).
+inline size_t lds_x_bytes(int k, int xt) { return (size_t)16 * xt * (k + 8) * 2; }
+inline bool use_lds_x(int k, int xt, int rows) { return rows >= 4 && lds_x_bytes(k, xt) <= 65536; }
+
 // Sums the accumulators of the KS waves that share a tile group (waves
 // g*KS .. g*KS+KS-1 of the workgroup) in a fixed order; the result is valid in
 // the first of them.  red: LDS scratch of 4 * NT * XT * 64 float4v.

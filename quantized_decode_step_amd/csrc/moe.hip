@@ -204,12 +204,13 @@ __global__ __launch_bounds__(1024) void route_group_kernel(MoeParams p) {
 // it for the expert kernels).  Router GEMV: wave w computes tile w % T over
 // k-split w / T (T = E/16 tiles), the k-splits are summed in a fixed order in
 // LDS; top-k reads the logits from LDS; the grouping works in LDS.
-template <int FMT, int XT>
+template <int FMT>
 __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const uint8_t* router, int H,
                                                             const uint16_t* x, int64_t ldx, const float* h_in,
                                                             const uint16_t* norm_w, float eps, uint16_t* x_out) {
     constexpr int CB = Geom<FMT>::CB;
-    __shared__ float4v red[2048];  // k-split partials, then the logits [32][E <= 256]
+    __shared__ float4v red[16 * 64];  // k-split partials of one pass
+    __shared__ float lg_s[32 * 256];  // logits [32][E <= 256]
     __shared__ int idx_s[256], rank_s[256], hist_s[4 * 256], counts_s[256], offsets_s[257], act_s[256];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = p.n_experts, T = E / 16;
@@ -225,37 +226,25 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
     const int cper = (int)((nch + nks - 1) / nks);
     const int c0 = ks * cper;
     const int c1 = ks < nks ? (int)min((int64_t)(c0 + cper), nch) : c0;
-    float4v acc[1][XT];
-#pragma unroll
-    for (int xt = 0; xt < XT; ++xt) acc[0][xt] = float4v{0.f, 0.f, 0.f, 0.f};
     const uint8_t* tp[1] = {router + (int64_t)tile * nch * CB};
     XDirect xs{x, ldx, p.rows};
-    kloop<FMT, 1, XT>(tp, c0, c1, xs, 0, H / 32, lane, acc);
-#pragma unroll
-    for (int xt = 0; xt < XT; ++xt) red[(wave * XT + xt) * 64 + lane] = acc[0][xt];
-    __syncthreads();
-    float lgv[XT][4];
-    if (wave < T) {
-#pragma unroll
-        for (int xt = 0; xt < XT; ++xt) {
-            float4v a = red[(wave * XT + xt) * 64 + lane];
-            for (int o = 1; o < nks; ++o) a += red[((wave + o * T) * XT + xt) * 64 + lane];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) lgv[xt][v] = a[v];
-        }
-    }
-    __syncthreads();
-    float* lg = (float*)red;  // [32][E] logits
-    if (wave < T) {
-#pragma unroll
-        for (int xt = 0; xt < XT; ++xt)
+    float* lg = lg_s;  // [32][E] logits
+    for (int tok0 = 0; tok0 < p.rows; tok0 += 16) {
+        float4v acc[1][1] = {{float4v{0.f, 0.f, 0.f, 0.f}}};
+        kloop<FMT, 1, 1>(tp, c0, c1, xs, tok0, H / 32, lane, acc);
+        red[wave * 64 + lane] = acc[0][0];
+        __syncthreads();
+        if (wave < T) {
+            float4v a = red[wave * 64 + lane];
+            for (int o = 1; o < nks; ++o) a += red[(wave + o * T) * 64 + lane];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int tok = 16 * xt + 4 * (lane >> 4) + v;
-                lg[tok * E + wave * 16 + (lane & 15)] = lgv[xt][v];
+                const int tok = tok0 + 4 * (lane >> 4) + v;
+                lg[tok * E + wave * 16 + (lane & 15)] = a[v];
             }
+        }
+        __syncthreads();
     }
-    __syncthreads();
     topk_rows(p, lg, E, idx_s);
     __syncthreads();
     group_pairs(p, GroupScratch{idx_s, rank_s, hist_s, counts_s, offsets_s, act_s});
@@ -270,10 +259,11 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
 // the expert's slots of a, fp32 y[slot][row].
 // ---------------------------------------------------------------------------
 
-template <int FMT, int XT, int KS, bool GLU>
+template <int FMT, int XT, int KS, bool GLU, bool LDSX>
 __global__ __launch_bounds__(256) void grouped_kernel(GroupedParams p) {
     constexpr int CB = Geom<FMT>::CB;
     constexpr int NT = GLU ? 2 : 1;
+    extern __shared__ __align__(16) uint16_t xl_dyn[];
     __shared__ float4v red[(KS > 1) ? 4 * NT * XT * 64 : 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int item = blockIdx.x * (4 / KS) + wave / KS;
@@ -315,7 +305,17 @@ __global__ __launch_bounds__(256) void grouped_kernel(GroupedParams p) {
 #pragma unroll
             for (int xt = 0; xt < XT; ++xt) acc[i][xt] = float4v{0.f, 0.f, 0.f, 0.f};
         const int cc1 = my_more ? c1 : c0;
-        if constexpr (GLU) {
+        if constexpr (LDSX) {
+            // the workgroup's waves share one expert (groups_per_expert is a
+            // multiple of the waves per workgroup), hence one token set
+            const int ldl = xlds_stride(p.k);
+            auto stage = [&]() {
+                if constexpr (GLU)
+                    stage_x(XGather{p.x, p.ldx, p.vrows + (int64_t)vc * p.np, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
+                else stage_x(XDirect{p.x + (int64_t)off * p.ldx, p.ldx, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
+            };
+            kloop_lds<FMT, NT, XT>(tile, c0, cc1, stage, xl_dyn, ldl, cnt - tok0, nblk, lane, acc);
+        } else if constexpr (GLU) {
             XGather xs{p.x, p.ldx, p.vrows + (int64_t)vc * p.np, cnt};
             kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
         } else {
@@ -478,25 +478,31 @@ ocrdec_status check_moe(const ocrdec_moe_weights* w, int rows) {
 namespace {
 
 template <int FMT, bool GLU>
-void launch_grouped_fmt(const GroupedParams& p, int xt, int ks, int grid, hipStream_t s) {
-#define OCR_G(XT_, KS_)                                                                               \
-    if (xt == XT_ && ks == KS_) {                                                                    \
-        hipLaunchKernelGGL((grouped_kernel<FMT, XT_, KS_, GLU>), dim3(grid), dim3(256), 0, s, p);   \
-        return;                                                                                      \
+void launch_grouped_fmt(const GroupedParams& p, int xt, int ks, bool lds, int grid, hipStream_t s) {
+    const size_t lb = lds ? lds_x_bytes(p.k, xt) : 0;
+#define OCR_G(XT_, KS_)                                                                                          \
+    if (xt == XT_ && ks == KS_) {                                                                               \
+        if (lds) hipLaunchKernelGGL((grouped_kernel<FMT, XT_, KS_, GLU, true>), dim3(grid), dim3(256), lb, s, p); \
+        else hipLaunchKernelGGL((grouped_kernel<FMT, XT_, KS_, GLU, false>), dim3(grid), dim3(256), 0, s, p);    \
+        return;                                                                                                 \
     }
     OCR_G(1, 1) OCR_G(2, 1) OCR_G(1, 4) OCR_G(2, 4)
 #undef OCR_G
 }
 
 void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream_t s) {
-    const int xt = rows_hint <= 16 ? 1 : 2;
     const int64_t items = (int64_t)p.max_virt * p.groups_per_expert;
     const int ks = items >= 2048 ? 1 : 4;
+    // LDS staging needs every wave of a workgroup on the same expert; it uses
+    // 16-token passes (routed experts usually get far fewer tokens than rows)
+    const bool same_expert = (p.groups_per_expert % (4 / ks)) == 0;
+    const bool lds = use_lds_x(p.k, 1, rows_hint) && same_expert;
+    const int xt = lds ? 1 : (rows_hint <= 16 ? 1 : 2);
     const int grid = (int)((items + (4 / ks) - 1) / (4 / ks));
 #define OCR_F(F_)                                                                          \
     case F_:                                                                               \
-        if (glu) launch_grouped_fmt<F_, true>(p, xt, ks, grid, s);                         \
-        else launch_grouped_fmt<F_, false>(p, xt, ks, grid, s);                            \
+        if (glu) launch_grouped_fmt<F_, true>(p, xt, ks, lds, grid, s);                    \
+        else launch_grouped_fmt<F_, false>(p, xt, ks, lds, grid, s);                       \
         break;
     switch (fmt) {
         OCR_F(OCRDEC_F16)
@@ -549,15 +555,10 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     if (small) {
         // router GEMV, top-k and grouping in one workgroup
         const uint8_t* rw = (const uint8_t*)w->router.data;
-        const bool two = rows > 16;
 #define OCR_R(F_)                                                                                               \
     case F_:                                                                                                    \
-        if (two)                                                                                                \
-            hipLaunchKernelGGL((route_fused_kernel<F_, 2>), dim3(1), dim3(1024), 0, s, p, rw, H, x, ldx, h_norm,  \
-                               norm_in, eps_in, (uint16_t*)x);                                                   \
-        else                                                                                                    \
-            hipLaunchKernelGGL((route_fused_kernel<F_, 1>), dim3(1), dim3(1024), 0, s, p, rw, H, x, ldx, h_norm,  \
-                               norm_in, eps_in, (uint16_t*)x);                                                   \
+        hipLaunchKernelGGL((route_fused_kernel<F_>), dim3(1), dim3(1024), 0, s, p, rw, H, x, ldx, h_norm, norm_in, \
+                           eps_in, (uint16_t*)x);                                                                  \
         break;
         switch (w->router.fmt) {
             OCR_R(OCRDEC_F16)
