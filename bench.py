@@ -27,6 +27,36 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 SEED = 1003
 T0 = 100
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# Counter-measured HBM traffic of the LM-head kernel (rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE runs of `bench.py --mode lm`, calibrated on a copy of known size).  It
+# applies only while the kernel sources hash to the value recorded with it.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_argmax_traffic.md")
+KERNEL_SOURCES = ["common.hpp", "gemv_core.hpp", "gemv.hpp", "gemv.hip"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantized_decode_step_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """(bytes per launch, note) from the counter summary if it matches the
+    current kernel sources, else (None, reason)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter summary"
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.strip().startswith(("source-hash", "traffic-bytes-per-launch")):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source-hash") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return float(vals["traffic-bytes-per-launch"]), "rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0 (calibrated)"
 
 
 def parse():
@@ -170,6 +200,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
     lm_us = e0.elapsed_time(e1) * 1000.0 / args.lm_iters
+    traffic, traffic_note = recorded_traffic() if R == 1 else (None, "counters taken at 1 row")
     lm_bytes = d.vocab * d.hidden * 2.0 + R * d.hidden * 2.0
     lm_gbs = lm_bytes / (lm_us * 1e-6) / 1e9
 
@@ -205,7 +236,8 @@ def main():
         "roofline": {"kernel": "gemv_kernel<F16,4,1,1,ARGMAX> (LM head %dx%d + fused argmax, %d row(s))"
                                % (d.vocab, d.hidden, R),
                      "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_note": traffic_note,
                      "avg_us": round(lm_us, 2), "algorithmic_bytes": lm_bytes},
         "cpu_baseline": cpu,
         "setup_s": round(t_build, 1),

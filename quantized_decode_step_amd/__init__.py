@@ -112,9 +112,11 @@ EXPORTED = ["ocrdec_last_error", "ocrdec_version", "ocrdec_packed_bytes", "ocrde
 
 
 def _ptr(t) -> int | None:
-    """Device/host address of a torch tensor or numpy array (None -> NULL)."""
+    """Device/host address of a torch tensor, numpy array or raw int (None -> NULL)."""
     if t is None:
         return None
+    if isinstance(t, int):
+        return t
     if isinstance(t, np.ndarray):
         return t.ctypes.data
     return t.data_ptr()
