@@ -210,9 +210,9 @@ def main():
         cpu = cpu_baseline(model, d, args.cpu_seconds)
 
     line = {
-        "metric": "decode rows*steps/s (12-layer MoE step)",
+        "metric": "decode rows\u00b7steps/s (12-layer MoE step) + achieved HBM GB/s vs peak",
         "value": round(main_run["rows_steps_per_s"], 2),
-        "unit": "rows*steps/s",
+        "unit": "rows\u00b7steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -294,7 +294,7 @@ def cpu_baseline(model, d, budget_s: float):
         if time.time() - t0 >= budget_s:
             break
     el = time.time() - t0
-    return {"value": round(steps / el, 4), "unit": "rows*steps/s", "cores": int(cores), "kind": "oracle",
+    return {"value": round(steps / el, 4), "unit": "rows\u00b7steps/s", "cores": int(cores), "kind": "oracle",
             "sample": "%d step(s) of 1 row of the same 12-layer workload (prefix 1100, ring from t=%d), "
                       "numpy float64, %.1f s" % (steps, T0, el)}
 

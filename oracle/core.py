@@ -400,6 +400,7 @@ class StepResult:
     def __init__(self):
         self.tok = None            # int32 [R] (or None without LM head)
         self.hidden = None         # float64 [R][H] residual after the last layer
+        self.layer_in = []         # per layer: float64 [R][H] residual entering the layer
         self.final_x = None        # float64 [R][H] normalised input of the LM head (fp16 values)
         self.lm_top2 = None        # float64 [R][2] best and second logits (float32 values)
         self.topk_idx = []         # per MoE layer: int32 [R][k]
@@ -478,6 +479,7 @@ def decode_step(model, state, tok_in=None, hidden_in=None, forced_topk=None,
         h = f32(np.asarray(hidden_in, np.float64)[rows])
     moe_l = 0
     for l, lay in enumerate(model.layers):
+        res.layer_in.append(h.copy())
         res.new_k.append([])
         res.new_v.append([])
         res.attn_out.append([])

@@ -296,6 +296,24 @@ class DeviceModel:
                               _ptr(self.embed), _ptr(self.final_norm),
                               self.lm_head.desc if self.lm_head is not None else _empty_qmat(), layers)
 
+    def layer_view(self, first: int, count: int, with_head: bool):
+        """ModelDesc over layers [first, first+count) of this model, sharing its
+        device weights (bind the caches first).  The embedding is kept only for
+        first == 0 (otherwise the input comes from `hidden`); the final norm and
+        LM head only if with_head."""
+        n = self.desc.n_layers
+        if not (0 <= first and count >= 1 and first + count <= n):
+            raise ValueError("layer range [%d, %d) outside 0..%d" % (first, first + count, n))
+        layers = (LayerDesc * count)()
+        for i in range(count):
+            layers[i] = self.layers[first + i]
+        d = self.desc
+        view = ModelDesc(count, d.hidden, d.n_heads, d.head_dim, d.vocab, d.rope_theta, d.norm_eps,
+                         d.embed if first == 0 else None, d.final_norm if with_head else None,
+                         d.lm_head if with_head else _empty_qmat(), layers)
+        view._keep_layers = layers
+        return view
+
     def bind_caches(self, k_cache, v_cache):
         """Point every layer at its slice of caches [L][R][NH][cap][D] (torch fp16/int16)."""
         for i in range(self.desc.n_layers):

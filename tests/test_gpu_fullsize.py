@@ -1,9 +1,16 @@
 """Parity at full size, in the launch configurations the benchmark times.
 
-* The 12-layer decoder at 24 rows (prefix 1100, ring wrapping after four
-  steps): two sampled rows checked against a stored oracle trajectory
-  (tests/golden/decode_full_r24.npz, written by make_decode_fixture.py from
-  the oracle alone); the other rows are checked for valid tokens.
+* The 12-layer decoder at 24 rows (prefix 1100), layer by layer: each layer
+  run alone from the oracle's own input to that layer, for two sampled rows,
+  at generation index 124 and 128 (ring just wrapped), against
+  tests/golden/decode_layers_r24.npz (written by make_decode_fixture.py from
+  the oracle alone).  Each layer's residual must be within 2e-3 * rms.
+* The same decoder composed over 8 steps (the ring wraps after four), rows
+  0, 11 and 23 against tests/golden/decode_full_r24.npz, with tokens and the
+  sampled rows' routing forced to the oracle's: the GPU's own routing and
+  tokens bit-exact except near-ties within TRAJ_NEAR_TIE; the composed
+  hidden state, routing weights and the last layer's new keys within
+  TRAJ_TOL; both bounds derived from the oracle's own sensitivity (below).
 * The prefill-shaped MoE layer: 2048 tokens, router bias, Q4_0 experts.
 * The sink-augmented attention block with int8-asymmetric projections:
   hidden 512, 8 heads of 64, 350 and 3000 cached positions.
@@ -20,6 +27,20 @@ from tests.gpu_util import NEAR_TIE, assert_close, assert_close_f16, f16_tensor,
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
+# The composed 12-layer residual cannot meet 2e-3 * rms against the oracle for
+# any fp32 implementation: perturbing only the oracle's own matrix-vector
+# products by relative noise of 3e-7 (fp32 accumulation size), with its routing
+# held fixed, moves its hidden state by up to 5.0e-3 * rms (median <= 1e-3)
+# and its router logits by up to 3.3e-3, because the fp16 storage points turn
+# the noise into whole-ulp flips that compound from layer to layer
+# (tests/golden/decode_sensitivity.py measures it).  The trajectory bounds are
+# twice the hidden-state spread and three times the logit spread (a decision
+# compares two logits); each single layer, from the oracle's input, is held to
+# 2e-3 * rms and the 1e-3 near-tie rule.
+TRAJ_TOL = 1e-2
+TRAJ_MEDIAN_TOL = 2e-3
+TRAJ_NEAR_TIE = 1e-2
+
 
 @pytest.fixture(scope="module")
 def q():
@@ -29,18 +50,102 @@ def q():
     return qd
 
 
-def test_decode_full_12_layers_24_rows(q):
+@pytest.fixture(scope="module")
+def full_model(q):
+    fx = np.load(os.path.join(GOLDEN, "decode_layers_r24.npz"))
+    d = synth.dims_full()
+    model = synth.make_model(d, int(fx["seed"]))
+    return d, model, q.DeviceModel(model)
+
+
+@pytest.mark.parametrize("case", ["a", "b"])
+def test_decode_full_each_layer_24_rows(q, full_model, case):
+    """Every layer of the full decoder, run alone (rows 24, launch as in the
+    benchmark) from the oracle's residual entering it; the last one also runs
+    the final norm, the LM head and the argmax."""
+    import torch
+    fx = np.load(os.path.join(GOLDEN, "decode_layers_r24.npz"))
+    seed, R = int(fx["seed"]), int(fx["rows"])
+    sampled = [int(r) for r in fx["sampled"]]
+    t = int(fx[case + "_t"])
+    d, model, dm = full_model
+    print("[case] full decoder per layer R=%d t=%d sampled=%s seed=%d" % (R, t, sampled, seed), flush=True)
+    st = synth.make_state(d, seed, [d.prefix_cap] * R, [t] * R)
+    ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+    del st
+    dm.bind_caches(ds.k_cache, ds.v_cache)
+    K, H = d.top_k, d.hidden
+    cap_idx = torch.zeros((1, R, K), dtype=torch.int32, device="cuda")
+    cap_w = torch.zeros((1, R, K), dtype=torch.float32, device="cuda")
+    top2 = torch.zeros((R, 2), dtype=torch.float32, device="cuda")
+    cap = q.StepCapture(cap_idx.data_ptr(), cap_w.data_ptr(), top2.data_ptr())
+    tok_out = torch.zeros(R, dtype=torch.int32, device="cuda")
+    layer_in = fx[case + "_layer_in"].astype(np.float64)      # [L][2][H]
+    slot = d.prefix_cap + t % d.ring_cap
+    moe_l = 0
+    worst = 0.0
+    for l in range(d.n_layers):
+        last = l == d.n_layers - 1
+        view = dm.layer_view(l, 1, with_head=last)
+        ds.gen_index.fill_(t)
+        if l == 0:
+            hidden = torch.zeros((R, H), dtype=torch.float32, device="cuda")
+            tin = torch.from_numpy(fx[case + "_tok_in"].astype(np.int32)).cuda()
+        else:
+            # rows that are not sampled carry unrelated inputs of the same scale
+            scale = np.sqrt(np.mean(layer_in[l] ** 2))
+            h_in = synth.normal_f64(synth.stream_id(seed, "layer-fill", t, l), (R, H)) * scale
+            h_in[sampled] = layer_in[l]
+            hidden = torch.from_numpy(h_in.astype(np.float32)).cuda()
+            tin = None
+        wsb = q.ocrdec_step_workspace_bytes(view, ds.desc)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        q.ocrdec_decode_step(view, ds.desc, tin, hidden, tok_out if last else None, None, cap, ws, wsb)
+        torch.cuda.synchronize()
+        assert np.all(ds.gen_index.cpu().numpy() == t + 1)
+        g_hid = hidden.cpu().numpy().astype(np.float64)
+        ref_out = fx[case + "_hidden"] if last else fx[case + "_layer_in"][l + 1]
+        kc = ds.k_cache[l].cpu().numpy().view(np.float16)
+        vc = ds.v_cache[l].cpu().numpy().view(np.float16)
+        for i, r in enumerate(sampled):
+            what = "case %s layer %d row %d" % (case, l, r)
+            assert_close_f16(kc[r, :, slot].astype(np.float64), fx[case + "_new_k"][l][i], what + " new k")
+            assert_close_f16(vc[r, :, slot].astype(np.float64), fx[case + "_new_v"][l][i], what + " new v")
+            if model.layers[l].is_moe:
+                g_idx = cap_idx[0, r].cpu().numpy()
+                if not np.array_equal(g_idx, fx[case + "_topk_idx"][moe_l][i]):
+                    gap = fx[case + "_router_gap"][moe_l][i]
+                    assert gap < NEAR_TIE, "%s: routing differs (gap %.3g)" % (what, gap)
+                    print("[near-tie] routing", what, "gap", gap)
+                    continue
+                assert_close(cap_w[0, r].cpu().numpy(), fx[case + "_topk_w"][moe_l][i], what + " routing weights")
+            worst = max(worst, assert_close(g_hid[r], ref_out[i], what + " residual"))
+            if last:
+                g_tok = int(tok_out[r].item())
+                if g_tok != fx[case + "_tok"][i]:
+                    gap = fx[case + "_lm_top2"][i][0] - fx[case + "_lm_top2"][i][1]
+                    assert gap < NEAR_TIE, "%s: token %d vs %d (gap %.3g)" % (what, g_tok, fx[case + "_tok"][i], gap)
+                    print("[near-tie] token", what, "gap", gap)
+        if model.layers[l].is_moe:
+            moe_l += 1
+    print("[result] worst per-layer residual error %.3g rms" % worst)
+
+
+def test_decode_full_12_layers_24_rows(q, full_model):
+    """Eight composed steps; tokens are teacher-forced and the sampled rows'
+    routing is forced to the oracle's, so a near-tie (where both choices are
+    correct) does not part the trajectories.  The GPU still reports its own
+    choice, which must equal the oracle's except at logged near-ties."""
     import torch
     fx = np.load(os.path.join(GOLDEN, "decode_full_r24.npz"))
     seed, R, t0, steps = int(fx["seed"]), int(fx["rows"]), int(fx["t0"]), int(fx["steps"])
     sampled = [int(r) for r in fx["sampled"]]
     print("[case] full decoder R=%d t0=%d steps=%d sampled=%s seed=%d" % (R, t0, steps, sampled, seed), flush=True)
-    d = synth.dims_full()
-    model = synth.make_model(d, seed)
+    d, _, dm = full_model
+    assert seed == int(np.load(os.path.join(GOLDEN, "decode_layers_r24.npz"))["seed"])
     st = synth.make_state(d, seed, [d.prefix_cap] * R, [t0] * R)
-    dm = q.DeviceModel(model)
-    del model
     ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+    del st
     dm.bind_caches(ds.k_cache, ds.v_cache)
     wsb = q.ocrdec_step_workspace_bytes(dm.desc, ds.desc)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
@@ -53,10 +158,13 @@ def test_decode_full_12_layers_24_rows(q):
     hidden = torch.zeros((R, d.hidden), dtype=torch.float32, device="cuda")
     tok_out = torch.zeros(R, dtype=torch.int32, device="cuda")
     tok = synth.first_tokens(d, seed, R)
-    live = {r: True for r in sampled}
+    ties = 0
     for step in range(steps):
         tok[sampled] = fx["tok_in"][step]
-        q.ocrdec_decode_step(dm.desc, ds.desc, torch.from_numpy(tok).cuda(), hidden, tok_out, None, cap, ws, wsb)
+        forced = np.full((n_moe, R, K), -1, np.int32)
+        forced[:, sampled] = fx["topk_idx"][step]
+        q.ocrdec_decode_step(dm.desc, ds.desc, torch.from_numpy(tok).cuda(), hidden, tok_out,
+                             torch.from_numpy(forced).cuda(), cap, ws, wsb)
         torch.cuda.synchronize()
         g_tok = tok_out.cpu().numpy()
         assert np.all((g_tok >= 0) & (g_tok < d.vocab))
@@ -64,31 +172,32 @@ def test_decode_full_12_layers_24_rows(q):
         g_hid = hidden.cpu().numpy().astype(np.float64)
         kc = ds.k_cache.cpu().numpy().view(np.float16) if step in (0, steps - 1) else None
         for i, r in enumerate(sampled):
-            if not live[r]:
-                continue
-            # routing: bit-exact unless the oracle's own gap is a near-tie (then the row's
-            # trajectories legitimately part and the row is no longer compared)
+            # the GPU's own routing: bit-exact unless the oracle's gap is a near-tie
             for ml in range(n_moe):
                 if not np.array_equal(g_idx[ml, r], fx["topk_idx"][step][ml][i]):
                     gap = fx["router_gap"][step][ml][i]
-                    assert gap < NEAR_TIE, "step %d layer %d row %d: routing differs (gap %.3g)" % (step, ml, r, gap)
+                    assert gap < TRAJ_NEAR_TIE, "step %d layer %d row %d: routing differs (gap %.3g)" % (
+                        step, ml, r, gap)
                     print("[near-tie] routing step", step, "layer", ml, "row", r, "gap", gap)
-                    live[r] = False
-                    break
-            if not live[r]:
-                continue
-            assert_close(g_w[:, r], fx["topk_w"][step][:, i], "step %d row %d routing weights" % (step, r))
-            assert_close(g_hid[r], fx["hidden"][step][i], "step %d row %d hidden" % (step, r))
+                    ties += 1
+            assert_close(g_w[:, r], fx["topk_w"][step][:, i], "step %d row %d routing weights" % (step, r),
+                         tol=TRAJ_TOL)
+            assert_close(g_hid[r], fx["hidden"][step][i], "step %d row %d hidden" % (step, r), tol=TRAJ_TOL)
+            dev = np.abs(g_hid[r] - fx["hidden"][step][i]) / np.sqrt(np.mean(fx["hidden"][step][i] ** 2.0))
+            assert np.median(dev) <= TRAJ_MEDIAN_TOL, "step %d row %d hidden: median %.3g" % (step, r, np.median(dev))
             if g_tok[r] != fx["tok"][step][i]:
                 gap = fx["lm_top2"][step][i][0] - fx["lm_top2"][step][i][1]
-                assert gap < NEAR_TIE, "step %d row %d: token %d vs %d (gap %.3g)" % (
+                assert gap < TRAJ_NEAR_TIE, "step %d row %d: token %d vs %d (gap %.3g)" % (
                     step, r, g_tok[r], fx["tok"][step][i], gap)
                 print("[near-tie] token step", step, "row", r, "gap", gap)
             if kc is not None:
                 slot = d.prefix_cap + (t0 + step) % d.ring_cap
                 assert_close_f16(kc[0, r, :, slot].astype(np.float64), fx["new_k_first"][step][i], "layer 0 new k")
-                assert_close_f16(kc[-1, r, :, slot].astype(np.float64), fx["new_k_last"][step][i], "last layer new k")
+                assert_close_f16(kc[-1, r, :, slot].astype(np.float64), fx["new_k_last"][step][i], "last layer new k",
+                                 tol=TRAJ_TOL)
         tok = g_tok.copy()
+    decisions = steps * n_moe * len(sampled)
+    assert ties <= 0.05 * decisions, "%d routing near-ties among %d decisions" % (ties, decisions)
     assert np.all(ds.gen_index.cpu().numpy() == t0 + steps)
 
 
