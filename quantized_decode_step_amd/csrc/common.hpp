@@ -127,15 +127,36 @@ OCR_DEV float4v mfma16(half8v a, half8v b, float4v c) {
 }
 
 // Sum over all 64 lanes (result in every lane).
+// Wavefront reductions through DPP lane moves (VALU operations, no LDS round
+// trip): quad swaps, half-row and row mirrors give every lane its 16-lane row
+// total, two row broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2
+// and 3) complete it in lane 63, which is returned to every lane.
+template <int CTRL, int ROW_MASK = 0xF>
+OCR_DEV float dpp_move(float v, float old) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                 __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
+                                                                 false));
+}
+OCR_DEV float lane63(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
 OCR_DEV float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_move<0xB1>(v, 0.f);        // quad_perm [1,0,3,2]
+    v += dpp_move<0x4E>(v, 0.f);        // quad_perm [2,3,0,1]
+    v += dpp_move<0x141>(v, 0.f);       // row_half_mirror
+    v += dpp_move<0x140>(v, 0.f);       // row_mirror
+    v += dpp_move<0x142, 0xA>(v, 0.f);  // row_bcast:15
+    v += dpp_move<0x143, 0xC>(v, 0.f);  // row_bcast:31
+    return lane63(v);
 }
 OCR_DEV float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, dpp_move<0xB1>(v, v));
+    v = fmaxf(v, dpp_move<0x4E>(v, v));
+    v = fmaxf(v, dpp_move<0x141>(v, v));
+    v = fmaxf(v, dpp_move<0x140>(v, v));
+    v = fmaxf(v, dpp_move<0x142, 0xA>(v, v));
+    v = fmaxf(v, dpp_move<0x143, 0xC>(v, v));
+    return lane63(v);
 }
 
 OCR_DEV half8v bits_to_half8(uint4 q) { return __builtin_bit_cast(half8v, q); }
@@ -180,33 +201,38 @@ OCR_DEV half8v deq_u8(uint32_t lo, uint32_t hi) {
 
 OCR_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// x = fp16(h / sqrt(mean(h^2) + eps) * gamma) for one fp32 row of H <= 4096
-// values (H % 4 == 0) by one wavefront: every load is issued before the
-// first use, so the row costs one memory round trip.
-OCR_DEV void wave_rmsnorm_row(const float* h, const uint16_t* gamma, int H, float eps, uint16_t* x) {
+// x = fp16(h / sqrt(mean(h^2) + eps) * gamma) for one fp32 row of
+// H <= 256 * NV values (H % 4 == 0) by one wavefront: every load (row and
+// gain) is issued before the first use, so the row costs one memory round
+// trip.  The result goes to x and, if xl is non-NULL, also to xl (LDS).
+template <int NV = 16>
+OCR_DEV void wave_rmsnorm_row(const float* h, const uint16_t* gamma, int H, float eps, uint16_t* x,
+                              uint16_t* xl = nullptr) {
     const int lane = threadIdx.x & 63;
     const int n4 = H / 4;
-    float4 v[16];
+    float4 v[NV];
+    uint2 g[NV];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NV; ++i) {
         const int c4 = lane + 64 * i;
         v[i] = c4 < n4 ? ((const float4*)h)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        g[i] = c4 < n4 ? ((const uint2*)gamma)[c4] : make_uint2(0, 0);
     }
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    for (int i = 0; i < NV; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / (float)H + eps);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NV; ++i) {
         const int c4 = lane + 64 * i;
         if (c4 < n4) {
-            const uint2 g = ((const uint2*)gamma)[c4];
-            const uint32_t lo = (uint32_t)f2h(v[i].x * inv * h2f((uint16_t)(g.x & 0xFFFF))) |
-                                ((uint32_t)f2h(v[i].y * inv * h2f((uint16_t)(g.x >> 16))) << 16);
-            const uint32_t hi = (uint32_t)f2h(v[i].z * inv * h2f((uint16_t)(g.y & 0xFFFF))) |
-                                ((uint32_t)f2h(v[i].w * inv * h2f((uint16_t)(g.y >> 16))) << 16);
+            const uint32_t lo = (uint32_t)f2h(v[i].x * inv * h2f((uint16_t)(g[i].x & 0xFFFF))) |
+                                ((uint32_t)f2h(v[i].y * inv * h2f((uint16_t)(g[i].x >> 16))) << 16);
+            const uint32_t hi = (uint32_t)f2h(v[i].z * inv * h2f((uint16_t)(g[i].y & 0xFFFF))) |
+                                ((uint32_t)f2h(v[i].w * inv * h2f((uint16_t)(g[i].y >> 16))) << 16);
             ((uint2*)x)[c4] = make_uint2(lo, hi);
+            if (xl) ((uint2*)xl)[c4] = make_uint2(lo, hi);
         }
     }
 }

@@ -20,68 +20,144 @@ namespace ocrdec {
 // Routing and grouping (one workgroup of 1024 threads = 16 wavefronts)
 // ---------------------------------------------------------------------------
 
-// Top-k of the rows of `lg` ([rows][E], fp32, row stride ldl), one wavefront
-// per row: lane l holds experts l, l+64, ...; k rounds of a wave-wide argmax
-// with ties to the lower index (a NaN logit counts as -inf).  Writes the
-// experts used (forced ones if given), their renormalised weights and the
-// captures.
-OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl, int* idx_out) {
+// Top-k of the rows of `lg` ([rows][E], fp32, row stride ldl; global memory
+// or LDS; `bias` [E] added if non-NULL), one wavefront per row: lane l holds
+// experts l, l+64, ...; each of the K rounds takes the wave-wide maximum (a
+// DPP reduction) and the lowest expert holding it (a ballot), so ties go to
+// the lower index; a NaN logit counts as -inf and a taken expert drops out.
+// Writes the experts used (forced ones if given) to idx_out [rows][K], their
+// renormalised weights and the captures.
+OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl, const float* bias, int* idx_out) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int E = p.n_experts, K = p.top_k;
+    const float taken = __builtin_nanf("");
     for (int r = wave; r < p.rows; r += nw) {
+        const float* l = lg + (int64_t)r * ldl;
         float v[4];
-        uint32_t taken = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = lane + 64 * j;
             float x = -INFINITY;
             if (e < E) {
-                x = lg[(int64_t)r * ldl + e] + (p.bias ? p.bias[e] : 0.f);
+                x = l[e] + (bias ? bias[e] : 0.f);
                 if (!(x == x)) x = -INFINITY;
             }
-            v[j] = x;
+            v[j] = e < E ? x : taken;
         }
-        int own = 0;  // lane j < K keeps the j-th choice
-        for (int j = 0; j < K; ++j) {
-            float bv = -INFINITY;
-            int be = 0x7fffffff;
+        int own = 0;  // lane k < K keeps the k-th choice
+        for (int k = 0; k < K; ++k) {
+            const float m = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+            int e = 0;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int e = lane + 64 * jj;
-                if (e < E && !((taken >> jj) & 1) && (v[jj] > bv || be == 0x7fffffff)) {
-                    bv = v[jj];
-                    be = e;
+            for (int j = 0; j < 4; ++j) {
+                const unsigned long long b = __ballot(v[j] == m);
+                if (b) {
+                    e = 64 * j + __ffsll((long long)b) - 1;
+                    break;
                 }
             }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oe = __shfl_xor(be, o, 64);
-                if (oe != 0x7fffffff && (be == 0x7fffffff || ov > bv || (ov == bv && oe < be))) {
-                    bv = ov;
-                    be = oe;
-                }
-            }
-            if ((be & 63) == lane) taken |= 1u << (be >> 6);
-            if (lane == j) own = be;
+            if ((e & 63) == lane) v[e >> 6] = taken;
+            if (lane == k) own = e;
         }
         int use = own;
         const bool forced = p.forced && p.forced[(int64_t)r * K] >= 0;
         if (forced && lane < K) use = p.forced[(int64_t)r * K + lane];
         use = min(max(use, 0), E - 1);  // device data: keep every index in range
-        float l = -INFINITY;
-        if (lane < K) l = lg[(int64_t)r * ldl + use] + (p.bias ? p.bias[use] : 0.f);
-        const float m = wave_max(l);
-        const float ex = lane < K ? __expf(l - m) : 0.f;
+        float lk = -INFINITY;
+        if (lane < K) lk = l[use] + (bias ? bias[use] : 0.f);
+        const float m = wave_max(lk);
+        const float ex = lane < K ? __expf(lk - m) : 0.f;
         const float den = wave_sum(ex);
         if (lane < K) {
             const float w = ex / den;
-            idx_out[(int64_t)r * K + lane] = use;
+            idx_out[r * K + lane] = use;
             p.w[(int64_t)r * K + lane] = w;
             if (p.cap_idx) p.cap_idx[(int64_t)r * K + lane] = own;
             if (p.cap_w) p.cap_w[(int64_t)r * K + lane] = w;
         }
     }
+}
+
+// Grouping of up to 256 (row, rank) pairs in LDS.  Every expert keeps a
+// 256-bit mask of the pairs routed to it; a pair's place among its expert's
+// pairs (stable: by row, then rank) is the popcount of the mask below it.
+// Outputs: perm/inv, vrows[slot] = the row of every grouped slot (routed
+// slots [0, NP), then shared expert s at NP + s*R + row) and the list of
+// work entries virt[v] = (expert, first slot, token count <= 16): the shared
+// experts' row blocks first (their work is the largest), then each routed
+// expert's tokens in blocks of 16.  mask_s: LDS [E][4] u64,
+// counts_s/offsets_s: LDS [E(+1)].
+OCR_DEV void group_pairs_small(const MoeParams& p, const int* idx_s, unsigned long long* mask_s, int* counts_s,
+                               int* offsets_s) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int R = p.rows, E = p.n_experts, K = p.top_k, S = p.n_shared;
+    const int NP = R * K;
+    const int rb = (R + 15) / 16;  // row blocks of a shared expert
+    for (int i = tid; i < 4 * E; i += blockDim.x) mask_s[i] = 0ull;
+    __syncthreads();
+    for (int pi = tid; pi < NP; pi += blockDim.x)
+        atomicOr(&mask_s[idx_s[pi] * 4 + (pi >> 6)], 1ull << (pi & 63));
+    __syncthreads();
+    // counts, exclusive offsets and the work list: wave 0, four experts per lane
+    if (wave == 0) {
+        int cnt[4], tot = 0, nb = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 4 * lane + j;
+            cnt[j] = 0;
+            if (e < E)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) cnt[j] += __popcll(mask_s[e * 4 + w]);
+            tot += cnt[j];
+            nb += (cnt[j] + 15) >> 4;
+        }
+        int incl = tot, nbi = nb;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o, 64);
+            const int tb = __shfl_up(nbi, o, 64);
+            if (lane >= o) {
+                incl += t;
+                nbi += tb;
+            }
+        }
+        int base = incl - tot, vb = S * rb + nbi - nb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 4 * lane + j;
+            if (e < E) {
+                counts_s[e] = cnt[j];
+                offsets_s[e] = base;
+                for (int b = 0; 16 * b < cnt[j]; ++b)
+                    p.virt[vb++] = make_int4(e, base + 16 * b, min(16, cnt[j] - 16 * b), 0);
+            }
+            base += cnt[j];
+        }
+        for (int i = lane; i < S * rb; i += 64) {
+            const int sx = i / rb, b = i % rb;
+            p.virt[i] = make_int4(E + sx, NP + sx * R + 16 * b, min(16, R - 16 * b), 0);
+        }
+        if (lane == 63) {
+            offsets_s[E] = incl;
+            p.n_virt[0] = S * rb + nbi;
+        }
+    }
+    __syncthreads();
+    for (int pi = tid; pi < NP; pi += blockDim.x) {
+        const int e = idx_s[pi], wd = pi >> 6;
+        int t = __popcll(mask_s[e * 4 + wd] & ((1ull << (pi & 63)) - 1ull));
+        for (int w = 0; w < wd; ++w) t += __popcll(mask_s[e * 4 + w]);
+        const int pos = offsets_s[e] + t;
+        p.perm[pos] = pi;
+        p.inv[pi] = pos;
+        p.vrows[pos] = pi / K;
+        if (p.cap_perm) p.cap_perm[pos] = pi;
+    }
+    for (int i = tid; i < S * R; i += blockDim.x) p.vrows[NP + i] = i % R;
+    if (p.cap_counts)
+        for (int e = tid; e < E; e += blockDim.x) p.cap_counts[e] = counts_s[e];
+    if (p.cap_offsets)
+        for (int e = tid; e <= E; e += blockDim.x) p.cap_offsets[e] = offsets_s[e];
 }
 
 // Scratch of the grouping: LDS for decode-sized batches, the workspace
@@ -92,15 +168,14 @@ struct GroupScratch {
     int* hist;       // [nchunk][E]
     int* counts;     // [E]
     int* offsets;    // [E + 1]
-    int* act_of;     // [E] index of an expert in the active list
 };
 
-// Stable counting sort of the (row, rank) pairs by expert and the list of
-// active experts (routed experts with tokens, then the shared experts).
-// Outputs: perm/inv, and per active expert v: virt[v] = (expert, first
-// grouped slot, token count) and vrows[v * NP + t] = the row of its token t.
+// Stable counting sort of the (row, rank) pairs by expert (any number of
+// pairs; the scratch is in the workspace).
+// Outputs: perm/inv, vrows[slot] = the row of every grouped slot (as in
+// group_pairs_small) and the work list virt[v] = (expert, first slot, token
+// count): the shared experts first, then every active routed expert.
 OCR_DEV void group_pairs(const MoeParams& p, const GroupScratch& g) {
-    __shared__ int n_act_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int R = p.rows, E = p.n_experts, K = p.top_k, S = p.n_shared;
     const int NP = R * K;
@@ -155,34 +230,28 @@ OCR_DEV void group_pairs(const MoeParams& p, const GroupScratch& g) {
             }
             const int excl = base + incl - cnt;
             if (e < E) g.offsets[e] = excl;
-            if (e < E && cnt > 0) {
-                const int v = act + ai - 1;
-                p.virt[v] = make_int4(e, excl, cnt, 0);
-                g.act_of[e] = v;
-            }
+            if (e < E && cnt > 0) p.virt[S + act + ai - 1] = make_int4(e, excl, cnt, 0);
             base += __shfl(incl, 63, 64);
             act += __shfl(ai, 63, 64);
         }
         if (lane == 0) {
             g.offsets[E] = base;
-            for (int s = 0; s < S; ++s) p.virt[act + s] = make_int4(E + s, NP + s * R, R, 0);
+            for (int s = 0; s < S; ++s) p.virt[s] = make_int4(E + s, NP + s * R, R, 0);
             p.n_virt[0] = act + S;
-            n_act_s = act;
         }
     }
     __syncthreads();
 
-    // scatter: grouped position of every pair; the row list of every expert
+    // scatter: grouped position and row of every pair
     for (int pi = tid; pi < NP; pi += blockDim.x) {
         const int e = g.idx[pi];
         const int t = g.hist[(int64_t)(pi / 64) * E + e] + g.rank[pi];
         const int pos = g.offsets[e] + t;
         p.perm[pos] = pi;
         p.inv[pi] = pos;
-        p.vrows[(int64_t)g.act_of[e] * NP + t] = pi / K;
+        p.vrows[pos] = pi / K;
     }
-    const int act = n_act_s;
-    for (int i = tid; i < S * R; i += blockDim.x) p.vrows[(int64_t)(act + i / R) * NP + i % R] = i % R;
+    for (int i = tid; i < S * R; i += blockDim.x) p.vrows[NP + i] = i % R;
     __syncthreads();
     if (p.cap_counts)
         for (int e = tid; e < E; e += blockDim.x) p.cap_counts[e] = g.counts[e];
@@ -194,32 +263,30 @@ OCR_DEV void group_pairs(const MoeParams& p, const GroupScratch& g) {
 
 // Routing of many rows: logits come from a separate router GEMV.
 __global__ __launch_bounds__(1024) void route_group_kernel(MoeParams p) {
-    topk_rows(p, p.logits, p.n_experts, p.idx);
+    topk_rows(p, p.logits, p.n_experts, p.bias, p.idx);
     __syncthreads();
-    group_pairs(p, GroupScratch{p.idx, p.rank, p.hist, p.counts, p.offsets, p.act_of});
+    group_pairs(p, GroupScratch{p.idx, p.rank, p.hist, p.counts, p.offsets});
 }
 
-// Routing of up to 32 rows in one workgroup.  Optionally it first forms the
-// MoE input x = fp16(RMSNorm(h) * gamma) from the fp32 residual (and writes
-// it for the expert kernels).  Router GEMV: wave w computes tile w % T over
-// k-split w / T (T = E/16 tiles), the k-splits are summed in a fixed order in
-// LDS; top-k reads the logits from LDS; the grouping works in LDS.
-template <int FMT>
+// Routing of up to 32 rows in one workgroup.  Router GEMV: wave w computes
+// tile w % T over k-split w / T (T = E/16 tiles); its first router chunks are
+// requested before anything else, then the MoE input is staged in LDS: either
+// formed here, x = fp16(RMSNorm(h) * gamma) from the fp32 residual (also
+// written out for the expert kernels), or copied from x.  The k-splits are
+// summed in a fixed order in LDS; top-k reads the logits from LDS; the
+// grouping works in LDS.  Dynamic LDS: rows * (H + 8) halves.
+template <int FMT, int NV>
 __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const uint8_t* router, int H,
                                                             const uint16_t* x, int64_t ldx, const float* h_in,
                                                             const uint16_t* norm_w, float eps, uint16_t* x_out) {
     constexpr int CB = Geom<FMT>::CB;
+    extern __shared__ __align__(16) uint16_t xl_dyn[];
     __shared__ float4v red[16 * 64];  // k-split partials of one pass
     __shared__ float lg_s[32 * 256];  // logits [32][E <= 256]
-    __shared__ int idx_s[256], rank_s[256], hist_s[4 * 256], counts_s[256], offsets_s[257], act_s[256];
+    __shared__ int use_s[256], counts_s[256], offsets_s[257];
+    __shared__ unsigned long long mask_s[4 * 256];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int E = p.n_experts, T = E / 16;
-    if (norm_w) {
-        for (int r = wave; r < p.rows; r += 16) wave_rmsnorm_row(h_in + (int64_t)r * H, norm_w, H, eps, x_out + (int64_t)r * ldx);
-        __threadfence_block();
-        __syncthreads();
-        x = x_out;
-    }
+    const int E = p.n_experts, T = E / 16, R = p.rows;
     const int nks = 16 / T;
     const int tile = wave % T, ks = wave / T;
     const int64_t nch = n_chunks_dev<FMT>(H);
@@ -227,11 +294,22 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
     const int c0 = ks * cper;
     const int c1 = ks < nks ? (int)min((int64_t)(c0 + cper), nch) : c0;
     const uint8_t* tp[1] = {router + (int64_t)tile * nch * CB};
-    XDirect xs{x, ldx, p.rows};
-    float* lg = lg_s;  // [32][E] logits
-    for (int tok0 = 0; tok0 < p.rows; tok0 += 16) {
+    const int ldl = xlds_stride(H);
+    int staged = 0;
+    auto stage = [&]() {
+        if (staged) return;
+        staged = 1;
+        if (norm_w) {
+            for (int r = wave; r < R; r += 16)
+                wave_rmsnorm_row<NV>(h_in + (int64_t)r * H, norm_w, H, eps, x_out + (int64_t)r * ldx,
+                                     xl_dyn + r * ldl);
+        } else {
+            stage_x(XDirect{x, ldx, R}, 0, R, H, xl_dyn, ldl);
+        }
+    };
+    for (int tok0 = 0; tok0 < R; tok0 += 16) {
         float4v acc[1][1] = {{float4v{0.f, 0.f, 0.f, 0.f}}};
-        kloop<FMT, 1, 1>(tp, c0, c1, xs, tok0, H / 32, lane, acc);
+        kloop_lds<FMT, 1, 1, decltype(stage), 4>(tp, c0, c1, stage, xl_dyn + tok0 * ldl, ldl, R - tok0, H / 32, lane, acc);
         red[wave * 64 + lane] = acc[0][0];
         __syncthreads();
         if (wave < T) {
@@ -240,15 +318,19 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int tok = tok0 + 4 * (lane >> 4) + v;
-                lg[tok * E + wave * 16 + (lane & 15)] = a[v];
+                const int e = wave * 16 + (lane & 15);
+                lg_s[tok * E + e] = a[v] + (p.bias ? p.bias[e] : 0.f);
             }
         }
         __syncthreads();
     }
-    topk_rows(p, lg, E, idx_s);
+    topk_rows(p, lg_s, E, nullptr, use_s);
     __syncthreads();
-    group_pairs(p, GroupScratch{idx_s, rank_s, hist_s, counts_s, offsets_s, act_s});
+    group_pairs_small(p, use_s, mask_s, counts_s, offsets_s);
 }
+
+// Dynamic LDS of route_fused_kernel.
+inline size_t route_lds_bytes(int rows, int H) { return (size_t)rows * (H + 8) * 2; }
 
 // ---------------------------------------------------------------------------
 // Grouped expert GEMV
@@ -260,7 +342,7 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
 // ---------------------------------------------------------------------------
 
 template <int FMT, int XT, int KS, bool GLU, bool LDSX>
-__global__ __launch_bounds__(256) void grouped_kernel(GroupedParams p) {
+__global__ __launch_bounds__(256, 2) void grouped_kernel(GroupedParams p) {
     constexpr int CB = Geom<FMT>::CB;
     constexpr int NT = GLU ? 2 : 1;
     extern __shared__ __align__(16) uint16_t xl_dyn[];
@@ -311,12 +393,12 @@ __global__ __launch_bounds__(256) void grouped_kernel(GroupedParams p) {
             const int ldl = xlds_stride(p.k);
             auto stage = [&]() {
                 if constexpr (GLU)
-                    stage_x(XGather{p.x, p.ldx, p.vrows + (int64_t)vc * p.np, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
+                    stage_x(XGather{p.x, p.ldx, p.vrows + off, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
                 else stage_x(XDirect{p.x + (int64_t)off * p.ldx, p.ldx, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
             };
             kloop_lds<FMT, NT, XT>(tile, c0, cc1, stage, xl_dyn, ldl, cnt - tok0, nblk, lane, acc);
         } else if constexpr (GLU) {
-            XGather xs{p.x, p.ldx, p.vrows + (int64_t)vc * p.np, cnt};
+            XGather xs{p.x, p.ldx, p.vrows + off, cnt};
             kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
         } else {
             XDirect xs{p.x + (int64_t)off * p.ldx, p.ldx, cnt};
@@ -420,6 +502,19 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineParams p) {
 // Host side
 // ---------------------------------------------------------------------------
 
+// Entries of the work list: decode-sized batches split every expert's tokens
+// into blocks of 16 (shared experts: ceil(rows/16) blocks); larger batches
+// keep one entry per active expert.
+bool moe_small(int rows, const ocrdec_moe_weights* w) {
+    const int E = w->n_experts, K = w->top_k, H = w->hidden;
+    return rows <= 32 && E % 16 == 0 && E <= 256 && rows * K <= 256 && route_lds_bytes(rows, H) <= 96 * 1024;
+}
+int moe_max_virt(int rows, const ocrdec_moe_weights* w) {
+    const int E = w->n_experts, S = w->n_shared, NP = rows * w->top_k;
+    if (moe_small(rows, w)) return S * ((rows + 15) / 16) + std::min(E, NP) + NP / 16;
+    return std::min(E, NP) + S;
+}
+
 MoeWs carve_moe(void* ws, int rows, const ocrdec_moe_weights* w) {
     Carve cv(ws);
     MoeWs m;
@@ -434,10 +529,9 @@ MoeWs carve_moe(void* ws, int rows, const ocrdec_moe_weights* w) {
     m.offsets = cv.take<int32_t>(E + 1);
     m.perm = cv.take<int32_t>(NP);
     m.inv = cv.take<int32_t>(NP);
-    m.vrows = cv.take<int32_t>((size_t)(E + S) * NP);
-    m.act_of = cv.take<int32_t>(E);
+    m.vrows = cv.take<int32_t>(nslots);
     m.n_virt = cv.take<int32_t>(1);
-    m.virt = cv.take<int4>(E + S);
+    m.virt = cv.take<int4>(moe_max_virt(rows, w));
     m.a = cv.take<uint16_t>((size_t)nslots * w->d_ff);
     m.y = cv.take<float>((size_t)nslots * w->hidden);
     m.bytes = cv.off;
@@ -538,7 +632,6 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     p.perm = m.perm;
     p.inv = m.inv;
     p.vrows = m.vrows;
-    p.act_of = m.act_of;
     p.n_virt = m.n_virt;
     p.virt = m.virt;
     p.cap_idx = cap_idx ? cap_idx : (cap ? cap->topk_idx : nullptr);
@@ -546,7 +639,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     p.cap_counts = cap ? cap->counts : nullptr;
     p.cap_offsets = cap ? cap->offsets : nullptr;
     p.cap_perm = cap ? cap->perm : nullptr;
-    const bool small = rows <= 32 && E % 16 == 0 && E <= 256 && rows * K <= 256;
+    const bool small = moe_small(rows, w);
     if (norm_in && !small) {
         // the MoE input is the normalised residual: form it first
         hipLaunchKernelGGL(moe_norm_kernel, dim3(rows), dim3(256), 0, s, h_norm, norm_in, H, eps_in, (uint16_t*)x,
@@ -555,10 +648,14 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     if (small) {
         // router GEMV, top-k and grouping in one workgroup
         const uint8_t* rw = (const uint8_t*)w->router.data;
-#define OCR_R(F_)                                                                                               \
-    case F_:                                                                                                    \
-        hipLaunchKernelGGL((route_fused_kernel<F_>), dim3(1), dim3(1024), 0, s, p, rw, H, x, ldx, h_norm, norm_in, \
-                           eps_in, (uint16_t*)x);                                                                  \
+#define OCR_RL(F_, NV_)                                                                                     \
+    hipLaunchKernelGGL((route_fused_kernel<F_, NV_>), dim3(1), dim3(1024), route_lds_bytes(rows, H), s, p, rw, H, \
+                       x, ldx, h_norm, norm_in, eps_in, (uint16_t*)x)
+#define OCR_R(F_)                      \
+    case F_:                           \
+        if (H <= 1280) OCR_RL(F_, 5);  \
+        else if (H <= 2048) OCR_RL(F_, 8); \
+        else OCR_RL(F_, 16);           \
         break;
         switch (w->router.fmt) {
             OCR_R(OCRDEC_F16)
@@ -567,6 +664,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
             OCR_R(OCRDEC_U8A_G32)
         }
 #undef OCR_R
+#undef OCR_RL
     } else {
         GemvPlan pl = plan_gemv(w->router.fmt, E, H, rows, EPI_F32);
         GemvParams gp{};
@@ -580,7 +678,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         launch_gemv(w->router.fmt, EPI_F32, pl, gp, s);
         hipLaunchKernelGGL(route_group_kernel, dim3(1), dim3(1024), 0, s, p);
     }
-    const int max_virt = std::min(E, NP) + S;
+    const int max_virt = moe_max_virt(rows, w);
     // gate/up with SwiGLU
     {
         GroupedParams p{};

@@ -26,8 +26,7 @@ struct MoeParams {
     int32_t* offsets;
     int32_t* perm;
     int32_t* inv;
-    int32_t* vrows;    // [n_experts + n_shared][rows * top_k] rows of each active expert's tokens
-    int32_t* act_of;   // [n_experts] scratch
+    int32_t* vrows;    // [rows * top_k + n_shared * rows] row of every grouped slot
     int32_t* n_virt;
     int4* virt;        // [n_experts + n_shared] (expert, first slot, count, -)
     int32_t* cap_idx;
@@ -83,7 +82,6 @@ struct MoeWs {
     int32_t* perm;
     int32_t* inv;
     int32_t* vrows;
-    int32_t* act_of;
     int32_t* n_virt;
     int4* virt;
     uint16_t* a;
