@@ -16,6 +16,8 @@
 // it covers 8 keys.
 #include "attn.hpp"
 
+#include <cmath>
+
 namespace ocrdec {
 
 namespace {
@@ -58,11 +60,11 @@ OCR_DEV int ord_to_idx(const AttnParams& p, const Window& w, int o) {
     return o;
 }
 
-// RoPE (rotate-half) of lane pair (i, i + D/2) at position pos.  The angle
-// pos * theta^(-2i/D) is formed and reduced modulo 2*pi in double (positions
-// reach thousands of radians), then rotated with a float sincos on [-pi, pi].
-OCR_DEV void rope_pair(float x1, float x2, int i, int D, int pos, float theta, float& y1, float& y2) {
-    const double f = exp2(-(2.0 * i / D) * log2((double)theta));
+// RoPE (rotate-half) of lane pair (i, i + D/2) at position pos with
+// frequency f = theta^(-2i/D) (computed on the host in double).  The angle
+// pos * f is formed and reduced modulo 2*pi in double (positions reach
+// thousands of radians), then rotated with a float sincos on [-pi, pi].
+OCR_DEV void rope_pair(float x1, float x2, double f, int pos, float& y1, float& y2) {
     const double a = (double)pos * f;
     const double two_pi_hi = 6.283185307179586232, two_pi_lo = 2.4492935982947064e-16;
     const double n = rint(a * 0.15915494309189535);
@@ -77,8 +79,9 @@ OCR_DEV void rope_pair(float x1, float x2, int i, int D, int pos, float theta, f
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
-    constexpr int LPK = D / 8;        // lanes per key
-    constexpr int KPL = 64 / LPK;     // keys per wavefront load
+    constexpr int LPK = D / 8;             // lanes per key
+    constexpr int KPL = 64 / LPK;          // keys per wavefront load
+    constexpr int ITER = KPS / (4 * KPL);  // key groups per wavefront
     __shared__ float q_s[D];
     __shared__ __align__(16) uint16_t knew_s[D];
     __shared__ __align__(16) uint16_t vnew_s[D];
@@ -88,51 +91,74 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
 
     const int s = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int HD = p.n_heads * D;
+    // the projections do not depend on the window: request them first
+    const float* qkv = p.qkv + (int64_t)r * p.ld_qkv;
+    float xq1 = 0.f, xq2 = 0.f, xk1 = 0.f, xk2 = 0.f, xv = 0.f;
+    if (tid < D / 2) {
+        xq1 = qkv[h * D + tid];
+        xq2 = qkv[h * D + tid + D / 2];
+        xk1 = qkv[HD + h * D + tid];
+        xk2 = qkv[HD + h * D + tid + D / 2];
+    } else if (tid >= 64 && tid < 64 + D) {
+        xv = qkv[2 * HD + h * D + tid - 64];
+    }
     const Window w = row_window(p, r);
     const int o0 = s * KPS, o1 = min(o0 + KPS, w.nkeys);
     float* part = p.part + (((int64_t)r * p.n_heads + h) * p.n_split + s) * (D + 2);
     if (o0 >= o1) return;  // beyond this row's window: not counted below
     const bool has_new = (w.new_ord >= o0 && w.new_ord < o1);
-    const float* qkv = p.qkv + (int64_t)r * p.ld_qkv;
-    const int HD = p.n_heads * D;
+    const int64_t head_off = ((int64_t)r * p.n_heads + h) * p.cache_cap;
+
+    // ---- keys and values of this wavefront (wave w takes keys o0 + w*KPL +
+    // it*4*KPL, one key per lane group), all requested before any use; the
+    // new token's slot is taken from LDS instead
+    const int dsub = (lane % LPK) * 8;
+    uint4 kr[ITER], vr[ITER];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int o = o0 + wave * KPL + it * 4 * KPL + lane / LPK;
+        kr[it] = vr[it] = make_uint4(0, 0, 0, 0);
+        if (o < o1) {
+            const int ci = ord_to_idx(p, w, o);
+            if (ci != w.new_idx) {
+                kr[it] = *(const uint4*)(p.k_cache + (head_off + ci) * D + dsub);
+                vr[it] = *(const uint4*)(p.v_cache + (head_off + ci) * D + dsub);
+            }
+        }
+    }
     if (tid < D / 2) {
         const int i = tid;
         float y1, y2;
-        rope_pair(qkv[h * D + i], qkv[h * D + i + D / 2], i, D, w.pos, p.theta, y1, y2);
+        rope_pair(xq1, xq2, p.inv_freq[i], w.pos, y1, y2);
         q_s[i] = h2f(f2h(y1));
         q_s[i + D / 2] = h2f(f2h(y2));
         if (has_new) {
             float k1, k2;
-            rope_pair(qkv[HD + h * D + i], qkv[HD + h * D + i + D / 2], i, D, w.pos, p.theta, k1, k2);
+            rope_pair(xk1, xk2, p.inv_freq[i], w.pos, k1, k2);
             knew_s[i] = f2h(k1);
             knew_s[i + D / 2] = f2h(k2);
         }
     } else if (has_new && tid >= 64 && tid < 64 + D) {
-        const int i = tid - 64;
-        vnew_s[i] = f2h(qkv[2 * HD + h * D + i]);
+        vnew_s[tid - 64] = f2h(xv);
     }
     __syncthreads();
-    const int64_t head_off = ((int64_t)r * p.n_heads + h) * p.cache_cap;
     if (has_new && tid < D) {
         p.k_cache[(head_off + w.new_idx) * D + tid] = knew_s[tid];
         p.v_cache[(head_off + w.new_idx) * D + tid] = vnew_s[tid];
     }
 
-    // ---- scores: wave w takes keys o0 + w*KPL + j*4*KPL, lane group -> one key
-    const int dsub = (lane % LPK) * 8;
+    // ---- scores
     float qf[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) qf[i] = q_s[dsub + i];
-    constexpr int ITER = KPS / (4 * KPL);  // key groups per wavefront; unrolled so all loads issue first
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
         const int o = o0 + wave * KPL + it * 4 * KPL + lane / LPK;
         float dot = 0.f;
         if (o < o1) {
             const int ci = ord_to_idx(p, w, o);
-            uint4 kv;
-            if (ci == w.new_idx) kv = *(const uint4*)(knew_s + dsub);
-            else kv = *(const uint4*)(p.k_cache + (head_off + ci) * D + dsub);
+            const uint4 kv = ci == w.new_idx ? *(const uint4*)(knew_s + dsub) : kr[it];
             half8v kh = bits_to_half8(kv);
 #pragma unroll
             for (int i = 0; i < 8; ++i) dot = fmaf(qf[i], (float)kh[i], dot);
@@ -169,9 +195,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
         const int o = o0 + wave * KPL + it * 4 * KPL + lane / LPK;
         if (o < o1) {
             const int ci = ord_to_idx(p, w, o);
-            uint4 vv;
-            if (ci == w.new_idx) vv = *(const uint4*)(vnew_s + dsub);
-            else vv = *(const uint4*)(p.v_cache + (head_off + ci) * D + dsub);
+            const uint4 vv = ci == w.new_idx ? *(const uint4*)(vnew_s + dsub) : vr[it];
             half8v vh = bits_to_half8(vv);
             const float pj = sc_s[o - o0];
 #pragma unroll
@@ -260,6 +284,11 @@ size_t attn_ws_bytes(int rows, int n_heads, int head_dim, int cache_cap) {
     return attn_part_bytes(rows, n_heads, head_dim, cache_cap);
 }
 
+void attn_set_rope(AttnParams& p, float theta) {
+    for (int i = 0; i < 64; ++i)
+        p.inv_freq[i] = i < p.head_dim / 2 ? std::pow((double)theta, -2.0 * i / p.head_dim) : 0.0;
+}
+
 void launch_attn(const AttnParams& p, hipStream_t s) {
     dim3 g1(p.n_split, p.n_heads, p.rows);
     dim3 g2(p.n_heads, p.rows);
@@ -324,7 +353,7 @@ extern "C" ocrdec_status ocrdec_attn_decode(const ocrdec_attn_args* a, void* ws,
     p.prefix_len = a->prefix_len;
     p.gen_index = a->gen_index;
     p.sink = a->sink;
-    p.theta = a->rope_theta;
+    attn_set_rope(p, a->rope_theta);
     p.scale = a->scale;
     p.out = a->out;
     p.ld_out = a->ld_out;

@@ -15,7 +15,8 @@ struct AttnParams {
     const int32_t* prefix_len;
     const int32_t* gen_index;
     const float* sink;
-    float theta, scale;
+    float scale;
+    double inv_freq[64];  // RoPE frequencies theta^(-2i/head_dim), i < head_dim/2 (host-computed)
     uint16_t* out;
     int64_t ld_out;
     int n_split;
@@ -25,6 +26,7 @@ struct AttnParams {
 int attn_n_split(int cache_cap);
 size_t attn_part_bytes(int rows, int n_heads, int head_dim, int cache_cap);
 size_t attn_ws_bytes(int rows, int n_heads, int head_dim, int cache_cap);
+void attn_set_rope(AttnParams& p, float theta);
 void launch_attn(const AttnParams& p, hipStream_t s);
 ocrdec_status check_attn(const ocrdec_attn_args* a);
 

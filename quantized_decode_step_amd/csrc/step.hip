@@ -204,6 +204,25 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
 
     hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(64), 0, s, tok_in, m->embed, m->vocab, hidden, w.h,
                        m->layers[0].attn_norm, H, m->norm_eps, w.x);
+    // attention arguments shared by every layer (RoPE frequencies once per call)
+    AttnParams ap0{};
+    ap0.rows = R;
+    ap0.n_heads = m->n_heads;
+    ap0.head_dim = m->head_dim;
+    ap0.qkv = w.qkv;
+    ap0.ld_qkv = 3 * HD;
+    ap0.prefix_cap = st->prefix_cap;
+    ap0.ring_cap = st->ring_cap;
+    ap0.cache_cap = cache_cap;
+    ap0.prefix_len = st->prefix_len;
+    ap0.gen_index = st->gen_index;
+    ap0.sink = nullptr;
+    ap0.scale = 1.0f / sqrtf((float)m->head_dim);
+    ap0.out = w.o;
+    ap0.ld_out = HD;
+    ap0.n_split = attn_n_split(cache_cap);
+    ap0.part = w.attn_part;
+    attn_set_rope(ap0, m->rope_theta);
     int moe_l = 0;
     for (int l = 0; l < m->n_layers; ++l) {
         const ocrdec_layer& L = m->layers[l];
@@ -223,26 +242,9 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
         }
         // attention
         {
-            AttnParams ap{};
-            ap.rows = R;
-            ap.n_heads = m->n_heads;
-            ap.head_dim = m->head_dim;
-            ap.qkv = w.qkv;
-            ap.ld_qkv = 3 * HD;
+            AttnParams ap = ap0;
             ap.k_cache = L.k_cache;
             ap.v_cache = L.v_cache;
-            ap.prefix_cap = st->prefix_cap;
-            ap.ring_cap = st->ring_cap;
-            ap.cache_cap = cache_cap;
-            ap.prefix_len = st->prefix_len;
-            ap.gen_index = st->gen_index;
-            ap.sink = nullptr;
-            ap.theta = m->rope_theta;
-            ap.scale = 1.0f / sqrtf((float)m->head_dim);
-            ap.out = w.o;
-            ap.ld_out = HD;
-            ap.n_split = attn_n_split(cache_cap);
-            ap.part = w.attn_part;
             launch_attn(ap, s);
         }
         // O projection + residual
