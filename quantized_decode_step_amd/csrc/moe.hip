@@ -342,7 +342,7 @@ inline size_t route_lds_bytes(int rows, int H) { return (size_t)rows * (H + 8) *
 // ---------------------------------------------------------------------------
 
 template <int FMT, int XT, int KS, bool GLU, bool LDSX>
-__global__ __launch_bounds__(256, 2) void grouped_kernel(GroupedParams p) {
+__global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(GroupedParams p) {
     constexpr int CB = Geom<FMT>::CB;
     constexpr int NT = GLU ? 2 : 1;
     extern __shared__ __align__(16) uint16_t xl_dyn[];
@@ -590,7 +590,9 @@ void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream
     // LDS staging needs every wave of a workgroup on the same expert; it uses
     // 16-token passes (routed experts usually get far fewer tokens than rows)
     const bool same_expert = (p.groups_per_expert % (4 / ks)) == 0;
-    const bool lds = use_lds_x(p.k, 1, rows_hint) && same_expert;
+    // the down projection reads its activations contiguously: LDS staging pays
+    // for any row count there (and keeps three workgroups per CU)
+    const bool lds = (glu ? use_lds_x(p.k, 1, rows_hint) : lds_x_bytes(p.k, 1) <= 65536) && same_expert;
     const int xt = lds ? 1 : (rows_hint <= 16 ? 1 : 2);
     const int grid = (int)((items + (4 / ks) - 1) / (4 / ks));
 #define OCR_F(F_)                                                                          \
