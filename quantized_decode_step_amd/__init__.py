@@ -23,6 +23,13 @@ OCRDEC_OUT_F32, OCRDEC_OUT_F16 = 0, 1
 if not os.path.exists(LIB_PATH):
     raise ImportError("libocrdec.so is not built: run `python quantized_decode_step_amd/build.py` "
                       "(hipcc --offload-arch=gfx950)")
+try:
+    # PyTorch-ROCm carries its own HIP runtime; loading it first makes the
+    # library bind to that same runtime (one runtime per process), whatever
+    # the caller imports first.
+    import torch  # noqa: F401
+except ImportError:
+    pass
 _lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float

@@ -124,12 +124,14 @@ OCR_DEV void chunk_mac(const WRegs& w, const half8v (&xa)[Geom<FMT>::SB][XT],
     }
 }
 
-// Activation source: token i of the current x-tile set -> fp16 row pointer.
+// Activation source: token i of the current x-tile set -> fp16 row pointer
+// (row: NULL past the last token; rowc: clamped to the last token, rows >= 1).
 struct XDirect {
     const uint16_t* x;
     int64_t ld;
     int rows;
     OCR_DEV const uint16_t* row(int tok) const { return tok < rows ? x + (int64_t)tok * ld : nullptr; }
+    OCR_DEV const uint16_t* rowc(int tok) const { return x + (int64_t)min(tok, rows - 1) * ld; }
 };
 
 // Gathered activations: token i -> x[map[i]] (grouped MoE rows).
@@ -141,22 +143,35 @@ struct XGather {
     OCR_DEV const uint16_t* row(int tok) const {
         return tok < rows ? x + (int64_t)map[tok] * ld : nullptr;
     }
+    OCR_DEV const uint16_t* rowc(int tok) const { return x + (int64_t)map[min(tok, rows - 1)] * ld; }
 };
 
-// Loads the A fragments of chunk c for tokens [tok0, tok0 + 16*XT).
+// Loads the A fragments of chunk c for tokens [tok0, tok0 + 16*XT).  Every
+// lane issues its loads (clamped to a real token and block); mask_xfrags
+// zeroes what lies past the tokens or k once the data is used, so neither the
+// loads nor anything right after them waits on their data.
 template <int FMT, int XT, class XS>
 OCR_DEV void load_xfrags(const XS& xs, int tok0, int c, int nblk, int lane, half8v (&xa)[Geom<FMT>::SB][XT]) {
     constexpr int SB = Geom<FMT>::SB;
 #pragma unroll
     for (int xt = 0; xt < XT; ++xt) {
-        const uint16_t* p = xs.row(tok0 + 16 * xt + (lane & 15));
+        const uint16_t* p = xs.rowc(tok0 + 16 * xt + (lane & 15));
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
-            const int blk = c * SB + j;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (p && blk < nblk) v = *(const uint4*)(p + blk * 32 + 8 * (lane >> 4));
-            xa[j][xt] = bits_to_half8(v);
-        }
+        for (int j = 0; j < SB; ++j)
+            xa[j][xt] = bits_to_half8(*(const uint4*)(p + min(c * SB + j, nblk - 1) * 32 + 8 * (lane >> 4)));
+    }
+}
+
+template <int FMT, int XT, class XS>
+OCR_DEV void mask_xfrags(const XS& xs, int tok0, int c, int nblk, int lane, half8v (&xa)[Geom<FMT>::SB][XT]) {
+    constexpr int SB = Geom<FMT>::SB;
+    const half8v zero = {};
+#pragma unroll
+    for (int xt = 0; xt < XT; ++xt) {
+        const bool tok_ok = tok0 + 16 * xt + (lane & 15) < xs.rows;
+#pragma unroll
+        for (int j = 0; j < SB; ++j)
+            if (!(tok_ok && c * SB + j < nblk)) xa[j][xt] = zero;
     }
 }
 
@@ -186,40 +201,55 @@ constexpr int kloop_depth() {
 // in flight; each slot holds a chunk's weights AND its activation fragments,
 // loaded together, so waiting for the oldest slot (vector loads complete in
 // issue order) never waits for the younger prefetches.  The load of chunk
-// c+PF is issued as soon as chunk c has been consumed.
+// c+PF is issued as soon as chunk c has been consumed.  The steady-state loop
+// has no branches around its loads (the range is wavefront-uniform and the
+// prologue reloads the last chunk when the range is shorter than the ring),
+// so the compiler can wait for exactly the oldest slot instead of draining
+// every load in flight.
 template <int FMT, int NT, int XT, class XS, int PF = kloop_depth<FMT, NT, XT>()>
 OCR_DEV void kloop(const uint8_t* const (&tile)[NT], int c0, int c1, const XS& xs, int tok0, int nblk, int lane,
                    float4v (&acc)[NT][XT]) {
     constexpr int CB = Geom<FMT>::CB;
     constexpr int SB = Geom<FMT>::SB;
-    if (c0 >= c1) return;
+    const int n = __builtin_amdgcn_readfirstlane(c1 - c0);
+    const int cb = __builtin_amdgcn_readfirstlane(c0);
+    if (n <= 0) return;
     WRegs wb[PF][NT];
     half8v xb[PF][SB][XT];
+    auto fetch = [&](int u, int c) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u)
-        if (c0 + u < c1) {
+        for (int i = 0; i < NT; ++i) load_wchunk<FMT>(tile[i] + (int64_t)(cb + c) * CB, lane, wb[u][i]);
+        load_xfrags<FMT, XT>(xs, tok0, cb + c, nblk, lane, xb[u]);
+    };
+    auto use = [&](int u, int c) {
+        mask_xfrags<FMT, XT>(xs, tok0, cb + c, nblk, lane, xb[u]);
+        float4v xsum[SB][XT];
+        xsums<FMT, XT>(xb[u], xsum);
 #pragma unroll
-            for (int i = 0; i < NT; ++i) load_wchunk<FMT>(tile[i] + (int64_t)(c0 + u) * CB, lane, wb[u][i]);
-            load_xfrags<FMT, XT>(xs, tok0, c0 + u, nblk, lane, xb[u]);
-        }
-    for (int c = c0; c < c1; c += PF) {
+        for (int i = 0; i < NT; ++i) chunk_mac<FMT, XT>(wb[u][i], xb[u], xsum, acc[i]);
+    };
+#pragma unroll
+    for (int u = 0; u < PF; ++u) fetch(u, min(u, n - 1));
+    int it = 0;
+    for (; it + 2 * PF <= n; it += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
-            const int cc = c + u;
-            if (cc < c1) {
-                float4v xsum[SB][XT];
-                xsums<FMT, XT>(xb[u], xsum);
-#pragma unroll
-                for (int i = 0; i < NT; ++i) chunk_mac<FMT, XT>(wb[u][i], xb[u], xsum, acc[i]);
-                if (cc + PF < c1) {
-#pragma unroll
-                    for (int i = 0; i < NT; ++i)
-                        load_wchunk<FMT>(tile[i] + (int64_t)(cc + PF) * CB, lane, wb[u][i]);
-                    load_xfrags<FMT, XT>(xs, tok0, cc + PF, nblk, lane, xb[u]);
-                }
-            }
+            use(u, it + u);
+            fetch(u, it + u + PF);
+            __builtin_amdgcn_sched_barrier(0);  // keep the slots in issue order
         }
     }
+    // the last n - it chunks
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+        if (it + u < n) {
+            use(u, it + u);
+            if (it + u + PF < n) fetch(u, it + u + PF);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+        if (it + PF + u < n) use(u, it + PF + u);
 }
 
 // ---------------------------------------------------------------------------
