@@ -70,8 +70,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--lm-iters", type=int, default=50)
-    ap.add_argument("--mode", choices=["full", "lm"], default="full",
-                    help="lm: only the LM-head argmax loop and a device copy of known size (for counter runs)")
+    ap.add_argument("--mode", choices=["full", "lm", "prefill"], default="full",
+                    help="lm: only the LM-head argmax loop and a device copy of known size (for counter runs); "
+                         "prefill: only the prefill-shaped MoE layer (2048 tokens)")
+    ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--copy-mb", type=int, default=512, help="size of the calibration copy in --mode lm")
     return ap.parse_args()
 
@@ -113,6 +115,9 @@ def main():
     dev = torch.device("cuda:0")
     d = synth.dims_full()
     stream = torch.cuda.Stream()
+    if args.mode == "prefill":
+        print(json.dumps(prefill_moe(args, q, torch, dev, stream)), flush=True)
+        return
     if args.mode == "lm":
         lm = synth.random_qmat(d.fmt_lm, synth.stream_id(SEED, "lm_head"), d.vocab, d.hidden, d.w_std)
 
@@ -243,6 +248,48 @@ def main():
         "setup_s": round(t_build, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+PREFILL_SEED = 1005
+PREFILL_TOKENS = 2048
+
+
+def prefill_moe(args, q, torch, dev, stream):
+    """The prefill-shaped MoE layer: 2048 tokens, router bias ~N(0,1) (skewed
+    expert loads), 64 routed top-6 + 2 shared Q4_0 SwiGLU experts of 896.
+    Returns its time per call and the MFMA-path throughput (useful flops: every
+    routed and shared expert product, 2 flop per multiply-add)."""
+    import synth
+
+    class _Lay:
+        pass
+    d = synth.Dims(fmt_router=synth.Q8_0, fmt_expert=synth.Q4_0, fmt_shared=synth.Q4_0)
+    lay = _Lay()
+    for k_, v_ in synth.make_moe_weights(d, PREFILL_SEED, 0, with_bias=True).items():
+        setattr(lay, k_, v_)
+    T = PREFILL_TOKENS
+    x = synth.normal_f16(synth.stream_id(PREFILL_SEED, "x"), (T, d.hidden))
+    w, keep = q.moe_weights(lay, d.hidden, d.top_k)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    out = torch.zeros((T, d.hidden), dtype=torch.int16, device=dev)
+    wsb = q.ocrdec_moe_workspace_bytes(w, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            q.ocrdec_moe_layer(w, T, xd, out, False, None, None, ws, wsb, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.prefill_iters):
+            q.ocrdec_moe_layer(w, T, xd, out, False, None, None, ws, wsb, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / args.prefill_iters
+    H, F, K, S = d.hidden, d.expert_ff, d.top_k, d.n_shared
+    flops = 2.0 * T * (K + S) * (2 * F * H + H * F) + 2.0 * T * d.n_experts * H
+    wbytes = sum(m.data.size for m in (lay.exp_gate_up, lay.exp_down, lay.sh_gate_up, lay.sh_down, lay.router))
+    return {"mode": "prefill", "tokens": T, "us_per_layer": round(us, 2), "gflop": round(flops / 1e9, 2),
+            "tflops": round(flops / (us * 1e-6) / 1e12, 2), "frac_of_fp16_mfma_peak": round(flops / (us * 1e-6) / 2.5e15, 4),
+            "weight_MB": round(wbytes / 1e6, 1)}
 
 
 def lm_only(args, dm, d, q, torch, dev, stream):

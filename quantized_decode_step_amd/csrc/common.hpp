@@ -114,6 +114,7 @@ struct Carve {
 
 typedef _Float16 f16_t;
 typedef f16_t half2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));  // 16 bytes in registers (arrays stay in VGPRs)
 typedef f16_t half8v __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 

@@ -27,11 +27,13 @@ namespace ocrdec {
 // the lower index; a NaN logit counts as -inf and a taken expert drops out.
 // Writes the experts used (forced ones if given) to idx_out [rows][K], their
 // renormalised weights and the captures.
-OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl, const float* bias, int* idx_out) {
+OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl, const float* bias, int* idx_out, int r0 = 0,
+                       int r1 = -1) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int E = p.n_experts, K = p.top_k;
     const float taken = __builtin_nanf("");
-    for (int r = wave; r < p.rows; r += nw) {
+    if (r1 < 0) r1 = p.rows;
+    for (int r = r0 + wave; r < r1; r += nw) {
         const float* l = lg + (int64_t)r * ldl;
         float v[4];
 #pragma unroll
@@ -266,6 +268,257 @@ __global__ __launch_bounds__(1024) void route_group_kernel(MoeParams p) {
     topk_rows(p, p.logits, p.n_experts, p.bias, p.idx);
     __syncthreads();
     group_pairs(p, GroupScratch{p.idx, p.rank, p.hist, p.counts, p.offsets});
+}
+
+// Top-k of many rows (large batches): 16 rows per workgroup, one wavefront
+// per row, logits from the router GEMM in global memory.
+__global__ __launch_bounds__(1024) void topk_kernel(MoeParams p) {
+    const int r0 = blockIdx.x * 16;
+    topk_rows(p, p.logits, p.n_experts, p.bias, p.idx, r0, min(r0 + 16, p.rows));
+}
+
+// Grouping of any number of pairs in one workgroup, 1024 pairs at a time:
+// per chunk, every expert's 1024-bit mask of its pairs gives each pair its
+// place among the expert's earlier pairs of the chunk (a popcount), added to
+// the expert's running count.  Work entries are blocks of up to `blk` tokens
+// (shared experts first); vrows[slot] as in group_pairs_small.
+// LDS: masks [E][16] u64 (E <= 256: 32 KiB).
+__global__ __launch_bounds__(1024) void group_large_kernel(MoeParams p, int blk) {
+    __shared__ unsigned long long mask_s[256 * 16];
+    __shared__ int run_s[256], offsets_s[257];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int R = p.rows, E = p.n_experts, K = p.top_k, S = p.n_shared;
+    const int NP = R * K;
+    for (int e = tid; e < E; e += 1024) run_s[e] = 0;
+    for (int c0 = 0; c0 < NP; c0 += 1024) {
+        for (int i = tid; i < 16 * E; i += 1024) mask_s[i] = 0ull;
+        __syncthreads();
+        const int pi = c0 + tid;
+        const int e = pi < NP ? p.idx[pi] : 0;
+        if (pi < NP) atomicOr(&mask_s[e * 16 + (tid >> 6)], 1ull << (tid & 63));
+        __syncthreads();
+        if (pi < NP) {
+            int t = __popcll(mask_s[e * 16 + (tid >> 6)] & ((1ull << (tid & 63)) - 1ull));
+            for (int w = 0; w < (tid >> 6); ++w) t += __popcll(mask_s[e * 16 + w]);
+            p.rank[pi] = run_s[e] + t;
+        }
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += 1024) {
+            int c = 0;
+#pragma unroll
+            for (int w = 0; w < 16; ++w) c += __popcll(mask_s[ee * 16 + w]);
+            run_s[ee] += c;
+        }
+        __syncthreads();
+    }
+    // offsets and the work list (wave 0, four experts per lane)
+    if (wave == 0) {
+        const int rb = (R + blk - 1) / blk;
+        int cnt[4], tot = 0, nb = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 4 * lane + j;
+            cnt[j] = e < E ? run_s[e] : 0;
+            tot += cnt[j];
+            nb += (cnt[j] + blk - 1) / blk;
+        }
+        int incl = tot, nbi = nb;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o, 64);
+            const int tb = __shfl_up(nbi, o, 64);
+            if (lane >= o) {
+                incl += t;
+                nbi += tb;
+            }
+        }
+        int base = incl - tot, vb = S * rb + nbi - nb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 4 * lane + j;
+            if (e < E) {
+                offsets_s[e] = base;
+                for (int b = 0; b * blk < cnt[j]; ++b)
+                    p.virt[vb++] = make_int4(e, base + b * blk, min(blk, cnt[j] - b * blk), 0);
+            }
+            base += cnt[j];
+        }
+        for (int i = lane; i < S * rb; i += 64) {
+            const int sx = i / rb, b = i % rb;
+            p.virt[i] = make_int4(E + sx, NP + sx * R + b * blk, min(blk, R - b * blk), 0);
+        }
+        if (lane == 63) {
+            offsets_s[E] = incl;
+            p.n_virt[0] = S * rb + nbi;
+        }
+    }
+    __syncthreads();
+    for (int pi = tid; pi < NP; pi += 1024) {
+        const int pos = offsets_s[p.idx[pi]] + p.rank[pi];
+        p.perm[pos] = pi;
+        p.inv[pi] = pos;
+        p.vrows[pos] = pi / K;
+        if (p.cap_perm) p.cap_perm[pos] = pi;
+    }
+    for (int i = tid; i < S * R; i += 1024) p.vrows[NP + i] = i % R;
+    if (p.cap_counts)
+        for (int e = tid; e < E; e += 1024) p.cap_counts[e] = run_s[e];
+    if (p.cap_offsets)
+        for (int e = tid; e <= E; e += 1024) p.cap_offsets[e] = offsets_s[e];
+}
+
+// ---------------------------------------------------------------------------
+// Expert GEMM for large token counts (prefill-shaped batches)
+//
+// Work item (entry v of up to 128 tokens of one expert, column group cg).
+// The workgroup stages the entry's activations chunk by chunk in LDS (double
+// buffered: the next chunk's rows are requested before the current chunk is
+// multiplied); every wavefront holds two weight tiles of the chunk in
+// registers, dequantises each 32-column block once and multiplies it by all
+// eight 16-token groups with v_mfma_f32_16x16x32_f16; the fp16 block scale is
+// applied to each block's fp32 product (exact products, fp32 sums).  SwiGLU:
+// wave w takes the gate tile 4*cg + w and its up tile and writes
+// fp16 silu(gate) * up; otherwise wave w takes tiles 8*cg + 2w, +1 and
+// writes fp32.  Formats F16, Q8_0, Q4_0.
+// ---------------------------------------------------------------------------
+
+constexpr int EG_TM = 128;  // tokens per work entry
+
+template <int FMT>
+constexpr int eg_lds_bytes() { return 2 * EG_TM * (32 * Geom<FMT>::SB + 8) * 2; }
+
+template <int FMT, bool GLU>
+__global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GroupedParams p) {
+    constexpr int CB = Geom<FMT>::CB, SB = Geom<FMT>::SB, KC = 32 * SB;
+    constexpr int NG = EG_TM / 16, LDX = KC + 8;
+    constexpr int NE = EG_TM * (KC / 8) / 256;  // 16-byte pieces staged per thread per chunk
+    extern __shared__ __align__(16) uint16_t xs_dyn[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
+    const int v = blockIdx.y, cg = blockIdx.x;
+    int e, off, cnt;
+    if (p.dense_rows > 0) {
+        e = 0;
+        off = v * EG_TM;
+        cnt = min(EG_TM, p.dense_rows - off);
+    } else {
+        if (v >= p.n_virt[0]) return;  // uniform per workgroup, before any barrier
+        const int4 ent = p.virt[v];
+        e = ent.x;
+        off = ent.y;
+        cnt = ent.z;
+    }
+    if (cnt <= 0) return;
+    const uint8_t* base = (e < p.n_experts) ? p.w_routed + (int64_t)e * p.expert_bytes
+                                            : p.w_shared + (int64_t)(e - p.n_experts) * p.expert_bytes;
+    int tile[2];
+    bool tv[2];
+    if constexpr (GLU) {
+        tile[0] = cg * 4 + wave;
+        tv[0] = tv[1] = tile[0] < p.out_tiles;
+        tile[1] = tile[0] + p.out_tiles;
+    } else {
+        tile[0] = cg * 8 + 2 * wave;
+        tile[1] = tile[0] + 1;
+        tv[0] = tile[0] < p.out_tiles;
+        tv[1] = tile[1] < p.out_tiles;
+    }
+    const uint8_t* tp[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) tp[t] = base + (int64_t)(tv[t] ? tile[t] : 0) * p.nchunks * CB;
+
+    // staging: thread tid copies 16-byte pieces el = tid + 256*i of the
+    // entry's [128 tokens][KC] chunk; rows past the count repeat the last one
+    // thread tid always copies column piece c8 of rows r0 + (256/(KC/8))*i
+    constexpr int RSTEP = 256 / (KC / 8);
+    const int c8 = (tid % (KC / 8)) * 8, r0 = tid / (KC / 8);
+    int srow[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const int rr = min(r0 + RSTEP * i, cnt - 1);
+        srow[i] = (GLU && p.dense_rows == 0) ? p.vrows[off + rr] : off + rr;
+    }
+    auto xsrc = [&](int i, int c) { return (const u32x4v*)(p.x + (int64_t)srow[i] * p.ldx + (int64_t)c * KC + c8); };
+    auto xdst = [&](uint16_t* buf, int i) { return (u32x4v*)(buf + (r0 + RSTEP * i) * LDX + c8); };
+    u32x4v xr[NE];
+    WRegs wc[2], wn[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) load_wchunk<FMT>(tp[t], lane, wc[t]);
+#pragma unroll
+    for (int i = 0; i < NE; ++i) xr[i] = *xsrc(i, 0);
+#pragma unroll
+    for (int i = 0; i < NE; ++i) *xdst(xs_dyn, i) = xr[i];
+    __syncthreads();
+
+    float4v acc[2][NG];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) acc[t][g] = float4v{0.f, 0.f, 0.f, 0.f};
+    const float4v zero = {0.f, 0.f, 0.f, 0.f};
+    const int nch = (int)p.nchunks;
+    for (int c = 0; c < nch; ++c) {
+        const uint16_t* xb = xs_dyn + (c & 1) * (EG_TM * LDX);
+        uint16_t* xn = xs_dyn + ((c + 1) & 1) * (EG_TM * LDX);
+        // the next chunk (the last one again at the end: its copy is never read)
+        const int cn = min(c + 1, nch - 1);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) load_wchunk<FMT>(tp[t] + (int64_t)cn * CB, lane, wn[t]);
+#pragma unroll
+        for (int i = 0; i < NE; ++i) xr[i] = *xsrc(i, cn);
+        // the chunk's weight blocks, dequantised once
+        half8v b[2][SB];
+        float d[2][SB];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                b[t][j] = wfrag<FMT>(wc[t], j);
+                d[t][j] = wscale<FMT>(wc[t], j);
+            }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            half8v a[SB];
+#pragma unroll
+            for (int j = 0; j < SB; ++j)
+                a[j] = *(const half8v*)(xb + (g * 16 + (lane & 15)) * LDX + j * 32 + 8 * (lane >> 4));
+#pragma unroll
+            for (int j = 0; j < SB; ++j)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    if constexpr (FMT == OCRDEC_F16) {
+                        acc[t][g] = mfma16(a[j], b[t][j], acc[t][g]);
+                    } else {
+                        const float4v m = mfma16(a[j], b[t][j], zero);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[t][g][q] = fmaf(d[t][j], m[q], acc[t][g][q]);
+                    }
+                }
+            if (g & 1) __builtin_amdgcn_sched_barrier(0);  // bound the activation reads in flight
+        }
+#pragma unroll
+        for (int i = 0; i < NE; ++i) *xdst(xn, i) = xr[i];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) wc[t] = wn[t];
+        __syncthreads();
+    }
+    // epilogue (MFMA D layout: lane l, register q -> token 16g + 4(l/16) + q, column l % 16)
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int tok = g * 16 + 4 * (lane >> 4) + q;
+            if (tok >= cnt) continue;
+            const int64_t slot = off + tok;
+            if constexpr (GLU) {
+                if (tv[0])
+                    ((uint16_t*)p.y)[slot * p.ldy + tile[0] * 16 + (lane & 15)] =
+                        f2h(silu(acc[0][g][q]) * acc[1][g][q]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    if (tv[t]) ((float*)p.y)[slot * p.ldy + tile[t] * 16 + (lane & 15)] = acc[t][g][q];
+            }
+        }
 }
 
 // Routing of up to 32 rows in one workgroup.  Router GEMV: wave w computes
@@ -509,9 +762,16 @@ bool moe_small(int rows, const ocrdec_moe_weights* w) {
     const int E = w->n_experts, K = w->top_k, H = w->hidden;
     return rows <= 32 && E % 16 == 0 && E <= 256 && rows * K <= 256 && route_lds_bytes(rows, H) <= 96 * 1024;
 }
+static bool eg_format(int fmt) { return fmt == OCRDEC_F16 || fmt == OCRDEC_Q8_0 || fmt == OCRDEC_Q4_0; }
+// Large batches go through the expert GEMM when every matrix format has it.
+bool moe_gemm_path(int rows, const ocrdec_moe_weights* w) {
+    return !moe_small(rows, w) && w->n_experts % 16 == 0 && eg_format(w->router.fmt) && eg_format(w->gate_up.fmt) &&
+           eg_format(w->down.fmt) && (w->n_shared == 0 || (eg_format(w->sh_gate_up.fmt) && eg_format(w->sh_down.fmt)));
+}
 int moe_max_virt(int rows, const ocrdec_moe_weights* w) {
     const int E = w->n_experts, S = w->n_shared, NP = rows * w->top_k;
     if (moe_small(rows, w)) return S * ((rows + 15) / 16) + std::min(E, NP) + NP / 16;
+    if (moe_gemm_path(rows, w)) return S * ((rows + EG_TM - 1) / EG_TM) + std::min(E, NP) + NP / EG_TM;
     return std::min(E, NP) + S;
 }
 
@@ -609,6 +869,26 @@ void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream
 #undef OCR_F
 }
 
+template <int FMT, bool GLU>
+void launch_eg_t(const GroupedParams& p, int n_entries, hipStream_t s) {
+    const int cgs = GLU ? (p.out_tiles + 3) / 4 : (p.out_tiles + 7) / 8;
+    hipLaunchKernelGGL((expert_gemm_kernel<FMT, GLU>), dim3(cgs, n_entries), dim3(256), eg_lds_bytes<FMT>(), s, p);
+}
+
+void launch_expert_gemm(int fmt, bool glu, const GroupedParams& p, int n_entries, hipStream_t s) {
+#define OCR_EG(F_)                                               \
+    case F_:                                                     \
+        if (glu) launch_eg_t<F_, true>(p, n_entries, s);         \
+        else launch_eg_t<F_, false>(p, n_entries, s);            \
+        break;
+    switch (fmt) {
+        OCR_EG(OCRDEC_F16)
+        OCR_EG(OCRDEC_Q8_0)
+        OCR_EG(OCRDEC_Q4_0)
+    }
+#undef OCR_EG
+}
+
 }  // namespace
 
 void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_f32, int64_t ldh,
@@ -667,6 +947,22 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         }
 #undef OCR_R
 #undef OCR_RL
+    } else if (moe_gemm_path(rows, w)) {
+        // router GEMM, parallel top-k, grouping into 128-token entries
+        GroupedParams rp{};
+        rp.w_routed = (const uint8_t*)w->router.data;
+        rp.n_experts = 1;
+        rp.k = H;
+        rp.nchunks = n_chunks(w->router.fmt, H);
+        rp.out_tiles = E / 16;
+        rp.dense_rows = rows;
+        rp.x = x;
+        rp.ldx = ldx;
+        rp.y = m.logits;
+        rp.ldy = E;
+        launch_expert_gemm(w->router.fmt, false, rp, (rows + EG_TM - 1) / EG_TM, s);
+        hipLaunchKernelGGL(topk_kernel, dim3((rows + 15) / 16), dim3(1024), 0, s, p);
+        hipLaunchKernelGGL(group_large_kernel, dim3(1), dim3(1024), 0, s, p, EG_TM);
     } else {
         GemvPlan pl = plan_gemv(w->router.fmt, E, H, rows, EPI_F32);
         GemvParams gp{};
@@ -701,7 +997,9 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.ldx = ldx;
         p.y = m.a;
         p.ldy = F;
-        launch_grouped(w->gate_up.fmt, true, p, rows, s);
+        p.out_tiles = F / 16;
+        if (moe_gemm_path(rows, w)) launch_expert_gemm(w->gate_up.fmt, true, p, max_virt, s);
+        else launch_grouped(w->gate_up.fmt, true, p, rows, s);
     }
     // down
     {
@@ -723,7 +1021,9 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.ldx = F;
         p.y = m.y;
         p.ldy = H;
-        launch_grouped(w->down.fmt, false, p, rows, s);
+        p.out_tiles = H / 16;
+        if (moe_gemm_path(rows, w)) launch_expert_gemm(w->down.fmt, false, p, max_virt, s);
+        else launch_grouped(w->down.fmt, false, p, rows, s);
     }
     // combine
     {

@@ -54,6 +54,8 @@ struct GroupedParams {
     int64_t ldx;
     void* y;
     int64_t ldy;
+    int out_tiles;   // expert GEMM: output tiles per expert (SwiGLU: tiles of each half)
+    int dense_rows;  // expert GEMM: > 0 means one implicit expert over rows [0, dense_rows) (router)
 };
 
 struct CombineParams {
