@@ -370,155 +370,252 @@ __global__ __launch_bounds__(1024) void group_large_kernel(MoeParams p, int blk)
 // ---------------------------------------------------------------------------
 // Expert GEMM for large token counts (prefill-shaped batches)
 //
-// Work item (entry v of up to 128 tokens of one expert, column group cg).
-// The workgroup stages the entry's activations chunk by chunk in LDS (double
-// buffered: the next chunk's rows are requested before the current chunk is
-// multiplied); every wavefront holds two weight tiles of the chunk in
-// registers, dequantises each 32-column block once and multiplies it by all
-// eight 16-token groups with v_mfma_f32_16x16x32_f16; the fp16 block scale is
-// applied to each block's fp32 product (exact products, fp32 sums).  SwiGLU:
-// wave w takes the gate tile 4*cg + w and its up tile and writes
-// fp16 silu(gate) * up; otherwise wave w takes tiles 8*cg + 2w, +1 and
-// writes fp32.  Formats F16, Q8_0, Q4_0.
+// Work item: entry v (up to 128 tokens of one expert) x column group cg, one
+// workgroup of four wavefronts, two per CU.  The activations move through LDS
+// in stages of 128 columns (two stage buffers of 128 x 128 fp16, 64 KiB): the
+// workgroup requests stage s+1 with buffer loads straight into LDS before it
+// multiplies stage s, so staging takes no registers.  Within a 256-byte row
+// the 16-byte pieces are stored at piece ^ (row % 16): the sixteen rows of
+// one MFMA operand read fall on different banks without padding.  Every
+// wavefront holds two weight tiles in registers (requested two stages
+// ahead) and forms block jj+1's operands (LDS reads, dequantisation) while
+// block jj's v_mfma_f32_16x16x32_f16 run over the entry's token groups (the
+// group index innermost; groups past the token count are skipped).  The
+// fp16 block scale is applied to each block's fp32 product (exact products,
+// fp32 sums).  SwiGLU: wave w takes the gate tile 4*cg + w and its up tile
+// and writes fp16 silu(gate) * up; otherwise wave w takes tiles 8*cg + 2w,
+// +1 and writes fp32.  Entries are dealt round-robin to the XCDs (workgroup
+// id mod 8) with all their column groups, so an entry's activations are read
+// into one L2 and every XCD gets a like mix of full and part-filled entries.
+// Formats F16, Q8_0, Q4_0; k a multiple of 128.
 // ---------------------------------------------------------------------------
 
-constexpr int EG_TM = 128;  // tokens per work entry
+constexpr int EG_TM = 128;   // tokens per work entry
+constexpr int EG_KS = 128;   // activation columns per LDS stage
+constexpr int EG_NW = 4;     // wavefronts per workgroup (two workgroups per CU)
+constexpr int EG_NBUF = 2;   // LDS stage buffers: stage s+1 in flight while s is multiplied
+constexpr int EG_LDS = EG_NBUF * EG_TM * EG_KS * 2;
+constexpr int EG_NDMA = EG_TM * EG_KS * 2 / 1024 / EG_NW;  // 1 KiB stage loads per wave and stage
 
-template <int FMT>
-constexpr int eg_lds_bytes() { return 2 * EG_TM * (32 * Geom<FMT>::SB + 8) * 2; }
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their
+// maxima, i.e. not waited for).
+template <int N>
+OCR_DEV void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 template <int FMT, bool GLU>
-__global__ __launch_bounds__(256, 2) void expert_gemm_kernel(GroupedParams p) {
-    constexpr int CB = Geom<FMT>::CB, SB = Geom<FMT>::SB, KC = 32 * SB;
-    constexpr int NG = EG_TM / 16, LDX = KC + 8;
-    constexpr int NE = EG_TM * (KC / 8) / 256;  // 16-byte pieces staged per thread per chunk
+__global__ __launch_bounds__(64 * EG_NW, 2) void expert_gemm_kernel(GroupedParams p, int n_cg) {
+    constexpr int SB = Geom<FMT>::SB, CB = Geom<FMT>::CB, KC = 32 * SB;
+    constexpr int CPS = EG_KS / KC;  // weight chunks per stage and tile
+    constexpr int NG = EG_TM / 16;
+    constexpr int PD = 2;                                        // weight prefetch distance (stages)
+    constexpr int NWL = 2 * CPS * (FMT == OCRDEC_F16 ? 1 : 2);  // weight load instructions per stage
+    constexpr int RW = EG_TM / EG_NW;                           // stage rows loaded per wave
+    static_assert(RW % 16 == 0 && RW == 4 * EG_NDMA, "staging geometry");
     extern __shared__ __align__(16) uint16_t xs_dyn[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
-    const int v = blockIdx.y, cg = blockIdx.x;
-    int e, off, cnt;
-    if (p.dense_rows > 0) {
-        e = 0;
-        off = v * EG_TM;
-        cnt = min(EG_TM, p.dense_rows - off);
-    } else {
-        if (v >= p.n_virt[0]) return;  // uniform per workgroup, before any barrier
-        const int4 ent = p.virt[v];
-        e = ent.x;
-        off = ent.y;
-        cnt = ent.z;
-    }
-    if (cnt <= 0) return;
-    const uint8_t* base = (e < p.n_experts) ? p.w_routed + (int64_t)e * p.expert_bytes
-                                            : p.w_shared + (int64_t)(e - p.n_experts) * p.expert_bytes;
-    int tile[2];
-    bool tv[2];
-    if constexpr (GLU) {
-        tile[0] = cg * 4 + wave;
-        tv[0] = tv[1] = tile[0] < p.out_tiles;
-        tile[1] = tile[0] + p.out_tiles;
-    } else {
-        tile[0] = cg * 8 + 2 * wave;
-        tile[1] = tile[0] + 1;
-        tv[0] = tile[0] < p.out_tiles;
-        tv[1] = tile[1] < p.out_tiles;
-    }
-    const uint8_t* tp[2];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_ent = p.dense_rows > 0 ? (p.dense_rows + EG_TM - 1) / EG_TM : p.n_virt[0];
+    // one work item: entry v, column group cg
+    auto item = [&](const int v, const int cg) {
+        int e, off, cnt;
+        if (p.dense_rows > 0) {
+            e = 0;
+            off = v * EG_TM;
+            cnt = min(EG_TM, p.dense_rows - off);
+        } else {
+            const int4 ent = p.virt[v];
+            e = ent.x;
+            off = ent.y;
+            cnt = ent.z;
+        }
+        if (cnt <= 0) return;
+        const uint8_t* base = (e < p.n_experts) ? p.w_routed + (int64_t)e * p.expert_bytes
+                                                : p.w_shared + (int64_t)(e - p.n_experts) * p.expert_bytes;
+        int tile[2];
+        bool tv[2];
+        if constexpr (GLU) {
+            tile[0] = cg * EG_NW + wave;
+            tv[0] = tv[1] = tile[0] < p.out_tiles;
+            tile[1] = tile[0] + p.out_tiles;
+        } else {
+            tile[0] = cg * 2 * EG_NW + 2 * wave;
+            tile[1] = tile[0] + 1;
+            tv[0] = tile[0] < p.out_tiles;
+            tv[1] = tile[1] < p.out_tiles;
+        }
+        const uint8_t* tp[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) tp[t] = base + (int64_t)(tv[t] ? tile[t] : 0) * p.nchunks * CB;
+        for (int t = 0; t < 2; ++t) tp[t] = base + (int64_t)(tv[t] ? tile[t] : 0) * p.nchunks * CB;
 
-    // staging: thread tid copies 16-byte pieces el = tid + 256*i of the
-    // entry's [128 tokens][KC] chunk; rows past the count repeat the last one
-    // thread tid always copies column piece c8 of rows r0 + (256/(KC/8))*i
-    constexpr int RSTEP = 256 / (KC / 8);
-    const int c8 = (tid % (KC / 8)) * 8, r0 = tid / (KC / 8);
-    int srow[NE];
+        // staging: wave w fills rows RW*w .. RW*w + RW-1 (RW = 128 / waves), four
+        // per load instruction; lane l of instruction i carries row
+        // RW*w + 4i + l/16 into stored piece
+        // l % 16, which holds column piece (l % 16) ^ (row % 16) of the stage.
+        // Rows past the token count repeat the last token (never stored).
+        // Buffer loads (MUBUF) into LDS: unlike the FLAT form they leave the
+        // compiler's vmcnt tracking of the weight registers exact.  Byte offsets
+        // are 32-bit (the host keeps the activation extent below 2 GiB).
+        const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc((void*)p.x, 0, 0x7fffffff, 0x00020000);
+        uint32_t voff[EG_NDMA];
 #pragma unroll
-    for (int i = 0; i < NE; ++i) {
-        const int rr = min(r0 + RSTEP * i, cnt - 1);
-        srow[i] = (GLU && p.dense_rows == 0) ? p.vrows[off + rr] : off + rr;
-    }
-    auto xsrc = [&](int i, int c) { return (const u32x4v*)(p.x + (int64_t)srow[i] * p.ldx + (int64_t)c * KC + c8); };
-    auto xdst = [&](uint16_t* buf, int i) { return (u32x4v*)(buf + (r0 + RSTEP * i) * LDX + c8); };
-    u32x4v xr[NE];
-    WRegs wc[2], wn[2];
+        for (int i = 0; i < EG_NDMA; ++i) {
+            const int rr = min(RW * wave + 4 * i + (lane >> 4), cnt - 1);
+            const int64_t sr = (GLU && p.dense_rows == 0) ? p.vrows[off + rr] : off + rr;
+            voff[i] = (uint32_t)(2 * (sr * p.ldx + 8 * ((lane & 15) ^ ((4 * i + (lane >> 4)) & 15))));
+        }
+        auto stage_load = [&](int s, int b) {
+            uint16_t* dst = xs_dyn + b * (EG_TM * EG_KS) + wave * RW * EG_KS;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) load_wchunk<FMT>(tp[t], lane, wc[t]);
+            for (int i = 0; i < EG_NDMA; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void_t*)(dst + i * 4 * EG_KS), 16, voff[i], 2 * s * EG_KS,
+                                                         0, 0);
+        };
+        // operand reads: lane l, block jj of a stage -> row l % 16 of the group,
+        // column piece 4 jj + l / 16
+        int aoff[4];
 #pragma unroll
-    for (int i = 0; i < NE; ++i) xr[i] = *xsrc(i, 0);
-#pragma unroll
-    for (int i = 0; i < NE; ++i) *xdst(xs_dyn, i) = xr[i];
-    __syncthreads();
+        for (int jj = 0; jj < 4; ++jj) aoff[jj] = (lane & 15) * EG_KS + 8 * ((4 * jj + (lane >> 4)) ^ (lane & 15));
 
-    float4v acc[2][NG];
+        auto wload = [&](int s, WRegs(&w)[2][CPS]) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int g = 0; g < NG; ++g) acc[t][g] = float4v{0.f, 0.f, 0.f, 0.f};
-    const float4v zero = {0.f, 0.f, 0.f, 0.f};
-    const int nch = (int)p.nchunks;
-    for (int c = 0; c < nch; ++c) {
-        const uint16_t* xb = xs_dyn + (c & 1) * (EG_TM * LDX);
-        uint16_t* xn = xs_dyn + ((c + 1) & 1) * (EG_TM * LDX);
-        // the next chunk (the last one again at the end: its copy is never read)
-        const int cn = min(c + 1, nch - 1);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) load_wchunk<FMT>(tp[t] + (int64_t)cn * CB, lane, wn[t]);
-#pragma unroll
-        for (int i = 0; i < NE; ++i) xr[i] = *xsrc(i, cn);
-        // the chunk's weight blocks, dequantised once
-        half8v b[2][SB];
-        float d[2][SB];
+                for (int c = 0; c < CPS; ++c) load_wchunk<FMT>(tp[t] + (int64_t)(s * CPS + c) * CB, lane, w[t][c]);
+        };
+        float4v acc[2][NG];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                b[t][j] = wfrag<FMT>(wc[t], j);
-                d[t][j] = wscale<FMT>(wc[t], j);
-            }
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            half8v a[SB];
-#pragma unroll
-            for (int j = 0; j < SB; ++j)
-                a[j] = *(const half8v*)(xb + (g * 16 + (lane & 15)) * LDX + j * 32 + 8 * (lane >> 4));
-#pragma unroll
-            for (int j = 0; j < SB; ++j)
+            for (int g = 0; g < NG; ++g) acc[t][g] = float4v{0.f, 0.f, 0.f, 0.f};
+        const float4v zero = {0.f, 0.f, 0.f, 0.f};
+        const int ns = p.k / EG_KS;
+        // Weight operands of one (tile, 32-column block): the codes q as fp16
+        // (exact) and the block scale d, applied to the block's fp32 product
+        // (Q8_0, Q4_0: exact products, fp32 sums); F16: the weights.
+        struct BPk {
+            half8v h;
+            float d;
+        };
+        // The main loop, specialised on the token groups that hold tokens (in
+        // pairs): a part-filled entry skips the empty groups' MFMAs and reads.
+        auto run = [&](auto nga) {
+            constexpr int NGA = decltype(nga)::value;
+            auto deq = [&](const WRegs(&w)[2][CPS], int jj, BPk(&o)[2]) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    if constexpr (FMT == OCRDEC_F16) {
-                        acc[t][g] = mfma16(a[j], b[t][j], acc[t][g]);
-                    } else {
-                        const float4v m = mfma16(a[j], b[t][j], zero);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) acc[t][g][q] = fmaf(d[t][j], m[q], acc[t][g][q]);
-                    }
+                    o[t].h = wfrag<FMT>(w[t][jj / SB], jj % SB);
+                    o[t].d = wscale<FMT>(w[t][jj / SB], jj % SB);
                 }
-            if (g & 1) __builtin_amdgcn_sched_barrier(0);  // bound the activation reads in flight
-        }
-#pragma unroll
-        for (int i = 0; i < NE; ++i) *xdst(xn, i) = xr[i];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) wc[t] = wn[t];
-        __syncthreads();
-    }
-    // epilogue (MFMA D layout: lane l, register q -> token 16g + 4(l/16) + q, column l % 16)
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int tok = g * 16 + 4 * (lane >> 4) + q;
-            if (tok >= cnt) continue;
-            const int64_t slot = off + tok;
-            if constexpr (GLU) {
-                if (tv[0])
-                    ((uint16_t*)p.y)[slot * p.ldy + tile[0] * 16 + (lane & 15)] =
-                        f2h(silu(acc[0][g][q]) * acc[1][g][q]);
-            } else {
+            };
+            // one block of the active token groups; the group index runs innermost
+            // so consecutive MFMAs write different accumulators
+            auto mma = [&](const half8v(&a)[NGA], const BPk(&b)[2]) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
-                    if (tv[t]) ((float*)p.y)[slot * p.ldy + tile[t] * 16 + (lane & 15)] = acc[t][g][q];
+#pragma unroll
+                    for (int g = 0; g < NGA; ++g) {
+                        if constexpr (FMT != OCRDEC_F16) {
+                            const float4v m = mfma16(a[g], b[t].h, zero);
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) acc[t][g][q] = fmaf(b[t].d, m[q], acc[t][g][q]);
+                        } else {
+                            acc[t][g] = mfma16(a[g], b[t].h, acc[t][g]);
+                        }
+                    }
+            };
+            auto lds_a = [&](const uint16_t* xb, int jj, half8v(&a)[NGA]) {
+#pragma unroll
+                for (int g = 0; g < NGA; ++g) a[g] = *(const half8v*)(xb + g * 16 * EG_KS + aoff[jj]);
+            };
+            // Step s: stage s sits in LDS buffer s % EG_NBUF, its weights in w (W(s),
+            // requested PD steps earlier), the next stage's in wn.  Block jj+1's
+            // operands (LDS reads, dequantisation) are formed while block jj's MFMAs
+            // run; the last block forms block 0 of the next stage from wn, carried
+            // into the next step in bc.  w is refilled with W(s+PD) once its last
+            // block has been formed.
+            BPk bc[2];
+            auto step = [&](int s, WRegs(&w)[2][CPS], const WRegs(&wn)[2][CPS]) {
+                // stage s complete in LDS; every wave is done with stage s-1's buffer.
+                // A plain s_barrier: a workgroup fence here would also wait for the
+                // next stage's loads.  Every LDS read of stage s-1 has been consumed
+                // by an MFMA before this point, so none is outstanding.
+                asm volatile("s_barrier" ::: "memory");
+                stage_load(min(s + EG_NBUF - 1, ns - 1), (s + EG_NBUF - 1) % EG_NBUF);
+                __builtin_amdgcn_sched_barrier(0);  // stage loads before the weight loads (vmcnt order)
+                const uint16_t* xb = xs_dyn + (s % EG_NBUF) * (EG_TM * EG_KS);
+                half8v ac[NGA];
+                lds_a(xb, 0, ac);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    half8v an[NGA];
+                    BPk bn[2];
+                    if (jj < 3) {
+                        lds_a(xb, jj + 1, an);
+                        deq(w, jj + 1, bn);
+                        if (jj == 2) wload(min(s + PD, ns - 1), w);
+                    } else {
+                        deq(wn, 0, bn);
+                    }
+                    mma(ac, bc);
+#pragma unroll
+                    for (int g = 0; g < NGA; ++g) ac[g] = an[g];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) bc[t] = bn[t];
+                }
+                // stage s+1 has landed once only the loads issued after it remain:
+                // the weight loads of the step that requested it and of the
+                // EG_NBUF - 2 steps since, and those steps' stage loads
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmcnt<NWL + (EG_NBUF - 2) * (EG_NDMA + NWL)>();
+            };
+            static_assert(PD == 2 && PD + 2 >= EG_NBUF, "prologue and wait counts");
+            WRegs wq[PD][2][CPS];
+#pragma unroll
+            for (int u = 0; u + 1 < EG_NBUF; ++u) stage_load(min(u, ns - 1), u);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < PD; ++u) wload(min(u, ns - 1), wq[u]);
+            deq(wq[0], 0, bc);
+            wait_vmcnt<(EG_NBUF - 2) * EG_NDMA + PD * NWL>();  // stage 0 (ahead of the weight loads)
+            for (int s = 0; s < ns; s += PD) {
+                step(s, wq[0], wq[1]);
+                if (s + 1 < ns) step(s + 1, wq[1], wq[0]);
             }
-        }
+        };
+        const int ngp = (cnt + 31) >> 5;
+        if (ngp >= 4) run(std::integral_constant<int, 8>{});
+        else if (ngp == 3) run(std::integral_constant<int, 6>{});
+        else if (ngp == 2) run(std::integral_constant<int, 4>{});
+        else run(std::integral_constant<int, 2>{});
+        // epilogue (MFMA D layout: lane l, register q -> token 16g + 4(l/16) + q, column l % 16)
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int tok = g * 16 + 4 * (lane >> 4) + q;
+                if (tok >= cnt) continue;
+                const int64_t slot = off + tok;
+                if constexpr (GLU) {
+                    if (tv[0])
+                        ((uint16_t*)p.y)[slot * p.ldy + tile[0] * 16 + (lane & 15)] =
+                            f2h(silu(acc[0][g][q]) * acc[1][g][q]);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        if (tv[t]) ((float*)p.y)[slot * p.ldy + tile[t] * 16 + (lane & 15)] = acc[t][g][q];
+                }
+            }
+    };
+    // one work item per workgroup: entries dealt round-robin to the XCDs
+    // (workgroup id mod 8), all column groups of an entry on one XCD
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int v = xcd + 8 * (j / n_cg);
+    if (v < n_ent) item(v, j % n_cg);  // uniform per workgroup
 }
 
 // Routing of up to 32 rows in one workgroup.  Router GEMV: wave w computes
@@ -765,8 +862,8 @@ bool moe_small(int rows, const ocrdec_moe_weights* w) {
 static bool eg_format(int fmt) { return fmt == OCRDEC_F16 || fmt == OCRDEC_Q8_0 || fmt == OCRDEC_Q4_0; }
 // Large batches go through the expert GEMM when every matrix format has it.
 bool moe_gemm_path(int rows, const ocrdec_moe_weights* w) {
-    return !moe_small(rows, w) && w->n_experts % 16 == 0 && eg_format(w->router.fmt) && eg_format(w->gate_up.fmt) &&
-           eg_format(w->down.fmt) && (w->n_shared == 0 || (eg_format(w->sh_gate_up.fmt) && eg_format(w->sh_down.fmt)));
+    return !moe_small(rows, w) && w->n_experts % 16 == 0 && w->hidden % EG_KS == 0 && w->d_ff % EG_KS == 0 &&
+           eg_format(w->router.fmt) && eg_format(w->gate_up.fmt) && eg_format(w->down.fmt) && (w->n_shared == 0 || (eg_format(w->sh_gate_up.fmt) && eg_format(w->sh_down.fmt)));
 }
 int moe_max_virt(int rows, const ocrdec_moe_weights* w) {
     const int E = w->n_experts, S = w->n_shared, NP = rows * w->top_k;
@@ -871,8 +968,10 @@ void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream
 
 template <int FMT, bool GLU>
 void launch_eg_t(const GroupedParams& p, int n_entries, hipStream_t s) {
-    const int cgs = GLU ? (p.out_tiles + 3) / 4 : (p.out_tiles + 7) / 8;
-    hipLaunchKernelGGL((expert_gemm_kernel<FMT, GLU>), dim3(cgs, n_entries), dim3(256), eg_lds_bytes<FMT>(), s, p);
+    const int cgs = GLU ? (p.out_tiles + EG_NW - 1) / EG_NW : (p.out_tiles + 2 * EG_NW - 1) / (2 * EG_NW);
+    // every XCD gets room for cgs * ceil(n_entries / 8) work items
+    const int grid = 8 * cgs * ((n_entries + 7) / 8);
+    hipLaunchKernelGGL((expert_gemm_kernel<FMT, GLU>), dim3(grid), dim3(64 * EG_NW), EG_LDS, s, p, cgs);
 }
 
 void launch_expert_gemm(int fmt, bool glu, const GroupedParams& p, int n_entries, hipStream_t s) {
@@ -922,6 +1021,9 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     p.cap_offsets = cap ? cap->offsets : nullptr;
     p.cap_perm = cap ? cap->perm : nullptr;
     const bool small = moe_small(rows, w);
+    // the expert GEMM addresses its activations with 32-bit byte offsets
+    const bool gemm = moe_gemm_path(rows, w) && (int64_t)(rows - 1) * ldx + H < (1ll << 30) &&
+                      (int64_t)(NP + S * rows) * F < (1ll << 30);
     if (norm_in && !small) {
         // the MoE input is the normalised residual: form it first
         hipLaunchKernelGGL(moe_norm_kernel, dim3(rows), dim3(256), 0, s, h_norm, norm_in, H, eps_in, (uint16_t*)x,
@@ -947,7 +1049,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         }
 #undef OCR_R
 #undef OCR_RL
-    } else if (moe_gemm_path(rows, w)) {
+    } else if (gemm) {
         // router GEMM, parallel top-k, grouping into 128-token entries
         GroupedParams rp{};
         rp.w_routed = (const uint8_t*)w->router.data;
@@ -998,7 +1100,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.y = m.a;
         p.ldy = F;
         p.out_tiles = F / 16;
-        if (moe_gemm_path(rows, w)) launch_expert_gemm(w->gate_up.fmt, true, p, max_virt, s);
+        if (gemm) launch_expert_gemm(w->gate_up.fmt, true, p, max_virt, s);
         else launch_grouped(w->gate_up.fmt, true, p, rows, s);
     }
     // down
@@ -1022,7 +1124,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.y = m.y;
         p.ldy = H;
         p.out_tiles = H / 16;
-        if (moe_gemm_path(rows, w)) launch_expert_gemm(w->down.fmt, false, p, max_virt, s);
+        if (gemm) launch_expert_gemm(w->down.fmt, false, p, max_virt, s);
         else launch_grouped(w->down.fmt, false, p, rows, s);
     }
     // combine

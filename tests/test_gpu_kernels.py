@@ -245,6 +245,14 @@ def test_moe_prefill_bias_parity(q):
     _moe_case(q, 300, 1005, H=1280, E=64, K=6, S=2, F=896, fmt=synth.Q4_0, bias=True, residual=False)
 
 
+# the expert GEMM with the other weight formats: an odd number of 128-column
+# stages in the down projection (640, 384) and a 2-token last entry (130)
+@pytest.mark.parametrize("rows,fmt,F", [(130, synth.Q8_0, 640), (257, synth.F16, 384)])
+def test_moe_prefill_formats(q, rows, fmt, F):
+    _say("moe prefill-shaped", rows, "rows", synth.FMT_NAMES[fmt], "F", F)
+    _moe_case(q, rows, 1100 + rows, H=1024, E=32, K=4, S=1, F=F, fmt=fmt)
+
+
 # -----------------------------------------------------------------------------
 # ocrdec_lm_argmax
 # -----------------------------------------------------------------------------
