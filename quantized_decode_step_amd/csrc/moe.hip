@@ -28,20 +28,26 @@ namespace ocrdec {
 // Writes the experts used (forced ones if given) to idx_out [rows][K], their
 // renormalised weights and the captures.
 OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl, const float* bias, int* idx_out, int r0 = 0,
-                       int r1 = -1) {
+                       int r1 = -1, int nsl = 1, int64_t lsl = 0) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int E = p.n_experts, K = p.top_k;
     const float taken = __builtin_nanf("");
     if (r1 < 0) r1 = p.rows;
     for (int r = r0 + wave; r < r1; r += nw) {
         const float* l = lg + (int64_t)r * ldl;
+        // logit e: the sum of the k-slices' partial products, in slice order
+        auto logit = [&](int e) {
+            float x = l[e];
+            for (int z = 1; z < nsl; ++z) x += l[z * lsl + e];
+            return x;
+        };
         float v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = lane + 64 * j;
             float x = -INFINITY;
             if (e < E) {
-                x = l[e] + (bias ? bias[e] : 0.f);
+                x = logit(e) + (bias ? bias[e] : 0.f);
                 if (!(x == x)) x = -INFINITY;
             }
             v[j] = e < E ? x : taken;
@@ -66,7 +72,7 @@ OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl, const float
         if (forced && lane < K) use = p.forced[(int64_t)r * K + lane];
         use = min(max(use, 0), E - 1);  // device data: keep every index in range
         float lk = -INFINITY;
-        if (lane < K) lk = l[use] + (bias ? bias[use] : 0.f);
+        if (lane < K) lk = logit(use) + (bias ? bias[use] : 0.f);
         const float m = wave_max(lk);
         const float ex = lane < K ? __expf(lk - m) : 0.f;
         const float den = wave_sum(ex);
@@ -271,46 +277,89 @@ __global__ __launch_bounds__(1024) void route_group_kernel(MoeParams p) {
 }
 
 // Top-k of many rows (large batches): 16 rows per workgroup, one wavefront
-// per row, logits from the router GEMM in global memory.
+// per row, logits from the router GEMM in global memory (the sum of its
+// k-slices' partial products).
 __global__ __launch_bounds__(1024) void topk_kernel(MoeParams p) {
     const int r0 = blockIdx.x * 16;
-    topk_rows(p, p.logits, p.n_experts, p.bias, p.idx, r0, min(r0 + 16, p.rows));
+    topk_rows(p, p.logits, p.n_experts, p.bias, p.idx, r0, min(r0 + 16, p.rows), max(p.lslices, 1), p.lslice);
 }
 
-// Grouping of any number of pairs in one workgroup, 1024 pairs at a time:
-// per chunk, every expert's 1024-bit mask of its pairs gives each pair its
-// place among the expert's earlier pairs of the chunk (a popcount), added to
-// the expert's running count.  Work entries are blocks of up to `blk` tokens
-// (shared experts first); vrows[slot] as in group_pairs_small.
-// LDS: masks [E][16] u64 (E <= 256: 32 KiB).
+// Grouping of any number of pairs in one workgroup.  Wave w takes the
+// contiguous pair range [w*NP/16, (w+1)*NP/16) in rounds of 64 (one pair per
+// lane, up to 16 rounds' expert ids loaded at once): per round, every expert's
+// 64-bit mask of the wave's lanes holding it (in the wave's own LDS table)
+// gives each pair its place among the round's earlier pairs of that expert,
+// added to the wave's running count of the expert.  A scan of the sixteen
+// waves' counts then places every wave's pairs after the earlier waves', so a
+// pair's slot follows pair order within its expert.  Work entries are blocks
+// of up to `blk` tokens (shared experts first); vrows[slot] as in
+// group_pairs_small.  LDS: masks and counts [16][E] (E <= 256: 48 KiB).
 __global__ __launch_bounds__(1024) void group_large_kernel(MoeParams p, int blk) {
-    __shared__ unsigned long long mask_s[256 * 16];
+    __shared__ unsigned long long mask_s[16 * 256];
+    __shared__ int wcnt_s[16 * 256];
     __shared__ int run_s[256], offsets_s[257];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int R = p.rows, E = p.n_experts, K = p.top_k, S = p.n_shared;
     const int NP = R * K;
-    for (int e = tid; e < E; e += 1024) run_s[e] = 0;
-    for (int c0 = 0; c0 < NP; c0 += 1024) {
-        for (int i = tid; i < 16 * E; i += 1024) mask_s[i] = 0ull;
-        __syncthreads();
-        const int pi = c0 + tid;
-        const int e = pi < NP ? p.idx[pi] : 0;
-        if (pi < NP) atomicOr(&mask_s[e * 16 + (tid >> 6)], 1ull << (tid & 63));
-        __syncthreads();
-        if (pi < NP) {
-            int t = __popcll(mask_s[e * 16 + (tid >> 6)] & ((1ull << (tid & 63)) - 1ull));
-            for (int w = 0; w < (tid >> 6); ++w) t += __popcll(mask_s[e * 16 + w]);
-            p.rank[pi] = run_s[e] + t;
-        }
-        __syncthreads();
-        for (int ee = tid; ee < E; ee += 1024) {
-            int c = 0;
-#pragma unroll
-            for (int w = 0; w < 16; ++w) c += __popcll(mask_s[ee * 16 + w]);
-            run_s[ee] += c;
-        }
-        __syncthreads();
+    unsigned long long* mask = mask_s + wave * E;
+    int* wcnt = wcnt_s + wave * E;
+    for (int e = lane; e < E; e += 64) {
+        mask[e] = 0ull;
+        wcnt[e] = 0;
     }
+    const int pw0 = (int)((int64_t)NP * wave / 16), pw1 = (int)((int64_t)NP * (wave + 1) / 16);
+    const unsigned long long below = (1ull << lane) - 1ull;
+    // rounds of this wave, in batches of 16 (expert ids loaded together); with
+    // one batch (NP <= 16384) the ids and places stay in registers
+    const bool one = NP <= 16 * 1024;
+    int ev[16], rv[16];
+    for (int b0 = pw0; b0 < pw1; b0 += 16 * 64) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int pi = b0 + 64 * c + lane;
+            ev[c] = pi < pw1 ? p.idx[pi] : -1;
+        }
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            if (b0 + 64 * c >= pw1) break;  // uniform
+            const int e = ev[c];
+            if (e >= 0) atomicOr(&mask[e], 1ull << lane);
+            __builtin_amdgcn_wave_barrier();
+            unsigned long long m = 0ull;
+            int base = 0;
+            if (e >= 0) {
+                m = mask[e];
+                base = wcnt[e];
+            }
+            __builtin_amdgcn_wave_barrier();
+            rv[c] = base + __popcll(m & below);
+            if (e >= 0 && (m & below) == 0ull) {  // the expert's first lane of the round
+                wcnt[e] = base + __popcll(m);
+                mask[e] = 0ull;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        if (!one) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const int pi = b0 + 64 * c + lane;
+                if (pi < pw1) p.rank[pi] = rv[c];
+            }
+        }
+    }
+    __syncthreads();
+    // exclusive scan of the waves' counts per expert; totals into run_s
+    for (int e = tid; e < E; e += 1024) {
+        int acc = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int c = wcnt_s[w * E + e];
+            wcnt_s[w * E + e] = acc;
+            acc += c;
+        }
+        run_s[e] = acc;
+    }
+    __syncthreads();
     // offsets and the work list (wave 0, four experts per lane)
     if (wave == 0) {
         const int rb = (R + blk - 1) / blk;
@@ -353,12 +402,21 @@ __global__ __launch_bounds__(1024) void group_large_kernel(MoeParams p, int blk)
         }
     }
     __syncthreads();
-    for (int pi = tid; pi < NP; pi += 1024) {
-        const int pos = offsets_s[p.idx[pi]] + p.rank[pi];
+    auto place = [&](int pi, int e, int r) {
+        const int pos = offsets_s[e] + wcnt_s[wave * E + e] + r;
         p.perm[pos] = pi;
         p.inv[pi] = pos;
         p.vrows[pos] = pi / K;
         if (p.cap_perm) p.cap_perm[pos] = pi;
+    };
+    if (one) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int pi = pw0 + 64 * c + lane;
+            if (pi < pw1) place(pi, ev[c], rv[c]);
+        }
+    } else {
+        for (int pi = pw0 + lane; pi < pw1; pi += 64) place(pi, p.idx[pi], p.rank[pi]);
     }
     for (int i = tid; i < S * R; i += 1024) p.vrows[NP + i] = i % R;
     if (p.cap_counts)
@@ -421,7 +479,7 @@ __global__ __launch_bounds__(64 * EG_NW, 2) void expert_gemm_kernel(GroupedParam
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_ent = p.dense_rows > 0 ? (p.dense_rows + EG_TM - 1) / EG_TM : p.n_virt[0];
     // one work item: entry v, column group cg
-    auto item = [&](const int v, const int cg) {
+    auto item = [&](const int v, const int cg, const int z) {
         int e, off, cnt;
         if (p.dense_rows > 0) {
             e = 0;
@@ -449,8 +507,14 @@ __global__ __launch_bounds__(64 * EG_NW, 2) void expert_gemm_kernel(GroupedParam
             tv[1] = tile[1] < p.out_tiles;
         }
         const uint8_t* tp[2];
+        // k-slice z: stages [z * kst, min((z + 1) * kst, k / 128)) of the k range
+        const int ns_all = p.k / EG_KS;
+        const int kst = p.kslices > 1 ? (ns_all + p.kslices - 1) / p.kslices : ns_all;
+        const int s0 = z * kst, ns = min(ns_all - s0, kst);
+        if (ns <= 0) return;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) tp[t] = base + (int64_t)(tv[t] ? tile[t] : 0) * p.nchunks * CB;
+        for (int t = 0; t < 2; ++t)
+            tp[t] = base + (int64_t)(tv[t] ? tile[t] : 0) * p.nchunks * CB + (int64_t)s0 * CPS * CB;
 
         // staging: wave w fills rows RW*w .. RW*w + RW-1 (RW = 128 / waves), four
         // per load instruction; lane l of instruction i carries row
@@ -472,7 +536,7 @@ __global__ __launch_bounds__(64 * EG_NW, 2) void expert_gemm_kernel(GroupedParam
             uint16_t* dst = xs_dyn + b * (EG_TM * EG_KS) + wave * RW * EG_KS;
 #pragma unroll
             for (int i = 0; i < EG_NDMA; ++i)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void_t*)(dst + i * 4 * EG_KS), 16, voff[i], 2 * s * EG_KS,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void_t*)(dst + i * 4 * EG_KS), 16, voff[i], 2 * (s0 + s) * EG_KS,
                                                          0, 0);
         };
         // operand reads: lane l, block jj of a stage -> row l % 16 of the group,
@@ -493,7 +557,6 @@ __global__ __launch_bounds__(64 * EG_NW, 2) void expert_gemm_kernel(GroupedParam
 #pragma unroll
             for (int g = 0; g < NG; ++g) acc[t][g] = float4v{0.f, 0.f, 0.f, 0.f};
         const float4v zero = {0.f, 0.f, 0.f, 0.f};
-        const int ns = p.k / EG_KS;
         // Weight operands of one (tile, 32-column block): the codes q as fp16
         // (exact) and the block scale d, applied to the block's fp32 product
         // (Q8_0, Q4_0: exact products, fp32 sums); F16: the weights.
@@ -607,15 +670,15 @@ __global__ __launch_bounds__(64 * EG_NW, 2) void expert_gemm_kernel(GroupedParam
                 } else {
 #pragma unroll
                     for (int t = 0; t < 2; ++t)
-                        if (tv[t]) ((float*)p.y)[slot * p.ldy + tile[t] * 16 + (lane & 15)] = acc[t][g][q];
+                        if (tv[t]) ((float*)p.y)[z * p.ly_slice + slot * p.ldy + tile[t] * 16 + (lane & 15)] = acc[t][g][q];
                 }
             }
     };
     // one work item per workgroup: entries dealt round-robin to the XCDs
     // (workgroup id mod 8), all column groups of an entry on one XCD
-    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    const int v = xcd + 8 * (j / n_cg);
-    if (v < n_ent) item(v, j % n_cg);  // uniform per workgroup
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3, nz = max(p.kslices, 1);
+    const int v = xcd + 8 * (j / (n_cg * nz)), r = j % (n_cg * nz);
+    if (v < n_ent) item(v, r % n_cg, r / n_cg);  // uniform per workgroup
 }
 
 // Routing of up to 32 rows in one workgroup.  Router GEMV: wave w computes
@@ -865,6 +928,14 @@ bool moe_gemm_path(int rows, const ocrdec_moe_weights* w) {
     return !moe_small(rows, w) && w->n_experts % 16 == 0 && w->hidden % EG_KS == 0 && w->d_ff % EG_KS == 0 &&
            eg_format(w->router.fmt) && eg_format(w->gate_up.fmt) && eg_format(w->down.fmt) && (w->n_shared == 0 || (eg_format(w->sh_gate_up.fmt) && eg_format(w->sh_down.fmt)));
 }
+// Router GEMM k-slices for large batches: about two 128-column stages per
+// slice, at most eight slices, none of them empty (the kernel gives slice z
+// the stages [z * ceil(n / slices), ...)).
+int router_kslices(int hidden) {
+    const int n = std::max(1, hidden / EG_KS), k0 = std::max(2, (n + 7) / 8);
+    return (n + k0 - 1) / k0;
+}
+
 int moe_max_virt(int rows, const ocrdec_moe_weights* w) {
     const int E = w->n_experts, S = w->n_shared, NP = rows * w->top_k;
     if (moe_small(rows, w)) return S * ((rows + 15) / 16) + std::min(E, NP) + NP / 16;
@@ -877,7 +948,7 @@ MoeWs carve_moe(void* ws, int rows, const ocrdec_moe_weights* w) {
     MoeWs m;
     const int NP = rows * w->top_k, E = w->n_experts, S = w->n_shared;
     const int nslots = NP + S * rows;
-    m.logits = cv.take<float>((size_t)rows * E);
+    m.logits = cv.take<float>((size_t)rows * E * (moe_gemm_path(rows, w) ? router_kslices(w->hidden) : 1));
     m.idx = cv.take<int32_t>(NP);
     m.w = cv.take<float>(NP);
     m.rank = cv.take<int32_t>(NP);
@@ -970,7 +1041,7 @@ template <int FMT, bool GLU>
 void launch_eg_t(const GroupedParams& p, int n_entries, hipStream_t s) {
     const int cgs = GLU ? (p.out_tiles + EG_NW - 1) / EG_NW : (p.out_tiles + 2 * EG_NW - 1) / (2 * EG_NW);
     // every XCD gets room for cgs * ceil(n_entries / 8) work items
-    const int grid = 8 * cgs * ((n_entries + 7) / 8);
+    const int grid = 8 * cgs * std::max(p.kslices, 1) * ((n_entries + 7) / 8);
     hipLaunchKernelGGL((expert_gemm_kernel<FMT, GLU>), dim3(grid), dim3(64 * EG_NW), EG_LDS, s, p, cgs);
 }
 
@@ -1062,6 +1133,10 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         rp.ldx = ldx;
         rp.y = m.logits;
         rp.ldy = E;
+        rp.kslices = router_kslices(H);  // few entries: the k range is split over workgroups
+        rp.ly_slice = (int64_t)rows * E;
+        p.lslices = rp.kslices;
+        p.lslice = rp.ly_slice;
         launch_expert_gemm(w->router.fmt, false, rp, (rows + EG_TM - 1) / EG_TM, s);
         hipLaunchKernelGGL(topk_kernel, dim3((rows + 15) / 16), dim3(1024), 0, s, p);
         hipLaunchKernelGGL(group_large_kernel, dim3(1), dim3(1024), 0, s, p, EG_TM);

@@ -34,6 +34,8 @@ struct MoeParams {
     int32_t* cap_counts;
     int32_t* cap_offsets;
     int32_t* cap_perm;
+    int lslices;     // router logits as lslices partial sums, lslice floats apart (0/1: one)
+    int64_t lslice;
 };
 
 struct GroupedParams {
@@ -56,6 +58,8 @@ struct GroupedParams {
     int64_t ldy;
     int out_tiles;   // expert GEMM: output tiles per expert (SwiGLU: tiles of each half)
     int dense_rows;  // expert GEMM: > 0 means one implicit expert over rows [0, dense_rows) (router)
+    int kslices;     // expert GEMM: k range split over this many workgroups (0/1: none), partial
+    int64_t ly_slice;  //   products of slice z written ly_slice elements after slice 0's
 };
 
 struct CombineParams {
