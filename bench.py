@@ -70,6 +70,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-shaped MoE layer line")
+    ap.add_argument("--no-qhead", action="store_true", help="skip the Q4_0 LM-head and embedding variant")
     ap.add_argument("--lm-iters", type=int, default=50)
     ap.add_argument("--mode", choices=["full", "lm", "prefill"], default="full",
                     help="lm: only the LM-head argmax loop and a device copy of known size (for counter runs); "
@@ -210,6 +211,38 @@ def main():
     lm_bytes = d.vocab * d.hidden * 2.0 + R * d.hidden * 2.0
     lm_gbs = lm_bytes / (lm_us * 1e-6) / 1e9
 
+    # ---- the same step with the LM head and the embedding table in Q4_0 (quantised from the same draws)
+    qhead = None
+    if not args.no_qhead:
+        lmq = synth.random_qmat(synth.Q4_0, synth.stream_id(SEED, "lm_head"), d.vocab, d.hidden, d.w_std)
+        emq = synth.random_qmat(synth.Q4_0, synth.stream_id(SEED, "embed"), d.vocab, d.hidden, d.w_std)
+        dlm, dem = q.DeviceQMat(lmq), q.DeviceQMat(emq)
+        saved = (dm.desc.lm_head, dm.desc.embed, dm.desc.embed_q, dm.src_lm)
+        dm.desc.lm_head, dm.desc.embed, dm.desc.embed_q, dm.src_lm = dlm.desc, None, dem.desc, lmq
+        qrun = run_rows(args.rows, args.steps, args.warmup, False)
+        ws_q = torch.zeros(q.ocrdec_lm_argmax_workspace_bytes(dlm.desc, args.rows), dtype=torch.uint8, device=dev)
+        xq = torch.from_numpy(synth.normal_f16(synth.stream_id(SEED, "lm_x"), (args.rows, d.hidden)).view(np.int16)).to(dev)
+        tq = torch.zeros(args.rows, dtype=torch.int32, device=dev)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                q.ocrdec_lm_argmax(dlm.desc, args.rows, xq, tq, None, ws_q, ws_q.numel(), stream=stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.lm_iters):
+                q.ocrdec_lm_argmax(dlm.desc, args.rows, xq, tq, None, ws_q, ws_q.numel(), stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        lmq_us = e0.elapsed_time(e1) * 1000.0 / args.lm_iters
+        lmq_bytes = d.vocab * d.hidden * 18 / 32 + args.rows * d.hidden * 2.0
+        dm.desc.lm_head, dm.desc.embed, dm.desc.embed_q, dm.src_lm = saved
+        qhead = {"lm_head": "Q4_0", "embed": "Q4_0", "rows": args.rows,
+                 "ms_per_step": round(qrun["ms_per_step"], 4),
+                 "rows_steps_per_s": round(qrun["rows_steps_per_s"], 2),
+                 "algorithmic_MB_per_step": round(qrun["algorithmic_MB_per_step"], 1),
+                 "step_GBps": round(qrun["step_GBps"], 1),
+                 "lm_head_us": round(lmq_us, 2), "lm_head_GBps": round(lmq_bytes / (lmq_us * 1e-6) / 1e9, 1),
+                 "lm_head_frac": round(lmq_bytes / (lmq_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
     # ---- the prefill-shaped MoE layer (2048 tokens, MFMA path), reported beside the decode metric
     prefill = None if args.no_prefill else prefill_moe(args, q, torch, dev, stream)
 
@@ -249,6 +282,7 @@ def main():
                      "traffic_note": traffic_note,
                      "avg_us": round(lm_us, 2), "algorithmic_bytes": lm_bytes},
         "cpu_baseline": cpu,
+        "quantised_head": qhead,
         "prefill_moe": prefill,
         "setup_s": round(t_build, 1),
     }

@@ -277,6 +277,9 @@ typedef struct {
     const uint16_t* final_norm;  /* fp16 [hidden] (needed with an LM head) */
     ocrdec_qmat lm_head;         /* [vocab][hidden]; lm_head.data NULL = no LM head */
     const ocrdec_layer* layers;  /* HOST array [n_layers] */
+    ocrdec_qmat embed_q;         /* [vocab][hidden] embedding in any storage format, used when embed is
+                                    NULL and embed_q.data is not: row tok dequantised (w = d*q, d*(q-8),
+                                    s*(q-z) or the fp16 value) into the fp32 residual */
 } ocrdec_model;
 
 typedef struct {
@@ -295,7 +298,8 @@ typedef struct {
 } ocrdec_step_capture;
 
 /* One decode step (Unlimited-OCR page, "Il decoder e il Mixture of Experts"):
- * h = embed[tok_in] (or `hidden` if tok_in is NULL); for each layer:
+ * h = embed[tok_in] (or row tok_in of embed_q dequantised; or `hidden` if
+ * tok_in is NULL); for each layer:
  *   x = fp16(RMSNorm(h) * attn_norm); qkv = Wqkv x; attention as in
  *   ocrdec_attn_decode (ring mode, scale 1/sqrt(head_dim)); h += Wo o;
  *   x = fp16(RMSNorm(h) * ffn_norm); h += MLP(x) with MLP the dense SwiGLU or

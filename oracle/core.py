@@ -474,7 +474,7 @@ def decode_step(model, state, tok_in=None, hidden_in=None, forced_topk=None,
     rows = list(range(R)) if rows is None else list(rows)
     res = StepResult()
     if tok_in is not None:
-        h = model.embed[np.asarray(tok_in)[rows]].astype(np.float64)
+        h = embed_rows(model, np.asarray(tok_in)[rows])
     else:
         h = f32(np.asarray(hidden_in, np.float64)[rows])
     moe_l = 0
@@ -513,6 +513,23 @@ def decode_step(model, state, tok_in=None, hidden_in=None, forced_topk=None,
     for r in rows:
         state.gen_index[r] += 1
     return res
+
+
+def embed_rows(model, tok) -> np.ndarray:
+    """Embedding lookup: row ``tok[i]`` of the table, as float64.
+
+    [UOCR] "In sintesi": the decode loop starts from the embedding lookup, and
+    the mixed profiles dequantise inside the kernels.  The fp16 table is read
+    as is; a quantised table (``model.embed_q``, any of the four formats) gives
+    each looked-up row dequantised exactly as ``dequant`` defines it.
+    """
+    tok = np.asarray(tok).reshape(-1)
+    if getattr(model, "embed", None) is not None:
+        return model.embed[tok].astype(np.float64)
+    m = model.embed_q
+    row_bytes = m.k * 2 if m.fmt == F16 else (m.k // QK) * _BLOCK_BYTES[m.fmt]
+    data = np.asarray(m.data, np.uint8).reshape(-1)
+    return np.stack([dequant(m.fmt, data[int(t) * row_bytes:(int(t) + 1) * row_bytes], 1, m.k)[0] for t in tok])
 
 
 def argmax_lowest(z: np.ndarray) -> int:

@@ -80,7 +80,7 @@ class LayerDesc(ctypes.Structure):
 class ModelDesc(ctypes.Structure):
     _fields_ = [("n_layers", _i32), ("hidden", _i32), ("n_heads", _i32), ("head_dim", _i32), ("vocab", _i32),
                 ("rope_theta", _f32), ("norm_eps", _f32), ("embed", _vp), ("final_norm", _vp),
-                ("lm_head", QMatDesc), ("layers", ctypes.POINTER(LayerDesc))]
+                ("lm_head", QMatDesc), ("layers", ctypes.POINTER(LayerDesc)), ("embed_q", QMatDesc)]
 
 
 class StateDesc(ctypes.Structure):
@@ -299,14 +299,17 @@ class DeviceModel:
         self.embed = _f16_dev(model.embed, device) if model.embed is not None else None
         self.final_norm = _f16_dev(model.final_norm, device) if model.final_norm is not None else None
         self.lm_head = DeviceQMat(model.lm_head, device) if model.lm_head is not None else None
+        eq = getattr(model, "embed_q", None)
+        self.embed_q = DeviceQMat(eq, device) if (eq is not None and model.embed is None) else None
         self.desc = ModelDesc(len(model.layers), d.hidden, d.n_heads, d.head_dim, d.vocab, d.rope_theta, d.norm_eps,
                               _ptr(self.embed), _ptr(self.final_norm),
-                              self.lm_head.desc if self.lm_head is not None else _empty_qmat(), layers)
+                              self.lm_head.desc if self.lm_head is not None else _empty_qmat(), layers,
+                              self.embed_q.desc if self.embed_q is not None else _empty_qmat())
 
     def layer_view(self, first: int, count: int, with_head: bool):
         """ModelDesc over layers [first, first+count) of this model, sharing its
-        device weights (bind the caches first).  The embedding is kept only for
-        first == 0 (otherwise the input comes from `hidden`); the final norm and
+        device weights (bind the caches first).  The embedding (fp16 or
+        quantised) is kept only for first == 0 (otherwise the input comes from `hidden`); the final norm and
         LM head only if with_head."""
         n = self.desc.n_layers
         if not (0 <= first and count >= 1 and first + count <= n):
@@ -317,7 +320,8 @@ class DeviceModel:
         d = self.desc
         view = ModelDesc(count, d.hidden, d.n_heads, d.head_dim, d.vocab, d.rope_theta, d.norm_eps,
                          d.embed if first == 0 else None, d.final_norm if with_head else None,
-                         d.lm_head if with_head else _empty_qmat(), layers)
+                         d.lm_head if with_head else _empty_qmat(), layers,
+                         d.embed_q if first == 0 else _empty_qmat())
         view._keep_layers = layers
         return view
 

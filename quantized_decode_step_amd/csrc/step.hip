@@ -57,6 +57,50 @@ __global__ __launch_bounds__(64) void embed_norm_kernel(const int32_t* tok, cons
     wave_rmsnorm_row(hr, gamma, H, eps, x + (int64_t)r * H);
 }
 
+// h[r] = row tok[r] of a packed quantised table, dequantised; x[r] = norm(h[r]).
+// One wavefront per row.  In the packed layout row t sits in 16-row tile
+// t / 16 at position t % 16: for chunk c and k-group g, "lane" t%16 + 16g of
+// the chunk holds the codes of columns c*KC + 32j + 8g + i (block j < SB,
+// i < 8) and the row's block scales.  Lane l of the wavefront takes the
+// (chunk, group) pairs p = l, l+64, ...; each product d*q is exact in fp32
+// (q and (q-8) are integers of at most 8 bits, d has 11).
+template <int FMT>
+__global__ __launch_bounds__(64) void embed_q_norm_kernel(const int32_t* tok, const uint8_t* table, int vocab,
+                                                          int64_t nchunks, float* h, const uint16_t* gamma, int H,
+                                                          float eps, uint16_t* x) {
+    constexpr int SB = Geom<FMT>::SB, CB = Geom<FMT>::CB, KC = 32 * SB;
+    const int r = blockIdx.x, lane = threadIdx.x;
+    float* hr = h + (int64_t)r * H;
+    int t = tok[r];
+    t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
+    const uint8_t* tile = table + (int64_t)(t >> 4) * nchunks * CB;
+    const int np = (int)nchunks * 4;
+    for (int p = lane; p < np; p += 64) {
+        const int c = p >> 2, g = p & 3;
+        WRegs w;
+        load_wchunk<FMT>(tile + (int64_t)c * CB, (t & 15) + 16 * g, w);
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const half8v q = wfrag<FMT>(w, j);
+            const float d = wscale<FMT>(w, j);
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if constexpr (FMT == OCRDEC_U8A_G32) v[i] = d * ((float)q[i] - wzero_u8a(w, j));
+                else if constexpr (FMT == OCRDEC_F16) v[i] = (float)q[i];
+                else v[i] = d * (float)q[i];
+            }
+            const int k0 = c * KC + 32 * j + 8 * g;
+            if (k0 < H) {
+                ((float4*)(hr + k0))[0] = make_float4(v[0], v[1], v[2], v[3]);
+                ((float4*)(hr + k0))[1] = make_float4(v[4], v[5], v[6], v[7]);
+            }
+        }
+    }
+    __threadfence_block();
+    wave_rmsnorm_row(hr, gamma, H, eps, x + (int64_t)r * H);
+}
+
 // x[r] = fp16(RMSNorm(h[r]) * gamma): one wavefront per row.
 __global__ __launch_bounds__(64) void norm_kernel(const float* h, const uint16_t* gamma, int H, float eps,
                                                   uint16_t* x) {
@@ -161,6 +205,10 @@ ocrdec_status check_step(const ocrdec_model* m, const ocrdec_state* st) {
                           tag + "dense_down must be [hidden][dense_ff]");
         }
     }
+    if (!m->embed && m->embed_q.data) {
+        if ((s = check_qmat(&m->embed_q, "embed_q")) != OCRDEC_OK) return s;
+        OCR_CHECK_ARG(m->embed_q.k == H && m->embed_q.n == m->vocab, "embed_q must be [vocab][hidden]");
+    }
     if (m->lm_head.data) {
         if ((s = check_qmat(&m->lm_head, "lm_head")) != OCRDEC_OK) return s;
         OCR_CHECK_ARG(m->lm_head.k == H && m->lm_head.n == m->vocab, "lm_head must be [vocab][hidden]");
@@ -191,7 +239,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     ocrdec_status s0 = check_step(m, st);
     if (s0 != OCRDEC_OK) return s0;
     OCR_CHECK_ARG(tok_in || hidden, "either tok_in or hidden must be given");
-    OCR_CHECK_ARG(!tok_in || m->embed, "tok_in needs an embedding table");
+    OCR_CHECK_ARG(!tok_in || m->embed || m->embed_q.data, "tok_in needs an embedding table");
     const int R = st->rows, H = m->hidden, HD = m->n_heads * m->head_dim;
     const int cache_cap = st->prefix_cap + st->ring_cap;
     OCR_CHECK_ARG(cache_cap <= (1 << 16), "prefix_cap + ring_cap must be <= 65536");
@@ -202,8 +250,25 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     hipStream_t s = (hipStream_t)stream;
     StepWs w = carve_step(ws, m, R, cache_cap);
 
-    hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(64), 0, s, tok_in, m->embed, m->vocab, hidden, w.h,
-                       m->layers[0].attn_norm, H, m->norm_eps, w.x);
+    if (tok_in && !m->embed) {
+        const uint8_t* tq = (const uint8_t*)m->embed_q.data;
+        const int64_t nch = n_chunks(m->embed_q.fmt, H);
+#define OCR_EQ(F_)                                                                                                 \
+    case F_:                                                                                                       \
+        hipLaunchKernelGGL(embed_q_norm_kernel<F_>, dim3(R), dim3(64), 0, s, tok_in, tq, m->vocab, nch, w.h,      \
+                           m->layers[0].attn_norm, H, m->norm_eps, w.x);                                           \
+        break;
+        switch (m->embed_q.fmt) {
+            OCR_EQ(OCRDEC_F16)
+            OCR_EQ(OCRDEC_Q8_0)
+            OCR_EQ(OCRDEC_Q4_0)
+            OCR_EQ(OCRDEC_U8A_G32)
+        }
+#undef OCR_EQ
+    } else {
+        hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(64), 0, s, tok_in, m->embed, m->vocab, hidden, w.h,
+                           m->layers[0].attn_norm, H, m->norm_eps, w.x);
+    }
     // attention arguments shared by every layer (RoPE frequencies once per call)
     AttnParams ap0{};
     ap0.rows = R;

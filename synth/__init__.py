@@ -174,6 +174,7 @@ class Dims:
     fmt_expert: int = Q4_0      # routed experts
     fmt_shared: int = Q4_0
     fmt_lm: int = F16
+    fmt_embed: int = F16        # F16: Model.embed (fp16 array); otherwise Model.embed_q (QMat)
     w_std: float = 0.02
 
 
@@ -202,6 +203,7 @@ class Model:
     final_norm: np.ndarray | None       # fp16 [H]
     lm_head: QMat | None                # [V, H]
     layers: list = field(default_factory=list)
+    embed_q: QMat | None = None         # [V, H] quantised embedding (when embed is None)
 
 
 def norm_weight(stream: int, n: int, std: float) -> np.ndarray:
@@ -245,10 +247,14 @@ def make_model(d: Dims, seed: int, with_embed: bool = True, with_lm: bool = True
             lay.dense_gate_up = random_qmat(d.fmt_dense, stream_id(seed, "dense_gate_up", l), 2 * d.dense_ff, H, d.w_std)
             lay.dense_down = random_qmat(d.fmt_dense, stream_id(seed, "dense_down", l), H, d.dense_ff, d.w_std)
         layers.append(lay)
-    embed = normal_f16(stream_id(seed, "embed"), (d.vocab, H), 0.0, d.w_std) if with_embed else None
+    embed = embed_q = None
+    if with_embed and d.fmt_embed == F16:
+        embed = normal_f16(stream_id(seed, "embed"), (d.vocab, H), 0.0, d.w_std)
+    elif with_embed:
+        embed_q = random_qmat(d.fmt_embed, stream_id(seed, "embed"), d.vocab, H, d.w_std)
     lm = random_qmat(d.fmt_lm, stream_id(seed, "lm_head"), d.vocab, H, d.w_std) if with_lm else None
     fnorm = norm_weight(stream_id(seed, "final_norm"), H, d.w_std) if with_lm else None
-    return Model(d, seed, embed, fnorm, lm, layers)
+    return Model(d, seed, embed, fnorm, lm, layers, embed_q)
 
 
 @dataclass

@@ -258,7 +258,7 @@ def test_moe_prefill_formats(q, rows, fmt, F):
 # -----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("fmt,n,rows", [(synth.F16, 129280, 1), (synth.F16, 129280, 24), (synth.Q8_0, 5000, 7),
-                                        (synth.Q4_0, 999, 32)])
+                                        (synth.Q4_0, 999, 32), (synth.Q4_0, 129280, 24), (synth.Q8_0, 129280, 1)])
 def test_lm_argmax_parity(q, fmt, n, rows):
     import torch
     seed = 77 + n + rows

@@ -127,6 +127,15 @@ def test_step_small_rows_32(q):
               n_steps=3)
 
 
+# quantised embedding tables and LM heads through the whole step (tokens from
+# the table, argmax over the quantised head)
+@pytest.mark.parametrize("fe,fl", [(synth.Q4_0, synth.Q4_0), (synth.Q8_0, synth.Q8_0), (synth.U8A_G32, synth.F16),
+                                   (synth.F16, synth.Q4_0)])
+def test_step_small_quantised_embed_and_head(q, fe, fl):
+    d = small_dims(fmt_embed=fe, fmt_lm=fl)
+    run_steps(q, d, 510 + 4 * fe + fl, prefix_len=[40, 9, 25], gen_index=[2, 7, 30], n_steps=6)
+
+
 def test_step_single_dense_layer_fp16(q):
     """One dense fp16 decoder layer over 256 cached positions (no embedding or
     LM head: the hidden state goes in and comes out)."""

@@ -86,6 +86,38 @@ def test_dequant_block_order_along_k():
     assert np.array_equal(w[1, :32], np.full(32, 4.0)) and np.array_equal(w[1, 32:], np.full(32, 8.0))
 
 
+def test_embed_rows_quantised_table():
+    """Embedding lookup from a quantised table: row t of a Q4_0 table whose row t
+    has scales (t+1, 2(t+1)) and every code 9 is (t+1) over the first block and
+    2(t+1) over the second; an fp16 table gives its rows as stored; the Q8_0 and
+    int8-asymmetric tables give the rows of their dense dequantisation."""
+    V, H = 7, 64
+
+    class M:
+        embed = None
+    m = M()
+    d = [[t + 1.0, 2.0 * (t + 1.0)] for t in range(V)]
+    m.embed_q = enc_q4_0(d, np.full((V, H), 9))
+    tok = np.array([6, 0, 3, 3])
+    h = O.embed_rows(m, tok)
+    for i, t in enumerate(tok):
+        assert np.array_equal(h[i, :32], np.full(32, t + 1.0)) and np.array_equal(h[i, 32:], np.full(32, 2.0 * (t + 1)))
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal((V, H)) * 0.1
+    m.embed_q = enc_f16(w)
+    assert np.array_equal(O.embed_rows(m, tok), O.f16(w)[tok])
+    for enc in (enc_q8_0, enc_u8a):
+        if enc is enc_q8_0:
+            m.embed_q = enc(np.abs(w[:, ::32]) + 0.01, rng.integers(-128, 128, (V, H)))
+        else:
+            m.embed_q = enc(np.abs(w[:, ::32]) + 0.01, np.full((V, 2), 3.0), rng.integers(0, 256, (V, H)))
+        dense = O.dequant(m.embed_q.fmt, m.embed_q.data, V, H)
+        assert np.array_equal(O.embed_rows(m, tok), dense[tok])
+    m2 = M()
+    m2.embed = O.f16(w).astype(np.float16)
+    assert np.array_equal(O.embed_rows(m2, tok), O.f16(w)[tok])
+
+
 def test_quantiser_roundtrip_error_bound():
     """Draws quantised by the input generator dequantise to within half a step
     (Q8_0, Q4_0, int8-asymmetric) of the drawn values, plus what the fp16
