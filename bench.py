@@ -275,7 +275,9 @@ def main():
                      "frac": round(main_run["step_GBps"] / HBM_PEAK_GBS, 4),
                      "distinct_experts_per_moe_layer": main_run["distinct_experts_per_moe_layer"]},
         "rows_sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in sweep],
-        "roofline": {"kernel": "gemv_kernel<F16,4,1,1,ARGMAX> (LM head %dx%d + fused argmax, %d row(s))"
+        "roofline": {"kernel": ("lm_argmax_kernel<F16, ring 10> (LM head %dx%d + fused argmax, %d row(s); "
+                                "one CU-balanced workgroup per CU, then the partial merge)" if R <= 16 else
+                                "gemv_kernel<F16,4,1,1,ARGMAX> (LM head %dx%d + fused argmax, %d row(s))")
                                % (d.vocab, d.hidden, R),
                      "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,

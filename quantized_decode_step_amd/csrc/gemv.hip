@@ -234,6 +234,183 @@ void launch_gemv(int fmt, int epi, const GemvPlan& pl, GemvParams p, hipStream_t
 
 size_t argmax_ws_bytes(int grid, int rows) { return align256((size_t)grid * rows * 3 * sizeof(float)); }
 
+// ---------------------------------------------------------------------------
+// LM head with fused argmax for up to 16 rows, balanced within each CU
+//
+// One workgroup of eight wavefronts per CU (its LDS request leaves room for
+// no second one) owns an equal slice of the 16-row tiles.  Its wavefronts
+// take tiles one at a time from an LDS counter, so a wavefront the CU favours
+// (the issue arbiter prefers older waves) simply takes more tiles, and all of
+// a CU's wavefronts finish within about one tile of each other.  Each
+// wavefront streams its tiles as one chunk sequence through a ring of PF
+// chunks: the ring runs on into the next tile's first chunks while the
+// current tile finishes.  The activations (<= 16 rows) are staged in LDS
+// once.  Per tile the 16 dot products of every row update a running (best,
+// index, second) per lane; the workgroup's partial goes to part[blockIdx.x].
+// ---------------------------------------------------------------------------
+
+constexpr int LM_WAVES = 8;
+constexpr size_t LM_LDS = 96 * 1024;  // > half the CU's LDS: one workgroup per CU
+
+template <int FMT, int PF>
+__global__ __launch_bounds__(64 * LM_WAVES, 1) void lm_argmax_kernel(GemvParams p) {
+    constexpr int SB = Geom<FMT>::SB, CB = Geom<FMT>::CB;
+    extern __shared__ __align__(16) uint16_t xl_dyn[];
+    __shared__ float amx[LM_WAVES * 16 * 3];
+    __shared__ int next_s;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ntiles = (p.n + 15) / 16;
+    const int t0 = (int)((int64_t)ntiles * blockIdx.x / gridDim.x);
+    const int nt = (int)((int64_t)ntiles * (blockIdx.x + 1) / gridDim.x) - t0;
+    const int nc = (int)p.nchunks, nblk = p.k / 32, ldl = xlds_stride(p.k), R = p.xs.rows;
+    // tiles of the slice: wave w starts with tile w, then asks the counter
+    if (threadIdx.x == 0) next_s = LM_WAVES;
+    auto tptr = [&](int u) { return p.w + (int64_t)(t0 + min(u, max(nt - 1, 0))) * nc * CB; };
+    WRegs ring[PF];
+    int ucur = wave;
+#pragma unroll
+    for (int s = 0; s < PF; ++s) load_wchunk<FMT>(tptr(ucur) + (int64_t)s * CB, lane, ring[s]);
+    stage_x(p.xs, 0, 16, p.k, xl_dyn, ldl);
+    __syncthreads();
+    auto grab = [&]() {
+        int u = 0;
+        if (lane == 0) u = atomicAdd(&next_s, 1);
+        return __builtin_amdgcn_readfirstlane(u);
+    };
+    int unxt = grab();
+    float best[4], second[4];
+    int bidx[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        best[v] = -INFINITY;
+        second[v] = -INFINITY;
+        bidx[v] = 0x7fffffff;
+    }
+    while (ucur < nt) {  // uniform per wavefront
+        const int unn = unxt < nt ? grab() : unxt;  // the tile after the next, asked for early
+        const uint8_t* tc = tptr(ucur);
+        const uint8_t* tn = tptr(unxt);
+        float4v acc[1][1] = {{float4v{0.f, 0.f, 0.f, 0.f}}};
+        for (int c0 = 0; c0 < nc; c0 += PF) {
+#pragma unroll
+            for (int s = 0; s < PF; ++s) {
+                const int c = c0 + s;
+                half8v xa[SB][1];
+                float4v xs[SB][1];
+                lds_xfrags<FMT, 1>(xl_dyn, ldl, R, c, nblk, lane, xa);
+                xsums<FMT, 1>(xa, xs);
+                chunk_mac<FMT, 1>(ring[s], xa, xs, acc[0]);
+                // refill the slot with the chunk PF further on in the stream
+                // (the next tile's, past this one's end; nc % PF == 0)
+                const int cf = c + PF;
+                load_wchunk<FMT>(cf < nc ? tc + (int64_t)cf * CB : tn + (int64_t)(cf - nc) * CB, lane, ring[s]);
+            }
+        }
+        const int row = (t0 + ucur) * 16 + (lane & 15);
+        if (row < p.n) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float val = acc[0][0][v];
+                if (val > best[v]) {
+                    second[v] = best[v];
+                    best[v] = val;
+                    bidx[v] = row;
+                } else if (val > second[v]) {
+                    second[v] = val;
+                }
+            }
+        }
+        ucur = unxt;
+        unxt = unn;
+    }
+    // merge across the 16 lanes that share a token, then across the wavefronts
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float ob = __shfl_xor(best[v], o, 64), os = __shfl_xor(second[v], o, 64);
+            const int oi = __shfl_xor(bidx[v], o, 64);
+            argmax_merge(best[v], bidx[v], second[v], ob, oi, os);
+        }
+    if ((lane & 15) == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float* e = amx + (wave * 16 + 4 * (lane >> 4) + v) * 3;
+            e[0] = best[v];
+            e[1] = __int_as_float(bidx[v]);
+            e[2] = second[v];
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < R) {
+        const int tok = threadIdx.x;
+        float b = -INFINITY, s2 = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int w = 0; w < LM_WAVES; ++w) {
+            const float* e = amx + (w * 16 + tok) * 3;
+            argmax_merge(b, bi, s2, e[0], __float_as_int(e[1]), e[2]);
+        }
+        float* out = p.part + ((int64_t)blockIdx.x * R + tok) * 3;
+        out[0] = b;
+        out[1] = __int_as_float(bi);
+        out[2] = s2;
+    }
+}
+
+namespace {
+int device_cus() {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!cus[dev]) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+        cus[dev] = c;
+    }
+    return cus[dev];
+}
+// ring depth in chunks: ~10 KiB per wavefront in flight; the chunk count of
+// a row must be a multiple of it (0: not supported, the general GEMV runs)
+int lm_pf(int fmt, int k) {
+    const int64_t nc = n_chunks(fmt, k);
+    if (fmt == OCRDEC_F16) return nc % 10 == 0 ? 10 : nc % 8 == 0 ? 8 : 0;
+    return nc % 5 == 0 ? 5 : nc % 4 == 0 ? 4 : 0;
+}
+}  // namespace
+
+LmPlan plan_lm(int fmt, int n, int k, int rows) {
+    LmPlan lp;
+    const int pf = lm_pf(fmt, k);
+    const int ntiles = (n + 15) / 16;
+    const size_t xb = (size_t)16 * (k + 8) * 2;  // the staged activations (row stride k + 8)
+    lp.dyn = rows <= 16 && pf > 0 && xb <= LM_LDS && ntiles >= 8 * device_cus();
+    lp.grid = lp.dyn ? device_cus() : plan_gemv(fmt, n, k, rows, EPI_ARGMAX).grid;
+    return lp;
+}
+
+void launch_lm_argmax(int fmt, const LmPlan& lp, GemvParams p, hipStream_t s) {
+    if (!lp.dyn) {
+        const GemvPlan pl = plan_gemv(fmt, p.n, p.k, p.xs.rows, EPI_ARGMAX);
+        launch_gemv(fmt, EPI_ARGMAX, pl, p, s);
+        return;
+    }
+    const int pf = lm_pf(fmt, p.k);
+#define OCR_LM(F_, A_, B_)                                                                                      \
+    case F_:                                                                                                    \
+        if (pf == A_)                                                                                           \
+            hipLaunchKernelGGL((lm_argmax_kernel<F_, A_>), dim3(lp.grid), dim3(64 * LM_WAVES), LM_LDS, s, p);    \
+        else                                                                                                    \
+            hipLaunchKernelGGL((lm_argmax_kernel<F_, B_>), dim3(lp.grid), dim3(64 * LM_WAVES), LM_LDS, s, p);    \
+        break;
+    switch (fmt) {
+        OCR_LM(OCRDEC_F16, 10, 8)
+        OCR_LM(OCRDEC_Q8_0, 5, 4)
+        OCR_LM(OCRDEC_Q4_0, 5, 4)
+        OCR_LM(OCRDEC_U8A_G32, 5, 4)
+    }
+#undef OCR_LM
+}
+
 // Merge of the per-workgroup (best, index, second) partials: one workgroup
 // per row, a strided pass then a tree in LDS (the merge is associative and
 // commutative, so the result does not depend on the order).
@@ -311,8 +488,7 @@ extern "C" ocrdec_status ocrdec_lm_argmax_workspace_bytes(const ocrdec_qmat* W, 
     if (st != OCRDEC_OK) return st;
     OCR_CHECK_ARG(rows >= 1 && rows <= 32, "rows must be in [1, 32]");
     OCR_CHECK_ARG(bytes, "bytes is NULL");
-    GemvPlan pl = plan_gemv(W->fmt, W->n, W->k, rows, EPI_ARGMAX);
-    *bytes = argmax_ws_bytes(pl.grid, rows);
+    *bytes = argmax_ws_bytes(plan_lm(W->fmt, W->n, W->k, rows).grid, rows);
     return OCRDEC_OK;
 }
 
@@ -323,8 +499,8 @@ extern "C" ocrdec_status ocrdec_lm_argmax(const ocrdec_qmat* W, int32_t rows, co
     OCR_CHECK_ARG(rows >= 1 && rows <= 32, "rows must be in [1, 32]");
     OCR_CHECK_ARG(x && tok_out, "x and tok_out must be non-NULL");
     OCR_CHECK_ARG(((uintptr_t)x & 15) == 0, "x must be 16-byte aligned");
-    GemvPlan pl = plan_gemv(W->fmt, W->n, W->k, rows, EPI_ARGMAX);
-    const size_t need = argmax_ws_bytes(pl.grid, rows);
+    const LmPlan lp = plan_lm(W->fmt, W->n, W->k, rows);
+    const size_t need = argmax_ws_bytes(lp.grid, rows);
     if (!ws || ws_bytes < need)
         return fail(OCRDEC_ERR_WORKSPACE, "argmax workspace: need " + std::to_string(need) + " bytes, got " +
                                               std::to_string(ws ? ws_bytes : 0));
@@ -335,7 +511,7 @@ extern "C" ocrdec_status ocrdec_lm_argmax(const ocrdec_qmat* W, int32_t rows, co
     p.nchunks = n_chunks(W->fmt, W->k);
     p.xs = XDirect{x, W->k, rows};
     p.part = (float*)ws;
-    launch_gemv(W->fmt, EPI_ARGMAX, pl, p, (hipStream_t)stream);
-    launch_argmax_final((float*)ws, pl.grid, rows, tok_out, top2, nullptr, (hipStream_t)stream);
+    launch_lm_argmax(W->fmt, lp, p, (hipStream_t)stream);
+    launch_argmax_final((float*)ws, lp.grid, rows, tok_out, top2, nullptr, (hipStream_t)stream);
     return launch_status("ocrdec_lm_argmax");
 }

@@ -27,6 +27,15 @@ struct GemvPlan {
 GemvPlan plan_gemv(int fmt, int n, int k, int rows, int epi);
 void launch_gemv(int fmt, int epi, const GemvPlan& pl, GemvParams p, hipStream_t s);
 size_t argmax_ws_bytes(int grid, int rows);
+
+// LM head with fused argmax: the CU-balanced kernel for up to 16 rows, or
+// the general GEMV; grid = number of partials for launch_argmax_final.
+struct LmPlan {
+    bool dyn;
+    int grid;
+};
+LmPlan plan_lm(int fmt, int n, int k, int rows);
+void launch_lm_argmax(int fmt, const LmPlan& lp, GemvParams p, hipStream_t s);
 void launch_argmax_final(const float* part, int n_wg, int rows, int32_t* tok_out, float* top2, int32_t* gen_index,
                          hipStream_t s);
 

@@ -132,7 +132,7 @@ struct StepWs {
 
 int lm_grid(const ocrdec_model* m, int rows) {
     if (!m->lm_head.data) return 0;
-    return plan_gemv(m->lm_head.fmt, m->lm_head.n, m->lm_head.k, rows, EPI_ARGMAX).grid;
+    return plan_lm(m->lm_head.fmt, m->lm_head.n, m->lm_head.k, rows).grid;
 }
 
 StepWs carve_step(void* ws, const ocrdec_model* m, int rows, int cache_cap) {
@@ -372,7 +372,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                            w.h, hidden, n);
     }
     if (m->lm_head.data && tok_out) {
-        GemvPlan pl = plan_gemv(m->lm_head.fmt, m->vocab, H, R, EPI_ARGMAX);
+        const LmPlan lp = plan_lm(m->lm_head.fmt, m->vocab, H, R);
         GemvParams gp{};
         gp.w = (const uint8_t*)m->lm_head.data;
         gp.n = m->vocab;
@@ -380,8 +380,8 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
         gp.nchunks = n_chunks(m->lm_head.fmt, H);
         gp.xs = XDirect{w.x, H, R};
         gp.part = w.lm_part;
-        launch_gemv(m->lm_head.fmt, EPI_ARGMAX, pl, gp, s);
-        launch_argmax_final(w.lm_part, pl.grid, R, tok_out, cap ? cap->lm_top2 : nullptr, st->gen_index, s);
+        launch_lm_argmax(m->lm_head.fmt, lp, gp, s);
+        launch_argmax_final(w.lm_part, lp.grid, R, tok_out, cap ? cap->lm_top2 : nullptr, st->gen_index, s);
     } else {
         hipLaunchKernelGGL(bump_kernel, dim3(1), dim3(64), 0, s, st->gen_index, R);
     }

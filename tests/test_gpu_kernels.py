@@ -257,8 +257,12 @@ def test_moe_prefill_formats(q, rows, fmt, F):
 # ocrdec_lm_argmax
 # -----------------------------------------------------------------------------
 
+# full-vocabulary heads with up to 16 rows take the CU-balanced kernel, the
+# others the general GEMV with the argmax epilogue
 @pytest.mark.parametrize("fmt,n,rows", [(synth.F16, 129280, 1), (synth.F16, 129280, 24), (synth.Q8_0, 5000, 7),
-                                        (synth.Q4_0, 999, 32), (synth.Q4_0, 129280, 24), (synth.Q8_0, 129280, 1)])
+                                        (synth.Q4_0, 999, 32), (synth.Q4_0, 129280, 24), (synth.Q8_0, 129280, 1),
+                                        (synth.F16, 129280, 16), (synth.Q4_0, 129280, 3),
+                                        (synth.U8A_G32, 100000, 2)])
 def test_lm_argmax_parity(q, fmt, n, rows):
     import torch
     seed = 77 + n + rows
@@ -287,15 +291,17 @@ def test_lm_argmax_parity(q, fmt, n, rows):
             assert abs(t2[r, 1] - srt[1]) <= 1e-4 * max(1, abs(srt[1]))
 
 
-def test_lm_argmax_ties_go_to_lowest_index(q):
+@pytest.mark.parametrize("n,k", [(4096, 128), (40000, 256)])
+def test_lm_argmax_ties_go_to_lowest_index(q, n, k):
     import torch
-    _say("lm_argmax planted ties")
-    n, k, rows = 4096, 128, 3
+    _say("lm_argmax planted ties", n, k)
+    rows = 3
     w = np.zeros((n, k), np.float16)
     x = np.zeros((rows, k), np.float16)
     x[:, 0] = 1
-    # row r of x: winners planted at several equal maxima
-    for v in (17, 900, 4000):
+    # row r of x: winners planted at several equal maxima (far apart: other
+    # workgroups and wavefronts of the CU-balanced kernel hold them)
+    for v in (17, 900, 4000, n - 5):
         w[v, 0] = 2.0
     w[3000, 0] = 1.5
     m = synth.QMat(synth.F16, n, k, w.reshape(-1).view(np.uint8).copy())

@@ -136,6 +136,12 @@ def test_step_small_quantised_embed_and_head(q, fe, fl):
     run_steps(q, d, 510 + 4 * fe + fl, prefix_len=[40, 9, 25], gen_index=[2, 7, 30], n_steps=6)
 
 
+# a full-size vocabulary: the step's LM head runs on the CU-balanced kernel
+def test_step_full_vocab_head(q):
+    d = small_dims(n_layers=2, vocab=129280)
+    run_steps(q, d, 520, prefix_len=[40, 3, 22, 31], gen_index=[1, 4, 9, 6], n_steps=3)
+
+
 def test_step_single_dense_layer_fp16(q):
     """One dense fp16 decoder layer over 256 cached positions (no embedding or
     LM head: the hidden state goes in and comes out)."""
