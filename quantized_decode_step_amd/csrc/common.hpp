@@ -205,7 +205,7 @@ OCR_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
 // x = fp16(h / sqrt(mean(h^2) + eps) * gamma) for one fp32 row of
 // H <= 256 * NV values (H % 4 == 0) by one wavefront: every load (row and
 // gain) is issued before the first use, so the row costs one memory round
-// trip.  The result goes to x and, if xl is non-NULL, also to xl (LDS).
+// trip.  The result goes to x and to xl (LDS), each if non-NULL.
 template <int NV = 16>
 OCR_DEV void wave_rmsnorm_row(const float* h, const uint16_t* gamma, int H, float eps, uint16_t* x,
                               uint16_t* xl = nullptr) {
@@ -232,7 +232,7 @@ OCR_DEV void wave_rmsnorm_row(const float* h, const uint16_t* gamma, int H, floa
                                 ((uint32_t)f2h(v[i].y * inv * h2f((uint16_t)(g[i].x >> 16))) << 16);
             const uint32_t hi = (uint32_t)f2h(v[i].z * inv * h2f((uint16_t)(g[i].y & 0xFFFF))) |
                                 ((uint32_t)f2h(v[i].w * inv * h2f((uint16_t)(g[i].y >> 16))) << 16);
-            ((uint2*)x)[c4] = make_uint2(lo, hi);
+            if (x) ((uint2*)x)[c4] = make_uint2(lo, hi);
             if (xl) ((uint2*)xl)[c4] = make_uint2(lo, hi);
         }
     }

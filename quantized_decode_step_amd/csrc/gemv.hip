@@ -5,10 +5,12 @@
 
 namespace ocrdec {
 
-// XT = 1, 2: 16 or 32 tokens per pass.  LDSX: activations staged in LDS;
-// otherwise their fragments are loaded from global memory alongside the
-// weights (for k too large to stage).
-template <int FMT, int NT, int XT, int KS, int EPI, bool LDSX>
+// XT = 1, 2: 16 or 32 tokens per pass.  XSRC: where the activations come
+// from: X_GLOBAL, their fragments are loaded from global memory alongside the
+// weights (for k too large to stage); X_LDS, they are staged in LDS;
+// X_NORM (XT = 1), formed in LDS as RMSNorm(hn) * gamma.
+constexpr int X_GLOBAL = 0, X_LDS = 1, X_NORM = 2;
+template <int FMT, int NT, int XT, int KS, int EPI, int XSRC>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
     constexpr int CB = Geom<FMT>::CB;
     extern __shared__ __align__(16) uint16_t xl_dyn[];
@@ -41,8 +43,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
         for (int i = 0; i < NT; ++i)
 #pragma unroll
             for (int xt = 0; xt < XT; ++xt) acc[i][xt] = float4v{0.f, 0.f, 0.f, 0.f};
-        if constexpr (LDSX) {
-            auto stage = [&]() { stage_x(p.xs, tok0, 16 * XT, p.k, xl_dyn, ldl); };
+        if constexpr (XSRC != X_GLOBAL) {
+            auto stage = [&]() {
+                if constexpr (XSRC == X_NORM) stage_norm(p.hn, p.gamma, p.eps, p.xs.rows, tok0, p.k, xl_dyn, ldl);
+                else stage_x(p.xs, tok0, 16 * XT, p.k, xl_dyn, ldl);
+            };
             kloop_lds<FMT, NT, XT>(tile, c0, c1, stage, xl_dyn, ldl, p.xs.rows - tok0, nblk, lane, acc);
         } else {
             kloop<FMT, NT, XT>(tile, c0, c1, p.xs, tok0, nblk, lane, acc);
@@ -161,21 +166,23 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
 
 namespace {
 
-template <int FMT, int NT, int XT, int KS, int EPI, bool LDSX>
+template <int FMT, int NT, int XT, int KS, int EPI, int XSRC>
 void launch_t(const GemvParams& p, hipStream_t s) {
     const int groups_per_wg = 4 / KS;
     const int grid = (p.n_groups + groups_per_wg - 1) / groups_per_wg;
-    const size_t lds = LDSX ? lds_x_bytes(p.k, XT) : 0;
-    hipLaunchKernelGGL((gemv_kernel<FMT, NT, XT, KS, EPI, LDSX>), dim3(grid), dim3(256), lds, s, p);
+    const size_t lds = XSRC != X_GLOBAL ? lds_x_bytes(p.k, XT) : 0;
+    hipLaunchKernelGGL((gemv_kernel<FMT, NT, XT, KS, EPI, XSRC>), dim3(grid), dim3(256), lds, s, p);
 }
 
 template <int FMT, int EPI>
-void launch_fmt(const GemvParams& p, int nt, int ks, int xt, bool lds, hipStream_t s) {
-#define OCR_L(NT_, KS_, XT_)                                                    \
-    if (nt == NT_ && ks == KS_ && xt == XT_) {                                  \
-        if (lds) launch_t<FMT, NT_, XT_, KS_, EPI, true>(p, s);                 \
-        else launch_t<FMT, NT_, XT_, KS_, EPI, false>(p, s);                    \
-        return;                                                                 \
+void launch_fmt(const GemvParams& p, int nt, int ks, int xt, int xsrc, hipStream_t s) {
+#define OCR_L(NT_, KS_, XT_)                                                                 \
+    if (nt == NT_ && ks == KS_ && xt == XT_) {                                               \
+        if constexpr (XT_ == 1)                                                              \
+            if (xsrc == X_NORM) return launch_t<FMT, NT_, XT_, KS_, EPI, X_NORM>(p, s);       \
+        if (xsrc == X_LDS) launch_t<FMT, NT_, XT_, KS_, EPI, X_LDS>(p, s);                   \
+        else launch_t<FMT, NT_, XT_, KS_, EPI, X_GLOBAL>(p, s);                              \
+        return;                                                                              \
     }
     if constexpr (EPI == EPI_GLU) {
         OCR_L(2, 1, 1) OCR_L(2, 1, 2) OCR_L(2, 4, 1) OCR_L(2, 4, 2)
@@ -211,15 +218,20 @@ GemvPlan plan_gemv(int fmt, int n, int k, int rows, int epi) {
     return pl;
 }
 
-void launch_gemv(int fmt, int epi, const GemvPlan& pl, GemvParams p, hipStream_t s) {
+void launch_gemv(int fmt, int epi, const GemvPlan& plan, GemvParams p, hipStream_t s) {
+    // forming the activations from the residual needs the LDS staging and
+    // 16-token passes
+    GemvPlan pl = plan;
+    if (p.hn) pl.xt = 1;
+    const int xsrc = p.hn ? X_NORM : (pl.lds ? X_LDS : X_GLOBAL);
     p.n_groups = pl.groups;
 #define OCR_E(E_)                                                                          \
     case E_:                                                                               \
         switch (fmt) {                                                                     \
-        case OCRDEC_F16: launch_fmt<OCRDEC_F16, E_>(p, pl.nt, pl.ks, pl.xt, pl.lds, s); break;     \
-        case OCRDEC_Q8_0: launch_fmt<OCRDEC_Q8_0, E_>(p, pl.nt, pl.ks, pl.xt, pl.lds, s); break;   \
-        case OCRDEC_Q4_0: launch_fmt<OCRDEC_Q4_0, E_>(p, pl.nt, pl.ks, pl.xt, pl.lds, s); break;   \
-        case OCRDEC_U8A_G32: launch_fmt<OCRDEC_U8A_G32, E_>(p, pl.nt, pl.ks, pl.xt, pl.lds, s); break; \
+        case OCRDEC_F16: launch_fmt<OCRDEC_F16, E_>(p, pl.nt, pl.ks, pl.xt, xsrc, s); break;     \
+        case OCRDEC_Q8_0: launch_fmt<OCRDEC_Q8_0, E_>(p, pl.nt, pl.ks, pl.xt, xsrc, s); break;   \
+        case OCRDEC_Q4_0: launch_fmt<OCRDEC_Q4_0, E_>(p, pl.nt, pl.ks, pl.xt, xsrc, s); break;   \
+        case OCRDEC_U8A_G32: launch_fmt<OCRDEC_U8A_G32, E_>(p, pl.nt, pl.ks, pl.xt, xsrc, s); break; \
         }                                                                                  \
         break;
     switch (epi) {
@@ -270,7 +282,8 @@ __global__ __launch_bounds__(64 * LM_WAVES, 1) void lm_argmax_kernel(GemvParams 
     int ucur = wave;
 #pragma unroll
     for (int s = 0; s < PF; ++s) load_wchunk<FMT>(tptr(ucur) + (int64_t)s * CB, lane, ring[s]);
-    stage_x(p.xs, 0, 16, p.k, xl_dyn, ldl);
+    if (p.hn) stage_norm(p.hn, p.gamma, p.eps, R, 0, p.k, xl_dyn, ldl);
+    else stage_x(p.xs, 0, 16, p.k, xl_dyn, ldl);
     __syncthreads();
     auto grab = [&]() {
         int u = 0;

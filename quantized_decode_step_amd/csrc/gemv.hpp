@@ -17,6 +17,12 @@ struct GemvParams {
     int half_tiles;   // EPI_GLU: tiles in the gate half (= d_ff / 16)
     float* part;      // EPI_ARGMAX: [grid][rows][3] (best, index bits, second)
     int n_groups;
+    // LDS-staged kernels: with hn non-NULL the activations are formed in the
+    // staging step, x = fp16(RMSNorm(hn[tok]) * gamma) from the fp32 rows hn
+    // [rows][k] (the previous block's residual), instead of read from xs.
+    const float* hn;
+    const uint16_t* gamma;
+    float eps;
 };
 
 struct GemvPlan {

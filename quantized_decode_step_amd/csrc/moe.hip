@@ -708,6 +708,8 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
     const int c1 = ks < nks ? (int)min((int64_t)(c0 + cper), nch) : c0;
     const uint8_t* tp[1] = {router + (int64_t)tile * nch * CB};
     const int ldl = xlds_stride(H);
+    if (p.tile_cnt)
+        for (int i = threadIdx.x; i < H / 16; i += blockDim.x) p.tile_cnt[i] = 0;
     int staged = 0;
     auto stage = [&]() {
         if (staged) return;
@@ -832,11 +834,56 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
                         ((uint16_t*)p.y)[slot * p.ldy + col] = f2h(silu(gv) * uv);
                     } else {
                         const int row = tidx[0] * 16 + (lane & 15);
-                        ((float*)p.y)[slot * p.ldy + row] = acc[0][xt][vv];
+                        float* yp = (float*)p.y + slot * p.ldy + row;
+                        // folded combine: written at device coherence (past this XCD's L2)
+                        if (p.tile_cnt) __hip_atomic_store(yp, acc[0][xt][vv], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        else *yp = acc[0][xt][vv];
                     }
                 }
         }
         __syncthreads();
+    }
+    if constexpr (!GLU) {
+        // folded combine (at most four rows: lane l serves row l / 16, column
+        // l % 16 of the tile): every valid item of tile g counts itself once
+        // its outputs have reached device coherence (device-scope stores,
+        // then a wait for their completion: no L2 write-back is needed); the
+        // last of the n_virt items reads the tile's outputs with device-scope
+        // loads and adds them into the residual, in the order of
+        // combine_kernel (shared outputs summed, then the routed ones by
+        // rank).  Slots, weights and the residual are fetched before the
+        // count, under the same wait.
+        if (p.tile_cnt && ks == 0 && valid) {
+            const int r = lane >> 4, K = p.top_k, S = p.n_shared, col = g * 16 + (lane & 15);
+            const int rr = r < p.rows ? r : 0;
+            int sl[8];
+            float wr[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                sl[j] = p.inv[rr * K + min(j, K - 1)];
+                wr[j] = p.cw[rr * K + min(j, K - 1)];
+            }
+            const float hv = p.h[(int64_t)rr * p.ldh + col];
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            int old = 0;
+            if (lane == 0) old = __hip_atomic_fetch_add(p.tile_cnt + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __shfl(old, 0);
+            if (old == n_virt - 1 && r < p.rows) {
+                float* y = (float*)p.y;
+                auto yld = [&](int64_t i) { return __hip_atomic_load(y + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+                float ys[8], yr[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) ys[s] = yld((int64_t)(s < S ? p.np + s * p.rows + r : 0) * p.ldy + col);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) yr[j] = yld((int64_t)sl[j] * p.ldy + col);
+                float a = 0.f;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) a += s < S ? ys[s] : 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a = fmaf(j < K ? wr[j] : 0.f, j < K ? yr[j] : 0.f, a);
+                p.h[(int64_t)r * p.ldh + col] = hv + a;
+            }
+        }
     }
 }
 
@@ -962,6 +1009,7 @@ MoeWs carve_moe(void* ws, int rows, const ocrdec_moe_weights* w) {
     m.virt = cv.take<int4>(moe_max_virt(rows, w));
     m.a = cv.take<uint16_t>((size_t)nslots * w->d_ff);
     m.y = cv.take<float>((size_t)nslots * w->hidden);
+    m.tile_cnt = cv.take<int32_t>((size_t)w->hidden / 16);
     m.bytes = cv.off;
     return m;
 }
@@ -1064,7 +1112,7 @@ void launch_expert_gemm(int fmt, bool glu, const GroupedParams& p, int n_entries
 void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_f32, int64_t ldh,
                 int add_residual, const int32_t* forced, const ocrdec_moe_capture* cap, int32_t* cap_idx,
                 float* cap_w, const MoeWs& m, const uint16_t* norm_w, float eps, uint16_t* x_out, int64_t ldxo,
-                hipStream_t s, const float* h_norm, const uint16_t* norm_in, float eps_in) {
+                hipStream_t s, const float* h_norm, const uint16_t* norm_in, float eps_in, bool fuse_combine) {
     const int E = w->n_experts, K = w->top_k, S = w->n_shared, F = w->d_ff, H = w->hidden;
     const int NP = rows * K;
     MoeParams p{};
@@ -1095,6 +1143,9 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     // the expert GEMM addresses its activations with 32-bit byte offsets
     const bool gemm = moe_gemm_path(rows, w) && (int64_t)(rows - 1) * ldx + H < (1ll << 30) &&
                       (int64_t)(NP + S * rows) * F < (1ll << 30);
+    // up to four rows: the down projection does the combine (fp32 residual)
+    const bool fused = fuse_combine && small && h_f32 && add_residual && rows <= 4;
+    if (fused) p.tile_cnt = m.tile_cnt;
     if (norm_in && !small) {
         // the MoE input is the normalised residual: form it first
         hipLaunchKernelGGL(moe_norm_kernel, dim3(rows), dim3(256), 0, s, h_norm, norm_in, H, eps_in, (uint16_t*)x,
@@ -1199,11 +1250,21 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.y = m.y;
         p.ldy = H;
         p.out_tiles = H / 16;
+        if (fused) {
+            p.tile_cnt = m.tile_cnt;
+            p.cw = m.w;
+            p.inv = m.inv;
+            p.h = (float*)h;
+            p.ldh = ldh;
+            p.rows = rows;
+            p.top_k = K;
+            p.n_shared = S;
+        }
         if (gemm) launch_expert_gemm(w->down.fmt, false, p, max_virt, s);
         else launch_grouped(w->down.fmt, false, p, rows, s);
     }
     // combine
-    {
+    if (!fused) {
         CombineParams p{};
         p.rows = rows;
         p.hidden = H;

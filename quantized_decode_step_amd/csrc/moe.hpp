@@ -36,6 +36,7 @@ struct MoeParams {
     int32_t* cap_perm;
     int lslices;     // router logits as lslices partial sums, lslice floats apart (0/1: one)
     int64_t lslice;
+    int32_t* tile_cnt;  // non-NULL: zeroed by the routing kernel (hidden / 16 counters)
 };
 
 struct GroupedParams {
@@ -60,6 +61,15 @@ struct GroupedParams {
     int dense_rows;  // expert GEMM: > 0 means one implicit expert over rows [0, dense_rows) (router)
     int kslices;     // expert GEMM: k range split over this many workgroups (0/1: none), partial
     int64_t ly_slice;  //   products of slice z written ly_slice elements after slice 0's
+    // Grouped down projection with the combine folded in (tile_cnt non-NULL):
+    // the last work item to finish output tile g adds that tile's weighted
+    // expert outputs into the fp32 residual h [rows][ldh].
+    int32_t* tile_cnt;
+    const float* cw;       // [rows * top_k] routing weights
+    const int32_t* inv;    // [rows * top_k] slot of every (row, rank)
+    float* h;
+    int64_t ldh;
+    int rows, top_k, n_shared;
 };
 
 struct CombineParams {
@@ -92,6 +102,7 @@ struct MoeWs {
     int4* virt;
     uint16_t* a;
     float* y;
+    int32_t* tile_cnt;
     size_t bytes;
 };
 
@@ -100,6 +111,7 @@ ocrdec_status check_moe(const ocrdec_moe_weights* w, int rows);
 void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_f32, int64_t ldh,
                 int add_residual, const int32_t* forced, const ocrdec_moe_capture* cap, int32_t* cap_idx,
                 float* cap_w, const MoeWs& m, const uint16_t* norm_w, float eps, uint16_t* x_out, int64_t ldxo,
-                hipStream_t s, const float* h_norm = nullptr, const uint16_t* norm_in = nullptr, float eps_in = 0.f);
+                hipStream_t s, const float* h_norm = nullptr, const uint16_t* norm_in = nullptr, float eps_in = 0.f,
+                bool fuse_combine = false);
 
 }  // namespace ocrdec

@@ -288,6 +288,12 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     ap0.n_split = attn_n_split(cache_cap);
     ap0.part = w.attn_part;
     attn_set_rope(ap0, m->rope_theta);
+    // Up to four rows: the kernels that consume a normalised residual (QKV,
+    // the dense MLP, the language head) form RMSNorm(h) in their LDS staging
+    // and the MoE down projection does the combine, so no separate norm or
+    // combine kernel runs.  (With more rows the combine's tail in the down
+    // projection costs more than the kernel it replaces.)
+    const bool prolog = R <= 4 && lds_x_bytes(H, 1) <= 65536;
     int moe_l = 0;
     for (int l = 0; l < m->n_layers; ++l) {
         const ocrdec_layer& L = m->layers[l];
@@ -303,6 +309,11 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             gp.xs = XDirect{w.x, H, R};
             gp.y = w.qkv;
             gp.ldy = 3 * HD;
+            if (prolog) {
+                gp.hn = w.h;
+                gp.gamma = L.attn_norm;
+                gp.eps = m->norm_eps;
+            }
             launch_gemv(L.wqkv.fmt, EPI_F32, pl, gp, s);
         }
         // attention
@@ -331,11 +342,11 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             float* cw = cap && cap->topk_w ? cap->topk_w + (int64_t)moe_l * R * K : nullptr;
             const int32_t* fo = forced_topk ? forced_topk + (int64_t)moe_l * R * K : nullptr;
             // the routing kernel forms x = RMSNorm(h) itself
-            launch_moe(&L.moe, R, w.x, H, w.h, 1, H, 1, fo, nullptr, ci, cw, w.moe, next_norm, m->norm_eps, w.x, H, s,
-                       w.h, L.ffn_norm, m->norm_eps);
+            launch_moe(&L.moe, R, w.x, H, w.h, 1, H, 1, fo, nullptr, ci, cw, w.moe, prolog ? nullptr : next_norm,
+                       m->norm_eps, w.x, H, s, w.h, L.ffn_norm, m->norm_eps, prolog);
             ++moe_l;
         } else {
-            hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(64), 0, s, w.h, L.ffn_norm, H, m->norm_eps, w.x);
+            if (!prolog) hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(64), 0, s, w.h, L.ffn_norm, H, m->norm_eps, w.x);
             const int F = L.dense_ff;
             {
                 GemvPlan pl = plan_gemv(L.dense_gate_up.fmt, 2 * F, H, R, EPI_GLU);
@@ -348,6 +359,11 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                 gp.y = w.a;
                 gp.ldy = F;
                 gp.half_tiles = F / 16;
+                if (prolog) {
+                    gp.hn = w.h;
+                    gp.gamma = L.ffn_norm;
+                    gp.eps = m->norm_eps;
+                }
                 launch_gemv(L.dense_gate_up.fmt, EPI_GLU, pl, gp, s);
             }
             {
@@ -362,7 +378,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                 gp.ldy = H;
                 launch_gemv(L.dense_down.fmt, EPI_RESID, pl, gp, s);
             }
-            if (next_norm)
+            if (next_norm && !prolog)
                 hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(64), 0, s, w.h, next_norm, H, m->norm_eps, w.x);
         }
     }
@@ -380,6 +396,11 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
         gp.nchunks = n_chunks(m->lm_head.fmt, H);
         gp.xs = XDirect{w.x, H, R};
         gp.part = w.lm_part;
+        if (prolog) {
+            gp.hn = w.h;
+            gp.gamma = m->final_norm;
+            gp.eps = m->norm_eps;
+        }
         launch_lm_argmax(m->lm_head.fmt, lp, gp, s);
         launch_argmax_final(w.lm_part, lp.grid, R, tok_out, cap ? cap->lm_top2 : nullptr, st->gen_index, s);
     } else {
