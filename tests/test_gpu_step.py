@@ -127,6 +127,16 @@ def test_step_small_rows_32(q):
               n_steps=3)
 
 
+# Up to four rows the MoE combine runs inside the down projection and the
+# norms inside the consuming kernels; five rows take the separate kernels.
+# Shared-expert counts 0..2 and top-k 1..8 exercise the combine's slot lists.
+@pytest.mark.parametrize("R,ns,k", [(1, 0, 8), (1, 1, 1), (3, 2, 6), (4, 2, 6), (5, 2, 6)])
+def test_step_rows_around_folded_combine(q, R, ns, k):
+    d = small_dims(n_shared=ns, top_k=k)
+    run_steps(q, d, 530 + 16 * R + 4 * ns + k, prefix_len=[(11 * i + 5) % 41 for i in range(R)],
+              gen_index=[(5 * i + 2) % 9 for i in range(R)], n_steps=4)
+
+
 # quantised embedding tables and LM heads through the whole step (tokens from
 # the table, argmax over the quantised head)
 @pytest.mark.parametrize("fe,fl", [(synth.Q4_0, synth.Q4_0), (synth.Q8_0, synth.Q8_0), (synth.U8A_G32, synth.F16),
