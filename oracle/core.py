@@ -515,6 +515,97 @@ def decode_step(model, state, tok_in=None, hidden_in=None, forced_topk=None,
     return res
 
 
+class PrefillResult:
+    def __init__(self):
+        self.tok = None          # int32: argmax at the last position (or None without LM head)
+        self.lm_top2 = None      # float64 [2]: best and second logit there (float32 values)
+        self.hidden = None       # float64 [P][H]: residual after the last layer
+        self.k = []              # per layer: float64 [NH][P][D] (fp16 values), cache indices 0..P-1
+        self.v = []
+        self.topk_idx = []       # per MoE layer: int32 [P][k]
+        self.topk_w = []         # per MoE layer: float64 [P][k]
+        self.router_gap = []     # per MoE layer: float64 [P]
+
+
+def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Causal self-attention of one head over P positions: query i attends
+    keys 0..i.  S = scale * Q K^T with the entries above the diagonal masked
+    out, softmax per row, O = softmax(S) V.
+
+    [NCNN] 3.2: prefill and incremental decoding use causal masks of
+    different shapes; the prompt pass sees every earlier position of the
+    prompt and itself.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    P = q.shape[0]
+    s = (q @ k.T) * scale
+    s[np.triu_indices(P, 1)] = -np.inf
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return (e @ v) / e.sum(axis=1, keepdims=True)
+
+
+def prefill(model, P: int, tok=None, emb=None, forced_topk=None, with_lm: bool = True) -> PrefillResult:
+    """The prompt pass of one row: P positions through every layer at once.
+
+    [UOCR] (the model needs a prefill before token-by-token generation;
+    "Il decoder e il Mixture of Experts" for the layer stack) and [NCNN] 3.2
+    (prefill with a causal mask, then one new token per decode call reusing
+    the cache of every layer).  Per layer: x = fp16(RMSNorm(h)); q, k, v from
+    the QKV projection, RoPE at the linear positions 0..P-1 ([NCNN] 3.3: the
+    current linear position), k and v are what the cache keeps at indices
+    0..P-1; causal attention; the O projection added to the residual; then
+    the dense SwiGLU or the MoE on fp16(RMSNorm(h)) added to the residual.
+    The pass ends with the language-head argmax at the last position, the
+    first generated token.  Readings: the input is either token ids (the
+    embedding table) or the P rows of fp16 input features (``emb``, e.g. the
+    image features spliced into the prompt); storage points as in decode.
+
+    ``forced_topk`` [n_moe][P][k] (rows < 0: not forced) replaces the routing.
+    """
+    dims = model.dims
+    NH, D, eps, theta = dims.n_heads, dims.head_dim, dims.norm_eps, dims.rope_theta
+    res = PrefillResult()
+    if tok is not None:
+        h = embed_rows(model, np.asarray(tok)[:P])
+    else:
+        h = np.asarray(emb, np.float64)[:P].copy()
+    pos = np.arange(P, dtype=np.float64)[:, None]
+    moe_l = 0
+    for lay in model.layers:
+        x = f16(rmsnorm(h, lay.attn_norm, eps))
+        qkv = gemv_qmat(lay.wqkv, x)
+        q = f16(rope(qkv[:, :NH * D].reshape(P, NH, D), pos, theta))
+        k = f16(rope(qkv[:, NH * D:2 * NH * D].reshape(P, NH, D), pos, theta))
+        v = f16(qkv[:, 2 * NH * D:].reshape(P, NH, D))
+        o = np.zeros((P, NH, D))
+        for hh in range(NH):
+            o[:, hh] = causal_attention(q[:, hh], k[:, hh], v[:, hh], 1.0 / np.sqrt(D))
+        h = h + gemv_qmat(lay.wo, f16(o.reshape(P, NH * D)))
+        res.k.append(k.transpose(1, 0, 2).copy())
+        res.v.append(v.transpose(1, 0, 2).copy())
+        x = f16(rmsnorm(h, lay.ffn_norm, eps))
+        if lay.is_moe:
+            forced = None if forced_topk is None else np.asarray(forced_topk[moe_l])[:P]
+            out, idx, w, logits = moe(lay, x, dims.top_k, forced)
+            h = h + out
+            res.topk_idx.append(idx)
+            res.topk_w.append(w)
+            res.router_gap.append(np.array([topk_gap(lg, dims.top_k) for lg in logits]))
+            moe_l += 1
+        else:
+            h = h + swiglu(lay.dense_gate_up, lay.dense_down, x)
+    res.hidden = h
+    if with_lm and model.lm_head is not None:
+        x = f16(rmsnorm(h[P - 1:P], model.final_norm, eps))
+        z = f32(gemv_qmat(model.lm_head, x))[0]
+        res.tok = np.int32(argmax_lowest(z))
+        res.lm_top2 = np.sort(z)[::-1][:2]
+    return res
+
+
 def embed_rows(model, tok) -> np.ndarray:
     """Embedding lookup: row ``tok[i]`` of the table, as float64.
 

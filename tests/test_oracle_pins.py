@@ -585,3 +585,74 @@ def test_step_sequence_wraps_ring():
         assert np.array_equal(st.k_cache[0, 0, :, slot].astype(np.float64), res.new_k[0][0])
         tok = res.tok
     assert st.gen_index[0] == 2 + 2 * d.ring_cap + 1
+
+
+# --- prefill (the prompt pass) ---------------------------------------------
+
+def _prefill_dims():
+    import synth
+    return synth.Dims(hidden=64, n_heads=2, head_dim=64, n_layers=3, n_dense=1, dense_ff=128, n_experts=8,
+                      top_k=3, n_shared=1, expert_ff=64, vocab=300, prefix_cap=4, ring_cap=24)
+
+
+@pytest.mark.parametrize("use_emb", [False, True])
+def test_prefill_equals_token_by_token_decode(use_emb):
+    """The prompt pass over P positions equals P decode steps of one row with
+    an empty prefix and a ring large enough to hold them all: step t writes
+    ring slot t at position t and attends slots 0..t, which is the causal
+    window of position t.  The two forms share no attention or batching
+    code (matrix form with a mask against one query at a time)."""
+    import synth
+    d = _prefill_dims()
+    P = 19
+    m = synth.make_model(d, 31)
+    tok = synth.uniform_i32(synth.stream_id(31, "prompt"), (P,), 0, d.vocab)
+    emb = synth.normal_f16(synth.stream_id(31, "emb"), (P, d.hidden)).astype(np.float64) if use_emb else None
+    pre = O.prefill(m, P, tok=None if use_emb else tok, emb=emb)
+    st = synth.make_state(d, 31, [0], [0])
+    steps = []
+    for t in range(P):
+        if use_emb:
+            steps.append(O.decode_step(m, st, hidden_in=emb[t:t + 1]))
+        else:
+            steps.append(O.decode_step(m, st, tok_in=tok[t:t + 1]))
+    for l in range(d.n_layers):
+        ring_k = st.k_cache[l, 0][:, d.prefix_cap:d.prefix_cap + P].astype(np.float64)
+        ring_v = st.v_cache[l, 0][:, d.prefix_cap:d.prefix_cap + P].astype(np.float64)
+        assert np.array_equal(ring_k, pre.k[l])
+        assert np.array_equal(ring_v, pre.v[l])
+    for ml in range(len(pre.topk_idx)):
+        for t in range(P):
+            assert np.array_equal(steps[t].topk_idx[ml][0], pre.topk_idx[ml][t])
+            assert np.allclose(steps[t].topk_w[ml][0], pre.topk_w[ml][t], rtol=1e-12, atol=0)
+    hid = np.array([s.hidden[0] for s in steps])
+    assert np.allclose(hid, pre.hidden, rtol=1e-11, atol=1e-12)
+    assert steps[-1].tok[0] == pre.tok
+
+
+def test_prefill_is_causal():
+    """Changing the last prompt token changes nothing at earlier positions."""
+    import synth
+    d = _prefill_dims()
+    P = 12
+    m = synth.make_model(d, 32)
+    tok = synth.uniform_i32(synth.stream_id(32, "prompt"), (P,), 0, d.vocab)
+    tok2 = tok.copy()
+    tok2[-1] = (tok[-1] + 1) % d.vocab
+    a = O.prefill(m, P, tok=tok)
+    b = O.prefill(m, P, tok=tok2)
+    for l in range(d.n_layers):
+        assert np.allclose(a.k[l][:, :P - 1], b.k[l][:, :P - 1], rtol=0, atol=0)
+        assert not np.array_equal(a.k[l][:, P - 1], b.k[l][:, P - 1])
+    assert np.allclose(a.hidden[:P - 1], b.hidden[:P - 1], rtol=1e-12, atol=1e-13)
+
+
+def test_causal_attention_cases():
+    """One position: the output is its value.  Position i of the masked
+    matrix form equals single-query attention over keys 0..i."""
+    rng = np.random.default_rng(5)
+    q, k, v = rng.standard_normal((3, 9, 16))
+    o = O.causal_attention(q, k, v, 0.25)
+    assert np.array_equal(O.causal_attention(q[:1], k[:1], v[:1], 0.25)[0], v[0])
+    for i in range(9):
+        assert np.allclose(o[i], O.attention(q[i], k[:i + 1], v[:i + 1], 0.25), rtol=1e-13, atol=1e-14)
