@@ -325,6 +325,44 @@ ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_state* st, 
                                  const ocrdec_step_capture* capture, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* ocrdec_prefill: the prompt pass of one row                                */
+/* ------------------------------------------------------------------------ */
+
+/* The prompt pass before token-by-token decoding (HunyuanOCR ncnn page,
+ * section 3.2: prefill and incremental decoding use causal masks of
+ * different shapes, and decoding reuses every layer's cache; Unlimited-OCR
+ * page: the model runs a prefill, then generates token by token).  P prompt
+ * positions of row `row` go through every layer at once: h = embed[tok[i]]
+ * (or embed_q's row dequantised), or h = emb[i] when tok is NULL; per layer
+ * x = fp16(RMSNorm(h) * attn_norm), q/k/v = Wqkv x, RoPE at the linear
+ * positions i = 0..P-1, k and v written to cache indices 0..P-1 of the row
+ * (fp16), causal attention (query i attends keys 0..i, scale
+ * 1/sqrt(head_dim)), h += Wo o, then h += MLP(fp16(RMSNorm(h) * ffn_norm))
+ * (dense SwiGLU, or the MoE of ocrdec_moe_layer over the P positions).  If
+ * the model has an LM head and tok_out is non-NULL, tok_out[0] = the argmax
+ * at position P-1 (the first generated token), as in ocrdec_decode_step.
+ * The call does not change prefix_len or gen_index: to decode after it, the
+ * caller sets prefix_len[row] = P and gen_index[row] = 0; the first decode
+ * step then places its token at RoPE position P.
+ *   st           the decode state the caches belong to (rows, prefix_cap,
+ *                ring_cap); only row `row` of every layer's cache is written
+ *   P            1 .. prefix_cap
+ *   tok          int32 [P] token ids, or NULL
+ *   emb          fp16 [P][hidden] input features (used when tok is NULL)
+ *   forced_topk  int32 [n_moe_layers][P][top_k] or NULL (see ocrdec_moe_layer)
+ *   hidden       fp32 [P][hidden] or NULL: the residual after the last layer
+ *   capture      topk_idx / topk_w [n_moe_layers][P][top_k], lm_top2 [1][2]
+ *                (any pointer may be NULL)
+ * Workspace: ocrdec_prefill_workspace_bytes(m, st, P) bytes.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE. */
+ocrdec_status ocrdec_prefill_workspace_bytes(const ocrdec_model* m, const ocrdec_state* st, int32_t P,
+                                             size_t* bytes);
+ocrdec_status ocrdec_prefill(const ocrdec_model* m, const ocrdec_state* st, int32_t row, int32_t P,
+                             const int32_t* tok, const uint16_t* emb, const int32_t* forced_topk,
+                             int32_t* tok_out, float* hidden, const ocrdec_step_capture* capture, void* ws,
+                             size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

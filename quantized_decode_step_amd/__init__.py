@@ -106,16 +106,20 @@ _lib.ocrdec_moe_workspace_bytes.argtypes = [_P(MoeWeights), _i32, _P(_sz)]
 _lib.ocrdec_moe_layer.argtypes = [_P(MoeWeights), _i32, _vp, _vp, _i32, _vp, _P(MoeCapture), _vp, _sz, _vp]
 _lib.ocrdec_step_workspace_bytes.argtypes = [_P(ModelDesc), _P(StateDesc), _P(_sz)]
 _lib.ocrdec_decode_step.argtypes = [_P(ModelDesc), _P(StateDesc), _vp, _vp, _vp, _vp, _P(StepCapture), _vp, _sz, _vp]
+_lib.ocrdec_prefill_workspace_bytes.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _P(_sz)]
+_lib.ocrdec_prefill.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _P(StepCapture),
+                                _vp, _sz, _vp]
 for _fn in ("ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack", "ocrdec_gemv_q", "ocrdec_lm_argmax_workspace_bytes",
             "ocrdec_lm_argmax", "ocrdec_attn_workspace_bytes",
             "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes", "ocrdec_moe_layer", "ocrdec_step_workspace_bytes",
-            "ocrdec_decode_step"):
+            "ocrdec_decode_step", "ocrdec_prefill_workspace_bytes", "ocrdec_prefill"):
     getattr(_lib, _fn).restype = ctypes.c_int
 
 EXPORTED = ["ocrdec_last_error", "ocrdec_version", "ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack",
             "ocrdec_gemv_q", "ocrdec_lm_argmax_workspace_bytes", "ocrdec_lm_argmax", "ocrdec_attn_workspace_bytes",
             "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes",
-            "ocrdec_moe_layer", "ocrdec_step_workspace_bytes", "ocrdec_decode_step"]
+            "ocrdec_moe_layer", "ocrdec_step_workspace_bytes", "ocrdec_decode_step",
+            "ocrdec_prefill_workspace_bytes", "ocrdec_prefill"]
 
 
 def _ptr(t) -> int | None:
@@ -217,6 +221,19 @@ def ocrdec_decode_step(m: ModelDesc, st: StateDesc, tok_in=None, hidden=None, to
     _check(_lib.ocrdec_decode_step(ctypes.byref(m), ctypes.byref(st), _ptr(tok_in), _ptr(hidden), _ptr(tok_out),
                                    _ptr(forced_topk), ctypes.byref(capture) if capture is not None else None,
                                    _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def ocrdec_prefill_workspace_bytes(m: ModelDesc, st: StateDesc, P: int) -> int:
+    b = _sz()
+    _check(_lib.ocrdec_prefill_workspace_bytes(ctypes.byref(m), ctypes.byref(st), P, ctypes.byref(b)))
+    return b.value
+
+
+def ocrdec_prefill(m: ModelDesc, st: StateDesc, row: int, P: int, tok=None, emb=None, forced_topk=None, tok_out=None,
+                   hidden=None, capture: StepCapture | None = None, ws=None, ws_bytes: int = 0, stream=None):
+    _check(_lib.ocrdec_prefill(ctypes.byref(m), ctypes.byref(st), row, P, _ptr(tok), _ptr(emb), _ptr(forced_topk),
+                               _ptr(tok_out), _ptr(hidden), ctypes.byref(capture) if capture is not None else None,
+                               _ptr(ws), ws_bytes, _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

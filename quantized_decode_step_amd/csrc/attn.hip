@@ -289,6 +289,206 @@ void attn_set_rope(AttnParams& p, float theta) {
         p.inv_freq[i] = i < p.head_dim / 2 ? std::pow((double)theta, -2.0 * i / p.head_dim) : 0.0;
 }
 
+// ---------------------------------------------------------------------------
+// Prompt pass (prefill): causal attention of P positions of one row
+// ("HunyuanOCR 的 ncnn 移植" 3.2: prefill and incremental decoding use causal
+// masks of different shapes, and the decode steps reuse every layer's cache).
+//
+// prefill_rope_kernel: RoPE of q and k at the linear positions 0..P-1 (the
+// same rotation as the decode kernel), q kept in a scratch buffer, k and v
+// written to cache indices 0..P-1.
+//
+// attn_prefill_kernel: flash-style.  A workgroup of four wavefronts owns 64
+// queries of one head (16 per wavefront) and walks the key blocks of 64 up to
+// its last query, online softmax.  Both products run on MFMA in transposed
+// form: S^T = K Q^T (keys on the MFMA rows, the wavefront's queries on its
+// columns) and O^T = V^T P^T, so that every value a lane holds belongs to
+// one query and the softmax rescaling is a per-lane factor.  P^T is the
+// score accumulators converted in place to two fp16 terms each (hi + lo,
+// so the weights keep about 22 bits): the 32 keys of one
+// contraction step are taken in the order the two 16-key score tiles hold
+// them (lane group g: keys 4g..4g+3 of each tile), and V^T is read from LDS
+// in that same key order.  K stays key-major in LDS; V is stored transposed
+// while it is staged.  The next key block is loaded into registers while the
+// current one is used.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(64) void prefill_rope_kernel(PrefillAttnParams p) {
+    const int pos = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
+    if (i >= D / 2) return;
+    const int HD = p.n_heads * D;
+    const float* r = p.qkv + (int64_t)pos * p.ld_qkv;
+    float y1, y2;
+    rope_pair(r[h * D + i], r[h * D + i + D / 2], p.inv_freq[i], pos, y1, y2);
+    uint16_t* qo = p.q + (int64_t)pos * HD + h * D;
+    qo[i] = f2h(y1);
+    qo[i + D / 2] = f2h(y2);
+    rope_pair(r[HD + h * D + i], r[HD + h * D + i + D / 2], p.inv_freq[i], pos, y1, y2);
+    uint16_t* kc = p.k_cache + ((int64_t)h * p.cache_cap + pos) * D;
+    kc[i] = f2h(y1);
+    kc[i + D / 2] = f2h(y2);
+    uint16_t* vc = p.v_cache + ((int64_t)h * p.cache_cap + pos) * D;
+    vc[i] = f2h(r[2 * HD + h * D + i]);
+    vc[i + D / 2] = f2h(r[2 * HD + h * D + i + D / 2]);
+}
+
+constexpr int PQB = 64;  // queries per workgroup (16 per wavefront)
+constexpr int PKB = 64;  // keys per block
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) {
+    constexpr int KS = D / 32;                 // contraction steps of the score product
+    constexpr int DT = D / 16;                 // 16-wide output tiles
+    constexpr int KLD = D + 8;                 // K block row stride (halves)
+    constexpr int VLD = PKB + 8;               // transposed V block row stride (halves)
+    constexpr int NPC = PKB * D / 8 / 256;     // 16-byte pieces per thread per block, K and V each
+    __shared__ __align__(16) uint16_t k_s[PKB * KLD];
+    __shared__ __align__(16) uint16_t vt_s[D * VLD];
+    // the longest query blocks start first
+    const int qb = (int)gridDim.x - 1 - (int)blockIdx.x, h = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+    const int P = p.P, HD = p.n_heads * D;
+    const int q0 = qb * PQB;
+    const int qw = q0 + 16 * wave + c16;  // this lane's query (an MFMA column)
+    const int nkb = (min(q0 + PQB, P) - 1) / PKB + 1;
+    const uint16_t* kbase = p.k_cache + (int64_t)h * p.cache_cap * D;
+    const uint16_t* vbase = p.v_cache + (int64_t)h * p.cache_cap * D;
+
+    // queries (B operand of S^T = K Q^T): step ks holds d = 32 ks + 8 g .. + 7
+    half8v qf[KS];
+    {
+        const uint16_t* qp = p.q + (int64_t)min(qw, P - 1) * HD + h * D + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = bits_to_half8(*(const uint4*)(qp + 32 * ks));
+    }
+    // staging: thread t carries key row t % 64, column pieces t / 64 + 4 i;
+    // keys past the prompt are zero (their scores are masked, and a zero
+    // value keeps the masked products finite)
+    uint4 kr[NPC], vr[NPC];
+    auto load_blk = [&](int kb) {
+        const int key = kb * PKB + (tid & 63);
+#pragma unroll
+        for (int i = 0; i < NPC; ++i) {
+            const int c = (tid >> 6) + 4 * i;
+            kr[i] = vr[i] = make_uint4(0, 0, 0, 0);
+            if (key < P) {
+                kr[i] = *(const uint4*)(kbase + (int64_t)key * D + 8 * c);
+                vr[i] = *(const uint4*)(vbase + (int64_t)key * D + 8 * c);
+            }
+        }
+    };
+    auto store_blk = [&]() {
+        const int r = tid & 63;
+#pragma unroll
+        for (int i = 0; i < NPC; ++i) {
+            const int c = (tid >> 6) + 4 * i;
+            *(uint4*)(k_s + r * KLD + 8 * c) = kr[i];
+            const uint32_t w4[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                vt_s[(8 * c + 2 * j) * VLD + r] = (uint16_t)(w4[j] & 0xFFFF);
+                vt_s[(8 * c + 2 * j + 1) * VLD + r] = (uint16_t)(w4[j] >> 16);
+            }
+        }
+    };
+
+    float4v o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = float4v{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    load_blk(0);
+    for (int kb = 0; kb < nkb; ++kb) {
+        __syncthreads();  // the previous block's LDS reads are done
+        store_blk();
+        __syncthreads();
+        if (kb + 1 < nkb) load_blk(kb + 1);
+        // scores of the 64 keys (4 tiles of 16) for this lane's query
+        float s[4][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const half8v ka = bits_to_half8(*(const uint4*)(k_s + (kt * 16 + c16) * KLD + 32 * ks + 8 * g));
+                acc = mfma16(ka, qf[ks], acc);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int key = kb * PKB + kt * 16 + 4 * g + v;
+                s[kt][v] = key <= qw ? acc[v] * p.scale : -INFINITY;
+            }
+        }
+        // online softmax: the block maximum over the 16 values and the four
+        // lane groups that share the query
+        float mb = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mb = fmaxf(mb, s[kt][v]);
+        mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+        const float m_new = fmaxf(m_run, mb);  // finite: key 0 is in every query's window
+        const float alpha = __expf(m_run - m_new);
+        // probabilities as two fp16 terms, hi + lo (hi = fp16(e), lo = fp16(e - hi)):
+        // their products with V are exact, so the weights keep ~22 bits
+        float ls = 0.f;
+        half8v pb[2], pl[2];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float e = __expf(s[kt][v] - m_new);
+                ls += e;
+                const f16_t hi = (f16_t)e;
+                pb[kt >> 1][(kt & 1) * 4 + v] = hi;
+                pl[kt >> 1][(kt & 1) * 4 + v] = (f16_t)(e - (float)hi);
+            }
+        ls += __shfl_xor(ls, 16, 64);
+        ls += __shfl_xor(ls, 32, 64);
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            o[dt] *= alpha;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const uint16_t* vp = vt_s + (dt * 16 + c16) * VLD + 32 * kk + 4 * g;
+                const uint2 lo = *(const uint2*)vp, hi = *(const uint2*)(vp + 16);
+                const half8v va = bits_to_half8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                o[dt] = mfma16(va, pb[kk], o[dt]);
+                o[dt] = mfma16(va, pl[kk], o[dt]);
+            }
+        }
+    }
+    if (qw < P) {
+        const float inv = 1.0f / l_run;
+        uint16_t* op = p.out + (int64_t)qw * p.ld_out + h * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const uint32_t lo = (uint32_t)f2h(o[dt][0] * inv) | ((uint32_t)f2h(o[dt][1] * inv) << 16);
+            const uint32_t hi = (uint32_t)f2h(o[dt][2] * inv) | ((uint32_t)f2h(o[dt][3] * inv) << 16);
+            *(uint2*)(op + dt * 16 + 4 * g) = make_uint2(lo, hi);
+        }
+    }
+}
+
+void prefill_set_rope(PrefillAttnParams& p, float theta) {
+    for (int i = 0; i < 64; ++i)
+        p.inv_freq[i] = i < p.head_dim / 2 ? std::pow((double)theta, -2.0 * i / p.head_dim) : 0.0;
+}
+
+void launch_attn_prefill(const PrefillAttnParams& p, hipStream_t s) {
+    const dim3 gr(p.P, p.n_heads), ga((p.P + PQB - 1) / PQB, p.n_heads);
+    if (p.head_dim == 128) {
+        hipLaunchKernelGGL(prefill_rope_kernel<128>, gr, dim3(64), 0, s, p);
+        hipLaunchKernelGGL(attn_prefill_kernel<128>, ga, dim3(256), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(prefill_rope_kernel<64>, gr, dim3(64), 0, s, p);
+        hipLaunchKernelGGL(attn_prefill_kernel<64>, ga, dim3(256), 0, s, p);
+    }
+}
+
 void launch_attn(const AttnParams& p, hipStream_t s) {
     dim3 g1(p.n_split, p.n_heads, p.rows);
     dim3 g2(p.n_heads, p.rows);

@@ -23,6 +23,24 @@ struct AttnParams {
     float* part;    // [rows][n_heads][n_split][head_dim + 2]
 };
 
+// Prompt pass (prefill) of one row: P positions, causal attention.
+struct PrefillAttnParams {
+    int P, n_heads, head_dim;
+    const float* qkv;    // [P][ld_qkv] fp32 projections (q | k | v)
+    int64_t ld_qkv;
+    uint16_t* q;         // [P][n_heads * head_dim] fp16 scratch: the rotated queries
+    uint16_t* k_cache;   // this row's caches [n_heads][cache_cap][head_dim]; indices 0..P-1 are written
+    uint16_t* v_cache;
+    int cache_cap;
+    float scale;
+    double inv_freq[64];
+    uint16_t* out;       // [P][ld_out] fp16 attention output
+    int64_t ld_out;
+};
+
+void prefill_set_rope(PrefillAttnParams& p, float theta);
+void launch_attn_prefill(const PrefillAttnParams& p, hipStream_t s);
+
 int attn_n_split(int cache_cap);
 size_t attn_part_bytes(int rows, int n_heads, int head_dim, int cache_cap);
 size_t attn_ws_bytes(int rows, int n_heads, int head_dim, int cache_cap);

@@ -1109,6 +1109,26 @@ void launch_expert_gemm(int fmt, bool glu, const GroupedParams& p, int n_entries
 
 }  // namespace
 
+bool dense_gemm_ok(int fmt, int n, int k, int rows, int64_t ldx) {
+    return eg_format(fmt) && k % EG_KS == 0 && n % 16 == 0 && rows >= 1 && (int64_t)(rows - 1) * ldx + k < (1ll << 30);
+}
+
+void launch_dense_gemm(int fmt, bool glu, const uint8_t* w, int n, int k, int rows, const uint16_t* x, int64_t ldx,
+                       void* y, int64_t ldy, hipStream_t s) {
+    GroupedParams p{};
+    p.w_routed = w;
+    p.n_experts = 1;
+    p.k = k;
+    p.nchunks = n_chunks(fmt, k);
+    p.out_tiles = n / 16;
+    p.dense_rows = rows;
+    p.x = x;
+    p.ldx = ldx;
+    p.y = y;
+    p.ldy = ldy;
+    launch_expert_gemm(fmt, glu, p, (rows + EG_TM - 1) / EG_TM, s);
+}
+
 void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_f32, int64_t ldh,
                 int add_residual, const int32_t* forced, const ocrdec_moe_capture* cap, int32_t* cap_idx,
                 float* cap_w, const MoeWs& m, const uint16_t* norm_w, float eps, uint16_t* x_out, int64_t ldxo,

@@ -106,6 +106,14 @@ struct MoeWs {
     size_t bytes;
 };
 
+// Dense GEMM over many rows on the expert GEMM (one implicit expert):
+// y[rows][n] = x[rows][k] W^T as fp32, or with glu, W = [gate; up] of n rows
+// each and y[rows][n] = fp16(silu(x G^T) * (x U^T)).  dense_gemm_ok says
+// whether the format and shape have that kernel (else use the GEMV).
+bool dense_gemm_ok(int fmt, int n, int k, int rows, int64_t ldx);
+void launch_dense_gemm(int fmt, bool glu, const uint8_t* w, int n, int k, int rows, const uint16_t* x, int64_t ldx,
+                       void* y, int64_t ldy, hipStream_t s);
+
 MoeWs carve_moe(void* ws, int rows, const ocrdec_moe_weights* w);
 ocrdec_status check_moe(const ocrdec_moe_weights* w, int rows);
 void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_f32, int64_t ldh,

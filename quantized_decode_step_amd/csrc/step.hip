@@ -18,14 +18,15 @@ constexpr int kMaxRows = 32;
 // One wavefront per row.
 __global__ __launch_bounds__(64) void embed_norm_kernel(const int32_t* tok, const uint16_t* embed, int vocab,
                                                         const float* src, float* h, const uint16_t* gamma, int H,
-                                                        float eps, uint16_t* x) {
+                                                        float eps, uint16_t* x, const uint16_t* rows16) {
     const int r = blockIdx.x, lane = threadIdx.x;
     float* hr = h + (int64_t)r * H;
     const int n4 = H / 4;
-    if (tok) {
-        int t = tok[r];
+    if (tok || rows16) {
+        // a row of the fp16 table, or row r of fp16 input features
+        int t = tok ? tok[r] : 0;
         t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
-        const uint2* from = (const uint2*)(embed + (int64_t)t * H);
+        const uint2* from = (const uint2*)(tok ? embed + (int64_t)t * H : rows16 + (int64_t)r * H);
         uint2 e[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -101,6 +102,29 @@ __global__ __launch_bounds__(64) void embed_q_norm_kernel(const int32_t* tok, co
     wave_rmsnorm_row(hr, gamma, H, eps, x + (int64_t)r * H);
 }
 
+// h[r] += y[r]; x[r] = fp16(RMSNorm(h[r]) * gamma): one wavefront per row.
+__global__ __launch_bounds__(64) void resid_norm_kernel(float* h, const float* y, const uint16_t* gamma, int H,
+                                                        float eps, uint16_t* x) {
+    const int r = blockIdx.x, lane = threadIdx.x;
+    float4* hr = (float4*)(h + (int64_t)r * H);
+    const float4* yr = (const float4*)(y + (int64_t)r * H);
+    const int n4 = H / 4;
+    float4 a[16], b[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int c4 = lane + 64 * i;
+        a[i] = c4 < n4 ? hr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        b[i] = c4 < n4 ? yr[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int c4 = lane + 64 * i;
+        if (c4 < n4) hr[c4] = make_float4(a[i].x + b[i].x, a[i].y + b[i].y, a[i].z + b[i].z, a[i].w + b[i].w);
+    }
+    __threadfence_block();
+    wave_rmsnorm_row(h + (int64_t)r * H, gamma, H, eps, x + (int64_t)r * H);
+}
+
 // x[r] = fp16(RMSNorm(h[r]) * gamma): one wavefront per row.
 __global__ __launch_bounds__(64) void norm_kernel(const float* h, const uint16_t* gamma, int H, float eps,
                                                   uint16_t* x) {
@@ -163,8 +187,74 @@ StepWs carve_step(void* ws, const ocrdec_model* m, int rows, int cache_cap) {
     return w;
 }
 
-ocrdec_status check_step(const ocrdec_model* m, const ocrdec_state* st) {
+struct PrefillWs {
+    float* h;
+    uint16_t* x;
+    float* qkv;
+    uint16_t* q;
+    uint16_t* o;
+    float* y;
+    uint16_t* a;
+    float* lm_part;
+    MoeWs moe;
+    size_t bytes;
+};
+
+PrefillWs carve_prefill(void* ws, const ocrdec_model* m, int P) {
+    Carve cv(ws);
+    PrefillWs w;
+    const int H = m->hidden, HD = m->n_heads * m->head_dim;
+    int dense_ff = 0;
+    const ocrdec_moe_weights* moe = nullptr;
+    for (int l = 0; l < m->n_layers; ++l) {
+        if (m->layers[l].is_moe) moe = &m->layers[l].moe;
+        else dense_ff = std::max(dense_ff, m->layers[l].dense_ff);
+    }
+    w.h = cv.take<float>((size_t)P * H);
+    w.x = cv.take<uint16_t>((size_t)P * H);
+    w.qkv = cv.take<float>((size_t)P * 3 * HD);
+    w.q = cv.take<uint16_t>((size_t)P * HD);
+    w.o = cv.take<uint16_t>((size_t)P * HD);
+    w.y = cv.take<float>((size_t)P * H);
+    w.a = cv.take<uint16_t>((size_t)P * std::max(dense_ff, 1));
+    w.lm_part = cv.take<float>(argmax_ws_bytes(std::max(lm_grid(m, 1), 1), 1) / sizeof(float));
+    if (moe) {
+        MoeWs probe = carve_moe(nullptr, P, moe);
+        char* base = (char*)cv.take<char>(probe.bytes);
+        w.moe = carve_moe(ws ? base : nullptr, P, moe);
+    } else {
+        w.moe = MoeWs{};
+    }
+    w.bytes = cv.off;
+    return w;
+}
+
+// y[rows][...] = x W^T: the expert GEMM where it has the format and shape,
+// else the GEMV kernel in 16/32-token passes
+void prefill_gemm(const ocrdec_qmat& W, bool glu, int rows, const uint16_t* x, int64_t ldx, void* y, int64_t ldy,
+                  hipStream_t s) {
+    const int n_out = glu ? W.n / 2 : W.n;
+    if (dense_gemm_ok(W.fmt, n_out, W.k, rows, ldx)) {
+        launch_dense_gemm(W.fmt, glu, (const uint8_t*)W.data, n_out, W.k, rows, x, ldx, y, ldy, s);
+        return;
+    }
+    const int epi = glu ? EPI_GLU : EPI_F32;
+    GemvPlan pl = plan_gemv(W.fmt, W.n, W.k, rows, epi);
+    GemvParams gp{};
+    gp.w = (const uint8_t*)W.data;
+    gp.n = W.n;
+    gp.k = W.k;
+    gp.nchunks = n_chunks(W.fmt, W.k);
+    gp.xs = XDirect{x, ldx, rows};
+    gp.y = y;
+    gp.ldy = ldy;
+    if (glu) gp.half_tiles = n_out / 16;
+    launch_gemv(W.fmt, epi, pl, gp, s);
+}
+
+ocrdec_status check_step(const ocrdec_model* m, const ocrdec_state* st, int moe_rows = -1) {
     OCR_CHECK_ARG(m && st, "model and state must be non-NULL");
+    if (moe_rows < 0) moe_rows = st->rows;
     OCR_CHECK_ARG(st->rows >= 1 && st->rows <= kMaxRows, "rows must be in [1, 32]");
     OCR_CHECK_ARG(st->ring_cap >= 1 && st->prefix_cap >= 0, "ring_cap must be >= 1 and prefix_cap >= 0");
     OCR_CHECK_ARG(st->prefix_len && st->gen_index, "state arrays must be non-NULL");
@@ -187,7 +277,7 @@ ocrdec_status check_step(const ocrdec_model* m, const ocrdec_state* st) {
         OCR_CHECK_ARG(L.wqkv.n == 3 * HD && L.wqkv.k == H, tag + "wqkv must be [3*n_heads*head_dim][hidden]");
         OCR_CHECK_ARG(L.wo.n == H && L.wo.k == HD, tag + "wo must be [hidden][n_heads*head_dim]");
         if (L.is_moe) {
-            if ((s = check_moe(&L.moe, st->rows)) != OCRDEC_OK) return s;
+            if ((s = check_moe(&L.moe, moe_rows)) != OCRDEC_OK) return s;
             OCR_CHECK_ARG(L.moe.hidden == H, tag + "moe.hidden must equal hidden");
             if (moe0) {
                 OCR_CHECK_ARG(L.moe.n_experts == moe0->n_experts && L.moe.top_k == moe0->top_k &&
@@ -267,7 +357,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
 #undef OCR_EQ
     } else {
         hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(64), 0, s, tok_in, m->embed, m->vocab, hidden, w.h,
-                           m->layers[0].attn_norm, H, m->norm_eps, w.x);
+                           m->layers[0].attn_norm, H, m->norm_eps, w.x, (const uint16_t*)nullptr);
     }
     // attention arguments shared by every layer (RoPE frequencies once per call)
     AttnParams ap0{};
@@ -407,4 +497,115 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
         hipLaunchKernelGGL(bump_kernel, dim3(1), dim3(64), 0, s, st->gen_index, R);
     }
     return launch_status("ocrdec_decode_step");
+}
+
+extern "C" ocrdec_status ocrdec_prefill_workspace_bytes(const ocrdec_model* m, const ocrdec_state* st, int32_t P,
+                                                        size_t* bytes) {
+    OCR_CHECK_ARG(P >= 1 && P <= 65536, "P must be in [1, 65536]");
+    ocrdec_status s0 = check_step(m, st, P);
+    if (s0 != OCRDEC_OK) return s0;
+    OCR_CHECK_ARG(bytes, "bytes is NULL");
+    *bytes = carve_prefill(nullptr, m, P).bytes;
+    return OCRDEC_OK;
+}
+
+extern "C" ocrdec_status ocrdec_prefill(const ocrdec_model* m, const ocrdec_state* st, int32_t row, int32_t P,
+                                        const int32_t* tok, const uint16_t* emb, const int32_t* forced_topk,
+                                        int32_t* tok_out, float* hidden, const ocrdec_step_capture* cap, void* ws,
+                                        size_t ws_bytes, void* stream) {
+    OCR_CHECK_ARG(P >= 1 && P <= 65536, "P must be in [1, 65536]");
+    ocrdec_status s0 = check_step(m, st, P);
+    if (s0 != OCRDEC_OK) return s0;
+    OCR_CHECK_ARG(row >= 0 && row < st->rows, "row must be in [0, rows)");
+    OCR_CHECK_ARG(P <= st->prefix_cap, "P must be <= prefix_cap (the prompt fills the prefix region)");
+    OCR_CHECK_ARG(tok || emb, "either tok or emb must be given");
+    OCR_CHECK_ARG(!tok || m->embed || m->embed_q.data, "tok needs an embedding table");
+    OCR_CHECK_ARG(!emb || ((uintptr_t)emb & 7) == 0, "emb must be 8-byte aligned");
+    const int H = m->hidden, HD = m->n_heads * m->head_dim, D = m->head_dim;
+    const int cache_cap = st->prefix_cap + st->ring_cap;
+    OCR_CHECK_ARG(cache_cap <= (1 << 16), "prefix_cap + ring_cap must be <= 65536");
+    const size_t need = carve_prefill(nullptr, m, P).bytes;
+    if (!ws || ws_bytes < need)
+        return fail(OCRDEC_ERR_WORKSPACE, "prefill workspace: need " + std::to_string(need) + " bytes, got " +
+                                              std::to_string(ws ? ws_bytes : 0));
+    hipStream_t s = (hipStream_t)stream;
+    PrefillWs w = carve_prefill(ws, m, P);
+    // h = the input rows, x = fp16(RMSNorm(h) * attn_norm of layer 0)
+    if (tok && !m->embed) {
+        const uint8_t* tq = (const uint8_t*)m->embed_q.data;
+        const int64_t nch = n_chunks(m->embed_q.fmt, H);
+#define OCR_EQ(F_)                                                                                                 \
+    case F_:                                                                                                       \
+        hipLaunchKernelGGL(embed_q_norm_kernel<F_>, dim3(P), dim3(64), 0, s, tok, tq, m->vocab, nch, w.h,          \
+                           m->layers[0].attn_norm, H, m->norm_eps, w.x);                                           \
+        break;
+        switch (m->embed_q.fmt) {
+            OCR_EQ(OCRDEC_F16)
+            OCR_EQ(OCRDEC_Q8_0)
+            OCR_EQ(OCRDEC_Q4_0)
+            OCR_EQ(OCRDEC_U8A_G32)
+        }
+#undef OCR_EQ
+    } else {
+        hipLaunchKernelGGL(embed_norm_kernel, dim3(P), dim3(64), 0, s, tok, m->embed, m->vocab, nullptr, w.h,
+                           m->layers[0].attn_norm, H, m->norm_eps, w.x, tok ? (const uint16_t*)nullptr : emb);
+    }
+    PrefillAttnParams ap{};
+    ap.P = P;
+    ap.n_heads = m->n_heads;
+    ap.head_dim = D;
+    ap.qkv = w.qkv;
+    ap.ld_qkv = 3 * HD;
+    ap.q = w.q;
+    ap.cache_cap = cache_cap;
+    ap.scale = 1.0f / sqrtf((float)D);
+    ap.out = w.o;
+    ap.ld_out = HD;
+    prefill_set_rope(ap, m->rope_theta);
+    const int64_t row_off = (int64_t)row * m->n_heads * cache_cap * D;
+    int moe_l = 0;
+    for (int l = 0; l < m->n_layers; ++l) {
+        const ocrdec_layer& L = m->layers[l];
+        const uint16_t* next_norm = (l + 1 < m->n_layers) ? m->layers[l + 1].attn_norm : m->final_norm;
+        if (!next_norm) next_norm = L.attn_norm;  // no LM head: the last norm is not used
+        prefill_gemm(L.wqkv, false, P, w.x, H, w.qkv, 3 * HD, s);
+        ap.k_cache = L.k_cache + row_off;
+        ap.v_cache = L.v_cache + row_off;
+        launch_attn_prefill(ap, s);
+        prefill_gemm(L.wo, false, P, w.o, HD, w.y, H, s);
+        hipLaunchKernelGGL(resid_norm_kernel, dim3(P), dim3(64), 0, s, w.h, w.y, L.ffn_norm, H, m->norm_eps, w.x);
+        if (L.is_moe) {
+            const int K = L.moe.top_k;
+            int32_t* ci = cap && cap->topk_idx ? cap->topk_idx + (int64_t)moe_l * P * K : nullptr;
+            float* cw = cap && cap->topk_w ? cap->topk_w + (int64_t)moe_l * P * K : nullptr;
+            const int32_t* fo = forced_topk ? forced_topk + (int64_t)moe_l * P * K : nullptr;
+            // the combine adds into h and forms the next block's normalised input
+            launch_moe(&L.moe, P, w.x, H, w.h, 1, H, 1, fo, nullptr, ci, cw, w.moe, next_norm, m->norm_eps, w.x, H, s);
+            ++moe_l;
+        } else {
+            const int F = L.dense_ff;
+            prefill_gemm(L.dense_gate_up, true, P, w.x, H, w.a, F, s);
+            prefill_gemm(L.dense_down, false, P, w.a, F, w.y, H, s);
+            hipLaunchKernelGGL(resid_norm_kernel, dim3(P), dim3(64), 0, s, w.h, w.y, next_norm, H, m->norm_eps, w.x);
+        }
+    }
+    if (hidden) {
+        const int64_t n = (int64_t)P * H;
+        hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 1024)), dim3(256), 0, s,
+                           w.h, hidden, n);
+    }
+    if (m->lm_head.data && tok_out) {
+        // the last position's x was normalised with final_norm by the last layer
+        const LmPlan lp = plan_lm(m->lm_head.fmt, m->vocab, H, 1);
+        GemvParams gp{};
+        gp.w = (const uint8_t*)m->lm_head.data;
+        gp.n = m->vocab;
+        gp.k = H;
+        gp.nchunks = n_chunks(m->lm_head.fmt, H);
+        gp.xs = XDirect{w.x + (int64_t)(P - 1) * H, H, 1};
+        gp.part = w.lm_part;
+        launch_lm_argmax(m->lm_head.fmt, lp, gp, s);
+        launch_argmax_final(w.lm_part, lp.grid, 1, tok_out, cap ? cap->lm_top2 : nullptr, nullptr, s);
+    }
+    return launch_status("ocrdec_prefill");
 }

@@ -1,0 +1,155 @@
+"""GPU parity of ocrdec_prefill (the prompt pass of one row) against the oracle.
+
+Routing is teacher-forced to the oracle's choice while the GPU still reports
+its own choice, which must equal the oracle's except at logged near-ties.
+Compared: every layer's keys and values at cache indices 0..P-1 (fp16 rule),
+the residual after the last layer at every position (fp32 rule), the argmax at
+the last position, and that nothing else in the caches changed.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from tests.gpu_util import NEAR_TIE, assert_close, assert_close_f16, f16_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import torch
+    assert torch.cuda.is_available()
+    import quantized_decode_step_amd as qd
+    return qd
+
+
+def small_dims(**kw):
+    d = synth.Dims(hidden=256, n_heads=2, head_dim=128, n_layers=3, n_dense=1, dense_ff=512, n_experts=16, top_k=6,
+                   n_shared=2, expert_ff=128, vocab=1000, prefix_cap=300, ring_cap=8)
+    for k_, v_ in kw.items():
+        setattr(d, k_, v_)
+    return d
+
+
+def run_prefill(q, d, seed, P, row=0, rows=1, use_emb=False, forced=True):
+    import torch
+    print("[case] prefill", d.n_layers, "layers H", d.hidden, "P", P, "row", row, "of", rows, "emb", use_emb,
+          "seed", seed, flush=True)
+    model = synth.make_model(d, seed)
+    st = synth.make_state(d, seed, [d.prefix_cap // 2] * rows, [3] * rows)
+    tok = synth.uniform_i32(synth.stream_id(seed, "prompt"), (P,), 0, d.vocab)
+    emb = synth.normal_f16(synth.stream_id(seed, "prompt_emb"), (P, d.hidden)) if use_emb else None
+    res = O.prefill(model, P, tok=None if use_emb else tok, emb=None if emb is None else emb.astype(np.float64))
+    n_moe = len(res.topk_idx)
+    dm = q.DeviceModel(model)
+    ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+    dm.bind_caches(ds.k_cache, ds.v_cache)
+    k_before = ds.k_cache.cpu().numpy().copy()
+    wsb = q.ocrdec_prefill_workspace_bytes(dm.desc, ds.desc, P)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    K = d.top_k
+    cap_idx = torch.zeros((max(n_moe, 1), P, K), dtype=torch.int32, device="cuda")
+    cap_w = torch.zeros((max(n_moe, 1), P, K), dtype=torch.float32, device="cuda")
+    top2 = torch.zeros((1, 2), dtype=torch.float32, device="cuda")
+    cap = q.StepCapture(cap_idx.data_ptr(), cap_w.data_ptr(), top2.data_ptr())
+    hidden = torch.zeros((P, d.hidden), dtype=torch.float32, device="cuda")
+    tok_out = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    forced_t = torch.from_numpy(np.array(res.topk_idx, np.int32)).cuda() if (forced and n_moe) else None
+    tok_t = torch.from_numpy(tok.astype(np.int32)).cuda()
+    emb_t = f16_tensor(emb) if use_emb else None
+    q.ocrdec_prefill(dm.desc, ds.desc, row, P, tok=None if use_emb else tok_t, emb=emb_t, forced_topk=forced_t,
+                     tok_out=tok_out, hidden=hidden, capture=cap, ws=ws, ws_bytes=wsb)
+    torch.cuda.synchronize()
+    kc = ds.k_cache.cpu().numpy()
+    vc = ds.v_cache.cpu().numpy().view(np.float16)
+    for l in range(d.n_layers):
+        assert_close_f16(kc.view(np.float16)[l, row, :, :P].astype(np.float64), res.k[l], "layer %d keys" % l)
+        assert_close_f16(vc[l, row, :, :P].astype(np.float64), res.v[l], "layer %d values" % l)
+    # nothing outside row `row`, indices 0..P-1 was written
+    mask = np.ones(kc.shape, bool)
+    mask[:, row, :, :P] = False
+    assert np.array_equal(kc[mask], k_before[mask])
+    ties = []
+    g_idx = cap_idx.cpu().numpy()
+    for ml in range(n_moe):
+        for t in range(P):
+            if not np.array_equal(g_idx[ml, t], res.topk_idx[ml][t]):
+                gap = res.router_gap[ml][t]
+                assert gap < NEAR_TIE, "moe layer %d position %d: routing differs, oracle gap %.3g" % (ml, t, gap)
+                ties.append(("route", ml, t, gap))
+        assert_close(cap_w.cpu().numpy()[ml], res.topk_w[ml], "moe layer %d weights" % ml)
+    assert_close(hidden.cpu().numpy(), res.hidden, "hidden after the last layer")
+    g_tok = int(tok_out.cpu().numpy()[0])
+    if g_tok != int(res.tok):
+        gap = res.lm_top2[0] - res.lm_top2[1]
+        assert gap < NEAR_TIE, "token %d vs oracle %d, oracle gap %.3g" % (g_tok, res.tok, gap)
+        ties.append(("token", gap))
+    if ties:
+        print("[near-tie]", ties, flush=True)
+    return res, dm, ds, model, st
+
+
+# P = 1 (one position), a ragged block of 19 (the MoE's single-workgroup
+# routing), 64 (one full query block), 70 and 257 (several query blocks and
+# the MoE's GEMM path)
+@pytest.mark.parametrize("P", [1, 19, 64, 70, 257])
+def test_prefill_small_tokens(q, P):
+    run_prefill(q, small_dims(), 600 + P, P)
+
+
+def test_prefill_input_features_row_offset(q):
+    """fp16 input features instead of tokens, written into row 2 of 3."""
+    run_prefill(q, small_dims(), 611, 45, row=2, rows=3, use_emb=True)
+
+
+def test_prefill_unforced_head_dim_64(q):
+    d = small_dims(n_heads=4, head_dim=64)
+    run_prefill(q, d, 612, 100, forced=False)
+
+
+def test_prefill_quantised_embed_and_head(q):
+    d = small_dims(fmt_embed=synth.Q4_0, fmt_lm=synth.Q8_0)
+    run_prefill(q, d, 613, 33)
+
+
+def test_prefill_full_width_two_layers(q):
+    """Full hidden size and head layout, one dense and one MoE layer, a
+    1100-position prompt (the decode workload's prefix)."""
+    d = synth.dims_full()
+    d.n_layers = 2
+    d.vocab = 5000
+    run_prefill(q, d, 614, 1100, use_emb=True)
+
+
+def test_prefill_then_decode(q):
+    """After the prompt pass, decode steps continue from it: the state says
+    prefix_len = P, gen_index = 0, and the step's token goes to RoPE position P."""
+    import torch
+    d = small_dims()
+    P = 37
+    res, dm, ds, model, st = run_prefill(q, d, 615, P)
+    ost = st.copy()
+    ost.prefix_len[0] = P
+    ost.gen_index[0] = 0
+    kc = ds.k_cache.cpu().numpy().view(np.float16)
+    vc = ds.v_cache.cpu().numpy().view(np.float16)
+    ost.k_cache[:, 0] = kc[:, 0]
+    ost.v_cache[:, 0] = vc[:, 0]
+    ds.prefix_len.fill_(P)
+    ds.gen_index.zero_()
+    wsb = q.ocrdec_step_workspace_bytes(dm.desc, ds.desc)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    tok = np.array([res.tok], np.int32)
+    for step in range(3):
+        ores = O.decode_step(model, ost, tok_in=tok)
+        tok_out = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        hidden = torch.zeros((1, d.hidden), dtype=torch.float32, device="cuda")
+        forced = torch.from_numpy(np.array(ores.topk_idx, np.int32)).cuda()
+        q.ocrdec_decode_step(dm.desc, ds.desc, torch.from_numpy(tok).cuda(), hidden, tok_out, forced, None, ws, wsb)
+        torch.cuda.synchronize()
+        assert_close(hidden.cpu().numpy(), ores.hidden, "decode step %d hidden" % step)
+        g = int(tok_out.cpu().numpy()[0])
+        if g != int(ores.tok[0]):
+            assert ores.lm_top2[0, 0] - ores.lm_top2[0, 1] < NEAR_TIE
+        tok = ores.tok.astype(np.int32)
