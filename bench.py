@@ -72,9 +72,12 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-shaped MoE layer line")
     ap.add_argument("--no-qhead", action="store_true", help="skip the Q4_0 LM-head and embedding variant")
     ap.add_argument("--lm-iters", type=int, default=50)
-    ap.add_argument("--mode", choices=["full", "lm", "prefill"], default="full",
+    ap.add_argument("--mode", choices=["full", "lm", "prefill", "prompt"], default="full",
                     help="lm: only the LM-head argmax loop and a device copy of known size (for counter runs); "
-                         "prefill: only the prefill-shaped MoE layer (2048 tokens)")
+                         "prefill: only the prefill-shaped MoE layer (2048 tokens); "
+                         "prompt: only the prompt pass of the 12-layer model (1100 positions)")
+    ap.add_argument("--no-prompt", action="store_true", help="skip the prompt-pass line")
+    ap.add_argument("--prompt-iters", type=int, default=5)
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--copy-mb", type=int, default=512, help="size of the calibration copy in --mode lm")
     return ap.parse_args()
@@ -133,6 +136,9 @@ def main():
     dm.src_layers = model.layers
     dm.src_lm = model.lm_head
     t_build = time.time() - t_build
+    if args.mode == "prompt":
+        print(json.dumps(prompt_pass(args, q, torch, dev, stream, dm, d)), flush=True)
+        return
 
     def run_rows(R: int, steps: int, warmup: int, want_sample: bool):
         st = synth.make_state(d, SEED, [d.prefix_cap] * R, [T0] * R)
@@ -246,6 +252,9 @@ def main():
     # ---- the prefill-shaped MoE layer (2048 tokens, MFMA path), reported beside the decode metric
     prefill = None if args.no_prefill else prefill_moe(args, q, torch, dev, stream)
 
+    # ---- the prompt pass of the same 12-layer model (1100 positions), beside the decode metric
+    prompt = None if args.no_prompt else prompt_pass(args, q, torch, dev, stream, dm, d)
+
     # ---- CPU oracle baseline on a bounded sample (1 row of the same workload)
     cpu = None
     if not args.no_cpu:
@@ -286,12 +295,14 @@ def main():
         "cpu_baseline": cpu,
         "quantised_head": qhead,
         "prefill_moe": prefill,
+        "prompt_pass": prompt,
         "setup_s": round(t_build, 1),
     }
     print(json.dumps(line), flush=True)
 
 
 PREFILL_SEED = 1005
+PROMPT_SEED = 1006
 PREFILL_TOKENS = 2048
 
 
@@ -333,6 +344,49 @@ def prefill_moe(args, q, torch, dev, stream):
             "tokens": T, "us_per_layer": round(us, 2), "gflop": round(flops / 1e9, 2),
             "tflops": round(flops / (us * 1e-6) / 1e12, 2), "frac_of_fp16_mfma_peak": round(flops / (us * 1e-6) / 2.5e15, 4),
             "weight_MB": round(wbytes / 1e6, 1)}
+
+
+def prompt_pass(args, q, torch, dev, stream, dm, d):
+    """The prompt pass (prefill) of one row through the 12-layer model: 1100
+    positions of fp16 input features ~N(0,1) (the image and prompt features
+    the decode's prefix stands for), causal attention, keys and values written
+    to the row's cache prefix, the LM-head argmax at the last position.
+    Useful flops count every projection, expert and attention product once
+    (2 flop per multiply-add; the causal half of the score and value products)."""
+    import synth
+    P = d.prefix_cap
+    st = synth.make_state(d, PROMPT_SEED, [0], [0])
+    ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+    dm.bind_caches(ds.k_cache, ds.v_cache)
+    emb = torch.from_numpy(synth.normal_f16(synth.stream_id(PROMPT_SEED, "features"), (P, d.hidden)).view(np.int16)).to(dev)
+    tok_out = torch.zeros(1, dtype=torch.int32, device=dev)
+    wsb = q.ocrdec_prefill_workspace_bytes(dm.desc, ds.desc, P)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            q.ocrdec_prefill(dm.desc, ds.desc, 0, P, emb=emb, tok_out=tok_out, ws=ws, ws_bytes=wsb, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.prompt_iters):
+            q.ocrdec_prefill(dm.desc, ds.desc, 0, P, emb=emb, tok_out=tok_out, ws=ws, ws_bytes=wsb, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.prompt_iters
+    H, HD, NH, D = d.hidden, d.n_heads * d.head_dim, d.n_heads, d.head_dim
+    flops = 0.0
+    for lay in dm.src_layers:
+        flops += 2.0 * P * H * 3 * HD + 2.0 * P * HD * H + 2.0 * 2 * D * NH * P * (P + 1) / 2
+        if lay.is_moe:
+            flops += 2.0 * P * H * d.n_experts + 2.0 * P * (d.top_k + d.n_shared) * 3 * H * d.expert_ff
+        else:
+            flops += 2.0 * P * 3 * H * d.dense_ff
+    flops += 2.0 * d.vocab * H
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "prompt pass of the 12-layer mixed-Q4_0 MoE decoder: 1 row, %d positions of fp16 input "
+                        "features, causal attention, cache prefix written, LM-head argmax at the last position" % P,
+            "positions": P, "ms": round(ms, 3), "positions_per_s": round(P / (ms * 1e-3), 1),
+            "gflop": round(flops / 1e9, 1), "tflops": round(tf, 1), "bound": "mfma", "peak_TFLOPs": 2500.0,
+            "frac_of_fp16_mfma_peak": round(tf / 2500.0, 4)}
 
 
 def lm_only(args, dm, d, q, torch, dev, stream):
