@@ -309,8 +309,11 @@ void attn_set_rope(AttnParams& p, float theta) {
 // contraction step are taken in the order the two 16-key score tiles hold
 // them (lane group g: keys 4g..4g+3 of each tile), and V^T is read from LDS
 // in that same key order.  K stays key-major in LDS; V is stored transposed
-// while it is staged.  The next key block is loaded into registers while the
-// current one is used.
+// while it is staged.  The next two key blocks are in flight in registers
+// while the current one is used.  A workgroup takes at most four key blocks:
+// the windows of later query blocks are split over several workgroups (so
+// the longest window does not set the kernel's length), whose unnormalised
+// partials attn_prefill_merge_kernel combines.
 // ---------------------------------------------------------------------------
 
 template <int D>
@@ -335,6 +338,8 @@ __global__ __launch_bounds__(64) void prefill_rope_kernel(PrefillAttnParams p) {
 
 constexpr int PQB = 64;  // queries per workgroup (16 per wavefront)
 constexpr int PKB = 64;  // keys per block
+constexpr int PKC = 4;   // key blocks per workgroup: longer windows are split over workgroups
+constexpr int PREC = 36; // floats per lane in a partial record: 32 outputs, max, sum (padded)
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) {
@@ -345,13 +350,17 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
     constexpr int NPC = PKB * D / 8 / 256;     // 16-byte pieces per thread per block, K and V each
     __shared__ __align__(16) uint16_t k_s[PKB * KLD];
     __shared__ __align__(16) uint16_t vt_s[D * VLD];
-    // the longest query blocks start first
-    const int qb = (int)gridDim.x - 1 - (int)blockIdx.x, h = blockIdx.y;
+    // workgroup (query block qb, chunk c of its key blocks, head h); query
+    // block qb needs key blocks 0..qb, taken PKC at a time
+    const int nch = (int)gridDim.x / p.n_qb;  // chunk slots per query block
+    const int qb = p.n_qb - 1 - (int)blockIdx.x / nch, c = (int)blockIdx.x % nch, h = blockIdx.y;
+    const int n_c = (qb + PKC) / PKC;
+    if (c >= n_c) return;  // uniform: this query block has fewer chunks
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
     const int P = p.P, HD = p.n_heads * D;
     const int q0 = qb * PQB;
     const int qw = q0 + 16 * wave + c16;  // this lane's query (an MFMA column)
-    const int nkb = (min(q0 + PQB, P) - 1) / PKB + 1;
+    const int kb0 = c * PKC, nkb = min(kb0 + PKC, qb + 1);
     const uint16_t* kbase = p.k_cache + (int64_t)h * p.cache_cap * D;
     const uint16_t* vbase = p.v_cache + (int64_t)h * p.cache_cap * D;
 
@@ -365,8 +374,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
     // staging: thread t carries key row t % 64, column pieces t / 64 + 4 i;
     // keys past the prompt are zero (their scores are masked, and a zero
     // value keeps the masked products finite)
-    uint4 kr[NPC], vr[NPC];
-    auto load_blk = [&](int kb) {
+    uint4 kr0[NPC], vr0[NPC], kr1[NPC], vr1[NPC];
+    auto load_blk = [&](int kb, uint4(&kr)[NPC], uint4(&vr)[NPC]) {
         const int key = kb * PKB + (tid & 63);
 #pragma unroll
         for (int i = 0; i < NPC; ++i) {
@@ -378,7 +387,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
             }
         }
     };
-    auto store_blk = [&]() {
+    auto store_blk = [&](const uint4(&kr)[NPC], const uint4(&vr)[NPC]) {
         const int r = tid & 63;
 #pragma unroll
         for (int i = 0; i < NPC; ++i) {
@@ -397,12 +406,13 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = float4v{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
-    load_blk(0);
-    for (int kb = 0; kb < nkb; ++kb) {
+    // two key blocks in flight: block kb + 2 is requested into the registers
+    // block kb has just left for LDS
+    auto step = [&](int kb, uint4(&kr)[NPC], uint4(&vr)[NPC]) {
         __syncthreads();  // the previous block's LDS reads are done
-        store_blk();
+        store_blk(kr, vr);
         __syncthreads();
-        if (kb + 1 < nkb) load_blk(kb + 1);
+        if (kb + 2 < nkb) load_blk(kb + 2, kr, vr);
         // scores of the 64 keys (4 tiles of 16) for this lane's query
         float s[4][4];
 #pragma unroll
@@ -460,6 +470,22 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
                 o[dt] = mfma16(va, pl[kk], o[dt]);
             }
         }
+    };
+    load_blk(kb0, kr0, vr0);
+    if (kb0 + 1 < nkb) load_blk(kb0 + 1, kr1, vr1);
+    for (int kb = kb0; kb < nkb; kb += 2) {
+        step(kb, kr0, vr0);
+        if (kb + 1 < nkb) step(kb + 1, kr1, vr1);
+    }
+    if (n_c > 1) {
+        // one of several chunks: the unnormalised partial of every lane (its
+        // 4 DT outputs, the running max and sum) for the merge kernel
+        float* rec = p.part + ((((int64_t)h * p.n_qb + qb) * nch + c) * 256 + tid) * PREC;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *(float4*)(rec + 4 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+        rec[32] = m_run;
+        rec[33] = l_run;
+        return;
     }
     if (qw < P) {
         const float inv = 1.0f / l_run;
@@ -473,19 +499,71 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
     }
 }
 
+// Merge of the chunks of every query block that has more than one: lane
+// (wave, l) of chunk c holds query q0 + 16 wave + l % 16; the chunks are
+// combined in chunk order (log-sum-exp rescaling), so the result does not
+// depend on which chunk finished first.
+template <int D>
+__global__ __launch_bounds__(256) void attn_prefill_merge_kernel(PrefillAttnParams p, int nch) {
+    constexpr int DT = D / 16;
+    const int qb = blockIdx.x, h = blockIdx.y;
+    const int n_c = (qb + PKC) / PKC;
+    if (n_c <= 1) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+    const int qw = qb * PQB + 16 * wave + c16;
+    if (qw >= p.P) return;
+    const float* base = p.part + (((int64_t)h * p.n_qb + qb) * nch * 256 + tid) * PREC;
+    float M = -INFINITY;
+    for (int c = 0; c < n_c; ++c) M = fmaxf(M, base[(int64_t)c * 256 * PREC + 32]);
+    float L = 0.f;
+    float4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < n_c; ++c) {
+        const float* rec = base + (int64_t)c * 256 * PREC;
+        const float f = __expf(rec[32] - M);
+        L = fmaf(rec[33], f, L);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const float4 v = *(const float4*)(rec + 4 * dt);
+            o[dt] = make_float4(fmaf(v.x, f, o[dt].x), fmaf(v.y, f, o[dt].y), fmaf(v.z, f, o[dt].z), fmaf(v.w, f, o[dt].w));
+        }
+    }
+    const float inv = 1.0f / L;
+    uint16_t* op = p.out + (int64_t)qw * p.ld_out + h * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t lo = (uint32_t)f2h(o[dt].x * inv) | ((uint32_t)f2h(o[dt].y * inv) << 16);
+        const uint32_t hi = (uint32_t)f2h(o[dt].z * inv) | ((uint32_t)f2h(o[dt].w * inv) << 16);
+        *(uint2*)(op + dt * 16 + 4 * g) = make_uint2(lo, hi);
+    }
+}
+
+int prefill_chunks(int P) { return ((P + PQB - 1) / PQB + PKC - 1) / PKC; }
+
+size_t prefill_attn_part_bytes(int P, int n_heads) {
+    const int n_qb = (P + PQB - 1) / PQB;
+    return align256((size_t)n_heads * n_qb * prefill_chunks(P) * 256 * PREC * sizeof(float));
+}
+
 void prefill_set_rope(PrefillAttnParams& p, float theta) {
     for (int i = 0; i < 64; ++i)
         p.inv_freq[i] = i < p.head_dim / 2 ? std::pow((double)theta, -2.0 * i / p.head_dim) : 0.0;
 }
 
-void launch_attn_prefill(const PrefillAttnParams& p, hipStream_t s) {
-    const dim3 gr(p.P, p.n_heads), ga((p.P + PQB - 1) / PQB, p.n_heads);
+void launch_attn_prefill(const PrefillAttnParams& p0, hipStream_t s) {
+    PrefillAttnParams p = p0;
+    p.n_qb = (p.P + PQB - 1) / PQB;
+    const int nch = prefill_chunks(p.P);
+    const dim3 gr(p.P, p.n_heads), ga(p.n_qb * nch, p.n_heads), gm(p.n_qb, p.n_heads);
     if (p.head_dim == 128) {
         hipLaunchKernelGGL(prefill_rope_kernel<128>, gr, dim3(64), 0, s, p);
         hipLaunchKernelGGL(attn_prefill_kernel<128>, ga, dim3(256), 0, s, p);
+        if (nch > 1) hipLaunchKernelGGL(attn_prefill_merge_kernel<128>, gm, dim3(256), 0, s, p, nch);
     } else {
         hipLaunchKernelGGL(prefill_rope_kernel<64>, gr, dim3(64), 0, s, p);
         hipLaunchKernelGGL(attn_prefill_kernel<64>, ga, dim3(256), 0, s, p);
+        if (nch > 1) hipLaunchKernelGGL(attn_prefill_merge_kernel<64>, gm, dim3(256), 0, s, p, nch);
     }
 }
 

@@ -36,8 +36,11 @@ struct PrefillAttnParams {
     double inv_freq[64];
     uint16_t* out;       // [P][ld_out] fp16 attention output
     int64_t ld_out;
+    float* part;         // prefill_attn_part_bytes(P, n_heads): partials of split windows
+    int n_qb;            // query blocks (set by the launcher)
 };
 
+size_t prefill_attn_part_bytes(int P, int n_heads);
 void prefill_set_rope(PrefillAttnParams& p, float theta);
 void launch_attn_prefill(const PrefillAttnParams& p, hipStream_t s);
 

@@ -196,6 +196,7 @@ struct PrefillWs {
     float* y;
     uint16_t* a;
     float* lm_part;
+    float* attn_part;
     MoeWs moe;
     size_t bytes;
 };
@@ -218,6 +219,7 @@ PrefillWs carve_prefill(void* ws, const ocrdec_model* m, int P) {
     w.y = cv.take<float>((size_t)P * H);
     w.a = cv.take<uint16_t>((size_t)P * std::max(dense_ff, 1));
     w.lm_part = cv.take<float>(argmax_ws_bytes(std::max(lm_grid(m, 1), 1), 1) / sizeof(float));
+    w.attn_part = cv.take<float>(prefill_attn_part_bytes(P, m->n_heads) / sizeof(float));
     if (moe) {
         MoeWs probe = carve_moe(nullptr, P, moe);
         char* base = (char*)cv.take<char>(probe.bytes);
@@ -561,6 +563,7 @@ extern "C" ocrdec_status ocrdec_prefill(const ocrdec_model* m, const ocrdec_stat
     ap.scale = 1.0f / sqrtf((float)D);
     ap.out = w.o;
     ap.ld_out = HD;
+    ap.part = w.attn_part;
     prefill_set_rope(ap, m->rope_theta);
     const int64_t row_off = (int64_t)row * m->n_heads * cache_cap * D;
     int moe_l = 0;
