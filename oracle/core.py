@@ -370,6 +370,34 @@ def moe(lay, x: np.ndarray, top_k: int, forced_idx: np.ndarray | None = None):
 # Ring KV cache
 # -----------------------------------------------------------------------------
 
+def kv_quantise(x: np.ndarray):
+    """INT8 KV cache entry of one key or value row (the last axis).
+
+    [FALCON] "How it is meant to be run": the project's CPU service keeps an
+    INT8 KV cache; its format is not given.  Reading: symmetric int8 codes with
+    one fp16 scale per row (per row of the batch, head and position):
+    s = fp16(max|x| / 127), the division in float32; q = round half away from
+    zero of float32(x) / float32(s) (float32 division), clamped to [-127, 127];
+    a row of zeros has s = 0 and q = 0.  The codes are an integer decision, so
+    it is taken in float32, the precision the kernel computes it in.
+
+    Returns (q int8 [..., D], s float16 [...]).
+    """
+    x32 = np.asarray(x, np.float32)
+    amax = np.max(np.abs(x32), axis=-1)
+    s = (amax / np.float32(127)).astype(np.float16)
+    s32 = s.astype(np.float32)[..., None]
+    safe = np.where(s32 > 0, s32, np.float32(1))
+    y = np.where(s32 > 0, x32 / safe, np.float32(0)).astype(np.float64)
+    q = np.sign(y) * np.floor(np.abs(y) + 0.5)
+    return np.clip(q, -127, 127).astype(np.int8), s
+
+
+def kv_dequant(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Values of INT8 KV cache rows: s * q (exact in float64)."""
+    return np.asarray(q, np.float64) * np.asarray(s, np.float64)[..., None]
+
+
 def ring_slot(t: int, ring_cap: int) -> int:
     """Slot of generated token t in the ring: t mod capacity.
 
@@ -412,13 +440,15 @@ class StepResult:
         self.attn_out = []         # per layer: float64 [R][NH*D] (fp16 values)
 
 
-def attention_block(lay, dims, h, kc, vc, prefix_len, t, res: StepResult | None = None):
+def attention_block(lay, dims, h, kc, vc, prefix_len, t, res: StepResult | None = None, ks=None, vs=None):
     """Pre-norm attention with the ring cache for one row; returns new h.
 
     kc, vc: this row's and layer's caches [NH][prefix_cap + ring_cap][D], fp16
     arrays, updated in place at ring slot t mod ring_cap.  [FALCON] "The KV
     cache is an INPUT": the step only reads the cache and contributes the new
-    token's keys and values.
+    token's keys and values.  With ``ks``, ``vs`` (fp16 [NH][cap]) the caches
+    are INT8 (``kv_quantise``): the new token is stored quantised, and the
+    attention reads every key and value, the new one included, as stored.
     """
     H, NH, D = dims.hidden, dims.n_heads, dims.head_dim
     x = f16(rmsnorm(h, lay.attn_norm, dims.norm_eps))
@@ -431,12 +461,19 @@ def attention_block(lay, dims, h, kc, vc, prefix_len, t, res: StepResult | None 
     k = f16(rope(k, pos, dims.rope_theta))
     v = f16(v)
     slot = dims.prefix_cap + ring_slot(t, dims.ring_cap)
-    kc[:, slot] = k.astype(np.float16)
-    vc[:, slot] = v.astype(np.float16)
     idx = window(prefix_len, dims.prefix_cap, t, dims.ring_cap)
     o = np.zeros((NH, D))
-    for hh in range(NH):
-        o[hh] = attention(q[hh], kc[hh, idx], vc[hh, idx], 1.0 / np.sqrt(D))
+    if ks is None:
+        kc[:, slot] = k.astype(np.float16)
+        vc[:, slot] = v.astype(np.float16)
+        for hh in range(NH):
+            o[hh] = attention(q[hh], kc[hh, idx], vc[hh, idx], 1.0 / np.sqrt(D))
+    else:
+        kc[:, slot], ks[:, slot] = kv_quantise(k)
+        vc[:, slot], vs[:, slot] = kv_quantise(v)
+        for hh in range(NH):
+            o[hh] = attention(q[hh], kv_dequant(kc[hh, idx], ks[hh, idx]), kv_dequant(vc[hh, idx], vs[hh, idx]),
+                              1.0 / np.sqrt(D))
     o = f16(o.reshape(-1))
     h = h + gemv_qmat(lay.wo, o[None])[0]
     if res is not None:
@@ -483,9 +520,11 @@ def decode_step(model, state, tok_in=None, hidden_in=None, forced_topk=None,
         res.new_k.append([])
         res.new_v.append([])
         res.attn_out.append([])
+        k8 = getattr(state, "k_scale", None) is not None
         for i, r in enumerate(rows):
             h[i] = attention_block(lay, dims, h[i], state.k_cache[l, r], state.v_cache[l, r],
-                                   int(state.prefix_len[r]), int(state.gen_index[r]), res)
+                                   int(state.prefix_len[r]), int(state.gen_index[r]), res,
+                                   state.k_scale[l, r] if k8 else None, state.v_scale[l, r] if k8 else None)
         res.new_k[-1] = np.array(res.new_k[-1])
         res.new_v[-1] = np.array(res.new_v[-1])
         res.attn_out[-1] = np.array(res.attn_out[-1])

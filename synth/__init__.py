@@ -259,14 +259,20 @@ def make_model(d: Dims, seed: int, with_embed: bool = True, with_lm: bool = True
 
 @dataclass
 class State:
-    """Per-row decode state: caches [L][R][NH][prefix_cap + ring_cap][D] fp16."""
+    """Per-row decode state: caches [L][R][NH][prefix_cap + ring_cap][D], fp16,
+    or int8 codes with one fp16 scale per (layer, row, head, slot) in k_scale /
+    v_scale [L][R][NH][cap]."""
     prefix_len: np.ndarray      # int32 [R]
     gen_index: np.ndarray       # int32 [R]
-    k_cache: np.ndarray         # fp16 [L, R, NH, cap, D]
+    k_cache: np.ndarray         # fp16 (or int8) [L, R, NH, cap, D]
     v_cache: np.ndarray
+    k_scale: np.ndarray | None = None   # fp16 [L, R, NH, cap] for int8 caches
+    v_scale: np.ndarray | None = None
 
     def copy(self) -> "State":
-        return State(self.prefix_len.copy(), self.gen_index.copy(), self.k_cache.copy(), self.v_cache.copy())
+        return State(self.prefix_len.copy(), self.gen_index.copy(), self.k_cache.copy(), self.v_cache.copy(),
+                     None if self.k_scale is None else self.k_scale.copy(),
+                     None if self.v_scale is None else self.v_scale.copy())
 
 
 def make_state(d: Dims, seed: int, prefix_len, gen_index, fill: str = "zero") -> State:
@@ -293,6 +299,34 @@ def make_state(d: Dims, seed: int, prefix_len, gen_index, fill: str = "zero") ->
             kc[l, r][:, ~valid] = pad
             vc[l, r][:, ~valid] = pad
     return State(prefix_len.copy(), gen_index.copy(), kc, vc)
+
+
+def make_state_int8(d: Dims, seed: int, prefix_len, gen_index) -> State:
+    """An int8 KV cache over every slot a row has already written: codes
+    round(40 * N(0,1)) clipped to [-127, 127] and scales fp16((1 + 0.1 N(0,1)) / 40),
+    so the stored values are about N(0,1).  Unwritten slots hold code 0 and
+    scale 0."""
+    prefix_len = np.asarray(prefix_len, np.int32)
+    gen_index = np.asarray(gen_index, np.int32)
+    R = prefix_len.size
+    L, NH, D, cap = d.n_layers, d.n_heads, d.head_dim, d.prefix_cap + d.ring_cap
+    caches, scales = [], []
+    for tag in ("k", "v"):
+        c = np.zeros((L, R, NH, cap, D), np.int8)
+        s = np.zeros((L, R, NH, cap), np.float16)
+        for l in range(L):
+            for r in range(R):
+                codes = np.clip(np.rint(40.0 * normal_f64(stream_id(seed, tag + "_cache8", l, r), (NH, cap, D))),
+                                -127, 127).astype(np.int8)
+                sc = ((1.0 + 0.1 * normal_f64(stream_id(seed, tag + "_scale8", l, r), (NH, cap))) / 40.0).astype(np.float16)
+                valid = np.zeros(cap, bool)
+                valid[:prefix_len[r]] = True
+                valid[d.prefix_cap:d.prefix_cap + min(int(gen_index[r]), d.ring_cap)] = True
+                c[l, r][:, valid] = codes[:, valid]
+                s[l, r][:, valid] = sc[:, valid]
+        caches.append(c)
+        scales.append(s)
+    return State(prefix_len.copy(), gen_index.copy(), caches[0], caches[1], scales[0], scales[1])
 
 
 def first_tokens(d: Dims, seed: int, rows: int) -> np.ndarray:

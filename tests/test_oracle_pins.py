@@ -656,3 +656,57 @@ def test_causal_attention_cases():
     assert np.array_equal(O.causal_attention(q[:1], k[:1], v[:1], 0.25)[0], v[0])
     for i in range(9):
         assert np.allclose(o[i], O.attention(q[i], k[:i + 1], v[:i + 1], 0.25), rtol=1e-13, atol=1e-14)
+
+
+# --- INT8 KV cache ------------------------------------------------------------
+
+def test_kv_quantise_hand_built():
+    """s = fp16(2/127) = 1.0078125 * 2^-6; codes by hand: 2/s = 127.008 -> 127,
+    -1/s = -63.504 -> -64, 0.5/s = 31.752 -> 32.  With s = 2^-7 exactly
+    (amax = 127 * 2^-7) the halves round away from zero: 2.5 -> 3, 0.5 -> 1,
+    -0.5 -> -1, 1.5 -> 2."""
+    q, s = O.kv_quantise(np.array([[2.0, -1.0, 0.5, 0.0]]))
+    assert s[0] == np.float16(0.0157470703125)
+    assert q[0].tolist() == [127, -64, 32, 0]
+    u = 2.0 ** -7
+    q, s = O.kv_quantise(np.array([127 * u, 2.5 * u, 0.5 * u, -0.5 * u, 1.5 * u, -127 * u]))
+    assert s == np.float16(u)
+    assert q.tolist() == [127, 3, 1, -1, 2, -127]
+
+
+def test_kv_quantise_zero_row_scaling_and_bound():
+    q, s = O.kv_quantise(np.zeros((2, 8)))
+    assert np.all(q == 0) and np.all(s == 0)
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((50, 128)).astype(np.float16).astype(np.float64)
+    q, s = O.kv_quantise(x)
+    for k in (-3, 2):
+        q2, s2 = O.kv_quantise(x * 2.0 ** k)
+        assert np.array_equal(q2, q)
+        assert np.array_equal(s2.astype(np.float64), s.astype(np.float64) * 2.0 ** k)
+    amax = np.max(np.abs(x), axis=1)
+    err = np.abs(O.kv_dequant(q, s) - x)
+    assert np.all(err <= 0.5 * s.astype(np.float64)[:, None] + 2.0 ** -11 * amax[:, None] + 1e-15)
+    assert np.all(np.max(np.abs(q.astype(int)), axis=1) >= 126)
+
+
+def test_step_int8_cache_writes_quantised_new_token():
+    """With an int8 cache the new slot holds kv_quantise of the same keys and
+    values an fp16-cache step computes (the layer-0 projections do not
+    depend on the cache), and nothing else in the cache changes."""
+    import synth
+    d = _tiny_dims()
+    m = synth.make_model(d, 41)
+    st8 = synth.make_state_int8(d, 41, [5], [2])
+    st16 = synth.make_state(d, 41, [5], [2])
+    tok = np.array([7], np.int32)
+    before = st8.k_cache.copy()
+    r8 = O.decode_step(m, st8, tok_in=tok)
+    r16 = O.decode_step(m, st16, tok_in=tok)
+    slot = d.prefix_cap + 2 % d.ring_cap
+    qk, sk = O.kv_quantise(r16.new_k[0][0])
+    assert np.array_equal(st8.k_cache[0, 0][:, slot], qk)
+    assert np.array_equal(st8.k_scale[0, 0][:, slot], sk)
+    changed = np.argwhere(np.any(before != st8.k_cache, axis=-1))
+    assert set(changed[:, 3].tolist()) <= {slot}
+    assert r8.tok is not None
