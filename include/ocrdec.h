@@ -172,6 +172,16 @@ ocrdec_status ocrdec_lm_argmax(const ocrdec_qmat* W, int32_t rows, const uint16_
  * a zero key and a zero value; this is the page's extra key with logit =
  * sink and value 0 (its constant-1 query lane folded into a logit).
  *
+ * INT8 KV cache (k_scale and v_scale non-NULL): k_cache and v_cache hold
+ * int8 codes [rows][n_heads][cache_cap][head_dim] and the cached value of a
+ * (row, head, slot) row is scale * code.  The new token's key and value
+ * rows are stored as s = fp16(max|x| / 127) and code = round-half-away(x / s)
+ * clamped to [-127, 127] (both divisions in fp32, correctly rounded; s = 0
+ * gives code 0), and the attention reads them as stored.  The pages say only
+ * that an INT8 KV cache exists (Falcon-OCR card, "How it is meant to be
+ * run"); this one-scale-per-row form is this library's.  Caches 16-byte
+ * aligned.
+ *
  * gen_index and prefix_len are read, never written.
  * head_dim: 64 or 128.  rows >= 1.  Workspace: ocrdec_attn_workspace_bytes.
  * Errors: INVALID_ARG (NULL pointers, head_dim, ld_* too small, caps),
@@ -190,6 +200,8 @@ typedef struct {
     float scale;               /* score scale, normally 1/sqrt(head_dim) */
     uint16_t* out;             /* [rows][ld_out] fp16 */
     int64_t ld_out;
+    uint16_t* k_scale;         /* INT8 KV cache: fp16 [rows][n_heads][cache_cap], see below; NULL: fp16 cache */
+    uint16_t* v_scale;
 } ocrdec_attn_args;
 
 ocrdec_status ocrdec_attn_workspace_bytes(const ocrdec_attn_args* a, size_t* bytes);
@@ -266,8 +278,10 @@ typedef struct {
     ocrdec_qmat dense_gate_up;   /* [2*dense_ff][hidden]: gate rows then up rows */
     ocrdec_qmat dense_down;      /* [hidden][dense_ff] */
     ocrdec_moe_weights moe;      /* MoE layers */
-    uint16_t* k_cache;           /* fp16 [rows][n_heads][prefix_cap+ring_cap][head_dim] */
+    uint16_t* k_cache;           /* fp16 [rows][n_heads][prefix_cap+ring_cap][head_dim], or int8 codes */
     uint16_t* v_cache;
+    uint16_t* k_scale;           /* INT8 KV cache (as in ocrdec_attn_args): fp16 [rows][n_heads][cap]; */
+    uint16_t* v_scale;           /* NULL for fp16 caches */
 } ocrdec_layer;
 
 typedef struct {

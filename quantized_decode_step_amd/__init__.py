@@ -58,7 +58,7 @@ class AttnArgs(ctypes.Structure):
     _fields_ = [("rows", _i32), ("n_heads", _i32), ("head_dim", _i32), ("qkv", _vp), ("ld_qkv", _i64),
                 ("k_cache", _vp), ("v_cache", _vp), ("prefix_cap", _i32), ("ring_cap", _i32),
                 ("prefix_len", _vp), ("gen_index", _vp), ("sink", _vp), ("rope_theta", _f32), ("scale", _f32),
-                ("out", _vp), ("ld_out", _i64)]
+                ("out", _vp), ("ld_out", _i64), ("k_scale", _vp), ("v_scale", _vp)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -74,7 +74,7 @@ class MoeCapture(ctypes.Structure):
 class LayerDesc(ctypes.Structure):
     _fields_ = [("attn_norm", _vp), ("wqkv", QMatDesc), ("wo", QMatDesc), ("ffn_norm", _vp), ("is_moe", _i32),
                 ("dense_ff", _i32), ("dense_gate_up", QMatDesc), ("dense_down", QMatDesc), ("moe", MoeWeights),
-                ("k_cache", _vp), ("v_cache", _vp)]
+                ("k_cache", _vp), ("v_cache", _vp), ("k_scale", _vp), ("v_scale", _vp)]
 
 
 class ModelDesc(ctypes.Structure):
@@ -342,12 +342,15 @@ class DeviceModel:
         view._keep_layers = layers
         return view
 
-    def bind_caches(self, k_cache, v_cache):
-        """Point every layer at its slice of caches [L][R][NH][cap][D] (torch fp16/int16)."""
+    def bind_caches(self, k_cache, v_cache, k_scale=None, v_scale=None):
+        """Point every layer at its slice of caches [L][R][NH][cap][D] (torch fp16/int16, or int8 codes with
+        fp16 scales [L][R][NH][cap])."""
         for i in range(self.desc.n_layers):
             self.layers[i].k_cache = k_cache[i].data_ptr()
             self.layers[i].v_cache = v_cache[i].data_ptr()
-        self._caches = (k_cache, v_cache)
+            self.layers[i].k_scale = k_scale[i].data_ptr() if k_scale is not None else None
+            self.layers[i].v_scale = v_scale[i].data_ptr() if v_scale is not None else None
+        self._caches = (k_cache, v_cache, k_scale, v_scale)
 
 
 class DeviceState:
@@ -357,7 +360,15 @@ class DeviceState:
         import torch
         self.prefix_len = torch.from_numpy(np.asarray(state.prefix_len, np.int32)).to(device)
         self.gen_index = torch.from_numpy(np.asarray(state.gen_index, np.int32)).to(device)
-        self.k_cache = torch.from_numpy(np.ascontiguousarray(state.k_cache).view(np.int16)).to(device)
-        self.v_cache = torch.from_numpy(np.ascontiguousarray(state.v_cache).view(np.int16)).to(device)
+        self.int8 = getattr(state, "k_scale", None) is not None
+        if self.int8:
+            self.k_cache = torch.from_numpy(np.ascontiguousarray(state.k_cache, np.int8)).to(device)
+            self.v_cache = torch.from_numpy(np.ascontiguousarray(state.v_cache, np.int8)).to(device)
+            self.k_scale = torch.from_numpy(np.ascontiguousarray(state.k_scale).view(np.int16)).to(device)
+            self.v_scale = torch.from_numpy(np.ascontiguousarray(state.v_scale).view(np.int16)).to(device)
+        else:
+            self.k_cache = torch.from_numpy(np.ascontiguousarray(state.k_cache).view(np.int16)).to(device)
+            self.v_cache = torch.from_numpy(np.ascontiguousarray(state.v_cache).view(np.int16)).to(device)
+            self.k_scale = self.v_scale = None
         self.rows = int(self.prefix_len.numel())
         self.desc = StateDesc(self.rows, prefix_cap, ring_cap, self.prefix_len.data_ptr(), self.gen_index.data_ptr())

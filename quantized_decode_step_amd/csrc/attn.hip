@@ -77,7 +77,20 @@ OCR_DEV void rope_pair(float x1, float x2, double f, int pos, float& y1, float& 
 
 }  // namespace
 
-template <int D>
+// INT8 KV cache (KV8): the cache holds int8 codes [rows][heads][cap][D] and
+// one fp16 scale per (row, head, slot); the stored value is scale * code.
+// The new token is quantised here: s = fp16(max|x| / 127) and code =
+// round-half-away(x / s) clamped to +-127, both divisions correctly rounded
+// in fp32; the attention reads the new token as stored, like every other key.
+OCR_DEV void i8x8_to_f32(uint2 c, float (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = (float)(int8_t)((c.x >> (8 * i)) & 0xFF);
+        v[4 + i] = (float)(int8_t)((c.y >> (8 * i)) & 0xFF);
+    }
+}
+
+template <int D, bool KV8>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
     constexpr int LPK = D / 8;             // lanes per key
     constexpr int KPL = 64 / LPK;          // keys per wavefront load
@@ -85,6 +98,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
     __shared__ float q_s[D];
     __shared__ __align__(16) uint16_t knew_s[D];
     __shared__ __align__(16) uint16_t vnew_s[D];
+    __shared__ __align__(16) int8_t knew8_s[KV8 ? D : 1];
+    __shared__ __align__(16) int8_t vnew8_s[KV8 ? D : 1];
+    __shared__ float snew_s[2];
     __shared__ float sc_s[KPS];
     __shared__ float o_s[4][D];
     __shared__ float red_s[8];
@@ -115,15 +131,29 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
     // new token's slot is taken from LDS instead
     const int dsub = (lane % LPK) * 8;
     uint4 kr[ITER], vr[ITER];
+    uint2 kr8[KV8 ? ITER : 1], vr8[KV8 ? ITER : 1];
+    float ksc[KV8 ? ITER : 1], vsc[KV8 ? ITER : 1];
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
         const int o = o0 + wave * KPL + it * 4 * KPL + lane / LPK;
-        kr[it] = vr[it] = make_uint4(0, 0, 0, 0);
+        if constexpr (KV8) {
+            kr8[it] = vr8[it] = make_uint2(0, 0);
+            ksc[it] = vsc[it] = 0.f;
+        } else {
+            kr[it] = vr[it] = make_uint4(0, 0, 0, 0);
+        }
         if (o < o1) {
             const int ci = ord_to_idx(p, w, o);
             if (ci != w.new_idx) {
-                kr[it] = *(const uint4*)(p.k_cache + (head_off + ci) * D + dsub);
-                vr[it] = *(const uint4*)(p.v_cache + (head_off + ci) * D + dsub);
+                if constexpr (KV8) {
+                    kr8[it] = *(const uint2*)((const int8_t*)p.k_cache + (head_off + ci) * D + dsub);
+                    vr8[it] = *(const uint2*)((const int8_t*)p.v_cache + (head_off + ci) * D + dsub);
+                    ksc[it] = h2f(p.k_scale[head_off + ci]);
+                    vsc[it] = h2f(p.v_scale[head_off + ci]);
+                } else {
+                    kr[it] = *(const uint4*)(p.k_cache + (head_off + ci) * D + dsub);
+                    vr[it] = *(const uint4*)(p.v_cache + (head_off + ci) * D + dsub);
+                }
             }
         }
     }
@@ -143,7 +173,35 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
         vnew_s[tid - 64] = f2h(xv);
     }
     __syncthreads();
-    if (has_new && tid < D) {
+    if constexpr (KV8) {
+        // wave 0 quantises the new key, wave 1 the new value (D / 64 values per lane)
+        if (has_new && wave < 2) {
+            constexpr int PER = D / 64;
+            const uint16_t* src = wave == 0 ? knew_s : vnew_s;
+            float x[PER], am = 0.f;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                x[j] = h2f(src[lane * PER + j]);
+                am = fmaxf(am, fabsf(x[j]));
+            }
+            am = wave_max(am);
+            const uint16_t s16 = f2h(__fdiv_rn(am, 127.0f));
+            const float sf = h2f(s16);
+            int8_t* dst = wave == 0 ? knew8_s : vnew8_s;
+            int8_t* gdst = (int8_t*)(wave == 0 ? p.k_cache : p.v_cache) + (head_off + w.new_idx) * D;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const float qv = sf > 0.f ? fminf(fmaxf(roundf(__fdiv_rn(x[j], sf)), -127.f), 127.f) : 0.f;
+                dst[lane * PER + j] = (int8_t)qv;
+                gdst[lane * PER + j] = (int8_t)qv;
+            }
+            if (lane == 0) {
+                snew_s[wave] = sf;
+                (wave == 0 ? p.k_scale : p.v_scale)[head_off + w.new_idx] = s16;
+            }
+        }
+        __syncthreads();
+    } else if (has_new && tid < D) {
         p.k_cache[(head_off + w.new_idx) * D + tid] = knew_s[tid];
         p.v_cache[(head_off + w.new_idx) * D + tid] = vnew_s[tid];
     }
@@ -158,10 +216,19 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
         float dot = 0.f;
         if (o < o1) {
             const int ci = ord_to_idx(p, w, o);
-            const uint4 kv = ci == w.new_idx ? *(const uint4*)(knew_s + dsub) : kr[it];
-            half8v kh = bits_to_half8(kv);
+            if constexpr (KV8) {
+                const bool nw = ci == w.new_idx;
+                float kf[8];
+                i8x8_to_f32(nw ? *(const uint2*)(knew8_s + dsub) : kr8[it], kf);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) dot = fmaf(qf[i], (float)kh[i], dot);
+                for (int i = 0; i < 8; ++i) dot = fmaf(qf[i], kf[i], dot);
+                dot *= nw ? snew_s[0] : ksc[it];
+            } else {
+                const uint4 kv = ci == w.new_idx ? *(const uint4*)(knew_s + dsub) : kr[it];
+                half8v kh = bits_to_half8(kv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dot = fmaf(qf[i], (float)kh[i], dot);
+            }
         }
 #pragma unroll
         for (int off = LPK / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
@@ -195,11 +262,20 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
         const int o = o0 + wave * KPL + it * 4 * KPL + lane / LPK;
         if (o < o1) {
             const int ci = ord_to_idx(p, w, o);
-            const uint4 vv = ci == w.new_idx ? *(const uint4*)(vnew_s + dsub) : vr[it];
-            half8v vh = bits_to_half8(vv);
-            const float pj = sc_s[o - o0];
+            if constexpr (KV8) {
+                const bool nw = ci == w.new_idx;
+                float vf[8];
+                i8x8_to_f32(nw ? *(const uint2*)(vnew8_s + dsub) : vr8[it], vf);
+                const float pj = sc_s[o - o0] * (nw ? snew_s[1] : vsc[it]);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(pj, (float)vh[i], acc[i]);
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(pj, vf[i], acc[i]);
+            } else {
+                const uint4 vv = ci == w.new_idx ? *(const uint4*)(vnew_s + dsub) : vr[it];
+                half8v vh = bits_to_half8(vv);
+                const float pj = sc_s[o - o0];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(pj, (float)vh[i], acc[i]);
+            }
         }
     }
     // reduce over the key groups of the wavefront (lanes sharing dsub)
@@ -570,11 +646,14 @@ void launch_attn_prefill(const PrefillAttnParams& p0, hipStream_t s) {
 void launch_attn(const AttnParams& p, hipStream_t s) {
     dim3 g1(p.n_split, p.n_heads, p.rows);
     dim3 g2(p.n_heads, p.rows);
+    const bool kv8 = p.k_scale != nullptr;
     if (p.head_dim == 128) {
-        hipLaunchKernelGGL(attn_partial_kernel<128>, g1, dim3(256), 0, s, p);
+        if (kv8) hipLaunchKernelGGL((attn_partial_kernel<128, true>), g1, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((attn_partial_kernel<128, false>), g1, dim3(256), 0, s, p);
         hipLaunchKernelGGL(attn_combine_kernel<128>, g2, dim3(128), 0, s, p);
     } else {
-        hipLaunchKernelGGL(attn_partial_kernel<64>, g1, dim3(256), 0, s, p);
+        if (kv8) hipLaunchKernelGGL((attn_partial_kernel<64, true>), g1, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((attn_partial_kernel<64, false>), g1, dim3(256), 0, s, p);
         hipLaunchKernelGGL(attn_combine_kernel<64>, g2, dim3(64), 0, s, p);
     }
 }
@@ -593,6 +672,8 @@ ocrdec_status check_attn(const ocrdec_attn_args* a) {
                   "prefix_cap and ring_cap must be >= 0 with a non-empty cache");
     OCR_CHECK_ARG(((uintptr_t)a->k_cache & 15) == 0 && ((uintptr_t)a->v_cache & 15) == 0,
                   "caches must be 16-byte aligned");
+    OCR_CHECK_ARG((a->k_scale == nullptr) == (a->v_scale == nullptr),
+                  "k_scale and v_scale must both be given (int8 cache) or both be NULL (fp16 cache)");
     OCR_CHECK_ARG(a->rope_theta > 0.f, "rope_theta must be positive");
     return OCRDEC_OK;
 }
@@ -631,6 +712,8 @@ extern "C" ocrdec_status ocrdec_attn_decode(const ocrdec_attn_args* a, void* ws,
     p.prefix_len = a->prefix_len;
     p.gen_index = a->gen_index;
     p.sink = a->sink;
+    p.k_scale = a->k_scale;
+    p.v_scale = a->v_scale;
     attn_set_rope(p, a->rope_theta);
     p.scale = a->scale;
     p.out = a->out;

@@ -21,6 +21,8 @@ struct AttnParams {
     int64_t ld_out;
     int n_split;
     float* part;    // [rows][n_heads][n_split][head_dim + 2]
+    uint16_t* k_scale;  // int8 caches: fp16 scale per (row, head, slot); NULL: fp16 caches
+    uint16_t* v_scale;
 };
 
 // Prompt pass (prefill) of one row: P positions, causal attention.

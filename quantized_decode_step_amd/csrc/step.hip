@@ -274,6 +274,8 @@ ocrdec_status check_step(const ocrdec_model* m, const ocrdec_state* st, int moe_
         const std::string tag = "layer " + std::to_string(l) + ": ";
         OCR_CHECK_ARG(L.attn_norm && L.ffn_norm, tag + "norm gains must be non-NULL");
         OCR_CHECK_ARG(L.k_cache && L.v_cache, tag + "caches must be non-NULL");
+        OCR_CHECK_ARG((L.k_scale == nullptr) == (L.v_scale == nullptr),
+                      tag + "k_scale and v_scale must both be given (int8 cache) or both be NULL");
         if ((s = check_qmat(&L.wqkv, "wqkv")) != OCRDEC_OK) return s;
         if ((s = check_qmat(&L.wo, "wo")) != OCRDEC_OK) return s;
         OCR_CHECK_ARG(L.wqkv.n == 3 * HD && L.wqkv.k == H, tag + "wqkv must be [3*n_heads*head_dim][hidden]");
@@ -413,6 +415,8 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             AttnParams ap = ap0;
             ap.k_cache = L.k_cache;
             ap.v_cache = L.v_cache;
+            ap.k_scale = L.k_scale;
+            ap.v_scale = L.v_scale;
             launch_attn(ap, s);
         }
         // O projection + residual
@@ -523,6 +527,8 @@ extern "C" ocrdec_status ocrdec_prefill(const ocrdec_model* m, const ocrdec_stat
     OCR_CHECK_ARG(tok || emb, "either tok or emb must be given");
     OCR_CHECK_ARG(!tok || m->embed || m->embed_q.data, "tok needs an embedding table");
     OCR_CHECK_ARG(!emb || ((uintptr_t)emb & 7) == 0, "emb must be 8-byte aligned");
+    for (int l = 0; l < m->n_layers; ++l)
+        if (m->layers[l].k_scale) return fail(OCRDEC_ERR_UNSUPPORTED, "the prompt pass writes fp16 caches only");
     const int H = m->hidden, HD = m->n_heads * m->head_dim, D = m->head_dim;
     const int cache_cap = st->prefix_cap + st->ring_cap;
     OCR_CHECK_ARG(cache_cap <= (1 << 16), "prefix_cap + ring_cap must be <= 65536");

@@ -175,6 +175,111 @@ def test_attn_ring_small_cap_wraps(q):
     _attn_case(q, 4, 2, 128, 70, 4, [0, 70, 3, 64], [0, 3, 4, 9], None, 5, fill="nan")
 
 
+def _attn_case_int8(q, rows, NH, D, prefix_cap, ring_cap, prefix_len, gen_index, sink, seed):
+    """ocrdec_attn_decode over an INT8 KV cache (codes + one fp16 scale per
+    row, head and slot) against the oracle reading the same stored values.
+    The new value row is fp16(v) on both sides, so its codes and scale must be
+    bit-equal; the new key is too where RoPE is the identity (position 0),
+    and elsewhere within one code step plus the fp16 rule."""
+    import torch
+    cap = prefix_cap + ring_cap
+    rng = np.random.default_rng(seed)
+    qkv = (rng.standard_normal((rows, 3 * NH * D)) * 0.7).astype(np.float32)
+
+    class _D:
+        pass
+    d = _D()
+    d.n_layers, d.n_heads, d.head_dim, d.prefix_cap, d.ring_cap = 1, NH, D, prefix_cap, ring_cap
+    if ring_cap == 0:
+        # linear mode: the window is [0, prefix_len]; draw codes for [0, prefix_len)
+        st = synth.make_state_int8(d, seed, prefix_len, [0] * rows)
+    else:
+        st = synth.make_state_int8(d, seed, prefix_len, gen_index)
+    kc, vc, ks, vs = st.k_cache[0], st.v_cache[0], st.k_scale[0], st.v_scale[0]
+    if sink is not None:
+        kc[:, :, 0] = 0
+        vc[:, :, 0] = 0
+    kd = torch.from_numpy(kc.copy()).cuda()
+    vd = torch.from_numpy(vc.copy()).cuda()
+    ksd = f16_tensor(ks)
+    vsd = f16_tensor(vs)
+    qkv_d = torch.from_numpy(qkv).cuda()
+    pl = torch.tensor(prefix_len, dtype=torch.int32, device="cuda")
+    gi = torch.tensor(gen_index, dtype=torch.int32, device="cuda")
+    sk = torch.tensor(np.asarray(sink, np.float32), device="cuda") if sink is not None else None
+    out = torch.full((rows, NH * D), -1, dtype=torch.int16, device="cuda")
+    a = q.AttnArgs(rows, NH, D, qkv_d.data_ptr(), 3 * NH * D, kd.data_ptr(), vd.data_ptr(), prefix_cap, ring_cap,
+                   pl.data_ptr(), gi.data_ptr(), sk.data_ptr() if sk is not None else None, 10000.0,
+                   float(1 / np.sqrt(D)), out.data_ptr(), NH * D, ksd.data_ptr(), vsd.data_ptr())
+    wsb = q.ocrdec_attn_workspace_bytes(a)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    q.ocrdec_attn_decode(a, ws, wsb)
+    torch.cuda.synchronize()
+    got = from_f16_tensor(out)
+    kc_after, vc_after = kd.cpu().numpy(), vd.cpu().numpy()
+    ks_after = ksd.cpu().numpy().view(np.float16)
+    vs_after = vsd.cpu().numpy().view(np.float16)
+    for r in range(rows):
+        qq = qkv[r, :NH * D].reshape(NH, D).astype(np.float64)
+        kk = qkv[r, NH * D:2 * NH * D].reshape(NH, D).astype(np.float64)
+        vv = qkv[r, 2 * NH * D:].reshape(NH, D).astype(np.float64)
+        if ring_cap:
+            t = gen_index[r]
+            pos = prefix_len[r] + t
+            slot = prefix_cap + O.ring_slot(t, ring_cap)
+            idx = O.window(prefix_len[r], prefix_cap, t, ring_cap)
+        else:
+            pos = prefix_len[r] - (1 if sink is not None else 0)
+            slot = prefix_len[r]
+            idx = np.arange(prefix_len[r] + 1)
+        qr = O.f16(O.rope(qq, pos, 10000.0))
+        kr = O.f16(O.rope(kk, pos, 10000.0))
+        vr = O.f16(vv)
+        kq, kss = O.kv_quantise(kr)
+        vq, vss = O.kv_quantise(vr)
+        kcr, vcr, ksr, vsr = kc[r].copy(), vc[r].copy(), ks[r].copy(), vs[r].copy()
+        kcr[:, slot], ksr[:, slot] = kq, kss
+        vcr[:, slot], vsr[:, slot] = vq, vss
+        ref = np.zeros((NH, D))
+        for h in range(NH):
+            K = O.kv_dequant(kcr[h, idx], ksr[h, idx])
+            V = O.kv_dequant(vcr[h, idx], vsr[h, idx])
+            if sink is not None:
+                ref[h] = O.attention(qr[h], K, V, 1 / np.sqrt(D), sink=float(sink[h]), sink_index=0)
+            else:
+                ref[h] = O.attention(qr[h], K, V, 1 / np.sqrt(D))
+        assert_close_f16(got[r], O.f16(ref.reshape(-1)), "int8 attn out row %d" % r)
+        assert np.array_equal(vc_after[r][:, slot], vq), "new v codes row %d" % r
+        assert np.array_equal(vs_after[r][:, slot], vss), "new v scales row %d" % r
+        if pos == 0:
+            assert np.array_equal(kc_after[r][:, slot], kq), "new k codes row %d" % r
+            assert np.array_equal(ks_after[r][:, slot], kss), "new k scales row %d" % r
+        else:
+            gk = O.kv_dequant(kc_after[r][:, slot], ks_after[r][:, slot])
+            ok = O.kv_dequant(kq, kss)
+            bound = 2e-3 * np.sqrt(np.mean(ok * ok)) + 2 * kss.astype(np.float64)[:, None]
+            assert np.all(np.abs(gk - ok) <= bound), "new k row %d" % r
+        mask = np.ones(kc.shape[2], bool)
+        mask[slot] = False
+        assert np.array_equal(kc_after[r][:, mask], kc[r][:, mask])
+        assert np.array_equal(ks_after[r][:, mask].view(np.uint16), ks[r][:, mask].view(np.uint16))
+
+
+@pytest.mark.parametrize("rows,prefix_len,gen_index", [
+    (1, [0], [0]), (1, [1100], [128]), (3, [1100, 0, 37], [5, 300, 127]), (24, [1100] * 24, list(range(100, 124))),
+])
+def test_attn_ring_int8_cache(q, rows, prefix_len, gen_index):
+    _say("attn ring int8", rows, prefix_len[:3], gen_index[:3])
+    _attn_case_int8(q, rows, 10, 128, 1100, 128, prefix_len, gen_index, None, 31 + rows)
+
+
+@pytest.mark.parametrize("rows,L", [(1, 350), (6, 3000)])
+def test_attn_sink_linear_int8_cache(q, rows, L):
+    _say("attn sink linear int8", rows, L)
+    sink = O.f16(np.random.default_rng(L + rows).standard_normal(8))
+    _attn_case_int8(q, rows, 8, 64, L + 1, 0, [L] * rows, [0] * rows, sink, 41 + rows)
+
+
 # -----------------------------------------------------------------------------
 # ocrdec_moe_layer
 # -----------------------------------------------------------------------------

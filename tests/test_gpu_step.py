@@ -34,16 +34,20 @@ def small_dims(**kw):
     return d
 
 
-def run_steps(q, d, seed, prefix_len, gen_index, n_steps, forced=True, sample_rows=None, check_cache=True):
+def run_steps(q, d, seed, prefix_len, gen_index, n_steps, forced=True, sample_rows=None, check_cache=True,
+              int8_kv=False):
     import torch
     R = len(prefix_len)
     print("[case] step", d.n_layers, "layers", "H", d.hidden, "V", d.vocab, "R", R, "steps", n_steps, "seed", seed,
-          flush=True)
+          "int8 kv" if int8_kv else "", flush=True)
     model = synth.make_model(d, seed)
-    st = synth.make_state(d, seed, prefix_len, gen_index)
+    st = synth.make_state_int8(d, seed, prefix_len, gen_index) if int8_kv else synth.make_state(d, seed, prefix_len,
+                                                                                                    gen_index)
     dm = q.DeviceModel(model)
     ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
-    dm.bind_caches(ds.k_cache, ds.v_cache)
+    dm.bind_caches(ds.k_cache, ds.v_cache, ds.k_scale, ds.v_scale)
+    if int8_kv:
+        check_cache = False  # the new slots are compared as stored values below
     wsb = q.ocrdec_step_workspace_bytes(dm.desc, ds.desc)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     n_moe = sum(1 for l in model.layers if l.is_moe)
@@ -101,6 +105,19 @@ def run_steps(q, d, seed, prefix_len, gen_index, n_steps, forced=True, sample_ro
                                      "step %d layer %d k" % (step, l))
                     assert_close_f16(vc[l, r, :, slot].astype(np.float64), res.new_v[l][i],
                                      "step %d layer %d v" % (step, l))
+        if int8_kv:
+            kc, ks = ds.k_cache.cpu().numpy(), ds.k_scale.cpu().numpy().view(np.float16)
+            vc, vs = ds.v_cache.cpu().numpy(), ds.v_scale.cpu().numpy().view(np.float16)
+            for l in range(d.n_layers):
+                for i, r in enumerate(rows):
+                    t = int(st.gen_index[r]) + step
+                    slot = d.prefix_cap + t % d.ring_cap
+                    for what, c, s, oc, os_ in (("k", kc, ks, ost.k_cache, ost.k_scale),
+                                                ("v", vc, vs, ost.v_cache, ost.v_scale)):
+                        g = O.kv_dequant(c[l, r, :, slot], s[l, r, :, slot])
+                        o = O.kv_dequant(oc[l, r, :, slot], os_[l, r, :, slot])
+                        bound = 2e-3 * np.sqrt(np.mean(o * o)) + 2 * os_[l, r, :, slot].astype(np.float64)[:, None]
+                        assert np.all(np.abs(g - o) <= bound), "step %d layer %d new %s" % (step, l, what)
         gi = ds.gen_index.cpu().numpy()
         assert np.array_equal(gi[rows], ost.gen_index[rows])
         nxt = tok.copy()
@@ -135,6 +152,14 @@ def test_step_rows_around_folded_combine(q, R, ns, k):
     d = small_dims(n_shared=ns, top_k=k)
     run_steps(q, d, 530 + 16 * R + 4 * ns + k, prefix_len=[(11 * i + 5) % 41 for i in range(R)],
               gen_index=[(5 * i + 2) % 9 for i in range(R)], n_steps=4)
+
+
+# INT8 KV cache through the whole step (fused and separate combine paths)
+@pytest.mark.parametrize("R", [1, 5])
+def test_step_int8_kv_cache(q, R):
+    d = small_dims()
+    run_steps(q, d, 540 + R, prefix_len=[(13 * i + 7) % 41 for i in range(R)], gen_index=[(3 * i + 4) % 11 for i in range(R)],
+              n_steps=10, int8_kv=True)
 
 
 # quantised embedding tables and LM heads through the whole step (tokens from
