@@ -77,13 +77,15 @@ def parse():
                          "prefill: only the prefill-shaped MoE layer (2048 tokens); "
                          "prompt: only the prompt pass of the 12-layer model (1100 positions)")
     ap.add_argument("--no-prompt", action="store_true", help="skip the prompt-pass line")
+    ap.add_argument("--no-int8kv", action="store_true", help="skip the INT8 KV cache runs")
     ap.add_argument("--prompt-iters", type=int, default=5)
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--copy-mb", type=int, default=512, help="size of the calibration copy in --mode lm")
     return ap.parse_args()
 
 
-def algorithmic_bytes(dm, d, rows: int, distinct_experts_per_layer: float, avg_keys: float) -> float:
+def algorithmic_bytes(dm, d, rows: int, distinct_experts_per_layer: float, avg_keys: float,
+                      kv_bytes_per_value: float = 2.0) -> float:
     """Bytes the method must move per step: every weight matrix once, the
     routed experts actually used, the KV window of every row and layer, and
     the embedding rows."""
@@ -102,7 +104,7 @@ def algorithmic_bytes(dm, d, rows: int, distinct_experts_per_layer: float, avg_k
             tot += nb(lay.dense_gate_up) + nb(lay.dense_down)
     tot += n_moe * distinct_experts_per_layer * per_expert
     tot += nb(dm.src_lm) + 2 * H + rows * 2 * H
-    tot += d.n_layers * rows * 2 * d.n_heads * d.head_dim * 2 * avg_keys
+    tot += d.n_layers * rows * 2 * d.n_heads * d.head_dim * kv_bytes_per_value * avg_keys
     return tot
 
 
@@ -140,10 +142,13 @@ def main():
         print(json.dumps(prompt_pass(args, q, torch, dev, stream, dm, d)), flush=True)
         return
 
-    def run_rows(R: int, steps: int, warmup: int, want_sample: bool):
-        st = synth.make_state(d, SEED, [d.prefix_cap] * R, [T0] * R)
+    def run_rows(R: int, steps: int, warmup: int, want_sample: bool, int8_kv: bool = False):
+        if int8_kv:
+            st = synth.make_state_int8(d, SEED, [d.prefix_cap] * R, [T0] * R)
+        else:
+            st = synth.make_state(d, SEED, [d.prefix_cap] * R, [T0] * R)
         ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
-        dm.bind_caches(ds.k_cache, ds.v_cache)
+        dm.bind_caches(ds.k_cache, ds.v_cache, ds.k_scale, ds.v_scale)
         wsb = q.ocrdec_step_workspace_bytes(dm.desc, ds.desc)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
         tok = torch.from_numpy(synth.first_tokens(d, SEED, R)).to(dev)
@@ -185,7 +190,8 @@ def main():
         # keys each row attends, averaged over the timed steps (prefix + ring so far, incl. the new token)
         ts = np.arange(T0 + warmup, T0 + warmup + steps)
         avg_keys = float(np.mean(d.prefix_cap + np.minimum(ts + 1, d.ring_cap)))
-        byt = algorithmic_bytes(dm, d, R, out["distinct_experts_per_moe_layer"] or d.top_k, avg_keys)
+        byt = algorithmic_bytes(dm, d, R, out["distinct_experts_per_moe_layer"] or d.top_k, avg_keys,
+                                kv_bytes_per_value=(1.0 + 2.0 / d.head_dim) if int8_kv else 2.0)
         out["algorithmic_MB_per_step"] = byt / 1e6
         out["step_GBps"] = byt / (ms * 1e-3) / 1e9
         del graph
@@ -196,6 +202,13 @@ def main():
     for r in [int(x) for x in args.sweep.split(",") if x.strip()]:
         if r != args.rows:
             sweep.append(run_rows(r, args.steps, args.warmup, False))
+
+    # ---- the same step over an INT8 KV cache (codes + one fp16 scale per row, head and slot)
+    int8_kv = None
+    if not args.no_int8kv:
+        runs8 = [run_rows(r, args.steps, args.warmup, False, int8_kv=True) for r in (1, 24)]
+        int8_kv = {"cache": "int8 codes + fp16 scale per (row, head, slot)",
+                   "runs": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in runs8]}
 
     # ---- roofline of the dominant kernel: the LM-head GEMV with fused argmax
     R = args.rows
@@ -296,6 +309,7 @@ def main():
         "quantised_head": qhead,
         "prefill_moe": prefill,
         "prompt_pass": prompt,
+        "int8_kv": int8_kv,
         "setup_s": round(t_build, 1),
     }
     print(json.dumps(line), flush=True)

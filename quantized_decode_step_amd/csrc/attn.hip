@@ -82,17 +82,18 @@ OCR_DEV void rope_pair(float x1, float x2, double f, int pos, float& y1, float& 
 // The new token is quantised here: s = fp16(max|x| / 127) and code =
 // round-half-away(x / s) clamped to +-127, both divisions correctly rounded
 // in fp32; the attention reads the new token as stored, like every other key.
-OCR_DEV void i8x8_to_f32(uint2 c, float (&v)[8]) {
+OCR_DEV void i8x16_to_f32(uint4 c, float (&v)[16]) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[i] = (float)(int8_t)((c.x >> (8 * i)) & 0xFF);
-        v[4 + i] = (float)(int8_t)((c.y >> (8 * i)) & 0xFF);
-    }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[4 * j + i] = (float)(int8_t)((w[j] >> (8 * i)) & 0xFF);
 }
 
 template <int D, bool KV8>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
-    constexpr int LPK = D / 8;             // lanes per key
+    constexpr int VPL = KV8 ? 16 : 8;      // values per lane and key (one 16-byte load)
+    constexpr int LPK = D / VPL;           // lanes per key
     constexpr int KPL = 64 / LPK;          // keys per wavefront load
     constexpr int ITER = KPS / (4 * KPL);  // key groups per wavefront
     __shared__ float q_s[D];
@@ -129,15 +130,15 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
     // ---- keys and values of this wavefront (wave w takes keys o0 + w*KPL +
     // it*4*KPL, one key per lane group), all requested before any use; the
     // new token's slot is taken from LDS instead
-    const int dsub = (lane % LPK) * 8;
+    const int dsub = (lane % LPK) * VPL;
     uint4 kr[ITER], vr[ITER];
-    uint2 kr8[KV8 ? ITER : 1], vr8[KV8 ? ITER : 1];
+    uint4 kr8[KV8 ? ITER : 1], vr8[KV8 ? ITER : 1];
     float ksc[KV8 ? ITER : 1], vsc[KV8 ? ITER : 1];
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
         const int o = o0 + wave * KPL + it * 4 * KPL + lane / LPK;
         if constexpr (KV8) {
-            kr8[it] = vr8[it] = make_uint2(0, 0);
+            kr8[it] = vr8[it] = make_uint4(0, 0, 0, 0);
             ksc[it] = vsc[it] = 0.f;
         } else {
             kr[it] = vr[it] = make_uint4(0, 0, 0, 0);
@@ -146,8 +147,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
             const int ci = ord_to_idx(p, w, o);
             if (ci != w.new_idx) {
                 if constexpr (KV8) {
-                    kr8[it] = *(const uint2*)((const int8_t*)p.k_cache + (head_off + ci) * D + dsub);
-                    vr8[it] = *(const uint2*)((const int8_t*)p.v_cache + (head_off + ci) * D + dsub);
+                    kr8[it] = *(const uint4*)((const int8_t*)p.k_cache + (head_off + ci) * D + dsub);
+                    vr8[it] = *(const uint4*)((const int8_t*)p.v_cache + (head_off + ci) * D + dsub);
                     ksc[it] = h2f(p.k_scale[head_off + ci]);
                     vsc[it] = h2f(p.v_scale[head_off + ci]);
                 } else {
@@ -207,9 +208,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
     }
 
     // ---- scores
-    float qf[8];
+    float qf[VPL];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qf[i] = q_s[dsub + i];
+    for (int i = 0; i < VPL; ++i) qf[i] = q_s[dsub + i];
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
         const int o = o0 + wave * KPL + it * 4 * KPL + lane / LPK;
@@ -218,10 +219,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
             const int ci = ord_to_idx(p, w, o);
             if constexpr (KV8) {
                 const bool nw = ci == w.new_idx;
-                float kf[8];
-                i8x8_to_f32(nw ? *(const uint2*)(knew8_s + dsub) : kr8[it], kf);
+                float kf[16];
+                i8x16_to_f32(nw ? *(const uint4*)(knew8_s + dsub) : kr8[it], kf);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) dot = fmaf(qf[i], kf[i], dot);
+                for (int i = 0; i < 16; ++i) dot = fmaf(qf[i], kf[i], dot);
                 dot *= nw ? snew_s[0] : ksc[it];
             } else {
                 const uint4 kv = ci == w.new_idx ? *(const uint4*)(knew_s + dsub) : kr[it];
@@ -254,9 +255,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
     }
     __syncthreads();
     // ---- p . V over the same key assignment
-    float acc[8];
+    float acc[VPL];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int i = 0; i < VPL; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
         const int o = o0 + wave * KPL + it * 4 * KPL + lane / LPK;
@@ -264,11 +265,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
             const int ci = ord_to_idx(p, w, o);
             if constexpr (KV8) {
                 const bool nw = ci == w.new_idx;
-                float vf[8];
-                i8x8_to_f32(nw ? *(const uint2*)(vnew8_s + dsub) : vr8[it], vf);
+                float vf[16];
+                i8x16_to_f32(nw ? *(const uint4*)(vnew8_s + dsub) : vr8[it], vf);
                 const float pj = sc_s[o - o0] * (nw ? snew_s[1] : vsc[it]);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = fmaf(pj, vf[i], acc[i]);
+                for (int i = 0; i < 16; ++i) acc[i] = fmaf(pj, vf[i], acc[i]);
             } else {
                 const uint4 vv = ci == w.new_idx ? *(const uint4*)(vnew_s + dsub) : vr[it];
                 half8v vh = bits_to_half8(vv);
@@ -282,10 +283,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
 #pragma unroll
     for (int off = LPK; off < 64; off <<= 1)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], off, 64);
+        for (int i = 0; i < VPL; ++i) acc[i] += __shfl_xor(acc[i], off, 64);
     if (lane < LPK) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o_s[wave][dsub + i] = acc[i];
+        for (int i = 0; i < VPL; ++i) o_s[wave][dsub + i] = acc[i];
     }
     __syncthreads();
     if (tid < D) part[tid] = o_s[0][tid] + o_s[1][tid] + o_s[2][tid] + o_s[3][tid];
