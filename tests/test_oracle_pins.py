@@ -710,3 +710,33 @@ def test_step_int8_cache_writes_quantised_new_token():
     changed = np.argwhere(np.any(before != st8.k_cache, axis=-1))
     assert set(changed[:, 3].tolist()) <= {slot}
     assert r8.tok is not None
+
+
+# --- generation of one request (the round's unit) -----------------------------
+
+def test_generate_first_token_eos_and_budget():
+    """max_new = 1 gives the prompt pass's token; a later token of the
+    sequence put in the EOS set ends it there (not handed out, or kept with
+    keep_eos); the sequence continues the prompt pass with decode steps."""
+    import synth
+    d = _prefill_dims()
+    d.prefix_cap = 16
+    m = synth.make_model(d, 51)
+    P = 9
+    tok = synth.uniform_i32(synth.stream_id(51, "prompt"), (P,), 0, d.vocab)
+    pre = O.prefill(m, P, tok=tok)
+    one, stop, _ = O.generate(m, P, tok=tok, max_new=1)
+    assert one == [int(pre.tok)] and stop == 2
+    seq, stop, gaps = O.generate(m, P, tok=tok, max_new=6)
+    assert len(seq) == 6 and stop == 2 and len(gaps) == 6 and seq[0] == int(pre.tok)
+    # each later token is the prompt pass's argmax over the prompt extended by
+    # the tokens generated so far (the hand-off puts the first decode step at
+    # position P with the prompt's cache)
+    for i in (1, 2):
+        ext = np.concatenate([tok, np.array(seq[:i], np.int32)])
+        assert seq[i] == int(O.prefill(m, P + i, tok=ext).tok)
+    k = next(i for i in range(1, 6) if seq[i] not in seq[:i])  # a token not seen before it
+    cut, stop, _ = O.generate(m, P, tok=tok, max_new=6, eos=[seq[k]])
+    assert cut == seq[:k] and stop == 1
+    kept, stop, _ = O.generate(m, P, tok=tok, max_new=6, eos=[seq[k]], keep_eos=True)
+    assert kept == seq[:k + 1] and stop == 1
