@@ -377,6 +377,48 @@ ocrdec_status ocrdec_prefill(const ocrdec_model* m, const ocrdec_state* st, int3
                              int32_t* tok_out, float* hidden, const ocrdec_step_capture* capture, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* ocrdec_run_round: a queue of requests decoded together                    */
+/* ------------------------------------------------------------------------ */
+
+/* One request of a round.  The prompt is `tokens` (device int32 [P]) or, when
+ * tokens is NULL, `features` (device fp16 [P][hidden]); out is a HOST buffer
+ * of max_new tokens.  n_out and stop are set by ocrdec_run_round: stop = 1
+ * (an EOS token was produced) or 2 (max_new tokens). */
+typedef struct {
+    const int32_t* tokens;
+    const uint16_t* features;
+    int32_t P;
+    int32_t max_new;
+    int32_t* out;
+    int32_t n_out;
+    int32_t stop;
+} ocrdec_request;
+
+/* Serves the requests with the rows of `st` (Falcon-OCR card, "How it is
+ * meant to be run": rows of one round share each decode step's read of the
+ * weights, and merging requests into a round is what makes a queue
+ * affordable).  Requests are taken in order; each gets the lowest free row,
+ * whose cache prefix its prompt pass (ocrdec_prefill) fills and which gives
+ * its first token; then decode steps (ocrdec_decode_step, tokens fed back on
+ * the device) advance every occupied row together.  After each step the new
+ * tokens are read on the host: a request stops at a token of the EOS set
+ * (HunyuanOCR ncnn page, section 3.5: the end token is not handed out; with
+ * keep_eos it is appended, for comparisons) or after max_new tokens, and
+ * its row takes the next request.  The call returns when every request has
+ * stopped; it synchronises the stream once per step.  It sets prefix_len and
+ * gen_index of the rows it admits and overwrites the rows' caches.
+ *   st       rows = the round's row slots (1..32); prefix_cap >= every P
+ *   eos      HOST int32 [n_eos] (may be empty)
+ * Workspace: ocrdec_round_workspace_bytes(m, st, max P) bytes.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE (a failed step ends
+ * the round; the requests keep what they had). */
+ocrdec_status ocrdec_round_workspace_bytes(const ocrdec_model* m, const ocrdec_state* st, int32_t max_P,
+                                           size_t* bytes);
+ocrdec_status ocrdec_run_round(const ocrdec_model* m, const ocrdec_state* st, ocrdec_request* reqs, int32_t n_reqs,
+                               const int32_t* eos, int32_t n_eos, int32_t keep_eos, void* ws, size_t ws_bytes,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -107,19 +107,22 @@ _lib.ocrdec_moe_layer.argtypes = [_P(MoeWeights), _i32, _vp, _vp, _i32, _vp, _P(
 _lib.ocrdec_step_workspace_bytes.argtypes = [_P(ModelDesc), _P(StateDesc), _P(_sz)]
 _lib.ocrdec_decode_step.argtypes = [_P(ModelDesc), _P(StateDesc), _vp, _vp, _vp, _vp, _P(StepCapture), _vp, _sz, _vp]
 _lib.ocrdec_prefill_workspace_bytes.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _P(_sz)]
+_lib.ocrdec_round_workspace_bytes.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _P(_sz)]
+_lib.ocrdec_run_round.argtypes = [_P(ModelDesc), _P(StateDesc), _vp, _i32, _vp, _i32, _i32, _vp, _sz, _vp]
 _lib.ocrdec_prefill.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _P(StepCapture),
                                 _vp, _sz, _vp]
 for _fn in ("ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack", "ocrdec_gemv_q", "ocrdec_lm_argmax_workspace_bytes",
             "ocrdec_lm_argmax", "ocrdec_attn_workspace_bytes",
             "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes", "ocrdec_moe_layer", "ocrdec_step_workspace_bytes",
-            "ocrdec_decode_step", "ocrdec_prefill_workspace_bytes", "ocrdec_prefill"):
+            "ocrdec_decode_step", "ocrdec_prefill_workspace_bytes", "ocrdec_prefill", "ocrdec_round_workspace_bytes",
+            "ocrdec_run_round"):
     getattr(_lib, _fn).restype = ctypes.c_int
 
 EXPORTED = ["ocrdec_last_error", "ocrdec_version", "ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack",
             "ocrdec_gemv_q", "ocrdec_lm_argmax_workspace_bytes", "ocrdec_lm_argmax", "ocrdec_attn_workspace_bytes",
             "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes",
             "ocrdec_moe_layer", "ocrdec_step_workspace_bytes", "ocrdec_decode_step",
-            "ocrdec_prefill_workspace_bytes", "ocrdec_prefill"]
+            "ocrdec_prefill_workspace_bytes", "ocrdec_prefill", "ocrdec_round_workspace_bytes", "ocrdec_run_round"]
 
 
 def _ptr(t) -> int | None:
@@ -221,6 +224,26 @@ def ocrdec_decode_step(m: ModelDesc, st: StateDesc, tok_in=None, hidden=None, to
     _check(_lib.ocrdec_decode_step(ctypes.byref(m), ctypes.byref(st), _ptr(tok_in), _ptr(hidden), _ptr(tok_out),
                                    _ptr(forced_topk), ctypes.byref(capture) if capture is not None else None,
                                    _ptr(ws), ws_bytes, _stream(stream)))
+
+
+class Request(ctypes.Structure):
+    _fields_ = [("tokens", _vp), ("features", _vp), ("P", _i32), ("max_new", _i32), ("out", _vp), ("n_out", _i32),
+                ("stop", _i32)]
+
+
+def ocrdec_round_workspace_bytes(m: ModelDesc, st: StateDesc, max_P: int) -> int:
+    b = _sz()
+    _check(_lib.ocrdec_round_workspace_bytes(ctypes.byref(m), ctypes.byref(st), max_P, ctypes.byref(b)))
+    return b.value
+
+
+def ocrdec_run_round(m: ModelDesc, st: StateDesc, reqs, eos=(), keep_eos: bool = False, ws=None, ws_bytes: int = 0,
+                     stream=None):
+    """reqs: a ctypes array of Request (host), filled in place."""
+    eos_arr = (ctypes.c_int32 * max(len(eos), 1))(*eos)
+    _check(_lib.ocrdec_run_round(ctypes.byref(m), ctypes.byref(st), ctypes.cast(reqs, _vp), len(reqs),
+                                 ctypes.cast(eos_arr, _vp), len(eos), int(keep_eos), _ptr(ws), ws_bytes,
+                                 _stream(stream)))
 
 
 def ocrdec_prefill_workspace_bytes(m: ModelDesc, st: StateDesc, P: int) -> int:

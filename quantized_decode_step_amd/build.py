@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libocrdec.so")
-SOURCES = ["api.cpp", "gemv.hip", "attn.hip", "moe.hip", "step.hip"]
+SOURCES = ["api.cpp", "gemv.hip", "attn.hip", "moe.hip", "step.hip", "round.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU ops are kept out of every code object.

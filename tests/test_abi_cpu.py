@@ -88,9 +88,9 @@ def test_q4_packed_lane_layout(q):
     assert np.array_equal(scales.astype(np.float64), d)
 
 
-def _err(q, fn, *a):
+def _err(q, fn, *a, **kw):
     with pytest.raises(q.OcrdecError) as e:
-        fn(*a)
+        fn(*a, **kw)
     return e.value.status
 
 
@@ -124,3 +124,28 @@ def test_validation_errors_without_a_device(q):
     assert _err(q, q.ocrdec_moe_layer, w, 1, fake, fake, True, None, None, None, 0, 0) == q.OCRDEC_ERR_WORKSPACE
     w.gate_up = q.QMatDesc(synth.Q4_0, 100, 1280, fake)
     assert _err(q, q.ocrdec_moe_workspace_bytes, w, 1) == q.OCRDEC_ERR_INVALID_ARG
+
+
+def test_prefill_and_round_validation_without_a_device(q):
+    """Prompt lengths, rows and requests are checked on the host before any
+    device work."""
+    fake = 1 << 20
+    m = q.ModelDesc()
+    m.n_layers, m.hidden, m.n_heads, m.head_dim, m.vocab = 1, 256, 2, 128, 1000
+    m.lm_head = q.QMatDesc(synth.F16, 1000, 256, fake)
+    st = q.StateDesc(2, 16, 8, fake, fake)
+    assert _err(q, q.ocrdec_prefill, m, st, 0, 0, stream=0) == q.OCRDEC_ERR_INVALID_ARG
+    assert _err(q, q.ocrdec_prefill_workspace_bytes, m, st, 0) == q.OCRDEC_ERR_INVALID_ARG
+    reqs = (q.Request * 2)()
+    out = (ctypes.c_int32 * 4)()
+    for r in reqs:
+        r.tokens, r.P, r.max_new, r.out = fake, 5, 4, ctypes.cast(out, ctypes.c_void_p)
+    reqs[1].P = 17  # beyond prefix_cap
+    assert _err(q, q.ocrdec_run_round, m, st, reqs, stream=0) == q.OCRDEC_ERR_INVALID_ARG
+    assert "prefix_cap" in q.ocrdec_last_error()
+    reqs[1].P = 5
+    reqs[1].max_new = 0
+    assert _err(q, q.ocrdec_run_round, m, st, reqs, stream=0) == q.OCRDEC_ERR_INVALID_ARG
+    reqs[1].max_new = 4
+    reqs[1].tokens = None
+    assert _err(q, q.ocrdec_run_round, m, st, reqs, stream=0) == q.OCRDEC_ERR_INVALID_ARG

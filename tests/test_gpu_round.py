@@ -1,0 +1,111 @@
+"""GPU parity of ocrdec_run_round: a queue of requests served by fewer rows
+than requests, each request's tokens against the oracle's greedy generation
+of that request alone (rows are independent).  A token may differ only where
+the oracle's own top-2 gap is below the near-tie threshold; the sequences
+are compared up to that point."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from tests.gpu_util import NEAR_TIE, f16_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    import torch
+    assert torch.cuda.is_available()
+    import quantized_decode_step_amd as qd
+    return qd
+
+
+def small_dims(**kw):
+    d = synth.Dims(hidden=256, n_heads=2, head_dim=128, n_layers=3, n_dense=1, dense_ff=512, n_experts=16, top_k=6,
+                   n_shared=2, expert_ff=128, vocab=1000, prefix_cap=64, ring_cap=8)
+    for k_, v_ in kw.items():
+        setattr(d, k_, v_)
+    return d
+
+
+def _compare(got, ref, gaps, what):
+    for i, (g, r) in enumerate(zip(got, ref)):
+        if g != r:
+            assert gaps[i] < NEAR_TIE, "%s token %d: %d vs oracle %d (oracle gap %.3g)" % (what, i, g, r, gaps[i])
+            print("[near-tie]", what, i, gaps[i], flush=True)
+            return False
+    assert len(got) == len(ref), "%s: %d tokens vs oracle %d" % (what, len(got), len(ref))
+    return True
+
+
+def run_round(q, d, seed, Ps, max_new, rows, use_features=(), eos_pick=(), keep_eos=False):
+    import torch
+    print("[case] round rows", rows, "P", Ps, "max_new", max_new, "seed", seed, flush=True)
+    model = synth.make_model(d, seed)
+    prompts = [synth.uniform_i32(synth.stream_id(seed, "prompt", i), (P,), 0, d.vocab) for i, P in enumerate(Ps)]
+    feats = [synth.normal_f16(synth.stream_id(seed, "feat", i), (P, d.hidden)) for i, P in enumerate(Ps)]
+    # the oracle, request by request, without EOS: pick EOS tokens from its sequences
+    full = []
+    for i, P in enumerate(Ps):
+        emb = feats[i].astype(np.float64) if i in use_features else None
+        full.append(O.generate(model, P, tok=None if emb is not None else prompts[i], emb=emb, max_new=max_new[i]))
+    eos = sorted(set(full[i][0][k] for i, k in eos_pick))
+    refs = []
+    for i, P in enumerate(Ps):
+        emb = feats[i].astype(np.float64) if i in use_features else None
+        refs.append(O.generate(model, P, tok=None if emb is not None else prompts[i], emb=emb, max_new=max_new[i],
+                               eos=eos, keep_eos=keep_eos))
+    st = synth.make_state(d, seed, [0] * rows, [0] * rows)
+    dm = q.DeviceModel(model)
+    ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+    dm.bind_caches(ds.k_cache, ds.v_cache)
+    keep = []
+    reqs = (q.Request * len(Ps))()
+    outs = []
+    for i, P in enumerate(Ps):
+        if i in use_features:
+            f = f16_tensor(feats[i])
+            keep.append(f)
+            reqs[i].tokens, reqs[i].features = None, f.data_ptr()
+        else:
+            tk = torch.from_numpy(prompts[i].astype(np.int32)).cuda()
+            keep.append(tk)
+            reqs[i].tokens, reqs[i].features = tk.data_ptr(), None
+        reqs[i].P, reqs[i].max_new = P, max_new[i]
+        o = (ctypes.c_int32 * max_new[i])()
+        outs.append(o)
+        reqs[i].out = ctypes.cast(o, ctypes.c_void_p)
+    wsb = q.ocrdec_round_workspace_bytes(dm.desc, ds.desc, max(Ps))
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    q.ocrdec_run_round(dm.desc, ds.desc, reqs, eos=eos, keep_eos=keep_eos, ws=ws, ws_bytes=wsb)
+    torch.cuda.synchronize()
+    for i in range(len(Ps)):
+        got = list(outs[i][:reqs[i].n_out])
+        ref, stop, gaps = refs[i]
+        if _compare(got, ref, gaps, "request %d" % i):
+            assert reqs[i].stop == stop, "request %d: stop %d vs oracle %d" % (i, reqs[i].stop, stop)
+    return refs, eos
+
+
+def test_round_queue_longer_than_rows(q):
+    """Five requests on three rows: rows are reused as requests finish; two
+    EOS tokens taken from the oracle's sequences cut some requests short."""
+    d = small_dims()
+    run_round(q, d, 701, Ps=[5, 23, 40, 9, 31], max_new=[6, 1, 8, 4, 7], rows=3, eos_pick=[(2, 3), (4, 2)])
+
+
+def test_round_keep_eos_and_features(q):
+    d = small_dims()
+    run_round(q, d, 702, Ps=[12, 7, 30, 18], max_new=[5, 9, 3, 6], rows=2, use_features=(1, 3),
+              eos_pick=[(1, 4)], keep_eos=True)
+
+
+def test_round_one_row_first_token_eos(q):
+    """One row serves three requests in turn; the second request's first
+    token is an EOS token, so it ends at its prompt pass."""
+    d = small_dims()
+    refs, eos = run_round(q, d, 703, Ps=[10, 14, 6], max_new=[4, 5, 3], rows=1, eos_pick=[(1, 0)])
+    assert refs[1][0] == [] and refs[1][1] == 1
