@@ -78,6 +78,7 @@ def parse():
                          "prompt: only the prompt pass of the 12-layer model (1100 positions)")
     ap.add_argument("--no-prompt", action="store_true", help="skip the prompt-pass line")
     ap.add_argument("--no-int8kv", action="store_true", help="skip the INT8 KV cache runs")
+    ap.add_argument("--no-round", action="store_true", help="skip the round-scheduler line")
     ap.add_argument("--prompt-iters", type=int, default=5)
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--copy-mb", type=int, default=512, help="size of the calibration copy in --mode lm")
@@ -268,6 +269,9 @@ def main():
     # ---- the prompt pass of the same 12-layer model (1100 positions), beside the decode metric
     prompt = None if args.no_prompt else prompt_pass(args, q, torch, dev, stream, dm, d)
 
+    # ---- a queue of requests through the round scheduler
+    round_line = None if args.no_round else round_queue(args, q, torch, dev, stream, dm, d)
+
     # ---- CPU oracle baseline on a bounded sample (1 row of the same workload)
     cpu = None
     if not args.no_cpu:
@@ -310,6 +314,7 @@ def main():
         "prefill_moe": prefill,
         "prompt_pass": prompt,
         "int8_kv": int8_kv,
+        "round": round_line,
         "setup_s": round(t_build, 1),
     }
     print(json.dumps(line), flush=True)
@@ -317,6 +322,7 @@ def main():
 
 PREFILL_SEED = 1005
 PROMPT_SEED = 1006
+ROUND_SEED = 1007
 PREFILL_TOKENS = 2048
 
 
@@ -401,6 +407,43 @@ def prompt_pass(args, q, torch, dev, stream, dm, d):
             "positions": P, "ms": round(ms, 3), "positions_per_s": round(P / (ms * 1e-3), 1),
             "gflop": round(flops / 1e9, 1), "tflops": round(tf, 1), "bound": "mfma", "peak_TFLOPs": 2500.0,
             "frac_of_fp16_mfma_peak": round(tf / 2500.0, 4)}
+
+
+def round_queue(args, q, torch, dev, stream, dm, d, n_req: int = 48, rows: int = 24, P: int = 1100,
+                max_new: int = 64):
+    """A queue of requests through ocrdec_run_round: 48 requests of 1100
+    positions of fp16 input features each, 64 generated tokens each (no EOS),
+    served by 24 rows.  Reports generated tokens/s and requests/s of the whole
+    queue (prompt passes and decode steps, one host read of the tokens per
+    step)."""
+    import ctypes
+    import synth
+    st = synth.make_state(d, ROUND_SEED, [0] * rows, [0] * rows)
+    ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+    dm.bind_caches(ds.k_cache, ds.v_cache)
+    feats = torch.from_numpy(synth.normal_f16(synth.stream_id(ROUND_SEED, "features"), (8, P, d.hidden))
+                             .view(np.int16)).to(dev)
+    reqs = (q.Request * n_req)()
+    outs = []
+    for i in range(n_req):
+        reqs[i].tokens, reqs[i].features = None, feats[i % 8].data_ptr()
+        reqs[i].P, reqs[i].max_new = P, max_new
+        o = (ctypes.c_int32 * max_new)()
+        outs.append(o)
+        reqs[i].out = ctypes.cast(o, ctypes.c_void_p)
+    wsb = q.ocrdec_round_workspace_bytes(dm.desc, ds.desc, P)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    q.ocrdec_run_round(dm.desc, ds.desc, reqs, ws=ws, ws_bytes=wsb, stream=stream)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    q.ocrdec_run_round(dm.desc, ds.desc, reqs, ws=ws, ws_bytes=wsb, stream=stream)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    gen = sum(r.n_out for r in reqs)
+    assert gen == n_req * max_new
+    return {"workload": "%d requests x (%d positions of fp16 input features, %d generated tokens) on %d rows of the "
+                        "12-layer decoder, no EOS" % (n_req, P, max_new, rows),
+            "s": round(dt, 3), "generated_tokens_per_s": round(gen / dt, 1), "requests_per_s": round(n_req / dt, 2)}
 
 
 def lm_only(args, dm, d, q, torch, dev, stream):
