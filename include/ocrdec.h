@@ -377,6 +377,26 @@ ocrdec_status ocrdec_prefill(const ocrdec_model* m, const ocrdec_state* st, int3
                              int32_t* tok_out, float* hidden, const ocrdec_step_capture* capture, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* The prompt passes of n rows at once (the same computation as ocrdec_prefill
+ * for each; batching lets the projections and experts of all the prompts
+ * share each weight read).  Sequence i has P[i] positions and goes to row
+ * rows[i] (distinct rows); the inputs are packed one sequence after
+ * another: tok int32 [sum P] or emb fp16 [sum P][hidden].
+ *   n            1 .. 32; sum of P at most 65536
+ *   rows, P      HOST int32 [n]
+ *   forced_topk  int32 [n_moe_layers][sum P][top_k] or NULL (packed positions)
+ *   tok_out      int32 [n]: the argmax at each sequence's last position
+ *   hidden       fp32 [sum P][hidden] or NULL
+ *   capture      topk_idx / topk_w [n_moe_layers][sum P][top_k], lm_top2 [n][2]
+ * Workspace: ocrdec_prefill_batch_workspace_bytes(m, st, n, rows, P).
+ * Errors: as ocrdec_prefill. */
+ocrdec_status ocrdec_prefill_batch_workspace_bytes(const ocrdec_model* m, const ocrdec_state* st, int32_t n,
+                                                   const int32_t* rows, const int32_t* P, size_t* bytes);
+ocrdec_status ocrdec_prefill_batch(const ocrdec_model* m, const ocrdec_state* st, int32_t n, const int32_t* rows,
+                                   const int32_t* P, const int32_t* tok, const uint16_t* emb,
+                                   const int32_t* forced_topk, int32_t* tok_out, float* hidden,
+                                   const ocrdec_step_capture* capture, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* ocrdec_run_round: a queue of requests decoded together                    */
 /* ------------------------------------------------------------------------ */

@@ -107,6 +107,9 @@ _lib.ocrdec_moe_layer.argtypes = [_P(MoeWeights), _i32, _vp, _vp, _i32, _vp, _P(
 _lib.ocrdec_step_workspace_bytes.argtypes = [_P(ModelDesc), _P(StateDesc), _P(_sz)]
 _lib.ocrdec_decode_step.argtypes = [_P(ModelDesc), _P(StateDesc), _vp, _vp, _vp, _vp, _P(StepCapture), _vp, _sz, _vp]
 _lib.ocrdec_prefill_workspace_bytes.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _P(_sz)]
+_lib.ocrdec_prefill_batch_workspace_bytes.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _vp, _vp, _P(_sz)]
+_lib.ocrdec_prefill_batch.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _P(StepCapture), _vp, _sz, _vp]
 _lib.ocrdec_round_workspace_bytes.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _P(_sz)]
 _lib.ocrdec_run_round.argtypes = [_P(ModelDesc), _P(StateDesc), _vp, _i32, _vp, _i32, _i32, _vp, _sz, _vp]
 _lib.ocrdec_prefill.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _P(StepCapture),
@@ -115,14 +118,15 @@ for _fn in ("ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack", "ocrdec_gemv_
             "ocrdec_lm_argmax", "ocrdec_attn_workspace_bytes",
             "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes", "ocrdec_moe_layer", "ocrdec_step_workspace_bytes",
             "ocrdec_decode_step", "ocrdec_prefill_workspace_bytes", "ocrdec_prefill", "ocrdec_round_workspace_bytes",
-            "ocrdec_run_round"):
+            "ocrdec_run_round", "ocrdec_prefill_batch_workspace_bytes", "ocrdec_prefill_batch"):
     getattr(_lib, _fn).restype = ctypes.c_int
 
 EXPORTED = ["ocrdec_last_error", "ocrdec_version", "ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack",
             "ocrdec_gemv_q", "ocrdec_lm_argmax_workspace_bytes", "ocrdec_lm_argmax", "ocrdec_attn_workspace_bytes",
             "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes",
             "ocrdec_moe_layer", "ocrdec_step_workspace_bytes", "ocrdec_decode_step",
-            "ocrdec_prefill_workspace_bytes", "ocrdec_prefill", "ocrdec_round_workspace_bytes", "ocrdec_run_round"]
+            "ocrdec_prefill_workspace_bytes", "ocrdec_prefill", "ocrdec_round_workspace_bytes", "ocrdec_run_round",
+            "ocrdec_prefill_batch_workspace_bytes", "ocrdec_prefill_batch"]
 
 
 def _ptr(t) -> int | None:
@@ -244,6 +248,27 @@ def ocrdec_run_round(m: ModelDesc, st: StateDesc, reqs, eos=(), keep_eos: bool =
     _check(_lib.ocrdec_run_round(ctypes.byref(m), ctypes.byref(st), ctypes.cast(reqs, _vp), len(reqs),
                                  ctypes.cast(eos_arr, _vp), len(eos), int(keep_eos), _ptr(ws), ws_bytes,
                                  _stream(stream)))
+
+
+def _i32_array(v):
+    return (ctypes.c_int32 * len(v))(*[int(x) for x in v])
+
+
+def ocrdec_prefill_batch_workspace_bytes(m: ModelDesc, st: StateDesc, rows, P) -> int:
+    b = _sz()
+    r, p = _i32_array(rows), _i32_array(P)
+    _check(_lib.ocrdec_prefill_batch_workspace_bytes(ctypes.byref(m), ctypes.byref(st), len(P), ctypes.cast(r, _vp),
+                                                     ctypes.cast(p, _vp), ctypes.byref(b)))
+    return b.value
+
+
+def ocrdec_prefill_batch(m: ModelDesc, st: StateDesc, rows, P, tok=None, emb=None, forced_topk=None, tok_out=None,
+                         hidden=None, capture: StepCapture | None = None, ws=None, ws_bytes: int = 0, stream=None):
+    r, p = _i32_array(rows), _i32_array(P)
+    _check(_lib.ocrdec_prefill_batch(ctypes.byref(m), ctypes.byref(st), len(P), ctypes.cast(r, _vp),
+                                     ctypes.cast(p, _vp), _ptr(tok), _ptr(emb), _ptr(forced_topk), _ptr(tok_out),
+                                     _ptr(hidden), ctypes.byref(capture) if capture is not None else None, _ptr(ws),
+                                     ws_bytes, _stream(stream)))
 
 
 def ocrdec_prefill_workspace_bytes(m: ModelDesc, st: StateDesc, P: int) -> int:

@@ -16,6 +16,7 @@
 // it covers 8 keys.
 #include "attn.hpp"
 
+#include <algorithm>
 #include <cmath>
 
 namespace ocrdec {
@@ -395,20 +396,25 @@ void attn_set_rope(AttnParams& p, float theta) {
 
 template <int D>
 __global__ __launch_bounds__(64) void prefill_rope_kernel(PrefillAttnParams p) {
-    const int pos = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
+    const int at = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
     if (i >= D / 2) return;
+    // the sequence of packed position `at` (sequences are packed in order)
+    int s = 0;
+    while (s + 1 < p.n_seq && at >= p.seq_off[s + 1]) ++s;
+    const int pos = at - p.seq_off[s];
+    const int64_t crow = ((int64_t)p.seq_row[s] * p.n_heads + h) * p.cache_cap;
     const int HD = p.n_heads * D;
-    const float* r = p.qkv + (int64_t)pos * p.ld_qkv;
+    const float* r = p.qkv + (int64_t)at * p.ld_qkv;
     float y1, y2;
     rope_pair(r[h * D + i], r[h * D + i + D / 2], p.inv_freq[i], pos, y1, y2);
-    uint16_t* qo = p.q + (int64_t)pos * HD + h * D;
+    uint16_t* qo = p.q + (int64_t)at * HD + h * D;
     qo[i] = f2h(y1);
     qo[i + D / 2] = f2h(y2);
     rope_pair(r[HD + h * D + i], r[HD + h * D + i + D / 2], p.inv_freq[i], pos, y1, y2);
-    uint16_t* kc = p.k_cache + ((int64_t)h * p.cache_cap + pos) * D;
+    uint16_t* kc = p.k_cache + (crow + pos) * D;
     kc[i] = f2h(y1);
     kc[i + D / 2] = f2h(y2);
-    uint16_t* vc = p.v_cache + ((int64_t)h * p.cache_cap + pos) * D;
+    uint16_t* vc = p.v_cache + (crow + pos) * D;
     vc[i] = f2h(r[2 * HD + h * D + i]);
     vc[i + D / 2] = f2h(r[2 * HD + h * D + i + D / 2]);
 }
@@ -427,24 +433,29 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
     constexpr int NPC = PKB * D / 8 / 256;     // 16-byte pieces per thread per block, K and V each
     __shared__ __align__(16) uint16_t k_s[PKB * KLD];
     __shared__ __align__(16) uint16_t vt_s[D * VLD];
-    // workgroup (query block qb, chunk c of its key blocks, head h); query
-    // block qb needs key blocks 0..qb, taken PKC at a time
+    // workgroup (query block qb, chunk c of its key blocks, head h, sequence
+    // sq); query block qb needs key blocks 0..qb, taken PKC at a time
     const int nch = (int)gridDim.x / p.n_qb;  // chunk slots per query block
-    const int qb = p.n_qb - 1 - (int)blockIdx.x / nch, c = (int)blockIdx.x % nch, h = blockIdx.y;
+    const int sq = blockIdx.z, P = p.seq_len[sq], n_qb = (P + PQB - 1) / PQB;
+    const int slot = (int)blockIdx.x / nch, c = (int)blockIdx.x % nch, h = blockIdx.y;
+    if (slot >= n_qb) return;  // uniform: a shorter sequence
+    const int qb = n_qb - 1 - slot;
     const int n_c = (qb + PKC) / PKC;
     if (c >= n_c) return;  // uniform: this query block has fewer chunks
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
-    const int P = p.P, HD = p.n_heads * D;
+    const int HD = p.n_heads * D;
+    const int64_t at0 = p.seq_off[sq];  // packed position of the sequence's first token
     const int q0 = qb * PQB;
     const int qw = q0 + 16 * wave + c16;  // this lane's query (an MFMA column)
     const int kb0 = c * PKC, nkb = min(kb0 + PKC, qb + 1);
-    const uint16_t* kbase = p.k_cache + (int64_t)h * p.cache_cap * D;
-    const uint16_t* vbase = p.v_cache + (int64_t)h * p.cache_cap * D;
+    const int64_t crow = ((int64_t)p.seq_row[sq] * p.n_heads + h) * p.cache_cap;
+    const uint16_t* kbase = p.k_cache + crow * D;
+    const uint16_t* vbase = p.v_cache + crow * D;
 
     // queries (B operand of S^T = K Q^T): step ks holds d = 32 ks + 8 g .. + 7
     half8v qf[KS];
     {
-        const uint16_t* qp = p.q + (int64_t)min(qw, P - 1) * HD + h * D + 8 * g;
+        const uint16_t* qp = p.q + (at0 + min(qw, P - 1)) * HD + h * D + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = bits_to_half8(*(const uint4*)(qp + 32 * ks));
     }
@@ -557,7 +568,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
     if (n_c > 1) {
         // one of several chunks: the unnormalised partial of every lane (its
         // 4 DT outputs, the running max and sum) for the merge kernel
-        float* rec = p.part + ((((int64_t)h * p.n_qb + qb) * nch + c) * 256 + tid) * PREC;
+        float* rec = p.part + (((((int64_t)sq * p.n_heads + h) * p.n_qb + qb) * nch + c) * 256 + tid) * PREC;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) *(float4*)(rec + 4 * dt) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
         rec[32] = m_run;
@@ -566,7 +577,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
     }
     if (qw < P) {
         const float inv = 1.0f / l_run;
-        uint16_t* op = p.out + (int64_t)qw * p.ld_out + h * D;
+        uint16_t* op = p.out + (at0 + qw) * p.ld_out + h * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const uint32_t lo = (uint32_t)f2h(o[dt][0] * inv) | ((uint32_t)f2h(o[dt][1] * inv) << 16);
@@ -583,13 +594,13 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
 template <int D>
 __global__ __launch_bounds__(256) void attn_prefill_merge_kernel(PrefillAttnParams p, int nch) {
     constexpr int DT = D / 16;
-    const int qb = blockIdx.x, h = blockIdx.y;
+    const int qb = blockIdx.x, h = blockIdx.y, sq = blockIdx.z, P = p.seq_len[sq];
     const int n_c = (qb + PKC) / PKC;
-    if (n_c <= 1) return;
+    if (n_c <= 1 || qb * PQB >= P) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
     const int qw = qb * PQB + 16 * wave + c16;
-    if (qw >= p.P) return;
-    const float* base = p.part + (((int64_t)h * p.n_qb + qb) * nch * 256 + tid) * PREC;
+    if (qw >= P) return;
+    const float* base = p.part + ((((int64_t)sq * p.n_heads + h) * p.n_qb + qb) * nch * 256 + tid) * PREC;
     float M = -INFINITY;
     for (int c = 0; c < n_c; ++c) M = fmaxf(M, base[(int64_t)c * 256 * PREC + 32]);
     float L = 0.f;
@@ -607,7 +618,7 @@ __global__ __launch_bounds__(256) void attn_prefill_merge_kernel(PrefillAttnPara
         }
     }
     const float inv = 1.0f / L;
-    uint16_t* op = p.out + (int64_t)qw * p.ld_out + h * D;
+    uint16_t* op = p.out + ((int64_t)p.seq_off[sq] + qw) * p.ld_out + h * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
         const uint32_t lo = (uint32_t)f2h(o[dt].x * inv) | ((uint32_t)f2h(o[dt].y * inv) << 16);
@@ -618,9 +629,9 @@ __global__ __launch_bounds__(256) void attn_prefill_merge_kernel(PrefillAttnPara
 
 int prefill_chunks(int P) { return ((P + PQB - 1) / PQB + PKC - 1) / PKC; }
 
-size_t prefill_attn_part_bytes(int P, int n_heads) {
-    const int n_qb = (P + PQB - 1) / PQB;
-    return align256((size_t)n_heads * n_qb * prefill_chunks(P) * 256 * PREC * sizeof(float));
+size_t prefill_attn_part_bytes(int n_seq, int max_len, int n_heads) {
+    const int n_qb = (max_len + PQB - 1) / PQB;
+    return align256((size_t)n_seq * n_heads * n_qb * prefill_chunks(max_len) * 256 * PREC * sizeof(float));
 }
 
 void prefill_set_rope(PrefillAttnParams& p, float theta) {
@@ -630,9 +641,11 @@ void prefill_set_rope(PrefillAttnParams& p, float theta) {
 
 void launch_attn_prefill(const PrefillAttnParams& p0, hipStream_t s) {
     PrefillAttnParams p = p0;
-    p.n_qb = (p.P + PQB - 1) / PQB;
-    const int nch = prefill_chunks(p.P);
-    const dim3 gr(p.P, p.n_heads), ga(p.n_qb * nch, p.n_heads), gm(p.n_qb, p.n_heads);
+    int max_len = 1;
+    for (int i = 0; i < p.n_seq; ++i) max_len = std::max(max_len, p.seq_len[i]);
+    p.n_qb = (max_len + PQB - 1) / PQB;
+    const int nch = prefill_chunks(max_len);
+    const dim3 gr(p.P, p.n_heads), ga(p.n_qb * nch, p.n_heads, p.n_seq), gm(p.n_qb, p.n_heads, p.n_seq);
     if (p.head_dim == 128) {
         hipLaunchKernelGGL(prefill_rope_kernel<128>, gr, dim3(64), 0, s, p);
         hipLaunchKernelGGL(attn_prefill_kernel<128>, ga, dim3(256), 0, s, p);

@@ -25,24 +25,30 @@ struct AttnParams {
     uint16_t* v_scale;
 };
 
-// Prompt pass (prefill) of one row: P positions, causal attention.
+// Prompt passes (prefill): n_seq sequences packed one after another (P
+// positions in all), causal attention within each sequence.
+constexpr int PREFILL_MAX_SEQ = 32;
 struct PrefillAttnParams {
     int P, n_heads, head_dim;
     const float* qkv;    // [P][ld_qkv] fp32 projections (q | k | v)
     int64_t ld_qkv;
     uint16_t* q;         // [P][n_heads * head_dim] fp16 scratch: the rotated queries
-    uint16_t* k_cache;   // this row's caches [n_heads][cache_cap][head_dim]; indices 0..P-1 are written
-    uint16_t* v_cache;
+    uint16_t* k_cache;   // the layer's caches [rows][n_heads][cache_cap][head_dim]; sequence s writes
+    uint16_t* v_cache;   //   indices 0..len-1 of row seq_row[s]
     int cache_cap;
     float scale;
     double inv_freq[64];
     uint16_t* out;       // [P][ld_out] fp16 attention output
     int64_t ld_out;
-    float* part;         // prefill_attn_part_bytes(P, n_heads): partials of split windows
-    int n_qb;            // query blocks (set by the launcher)
+    float* part;         // prefill_attn_part_bytes(...): partials of split windows
+    int n_qb;            // query blocks of the longest sequence (set by the launcher)
+    int n_seq;
+    int seq_off[PREFILL_MAX_SEQ];  // first packed position of each sequence
+    int seq_len[PREFILL_MAX_SEQ];
+    int seq_row[PREFILL_MAX_SEQ];  // its cache row
 };
 
-size_t prefill_attn_part_bytes(int P, int n_heads);
+size_t prefill_attn_part_bytes(int n_seq, int max_len, int n_heads);
 void prefill_set_rope(PrefillAttnParams& p, float theta);
 void launch_attn_prefill(const PrefillAttnParams& p, hipStream_t s);
 

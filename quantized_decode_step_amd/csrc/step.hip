@@ -125,6 +125,16 @@ __global__ __launch_bounds__(64) void resid_norm_kernel(float* h, const float* y
     wave_rmsnorm_row(h + (int64_t)r * H, gamma, H, eps, x + (int64_t)r * H);
 }
 
+// dst[i] = src[idx[i]]: rows of H halves (H % 8 == 0), one workgroup per row.
+struct RowList {
+    int idx[PREFILL_MAX_SEQ];
+};
+__global__ __launch_bounds__(64) void gather_rows_kernel(const uint16_t* src, uint16_t* dst, int H, RowList rl) {
+    const uint4* s = (const uint4*)(src + (int64_t)rl.idx[blockIdx.x] * H);
+    uint4* d = (uint4*)(dst + (int64_t)blockIdx.x * H);
+    for (int c = threadIdx.x; c < H / 8; c += blockDim.x) d[c] = s[c];
+}
+
 // x[r] = fp16(RMSNorm(h[r]) * gamma): one wavefront per row.
 __global__ __launch_bounds__(64) void norm_kernel(const float* h, const uint16_t* gamma, int H, float eps,
                                                   uint16_t* x) {
@@ -197,11 +207,13 @@ struct PrefillWs {
     uint16_t* a;
     float* lm_part;
     float* attn_part;
+    uint16_t* x_last;  // [n_seq][H] the last position of every sequence (LM-head input)
     MoeWs moe;
     size_t bytes;
 };
 
-PrefillWs carve_prefill(void* ws, const ocrdec_model* m, int P) {
+// P: packed positions of all sequences; n_seq sequences, the longest max_len
+PrefillWs carve_prefill(void* ws, const ocrdec_model* m, int P, int n_seq, int max_len) {
     Carve cv(ws);
     PrefillWs w;
     const int H = m->hidden, HD = m->n_heads * m->head_dim;
@@ -218,8 +230,9 @@ PrefillWs carve_prefill(void* ws, const ocrdec_model* m, int P) {
     w.o = cv.take<uint16_t>((size_t)P * HD);
     w.y = cv.take<float>((size_t)P * H);
     w.a = cv.take<uint16_t>((size_t)P * std::max(dense_ff, 1));
-    w.lm_part = cv.take<float>(argmax_ws_bytes(std::max(lm_grid(m, 1), 1), 1) / sizeof(float));
-    w.attn_part = cv.take<float>(prefill_attn_part_bytes(P, m->n_heads) / sizeof(float));
+    w.lm_part = cv.take<float>(argmax_ws_bytes(std::max(lm_grid(m, n_seq), 1), n_seq) / sizeof(float));
+    w.attn_part = cv.take<float>(prefill_attn_part_bytes(n_seq, max_len, m->n_heads) / sizeof(float));
+    w.x_last = cv.take<uint16_t>((size_t)n_seq * H);
     if (moe) {
         MoeWs probe = carve_moe(nullptr, P, moe);
         char* base = (char*)cv.take<char>(probe.bytes);
@@ -505,46 +518,73 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     return launch_status("ocrdec_decode_step");
 }
 
-extern "C" ocrdec_status ocrdec_prefill_workspace_bytes(const ocrdec_model* m, const ocrdec_state* st, int32_t P,
-                                                        size_t* bytes) {
-    OCR_CHECK_ARG(P >= 1 && P <= 65536, "P must be in [1, 65536]");
-    ocrdec_status s0 = check_step(m, st, P);
+namespace {
+
+// Validation of a batch of prompt passes; fills the packed offsets.
+ocrdec_status check_prefill(const ocrdec_model* m, const ocrdec_state* st, int n, const int32_t* rows,
+                            const int32_t* P, int* total, int* max_len) {
+    OCR_CHECK_ARG(n >= 1 && n <= PREFILL_MAX_SEQ, "n must be in [1, 32]");
+    OCR_CHECK_ARG(rows && P, "rows and P must be non-NULL");
+    OCR_CHECK_ARG(m && st, "model and state must be non-NULL");
+    int64_t T = 0;
+    *max_len = 1;
+    for (int i = 0; i < n; ++i) {
+        const std::string tag = "sequence " + std::to_string(i) + ": ";
+        OCR_CHECK_ARG(P[i] >= 1 && P[i] <= st->prefix_cap, tag + "P must be in [1, prefix_cap] (the prompt fills the prefix region)");
+        OCR_CHECK_ARG(rows[i] >= 0 && rows[i] < st->rows, tag + "row must be in [0, rows)");
+        for (int j = 0; j < i; ++j) OCR_CHECK_ARG(rows[j] != rows[i], tag + "rows must be distinct");
+        T += P[i];
+        *max_len = std::max(*max_len, (int)P[i]);
+    }
+    OCR_CHECK_ARG(T <= 65536, "the positions of all sequences must total at most 65536");
+    *total = (int)T;
+    ocrdec_status s0 = check_step(m, st, *total);
     if (s0 != OCRDEC_OK) return s0;
-    OCR_CHECK_ARG(bytes, "bytes is NULL");
-    *bytes = carve_prefill(nullptr, m, P).bytes;
+    OCR_CHECK_ARG(st->prefix_cap + st->ring_cap <= (1 << 16), "prefix_cap + ring_cap must be <= 65536");
+    for (int l = 0; l < m->n_layers; ++l)
+        if (m->layers[l].k_scale) return fail(OCRDEC_ERR_UNSUPPORTED, "the prompt pass writes fp16 caches only");
     return OCRDEC_OK;
 }
 
-extern "C" ocrdec_status ocrdec_prefill(const ocrdec_model* m, const ocrdec_state* st, int32_t row, int32_t P,
-                                        const int32_t* tok, const uint16_t* emb, const int32_t* forced_topk,
-                                        int32_t* tok_out, float* hidden, const ocrdec_step_capture* cap, void* ws,
-                                        size_t ws_bytes, void* stream) {
-    OCR_CHECK_ARG(P >= 1 && P <= 65536, "P must be in [1, 65536]");
-    ocrdec_status s0 = check_step(m, st, P);
+}  // namespace
+
+extern "C" ocrdec_status ocrdec_prefill_batch_workspace_bytes(const ocrdec_model* m, const ocrdec_state* st,
+                                                              int32_t n, const int32_t* rows, const int32_t* P,
+                                                              size_t* bytes) {
+    int T = 0, max_len = 1;
+    ocrdec_status s0 = check_prefill(m, st, n, rows, P, &T, &max_len);
     if (s0 != OCRDEC_OK) return s0;
-    OCR_CHECK_ARG(row >= 0 && row < st->rows, "row must be in [0, rows)");
-    OCR_CHECK_ARG(P <= st->prefix_cap, "P must be <= prefix_cap (the prompt fills the prefix region)");
+    OCR_CHECK_ARG(bytes, "bytes is NULL");
+    *bytes = carve_prefill(nullptr, m, T, n, max_len).bytes;
+    return OCRDEC_OK;
+}
+
+extern "C" ocrdec_status ocrdec_prefill_batch(const ocrdec_model* m, const ocrdec_state* st, int32_t n,
+                                              const int32_t* rows, const int32_t* P, const int32_t* tok,
+                                              const uint16_t* emb, const int32_t* forced_topk, int32_t* tok_out,
+                                              float* hidden, const ocrdec_step_capture* cap, void* ws,
+                                              size_t ws_bytes, void* stream) {
+    int T = 0, max_len = 1;
+    ocrdec_status s0 = check_prefill(m, st, n, rows, P, &T, &max_len);
+    if (s0 != OCRDEC_OK) return s0;
     OCR_CHECK_ARG(tok || emb, "either tok or emb must be given");
     OCR_CHECK_ARG(!tok || m->embed || m->embed_q.data, "tok needs an embedding table");
     OCR_CHECK_ARG(!emb || ((uintptr_t)emb & 7) == 0, "emb must be 8-byte aligned");
-    for (int l = 0; l < m->n_layers; ++l)
-        if (m->layers[l].k_scale) return fail(OCRDEC_ERR_UNSUPPORTED, "the prompt pass writes fp16 caches only");
     const int H = m->hidden, HD = m->n_heads * m->head_dim, D = m->head_dim;
     const int cache_cap = st->prefix_cap + st->ring_cap;
-    OCR_CHECK_ARG(cache_cap <= (1 << 16), "prefix_cap + ring_cap must be <= 65536");
-    const size_t need = carve_prefill(nullptr, m, P).bytes;
+    const size_t need = carve_prefill(nullptr, m, T, n, max_len).bytes;
     if (!ws || ws_bytes < need)
         return fail(OCRDEC_ERR_WORKSPACE, "prefill workspace: need " + std::to_string(need) + " bytes, got " +
                                               std::to_string(ws ? ws_bytes : 0));
     hipStream_t s = (hipStream_t)stream;
-    PrefillWs w = carve_prefill(ws, m, P);
+    PrefillWs w = carve_prefill(ws, m, T, n, max_len);
     // h = the input rows, x = fp16(RMSNorm(h) * attn_norm of layer 0)
     if (tok && !m->embed) {
         const uint8_t* tq = (const uint8_t*)m->embed_q.data;
         const int64_t nch = n_chunks(m->embed_q.fmt, H);
 #define OCR_EQ(F_)                                                                                                 \
     case F_:                                                                                                       \
-        hipLaunchKernelGGL(embed_q_norm_kernel<F_>, dim3(P), dim3(64), 0, s, tok, tq, m->vocab, nch, w.h,          \
+        hipLaunchKernelGGL(embed_q_norm_kernel<F_>, dim3(T), dim3(64), 0, s, tok, tq, m->vocab, nch, w.h,          \
                            m->layers[0].attn_norm, H, m->norm_eps, w.x);                                           \
         break;
         switch (m->embed_q.fmt) {
@@ -555,11 +595,11 @@ extern "C" ocrdec_status ocrdec_prefill(const ocrdec_model* m, const ocrdec_stat
         }
 #undef OCR_EQ
     } else {
-        hipLaunchKernelGGL(embed_norm_kernel, dim3(P), dim3(64), 0, s, tok, m->embed, m->vocab, nullptr, w.h,
+        hipLaunchKernelGGL(embed_norm_kernel, dim3(T), dim3(64), 0, s, tok, m->embed, m->vocab, nullptr, w.h,
                            m->layers[0].attn_norm, H, m->norm_eps, w.x, tok ? (const uint16_t*)nullptr : emb);
     }
     PrefillAttnParams ap{};
-    ap.P = P;
+    ap.P = T;
     ap.n_heads = m->n_heads;
     ap.head_dim = D;
     ap.qkv = w.qkv;
@@ -570,51 +610,73 @@ extern "C" ocrdec_status ocrdec_prefill(const ocrdec_model* m, const ocrdec_stat
     ap.out = w.o;
     ap.ld_out = HD;
     ap.part = w.attn_part;
+    ap.n_seq = n;
+    RowList last{};
+    for (int i = 0, off = 0; i < n; off += P[i], ++i) {
+        ap.seq_off[i] = off;
+        ap.seq_len[i] = P[i];
+        ap.seq_row[i] = rows[i];
+        last.idx[i] = off + P[i] - 1;
+    }
     prefill_set_rope(ap, m->rope_theta);
-    const int64_t row_off = (int64_t)row * m->n_heads * cache_cap * D;
     int moe_l = 0;
     for (int l = 0; l < m->n_layers; ++l) {
         const ocrdec_layer& L = m->layers[l];
         const uint16_t* next_norm = (l + 1 < m->n_layers) ? m->layers[l + 1].attn_norm : m->final_norm;
         if (!next_norm) next_norm = L.attn_norm;  // no LM head: the last norm is not used
-        prefill_gemm(L.wqkv, false, P, w.x, H, w.qkv, 3 * HD, s);
-        ap.k_cache = L.k_cache + row_off;
-        ap.v_cache = L.v_cache + row_off;
+        prefill_gemm(L.wqkv, false, T, w.x, H, w.qkv, 3 * HD, s);
+        ap.k_cache = L.k_cache;
+        ap.v_cache = L.v_cache;
         launch_attn_prefill(ap, s);
-        prefill_gemm(L.wo, false, P, w.o, HD, w.y, H, s);
-        hipLaunchKernelGGL(resid_norm_kernel, dim3(P), dim3(64), 0, s, w.h, w.y, L.ffn_norm, H, m->norm_eps, w.x);
+        prefill_gemm(L.wo, false, T, w.o, HD, w.y, H, s);
+        hipLaunchKernelGGL(resid_norm_kernel, dim3(T), dim3(64), 0, s, w.h, w.y, L.ffn_norm, H, m->norm_eps, w.x);
         if (L.is_moe) {
             const int K = L.moe.top_k;
-            int32_t* ci = cap && cap->topk_idx ? cap->topk_idx + (int64_t)moe_l * P * K : nullptr;
-            float* cw = cap && cap->topk_w ? cap->topk_w + (int64_t)moe_l * P * K : nullptr;
-            const int32_t* fo = forced_topk ? forced_topk + (int64_t)moe_l * P * K : nullptr;
+            int32_t* ci = cap && cap->topk_idx ? cap->topk_idx + (int64_t)moe_l * T * K : nullptr;
+            float* cw = cap && cap->topk_w ? cap->topk_w + (int64_t)moe_l * T * K : nullptr;
+            const int32_t* fo = forced_topk ? forced_topk + (int64_t)moe_l * T * K : nullptr;
             // the combine adds into h and forms the next block's normalised input
-            launch_moe(&L.moe, P, w.x, H, w.h, 1, H, 1, fo, nullptr, ci, cw, w.moe, next_norm, m->norm_eps, w.x, H, s);
+            launch_moe(&L.moe, T, w.x, H, w.h, 1, H, 1, fo, nullptr, ci, cw, w.moe, next_norm, m->norm_eps, w.x, H, s);
             ++moe_l;
         } else {
             const int F = L.dense_ff;
-            prefill_gemm(L.dense_gate_up, true, P, w.x, H, w.a, F, s);
-            prefill_gemm(L.dense_down, false, P, w.a, F, w.y, H, s);
-            hipLaunchKernelGGL(resid_norm_kernel, dim3(P), dim3(64), 0, s, w.h, w.y, next_norm, H, m->norm_eps, w.x);
+            prefill_gemm(L.dense_gate_up, true, T, w.x, H, w.a, F, s);
+            prefill_gemm(L.dense_down, false, T, w.a, F, w.y, H, s);
+            hipLaunchKernelGGL(resid_norm_kernel, dim3(T), dim3(64), 0, s, w.h, w.y, next_norm, H, m->norm_eps, w.x);
         }
     }
     if (hidden) {
-        const int64_t n = (int64_t)P * H;
-        hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 1024)), dim3(256), 0, s,
-                           w.h, hidden, n);
+        const int64_t cnt = (int64_t)T * H;
+        hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)std::min<int64_t>((cnt + 255) / 256, 1024)), dim3(256), 0,
+                           s, w.h, hidden, cnt);
     }
     if (m->lm_head.data && tok_out) {
-        // the last position's x was normalised with final_norm by the last layer
-        const LmPlan lp = plan_lm(m->lm_head.fmt, m->vocab, H, 1);
+        // the last position of every sequence, normalised with final_norm by the last layer
+        hipLaunchKernelGGL(gather_rows_kernel, dim3(n), dim3(64), 0, s, w.x, w.x_last, H, last);
+        const LmPlan lp = plan_lm(m->lm_head.fmt, m->vocab, H, n);
         GemvParams gp{};
         gp.w = (const uint8_t*)m->lm_head.data;
         gp.n = m->vocab;
         gp.k = H;
         gp.nchunks = n_chunks(m->lm_head.fmt, H);
-        gp.xs = XDirect{w.x + (int64_t)(P - 1) * H, H, 1};
+        gp.xs = XDirect{w.x_last, H, n};
         gp.part = w.lm_part;
         launch_lm_argmax(m->lm_head.fmt, lp, gp, s);
-        launch_argmax_final(w.lm_part, lp.grid, 1, tok_out, cap ? cap->lm_top2 : nullptr, nullptr, s);
+        launch_argmax_final(w.lm_part, lp.grid, n, tok_out, cap ? cap->lm_top2 : nullptr, nullptr, s);
     }
-    return launch_status("ocrdec_prefill");
+    return launch_status("ocrdec_prefill_batch");
+}
+
+extern "C" ocrdec_status ocrdec_prefill_workspace_bytes(const ocrdec_model* m, const ocrdec_state* st, int32_t P,
+                                                        size_t* bytes) {
+    const int32_t row = 0;
+    return ocrdec_prefill_batch_workspace_bytes(m, st, 1, &row, &P, bytes);
+}
+
+extern "C" ocrdec_status ocrdec_prefill(const ocrdec_model* m, const ocrdec_state* st, int32_t row, int32_t P,
+                                        const int32_t* tok, const uint16_t* emb, const int32_t* forced_topk,
+                                        int32_t* tok_out, float* hidden, const ocrdec_step_capture* cap, void* ws,
+                                        size_t ws_bytes, void* stream) {
+    return ocrdec_prefill_batch(m, st, 1, &row, &P, tok, emb, forced_topk, tok_out, hidden, cap, ws, ws_bytes,
+                                stream);
 }

@@ -153,3 +153,62 @@ def test_prefill_then_decode(q):
         if g != int(ores.tok[0]):
             assert ores.lm_top2[0, 0] - ores.lm_top2[0, 1] < NEAR_TIE
         tok = ores.tok.astype(np.int32)
+
+
+@pytest.mark.parametrize("Ps,rows_used,use_emb", [([19, 70, 3], [2, 0, 3], False), ([130, 64, 257, 1], [1, 3, 0, 2], True)])
+def test_prefill_batch_matches_each_sequence(q, Ps, rows_used, use_emb):
+    """Several prompt passes in one call: every sequence's caches, residual,
+    routing and first token equal the oracle's prompt pass of that sequence
+    alone (routing teacher-forced, packed in sequence order)."""
+    import torch
+    d = small_dims()
+    seed = 620 + len(Ps)
+    print("[case] prefill batch", Ps, "rows", rows_used, "emb", use_emb, flush=True)
+    model = synth.make_model(d, seed)
+    st = synth.make_state(d, seed, [d.prefix_cap // 2] * 4, [3] * 4)
+    res, toks, embs = [], [], []
+    for i, P in enumerate(Ps):
+        tk = synth.uniform_i32(synth.stream_id(seed, "prompt", i), (P,), 0, d.vocab)
+        em = synth.normal_f16(synth.stream_id(seed, "prompt_emb", i), (P, d.hidden))
+        toks.append(tk)
+        embs.append(em)
+        res.append(O.prefill(model, P, tok=None if use_emb else tk, emb=em.astype(np.float64) if use_emb else None))
+    T = sum(Ps)
+    n_moe = len(res[0].topk_idx)
+    forced = np.concatenate([np.array(r.topk_idx, np.int32) for r in res], axis=1)
+    dm = q.DeviceModel(model)
+    ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+    dm.bind_caches(ds.k_cache, ds.v_cache)
+    wsb = q.ocrdec_prefill_batch_workspace_bytes(dm.desc, ds.desc, rows_used, Ps)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    K = d.top_k
+    cap_idx = torch.zeros((n_moe, T, K), dtype=torch.int32, device="cuda")
+    top2 = torch.zeros((len(Ps), 2), dtype=torch.float32, device="cuda")
+    cap = q.StepCapture(cap_idx.data_ptr(), None, top2.data_ptr())
+    hidden = torch.zeros((T, d.hidden), dtype=torch.float32, device="cuda")
+    tok_out = torch.full((len(Ps),), -1, dtype=torch.int32, device="cuda")
+    tok_t = torch.from_numpy(np.concatenate(toks).astype(np.int32)).cuda()
+    emb_t = f16_tensor(np.concatenate(embs))
+    q.ocrdec_prefill_batch(dm.desc, ds.desc, rows_used, Ps, tok=None if use_emb else tok_t,
+                           emb=emb_t if use_emb else None, forced_topk=torch.from_numpy(forced).cuda(),
+                           tok_out=tok_out, hidden=hidden, capture=cap, ws=ws, ws_bytes=wsb)
+    torch.cuda.synchronize()
+    kc = ds.k_cache.cpu().numpy().view(np.float16)
+    vc = ds.v_cache.cpu().numpy().view(np.float16)
+    hid = hidden.cpu().numpy()
+    g_idx = cap_idx.cpu().numpy()
+    g_tok = tok_out.cpu().numpy()
+    off = 0
+    for i, P in enumerate(Ps):
+        r = rows_used[i]
+        for l in range(d.n_layers):
+            assert_close_f16(kc[l, r, :, :P].astype(np.float64), res[i].k[l], "seq %d layer %d keys" % (i, l))
+            assert_close_f16(vc[l, r, :, :P].astype(np.float64), res[i].v[l], "seq %d layer %d values" % (i, l))
+        assert_close(hid[off:off + P], res[i].hidden, "seq %d hidden" % i)
+        for ml in range(n_moe):
+            for t_ in range(P):
+                if not np.array_equal(g_idx[ml, off + t_], res[i].topk_idx[ml][t_]):
+                    assert res[i].router_gap[ml][t_] < NEAR_TIE
+        if g_tok[i] != int(res[i].tok):
+            assert res[i].lm_top2[0] - res[i].lm_top2[1] < NEAR_TIE
+        off += P
