@@ -418,10 +418,12 @@ typedef struct {
 /* Serves the requests with the rows of `st` (Falcon-OCR card, "How it is
  * meant to be run": rows of one round share each decode step's read of the
  * weights, and merging requests into a round is what makes a queue
- * affordable).  Requests are taken in order; each gets the lowest free row,
- * whose cache prefix its prompt pass (ocrdec_prefill) fills and which gives
- * its first token; then decode steps (ocrdec_decode_step, tokens fed back on
- * the device) advance every occupied row together.  After each step the new
+ * affordable).  Requests are taken in order; each gets the lowest free row.
+ * The prompt passes of the requests admitted together run as one
+ * ocrdec_prefill_batch (token requests and feature requests separately, the
+ * inputs packed into the workspace), which fills the rows' cache prefixes
+ * and gives their first tokens; then decode steps (ocrdec_decode_step,
+ * tokens fed back on the device) advance every occupied row together.  After each step the new
  * tokens are read on the host: a request stops at a token of the EOS set
  * (HunyuanOCR ncnn page, section 3.5: the end token is not handed out; with
  * keep_eos it is appended, for comparisons) or after max_new tokens, and

@@ -5,11 +5,13 @@
 // queue affordable; "HunyuanOCR 的 ncnn 移植" 3.5: generation stops at any
 // token of the EOS set, before the token is handed out).
 //
-// Each request gets a free row (lowest first, requests in order), its prompt
-// pass fills the row's cache prefix and gives the first token, then one
-// decode step over the occupied rows advances all of them together.  After
-// every step the host reads the new tokens and retires the rows that reached
-// an EOS token or their token budget; freed rows take the next requests.
+// Each request gets a free row (lowest first, requests in order); the prompt
+// passes of the requests admitted together run as one batch (their inputs
+// packed into the workspace), fill the rows' cache prefixes and give the
+// first tokens; then one decode step over the occupied rows advances all of
+// them together.  After every step the host reads the new tokens and retires
+// the rows that reached an EOS token or their token budget; freed rows take
+// the next requests.
 #include <algorithm>
 #include <vector>
 
@@ -18,11 +20,48 @@
 namespace ocrdec {
 namespace {
 
-__global__ void admit_row_kernel(int32_t* prefix_len, int32_t* gen_index, int row, int P) {
-    if (threadIdx.x == 0) {
-        prefix_len[row] = P;
-        gen_index[row] = 0;
+struct Admitted {
+    int n;
+    int row[32];
+    int P[32];
+};
+
+// rows admitted together: prefix_len = P, generation index 0, and the first
+// token of sequence i (tok_first[i]) into the row's token slot
+__global__ void admit_rows_kernel(int32_t* prefix_len, int32_t* gen_index, int32_t* tok, const int32_t* tok_first,
+                                  Admitted a) {
+    const int i = threadIdx.x;
+    if (i < a.n) {
+        prefix_len[a.row[i]] = a.P[i];
+        gen_index[a.row[i]] = 0;
+        tok[a.row[i]] = tok_first[i];
     }
+}
+
+// workspace: the row tokens, the first tokens of a batch, the packed prompt
+// tokens and features of up to `rows` requests, then the larger of the
+// batched prompt-pass and step workspaces
+struct RoundWs {
+    int32_t* tok;
+    int32_t* first;
+    int32_t* ptok;
+    uint16_t* pemb;
+    char* inner;
+    size_t inner_bytes;
+    size_t bytes;
+};
+
+RoundWs carve_round(void* ws, int rows, int max_P, int H, size_t inner_bytes) {
+    Carve cv(ws);
+    RoundWs w;
+    w.tok = cv.take<int32_t>(rows);
+    w.first = cv.take<int32_t>(rows);
+    w.ptok = cv.take<int32_t>((size_t)rows * max_P);
+    w.pemb = cv.take<uint16_t>((size_t)rows * max_P * H);
+    w.inner = cv.take<char>(inner_bytes);
+    w.inner_bytes = inner_bytes;
+    w.bytes = cv.off;
+    return w;
 }
 
 }  // namespace
@@ -30,15 +69,27 @@ __global__ void admit_row_kernel(int32_t* prefix_len, int32_t* gen_index, int ro
 
 using namespace ocrdec;
 
+namespace {
+ocrdec_status round_sizes(const ocrdec_model* m, const ocrdec_state* st, int max_P, size_t* inner, size_t* total) {
+    OCR_CHECK_ARG(m && st, "model and state must be non-NULL");
+    OCR_CHECK_ARG(st->rows >= 1 && st->rows <= 32, "rows must be in [1, 32]");
+    std::vector<int32_t> rows(st->rows), P(st->rows, max_P);
+    for (int i = 0; i < st->rows; ++i) rows[i] = i;
+    size_t pre = 0, step = 0;
+    ocrdec_status s;
+    if ((s = ocrdec_prefill_batch_workspace_bytes(m, st, st->rows, rows.data(), P.data(), &pre)) != OCRDEC_OK) return s;
+    if ((s = ocrdec_step_workspace_bytes(m, st, &step)) != OCRDEC_OK) return s;
+    *inner = std::max(pre, step);
+    *total = carve_round(nullptr, st->rows, max_P, m->hidden, *inner).bytes;
+    return OCRDEC_OK;
+}
+}  // namespace
+
 extern "C" ocrdec_status ocrdec_round_workspace_bytes(const ocrdec_model* m, const ocrdec_state* st, int32_t max_P,
                                                       size_t* bytes) {
     OCR_CHECK_ARG(bytes, "bytes is NULL");
-    size_t pre = 0, step = 0;
-    ocrdec_status s;
-    if ((s = ocrdec_prefill_workspace_bytes(m, st, max_P, &pre)) != OCRDEC_OK) return s;
-    if ((s = ocrdec_step_workspace_bytes(m, st, &step)) != OCRDEC_OK) return s;
-    *bytes = align256((size_t)st->rows * sizeof(int32_t)) + std::max(pre, step);
-    return OCRDEC_OK;
+    size_t inner = 0;
+    return round_sizes(m, st, max_P, &inner, bytes);
 }
 
 extern "C" ocrdec_status ocrdec_run_round(const ocrdec_model* m, const ocrdec_state* st, ocrdec_request* reqs,
@@ -58,17 +109,18 @@ extern "C" ocrdec_status ocrdec_run_round(const ocrdec_model* m, const ocrdec_st
         OCR_CHECK_ARG(r.out, tag + "out is NULL");
         max_P = std::max(max_P, (int)r.P);
     }
-    size_t need = 0;
-    ocrdec_status s = ocrdec_round_workspace_bytes(m, st, max_P, &need);
+    size_t need = 0, inner_need = 0;
+    ocrdec_status s = round_sizes(m, st, max_P, &inner_need, &need);
     if (s != OCRDEC_OK) return s;
     if (!ws || ws_bytes < need)
         return fail(OCRDEC_ERR_WORKSPACE, "round workspace: need " + std::to_string(need) + " bytes, got " +
                                               std::to_string(ws ? ws_bytes : 0));
     hipStream_t hs = (hipStream_t)stream;
-    const int rows = st->rows;
-    int32_t* tok = (int32_t*)ws;
-    char* inner = (char*)ws + align256((size_t)rows * sizeof(int32_t));
-    const size_t inner_bytes = ws_bytes - align256((size_t)rows * sizeof(int32_t));
+    const int rows = st->rows, H = m->hidden;
+    const RoundWs W = carve_round(ws, rows, max_P, H, inner_need);
+    int32_t* tok = W.tok;
+    char* inner = W.inner;
+    const size_t inner_bytes = W.inner_bytes;
     const std::vector<int32_t> eos_set(eos, eos + n_eos);
     auto is_eos = [&](int32_t t) { return std::find(eos_set.begin(), eos_set.end(), t) != eos_set.end(); };
     for (int i = 0; i < n_reqs; ++i) {
@@ -107,17 +159,39 @@ extern "C" ocrdec_status ocrdec_run_round(const ocrdec_model* m, const ocrdec_st
             std::vector<int> fresh;
             for (int row = 0; row < rows && next < n_reqs; ++row) {
                 if (owner[row] >= 0) continue;
-                const ocrdec_request& r = reqs[next];
-                ocrdec_state one = *st;
-                s = ocrdec_prefill(m, &one, row, r.P, r.tokens, r.tokens ? nullptr : r.features, nullptr, tok + row,
-                                   nullptr, nullptr, inner, inner_bytes, stream);
-                if (s != OCRDEC_OK) return s;
-                hipLaunchKernelGGL(admit_row_kernel, dim3(1), dim3(64), 0, hs, (int32_t*)st->prefix_len, st->gen_index,
-                                   row, r.P);
                 owner[row] = next++;
                 fresh.push_back(row);
             }
             if (fresh.empty()) break;
+            // one batched prompt pass for the token requests, one for the
+            // feature requests, their inputs packed into the workspace
+            for (int kind = 0; kind < 2; ++kind) {
+                Admitted a{};
+                std::vector<int32_t> brow, bP;
+                int64_t off = 0;
+                for (int row : fresh) {
+                    const ocrdec_request& r = reqs[owner[row]];
+                    if ((r.tokens != nullptr) != (kind == 0)) continue;
+                    hipError_t e = kind == 0 ? hipMemcpyAsync(W.ptok + off, r.tokens, (size_t)r.P * sizeof(int32_t),
+                                                              hipMemcpyDeviceToDevice, hs)
+                                             : hipMemcpyAsync(W.pemb + off * H, r.features, (size_t)r.P * H * 2,
+                                                              hipMemcpyDeviceToDevice, hs);
+                    if (e != hipSuccess) return fail(OCRDEC_ERR_DEVICE, "ocrdec_run_round: packing a prompt failed");
+                    off += r.P;
+                    a.row[a.n] = row;
+                    a.P[a.n] = r.P;
+                    ++a.n;
+                    brow.push_back(row);
+                    bP.push_back(r.P);
+                }
+                if (a.n == 0) continue;
+                s = ocrdec_prefill_batch(m, st, a.n, brow.data(), bP.data(), kind == 0 ? W.ptok : nullptr,
+                                         kind == 0 ? nullptr : W.pemb, nullptr, W.first, nullptr, nullptr, inner,
+                                         inner_bytes, stream);
+                if (s != OCRDEC_OK) return s;
+                hipLaunchKernelGGL(admit_rows_kernel, dim3(1), dim3(64), 0, hs, (int32_t*)st->prefix_len,
+                                   st->gen_index, tok, W.first, a);
+            }
             if ((s = launch_status("ocrdec_run_round")) != OCRDEC_OK) return s;
             if ((s = read_tokens(rows)) != OCRDEC_OK) return s;
             for (int row : fresh)
