@@ -564,6 +564,8 @@ class PrefillResult:
         self.topk_idx = []       # per MoE layer: int32 [P][k]
         self.topk_w = []         # per MoE layer: float64 [P][k]
         self.router_gap = []     # per MoE layer: float64 [P]
+        self.kq, self.ks = [], []  # INT8 caches: per layer codes int8 [NH][P][D], scales fp16 [NH][P]
+        self.vq, self.vs = [], []
 
 
 def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
@@ -586,7 +588,8 @@ def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) 
     return (e @ v) / e.sum(axis=1, keepdims=True)
 
 
-def prefill(model, P: int, tok=None, emb=None, forced_topk=None, with_lm: bool = True) -> PrefillResult:
+def prefill(model, P: int, tok=None, emb=None, forced_topk=None, with_lm: bool = True,
+            int8_kv: bool = False) -> PrefillResult:
     """The prompt pass of one row: P positions through every layer at once.
 
     [UOCR] (the model needs a prefill before token-by-token generation;
@@ -603,6 +606,8 @@ def prefill(model, P: int, tok=None, emb=None, forced_topk=None, with_lm: bool =
     image features spliced into the prompt); storage points as in decode.
 
     ``forced_topk`` [n_moe][P][k] (rows < 0: not forced) replaces the routing.
+    With ``int8_kv`` the cache is INT8 (``kv_quantise``): keys and values are
+    stored quantised and the attention reads them as stored, as in decode.
     """
     dims = model.dims
     NH, D, eps, theta = dims.n_heads, dims.head_dim, dims.norm_eps, dims.rope_theta
@@ -619,9 +624,18 @@ def prefill(model, P: int, tok=None, emb=None, forced_topk=None, with_lm: bool =
         q = f16(rope(qkv[:, :NH * D].reshape(P, NH, D), pos, theta))
         k = f16(rope(qkv[:, NH * D:2 * NH * D].reshape(P, NH, D), pos, theta))
         v = f16(qkv[:, 2 * NH * D:].reshape(P, NH, D))
+        ka, va = k, v
+        if int8_kv:
+            kq, ks = kv_quantise(k)
+            vq, vs = kv_quantise(v)
+            ka, va = kv_dequant(kq, ks), kv_dequant(vq, vs)
+            res.kq.append(kq.transpose(1, 0, 2).copy())
+            res.ks.append(ks.T.copy())
+            res.vq.append(vq.transpose(1, 0, 2).copy())
+            res.vs.append(vs.T.copy())
         o = np.zeros((P, NH, D))
         for hh in range(NH):
-            o[:, hh] = causal_attention(q[:, hh], k[:, hh], v[:, hh], 1.0 / np.sqrt(D))
+            o[:, hh] = causal_attention(q[:, hh], ka[:, hh], va[:, hh], 1.0 / np.sqrt(D))
         h = h + gemv_qmat(lay.wo, f16(o.reshape(P, NH * D)))
         res.k.append(k.transpose(1, 0, 2).copy())
         res.v.append(v.transpose(1, 0, 2).copy())

@@ -740,3 +740,29 @@ def test_generate_first_token_eos_and_budget():
     assert cut == seq[:k] and stop == 1
     kept, stop, _ = O.generate(m, P, tok=tok, max_new=6, eos=[seq[k]], keep_eos=True)
     assert kept == seq[:k + 1] and stop == 1
+
+
+def test_prefill_int8_equals_token_by_token_decode():
+    """With an INT8 cache the prompt pass stores the same codes and scales,
+    and leaves the same residual, as P decode steps over an empty prefix with
+    an INT8 cache (both quantise the same fp16 keys and values and attend to
+    them as stored)."""
+    import synth
+    d = _prefill_dims()
+    P = 15
+    m = synth.make_model(d, 33)
+    tok = synth.uniform_i32(synth.stream_id(33, "prompt"), (P,), 0, d.vocab)
+    pre = O.prefill(m, P, tok=tok, int8_kv=True)
+    st = synth.make_state_int8(d, 33, [0], [0])
+    steps = [O.decode_step(m, st, tok_in=tok[t:t + 1]) for t in range(P)]
+    for l in range(d.n_layers):
+        sl = slice(d.prefix_cap, d.prefix_cap + P)
+        assert np.array_equal(st.k_cache[l, 0][:, sl], pre.kq[l])
+        assert np.array_equal(st.k_scale[l, 0][:, sl], pre.ks[l])
+        assert np.array_equal(st.v_cache[l, 0][:, sl], pre.vq[l])
+        assert np.array_equal(st.v_scale[l, 0][:, sl], pre.vs[l])
+    hid = np.array([s.hidden[0] for s in steps])
+    assert np.allclose(hid, pre.hidden, rtol=1e-11, atol=1e-12)
+    assert steps[-1].tok[0] == pre.tok
+    # and the int8 cache changes the result: the stored values are not the fp16 ones
+    assert not np.allclose(O.prefill(m, P, tok=tok).hidden, pre.hidden, rtol=1e-9, atol=0)
