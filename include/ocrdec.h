@@ -351,8 +351,11 @@ ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_state* st, 
  * (or embed_q's row dequantised), or h = emb[i] when tok is NULL; per layer
  * x = fp16(RMSNorm(h) * attn_norm), q/k/v = Wqkv x, RoPE at the linear
  * positions i = 0..P-1, k and v written to cache indices 0..P-1 of the row
- * (fp16), causal attention (query i attends keys 0..i, scale
- * 1/sqrt(head_dim)), h += Wo o, then h += MLP(fp16(RMSNorm(h) * ffn_norm))
+ * (fp16; or, where the layer's k_scale and v_scale are set, int8 codes and
+ * fp16 scales quantised as the decode step quantises a new token), causal
+ * attention (query i attends keys 0..i, scale 1/sqrt(head_dim)) over the
+ * values as stored (scale x code for an INT8 cache), h += Wo o, then
+ * h += MLP(fp16(RMSNorm(h) * ffn_norm))
  * (dense SwiGLU, or the MoE of ocrdec_moe_layer over the P positions).  If
  * the model has an LM head and tok_out is non-NULL, tok_out[0] = the argmax
  * at position P-1 (the first generated token), as in ocrdec_decode_step.

@@ -662,17 +662,19 @@ def prefill(model, P: int, tok=None, emb=None, forced_topk=None, with_lm: bool =
 class _OneRow:
     """Decode state of one row (the attributes decode_step reads)."""
 
-    def __init__(self, dims, P: int):
+    def __init__(self, dims, P: int, int8_kv: bool = False):
         cap = dims.prefix_cap + dims.ring_cap
         shape = (dims.n_layers, 1, dims.n_heads, cap, dims.head_dim)
         self.prefix_len = np.array([P], np.int32)
         self.gen_index = np.zeros(1, np.int32)
-        self.k_cache = np.zeros(shape, np.float16)
-        self.v_cache = np.zeros(shape, np.float16)
-        self.k_scale = self.v_scale = None
+        self.k_cache = np.zeros(shape, np.int8 if int8_kv else np.float16)
+        self.v_cache = np.zeros(shape, np.int8 if int8_kv else np.float16)
+        self.k_scale = np.zeros(shape[:4], np.float16) if int8_kv else None
+        self.v_scale = np.zeros(shape[:4], np.float16) if int8_kv else None
 
 
-def generate(model, P: int, tok=None, emb=None, max_new: int = 1, eos=(), keep_eos: bool = False):
+def generate(model, P: int, tok=None, emb=None, max_new: int = 1, eos=(), keep_eos: bool = False,
+             int8_kv: bool = False):
     """Greedy generation for one request: the prompt pass, then decode steps
     that feed each token back, until a token of the EOS set or max_new tokens.
 
@@ -680,18 +682,23 @@ def generate(model, P: int, tok=None, emb=None, max_new: int = 1, eos=(), keep_e
     cache) and 3.5 (generation stops at any token of the EOS set before it is
     handed out; a debug mode keeps the end token for comparisons: keep_eos).
     The prompt's keys and values fill cache indices 0..P-1 and decoding
-    continues at prefix_len = P, generation index 0.
+    continues at prefix_len = P, generation index 0.  ``int8_kv``: the cache
+    is INT8 throughout (``kv_quantise``).
 
     Returns (tokens, stop, gaps): stop 1 = EOS, 2 = max_new; gaps[i] is this
     side's top-2 logit gap behind token i (near-ties admit other answers).
     """
     dims = model.dims
     assert 1 <= P <= dims.prefix_cap, "the prompt fills the prefix region"
-    pre = prefill(model, P, tok=tok, emb=emb)
-    st = _OneRow(dims, P)
+    pre = prefill(model, P, tok=tok, emb=emb, int8_kv=int8_kv)
+    st = _OneRow(dims, P, int8_kv)
     for l in range(dims.n_layers):
-        st.k_cache[l, 0][:, :P] = pre.k[l].astype(np.float16)
-        st.v_cache[l, 0][:, :P] = pre.v[l].astype(np.float16)
+        if int8_kv:
+            st.k_cache[l, 0][:, :P], st.k_scale[l, 0][:, :P] = pre.kq[l], pre.ks[l]
+            st.v_cache[l, 0][:, :P], st.v_scale[l, 0][:, :P] = pre.vq[l], pre.vs[l]
+        else:
+            st.k_cache[l, 0][:, :P] = pre.k[l].astype(np.float16)
+            st.v_cache[l, 0][:, :P] = pre.v[l].astype(np.float16)
     out, gaps = [], []
     t, gap = int(pre.tok), float(pre.lm_top2[0] - pre.lm_top2[1])
     eos = set(int(e) for e in eos)

@@ -394,10 +394,10 @@ void attn_set_rope(AttnParams& p, float theta) {
 // partials attn_prefill_merge_kernel combines.
 // ---------------------------------------------------------------------------
 
-template <int D>
+template <int D, bool KV8>
 __global__ __launch_bounds__(64) void prefill_rope_kernel(PrefillAttnParams p) {
     const int at = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
-    if (i >= D / 2) return;
+    const bool on = i < D / 2;  // lane i holds the pair (i, i + D/2)
     // the sequence of packed position `at` (sequences are packed in order)
     int s = 0;
     while (s + 1 < p.n_seq && at >= p.seq_off[s + 1]) ++s;
@@ -405,18 +405,50 @@ __global__ __launch_bounds__(64) void prefill_rope_kernel(PrefillAttnParams p) {
     const int64_t crow = ((int64_t)p.seq_row[s] * p.n_heads + h) * p.cache_cap;
     const int HD = p.n_heads * D;
     const float* r = p.qkv + (int64_t)at * p.ld_qkv;
-    float y1, y2;
-    rope_pair(r[h * D + i], r[h * D + i + D / 2], p.inv_freq[i], pos, y1, y2);
-    uint16_t* qo = p.q + (int64_t)at * HD + h * D;
-    qo[i] = f2h(y1);
-    qo[i + D / 2] = f2h(y2);
-    rope_pair(r[HD + h * D + i], r[HD + h * D + i + D / 2], p.inv_freq[i], pos, y1, y2);
-    uint16_t* kc = p.k_cache + (crow + pos) * D;
-    kc[i] = f2h(y1);
-    kc[i + D / 2] = f2h(y2);
-    uint16_t* vc = p.v_cache + (crow + pos) * D;
-    vc[i] = f2h(r[2 * HD + h * D + i]);
-    vc[i + D / 2] = f2h(r[2 * HD + h * D + i + D / 2]);
+    uint16_t k1 = 0, k2 = 0, v1 = 0, v2 = 0;  // fp16 key and value pair
+    if (on) {
+        float y1, y2;
+        rope_pair(r[h * D + i], r[h * D + i + D / 2], p.inv_freq[i], pos, y1, y2);
+        uint16_t* qo = p.q + (int64_t)at * HD + h * D;
+        qo[i] = f2h(y1);
+        qo[i + D / 2] = f2h(y2);
+        rope_pair(r[HD + h * D + i], r[HD + h * D + i + D / 2], p.inv_freq[i], pos, y1, y2);
+        k1 = f2h(y1);
+        k2 = f2h(y2);
+        v1 = f2h(r[2 * HD + h * D + i]);
+        v2 = f2h(r[2 * HD + h * D + i + D / 2]);
+    }
+    if constexpr (!KV8) {
+        if (on) {
+            uint16_t* kc = p.k_cache + (crow + pos) * D;
+            kc[i] = k1;
+            kc[i + D / 2] = k2;
+            uint16_t* vc = p.v_cache + (crow + pos) * D;
+            vc[i] = v1;
+            vc[i + D / 2] = v2;
+        }
+    } else {
+        // INT8 cache: one scale per key row and per value row, as in decode
+        const float kx1 = h2f(k1), kx2 = h2f(k2), vx1 = h2f(v1), vx2 = h2f(v2);
+        const float ka = wave_max(fmaxf(fabsf(kx1), fabsf(kx2))), va = wave_max(fmaxf(fabsf(vx1), fabsf(vx2)));
+        const uint16_t ks16 = f2h(__fdiv_rn(ka, 127.0f)), vs16 = f2h(__fdiv_rn(va, 127.0f));
+        const float ksf = h2f(ks16), vsf = h2f(vs16);
+        auto code = [](float x, float sc) {
+            return (int8_t)(sc > 0.f ? fminf(fmaxf(roundf(__fdiv_rn(x, sc)), -127.f), 127.f) : 0.f);
+        };
+        if (on) {
+            int8_t* kc = (int8_t*)p.k_cache + (crow + pos) * D;
+            kc[i] = code(kx1, ksf);
+            kc[i + D / 2] = code(kx2, ksf);
+            int8_t* vc = (int8_t*)p.v_cache + (crow + pos) * D;
+            vc[i] = code(vx1, vsf);
+            vc[i + D / 2] = code(vx2, vsf);
+        }
+        if (i == 0) {
+            p.k_scale[crow + pos] = ks16;
+            p.v_scale[crow + pos] = vs16;
+        }
+    }
 }
 
 constexpr int PQB = 64;  // queries per workgroup (16 per wavefront)
@@ -424,7 +456,23 @@ constexpr int PKB = 64;  // keys per block
 constexpr int PKC = 4;   // key blocks per workgroup: longer windows are split over workgroups
 constexpr int PREC = 36; // floats per lane in a partial record: 32 outputs, max, sum (padded)
 
-template <int D>
+// INT8 caches (KV8): the codes are staged in LDS as fp16 (exact), the key
+// scales multiply the score accumulators and the value scales the
+// probabilities, so both products stay exact up to fp32 accumulation.
+OCR_DEV uint4 i8x8_to_h8(uint2 c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t src = j < 2 ? c.x : c.y;
+        const int sh = 16 * (j & 1);
+        const f16_t a = (f16_t)(float)(int8_t)((src >> sh) & 0xFF);
+        const f16_t b = (f16_t)(float)(int8_t)((src >> (sh + 8)) & 0xFF);
+        w[j] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int D, bool KV8>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) {
     constexpr int KS = D / 32;                 // contraction steps of the score product
     constexpr int DT = D / 16;                 // 16-wide output tiles
@@ -433,6 +481,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
     constexpr int NPC = PKB * D / 8 / 256;     // 16-byte pieces per thread per block, K and V each
     __shared__ __align__(16) uint16_t k_s[PKB * KLD];
     __shared__ __align__(16) uint16_t vt_s[D * VLD];
+    __shared__ float ksc_s[KV8 ? PKB : 1], vsc_s[KV8 ? PKB : 1];
     // workgroup (query block qb, chunk c of its key blocks, head h, sequence
     // sq); query block qb needs key blocks 0..qb, taken PKC at a time
     const int nch = (int)gridDim.x / p.n_qb;  // chunk slots per query block
@@ -463,20 +512,34 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
     // keys past the prompt are zero (their scores are masked, and a zero
     // value keeps the masked products finite)
     uint4 kr0[NPC], vr0[NPC], kr1[NPC], vr1[NPC];
-    auto load_blk = [&](int kb, uint4(&kr)[NPC], uint4(&vr)[NPC]) {
+    float sc0 = 0.f, sc1 = 0.f;  // KV8: key (threads 0..63) or value (64..127) scale of the staged row
+    auto load_blk = [&](int kb, uint4(&kr)[NPC], uint4(&vr)[NPC], float& sc) {
         const int key = kb * PKB + (tid & 63);
 #pragma unroll
         for (int i = 0; i < NPC; ++i) {
             const int c = (tid >> 6) + 4 * i;
             kr[i] = vr[i] = make_uint4(0, 0, 0, 0);
             if (key < P) {
-                kr[i] = *(const uint4*)(kbase + (int64_t)key * D + 8 * c);
-                vr[i] = *(const uint4*)(vbase + (int64_t)key * D + 8 * c);
+                if constexpr (KV8) {
+                    kr[i] = i8x8_to_h8(*(const uint2*)((const int8_t*)p.k_cache + (crow + key) * D + 8 * c));
+                    vr[i] = i8x8_to_h8(*(const uint2*)((const int8_t*)p.v_cache + (crow + key) * D + 8 * c));
+                } else {
+                    kr[i] = *(const uint4*)(kbase + (int64_t)key * D + 8 * c);
+                    vr[i] = *(const uint4*)(vbase + (int64_t)key * D + 8 * c);
+                }
             }
         }
+        if constexpr (KV8) {
+            sc = 0.f;
+            if (tid < 128 && key < P) sc = h2f((tid < 64 ? p.k_scale : p.v_scale)[crow + key]);
+        }
     };
-    auto store_blk = [&](const uint4(&kr)[NPC], const uint4(&vr)[NPC]) {
+    auto store_blk = [&](const uint4(&kr)[NPC], const uint4(&vr)[NPC], float sc) {
         const int r = tid & 63;
+        if constexpr (KV8) {
+            if (tid < 64) ksc_s[r] = sc;
+            else if (tid < 128) vsc_s[r] = sc;
+        }
 #pragma unroll
         for (int i = 0; i < NPC; ++i) {
             const int c = (tid >> 6) + 4 * i;
@@ -496,11 +559,11 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
     float m_run = -INFINITY, l_run = 0.f;
     // two key blocks in flight: block kb + 2 is requested into the registers
     // block kb has just left for LDS
-    auto step = [&](int kb, uint4(&kr)[NPC], uint4(&vr)[NPC]) {
+    auto step = [&](int kb, uint4(&kr)[NPC], uint4(&vr)[NPC], float& sc) {
         __syncthreads();  // the previous block's LDS reads are done
-        store_blk(kr, vr);
+        store_blk(kr, vr, sc);
         __syncthreads();
-        if (kb + 2 < nkb) load_blk(kb + 2, kr, vr);
+        if (kb + 2 < nkb) load_blk(kb + 2, kr, vr, sc);
         // scores of the 64 keys (4 tiles of 16) for this lane's query
         float s[4][4];
 #pragma unroll
@@ -514,7 +577,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int key = kb * PKB + kt * 16 + 4 * g + v;
-                s[kt][v] = key <= qw ? acc[v] * p.scale : -INFINITY;
+                float sv = acc[v] * p.scale;
+                if constexpr (KV8) sv *= ksc_s[kt * 16 + 4 * g + v];
+                s[kt][v] = key <= qw ? sv : -INFINITY;
             }
         }
         // online softmax: the block maximum over the 16 values and the four
@@ -538,9 +603,11 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
             for (int v = 0; v < 4; ++v) {
                 const float e = __expf(s[kt][v] - m_new);
                 ls += e;
-                const f16_t hi = (f16_t)e;
+                float ev = e;
+                if constexpr (KV8) ev *= vsc_s[kt * 16 + 4 * g + v];
+                const f16_t hi = (f16_t)ev;
                 pb[kt >> 1][(kt & 1) * 4 + v] = hi;
-                pl[kt >> 1][(kt & 1) * 4 + v] = (f16_t)(e - (float)hi);
+                pl[kt >> 1][(kt & 1) * 4 + v] = (f16_t)(ev - (float)hi);
             }
         ls += __shfl_xor(ls, 16, 64);
         ls += __shfl_xor(ls, 32, 64);
@@ -559,11 +626,11 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillAttnParams p) 
             }
         }
     };
-    load_blk(kb0, kr0, vr0);
-    if (kb0 + 1 < nkb) load_blk(kb0 + 1, kr1, vr1);
+    load_blk(kb0, kr0, vr0, sc0);
+    if (kb0 + 1 < nkb) load_blk(kb0 + 1, kr1, vr1, sc1);
     for (int kb = kb0; kb < nkb; kb += 2) {
-        step(kb, kr0, vr0);
-        if (kb + 1 < nkb) step(kb + 1, kr1, vr1);
+        step(kb, kr0, vr0, sc0);
+        if (kb + 1 < nkb) step(kb + 1, kr1, vr1, sc1);
     }
     if (n_c > 1) {
         // one of several chunks: the unnormalised partial of every lane (its
@@ -646,15 +713,17 @@ void launch_attn_prefill(const PrefillAttnParams& p0, hipStream_t s) {
     p.n_qb = (max_len + PQB - 1) / PQB;
     const int nch = prefill_chunks(max_len);
     const dim3 gr(p.P, p.n_heads), ga(p.n_qb * nch, p.n_heads, p.n_seq), gm(p.n_qb, p.n_heads, p.n_seq);
+    const bool kv8 = p.k_scale != nullptr;
+#define OCR_PF(D_, K_)                                                                                   \
+    hipLaunchKernelGGL((prefill_rope_kernel<D_, K_>), gr, dim3(64), 0, s, p);                             \
+    hipLaunchKernelGGL((attn_prefill_kernel<D_, K_>), ga, dim3(256), 0, s, p);                            \
+    if (nch > 1) hipLaunchKernelGGL(attn_prefill_merge_kernel<D_>, gm, dim3(256), 0, s, p, nch);
     if (p.head_dim == 128) {
-        hipLaunchKernelGGL(prefill_rope_kernel<128>, gr, dim3(64), 0, s, p);
-        hipLaunchKernelGGL(attn_prefill_kernel<128>, ga, dim3(256), 0, s, p);
-        if (nch > 1) hipLaunchKernelGGL(attn_prefill_merge_kernel<128>, gm, dim3(256), 0, s, p, nch);
+        if (kv8) { OCR_PF(128, true) } else { OCR_PF(128, false) }
     } else {
-        hipLaunchKernelGGL(prefill_rope_kernel<64>, gr, dim3(64), 0, s, p);
-        hipLaunchKernelGGL(attn_prefill_kernel<64>, ga, dim3(256), 0, s, p);
-        if (nch > 1) hipLaunchKernelGGL(attn_prefill_merge_kernel<64>, gm, dim3(256), 0, s, p, nch);
+        if (kv8) { OCR_PF(64, true) } else { OCR_PF(64, false) }
     }
+#undef OCR_PF
 }
 
 void launch_attn(const AttnParams& p, hipStream_t s) {

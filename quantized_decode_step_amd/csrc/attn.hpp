@@ -46,6 +46,8 @@ struct PrefillAttnParams {
     int seq_off[PREFILL_MAX_SEQ];  // first packed position of each sequence
     int seq_len[PREFILL_MAX_SEQ];
     int seq_row[PREFILL_MAX_SEQ];  // its cache row
+    uint16_t* k_scale;   // INT8 caches: fp16 scales [rows][n_heads][cache_cap]; NULL: fp16 caches
+    uint16_t* v_scale;
 };
 
 size_t prefill_attn_part_bytes(int n_seq, int max_len, int n_heads);

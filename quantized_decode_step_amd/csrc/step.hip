@@ -541,8 +541,6 @@ ocrdec_status check_prefill(const ocrdec_model* m, const ocrdec_state* st, int n
     ocrdec_status s0 = check_step(m, st, *total);
     if (s0 != OCRDEC_OK) return s0;
     OCR_CHECK_ARG(st->prefix_cap + st->ring_cap <= (1 << 16), "prefix_cap + ring_cap must be <= 65536");
-    for (int l = 0; l < m->n_layers; ++l)
-        if (m->layers[l].k_scale) return fail(OCRDEC_ERR_UNSUPPORTED, "the prompt pass writes fp16 caches only");
     return OCRDEC_OK;
 }
 
@@ -627,6 +625,8 @@ extern "C" ocrdec_status ocrdec_prefill_batch(const ocrdec_model* m, const ocrde
         prefill_gemm(L.wqkv, false, T, w.x, H, w.qkv, 3 * HD, s);
         ap.k_cache = L.k_cache;
         ap.v_cache = L.v_cache;
+        ap.k_scale = L.k_scale;
+        ap.v_scale = L.v_scale;
         launch_attn_prefill(ap, s);
         prefill_gemm(L.wo, false, T, w.o, HD, w.y, H, s);
         hipLaunchKernelGGL(resid_norm_kernel, dim3(T), dim3(64), 0, s, w.h, w.y, L.ffn_norm, H, m->norm_eps, w.x);

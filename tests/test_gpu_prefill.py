@@ -32,19 +32,32 @@ def small_dims(**kw):
     return d
 
 
-def run_prefill(q, d, seed, P, row=0, rows=1, use_emb=False, forced=True):
+# Prompt passes into INT8 caches: every key and value row is quantised, and a
+# value within rounding noise of a code boundary flips a whole code step that
+# the next layers amplify.  The oracle's own residual moves by up to 8.4e-3 rms
+# under float32-size input noise (tests/golden/int8_prefill_sensitivity.py),
+# so the residual is held to 2e-2 rms and decisions may differ where the
+# oracle's gap is below 1e-2 (as for the composed 12-layer decoder).
+INT8_TOL, INT8_TIE = 2e-2, 1e-2
+
+
+def run_prefill(q, d, seed, P, row=0, rows=1, use_emb=False, forced=True, int8_kv=False):
     import torch
     print("[case] prefill", d.n_layers, "layers H", d.hidden, "P", P, "row", row, "of", rows, "emb", use_emb,
-          "seed", seed, flush=True)
+          "int8 kv" if int8_kv else "", "seed", seed, flush=True)
     model = synth.make_model(d, seed)
-    st = synth.make_state(d, seed, [d.prefix_cap // 2] * rows, [3] * rows)
+    if int8_kv:
+        st = synth.make_state_int8(d, seed, [d.prefix_cap // 2] * rows, [3] * rows)
+    else:
+        st = synth.make_state(d, seed, [d.prefix_cap // 2] * rows, [3] * rows)
     tok = synth.uniform_i32(synth.stream_id(seed, "prompt"), (P,), 0, d.vocab)
     emb = synth.normal_f16(synth.stream_id(seed, "prompt_emb"), (P, d.hidden)) if use_emb else None
-    res = O.prefill(model, P, tok=None if use_emb else tok, emb=None if emb is None else emb.astype(np.float64))
+    res = O.prefill(model, P, tok=None if use_emb else tok, emb=None if emb is None else emb.astype(np.float64),
+                    int8_kv=int8_kv)
     n_moe = len(res.topk_idx)
     dm = q.DeviceModel(model)
     ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
-    dm.bind_caches(ds.k_cache, ds.v_cache)
+    dm.bind_caches(ds.k_cache, ds.v_cache, ds.k_scale, ds.v_scale)
     k_before = ds.k_cache.cpu().numpy().copy()
     wsb = q.ocrdec_prefill_workspace_bytes(dm.desc, ds.desc, P)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
@@ -62,28 +75,45 @@ def run_prefill(q, d, seed, P, row=0, rows=1, use_emb=False, forced=True):
                      tok_out=tok_out, hidden=hidden, capture=cap, ws=ws, ws_bytes=wsb)
     torch.cuda.synchronize()
     kc = ds.k_cache.cpu().numpy()
-    vc = ds.v_cache.cpu().numpy().view(np.float16)
-    for l in range(d.n_layers):
-        assert_close_f16(kc.view(np.float16)[l, row, :, :P].astype(np.float64), res.k[l], "layer %d keys" % l)
-        assert_close_f16(vc[l, row, :, :P].astype(np.float64), res.v[l], "layer %d values" % l)
+    if int8_kv:
+        vc = ds.v_cache.cpu().numpy()
+        ks = ds.k_scale.cpu().numpy().view(np.float16)
+        vs = ds.v_scale.cpu().numpy().view(np.float16)
+        for l in range(d.n_layers):
+            for what, c, s, oq, os_ in (("keys", kc, ks, res.kq[l], res.ks[l]), ("values", vc, vs, res.vq[l], res.vs[l])):
+                g = O.kv_dequant(c[l, row, :, :P], s[l, row, :, :P])
+                o = O.kv_dequant(oq, os_)
+                bound = 2e-3 * np.sqrt(np.mean(o * o)) + 2 * os_.astype(np.float64)[..., None]
+                assert np.all(np.abs(g - o) <= bound), "layer %d %s" % (l, what)
+                if l == 0:
+                    # first layer: both sides quantise fp16 keys that rarely differ, so codes rarely do;
+                    # deeper layers inherit the residual's 1e-3-level differences, one code step apart
+                    # wherever a value sits near a rounding boundary
+                    assert np.mean(c[l, row, :, :P] == oq) > 0.99, "layer %d %s codes" % (l, what)
+    else:
+        vc = ds.v_cache.cpu().numpy().view(np.float16)
+        for l in range(d.n_layers):
+            assert_close_f16(kc.view(np.float16)[l, row, :, :P].astype(np.float64), res.k[l], "layer %d keys" % l)
+            assert_close_f16(vc[l, row, :, :P].astype(np.float64), res.v[l], "layer %d values" % l)
     # nothing outside row `row`, indices 0..P-1 was written
     mask = np.ones(kc.shape, bool)
     mask[:, row, :, :P] = False
     assert np.array_equal(kc[mask], k_before[mask])
     ties = []
+    tie, tol = (INT8_TIE, INT8_TOL) if int8_kv else (NEAR_TIE, 2e-3)
     g_idx = cap_idx.cpu().numpy()
     for ml in range(n_moe):
         for t in range(P):
             if not np.array_equal(g_idx[ml, t], res.topk_idx[ml][t]):
                 gap = res.router_gap[ml][t]
-                assert gap < NEAR_TIE, "moe layer %d position %d: routing differs, oracle gap %.3g" % (ml, t, gap)
+                assert gap < tie, "moe layer %d position %d: routing differs, oracle gap %.3g" % (ml, t, gap)
                 ties.append(("route", ml, t, gap))
-        assert_close(cap_w.cpu().numpy()[ml], res.topk_w[ml], "moe layer %d weights" % ml)
-    assert_close(hidden.cpu().numpy(), res.hidden, "hidden after the last layer")
+        assert_close(cap_w.cpu().numpy()[ml], res.topk_w[ml], "moe layer %d weights" % ml, tol)
+    assert_close(hidden.cpu().numpy(), res.hidden, "hidden after the last layer", tol)
     g_tok = int(tok_out.cpu().numpy()[0])
     if g_tok != int(res.tok):
         gap = res.lm_top2[0] - res.lm_top2[1]
-        assert gap < NEAR_TIE, "token %d vs oracle %d, oracle gap %.3g" % (g_tok, res.tok, gap)
+        assert gap < tie, "token %d vs oracle %d, oracle gap %.3g" % (g_tok, res.tok, gap)
         ties.append(("token", gap))
     if ties:
         print("[near-tie]", ties, flush=True)
@@ -111,6 +141,14 @@ def test_prefill_unforced_head_dim_64(q):
 def test_prefill_quantised_embed_and_head(q):
     d = small_dims(fmt_embed=synth.Q4_0, fmt_lm=synth.Q8_0)
     run_prefill(q, d, 613, 33)
+
+
+@pytest.mark.parametrize("P", [40, 257])
+def test_prefill_int8_kv_cache(q, P):
+    """The prompt pass into INT8 caches: codes and scales as the oracle stores
+    them (dequantised within one code step plus the fp16 rule), and the
+    residual after attending over the stored values."""
+    run_prefill(q, small_dims(), 630 + P, P, row=1, rows=2, int8_kv=True)
 
 
 def test_prefill_full_width_two_layers(q):

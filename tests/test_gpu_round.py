@@ -31,17 +31,17 @@ def small_dims(**kw):
     return d
 
 
-def _compare(got, ref, gaps, what):
+def _compare(got, ref, gaps, what, tie=NEAR_TIE):
     for i, (g, r) in enumerate(zip(got, ref)):
         if g != r:
-            assert gaps[i] < NEAR_TIE, "%s token %d: %d vs oracle %d (oracle gap %.3g)" % (what, i, g, r, gaps[i])
+            assert gaps[i] < tie, "%s token %d: %d vs oracle %d (oracle gap %.3g)" % (what, i, g, r, gaps[i])
             print("[near-tie]", what, i, gaps[i], flush=True)
             return False
     assert len(got) == len(ref), "%s: %d tokens vs oracle %d" % (what, len(got), len(ref))
     return True
 
 
-def run_round(q, d, seed, Ps, max_new, rows, use_features=(), eos_pick=(), keep_eos=False):
+def run_round(q, d, seed, Ps, max_new, rows, use_features=(), eos_pick=(), keep_eos=False, int8_kv=False):
     import torch
     print("[case] round rows", rows, "P", Ps, "max_new", max_new, "seed", seed, flush=True)
     model = synth.make_model(d, seed)
@@ -51,17 +51,21 @@ def run_round(q, d, seed, Ps, max_new, rows, use_features=(), eos_pick=(), keep_
     full = []
     for i, P in enumerate(Ps):
         emb = feats[i].astype(np.float64) if i in use_features else None
-        full.append(O.generate(model, P, tok=None if emb is not None else prompts[i], emb=emb, max_new=max_new[i]))
+        full.append(O.generate(model, P, tok=None if emb is not None else prompts[i], emb=emb, max_new=max_new[i],
+                               int8_kv=int8_kv))
     eos = sorted(set(full[i][0][k] for i, k in eos_pick))
     refs = []
     for i, P in enumerate(Ps):
         emb = feats[i].astype(np.float64) if i in use_features else None
         refs.append(O.generate(model, P, tok=None if emb is not None else prompts[i], emb=emb, max_new=max_new[i],
-                               eos=eos, keep_eos=keep_eos))
-    st = synth.make_state(d, seed, [0] * rows, [0] * rows)
+                               eos=eos, keep_eos=keep_eos, int8_kv=int8_kv))
+    if int8_kv:
+        st = synth.make_state_int8(d, seed, [0] * rows, [0] * rows)
+    else:
+        st = synth.make_state(d, seed, [0] * rows, [0] * rows)
     dm = q.DeviceModel(model)
     ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
-    dm.bind_caches(ds.k_cache, ds.v_cache)
+    dm.bind_caches(ds.k_cache, ds.v_cache, ds.k_scale, ds.v_scale)
     keep = []
     reqs = (q.Request * len(Ps))()
     outs = []
@@ -85,7 +89,8 @@ def run_round(q, d, seed, Ps, max_new, rows, use_features=(), eos_pick=(), keep_
     for i in range(len(Ps)):
         got = list(outs[i][:reqs[i].n_out])
         ref, stop, gaps = refs[i]
-        if _compare(got, ref, gaps, "request %d" % i):
+        # INT8 caches: decisions may differ where the oracle's gap is below 1e-2 (see test_gpu_prefill)
+        if _compare(got, ref, gaps, "request %d" % i, 1e-2 if int8_kv else NEAR_TIE):
             assert reqs[i].stop == stop, "request %d: stop %d vs oracle %d" % (i, reqs[i].stop, stop)
     return refs, eos
 
@@ -109,3 +114,10 @@ def test_round_one_row_first_token_eos(q):
     d = small_dims()
     refs, eos = run_round(q, d, 703, Ps=[10, 14, 6], max_new=[4, 5, 3], rows=1, eos_pick=[(1, 0)])
     assert refs[1][0] == [] and refs[1][1] == 1
+
+
+def test_round_int8_kv_cache(q):
+    """The round over INT8 caches: prompt passes and decode steps store keys
+    and values quantised; tokens equal the oracle's INT8 generation."""
+    d = small_dims()
+    run_round(q, d, 704, Ps=[17, 33, 8, 25], max_new=[6, 4, 7, 5], rows=2, eos_pick=[(0, 3)], int8_kv=True)
