@@ -10,8 +10,11 @@
 // window, keeps them in LDS, and writes an unnormalised partial (max, sum,
 // sum of p*v); a combine kernel merges the splits with the usual
 // log-sum-exp rescaling.  (A last-arriving-workgroup merge inside the first
-// kernel was measured slower: device-scope fences and the arrival atomics cost
-// more than a second launch.)  Keys are streamed with one 16-byte load per lane:
+// kernel was measured slower twice: with device-scope fences, and with
+// device-scope stores and an arrival counter, where waiting for the stores
+// and then for the counter cost more than the second launch.  An online merge
+// that requests every split's max, sum and output at once was slower too.)
+// Keys are streamed with one 16-byte load per lane:
 // for head_dim 128 a wavefront load covers 4 keys (16 lanes per key), for 64
 // it covers 8 keys.
 #include "attn.hpp"

@@ -107,15 +107,19 @@ OCR_DEV void group_pairs_small(const MoeParams& p, const int* idx_s, unsigned lo
         atomicOr(&mask_s[idx_s[pi] * 4 + (pi >> 6)], 1ull << (pi & 63));
     __syncthreads();
     // counts, exclusive offsets and the work list: wave 0, four experts per lane
+    // (the lane's 16 mask words are read at once: mask_s holds 4 * 256 words)
     if (wave == 0) {
         int cnt[4], tot = 0, nb = 0;
+        unsigned long long mk[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mk[i] = mask_s[16 * lane + i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = 4 * lane + j;
             cnt[j] = 0;
-            if (e < E)
 #pragma unroll
-                for (int w = 0; w < 4; ++w) cnt[j] += __popcll(mask_s[e * 4 + w]);
+            for (int w = 0; w < 4; ++w) cnt[j] += __popcll(mk[4 * j + w]);
+            if (e >= E) cnt[j] = 0;
             tot += cnt[j];
             nb += (cnt[j] + 15) >> 4;
         }
@@ -681,14 +685,15 @@ __global__ __launch_bounds__(64 * EG_NW, 2) void expert_gemm_kernel(GroupedParam
     if (v < n_ent) item(v, r % n_cg, r / n_cg);  // uniform per workgroup
 }
 
-// Routing of up to 32 rows in one workgroup.  Router GEMV: wave w computes
+// Routing of up to 32 rows in one workgroup (BIAS: the router has a bias).
+// Router GEMV: wave w computes
 // tile w % T over k-split w / T (T = E/16 tiles); its first router chunks are
 // requested before anything else, then the MoE input is staged in LDS: either
 // formed here, x = fp16(RMSNorm(h) * gamma) from the fp32 residual (also
 // written out for the expert kernels), or copied from x.  The k-splits are
 // summed in a fixed order in LDS; top-k reads the logits from LDS; the
 // grouping works in LDS.  Dynamic LDS: rows * (H + 8) halves.
-template <int FMT, int NV>
+template <int FMT, int NV, bool BIAS>
 __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const uint8_t* router, int H,
                                                             const uint16_t* x, int64_t ldx, const float* h_in,
                                                             const uint16_t* norm_w, float eps, uint16_t* x_out) {
@@ -700,6 +705,10 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
     __shared__ unsigned long long mask_s[4 * 256];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = p.n_experts, T = E / 16, R = p.rows;
+    // The arguments the serial tail (top-k, grouping) reads are requested
+    // now: a scalar-cache miss there stalls the only workgroup for a memory
+    // round trip.
+    asm volatile("" ::"s"(p.perm), "s"(p.virt), "s"(p.cap_perm));
     const int nks = 16 / T;
     const int tile = wave % T, ks = wave / T;
     const int64_t nch = n_chunks_dev<FMT>(H);
@@ -734,7 +743,10 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
             for (int v = 0; v < 4; ++v) {
                 const int tok = tok0 + 4 * (lane >> 4) + v;
                 const int e = wave * 16 + (lane & 15);
-                lg_s[tok * E + e] = a[v] + (p.bias ? p.bias[e] : 0.f);
+                // (no load without a bias: a conditional load here makes the
+                // wave wait for every store in flight, the normalised rows too)
+                if constexpr (BIAS) lg_s[tok * E + e] = a[v] + p.bias[e];
+                else lg_s[tok * E + e] = a[v];
             }
         }
         __syncthreads();
@@ -1174,9 +1186,14 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     if (small) {
         // router GEMV, top-k and grouping in one workgroup
         const uint8_t* rw = (const uint8_t*)w->router.data;
-#define OCR_RL(F_, NV_)                                                                                     \
-    hipLaunchKernelGGL((route_fused_kernel<F_, NV_>), dim3(1), dim3(1024), route_lds_bytes(rows, H), s, p, rw, H, \
-                       x, ldx, h_norm, norm_in, eps_in, (uint16_t*)x)
+#define OCR_RLB(F_, NV_, B_)                                                                                \
+    hipLaunchKernelGGL((route_fused_kernel<F_, NV_, B_>), dim3(1), dim3(1024), route_lds_bytes(rows, H), s, p, rw, \
+                       H, x, ldx, h_norm, norm_in, eps_in, (uint16_t*)x)
+#define OCR_RL(F_, NV_)                     \
+    do {                                    \
+        if (p.bias) OCR_RLB(F_, NV_, true); \
+        else OCR_RLB(F_, NV_, false);       \
+    } while (0)
 #define OCR_R(F_)                      \
     case F_:                           \
         if (H <= 1280) OCR_RL(F_, 5);  \
@@ -1191,6 +1208,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         }
 #undef OCR_R
 #undef OCR_RL
+#undef OCR_RLB
     } else if (gemm) {
         // router GEMM, parallel top-k, grouping into 128-token entries
         GroupedParams rp{};
