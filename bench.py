@@ -80,6 +80,7 @@ def parse():
     ap.add_argument("--no-int8kv", action="store_true", help="skip the INT8 KV cache runs")
     ap.add_argument("--no-round", action="store_true", help="skip the round-scheduler line")
     ap.add_argument("--prompt-iters", type=int, default=5)
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-call HBM GB/s of one layer's entry points")
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--copy-mb", type=int, default=512, help="size of the calibration copy in --mode lm")
     return ap.parse_args()
@@ -263,6 +264,9 @@ def main():
                  "lm_head_us": round(lmq_us, 2), "lm_head_GBps": round(lmq_bytes / (lmq_us * 1e-6) / 1e9, 1),
                  "lm_head_frac": round(lmq_bytes / (lmq_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
+    # ---- HBM GB/s of one decoder layer's entry points at one row
+    kernels = None if args.no_kernels else per_call_bandwidth(q, torch, dev, stream, dm, d)
+
     # ---- the prefill-shaped MoE layer (2048 tokens, MFMA path), reported beside the decode metric
     prefill = None if args.no_prefill else prefill_moe(args, q, torch, dev, stream)
 
@@ -311,6 +315,7 @@ def main():
                      "avg_us": round(lm_us, 2), "algorithmic_bytes": lm_bytes},
         "cpu_baseline": cpu,
         "quantised_head": qhead,
+        "kernels": kernels,
         "prefill_moe": prefill,
         "prompt_pass": prompt,
         "int8_kv": int8_kv,
@@ -318,6 +323,75 @@ def main():
         "setup_s": round(t_build, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def per_call_bandwidth(q, torch, dev, stream, dm, d, layer: int = 1, reps: int = 20, replays: int = 5):
+    """Achieved HBM GB/s of the C-ABI calls one MoE layer of the decode step is
+    made of, at one row and the step's shapes: each call is captured `reps`
+    times in a HIP graph and the graph replayed `replays` times between HIP
+    events on its stream (GPU time only; the launch gaps between the captured
+    kernels are included, as in the step).  Algorithmic bytes: the weight
+    blocks a call must read (for the MoE layer the router, the 6 routed experts
+    the row takes and the 2 shared experts), the KV window for attention."""
+    import synth
+    lay, L = dm.src_layers[layer], dm.layers[layer]
+    H, NH, D, HD = d.hidden, d.n_heads, d.head_dim, d.n_heads * d.head_dim
+
+    def nb(m):
+        return {0: 2.0, 1: 34 / 32, 2: 18 / 32, 3: 36 / 32}[m.fmt] * m.n * m.k
+    x = torch.from_numpy(synth.normal_f16(synth.stream_id(SEED, "kern_x"), (1, H)).view(np.int16)).to(dev)
+    o16 = torch.from_numpy(synth.normal_f16(synth.stream_id(SEED, "kern_o"), (1, HD)).view(np.int16)).to(dev)
+    qkv = torch.zeros((1, 3 * HD), dtype=torch.float32, device=dev)
+    y = torch.zeros((1, H), dtype=torch.float32, device=dev)
+    # attention over a full window: prefix 1100 + the whole 128-slot ring
+    st = synth.make_state(d, SEED, [d.prefix_cap], [2 * d.ring_cap])
+    ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+    att_out = torch.zeros((1, HD), dtype=torch.int16, device=dev)
+    a = q.AttnArgs(1, NH, D, qkv.data_ptr(), 3 * HD, ds.k_cache[layer].data_ptr(), ds.v_cache[layer].data_ptr(),
+                   d.prefix_cap, d.ring_cap, ds.prefix_len.data_ptr(), ds.gen_index.data_ptr(), None,
+                   d.rope_theta, 1.0 / np.sqrt(D), att_out.data_ptr(), HD, None, None)
+    a_wsb = q.ocrdec_attn_workspace_bytes(a)
+    a_ws = torch.zeros(a_wsb, dtype=torch.uint8, device=dev)
+    h16 = torch.zeros((1, H), dtype=torch.int16, device=dev)
+    m_wsb = q.ocrdec_moe_workspace_bytes(L.moe, 1)
+    m_ws = torch.zeros(m_wsb, dtype=torch.uint8, device=dev)
+    keys = d.prefix_cap + d.ring_cap
+    per_expert = nb(lay.exp_gate_up) / d.n_experts + nb(lay.exp_down) / d.n_experts
+    calls = [
+        ("ocrdec_gemv_q: QKV projection, Q8_0 %dx%d" % (3 * HD, H), nb(lay.wqkv),
+         lambda s: q.ocrdec_gemv_q(L.wqkv, 1, x, H, qkv, q.OCRDEC_OUT_F32, 3 * HD, stream=s)),
+        ("ocrdec_attn_decode: %d heads x %d over %d keys (prefix %d + full ring)" % (NH, D, keys, d.prefix_cap),
+         keys * NH * D * 2 * 2.0, lambda s: q.ocrdec_attn_decode(a, a_ws, a_wsb, stream=s)),
+        ("ocrdec_gemv_q: O projection, Q8_0 %dx%d" % (H, HD), nb(lay.wo),
+         lambda s: q.ocrdec_gemv_q(L.wo, 1, o16, HD, y, q.OCRDEC_OUT_F32, H, stream=s)),
+        ("ocrdec_moe_layer: router + %d routed + %d shared Q4_0 experts of %d" % (d.top_k, d.n_shared, d.expert_ff),
+         nb(lay.router) + d.top_k * per_expert + nb(lay.sh_gate_up) + nb(lay.sh_down),
+         lambda s: q.ocrdec_moe_layer(L.moe, 1, x, h16, True, ws=m_ws, ws_bytes=m_wsb, stream=s)),
+    ]
+    out = []
+    with torch.cuda.stream(stream):
+        for name, byt, fn in calls:
+            for _ in range(3):
+                fn(stream)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(reps):
+                    fn(torch.cuda.current_stream())
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(replays):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0 / (reps * replays)
+            gbs = byt / (us * 1e-6) / 1e9
+            out.append({"call": name, "us": round(us, 2), "algorithmic_bytes": round(byt), "GBps": round(gbs, 1),
+                        "frac": round(gbs / HBM_PEAK_GBS, 4)})
+            del g
+    return {"rows": 1, "layer": "MoE layer %d of the 12-layer decoder" % layer, "peak_GBps": HBM_PEAK_GBS,
+            "calls": out}
 
 
 PREFILL_SEED = 1005
