@@ -124,42 +124,56 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
     } else if (tid >= 64 && tid < 64 + D) {
         xv = qkv[2 * HD + h * D + tid - 64];
     }
+    const int64_t head_off = ((int64_t)r * p.n_heads + h) * p.cache_cap;
+
+    // ---- keys and values of this wavefront (wave w takes keys o0 + w*KPL +
+    // it*4*KPL, one key per lane group), all requested before any use.  They
+    // are requested before the window is known, at cache index = ordinal:
+    // that is the key's slot whenever the prefix is full (and always in
+    // linear mode), so the loads travel with the projections' instead of
+    // waiting a round trip for the lengths.  Keys whose slot differs (ring
+    // keys behind a shorter prefix) are requested again below; the new
+    // token's slot is taken from LDS.
+    const int dsub = (lane % LPK) * VPL;
+    uint4 kr[ITER], vr[ITER];
+    uint4 kr8[KV8 ? ITER : 1], vr8[KV8 ? ITER : 1];
+    float ksc[KV8 ? ITER : 1], vsc[KV8 ? ITER : 1];
+    auto load_kv = [&](int it, int ci) {
+        if constexpr (KV8) {
+            kr8[it] = *(const uint4*)((const int8_t*)p.k_cache + (head_off + ci) * D + dsub);
+            vr8[it] = *(const uint4*)((const int8_t*)p.v_cache + (head_off + ci) * D + dsub);
+            ksc[it] = h2f(p.k_scale[head_off + ci]);
+            vsc[it] = h2f(p.v_scale[head_off + ci]);
+        } else {
+            kr[it] = *(const uint4*)(p.k_cache + (head_off + ci) * D + dsub);
+            vr[it] = *(const uint4*)(p.v_cache + (head_off + ci) * D + dsub);
+        }
+    };
+    {
+        const int os0 = s * KPS, os1 = min(os0 + KPS, p.cache_cap);
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            const int o = os0 + wave * KPL + it * 4 * KPL + lane / LPK;
+            if constexpr (KV8) {
+                kr8[it] = vr8[it] = make_uint4(0, 0, 0, 0);
+                ksc[it] = vsc[it] = 0.f;
+            } else {
+                kr[it] = vr[it] = make_uint4(0, 0, 0, 0);
+            }
+            if (o < os1) load_kv(it, o);
+        }
+    }
     const Window w = row_window(p, r);
     const int o0 = s * KPS, o1 = min(o0 + KPS, w.nkeys);
     float* part = p.part + (((int64_t)r * p.n_heads + h) * p.n_split + s) * (D + 2);
     if (o0 >= o1) return;  // beyond this row's window: not counted below
     const bool has_new = (w.new_ord >= o0 && w.new_ord < o1);
-    const int64_t head_off = ((int64_t)r * p.n_heads + h) * p.cache_cap;
-
-    // ---- keys and values of this wavefront (wave w takes keys o0 + w*KPL +
-    // it*4*KPL, one key per lane group), all requested before any use; the
-    // new token's slot is taken from LDS instead
-    const int dsub = (lane % LPK) * VPL;
-    uint4 kr[ITER], vr[ITER];
-    uint4 kr8[KV8 ? ITER : 1], vr8[KV8 ? ITER : 1];
-    float ksc[KV8 ? ITER : 1], vsc[KV8 ? ITER : 1];
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
         const int o = o0 + wave * KPL + it * 4 * KPL + lane / LPK;
-        if constexpr (KV8) {
-            kr8[it] = vr8[it] = make_uint4(0, 0, 0, 0);
-            ksc[it] = vsc[it] = 0.f;
-        } else {
-            kr[it] = vr[it] = make_uint4(0, 0, 0, 0);
-        }
         if (o < o1) {
             const int ci = ord_to_idx(p, w, o);
-            if (ci != w.new_idx) {
-                if constexpr (KV8) {
-                    kr8[it] = *(const uint4*)((const int8_t*)p.k_cache + (head_off + ci) * D + dsub);
-                    vr8[it] = *(const uint4*)((const int8_t*)p.v_cache + (head_off + ci) * D + dsub);
-                    ksc[it] = h2f(p.k_scale[head_off + ci]);
-                    vsc[it] = h2f(p.v_scale[head_off + ci]);
-                } else {
-                    kr[it] = *(const uint4*)(p.k_cache + (head_off + ci) * D + dsub);
-                    vr[it] = *(const uint4*)(p.v_cache + (head_off + ci) * D + dsub);
-                }
-            }
+            if (ci != o) load_kv(it, ci);
         }
     }
     if (tid < D / 2) {
