@@ -315,18 +315,29 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
 
 }
 
-// Merge of the splits of one (head, row): the max and sums of every split are
-// loaded in parallel into LDS, then each thread (one per output lane) sums the
-// rescaled partial outputs with independent loads.
+// Merge of the splits of one (head, row).  Everything the merge reads is
+// requested before the row's window is known (the partial buffer holds
+// n_split splits whatever the window; splits beyond it are ignored): thread
+// t's split max and sum, and its output lane of the first 24 splits.  The
+// maxima go through LDS, then each thread (one per output lane) sums the
+// rescaled partial outputs in split order.
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(AttnParams p) {
+    constexpr int PRE = 24;
     __shared__ float f_s[1024 + 1];
     __shared__ float red[2];
     const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+    const int ns = p.n_split;
+    const float* part0 = p.part + ((int64_t)r * p.n_heads + h) * ns * (D + 2);
+    const float mv = tid < ns ? part0[tid * (D + 2) + D] : -INFINITY;
+    const float lv = tid < ns ? part0[tid * (D + 2) + D + 1] : 0.f;
+    float ov[PRE];
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) ov[j] = j < ns ? part0[j * (D + 2) + tid] : 0.f;
     const Window w = row_window(p, r);
     const int n_used = (w.nkeys + KPS - 1) / KPS;
-    const float* part0 = p.part + ((int64_t)r * p.n_heads + h) * p.n_split * (D + 2);
-    for (int i = tid; i < n_used; i += D) f_s[i] = part0[i * (D + 2) + D];
+    if (tid < n_used) f_s[tid] = mv;
+    for (int i = tid + D; i < n_used; i += D) f_s[i] = part0[i * (D + 2) + D];
     __syncthreads();
     if (tid < 64) {
         float M = -INFINITY;
@@ -337,7 +348,12 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnParams p) {
     __syncthreads();
     const float M = red[0];
     float Lp = 0.f;
-    for (int i = tid; i < n_used; i += D) {
+    if (tid < n_used) {
+        const float f = __expf(mv - M);
+        Lp = lv * f;
+        f_s[tid] = f;
+    }
+    for (int i = tid + D; i < n_used; i += D) {
         const float f = __expf(f_s[i] - M);
         Lp = fmaf(part0[i * (D + 2) + D + 1], f, Lp);
         f_s[i] = f;
@@ -354,7 +370,10 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnParams p) {
     }
     __syncthreads();
     float o = 0.f;
-    int i = 0;
+#pragma unroll
+    for (int j = 0; j < PRE; ++j)
+        if (j < n_used) o = fmaf(ov[j], f_s[j], o);
+    int i = PRE;
     for (; i + 4 <= n_used; i += 4) {
         const float a0 = part0[(i + 0) * (D + 2) + tid];
         const float a1 = part0[(i + 1) * (D + 2) + tid];
