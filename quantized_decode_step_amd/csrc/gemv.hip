@@ -43,6 +43,24 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
         for (int i = 0; i < NT; ++i)
 #pragma unroll
             for (int xt = 0; xt < XT; ++xt) acc[i][xt] = float4v{0.f, 0.f, 0.f, 0.f};
+        // residual epilogue: the residual values are requested now, so that
+        // the add does not wait a memory round trip after the k-loop (every
+        // output element belongs to one workgroup: nobody else writes it)
+        float hpre[(EPI == EPI_RESID) ? NT : 1][(EPI == EPI_RESID) ? XT : 1][4];
+        if constexpr (EPI == EPI_RESID) {
+            const float* h = (const float*)p.y;
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int xt = 0; xt < XT; ++xt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int tok = tok0 + 16 * xt + 4 * (lane >> 4) + v;
+                        const int row = tidx[i] * 16 + (lane & 15);
+                        const bool in = ks == 0 && valid && tok < p.xs.rows && row < p.n;
+                        hpre[i][xt][v] = in ? h[(int64_t)tok * p.ldy + row] : 0.f;
+                    }
+        }
         if constexpr (XSRC != X_GLOBAL) {
             auto stage = [&]() {
                 if constexpr (XSRC == X_NORM) stage_norm(p.hn, p.gamma, p.eps, p.xs.rows, tok0, p.k, xl_dyn, ldl);
@@ -153,8 +171,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
                             } else if constexpr (EPI == EPI_F16) {
                                 ((uint16_t*)p.y)[o] = f2h(acc[i][xt][v]);
                             } else if constexpr (EPI == EPI_RESID) {
-                                float* h = (float*)p.y;
-                                h[o] = h[o] + acc[i][xt][v];
+                                ((float*)p.y)[o] = hpre[i][xt][v] + acc[i][xt][v];
                             }
                         }
                     }
@@ -429,37 +446,36 @@ void launch_lm_argmax(int fmt, const LmPlan& lp, GemvParams p, hipStream_t s) {
 // commutative, so the result does not depend on the order).
 __global__ __launch_bounds__(256) void argmax_final_kernel(const float* part, int n_wg, int rows, int32_t* tok_out,
                                                            float* top2, int32_t* gen_index) {
-    __shared__ float sb[256], ss[256];
-    __shared__ int si[256];
-    const int r = blockIdx.x, tid = threadIdx.x;
+    __shared__ float sb[4], ss[4];
+    __shared__ int si[4];
+    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the generation index is requested with the partials (not after the merge)
+    const int gi = (gen_index && tid == 0) ? gen_index[r] : 0;
     float b = -INFINITY, s = -INFINITY;
     int bi = 0x7fffffff;
     for (int w = tid; w < n_wg; w += blockDim.x) {
         const float* e = part + ((int64_t)w * rows + r) * 3;
         argmax_merge(b, bi, s, e[0], __float_as_int(e[1]), e[2]);
     }
-    sb[tid] = b;
-    ss[tid] = s;
-    si[tid] = bi;
-    __syncthreads();
-    for (int o = blockDim.x / 2; o > 0; o >>= 1) {
-        if (tid < o) {
-            float b2 = sb[tid], s2 = ss[tid];
-            int i2 = si[tid];
-            argmax_merge(b2, i2, s2, sb[tid + o], si[tid + o], ss[tid + o]);
-            sb[tid] = b2;
-            ss[tid] = s2;
-            si[tid] = i2;
-        }
-        __syncthreads();
+    for (int o = 32; o > 0; o >>= 1) {
+        const float b2 = __shfl_xor(b, o, 64), s2 = __shfl_xor(s, o, 64);
+        const int i2 = __shfl_xor(bi, o, 64);
+        argmax_merge(b, bi, s, b2, i2, s2);
     }
+    if (lane == 0) {
+        sb[wave] = b;
+        ss[wave] = s;
+        si[wave] = bi;
+    }
+    __syncthreads();
     if (tid == 0) {
-        if (tok_out) tok_out[r] = (si[0] == 0x7fffffff) ? 0 : si[0];
+        for (int w = 1; w < (int)(blockDim.x >> 6); ++w) argmax_merge(b, bi, s, sb[w], si[w], ss[w]);
+        if (tok_out) tok_out[r] = (bi == 0x7fffffff) ? 0 : bi;
         if (top2) {
-            top2[2 * r] = sb[0];
-            top2[2 * r + 1] = ss[0];
+            top2[2 * r] = b;
+            top2[2 * r + 1] = s;
         }
-        if (gen_index) gen_index[r] += 1;
+        if (gen_index) gen_index[r] = gi + 1;
     }
 }
 
