@@ -693,13 +693,13 @@ __global__ __launch_bounds__(64 * EG_NW, 2) void expert_gemm_kernel(GroupedParam
 // written out for the expert kernels), or copied from x.  The k-splits are
 // summed in a fixed order in LDS; top-k reads the logits from LDS; the
 // grouping works in LDS.  Dynamic LDS: rows * (H + 8) halves.
-template <int FMT, int NV, bool BIAS>
+template <int FMT, int NV, bool BIAS, int XT>
 __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const uint8_t* router, int H,
                                                             const uint16_t* x, int64_t ldx, const float* h_in,
                                                             const uint16_t* norm_w, float eps, uint16_t* x_out) {
     constexpr int CB = Geom<FMT>::CB;
     extern __shared__ __align__(16) uint16_t xl_dyn[];
-    __shared__ float4v red[16 * 64];  // k-split partials of one pass
+    __shared__ float4v red[XT * 16 * 64];  // k-split partials of one pass (XT x 16 tokens)
     __shared__ float lg_s[32 * 256];  // logits [32][E <= 256]
     __shared__ int use_s[256], counts_s[256], offsets_s[257];
     __shared__ unsigned long long mask_s[4 * 256];
@@ -731,22 +731,30 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
             stage_x(XDirect{x, ldx, R}, 0, R, H, xl_dyn, ldl);
         }
     };
-    for (int tok0 = 0; tok0 < R; tok0 += 16) {
-        float4v acc[1][1] = {{float4v{0.f, 0.f, 0.f, 0.f}}};
-        kloop_lds<FMT, 1, 1, decltype(stage), 4>(tp, c0, c1, stage, xl_dyn + tok0 * ldl, ldl, R - tok0, H / 32, lane, acc);
-        red[wave * 64 + lane] = acc[0][0];
+    // XT = 2: 17-32 rows in one pass over the router weights
+    for (int tok0 = 0; tok0 < R; tok0 += 16 * XT) {
+        float4v acc[1][XT];
+#pragma unroll
+        for (int xt = 0; xt < XT; ++xt) acc[0][xt] = float4v{0.f, 0.f, 0.f, 0.f};
+        kloop_lds<FMT, 1, XT, decltype(stage), 4>(tp, c0, c1, stage, xl_dyn + tok0 * ldl, ldl, R - tok0, H / 32, lane,
+                                                  acc);
+#pragma unroll
+        for (int xt = 0; xt < XT; ++xt) red[(xt * 16 + wave) * 64 + lane] = acc[0][xt];
         __syncthreads();
         if (wave < T) {
-            float4v a = red[wave * 64 + lane];
-            for (int o = 1; o < nks; ++o) a += red[(wave + o * T) * 64 + lane];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int tok = tok0 + 4 * (lane >> 4) + v;
-                const int e = wave * 16 + (lane & 15);
-                // (no load without a bias: a conditional load here makes the
-                // wave wait for every store in flight, the normalised rows too)
-                if constexpr (BIAS) lg_s[tok * E + e] = a[v] + p.bias[e];
-                else lg_s[tok * E + e] = a[v];
+            for (int xt = 0; xt < XT; ++xt) {
+                float4v a = red[(xt * 16 + wave) * 64 + lane];
+                for (int o = 1; o < nks; ++o) a += red[(xt * 16 + wave + o * T) * 64 + lane];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int tok = tok0 + 16 * xt + 4 * (lane >> 4) + v;
+                    const int e = wave * 16 + (lane & 15);
+                    // (no load without a bias: a conditional load here makes the
+                    // wave wait for every store in flight, the normalised rows too)
+                    if constexpr (BIAS) lg_s[tok * E + e] = a[v] + p.bias[e];
+                    else lg_s[tok * E + e] = a[v];
+                }
             }
         }
         __syncthreads();
@@ -1186,13 +1194,24 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     if (small) {
         // router GEMV, top-k and grouping in one workgroup
         const uint8_t* rw = (const uint8_t*)w->router.data;
-#define OCR_RLB(F_, NV_, B_)                                                                                \
-    hipLaunchKernelGGL((route_fused_kernel<F_, NV_, B_>), dim3(1), dim3(1024), route_lds_bytes(rows, H), s, p, rw, \
-                       H, x, ldx, h_norm, norm_in, eps_in, (uint16_t*)x)
-#define OCR_RL(F_, NV_)                     \
-    do {                                    \
-        if (p.bias) OCR_RLB(F_, NV_, true); \
-        else OCR_RLB(F_, NV_, false);       \
+        // 17-32 rows: one 32-token pass over the router weights where the LDS
+        // allows (fp16 and Q8_0 routers; the other formats' variants spill)
+        const bool xt2 = rows > 16 && route_lds_bytes(rows, H) <= 84 * 1024 &&
+                         (w->router.fmt == OCRDEC_F16 || w->router.fmt == OCRDEC_Q8_0);
+#define OCR_RLB(F_, NV_, B_)                                                                                   \
+    if (xt2)                                                                                                   \
+        hipLaunchKernelGGL((route_fused_kernel<F_, NV_, B_, 2>), dim3(1), dim3(1024), route_lds_bytes(rows, H), s, p, \
+                           rw, H, x, ldx, h_norm, norm_in, eps_in, (uint16_t*)x);                              \
+    else                                                                                                       \
+        hipLaunchKernelGGL((route_fused_kernel<F_, NV_, B_, 1>), dim3(1), dim3(1024), route_lds_bytes(rows, H), s, p, \
+                           rw, H, x, ldx, h_norm, norm_in, eps_in, (uint16_t*)x)
+#define OCR_RL(F_, NV_)                 \
+    do {                                \
+        if (p.bias) {                   \
+            OCR_RLB(F_, NV_, true);     \
+        } else {                        \
+            OCR_RLB(F_, NV_, false);    \
+        }                               \
     } while (0)
 #define OCR_R(F_)                      \
     case F_:                           \
