@@ -18,6 +18,7 @@
 // for head_dim 128 a wavefront load covers 4 keys (16 lanes per key), for 64
 // it covers 8 keys.
 #include "attn.hpp"
+#include "gemv_core.hpp"
 
 #include <algorithm>
 #include <cmath>
@@ -386,6 +387,114 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnParams p) {
     }
     for (; i < n_used; ++i) o = fmaf(part0[i * (D + 2) + tid], f_s[i], o);
     p.out[(int64_t)r * p.ld_out + h * D + tid] = f2h(o / red[1]);
+}
+
+// Decode of up to four rows with head_dim 128: the merge of each head's
+// splits and that head's share of the O projection in one launch, in place
+// of the merge kernel, a launch gap and the O projection's GEMV.  Workgroup
+// (g, hd) merges head hd of every row (thread group r < rows, as
+// attn_combine_kernel: the partials requested before the window is known)
+// into LDS; its eight wavefronts then multiply the merged row with the
+// head's D columns of W_o for the 16-row tiles 8g .. 8g+7 (one tile each;
+// the weights were requested before the merge) and add the products into
+// the fp32 residual with atomic adds.  The residual receives one addend per
+// head in the order the workgroups finish, so it is not bitwise reproducible
+// from run to run (the sum itself is fp32 either way).
+template <int FMT>
+__global__ __launch_bounds__(512) void attn_merge_o_kernel(AttnParams p, const uint8_t* wo, int n_out, int64_t nchunks,
+                                                           float* h, int64_t ldh) {
+    constexpr int D = 128, PRE = 24, KC = 32 * Geom<FMT>::SB, CPH = D / KC;
+    extern __shared__ __align__(16) uint16_t xl[];  // [rows][n_heads * D + 8] fp16: head hd's columns
+    __shared__ float f_s[4][1024 + 1];
+    __shared__ float red[4], l2[4][2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = blockIdx.x, hd = blockIdx.y;
+    const int rg = tid >> 7, t = tid & 127;
+    const bool act = rg < p.rows;
+    const int ldl = p.n_heads * D + 8;
+    auto merge = [&]() {
+        const int r = act ? rg : 0;
+        const int ns = p.n_split;
+        const float* part0 = p.part + ((int64_t)r * p.n_heads + hd) * ns * (D + 2);
+        const float mv = (act && t < ns) ? part0[t * (D + 2) + D] : -INFINITY;
+        const float lv = (act && t < ns) ? part0[t * (D + 2) + D + 1] : 0.f;
+        float ov[PRE];
+#pragma unroll
+        for (int j = 0; j < PRE; ++j) ov[j] = (act && j < ns) ? part0[j * (D + 2) + t] : 0.f;
+        const Window w = row_window(p, r);
+        const int n_used = act ? (w.nkeys + KPS - 1) / KPS : 0;
+        float* fs = f_s[rg];
+        if (t < n_used) fs[t] = mv;
+        for (int i = t + D; i < n_used; i += D) fs[i] = part0[i * (D + 2) + D];
+        __syncthreads();
+        if (t < 64) {
+            float M = -INFINITY;
+            for (int i = t; i < n_used; i += 64) M = fmaxf(M, fs[i]);
+            M = wave_max(M);
+            if (t == 0) red[rg] = M;
+        }
+        __syncthreads();
+        const float M = red[rg];
+        float Lp = 0.f;
+        if (t < n_used) {
+            const float f = __expf(mv - M);
+            Lp = lv * f;
+            fs[t] = f;
+        }
+        for (int i = t + D; i < n_used; i += D) {
+            const float f = __expf(fs[i] - M);
+            Lp = fmaf(part0[i * (D + 2) + D + 1], f, Lp);
+            fs[i] = f;
+        }
+        Lp = wave_sum(Lp);
+        if ((t & 63) == 0) l2[rg][t >> 6] = Lp;
+        __syncthreads();
+        float o = 0.f;
+#pragma unroll
+        for (int j = 0; j < PRE; ++j)
+            if (j < n_used) o = fmaf(ov[j], fs[j], o);
+        for (int i = PRE; i < n_used; ++i) o = fmaf(part0[i * (D + 2) + t], fs[i], o);
+        if (act) xl[rg * ldl + hd * D + t] = f2h(o / (l2[rg][0] + l2[rg][1]));
+    };
+    const int tile = g * 8 + wave;
+    const bool on = tile * 16 < n_out;
+    const uint8_t* tp[1] = {wo + (int64_t)(on ? tile : 0) * nchunks * Geom<FMT>::CB};
+    const int c0 = hd * CPH, c1 = on ? c0 + CPH : c0;
+    float4v acc[1][1] = {{float4v{0.f, 0.f, 0.f, 0.f}}};
+    kloop_lds<FMT, 1, 1, decltype(merge), CPH>(tp, c0, c1, merge, xl, ldl, p.rows, p.n_heads * D / 32, lane, acc);
+    if (!on) return;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int tok = 4 * (lane >> 4) + v, row = tile * 16 + (lane & 15);
+        if (tok < p.rows && row < n_out) unsafeAtomicAdd(h + (int64_t)tok * ldh + row, acc[0][0][v]);
+    }
+}
+
+bool attn_merge_o_ok(const AttnParams& p, int fmt, int n_out) {
+    if (p.rows < 1 || p.rows > 4 || p.head_dim != 128 || n_out % 16 != 0) return false;
+    return fmt == OCRDEC_F16 || fmt == OCRDEC_Q8_0 || fmt == OCRDEC_Q4_0 || fmt == OCRDEC_U8A_G32;
+}
+
+void launch_attn_merge_o(const AttnParams& p0, int fmt, const uint8_t* wo, int n_out, float* h, int64_t ldh,
+                         hipStream_t s) {
+    AttnParams p = p0;
+    p.n_split = attn_n_split(p.cache_cap);
+    dim3 g1(p.n_split, p.n_heads, p.rows);
+    if (p.k_scale) hipLaunchKernelGGL((attn_partial_kernel<128, true>), g1, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((attn_partial_kernel<128, false>), g1, dim3(256), 0, s, p);
+    const int HD = p.n_heads * 128;
+    const int64_t nch = n_chunks(fmt, HD);
+    const size_t lds = (size_t)p.rows * (HD + 8) * 2;
+    dim3 g2((n_out / 16 + 7) / 8, p.n_heads);
+#define OCR_MO(F_) \
+    case F_: hipLaunchKernelGGL(attn_merge_o_kernel<F_>, g2, dim3(512), lds, s, p, wo, n_out, nch, h, ldh); break;
+    switch (fmt) {
+        OCR_MO(OCRDEC_F16)
+        OCR_MO(OCRDEC_Q8_0)
+        OCR_MO(OCRDEC_Q4_0)
+        OCR_MO(OCRDEC_U8A_G32)
+    }
+#undef OCR_MO
 }
 
 int attn_n_split(int cache_cap) { return (cache_cap + KPS - 1) / KPS; }
