@@ -172,6 +172,48 @@ OCR_DEV void group_pairs_small(const MoeParams& p, const int* idx_s, unsigned lo
         for (int e = tid; e <= E; e += blockDim.x) p.cap_offsets[e] = offsets_s[e];
 }
 
+// The grouping of group_pairs_small for one row, in wavefront 0 alone: the
+// row's top_k experts are distinct, so every routed expert gets one token
+// and an expert's entry, slot and place in the work list is the rank of its
+// id among the chosen ones.  Same outputs as group_pairs_small with rows = 1
+// (shared experts' entries first, then the routed ones by expert id).
+OCR_DEV void group_one_row(const MoeParams& p, const int* idx_s) {
+    const int lane = threadIdx.x & 63;
+    const int E = p.n_experts, K = p.top_k, S = p.n_shared;
+    const int e = lane < K ? idx_s[lane] : 0x7fffffff;
+    // (a forced choice may repeat an expert: equal ids rank by choice, one
+    // entry per token, which the expert kernels treat like one of two tokens)
+    int rank = 0;
+    for (int j = 0; j < K; ++j) {
+        const int ej = __shfl(e, j, 64);
+        rank += (ej < e || (ej == e && j < lane)) ? 1 : 0;
+    }
+    if (lane < K) {
+        p.virt[S + rank] = make_int4(e, rank, 1, 0);
+        p.perm[rank] = lane;
+        p.inv[lane] = rank;
+        p.vrows[rank] = 0;
+        if (p.cap_perm) p.cap_perm[rank] = lane;
+    }
+    if (lane < S) {
+        p.virt[lane] = make_int4(E + lane, K + lane, 1, 0);
+        p.vrows[K + lane] = 0;
+    }
+    if (lane == 0) p.n_virt[0] = S + K;
+    if (p.cap_counts || p.cap_offsets) {
+        for (int x = lane; x <= E; x += 64) {
+            int chosen = 0, below = 0;
+            for (int j = 0; j < K; ++j) {
+                const int ej = __shfl(e, j, 64);
+                chosen += ej == x ? 1 : 0;
+                below += ej < x ? 1 : 0;
+            }
+            if (p.cap_counts && x < E) p.cap_counts[x] = chosen;
+            if (p.cap_offsets) p.cap_offsets[x] = below;
+        }
+    }
+}
+
 // Scratch of the grouping: LDS for decode-sized batches, the workspace
 // otherwise (generic pointers serve both).
 struct GroupScratch {
@@ -760,6 +802,11 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
         __syncthreads();
     }
     topk_rows(p, lg_s, E, nullptr, use_s);
+    if (R == 1) {
+        // wavefront 0 chose the row's experts and groups them itself
+        if (wave == 0) group_one_row(p, use_s);
+        return;
+    }
     __syncthreads();
     group_pairs_small(p, use_s, mask_s, counts_s, offsets_s);
 }
