@@ -340,6 +340,46 @@ def test_moe_q8_parity(q, rows):
     _moe_case(q, rows, 1002 + rows)
 
 
+# One row with a forced choice that names one expert twice: the one-row
+# grouping in the routing kernel gives each of the two tokens its own entry
+# (the general grouping would make one entry of two); the output, the
+# weights and the captured counts, offsets and permutation are the same.
+def test_moe_one_row_forced_repeat(q):
+    import torch
+    _say("moe one row forced with a repeated expert")
+    H, E, K, S, F = 1280, 64, 6, 2, 896
+    d = synth.Dims(hidden=H, n_experts=E, top_k=K, n_shared=S, expert_ff=F, fmt_router=synth.Q8_0,
+                   fmt_expert=synth.Q4_0, fmt_shared=synth.Q4_0)
+    lay = _Lay()
+    for k_, v_ in synth.make_moe_weights(d, 1201, 0).items():
+        setattr(lay, k_, v_)
+    lay.router_bias = None
+    x = synth.normal_f16(synth.stream_id(1201, "x"), (1, H))
+    h = synth.normal_f16(synth.stream_id(1201, "h"), (1, H))
+    forced = np.array([[40, 5, 63, 5, 0, 17]], np.int32)
+    w, keep = q.moe_weights(lay, H, K)
+    xd, hd = f16_tensor(x), f16_tensor(h)
+    ft = torch.from_numpy(forced).cuda()
+    cap_w = torch.zeros((1, K), dtype=torch.float32, device="cuda")
+    counts = torch.zeros(E, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.zeros(K, dtype=torch.int32, device="cuda")
+    cap = q.MoeCapture(None, cap_w.data_ptr(), counts.data_ptr(), offsets.data_ptr(), perm.data_ptr())
+    wsb = q.ocrdec_moe_workspace_bytes(w, 1)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    q.ocrdec_moe_layer(w, 1, xd, hd, True, ft, cap, ws, wsb)
+    torch.cuda.synchronize()
+    out, idx, wt, _ = O.moe(lay, x.astype(np.float64), K, forced_idx=forced)
+    assert np.array_equal(idx, forced)
+    c, o, pm, _ = O.group(idx, E)
+    assert c[5] == 2
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(perm.cpu().numpy(), pm)
+    assert_close(cap_w.cpu().numpy(), wt, "forced weights")
+    assert_close_f16(from_f16_tensor(hd), O.f16(h + out), "moe out")
+
+
 def test_moe_q4_small_parity(q):
     _say("moe q4 small")
     _moe_case(q, 7, 77, H=256, E=16, K=4, S=1, F=128, fmt=synth.Q4_0)
