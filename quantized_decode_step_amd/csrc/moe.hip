@@ -28,7 +28,7 @@ namespace ocrdec {
 // Writes the experts used (forced ones if given) to idx_out [rows][K], their
 // renormalised weights and the captures.
 OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl, const float* bias, int* idx_out, int r0 = 0,
-                       int r1 = -1, int nsl = 1, int64_t lsl = 0) {
+                       int r1 = -1, int nsl = 1, int64_t lsl = 0, float* w_out = nullptr) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int E = p.n_experts, K = p.top_k;
     const float taken = __builtin_nanf("");
@@ -80,6 +80,7 @@ OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl, const float
             const float w = ex / den;
             idx_out[r * K + lane] = use;
             p.w[(int64_t)r * K + lane] = w;
+            if (w_out) w_out[r * K + lane] = w;
             if (p.cap_idx) p.cap_idx[(int64_t)r * K + lane] = own;
             if (p.cap_w) p.cap_w[(int64_t)r * K + lane] = w;
         }
@@ -96,7 +97,7 @@ OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl, const float
 // expert's tokens in blocks of 16.  mask_s: LDS [E][4] u64,
 // counts_s/offsets_s: LDS [E(+1)].
 OCR_DEV void group_pairs_small(const MoeParams& p, const int* idx_s, unsigned long long* mask_s, int* counts_s,
-                               int* offsets_s) {
+                               int* offsets_s, const float* w_s) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int R = p.rows, E = p.n_experts, K = p.top_k, S = p.n_shared;
     const int NP = R * K;
@@ -163,9 +164,13 @@ OCR_DEV void group_pairs_small(const MoeParams& p, const int* idx_s, unsigned lo
         p.perm[pos] = pi;
         p.inv[pi] = pos;
         p.vrows[pos] = pi / K;
+        if (p.sw) p.sw[pos] = w_s[pi];
         if (p.cap_perm) p.cap_perm[pos] = pi;
     }
-    for (int i = tid; i < S * R; i += blockDim.x) p.vrows[NP + i] = i % R;
+    for (int i = tid; i < S * R; i += blockDim.x) {
+        p.vrows[NP + i] = i % R;
+        if (p.sw) p.sw[NP + i] = 1.f;
+    }
     if (p.cap_counts)
         for (int e = tid; e < E; e += blockDim.x) p.cap_counts[e] = counts_s[e];
     if (p.cap_offsets)
@@ -177,7 +182,7 @@ OCR_DEV void group_pairs_small(const MoeParams& p, const int* idx_s, unsigned lo
 // and an expert's entry, slot and place in the work list is the rank of its
 // id among the chosen ones.  Same outputs as group_pairs_small with rows = 1
 // (shared experts' entries first, then the routed ones by expert id).
-OCR_DEV void group_one_row(const MoeParams& p, const int* idx_s) {
+OCR_DEV void group_one_row(const MoeParams& p, const int* idx_s, const float* w_s) {
     const int lane = threadIdx.x & 63;
     const int E = p.n_experts, K = p.top_k, S = p.n_shared;
     const int e = lane < K ? idx_s[lane] : 0x7fffffff;
@@ -193,11 +198,13 @@ OCR_DEV void group_one_row(const MoeParams& p, const int* idx_s) {
         p.perm[rank] = lane;
         p.inv[lane] = rank;
         p.vrows[rank] = 0;
+        if (p.sw) p.sw[rank] = w_s[lane];
         if (p.cap_perm) p.cap_perm[rank] = lane;
     }
     if (lane < S) {
         p.virt[lane] = make_int4(E + lane, K + lane, 1, 0);
         p.vrows[K + lane] = 0;
+        if (p.sw) p.sw[K + lane] = 1.f;
     }
     if (lane == 0) p.n_virt[0] = S + K;
     if (p.cap_counts || p.cap_offsets) {
@@ -744,6 +751,7 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
     __shared__ float4v red[XT * 16 * 64];  // k-split partials of one pass (XT x 16 tokens)
     __shared__ float lg_s[32 * 256];  // logits [32][E <= 256]
     __shared__ int use_s[256], counts_s[256], offsets_s[257];
+    __shared__ float wsel_s[256];
     __shared__ unsigned long long mask_s[4 * 256];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = p.n_experts, T = E / 16, R = p.rows;
@@ -759,8 +767,6 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
     const int c1 = ks < nks ? (int)min((int64_t)(c0 + cper), nch) : c0;
     const uint8_t* tp[1] = {router + (int64_t)tile * nch * CB};
     const int ldl = xlds_stride(H);
-    if (p.tile_cnt)
-        for (int i = threadIdx.x; i < H / 16; i += blockDim.x) p.tile_cnt[i] = 0;
     int staged = 0;
     auto stage = [&]() {
         if (staged) return;
@@ -801,14 +807,14 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
         }
         __syncthreads();
     }
-    topk_rows(p, lg_s, E, nullptr, use_s);
+    topk_rows(p, lg_s, E, nullptr, use_s, 0, -1, 1, 0, p.sw ? wsel_s : nullptr);
     if (R == 1) {
         // wavefront 0 chose the row's experts and groups them itself
-        if (wave == 0) group_one_row(p, use_s);
+        if (wave == 0) group_one_row(p, use_s, wsel_s);
         return;
     }
     __syncthreads();
-    group_pairs_small(p, use_s, mask_s, counts_s, offsets_s);
+    group_pairs_small(p, use_s, mask_s, counts_s, offsets_s, wsel_s);
 }
 
 // Dynamic LDS of route_fused_kernel.
@@ -823,7 +829,7 @@ inline size_t route_lds_bytes(int rows, int H) { return (size_t)rows * (H + 8) *
 // the expert's slots of a, fp32 y[slot][row].
 // ---------------------------------------------------------------------------
 
-template <int FMT, int XT, int KS, bool GLU, bool LDSX>
+template <int FMT, int XT, int KS, bool GLU, bool LDSX, bool HADD = false>
 __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(GroupedParams p) {
     constexpr int CB = Geom<FMT>::CB;
     constexpr int NT = GLU ? 2 : 1;
@@ -856,6 +862,22 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
     const int c0 = ks * cper;
     const int c1 = valid ? (int)min((int64_t)(c0 + cper), p.nchunks) : c0;
     const int nblk = p.k / 32;
+    // residual-adding down projection: the rows and weights of this lane's
+    // slots travel with the weights (they depend only on the entry)
+    int hrow[HADD ? XT : 1][4];
+    float swt[HADD ? XT : 1][4];
+    if constexpr (HADD) {
+        {
+#pragma unroll
+            for (int xt = 0; xt < XT; ++xt)
+#pragma unroll
+                for (int vv = 0; vv < 4; ++vv) {
+                    const int s_ = off + min(16 * xt + 4 * (lane >> 4) + vv, max(cnt - 1, 0));
+                    hrow[xt][vv] = p.vrows[s_];
+                    swt[xt][vv] = p.sw[s_];
+                }
+        }
+    }
     // token passes: the workgroup loops to the largest count among its waves
     int passes = (cnt + 16 * XT - 1) / (16 * XT);
     for (int pass = 0;; ++pass) {
@@ -902,55 +924,16 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
                     } else {
                         const int row = tidx[0] * 16 + (lane & 15);
                         float* yp = (float*)p.y + slot * p.ldy + row;
-                        // folded combine: written at device coherence (past this XCD's L2)
-                        if (p.tile_cnt) __hip_atomic_store(yp, acc[0][xt][vv], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        else *yp = acc[0][xt][vv];
+                        if constexpr (HADD) {
+                            // one pass per entry here (entries of <= 16 tokens)
+                            unsafeAtomicAdd(p.h + (int64_t)hrow[xt][vv] * p.ldh + row, swt[xt][vv] * acc[0][xt][vv]);
+                        } else {
+                            *yp = acc[0][xt][vv];
+                        }
                     }
                 }
         }
         __syncthreads();
-    }
-    if constexpr (!GLU) {
-        // folded combine (at most four rows: lane l serves row l / 16, column
-        // l % 16 of the tile): every valid item of tile g counts itself once
-        // its outputs have reached device coherence (device-scope stores,
-        // then a wait for their completion: no L2 write-back is needed); the
-        // last of the n_virt items reads the tile's outputs with device-scope
-        // loads and adds them into the residual, in the order of
-        // combine_kernel (shared outputs summed, then the routed ones by
-        // rank).  Slots, weights and the residual are fetched before the
-        // count, under the same wait.
-        if (p.tile_cnt && ks == 0 && valid) {
-            const int r = lane >> 4, K = p.top_k, S = p.n_shared, col = g * 16 + (lane & 15);
-            const int rr = r < p.rows ? r : 0;
-            int sl[8];
-            float wr[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                sl[j] = p.inv[rr * K + min(j, K - 1)];
-                wr[j] = p.cw[rr * K + min(j, K - 1)];
-            }
-            const float hv = p.h[(int64_t)rr * p.ldh + col];
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            int old = 0;
-            if (lane == 0) old = __hip_atomic_fetch_add(p.tile_cnt + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            old = __shfl(old, 0);
-            if (old == n_virt - 1 && r < p.rows) {
-                float* y = (float*)p.y;
-                auto yld = [&](int64_t i) { return __hip_atomic_load(y + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-                float ys[8], yr[8];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) ys[s] = yld((int64_t)(s < S ? p.np + s * p.rows + r : 0) * p.ldy + col);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) yr[j] = yld((int64_t)sl[j] * p.ldy + col);
-                float a = 0.f;
-#pragma unroll
-                for (int s = 0; s < 8; ++s) a += s < S ? ys[s] : 0.f;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) a = fmaf(j < K ? wr[j] : 0.f, j < K ? yr[j] : 0.f, a);
-                p.h[(int64_t)r * p.ldh + col] = hv + a;
-            }
-        }
     }
 }
 
@@ -1076,7 +1059,7 @@ MoeWs carve_moe(void* ws, int rows, const ocrdec_moe_weights* w) {
     m.virt = cv.take<int4>(moe_max_virt(rows, w));
     m.a = cv.take<uint16_t>((size_t)nslots * w->d_ff);
     m.y = cv.take<float>((size_t)nslots * w->hidden);
-    m.tile_cnt = cv.take<int32_t>((size_t)w->hidden / 16);
+    m.sw = cv.take<float>(nslots);
     m.bytes = cv.off;
     return m;
 }
@@ -1119,8 +1102,14 @@ void launch_grouped_fmt(const GroupedParams& p, int xt, int ks, bool lds, int gr
     const size_t lb = lds ? lds_x_bytes(p.k, xt) : 0;
 #define OCR_G(XT_, KS_)                                                                                          \
     if (xt == XT_ && ks == KS_) {                                                                               \
-        if (lds) hipLaunchKernelGGL((grouped_kernel<FMT, XT_, KS_, GLU, true>), dim3(grid), dim3(256), lb, s, p); \
-        else hipLaunchKernelGGL((grouped_kernel<FMT, XT_, KS_, GLU, false>), dim3(grid), dim3(256), 0, s, p);    \
+        if (!GLU && p.sw) {                                                                                     \
+            if (lds) hipLaunchKernelGGL((grouped_kernel<FMT, XT_, KS_, GLU, true, !GLU>), dim3(grid), dim3(256), lb, s, p); \
+            else hipLaunchKernelGGL((grouped_kernel<FMT, XT_, KS_, GLU, false, !GLU>), dim3(grid), dim3(256), 0, s, p);    \
+        } else if (lds) {                                                                                       \
+            hipLaunchKernelGGL((grouped_kernel<FMT, XT_, KS_, GLU, true>), dim3(grid), dim3(256), lb, s, p);     \
+        } else {                                                                                                \
+            hipLaunchKernelGGL((grouped_kernel<FMT, XT_, KS_, GLU, false>), dim3(grid), dim3(256), 0, s, p);     \
+        }                                                                                                       \
         return;                                                                                                 \
     }
     OCR_G(1, 1) OCR_G(2, 1) OCR_G(1, 4) OCR_G(2, 4)
@@ -1230,9 +1219,12 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     // the expert GEMM addresses its activations with 32-bit byte offsets
     const bool gemm = moe_gemm_path(rows, w) && (int64_t)(rows - 1) * ldx + H < (1ll << 30) &&
                       (int64_t)(NP + S * rows) * F < (1ll << 30);
-    // up to four rows: the down projection does the combine (fp32 residual)
+    // up to four rows: the down projection adds its weighted outputs into the
+    // fp32 residual itself (atomic adds), no combine kernel
     const bool fused = fuse_combine && small && h_f32 && add_residual && rows <= 4;
-    if (fused) p.tile_cnt = m.tile_cnt;
+    // the grouping also lists every slot's combine weight: the down projection
+    // adds its outputs into the residual itself
+    if (fused) p.sw = m.sw;
     if (norm_in && !small) {
         // the MoE input is the normalised residual: form it first
         hipLaunchKernelGGL(moe_norm_kernel, dim3(rows), dim3(256), 0, s, h_norm, norm_in, H, eps_in, (uint16_t*)x,
@@ -1355,9 +1347,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.ldy = H;
         p.out_tiles = H / 16;
         if (fused) {
-            p.tile_cnt = m.tile_cnt;
-            p.cw = m.w;
-            p.inv = m.inv;
+            p.sw = m.sw;
             p.h = (float*)h;
             p.ldh = ldh;
             p.rows = rows;

@@ -36,7 +36,7 @@ struct MoeParams {
     int32_t* cap_perm;
     int lslices;     // router logits as lslices partial sums, lslice floats apart (0/1: one)
     int64_t lslice;
-    int32_t* tile_cnt;  // non-NULL: zeroed by the routing kernel (hidden / 16 counters)
+    float* sw;          // non-NULL (decode-sized grouping): the combine weight of every grouped slot
 };
 
 struct GroupedParams {
@@ -61,15 +61,13 @@ struct GroupedParams {
     int dense_rows;  // expert GEMM: > 0 means one implicit expert over rows [0, dense_rows) (router)
     int kslices;     // expert GEMM: k range split over this many workgroups (0/1: none), partial
     int64_t ly_slice;  //   products of slice z written ly_slice elements after slice 0's
-    // Grouped down projection with the combine folded in (tile_cnt non-NULL):
-    // the last work item to finish output tile g adds that tile's weighted
-    // expert outputs into the fp32 residual h [rows][ldh].
-    int32_t* tile_cnt;
-    const float* cw;       // [rows * top_k] routing weights
-    const int32_t* inv;    // [rows * top_k] slot of every (row, rank)
+    // Grouped down projection adding into the fp32 residual h [rows][ldh]
+    // itself (sw non-NULL): every output of slot s goes to h[vrows[s]] with
+    // weight sw[s] by an atomic add (no expert-output buffer, no combine).
     float* h;
     int64_t ldh;
     int rows, top_k, n_shared;
+    const float* sw;
 };
 
 struct CombineParams {
@@ -102,7 +100,7 @@ struct MoeWs {
     int4* virt;
     uint16_t* a;
     float* y;
-    int32_t* tile_cnt;
+    float* sw;
     size_t bytes;
 };
 
