@@ -1219,9 +1219,9 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     // the expert GEMM addresses its activations with 32-bit byte offsets
     const bool gemm = moe_gemm_path(rows, w) && (int64_t)(rows - 1) * ldx + H < (1ll << 30) &&
                       (int64_t)(NP + S * rows) * F < (1ll << 30);
-    // up to four rows: the down projection adds its weighted outputs into the
-    // fp32 residual itself (atomic adds), no combine kernel
-    const bool fused = fuse_combine && small && h_f32 && add_residual && rows <= 4;
+    // decode-sized batches with an fp32 residual: the down projection adds its
+    // weighted outputs into the residual itself (atomic adds), no combine kernel
+    const bool fused = fuse_combine && small && h_f32 && add_residual;
     // the grouping also lists every slot's combine weight: the down projection
     // adds its outputs into the residual itself
     if (fused) p.sw = m.sw;
@@ -1357,8 +1357,12 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         if (gemm) launch_expert_gemm(w->down.fmt, false, p, max_virt, s);
         else launch_grouped(w->down.fmt, false, p, rows, s);
     }
-    // combine
-    if (!fused) {
+    // combine, or (down projection added into the residual) the next norm
+    if (fused) {
+        if (norm_w)
+            hipLaunchKernelGGL(moe_norm_kernel, dim3(rows), dim3(256), 0, s, (const float*)h, norm_w, H, eps, x_out,
+                               ldxo);
+    } else {
         CombineParams p{};
         p.rows = rows;
         p.hidden = H;

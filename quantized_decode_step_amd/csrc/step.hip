@@ -453,7 +453,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             const int32_t* fo = forced_topk ? forced_topk + (int64_t)moe_l * R * K : nullptr;
             // the routing kernel forms x = RMSNorm(h) itself
             launch_moe(&L.moe, R, w.x, H, w.h, 1, H, 1, fo, nullptr, ci, cw, w.moe, prolog ? nullptr : next_norm,
-                       m->norm_eps, w.x, H, s, w.h, L.ffn_norm, m->norm_eps, prolog);
+                       m->norm_eps, w.x, H, s, w.h, L.ffn_norm, m->norm_eps, true);
             ++moe_l;
         } else {
             if (!prolog) hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(64), 0, s, w.h, L.ffn_norm, H, m->norm_eps, w.x);
