@@ -327,6 +327,11 @@ typedef struct {
  * between blocks for the same reason: no accumulation of low-precision round
  * trips).  tok_out may alias tok_in (the step reads tok_in before it writes
  * tok_out), so a caller can feed tokens back on the device.
+ * Reproducibility: the MoE's expert outputs (up to 32 rows) and, up to four
+ * rows, the per-head parts of the O projection are added into the fp32
+ * residual with atomic adds, in the order the GPU finishes them; two runs on
+ * the same inputs can therefore differ in the last bits of h, and a token
+ * can differ where two logits are that close.
  *   hidden       fp32 [rows][hidden]: input if tok_in is NULL; output if non-NULL
  *   forced_topk  int32 [n_moe_layers][rows][top_k] or NULL (see ocrdec_moe_layer)
  *   rows         1 .. 32; prefix_cap + ring_cap <= 65536
