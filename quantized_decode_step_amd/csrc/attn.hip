@@ -389,10 +389,10 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnParams p) {
     p.out[(int64_t)r * p.ld_out + h * D + tid] = f2h(o / red[1]);
 }
 
-// Decode of up to four rows with head_dim 128: the merge of each head's
+// Decode of up to eight rows with head_dim 128: the merge of each head's
 // splits and that head's share of the O projection in one launch, in place
 // of the merge kernel, a launch gap and the O projection's GEMV.  Workgroup
-// (g, hd) merges head hd of every row (thread group r < rows, as
+// (g, hd) merges head hd of every row (thread group r takes rows r and r + 4, as
 // attn_combine_kernel: the partials requested before the window is known)
 // into LDS; its eight wavefronts then multiply the merged row with the
 // head's D columns of W_o for the 16-row tiles 8g .. 8g+7 (one tile each;
@@ -410,10 +410,11 @@ __global__ __launch_bounds__(512) void attn_merge_o_kernel(AttnParams p, const u
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = blockIdx.x, hd = blockIdx.y;
     const int rg = tid >> 7, t = tid & 127;
-    const bool act = rg < p.rows;
     const int ldl = p.n_heads * D + 8;
-    auto merge = [&]() {
-        const int r = act ? rg : 0;
+    // thread group rg merges rows rg, rg + 4 (up to eight rows: two passes)
+    auto merge_row = [&](int rr) {
+        const bool act = rr < p.rows;
+        const int r = act ? rr : 0;
         const int ns = p.n_split;
         const float* part0 = p.part + ((int64_t)r * p.n_heads + hd) * ns * (D + 2);
         const float mv = (act && t < ns) ? part0[t * (D + 2) + D] : -INFINITY;
@@ -454,7 +455,14 @@ __global__ __launch_bounds__(512) void attn_merge_o_kernel(AttnParams p, const u
         for (int j = 0; j < PRE; ++j)
             if (j < n_used) o = fmaf(ov[j], fs[j], o);
         for (int i = PRE; i < n_used; ++i) o = fmaf(part0[i * (D + 2) + t], fs[i], o);
-        if (act) xl[rg * ldl + hd * D + t] = f2h(o / (l2[rg][0] + l2[rg][1]));
+        if (act) xl[rr * ldl + hd * D + t] = f2h(o / (l2[rg][0] + l2[rg][1]));
+    };
+    auto merge = [&]() {
+        merge_row(rg);
+        if (p.rows > 4) {
+            __syncthreads();  // this group's LDS scratch is reused
+            merge_row(rg + 4);
+        }
     };
     const int tile = g * 8 + wave;
     const bool on = tile * 16 < n_out;
@@ -471,7 +479,7 @@ __global__ __launch_bounds__(512) void attn_merge_o_kernel(AttnParams p, const u
 }
 
 bool attn_merge_o_ok(const AttnParams& p, int fmt, int n_out) {
-    if (p.rows < 1 || p.rows > 4 || p.head_dim != 128 || n_out % 16 != 0) return false;
+    if (p.rows < 1 || p.rows > 8 || p.head_dim != 128 || n_out % 16 != 0) return false;
     return fmt == OCRDEC_F16 || fmt == OCRDEC_Q8_0 || fmt == OCRDEC_Q4_0 || fmt == OCRDEC_U8A_G32;
 }
 

@@ -424,14 +424,14 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             }
             launch_gemv(L.wqkv.fmt, EPI_F32, pl, gp, s);
         }
-        // attention, and the O projection + residual (up to four rows: the
+        // attention, and the O projection + residual (up to eight rows: the
         // merge of the splits and the projection are one launch)
         AttnParams ap = ap0;
         ap.k_cache = L.k_cache;
         ap.v_cache = L.v_cache;
         ap.k_scale = L.k_scale;
         ap.v_scale = L.v_scale;
-        if (prolog && attn_merge_o_ok(ap, L.wo.fmt, H)) {
+        if (attn_merge_o_ok(ap, L.wo.fmt, H)) {
             launch_attn_merge_o(ap, L.wo.fmt, (const uint8_t*)L.wo.data, H, w.h, H, s);
         } else {
             launch_attn(ap, s);
