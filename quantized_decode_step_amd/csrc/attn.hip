@@ -389,10 +389,10 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnParams p) {
     p.out[(int64_t)r * p.ld_out + h * D + tid] = f2h(o / red[1]);
 }
 
-// Decode of up to eight rows with head_dim 128: the merge of each head's
+// Decode of up to 16 rows with head_dim 128: the merge of each head's
 // splits and that head's share of the O projection in one launch, in place
 // of the merge kernel, a launch gap and the O projection's GEMV.  Workgroup
-// (g, hd) merges head hd of every row (thread group r takes rows r and r + 4, as
+// (g, hd) merges head hd of every row (thread group r takes rows r, r + 4, ..., as
 // attn_combine_kernel: the partials requested before the window is known)
 // into LDS; its eight wavefronts then multiply the merged row with the
 // head's D columns of W_o for the 16-row tiles 8g .. 8g+7 (one tile each;
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(512) void attn_merge_o_kernel(AttnParams p, const u
     const int g = blockIdx.x, hd = blockIdx.y;
     const int rg = tid >> 7, t = tid & 127;
     const int ldl = p.n_heads * D + 8;
-    // thread group rg merges rows rg, rg + 4 (up to eight rows: two passes)
+    // thread group rg merges rows rg, rg + 4, ... (passes of four rows)
     auto merge_row = [&](int rr) {
         const bool act = rr < p.rows;
         const int r = act ? rr : 0;
@@ -459,9 +459,9 @@ __global__ __launch_bounds__(512) void attn_merge_o_kernel(AttnParams p, const u
     };
     auto merge = [&]() {
         merge_row(rg);
-        if (p.rows > 4) {
+        for (int r0 = 4; r0 < p.rows; r0 += 4) {
             __syncthreads();  // this group's LDS scratch is reused
-            merge_row(rg + 4);
+            merge_row(r0 + rg);
         }
     };
     const int tile = g * 8 + wave;
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(512) void attn_merge_o_kernel(AttnParams p, const u
 }
 
 bool attn_merge_o_ok(const AttnParams& p, int fmt, int n_out) {
-    if (p.rows < 1 || p.rows > 8 || p.head_dim != 128 || n_out % 16 != 0) return false;
+    if (p.rows < 1 || p.rows > 16 || p.head_dim != 128 || n_out % 16 != 0) return false;
     return fmt == OCRDEC_F16 || fmt == OCRDEC_Q8_0 || fmt == OCRDEC_Q4_0 || fmt == OCRDEC_U8A_G32;
 }
 

@@ -59,7 +59,7 @@ size_t attn_part_bytes(int rows, int n_heads, int head_dim, int cache_cap);
 size_t attn_ws_bytes(int rows, int n_heads, int head_dim, int cache_cap);
 void attn_set_rope(AttnParams& p, float theta);
 void launch_attn(const AttnParams& p, hipStream_t s);
-// Up to eight rows with head_dim 128: the attention, then the merge of the
+// Up to 16 rows with head_dim 128: the attention, then the merge of the
 // splits fused with the O projection (W_o [n_out][n_heads * 128] in format
 // fmt), added into the fp32 residual h [rows][ldh] with atomic adds.
 bool attn_merge_o_ok(const AttnParams& p, int fmt, int n_out);

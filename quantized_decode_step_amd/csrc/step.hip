@@ -424,7 +424,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             }
             launch_gemv(L.wqkv.fmt, EPI_F32, pl, gp, s);
         }
-        // attention, and the O projection + residual (up to eight rows: the
+        // attention, and the O projection + residual (up to 16 rows: the
         // merge of the splits and the projection are one launch)
         AttnParams ap = ap0;
         ap.k_cache = L.k_cache;
