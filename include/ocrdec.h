@@ -327,7 +327,7 @@ typedef struct {
  * between blocks for the same reason: no accumulation of low-precision round
  * trips).  tok_out may alias tok_in (the step reads tok_in before it writes
  * tok_out), so a caller can feed tokens back on the device.
- * Reproducibility: the MoE's expert outputs (up to 32 rows) and, up to four
+ * Reproducibility: the MoE's expert outputs (up to 32 rows) and, up to 16
  * rows, the per-head parts of the O projection are added into the fp32
  * residual with atomic adds, in the order the GPU finishes them; two runs on
  * the same inputs can therefore differ in the last bits of h, and a token
