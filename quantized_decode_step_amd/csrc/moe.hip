@@ -1350,9 +1350,6 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
             p.sw = m.sw;
             p.h = (float*)h;
             p.ldh = ldh;
-            p.rows = rows;
-            p.top_k = K;
-            p.n_shared = S;
         }
         if (gemm) launch_expert_gemm(w->down.fmt, false, p, max_virt, s);
         else launch_grouped(w->down.fmt, false, p, rows, s);

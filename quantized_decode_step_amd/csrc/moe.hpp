@@ -66,7 +66,6 @@ struct GroupedParams {
     // weight sw[s] by an atomic add (no expert-output buffer, no combine).
     float* h;
     int64_t ldh;
-    int rows, top_k, n_shared;
     const float* sw;
 };
 
