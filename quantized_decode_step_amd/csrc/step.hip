@@ -395,13 +395,13 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     ap0.n_split = attn_n_split(cache_cap);
     ap0.part = w.attn_part;
     attn_set_rope(ap0, m->rope_theta);
-    // Up to eight rows: the kernels that consume a normalised residual (QKV,
+    // Up to 16 rows: the kernels that consume a normalised residual (QKV,
     // the dense MLP, the language head) form RMSNorm(h) in their LDS staging,
     // the attention merge runs inside the O projection and the MoE down
     // projection adds its weighted outputs into the residual, so no separate
     // norm, merge or combine kernel runs.  (With more rows the per-consumer
     // norms cost more than the kernels they replace.)
-    const bool prolog = R <= 8 && lds_x_bytes(H, 1) <= 65536;
+    const bool prolog = R <= 16 && lds_x_bytes(H, 1) <= 65536;
     int moe_l = 0;
     for (int l = 0; l < m->n_layers; ++l) {
         const ocrdec_layer& L = m->layers[l];
