@@ -906,6 +906,10 @@ ocrdec_status check_attn(const ocrdec_attn_args* a) {
     OCR_CHECK_ARG(a->ld_out >= (int64_t)a->n_heads * a->head_dim, "ld_out too small");
     OCR_CHECK_ARG(a->prefix_cap >= 0 && a->ring_cap >= 0 && a->prefix_cap + a->ring_cap >= 1,
                   "prefix_cap and ring_cap must be >= 0 with a non-empty cache");
+    // the merge kernel holds one weight per 64-key split in LDS (1024 splits)
+    OCR_CHECK_ARG((int64_t)a->prefix_cap + a->ring_cap <= 65536, "prefix_cap + ring_cap must be <= 65536");
+    // rows are a grid dimension of the attention kernels
+    OCR_CHECK_ARG(a->rows <= 65535, "rows must be <= 65535");
     OCR_CHECK_ARG(((uintptr_t)a->k_cache & 15) == 0 && ((uintptr_t)a->v_cache & 15) == 0,
                   "caches must be 16-byte aligned");
     OCR_CHECK_ARG((a->k_scale == nullptr) == (a->v_scale == nullptr),

@@ -114,6 +114,16 @@ def test_validation_errors_without_a_device(q):
     a.ld_out = 1280
     assert _err(q, q.ocrdec_attn_decode, a, None, 0, 0) == q.OCRDEC_ERR_WORKSPACE
     assert "need" in q.ocrdec_last_error()
+    # the cache capacity and the row count have hard limits (one merge weight
+    # per 64-key split in LDS; rows are a grid dimension)
+    a.prefix_cap, a.ring_cap = 65536 - 127, 128
+    assert _err(q, q.ocrdec_attn_workspace_bytes, a) == q.OCRDEC_ERR_INVALID_ARG
+    assert "65536" in q.ocrdec_last_error()
+    a.prefix_cap = 65536 - 128
+    assert q.ocrdec_attn_workspace_bytes(a) > 0
+    a.rows = 65536
+    assert _err(q, q.ocrdec_attn_workspace_bytes, a) == q.OCRDEC_ERR_INVALID_ARG
+    a.rows, a.prefix_cap = 1, 100
     r = q.QMatDesc(synth.Q8_0, 64, 1280, fake)
     gu = q.QMatDesc(synth.Q4_0, 64 * 2 * 896, 1280, fake)
     dn = q.QMatDesc(synth.Q4_0, 64 * 1280, 896, fake)

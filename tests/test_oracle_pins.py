@@ -313,6 +313,121 @@ def test_sink_as_65th_lane_equals_sink_logit():
     assert np.allclose(folded, separate, rtol=1e-13)
 
 
+def _u8a_scaled_identities(scales, H):
+    """U8A_G32 matrix [len(scales)*H][H] made of stacked identities, block i
+    scaled by scales[i] (s = scale, z = 0, code 1 on the diagonal)."""
+    n = len(scales) * H
+    q = np.zeros((n, H), np.int64)
+    s = np.zeros((n, H // 32))
+    for i, sc in enumerate(scales):
+        for r in range(H):
+            q[i * H + r, r] = 1
+            s[i * H + r, :] = sc
+    return enc_u8a(s, np.zeros_like(s), q)
+
+
+def test_sink_block_literal_65_lane_construction():
+    """The sink-augmented block against the page's own construction, worked
+    out independently ([FALCON] attention-sink paragraph: queries carry a
+    constant extra lane, the key at cache index 0 carries the sink logit in
+    that lane and its value is 0; the new token's key and value are appended
+    after the cache).
+
+    Projections are stacked identities with distinct scales (q = x, k = x/2,
+    v = 2x), so the q/k/v slices are known.  Each head's input is nonzero only
+    in lane 0, so RoPE moves it within the (0, 32) plane, whose frequency is
+    theta^0 = 1: the rotated query is a*(cos p, sin p) for position p.  The
+    cached keys sit at known angles in that plane and the cached values are
+    one-hot in distinct lanes, so every score and every weight is visible in
+    the output.  The expected output is the plain softmax over 65-lane keys
+    [0, L] (sink slot, cached keys, new key) with scale 1/8, evaluated here
+    from cosines and sines.  A RoPE position of L instead of L - 1, a window
+    that drops the new key or a missing sink term each move the output by far
+    more than the fp16 rounding allowed below."""
+    NH, D, L = 2, 64, 6
+    H = NH * D
+    wqkv = _u8a_scaled_identities([1.0, 0.5, 2.0], H)
+    wo = _u8a_scaled_identities([1.0], H)
+    a = np.array([2.0, 1.5])          # lane 0 of each head
+    b = np.array([4.0, 3.0])          # magnitude of the cached keys
+    phi = np.array([5.0, 1.0, 2.0, 3.0, 4.0])  # angles of cached keys 1..L-1
+    sink = np.array([0.75, -0.5])
+    x = np.zeros(H)
+    x[0], x[D] = a
+    cap = L + 1
+    kc = np.zeros((NH, cap, D))
+    vc = np.zeros((NH, cap, D))
+    for h in range(NH):
+        for j in range(1, L):
+            kc[h, j, 0] = b[h] * np.cos(phi[j - 1])
+            kc[h, j, 32] = b[h] * np.sin(phi[j - 1])
+            vc[h, j, j] = 1.0 + 0.25 * j
+    kc, vc = O.f16(kc), O.f16(vc)
+    y, k_new, v_new, _ = O.sink_attention_block(wqkv, wo, x, kc.copy(), vc.copy(), L, sink, NH, D, 10000.0)
+
+    p = L - 1  # real tokens before the new one (the sink slot is not a token)
+    f16 = lambda v: np.float64(np.float16(v))
+    expect = np.zeros(H)
+    for h in range(NH):
+        qv = np.zeros(65)
+        qv[0], qv[32], qv[64] = f16(a[h] * np.cos(p)), f16(a[h] * np.sin(p)), 1.0
+        kn = np.zeros(D)
+        kn[0], kn[32] = f16(0.5 * a[h] * np.cos(p)), f16(0.5 * a[h] * np.sin(p))
+        assert np.array_equal(k_new[h], kn)
+        vn = np.zeros(D)
+        vn[0] = f16(2.0 * a[h])
+        assert np.array_equal(v_new[h], vn)
+        K65 = np.zeros((L + 1, 65))
+        V = np.zeros((L + 1, D))
+        K65[0, 64] = 8.0 * sink[h]
+        K65[1:L, :D] = kc[h, 1:L]
+        V[1:L] = vc[h, 1:L]
+        K65[L, :D] = kn
+        V[L] = vn
+        s = K65 @ qv / 8.0
+        w = np.exp(s - s.max())
+        w /= w.sum()
+        expect[h * D:(h + 1) * D] = O.f16(w @ V)
+    ulp = np.spacing(np.abs(expect).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(y - expect) <= ulp), np.max(np.abs(y - expect))
+    # the new token carries weight (it is attended) and lane 0 is its alone
+    assert np.all(np.abs(y[[0, D]]) > 0.1)
+
+
+# -----------------------------------------------------------------------------
+# Near-tie classification
+# -----------------------------------------------------------------------------
+
+def test_topk_gap_hand_built():
+    """The gap that decides whether two routings are both correct is the
+    smallest difference between adjacent ranks 1 .. k+1 of the logits: a
+    near-tie between ranks k and k+1 swaps which expert is chosen, one between
+    ranks i < k swaps the order of the chosen ones, one below rank k+1 changes
+    nothing ([NCNN] section 3.4: a tie rule matters only where the candidates
+    are that close)."""
+    E, k = 16, 6
+    perm = np.random.default_rng(3).permutation(E)
+
+    def place(vals):
+        out = np.full(E, -5.0)
+        out[perm[:len(vals)]] = vals
+        return out
+
+    # only the 6th/7th gap is small
+    assert O.topk_gap(place([10, 9, 8, 7, 6, 5, 4.9995, 0]), k) == pytest.approx(5e-4, abs=1e-12)
+    # the 2nd/3rd gap is the smallest
+    assert O.topk_gap(place([10, 9, 8.9999, 7, 6, 5, 4]), k) == pytest.approx(1e-4, abs=1e-12)
+    # a tie below rank k+1 does not count
+    assert O.topk_gap(place([10, 9, 8, 7, 6, 5, 4, 3, 3]), k) == pytest.approx(1.0, abs=1e-12)
+    # an exact tie at ranks k, k+1
+    assert O.topk_gap(place([10, 9, 8, 7, 6, 5, 5]), k) == 0.0
+    # the bias is part of the routed logits: all logits equal, the bias separates them
+    bias = place([3, 2.5, 2, 1.5, 1, 0.5, 0.4997]) + 5.0
+    assert O.topk_gap(np.zeros(E), k, bias) == pytest.approx(3e-4, abs=1e-12)
+    # top-1: the gap between the best and the second
+    assert O.topk_gap(place([2.0, 1.25]), 1) == pytest.approx(0.75, abs=1e-12)
+
+
 # -----------------------------------------------------------------------------
 # Ring window
 # -----------------------------------------------------------------------------
