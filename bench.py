@@ -5,7 +5,9 @@ SwiGLU 3584 in Q4_0, layers 1-11 MoE with 64 routed + 2 shared Q4_0 experts of
 896, top-6; attention and router Q8_0; fp16 embedding and LM head over 129280
 tokens), every row with a 1100-position prefix and a 128-slot ring that starts
 at generation index 100, so the ring wraps during a 64-step run.  All weights,
-caches and first tokens are seeded synthetic data (``synth``).
+caches and first tokens are seeded synthetic data (``synth``).  The ring
+starts at generation index t0 = 128 - warmup - steps // 2 (at least 0), so the
+timed steps straddle the wrap at t = 128 whatever --steps and --warmup are.
 
 A step is one ocrdec_decode_step call for all rows: embedding, 12 layers, final
 norm, LM head with fused argmax; the token feeds the next step on the device.
@@ -26,7 +28,6 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 SEED = 1003
-T0 = 100
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # Counter-measured HBM traffic of the LM-head kernel (rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE runs of `bench.py --mode lm`, calibrated on a copy of known size).  It
@@ -110,8 +111,16 @@ def algorithmic_bytes(dm, d, rows: int, distinct_experts_per_layer: float, avg_k
     return tot
 
 
+def first_gen_index(steps: int, warmup: int, ring: int = 128) -> int:
+    """Generation index of the first warm-up step: the timed steps then run
+    over t = t0 + warmup .. t0 + warmup + steps - 1, which holds t = ring (the
+    first step that overwrites a ring slot) in its middle."""
+    return max(0, ring - warmup - steps // 2)
+
+
 def main():
     args = parse()
+    T0 = first_gen_index(args.steps, args.warmup)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU: the decode step here is single-GPU (no collectives); "
               "use --gpus 1", file=sys.stderr)
@@ -279,7 +288,7 @@ def main():
     # ---- CPU oracle baseline on a bounded sample (1 row of the same workload)
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(model, d, args.cpu_seconds)
+        cpu = cpu_baseline(model, d, args.cpu_seconds, T0)
 
     line = {
         "metric": "decode rows\u00b7steps/s (12-layer MoE step) + achieved HBM GB/s vs peak",
@@ -295,8 +304,9 @@ def main():
         "dtype": "f16",
         "data": "synthetic (seeded weights ~N(0,0.02) quantised Q4_0/Q8_0, caches ~N(0,1))",
         "config": {
-            "workload": "12-layer mixed-Q4_0 MoE OCR decoder decode step: %d row(s), prefix 1100 + 128-slot ring "
-                        "from t=%d, vocab 129280, tokens fed back on device" % (args.rows, T0),
+            "workload": "12-layer mixed-Q4_0 MoE OCR decoder decode step: %d row(s), prefix 1100 + 128-slot ring, "
+                        "timed steps t=%d..%d (the ring wraps at t=128), vocab 129280, tokens fed back on device"
+                        % (args.rows, T0 + args.warmup, T0 + args.warmup + args.steps - 1),
             "rows": args.rows, "layers": d.n_layers, "hidden": d.hidden, "experts": "64 routed top-6 + 2 shared",
             "graph": not args.no_graph,
         },
@@ -575,7 +585,7 @@ def lm_only(args, dm, d, q, torch, dev, stream):
                       "copy_bytes": n, "copy_launches": 3}), flush=True)
 
 
-def cpu_baseline(model, d, budget_s: float):
+def cpu_baseline(model, d, budget_s: float, T0: int):
     """The oracle, as it stands, on one row of the same workload: as many whole
     steps as fit in the budget (at least one)."""
     import synth

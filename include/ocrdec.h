@@ -327,22 +327,51 @@ typedef struct {
  * between blocks for the same reason: no accumulation of low-precision round
  * trips).  tok_out may alias tok_in (the step reads tok_in before it writes
  * tok_out), so a caller can feed tokens back on the device.
- * Reproducibility: the MoE's expert outputs (up to 32 rows) and, up to 16
- * rows, the per-head parts of the O projection are added into the fp32
- * residual with atomic adds, in the order the GPU finishes them; two runs on
- * the same inputs can therefore differ in the last bits of h, and a token
- * can differ where two logits are that close.
+ * The residual is accumulated exactly: every addend (an fp32 projection or
+ * expert output) is rounded once to a multiple of 2^-32 and the sums are
+ * 64-bit integer sums, so the result does not depend on the order in which
+ * the GPU adds the parts, and two runs on the same inputs give the same bits
+ * (tokens, routing, hidden state).  Readers take it as fp32.  Its range is
+ * |h| < 2^30; see ocrdec_device_status for values beyond it.
  *   hidden       fp32 [rows][hidden]: input if tok_in is NULL; output if non-NULL
  *   forced_topk  int32 [n_moe_layers][rows][top_k] or NULL (see ocrdec_moe_layer)
  *   rows         1 .. 32; prefix_cap + ring_cap <= 65536
  * Workspace: ocrdec_step_workspace_bytes(m, st) bytes (it depends on rows and
- * the cache capacity of the state).
+ * the cache capacity of the state).  Its first bytes hold the step's device
+ * status word (ocrdec_device_status).
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, DEVICE. */
 ocrdec_status ocrdec_step_workspace_bytes(const ocrdec_model* m, const ocrdec_state* st, size_t* bytes);
 ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_state* st, const int32_t* tok_in,
                                  float* hidden, int32_t* tok_out, const int32_t* forced_topk,
                                  const ocrdec_step_capture* capture, void* ws, size_t ws_bytes,
                                  void* stream);
+
+/* Device-side conditions of the most recent ocrdec_decode_step that used the
+ * workspace `ws` (the Falcon-OCR card, "Two traps the host must avoid": a
+ * wrong cache length or position does not fail, it yields fluent but
+ * degenerate text; the Unlimited-OCR page, "Memoria": what cannot be served
+ * is rejected with a detailed error).  The step cannot return these through
+ * its status (it is asynchronous), so it records them on the device: each
+ * step clears the bits in its first kernel and sets them as it runs.
+ *   OCRDEC_DEV_TOKEN_RANGE  a tok_in id outside [0, vocab) was clamped
+ *   OCRDEC_DEV_RESIDUAL     a non-finite value, or one of magnitude >= 2^30,
+ *                           was to enter the residual (it was replaced by 0)
+ *   OCRDEC_DEV_LOGIT        a language-head logit was NaN or infinite (a NaN
+ *                           never wins the argmax)
+ *   OCRDEC_DEV_NO_TOKEN     a row had no finite best logit; its token was set
+ *                           to 0
+ * The call synchronises `stream` (the stream the step ran on), then reads the
+ * bits into *flags (0: nothing to report).  It does not clear them.
+ *   ws, ws_bytes  the step's workspace (device) and its size
+ * Errors: INVALID_ARG (NULL pointers), WORKSPACE (ws_bytes smaller than the
+ * status area), DEVICE (synchronisation or copy failed). */
+typedef enum {
+    OCRDEC_DEV_TOKEN_RANGE = 1,
+    OCRDEC_DEV_RESIDUAL = 2,
+    OCRDEC_DEV_LOGIT = 4,
+    OCRDEC_DEV_NO_TOKEN = 8
+} ocrdec_device_flag;
+ocrdec_status ocrdec_device_status(const void* ws, size_t ws_bytes, void* stream, uint32_t* flags);
 
 /* ------------------------------------------------------------------------ */
 /* ocrdec_prefill: the prompt pass of one row                                */

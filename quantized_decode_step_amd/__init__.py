@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libocrdec.so")
 OCRDEC_OK, OCRDEC_ERR_INVALID_ARG, OCRDEC_ERR_UNSUPPORTED, OCRDEC_ERR_WORKSPACE, OCRDEC_ERR_DEVICE = range(5)
 OCRDEC_F16, OCRDEC_Q8_0, OCRDEC_Q4_0, OCRDEC_U8A_G32 = range(4)
 OCRDEC_OUT_F32, OCRDEC_OUT_F16 = 0, 1
+OCRDEC_DEV_TOKEN_RANGE, OCRDEC_DEV_RESIDUAL, OCRDEC_DEV_LOGIT, OCRDEC_DEV_NO_TOKEN = 1, 2, 4, 8
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libocrdec.so is not built: run `python quantized_decode_step_amd/build.py` "
@@ -112,13 +113,14 @@ _lib.ocrdec_prefill_batch.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _vp, _
                                       _P(StepCapture), _vp, _sz, _vp]
 _lib.ocrdec_round_workspace_bytes.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _P(_sz)]
 _lib.ocrdec_run_round.argtypes = [_P(ModelDesc), _P(StateDesc), _vp, _i32, _vp, _i32, _i32, _vp, _sz, _vp]
+_lib.ocrdec_device_status.argtypes = [_vp, _sz, _vp, _P(ctypes.c_uint32)]
 _lib.ocrdec_prefill.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _P(StepCapture),
                                 _vp, _sz, _vp]
 for _fn in ("ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack", "ocrdec_gemv_q", "ocrdec_lm_argmax_workspace_bytes",
             "ocrdec_lm_argmax", "ocrdec_attn_workspace_bytes",
             "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes", "ocrdec_moe_layer", "ocrdec_step_workspace_bytes",
             "ocrdec_decode_step", "ocrdec_prefill_workspace_bytes", "ocrdec_prefill", "ocrdec_round_workspace_bytes",
-            "ocrdec_run_round", "ocrdec_prefill_batch_workspace_bytes", "ocrdec_prefill_batch"):
+            "ocrdec_run_round", "ocrdec_prefill_batch_workspace_bytes", "ocrdec_prefill_batch", "ocrdec_device_status"):
     getattr(_lib, _fn).restype = ctypes.c_int
 
 EXPORTED = ["ocrdec_last_error", "ocrdec_version", "ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack",
@@ -126,7 +128,7 @@ EXPORTED = ["ocrdec_last_error", "ocrdec_version", "ocrdec_packed_bytes", "ocrde
             "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes",
             "ocrdec_moe_layer", "ocrdec_step_workspace_bytes", "ocrdec_decode_step",
             "ocrdec_prefill_workspace_bytes", "ocrdec_prefill", "ocrdec_round_workspace_bytes", "ocrdec_run_round",
-            "ocrdec_prefill_batch_workspace_bytes", "ocrdec_prefill_batch"]
+            "ocrdec_prefill_batch_workspace_bytes", "ocrdec_prefill_batch", "ocrdec_device_status"]
 
 
 def _ptr(t) -> int | None:
@@ -228,6 +230,13 @@ def ocrdec_decode_step(m: ModelDesc, st: StateDesc, tok_in=None, hidden=None, to
     _check(_lib.ocrdec_decode_step(ctypes.byref(m), ctypes.byref(st), _ptr(tok_in), _ptr(hidden), _ptr(tok_out),
                                    _ptr(forced_topk), ctypes.byref(capture) if capture is not None else None,
                                    _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def ocrdec_device_status(ws, ws_bytes: int, stream=None) -> int:
+    """Flags (OCRDEC_DEV_*) of the last decode step that used `ws`; synchronises the stream."""
+    f = ctypes.c_uint32()
+    _check(_lib.ocrdec_device_status(_ptr(ws), ws_bytes, _stream(stream), ctypes.byref(f)))
+    return f.value
 
 
 class Request(ctypes.Structure):

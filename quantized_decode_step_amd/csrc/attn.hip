@@ -397,12 +397,12 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnParams p) {
 // into LDS; its eight wavefronts then multiply the merged row with the
 // head's D columns of W_o for the 16-row tiles 8g .. 8g+7 (one tile each;
 // the weights were requested before the merge) and add the products into
-// the fp32 residual with atomic adds.  The residual receives one addend per
-// head in the order the workgroups finish, so it is not bitwise reproducible
-// from run to run (the sum itself is fp32 either way).
+// the fixed-point residual with atomic integer adds: the residual receives one
+// addend per head in the order the workgroups finish, and the integer sum is
+// the same in any order.
 template <int FMT>
 __global__ __launch_bounds__(512) void attn_merge_o_kernel(AttnParams p, const uint8_t* wo, int n_out, int64_t nchunks,
-                                                           float* h, int64_t ldh) {
+                                                           fix_t* h, int64_t ldh, uint32_t* status) {
     constexpr int D = 128, PRE = 24, KC = 32 * Geom<FMT>::SB, CPH = D / KC;
     extern __shared__ __align__(16) uint16_t xl[];  // [rows][n_heads * D + 8] fp16: head hd's columns
     __shared__ float f_s[4][1024 + 1];
@@ -471,11 +471,13 @@ __global__ __launch_bounds__(512) void attn_merge_o_kernel(AttnParams p, const u
     float4v acc[1][1] = {{float4v{0.f, 0.f, 0.f, 0.f}}};
     kloop_lds<FMT, 1, 1, decltype(merge), CPH>(tp, c0, c1, merge, xl, ldl, p.rows, p.n_heads * D / 32, lane, acc);
     if (!on) return;
+    bool bad = false;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int tok = 4 * (lane >> 4) + v, row = tile * 16 + (lane & 15);
-        if (tok < p.rows && row < n_out) unsafeAtomicAdd(h + (int64_t)tok * ldh + row, acc[0][0][v]);
+        if (tok < p.rows && row < n_out) fix_atomic_add(h + (int64_t)tok * ldh + row, acc[0][0][v], bad);
     }
+    report_status(status, bad, kStatResidual);
 }
 
 bool attn_merge_o_ok(const AttnParams& p, int fmt, int n_out) {
@@ -483,8 +485,8 @@ bool attn_merge_o_ok(const AttnParams& p, int fmt, int n_out) {
     return fmt == OCRDEC_F16 || fmt == OCRDEC_Q8_0 || fmt == OCRDEC_Q4_0 || fmt == OCRDEC_U8A_G32;
 }
 
-void launch_attn_merge_o(const AttnParams& p0, int fmt, const uint8_t* wo, int n_out, float* h, int64_t ldh,
-                         hipStream_t s) {
+void launch_attn_merge_o(const AttnParams& p0, int fmt, const uint8_t* wo, int n_out, fix_t* h, int64_t ldh,
+                         uint32_t* status, hipStream_t s) {
     AttnParams p = p0;
     p.n_split = attn_n_split(p.cache_cap);
     dim3 g1(p.n_split, p.n_heads, p.rows);
@@ -495,7 +497,7 @@ void launch_attn_merge_o(const AttnParams& p0, int fmt, const uint8_t* wo, int n
     const size_t lds = (size_t)p.rows * (HD + 8) * 2;
     dim3 g2((n_out / 16 + 7) / 8, p.n_heads);
 #define OCR_MO(F_) \
-    case F_: hipLaunchKernelGGL(attn_merge_o_kernel<F_>, g2, dim3(512), lds, s, p, wo, n_out, nch, h, ldh); break;
+    case F_: hipLaunchKernelGGL(attn_merge_o_kernel<F_>, g2, dim3(512), lds, s, p, wo, n_out, nch, h, ldh, status); break;
     switch (fmt) {
         OCR_MO(OCRDEC_F16)
         OCR_MO(OCRDEC_Q8_0)

@@ -61,10 +61,11 @@ void attn_set_rope(AttnParams& p, float theta);
 void launch_attn(const AttnParams& p, hipStream_t s);
 // Up to 16 rows with head_dim 128: the attention, then the merge of the
 // splits fused with the O projection (W_o [n_out][n_heads * 128] in format
-// fmt), added into the fp32 residual h [rows][ldh] with atomic adds.
+// fmt), added into the fixed-point residual h [rows][ldh] with atomic integer
+// adds (order-independent).
 bool attn_merge_o_ok(const AttnParams& p, int fmt, int n_out);
-void launch_attn_merge_o(const AttnParams& p, int fmt, const uint8_t* wo, int n_out, float* h, int64_t ldh,
-                         hipStream_t s);
+void launch_attn_merge_o(const AttnParams& p, int fmt, const uint8_t* wo, int n_out, fix_t* h, int64_t ldh,
+                         uint32_t* status, hipStream_t s);
 ocrdec_status check_attn(const ocrdec_attn_args* a);
 
 }  // namespace ocrdec

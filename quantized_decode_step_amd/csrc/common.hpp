@@ -202,12 +202,61 @@ OCR_DEV half8v deq_u8(uint32_t lo, uint32_t hi) {
 
 OCR_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// x = fp16(h / sqrt(mean(h^2) + eps) * gamma) for one fp32 row of
+// ---------------------------------------------------------------------------
+// The decode step's residual stream in exact fixed point
+//
+// h is held as int64 with 32 fraction bits.  Every addend (an fp32 projection
+// output) is converted once, rounded to the nearest multiple of 2^-32, and
+// the sums are integer sums: exact and independent of the order in which
+// workgroups add their parts (atomic adds included), so the step is bitwise
+// reproducible.  The range is |h| < 2^30; a non-finite addend or one beyond
+// the range is replaced by 0 and reported through the status word.  Readers
+// convert to fp32 (correctly rounded through fp64).
+// ---------------------------------------------------------------------------
+
+typedef long long fix_t;
+constexpr float kFixLimit = 1073741824.0f;  // 2^30
+
+// Status word bits (the decode step's workspace; ocrdec_device_status).
+constexpr uint32_t kStatTokenRange = 1u, kStatResidual = 2u, kStatLogit = 4u, kStatNoToken = 8u;
+
+OCR_DEV fix_t fix_from(float a, bool& bad) {
+    const bool ok = fabsf(a) < kFixLimit;  // false for NaN
+    bad |= !ok;
+    return ok ? (fix_t)__builtin_rint((double)a * 4294967296.0) : 0;
+}
+OCR_DEV float fix_to(fix_t v) { return (float)((double)v * (1.0 / 4294967296.0)); }
+
+// Four consecutive residual values (fp32 or fixed point) at index 4*c4.
+OCR_DEV float4 ld_resid4(const float* h, int c4) { return ((const float4*)h)[c4]; }
+OCR_DEV float4 ld_resid4(const fix_t* h, int c4) {
+    const longlong2 a = ((const longlong2*)h)[2 * c4], b = ((const longlong2*)h)[2 * c4 + 1];
+    return make_float4(fix_to(a.x), fix_to(a.y), fix_to(b.x), fix_to(b.y));
+}
+OCR_DEV void st_resid4(float* h, int c4, float4 v, bool&) { ((float4*)h)[c4] = v; }
+OCR_DEV void st_resid4(fix_t* h, int c4, float4 v, bool& bad) {
+    ((longlong2*)h)[2 * c4] = make_longlong2(fix_from(v.x, bad), fix_from(v.y, bad));
+    ((longlong2*)h)[2 * c4 + 1] = make_longlong2(fix_from(v.z, bad), fix_from(v.w, bad));
+}
+
+// h[i] += a as an atomic integer add (any order gives the same sum).
+OCR_DEV void fix_atomic_add(fix_t* h, float a, bool& bad) {
+    atomicAdd((unsigned long long*)h, (unsigned long long)fix_from(a, bad));
+}
+
+// Sets `bits` in the status word if any lane of the wavefront raised `flag`
+// (one atomic per wavefront).
+OCR_DEV void report_status(uint32_t* status, bool flag, uint32_t bits) {
+    const unsigned long long m = __ballot(flag);
+    if (status && m && (threadIdx.x & 63) == (unsigned)__builtin_ctzll(m)) atomicOr(status, bits);
+}
+
+// x = fp16(h / sqrt(mean(h^2) + eps) * gamma) for one residual row (fp32 or fixed point) of
 // H <= 256 * NV values (H % 4 == 0) by one wavefront: every load (row and
 // gain) is issued before the first use, so the row costs one memory round
 // trip.  The result goes to x and to xl (LDS), each if non-NULL.
-template <int NV = 16>
-OCR_DEV void wave_rmsnorm_row(const float* h, const uint16_t* gamma, int H, float eps, uint16_t* x,
+template <int NV = 16, class HT = float>
+OCR_DEV void wave_rmsnorm_row(const HT* h, const uint16_t* gamma, int H, float eps, uint16_t* x,
                               uint16_t* xl = nullptr) {
     const int lane = threadIdx.x & 63;
     const int n4 = H / 4;
@@ -216,7 +265,7 @@ OCR_DEV void wave_rmsnorm_row(const float* h, const uint16_t* gamma, int H, floa
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int c4 = lane + 64 * i;
-        v[i] = c4 < n4 ? ((const float4*)h)[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[i] = c4 < n4 ? ld_resid4(h, c4) : make_float4(0.f, 0.f, 0.f, 0.f);
         g[i] = c4 < n4 ? ((const uint2*)gamma)[c4] : make_uint2(0, 0);
     }
     float ss = 0.f;

@@ -46,9 +46,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
         // residual epilogue: the residual values are requested now, so that
         // the add does not wait a memory round trip after the k-loop (every
         // output element belongs to one workgroup: nobody else writes it)
-        float hpre[(EPI == EPI_RESID) ? NT : 1][(EPI == EPI_RESID) ? XT : 1][4];
+        fix_t hpre[(EPI == EPI_RESID) ? NT : 1][(EPI == EPI_RESID) ? XT : 1][4];
         if constexpr (EPI == EPI_RESID) {
-            const float* h = (const float*)p.y;
+            const fix_t* h = (const fix_t*)p.y;
 #pragma unroll
             for (int i = 0; i < NT; ++i)
 #pragma unroll
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
                         const int tok = tok0 + 16 * xt + 4 * (lane >> 4) + v;
                         const int row = tidx[i] * 16 + (lane & 15);
                         const bool in = ks == 0 && valid && tok < p.xs.rows && row < p.n;
-                        hpre[i][xt][v] = in ? h[(int64_t)tok * p.ldy + row] : 0.f;
+                        hpre[i][xt][v] = in ? h[(int64_t)tok * p.ldy + row] : 0;
                     }
         }
         if constexpr (XSRC != X_GLOBAL) {
@@ -77,6 +77,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
             // per token: best value, its row (lowest on ties), second-best value
             float best[XT][4], second[XT][4];
             int bidx[XT][4];
+            bool nonfin = false;
 #pragma unroll
             for (int xt = 0; xt < XT; ++xt)
 #pragma unroll
@@ -95,6 +96,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
 #pragma unroll
                             for (int v = 0; v < 4; ++v) {
                                 float val = acc[i][xt][v];
+                                nonfin |= !(fabsf(val) < INFINITY);
                                 if (val > best[xt][v]) {
                                     second[xt][v] = best[xt][v];
                                     best[xt][v] = val;
@@ -131,7 +133,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
                         e[2] = second[xt][v];
                     }
             }
-            __syncthreads();
+            // a non-finite logit anywhere in the workgroup is recorded with
+            // every token's partial (the final merge ORs the flags)
+            const int wg_nonfin = __syncthreads_or(nonfin ? 1 : 0);
             if (threadIdx.x < 16 * XT) {
                 const int tok = threadIdx.x;
                 float b = -INFINITY, s = -INFINITY;
@@ -141,13 +145,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
                     argmax_merge(b, bi, s, e[0], __float_as_int(e[1]), e[2]);
                 }
                 if (tok0 + tok < p.xs.rows) {
-                    float* out = p.part + ((int64_t)blockIdx.x * p.xs.rows + tok0 + tok) * 3;
+                    float* out = p.part + ((int64_t)blockIdx.x * p.xs.rows + tok0 + tok) * 4;
                     out[0] = b;
                     out[1] = __int_as_float(bi);
                     out[2] = s;
+                    out[3] = __int_as_float(wg_nonfin ? (int)kStatLogit : 0);
                 }
             }
-        } else if (owner) {
+        } else {
+            bool bad = false;
+            if (owner) {
 #pragma unroll
             for (int xt = 0; xt < XT; ++xt)
 #pragma unroll
@@ -171,11 +178,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
                             } else if constexpr (EPI == EPI_F16) {
                                 ((uint16_t*)p.y)[o] = f2h(acc[i][xt][v]);
                             } else if constexpr (EPI == EPI_RESID) {
-                                ((float*)p.y)[o] = hpre[i][xt][v] + acc[i][xt][v];
+                                ((fix_t*)p.y)[o] = hpre[i][xt][v] + fix_from(acc[i][xt][v], bad);
                             }
                         }
                     }
                 }
+            }
+            if constexpr (EPI == EPI_RESID) report_status(p.status, bad, kStatResidual);
         }
         __syncthreads();
     }
@@ -261,7 +270,7 @@ void launch_gemv(int fmt, int epi, const GemvPlan& plan, GemvParams p, hipStream
 #undef OCR_E
 }
 
-size_t argmax_ws_bytes(int grid, int rows) { return align256((size_t)grid * rows * 3 * sizeof(float)); }
+size_t argmax_ws_bytes(int grid, int rows) { return align256((size_t)grid * rows * 4 * sizeof(float)); }
 
 // ---------------------------------------------------------------------------
 // LM head with fused argmax for up to 16 rows, balanced within each CU
@@ -310,6 +319,7 @@ __global__ __launch_bounds__(64 * LM_WAVES, 1) void lm_argmax_kernel(GemvParams 
     int unxt = grab();
     float best[4], second[4];
     int bidx[4];
+    bool nonfin = false;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         best[v] = -INFINITY;
@@ -341,6 +351,7 @@ __global__ __launch_bounds__(64 * LM_WAVES, 1) void lm_argmax_kernel(GemvParams 
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const float val = acc[0][0][v];
+                nonfin |= !(fabsf(val) < INFINITY);
                 if (val > best[v]) {
                     second[v] = best[v];
                     best[v] = val;
@@ -371,7 +382,7 @@ __global__ __launch_bounds__(64 * LM_WAVES, 1) void lm_argmax_kernel(GemvParams 
             e[2] = second[v];
         }
     }
-    __syncthreads();
+    const int wg_nonfin = __syncthreads_or(nonfin ? 1 : 0);
     if ((int)threadIdx.x < R) {
         const int tok = threadIdx.x;
         float b = -INFINITY, s2 = -INFINITY;
@@ -380,10 +391,11 @@ __global__ __launch_bounds__(64 * LM_WAVES, 1) void lm_argmax_kernel(GemvParams 
             const float* e = amx + (w * 16 + tok) * 3;
             argmax_merge(b, bi, s2, e[0], __float_as_int(e[1]), e[2]);
         }
-        float* out = p.part + ((int64_t)blockIdx.x * R + tok) * 3;
+        float* out = p.part + ((int64_t)blockIdx.x * R + tok) * 4;
         out[0] = b;
         out[1] = __int_as_float(bi);
         out[2] = s2;
+        out[3] = __int_as_float(wg_nonfin ? (int)kStatLogit : 0);
     }
 }
 
@@ -444,8 +456,12 @@ void launch_lm_argmax(int fmt, const LmPlan& lp, GemvParams p, hipStream_t s) {
 // Merge of the per-workgroup (best, index, second) partials: one workgroup
 // per row, a strided pass then a tree in LDS (the merge is associative and
 // commutative, so the result does not depend on the order).
+//
+// Status: a non-finite logit seen by any workgroup sets kStatLogit; a row
+// without a finite winner (every logit NaN or -inf) gets token 0 and sets
+// kStatNoToken.
 __global__ __launch_bounds__(256) void argmax_final_kernel(const float* part, int n_wg, int rows, int32_t* tok_out,
-                                                           float* top2, int32_t* gen_index) {
+                                                           float* top2, int32_t* gen_index, uint32_t* status) {
     __shared__ float sb[4], ss[4];
     __shared__ int si[4];
     const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -453,10 +469,13 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const float* part, in
     const int gi = (gen_index && tid == 0) ? gen_index[r] : 0;
     float b = -INFINITY, s = -INFINITY;
     int bi = 0x7fffffff;
+    int fl = 0;
     for (int w = tid; w < n_wg; w += blockDim.x) {
-        const float* e = part + ((int64_t)w * rows + r) * 3;
+        const float* e = part + ((int64_t)w * rows + r) * 4;
         argmax_merge(b, bi, s, e[0], __float_as_int(e[1]), e[2]);
+        fl |= __float_as_int(e[3]);
     }
+    fl = __syncthreads_or(fl);
     for (int o = 32; o > 0; o >>= 1) {
         const float b2 = __shfl_xor(b, o, 64), s2 = __shfl_xor(s, o, 64);
         const int i2 = __shfl_xor(bi, o, 64);
@@ -471,6 +490,8 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const float* part, in
     if (tid == 0) {
         for (int w = 1; w < (int)(blockDim.x >> 6); ++w) argmax_merge(b, bi, s, sb[w], si[w], ss[w]);
         if (tok_out) tok_out[r] = (bi == 0x7fffffff) ? 0 : bi;
+        const uint32_t st = (uint32_t)(fl ? kStatLogit : 0) | (bi == 0x7fffffff ? kStatNoToken : 0);
+        if (status && st) atomicOr(status, st);
         if (top2) {
             top2[2 * r] = b;
             top2[2 * r + 1] = s;
@@ -480,8 +501,9 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const float* part, in
 }
 
 void launch_argmax_final(const float* part, int n_wg, int rows, int32_t* tok_out, float* top2, int32_t* gen_index,
-                         hipStream_t s) {
-    hipLaunchKernelGGL(argmax_final_kernel, dim3(rows), dim3(256), 0, s, part, n_wg, rows, tok_out, top2, gen_index);
+                         uint32_t* status, hipStream_t s) {
+    hipLaunchKernelGGL(argmax_final_kernel, dim3(rows), dim3(256), 0, s, part, n_wg, rows, tok_out, top2, gen_index,
+                       status);
 }
 
 }  // namespace ocrdec
@@ -541,6 +563,6 @@ extern "C" ocrdec_status ocrdec_lm_argmax(const ocrdec_qmat* W, int32_t rows, co
     p.xs = XDirect{x, W->k, rows};
     p.part = (float*)ws;
     launch_lm_argmax(W->fmt, lp, p, (hipStream_t)stream);
-    launch_argmax_final((float*)ws, lp.grid, rows, tok_out, top2, nullptr, (hipStream_t)stream);
+    launch_argmax_final((float*)ws, lp.grid, rows, tok_out, top2, nullptr, nullptr, (hipStream_t)stream);
     return launch_status("ocrdec_lm_argmax");
 }

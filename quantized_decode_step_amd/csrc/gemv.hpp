@@ -12,17 +12,18 @@ struct GemvParams {
     int n, k;
     int64_t nchunks;
     XDirect xs;
-    void* y;          // output (EPI_RESID: the fp32 residual, updated in place)
+    void* y;          // output (EPI_RESID: the fixed-point residual, updated in place)
     int64_t ldy;
     int half_tiles;   // EPI_GLU: tiles in the gate half (= d_ff / 16)
-    float* part;      // EPI_ARGMAX: [grid][rows][3] (best, index bits, second)
+    float* part;      // EPI_ARGMAX: [grid][rows][4] (best, index bits, second, flag bits)
     int n_groups;
     // LDS-staged kernels: with hn non-NULL the activations are formed in the
-    // staging step, x = fp16(RMSNorm(hn[tok]) * gamma) from the fp32 rows hn
-    // [rows][k] (the previous block's residual), instead of read from xs.
-    const float* hn;
+    // staging step, x = fp16(RMSNorm(hn[tok]) * gamma) from the fixed-point
+    // rows hn [rows][k] (the decode step's residual), instead of read from xs.
+    const fix_t* hn;
     const uint16_t* gamma;
     float eps;
+    uint32_t* status;  // status word (kStat* bits) or NULL
 };
 
 struct GemvPlan {
@@ -43,7 +44,7 @@ struct LmPlan {
 LmPlan plan_lm(int fmt, int n, int k, int rows);
 void launch_lm_argmax(int fmt, const LmPlan& lp, GemvParams p, hipStream_t s);
 void launch_argmax_final(const float* part, int n_wg, int rows, int32_t* tok_out, float* top2, int32_t* gen_index,
-                         hipStream_t s);
+                         uint32_t* status, hipStream_t s);
 
 // Merge of two (best, index, second) argmax states; ties go to the lower index.
 OCR_DEV void argmax_merge(float& b, int& bi, float& s, float ob, int oi, float os) {

@@ -288,17 +288,17 @@ OCR_DEV void stage_x(const XS& xs, int tok0, int ntok, int k, uint16_t* xl, int 
 }
 
 // x = fp16(RMSNorm(h[tok]) * gamma) for tokens tok0 .. tok0+15 of rows into
-// LDS (row stride ldl), one wavefront per token; tokens past the row count
-// are not written (their fragments read as zero).  Rows of up to 1280 values
-// are held in registers (one memory round trip); longer rows take a second
-// pass over the row (from cache), so that the staging adds few registers to
-// the kernel around it.
-OCR_DEV void stage_norm(const float* h, const uint16_t* gamma, float eps, int rows, int tok0, int H, uint16_t* xl,
+// LDS (row stride ldl), one wavefront per token, from the decode step's
+// fixed-point residual; tokens past the row count are not written (their
+// fragments read as zero).  Rows of up to 1280 values are held in registers
+// (one memory round trip); longer rows take a second pass over the row (from
+// cache), so that the staging adds few registers to the kernel around it.
+OCR_DEV void stage_norm(const fix_t* h, const uint16_t* gamma, float eps, int rows, int tok0, int H, uint16_t* xl,
                         int ldl) {
     const int nw = (int)blockDim.x >> 6, wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
     const int nt = min(16, rows - tok0);
     for (int t = wave; t < nt; t += nw) {
-        const float* hr = h + (int64_t)(tok0 + t) * H;
+        const fix_t* hr = h + (int64_t)(tok0 + t) * H;
         if (H <= 1280) {
             wave_rmsnorm_row<5>(hr, gamma, H, eps, nullptr, xl + t * ldl);
             continue;
@@ -306,13 +306,13 @@ OCR_DEV void stage_norm(const float* h, const uint16_t* gamma, float eps, int ro
         const int n4 = H / 4;
         float ss = 0.f;
         for (int c4 = lane; c4 < n4; c4 += 64) {
-            const float4 v = ((const float4*)hr)[c4];
+            const float4 v = ld_resid4(hr, c4);
             ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
         }
         ss = wave_sum(ss);
         const float inv = 1.0f / sqrtf(ss / (float)H + eps);
         for (int c4 = lane; c4 < n4; c4 += 64) {
-            const float4 v = ((const float4*)hr)[c4];
+            const float4 v = ld_resid4(hr, c4);
             const uint2 g = ((const uint2*)gamma)[c4];
             const uint32_t lo = (uint32_t)f2h(v.x * inv * h2f((uint16_t)(g.x & 0xFFFF))) |
                                 ((uint32_t)f2h(v.y * inv * h2f((uint16_t)(g.x >> 16))) << 16);

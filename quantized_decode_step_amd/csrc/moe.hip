@@ -744,7 +744,7 @@ __global__ __launch_bounds__(64 * EG_NW, 2) void expert_gemm_kernel(GroupedParam
 // grouping works in LDS.  Dynamic LDS: rows * (H + 8) halves.
 template <int FMT, int NV, bool BIAS, int XT>
 __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const uint8_t* router, int H,
-                                                            const uint16_t* x, int64_t ldx, const float* h_in,
+                                                            const uint16_t* x, int64_t ldx, const fix_t* h_in,
                                                             const uint16_t* norm_w, float eps, uint16_t* x_out) {
     constexpr int CB = Geom<FMT>::CB;
     extern __shared__ __align__(16) uint16_t xl_dyn[];
@@ -909,6 +909,7 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
             kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
         }
         ksplit_reduce<NT, XT, KS>(acc, red, wave, lane);
+        bool bad = false;
         if (ks == 0 && my_more) {
 #pragma unroll
             for (int xt = 0; xt < XT; ++xt)
@@ -926,30 +927,32 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
                         float* yp = (float*)p.y + slot * p.ldy + row;
                         if constexpr (HADD) {
                             // one pass per entry here (entries of <= 16 tokens)
-                            unsafeAtomicAdd(p.h + (int64_t)hrow[xt][vv] * p.ldh + row, swt[xt][vv] * acc[0][xt][vv]);
+                            fix_atomic_add(p.h + (int64_t)hrow[xt][vv] * p.ldh + row, swt[xt][vv] * acc[0][xt][vv],
+                                           bad);
                         } else {
                             *yp = acc[0][xt][vv];
                         }
                     }
                 }
         }
+        if constexpr (HADD) report_status(p.status, bad, kStatResidual);
         __syncthreads();
     }
 }
 
-// x = fp16(RMSNorm(h) * gamma) of one fp32 residual row per workgroup.
-__global__ __launch_bounds__(256) void moe_norm_kernel(const float* h, const uint16_t* gamma, int H, float eps,
+// x = fp16(RMSNorm(h) * gamma) of one fixed-point residual row per workgroup.
+__global__ __launch_bounds__(256) void moe_norm_kernel(const fix_t* h, const uint16_t* gamma, int H, float eps,
                                                        uint16_t* x, int64_t ldx) {
     __shared__ float red[4];
     const int r = blockIdx.x, tid = threadIdx.x;
-    const float* hr = h + (int64_t)r * H;
+    const fix_t* hr = h + (int64_t)r * H;
     float ss = 0.f;
-    for (int c = tid; c < H; c += blockDim.x) ss = fmaf(hr[c], hr[c], ss);
+    for (int c = tid; c < H; c += blockDim.x) ss = fmaf(fix_to(hr[c]), fix_to(hr[c]), ss);
     ss = wave_sum(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
-    for (int c = tid; c < H; c += blockDim.x) x[(int64_t)r * ldx + c] = f2h(hr[c] * inv * h2f(gamma[c]));
+    for (int c = tid; c < H; c += blockDim.x) x[(int64_t)r * ldx + c] = f2h(fix_to(hr[c]) * inv * h2f(gamma[c]));
 }
 
 // ---------------------------------------------------------------------------
@@ -971,7 +974,9 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineParams p) {
     __syncthreads();
     uint16_t* h16 = (uint16_t*)p.h + (int64_t)r * p.ldh;
     float* h32 = (float*)p.h + (int64_t)r * p.ldh;
+    fix_t* hfx = (fix_t*)p.h + (int64_t)r * p.ldh;
     float ss = 0.f;
+    bool bad = false;
     for (int col = tid; col < H; col += blockDim.x) {
         float ys[8], yr[8];
 #pragma unroll
@@ -984,7 +989,11 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc = fmaf(j < K ? w_s[j] : 0.f, yr[j], acc);
         float hr;
-        if (p.h_f32) {
+        if (p.h_mode == RESID_FIX) {
+            const fix_t hv = (p.add_residual ? hfx[col] : 0) + fix_from(acc, bad);
+            hfx[col] = hv;
+            hr = fix_to(hv);
+        } else if (p.h_mode == RESID_F32) {
             hr = p.add_residual ? h32[col] + acc : acc;
             h32[col] = hr;
         } else {
@@ -994,6 +1003,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineParams p) {
         }
         ss = fmaf(hr, hr, ss);
     }
+    report_status(p.status, bad, kStatResidual);
     if (!p.norm_w) return;
     ss = wave_sum(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
@@ -1003,7 +1013,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(CombineParams p) {
     const float inv = 1.0f / sqrtf(tot / (float)H + p.eps);
     uint16_t* x = p.x_out + (int64_t)r * p.ldx;
     for (int col = tid; col < H; col += blockDim.x) {
-        const float hv = p.h_f32 ? h32[col] : h2f(h16[col]);
+        const float hv = p.h_mode == RESID_FIX ? fix_to(hfx[col]) : p.h_mode == RESID_F32 ? h32[col] : h2f(h16[col]);
         x[col] = f2h(hv * inv * h2f(p.norm_w[col]));
     }
 }
@@ -1185,10 +1195,11 @@ void launch_dense_gemm(int fmt, bool glu, const uint8_t* w, int n, int k, int ro
     launch_expert_gemm(fmt, glu, p, (rows + EG_TM - 1) / EG_TM, s);
 }
 
-void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_f32, int64_t ldh,
+void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_mode, int64_t ldh,
                 int add_residual, const int32_t* forced, const ocrdec_moe_capture* cap, int32_t* cap_idx,
                 float* cap_w, const MoeWs& m, const uint16_t* norm_w, float eps, uint16_t* x_out, int64_t ldxo,
-                hipStream_t s, const float* h_norm, const uint16_t* norm_in, float eps_in, bool fuse_combine) {
+                hipStream_t s, const fix_t* h_norm, const uint16_t* norm_in, float eps_in, bool fuse_combine,
+                uint32_t* status) {
     const int E = w->n_experts, K = w->top_k, S = w->n_shared, F = w->d_ff, H = w->hidden;
     const int NP = rows * K;
     MoeParams p{};
@@ -1219,9 +1230,10 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     // the expert GEMM addresses its activations with 32-bit byte offsets
     const bool gemm = moe_gemm_path(rows, w) && (int64_t)(rows - 1) * ldx + H < (1ll << 30) &&
                       (int64_t)(NP + S * rows) * F < (1ll << 30);
-    // decode-sized batches with an fp32 residual: the down projection adds its
-    // weighted outputs into the residual itself (atomic adds), no combine kernel
-    const bool fused = fuse_combine && small && h_f32 && add_residual;
+    // decode-sized batches with the fixed-point residual: the down projection
+    // adds its weighted outputs into the residual itself (atomic integer adds),
+    // no combine kernel
+    const bool fused = fuse_combine && small && h_mode == RESID_FIX && add_residual;
     // the grouping also lists every slot's combine weight: the down projection
     // adds its outputs into the residual itself
     if (fused) p.sw = m.sw;
@@ -1348,8 +1360,9 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.out_tiles = H / 16;
         if (fused) {
             p.sw = m.sw;
-            p.h = (float*)h;
+            p.h = (fix_t*)h;
             p.ldh = ldh;
+            p.status = status;
         }
         if (gemm) launch_expert_gemm(w->down.fmt, false, p, max_virt, s);
         else launch_grouped(w->down.fmt, false, p, rows, s);
@@ -1357,7 +1370,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     // combine, or (down projection added into the residual) the next norm
     if (fused) {
         if (norm_w)
-            hipLaunchKernelGGL(moe_norm_kernel, dim3(rows), dim3(256), 0, s, (const float*)h, norm_w, H, eps, x_out,
+            hipLaunchKernelGGL(moe_norm_kernel, dim3(rows), dim3(256), 0, s, (const fix_t*)h, norm_w, H, eps, x_out,
                                ldxo);
     } else {
         CombineParams p{};
@@ -1370,7 +1383,8 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.inv = m.inv;
         p.y = m.y;
         p.h = h;
-        p.h_f32 = h_f32;
+        p.h_mode = h_mode;
+        p.status = status;
         p.ldh = ldh;
         p.add_residual = add_residual;
         p.norm_w = norm_w;
@@ -1406,7 +1420,7 @@ extern "C" ocrdec_status ocrdec_moe_layer(const ocrdec_moe_weights* w, int32_t r
         return fail(OCRDEC_ERR_WORKSPACE, "MoE workspace: need " + std::to_string(need) + " bytes, got " +
                                               std::to_string(ws ? ws_bytes : 0));
     MoeWs m = carve_moe(ws, rows, w);
-    launch_moe(w, rows, x, w->hidden, h, 0, w->hidden, add_residual, forced_topk, capture, nullptr, nullptr, m, nullptr,
+    launch_moe(w, rows, x, w->hidden, h, RESID_F16, w->hidden, add_residual, forced_topk, capture, nullptr, nullptr, m, nullptr,
                0.f, nullptr, 0, (hipStream_t)stream, nullptr, nullptr, 0.f);
     return launch_status("ocrdec_moe_layer");
 }

@@ -61,12 +61,14 @@ struct GroupedParams {
     int dense_rows;  // expert GEMM: > 0 means one implicit expert over rows [0, dense_rows) (router)
     int kslices;     // expert GEMM: k range split over this many workgroups (0/1: none), partial
     int64_t ly_slice;  //   products of slice z written ly_slice elements after slice 0's
-    // Grouped down projection adding into the fp32 residual h [rows][ldh]
-    // itself (sw non-NULL): every output of slot s goes to h[vrows[s]] with
-    // weight sw[s] by an atomic add (no expert-output buffer, no combine).
-    float* h;
+    // Grouped down projection adding into the fixed-point residual h
+    // [rows][ldh] itself (sw non-NULL): every output of slot s goes to
+    // h[vrows[s]] with weight sw[s] by an atomic integer add (no expert-output
+    // buffer, no combine; the sum does not depend on the order).
+    fix_t* h;
     int64_t ldh;
     const float* sw;
+    uint32_t* status;
 };
 
 struct CombineParams {
@@ -74,14 +76,15 @@ struct CombineParams {
     const float* w;
     const int32_t* inv;
     const float* y;
-    void* h;          // fp16 (h_f32 == 0) or fp32 residual
-    int h_f32;
+    void* h;          // the residual: fp16, fp32 or fixed point (h_mode)
+    int h_mode;
     int64_t ldh;
     int add_residual;
     const uint16_t* norm_w;  // RMSNorm gain of the next block, or NULL
     float eps;
     uint16_t* x_out;
     int64_t ldx;
+    uint32_t* status;
 };
 
 struct MoeWs {
@@ -113,10 +116,17 @@ void launch_dense_gemm(int fmt, bool glu, const uint8_t* w, int n, int k, int ro
 
 MoeWs carve_moe(void* ws, int rows, const ocrdec_moe_weights* w);
 ocrdec_status check_moe(const ocrdec_moe_weights* w, int rows);
-void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_f32, int64_t ldh,
+// Residual representations of launch_moe's h.
+enum { RESID_F16 = 0, RESID_F32 = 1, RESID_FIX = 2 };
+
+// h: the residual in representation h_mode.  h_norm (fixed point, the decode
+// step's residual) with norm_in: the MoE input x is formed as
+// fp16(RMSNorm(h_norm) * norm_in) first.  fuse_combine (with RESID_FIX and a
+// decode-sized batch): the down projection adds into h itself.
+void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_mode, int64_t ldh,
                 int add_residual, const int32_t* forced, const ocrdec_moe_capture* cap, int32_t* cap_idx,
                 float* cap_w, const MoeWs& m, const uint16_t* norm_w, float eps, uint16_t* x_out, int64_t ldxo,
-                hipStream_t s, const float* h_norm = nullptr, const uint16_t* norm_in = nullptr, float eps_in = 0.f,
-                bool fuse_combine = false);
+                hipStream_t s, const fix_t* h_norm = nullptr, const uint16_t* norm_in = nullptr, float eps_in = 0.f,
+                bool fuse_combine = false, uint32_t* status = nullptr);
 
 }  // namespace ocrdec

@@ -14,17 +14,39 @@ namespace {
 
 constexpr int kMaxRows = 32;
 
+// The status area of the decode step's workspace: word 0 collects the bits
+// the step's kernels raise with atomic ORs; word 1 + r holds row r's input
+// bits, written by the first kernel, which also clears word 0 and the words
+// of rows past the batch (up to kStatusRows).  Later kernels run after it in
+// stream order, so nothing is lost to the clearing.
+constexpr int kStatusRows = 32;
+OCR_DEV void status_begin(uint32_t* status, int r, int rows, bool tok_bad, bool resid_bad) {
+    if (!status) return;
+    const int lane = threadIdx.x & 63;
+    const bool rb = __ballot(resid_bad) != 0;
+    if (lane == 0) status[1 + r] = (tok_bad ? kStatTokenRange : 0u) | (rb ? kStatResidual : 0u);
+    if (r == 0) {
+        if (lane == 0) status[0] = 0;
+        if (lane >= rows && lane < kStatusRows) status[1 + lane] = 0;
+    }
+}
+
 // h[r] = embed[tok[r]] (fp16 table) or src[r] (fp32); x[r] = norm(h[r]).
-// One wavefront per row.
+// One wavefront per row.  HT: the residual's representation (the decode
+// step's fixed point, or fp32 for the prompt pass).
+template <class HT>
 __global__ __launch_bounds__(64) void embed_norm_kernel(const int32_t* tok, const uint16_t* embed, int vocab,
-                                                        const float* src, float* h, const uint16_t* gamma, int H,
-                                                        float eps, uint16_t* x, const uint16_t* rows16) {
+                                                        const float* src, HT* h, const uint16_t* gamma, int H,
+                                                        float eps, uint16_t* x, const uint16_t* rows16,
+                                                        uint32_t* status, int rows) {
     const int r = blockIdx.x, lane = threadIdx.x;
-    float* hr = h + (int64_t)r * H;
+    HT* hr = h + (int64_t)r * H;
     const int n4 = H / 4;
+    bool tok_bad = false, bad = false;
     if (tok || rows16) {
         // a row of the fp16 table, or row r of fp16 input features
         int t = tok ? tok[r] : 0;
+        tok_bad = t < 0 || t >= vocab;
         t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
         const uint2* from = (const uint2*)(tok ? embed + (int64_t)t * H : rows16 + (int64_t)r * H);
         uint2 e[16];
@@ -37,8 +59,10 @@ __global__ __launch_bounds__(64) void embed_norm_kernel(const int32_t* tok, cons
         for (int i = 0; i < 16; ++i) {
             const int c4 = lane + 64 * i;
             if (c4 < n4)
-                ((float4*)hr)[c4] = make_float4(h2f((uint16_t)(e[i].x & 0xFFFF)), h2f((uint16_t)(e[i].x >> 16)),
-                                                h2f((uint16_t)(e[i].y & 0xFFFF)), h2f((uint16_t)(e[i].y >> 16)));
+                st_resid4(hr, c4,
+                          make_float4(h2f((uint16_t)(e[i].x & 0xFFFF)), h2f((uint16_t)(e[i].x >> 16)),
+                                      h2f((uint16_t)(e[i].y & 0xFFFF)), h2f((uint16_t)(e[i].y >> 16))),
+                          bad);
         }
     } else {
         const float4* from = (const float4*)(src + (int64_t)r * H);
@@ -51,9 +75,10 @@ __global__ __launch_bounds__(64) void embed_norm_kernel(const int32_t* tok, cons
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int c4 = lane + 64 * i;
-            if (c4 < n4) ((float4*)hr)[c4] = v[i];
+            if (c4 < n4) st_resid4(hr, c4, v[i], bad);
         }
     }
+    status_begin(status, r, rows, tok_bad, bad);
     __threadfence_block();
     wave_rmsnorm_row(hr, gamma, H, eps, x + (int64_t)r * H);
 }
@@ -65,14 +90,16 @@ __global__ __launch_bounds__(64) void embed_norm_kernel(const int32_t* tok, cons
 // i < 8) and the row's block scales.  Lane l of the wavefront takes the
 // (chunk, group) pairs p = l, l+64, ...; each product d*q is exact in fp32
 // (q and (q-8) are integers of at most 8 bits, d has 11).
-template <int FMT>
+template <int FMT, class HT>
 __global__ __launch_bounds__(64) void embed_q_norm_kernel(const int32_t* tok, const uint8_t* table, int vocab,
-                                                          int64_t nchunks, float* h, const uint16_t* gamma, int H,
-                                                          float eps, uint16_t* x) {
+                                                          int64_t nchunks, HT* h, const uint16_t* gamma, int H,
+                                                          float eps, uint16_t* x, uint32_t* status, int rows) {
     constexpr int SB = Geom<FMT>::SB, CB = Geom<FMT>::CB, KC = 32 * SB;
     const int r = blockIdx.x, lane = threadIdx.x;
-    float* hr = h + (int64_t)r * H;
+    HT* hr = h + (int64_t)r * H;
     int t = tok[r];
+    const bool tok_bad = t < 0 || t >= vocab;
+    bool bad = false;
     t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
     const uint8_t* tile = table + (int64_t)(t >> 4) * nchunks * CB;
     const int np = (int)nchunks * 4;
@@ -93,11 +120,12 @@ __global__ __launch_bounds__(64) void embed_q_norm_kernel(const int32_t* tok, co
             }
             const int k0 = c * KC + 32 * j + 8 * g;
             if (k0 < H) {
-                ((float4*)(hr + k0))[0] = make_float4(v[0], v[1], v[2], v[3]);
-                ((float4*)(hr + k0))[1] = make_float4(v[4], v[5], v[6], v[7]);
+                st_resid4(hr, k0 / 4, make_float4(v[0], v[1], v[2], v[3]), bad);
+                st_resid4(hr, k0 / 4 + 1, make_float4(v[4], v[5], v[6], v[7]), bad);
             }
         }
     }
+    status_begin(status, r, rows, tok_bad, bad);
     __threadfence_block();
     wave_rmsnorm_row(hr, gamma, H, eps, x + (int64_t)r * H);
 }
@@ -135,8 +163,9 @@ __global__ __launch_bounds__(64) void gather_rows_kernel(const uint16_t* src, ui
     for (int c = threadIdx.x; c < H / 8; c += blockDim.x) d[c] = s[c];
 }
 
-// x[r] = fp16(RMSNorm(h[r]) * gamma): one wavefront per row.
-__global__ __launch_bounds__(64) void norm_kernel(const float* h, const uint16_t* gamma, int H, float eps,
+// x[r] = fp16(RMSNorm(h[r]) * gamma) of the fixed-point residual: one
+// wavefront per row.
+__global__ __launch_bounds__(64) void norm_kernel(const fix_t* h, const uint16_t* gamma, int H, float eps,
                                                   uint16_t* x) {
     const int r = blockIdx.x;
     wave_rmsnorm_row(h + (int64_t)r * H, gamma, H, eps, x + (int64_t)r * H);
@@ -147,13 +176,20 @@ __global__ void copy_rows_kernel(const float* src, float* dst, int64_t n) {
         dst[i] = src[i];
 }
 
+// The fixed-point residual as fp32.
+__global__ void fix_rows_kernel(const fix_t* src, float* dst, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = fix_to(src[i]);
+}
+
 __global__ void bump_kernel(int32_t* gen_index, int rows) {
     const int r = blockIdx.x * blockDim.x + threadIdx.x;
     if (r < rows) gen_index[r] += 1;
 }
 
 struct StepWs {
-    float* h;
+    uint32_t* status;  // [1 + kStatusRows] (first in the workspace)
+    fix_t* h;
     uint16_t* x;
     float* qkv;
     float* attn_part;
@@ -179,7 +215,8 @@ StepWs carve_step(void* ws, const ocrdec_model* m, int rows, int cache_cap) {
         if (m->layers[l].is_moe) moe = &m->layers[l].moe;
         else dense_ff = std::max(dense_ff, m->layers[l].dense_ff);
     }
-    w.h = cv.take<float>((size_t)rows * H);
+    w.status = cv.take<uint32_t>(1 + kStatusRows);
+    w.h = cv.take<fix_t>((size_t)rows * H);
     w.x = cv.take<uint16_t>((size_t)rows * H);
     w.qkv = cv.take<float>((size_t)rows * 3 * HD);
     w.attn_part = cv.take<float>(attn_ws_bytes(rows, m->n_heads, m->head_dim, cache_cap) / sizeof(float));
@@ -340,6 +377,21 @@ extern "C" ocrdec_status ocrdec_step_workspace_bytes(const ocrdec_model* m, cons
     return OCRDEC_OK;
 }
 
+extern "C" ocrdec_status ocrdec_device_status(const void* ws, size_t ws_bytes, void* stream, uint32_t* flags) {
+    OCR_CHECK_ARG(ws && flags, "ws and flags must be non-NULL");
+    const size_t need = sizeof(uint32_t) * (1 + kStatusRows);
+    if (ws_bytes < need)
+        return fail(OCRDEC_ERR_WORKSPACE, "status: a step workspace holds at least " + std::to_string(need) +
+                                              " bytes, got " + std::to_string(ws_bytes));
+    OCR_HIP(hipStreamSynchronize((hipStream_t)stream));
+    uint32_t words[1 + kStatusRows];
+    OCR_HIP(hipMemcpy(words, ws, sizeof(words), hipMemcpyDeviceToHost));
+    uint32_t f = 0;
+    for (uint32_t w : words) f |= w;
+    *flags = f & (OCRDEC_DEV_TOKEN_RANGE | OCRDEC_DEV_RESIDUAL | OCRDEC_DEV_LOGIT | OCRDEC_DEV_NO_TOKEN);
+    return OCRDEC_OK;
+}
+
 extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_state* st, const int32_t* tok_in,
                                             float* hidden, int32_t* tok_out, const int32_t* forced_topk,
                                             const ocrdec_step_capture* cap, void* ws, size_t ws_bytes, void* stream) {
@@ -362,8 +414,8 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
         const int64_t nch = n_chunks(m->embed_q.fmt, H);
 #define OCR_EQ(F_)                                                                                                 \
     case F_:                                                                                                       \
-        hipLaunchKernelGGL(embed_q_norm_kernel<F_>, dim3(R), dim3(64), 0, s, tok_in, tq, m->vocab, nch, w.h,      \
-                           m->layers[0].attn_norm, H, m->norm_eps, w.x);                                           \
+        hipLaunchKernelGGL((embed_q_norm_kernel<F_, fix_t>), dim3(R), dim3(64), 0, s, tok_in, tq, m->vocab, nch,   \
+                           w.h, m->layers[0].attn_norm, H, m->norm_eps, w.x, w.status, R);                         \
         break;
         switch (m->embed_q.fmt) {
             OCR_EQ(OCRDEC_F16)
@@ -373,8 +425,8 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
         }
 #undef OCR_EQ
     } else {
-        hipLaunchKernelGGL(embed_norm_kernel, dim3(R), dim3(64), 0, s, tok_in, m->embed, m->vocab, hidden, w.h,
-                           m->layers[0].attn_norm, H, m->norm_eps, w.x, (const uint16_t*)nullptr);
+        hipLaunchKernelGGL(embed_norm_kernel<fix_t>, dim3(R), dim3(64), 0, s, tok_in, m->embed, m->vocab, hidden,
+                           w.h, m->layers[0].attn_norm, H, m->norm_eps, w.x, (const uint16_t*)nullptr, w.status, R);
     }
     // attention arguments shared by every layer (RoPE frequencies once per call)
     AttnParams ap0{};
@@ -432,7 +484,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
         ap.k_scale = L.k_scale;
         ap.v_scale = L.v_scale;
         if (attn_merge_o_ok(ap, L.wo.fmt, H)) {
-            launch_attn_merge_o(ap, L.wo.fmt, (const uint8_t*)L.wo.data, H, w.h, H, s);
+            launch_attn_merge_o(ap, L.wo.fmt, (const uint8_t*)L.wo.data, H, w.h, H, w.status, s);
         } else {
             launch_attn(ap, s);
             GemvPlan pl = plan_gemv(L.wo.fmt, H, HD, R, EPI_RESID);
@@ -444,6 +496,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             gp.xs = XDirect{w.o, HD, R};
             gp.y = w.h;
             gp.ldy = H;
+            gp.status = w.status;
             launch_gemv(L.wo.fmt, EPI_RESID, pl, gp, s);
         }
         if (L.is_moe) {
@@ -452,8 +505,9 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             float* cw = cap && cap->topk_w ? cap->topk_w + (int64_t)moe_l * R * K : nullptr;
             const int32_t* fo = forced_topk ? forced_topk + (int64_t)moe_l * R * K : nullptr;
             // the routing kernel forms x = RMSNorm(h) itself
-            launch_moe(&L.moe, R, w.x, H, w.h, 1, H, 1, fo, nullptr, ci, cw, w.moe, prolog ? nullptr : next_norm,
-                       m->norm_eps, w.x, H, s, w.h, L.ffn_norm, m->norm_eps, true);
+            launch_moe(&L.moe, R, w.x, H, w.h, RESID_FIX, H, 1, fo, nullptr, ci, cw, w.moe,
+                       prolog ? nullptr : next_norm, m->norm_eps, w.x, H, s, w.h, L.ffn_norm, m->norm_eps, true,
+                       w.status);
             ++moe_l;
         } else {
             if (!prolog) hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(64), 0, s, w.h, L.ffn_norm, H, m->norm_eps, w.x);
@@ -486,6 +540,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                 gp.xs = XDirect{w.a, F, R};
                 gp.y = w.h;
                 gp.ldy = H;
+                gp.status = w.status;
                 launch_gemv(L.dense_down.fmt, EPI_RESID, pl, gp, s);
             }
             if (next_norm && !prolog)
@@ -494,7 +549,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     }
     if (hidden) {
         const int64_t n = (int64_t)R * H;
-        hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 1024)), dim3(256), 0, s,
+        hipLaunchKernelGGL(fix_rows_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 1024)), dim3(256), 0, s,
                            w.h, hidden, n);
     }
     if (m->lm_head.data && tok_out) {
@@ -512,7 +567,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             gp.eps = m->norm_eps;
         }
         launch_lm_argmax(m->lm_head.fmt, lp, gp, s);
-        launch_argmax_final(w.lm_part, lp.grid, R, tok_out, cap ? cap->lm_top2 : nullptr, st->gen_index, s);
+        launch_argmax_final(w.lm_part, lp.grid, R, tok_out, cap ? cap->lm_top2 : nullptr, st->gen_index, w.status, s);
     } else {
         hipLaunchKernelGGL(bump_kernel, dim3(1), dim3(64), 0, s, st->gen_index, R);
     }
@@ -583,8 +638,8 @@ extern "C" ocrdec_status ocrdec_prefill_batch(const ocrdec_model* m, const ocrde
         const int64_t nch = n_chunks(m->embed_q.fmt, H);
 #define OCR_EQ(F_)                                                                                                 \
     case F_:                                                                                                       \
-        hipLaunchKernelGGL(embed_q_norm_kernel<F_>, dim3(T), dim3(64), 0, s, tok, tq, m->vocab, nch, w.h,          \
-                           m->layers[0].attn_norm, H, m->norm_eps, w.x);                                           \
+        hipLaunchKernelGGL((embed_q_norm_kernel<F_, float>), dim3(T), dim3(64), 0, s, tok, tq, m->vocab, nch, w.h, \
+                           m->layers[0].attn_norm, H, m->norm_eps, w.x, (uint32_t*)nullptr, T);                    \
         break;
         switch (m->embed_q.fmt) {
             OCR_EQ(OCRDEC_F16)
@@ -594,8 +649,9 @@ extern "C" ocrdec_status ocrdec_prefill_batch(const ocrdec_model* m, const ocrde
         }
 #undef OCR_EQ
     } else {
-        hipLaunchKernelGGL(embed_norm_kernel, dim3(T), dim3(64), 0, s, tok, m->embed, m->vocab, nullptr, w.h,
-                           m->layers[0].attn_norm, H, m->norm_eps, w.x, tok ? (const uint16_t*)nullptr : emb);
+        hipLaunchKernelGGL(embed_norm_kernel<float>, dim3(T), dim3(64), 0, s, tok, m->embed, m->vocab, nullptr, w.h,
+                           m->layers[0].attn_norm, H, m->norm_eps, w.x, tok ? (const uint16_t*)nullptr : emb,
+                           (uint32_t*)nullptr, T);
     }
     PrefillAttnParams ap{};
     ap.P = T;
@@ -637,7 +693,8 @@ extern "C" ocrdec_status ocrdec_prefill_batch(const ocrdec_model* m, const ocrde
             float* cw = cap && cap->topk_w ? cap->topk_w + (int64_t)moe_l * T * K : nullptr;
             const int32_t* fo = forced_topk ? forced_topk + (int64_t)moe_l * T * K : nullptr;
             // the combine adds into h and forms the next block's normalised input
-            launch_moe(&L.moe, T, w.x, H, w.h, 1, H, 1, fo, nullptr, ci, cw, w.moe, next_norm, m->norm_eps, w.x, H, s);
+            launch_moe(&L.moe, T, w.x, H, w.h, RESID_F32, H, 1, fo, nullptr, ci, cw, w.moe, next_norm, m->norm_eps, w.x, H,
+                       s);
             ++moe_l;
         } else {
             const int F = L.dense_ff;
@@ -663,7 +720,7 @@ extern "C" ocrdec_status ocrdec_prefill_batch(const ocrdec_model* m, const ocrde
         gp.xs = XDirect{w.x_last, H, n};
         gp.part = w.lm_part;
         launch_lm_argmax(m->lm_head.fmt, lp, gp, s);
-        launch_argmax_final(w.lm_part, lp.grid, n, tok_out, cap ? cap->lm_top2 : nullptr, nullptr, s);
+        launch_argmax_final(w.lm_part, lp.grid, n, tok_out, cap ? cap->lm_top2 : nullptr, nullptr, nullptr, s);
     }
     return launch_status("ocrdec_prefill_batch");
 }

@@ -1,5 +1,5 @@
-"""Writes the oracle fixtures of the full 12-layer decoder at 24 rows (prefix
-1100) for sampled rows, from the oracle and the input generator alone:
+"""Writes the oracle fixtures of the full 12-layer decoder (prefix 1100) for
+sampled rows, from the oracle and the input generator alone:
 
 * decode_full_r24.npz: an 8-step trajectory of rows 0, 11 and 23 from
   generation index 124 (the ring wraps after four steps), teacher-forced on
@@ -9,9 +9,17 @@
   124 and 128 (just wrapped), with the residual entering every layer and the
   final LM-head input, so each layer can be checked from the oracle's own
   inputs.
+* decode_layers_r1_6_12.npz: the same at 1, 6 and 12 rows (sampled rows: the
+  first and the last), the batch sizes of the decode rows sweep.
+* decode_r1_64.npz: 64 consecutive steps of one row from generation index 100
+  (the ring wraps at step 28), teacher-forced on the oracle's own tokens: per
+  step the tokens, routing and final hidden state, and the last layer's new
+  keys at steps 0, 27, 28 and 63.
 
 Run from the repo root:  python tests/golden/make_decode_fixture.py
-(about five minutes on 8 cores; --layers-only / --trajectory-only write one).
+(about five minutes on 8 cores for the 24-row files and as long again for the
+64-step trajectory; --layers-only / --trajectory-only / --small-rows /
+--r1-64 write one of them).
 """
 import os
 import sys
@@ -59,12 +67,13 @@ def trajectory(d, model):
                         t0=T0, steps=STEPS, n_moe=n_moe, **{k: np.array(v) for k, v in out.items()})
 
 
-def per_layer(d, model):
+def per_layer(d, model, rows=ROWS, sampled=SAMPLED, prefix=""):
     out = {}
     for case, t in (("a", 124), ("b", 128)):
-        st = synth.make_state(d, SEED, [d.prefix_cap] * ROWS, [t] * ROWS)
-        tok = synth.first_tokens(d, SEED + t, ROWS)
-        res = O.decode_step(model, st, tok_in=tok, rows=SAMPLED)
+        st = synth.make_state(d, SEED, [d.prefix_cap] * rows, [t] * rows)
+        tok = synth.first_tokens(d, SEED + t, rows)
+        res = O.decode_step(model, st, tok_in=tok, rows=sampled)
+        case = prefix + case
         out[case + "_t"] = t
         out[case + "_tok_in"] = tok
         out[case + "_layer_in"] = np.array(res.layer_in, np.float32)       # [L][2][H]
@@ -78,17 +87,57 @@ def per_layer(d, model):
         out[case + "_new_k"] = np.array(res.new_k, np.float32)             # [L][2][NH][D]
         out[case + "_new_v"] = np.array(res.new_v, np.float32)
         print("case", case, "t", t, "tokens", res.tok.tolist(), flush=True)
-    np.savez_compressed(os.path.join(HERE, "decode_layers_r24.npz"), seed=SEED, rows=ROWS,
-                        sampled=np.array(SAMPLED), **out)
+    return out
+
+
+SMALL_ROWS = {1: [0], 6: [0, 5], 12: [0, 11]}
+R1_T0, R1_STEPS = 100, 64
+R1_KEY_STEPS = [0, 27, 28, 63]
+
+
+def trajectory_r1(d, model):
+    """64 steps of one row across the ring wrap (t = 100 .. 163)."""
+    st = synth.make_state(d, SEED, [d.prefix_cap], [R1_T0])
+    tok = synth.first_tokens(d, SEED, 1)
+    out = {k: [] for k in ("tok_in", "tok", "lm_top2", "hidden", "topk_idx", "topk_w", "router_gap")}
+    new_k_last = []
+    for step in range(R1_STEPS):
+        res = O.decode_step(model, st, tok_in=tok, rows=[0])
+        out["tok_in"].append(tok.copy())
+        out["tok"].append(res.tok)
+        out["lm_top2"].append(res.lm_top2)
+        out["hidden"].append(res.hidden.astype(np.float32))
+        out["topk_idx"].append(np.array(res.topk_idx, np.int32))
+        out["topk_w"].append(np.array(res.topk_w, np.float64))
+        out["router_gap"].append(np.array(res.router_gap, np.float64))
+        if step in R1_KEY_STEPS:
+            new_k_last.append(res.new_k[-1].astype(np.float32))
+        tok = np.array(res.tok, np.int32)
+        print("r1 step", step, "token", int(res.tok[0]), flush=True)
+    np.savez_compressed(os.path.join(HERE, "decode_r1_64.npz"), seed=SEED, t0=R1_T0, steps=R1_STEPS,
+                        key_steps=np.array(R1_KEY_STEPS), new_k_last=np.array(new_k_last),
+                        **{k: np.array(v) for k, v in out.items()})
 
 
 def main():
     d = synth.dims_full()
     model = synth.make_model(d, SEED)
-    if "--trajectory-only" not in sys.argv:
-        per_layer(d, model)
-    if "--layers-only" not in sys.argv:
+    only = [a for a in sys.argv[1:] if a.startswith("--")]
+    if not only or "--layers-only" in only:
+        out = per_layer(d, model)
+        np.savez_compressed(os.path.join(HERE, "decode_layers_r24.npz"), seed=SEED, rows=ROWS,
+                            sampled=np.array(SAMPLED), **out)
+    if not only or "--trajectory-only" in only:
         trajectory(d, model)
+    if not only or "--small-rows" in only:
+        out = {}
+        for R, smp in SMALL_ROWS.items():
+            out.update(per_layer(d, model, R, smp, "r%d_" % R))
+            out["r%d_sampled" % R] = np.array(smp)
+        np.savez_compressed(os.path.join(HERE, "decode_layers_r1_6_12.npz"), seed=SEED,
+                            rows=np.array(sorted(SMALL_ROWS)), **out)
+    if not only or "--r1-64" in only:
+        trajectory_r1(d, model)
     print("done")
 
 

@@ -11,6 +11,9 @@ Comparison rule for floating point (derived in the design doc):
     alone cannot hold for a tensor stored in fp16.  Such flips must stay rare:
     at most 1% of the elements may exceed 2e-3 * rms.
 """
+import json
+import os
+
 import numpy as np
 
 REL_TOL = 2e-3
@@ -69,3 +72,19 @@ def f16_tensor(a, device="cuda"):
 
 def from_f16_tensor(t) -> np.ndarray:
     return t.cpu().numpy().view(np.float16).astype(np.float64)
+
+
+def log_near_tie(kind: str, what: str, gap: float):
+    """Records an accepted near-tie (a routing or argmax decision that differs
+    from the oracle's where the oracle's own gap is below the threshold) in
+    the JSONL log named by OCRDEC_NEAR_TIE_LOG (default
+    gpurun_out/near_ties.jsonl) and on stdout."""
+    rec = {"kind": kind, "case": what, "oracle_gap": float(gap)}
+    print("[near-tie]", json.dumps(rec), flush=True)
+    path = os.environ.get("OCRDEC_NEAR_TIE_LOG", os.path.join("gpurun_out", "near_ties.jsonl"))
+    try:
+        os.makedirs(os.path.dirname(path) or ".", exist_ok=True)
+        with open(path, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+    except OSError:
+        pass

@@ -136,6 +136,13 @@ def test_validation_errors_without_a_device(q):
     assert _err(q, q.ocrdec_moe_workspace_bytes, w, 1) == q.OCRDEC_ERR_INVALID_ARG
 
 
+def test_device_status_validation_without_a_device(q):
+    """The status query checks its arguments before touching the device."""
+    assert _err(q, q.ocrdec_device_status, None, 4096, 0) == q.OCRDEC_ERR_INVALID_ARG
+    assert _err(q, q.ocrdec_device_status, 1 << 20, 16, 0) == q.OCRDEC_ERR_WORKSPACE
+    assert "status" in q.ocrdec_last_error()
+
+
 def test_prefill_and_round_validation_without_a_device(q):
     """Prompt lengths, rows and requests are checked on the host before any
     device work."""

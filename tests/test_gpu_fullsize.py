@@ -1,10 +1,15 @@
 """Parity at full size, in the launch configurations the benchmark times.
 
-* The 12-layer decoder at 24 rows (prefix 1100), layer by layer: each layer
-  run alone from the oracle's own input to that layer, for two sampled rows,
-  at generation index 124 and 128 (ring just wrapped), against
-  tests/golden/decode_layers_r24.npz (written by make_decode_fixture.py from
-  the oracle alone).  Each layer's residual must be within 2e-3 * rms.
+* The 12-layer decoder at 1, 6, 12 and 24 rows (prefix 1100), layer by
+  layer: each layer run alone from the oracle's own input to that layer, for
+  the sampled rows, at generation index 124 and 128 (ring just wrapped),
+  against tests/golden/decode_layers_r24.npz and decode_layers_r1_6_12.npz
+  (written by make_decode_fixture.py from the oracle alone).  Each layer's
+  residual must be within 2e-3 * rms.  The row counts cover every launch
+  path of the step (one row, norms staged in the consumers and the merge in
+  the O projection up to 16 rows, the separate kernels above).
+* One row over 64 consecutive steps from generation index 100 (the ring wraps
+  at step 28), teacher-forced, against decode_r1_64.npz.
 * The same decoder composed over 8 steps (the ring wraps after four), rows
   0, 11 and 23 against tests/golden/decode_full_r24.npz, with tokens and the
   sampled rows' routing forced to the oracle's: the GPU's own routing and
@@ -22,7 +27,7 @@ import pytest
 
 import oracle as O
 import synth
-from tests.gpu_util import NEAR_TIE, assert_close, assert_close_f16, f16_tensor, from_f16_tensor
+from tests.gpu_util import NEAR_TIE, assert_close, assert_close_f16, f16_tensor, from_f16_tensor, log_near_tie
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -58,15 +63,33 @@ def full_model(q):
     return d, model, q.DeviceModel(model)
 
 
+class _Prefixed:
+    """Keys of one row count in a fixture file that holds several."""
+
+    def __init__(self, fx, prefix):
+        self.fx, self.prefix = fx, prefix
+
+    def __getitem__(self, k):
+        return self.fx[self.prefix + k] if k not in ("seed",) else self.fx[k]
+
+
+def _layer_fixture(R):
+    if R == 24:
+        fx = np.load(os.path.join(GOLDEN, "decode_layers_r24.npz"))
+        return fx, [int(r) for r in fx["sampled"]], int(fx["seed"])
+    fx = np.load(os.path.join(GOLDEN, "decode_layers_r1_6_12.npz"))
+    pf = _Prefixed(fx, "r%d_" % R)
+    return pf, [int(r) for r in pf["sampled"]], int(fx["seed"])
+
+
+@pytest.mark.parametrize("R", [1, 6, 12, 24])
 @pytest.mark.parametrize("case", ["a", "b"])
-def test_decode_full_each_layer_24_rows(q, full_model, case):
-    """Every layer of the full decoder, run alone (rows 24, launch as in the
-    benchmark) from the oracle's residual entering it; the last one also runs
-    the final norm, the LM head and the argmax."""
+def test_decode_full_each_layer(q, full_model, R, case):
+    """Every layer of the full decoder, run alone (launch as in the benchmark
+    at that row count) from the oracle's residual entering it; the last one
+    also runs the final norm, the LM head and the argmax."""
     import torch
-    fx = np.load(os.path.join(GOLDEN, "decode_layers_r24.npz"))
-    seed, R = int(fx["seed"]), int(fx["rows"])
-    sampled = [int(r) for r in fx["sampled"]]
+    fx, sampled, seed = _layer_fixture(R)
     t = int(fx[case + "_t"])
     d, model, dm = full_model
     print("[case] full decoder per layer R=%d t=%d sampled=%s seed=%d" % (R, t, sampled, seed), flush=True)
@@ -116,7 +139,7 @@ def test_decode_full_each_layer_24_rows(q, full_model, case):
                 if not np.array_equal(g_idx, fx[case + "_topk_idx"][moe_l][i]):
                     gap = fx[case + "_router_gap"][moe_l][i]
                     assert gap < NEAR_TIE, "%s: routing differs (gap %.3g)" % (what, gap)
-                    print("[near-tie] routing", what, "gap", gap)
+                    log_near_tie("routing", what, gap)
                     continue
                 assert_close(cap_w[0, r].cpu().numpy(), fx[case + "_topk_w"][moe_l][i], what + " routing weights")
             worst = max(worst, assert_close(g_hid[r], ref_out[i], what + " residual"))
@@ -125,10 +148,10 @@ def test_decode_full_each_layer_24_rows(q, full_model, case):
                 if g_tok != fx[case + "_tok"][i]:
                     gap = fx[case + "_lm_top2"][i][0] - fx[case + "_lm_top2"][i][1]
                     assert gap < NEAR_TIE, "%s: token %d vs %d (gap %.3g)" % (what, g_tok, fx[case + "_tok"][i], gap)
-                    print("[near-tie] token", what, "gap", gap)
+                    log_near_tie("token", what, gap)
         if model.layers[l].is_moe:
             moe_l += 1
-    print("[result] worst per-layer residual error %.3g rms" % worst)
+    print("[result] R=%d case %s: worst per-layer residual error %.3g rms" % (R, case, worst))
 
 
 def test_decode_full_12_layers_24_rows(q, full_model):
@@ -178,7 +201,7 @@ def test_decode_full_12_layers_24_rows(q, full_model):
                     gap = fx["router_gap"][step][ml][i]
                     assert gap < TRAJ_NEAR_TIE, "step %d layer %d row %d: routing differs (gap %.3g)" % (
                         step, ml, r, gap)
-                    print("[near-tie] routing step", step, "layer", ml, "row", r, "gap", gap)
+                    log_near_tie("routing", "R=24 trajectory step %d layer %d row %d" % (step, ml, r), gap)
                     ties += 1
             assert_close(g_w[:, r], fx["topk_w"][step][:, i], "step %d row %d routing weights" % (step, r),
                          tol=TRAJ_TOL)
@@ -189,7 +212,7 @@ def test_decode_full_12_layers_24_rows(q, full_model):
                 gap = fx["lm_top2"][step][i][0] - fx["lm_top2"][step][i][1]
                 assert gap < TRAJ_NEAR_TIE, "step %d row %d: token %d vs %d (gap %.3g)" % (
                     step, r, g_tok[r], fx["tok"][step][i], gap)
-                print("[near-tie] token step", step, "row", r, "gap", gap)
+                log_near_tie("token", "R=24 trajectory step %d row %d" % (step, r), gap)
             if kc is not None:
                 slot = d.prefix_cap + (t0 + step) % d.ring_cap
                 assert_close_f16(kc[0, r, :, slot].astype(np.float64), fx["new_k_first"][step][i], "layer 0 new k")
@@ -199,6 +222,67 @@ def test_decode_full_12_layers_24_rows(q, full_model):
     decisions = steps * n_moe * len(sampled)
     assert ties <= 0.05 * decisions, "%d routing near-ties among %d decisions" % (ties, decisions)
     assert np.all(ds.gen_index.cpu().numpy() == t0 + steps)
+
+
+def test_decode_full_one_row_64_steps(q, full_model):
+    """One row, 64 consecutive steps from generation index 100: the ring wraps
+    at step 28 and the window then slides over the ring.  Tokens are
+    teacher-forced and routing forced to the oracle's (so a near-tie cannot
+    part the two runs); the GPU's own routing and tokens must equal the
+    oracle's except at near-ties; the hidden state and routing weights are
+    held to the composed-decoder bounds above."""
+    import torch
+    fx = np.load(os.path.join(GOLDEN, "decode_r1_64.npz"))
+    seed, t0, steps = int(fx["seed"]), int(fx["t0"]), int(fx["steps"])
+    key_steps = [int(s) for s in fx["key_steps"]]
+    print("[case] full decoder R=1 t0=%d steps=%d seed=%d" % (t0, steps, seed), flush=True)
+    d, _, dm = full_model
+    st = synth.make_state(d, seed, [d.prefix_cap], [t0])
+    ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+    del st
+    dm.bind_caches(ds.k_cache, ds.v_cache)
+    wsb = q.ocrdec_step_workspace_bytes(dm.desc, ds.desc)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    n_moe, K = d.n_layers - d.n_dense, d.top_k
+    cap_idx = torch.zeros((n_moe, 1, K), dtype=torch.int32, device="cuda")
+    cap_w = torch.zeros((n_moe, 1, K), dtype=torch.float32, device="cuda")
+    top2 = torch.zeros((1, 2), dtype=torch.float32, device="cuda")
+    cap = q.StepCapture(cap_idx.data_ptr(), cap_w.data_ptr(), top2.data_ptr())
+    hidden = torch.zeros((1, d.hidden), dtype=torch.float32, device="cuda")
+    tok_out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ties, worst, medians = 0, 0.0, []
+    for step in range(steps):
+        forced = torch.from_numpy(fx["topk_idx"][step].reshape(n_moe, 1, K).astype(np.int32)).cuda()
+        q.ocrdec_decode_step(dm.desc, ds.desc, torch.from_numpy(fx["tok_in"][step].astype(np.int32)).cuda(), hidden,
+                             tok_out, forced, cap, ws, wsb)
+        torch.cuda.synchronize()
+        g_idx, g_w = cap_idx.cpu().numpy()[:, 0], cap_w.cpu().numpy()[:, 0]
+        for ml in range(n_moe):
+            if not np.array_equal(g_idx[ml], fx["topk_idx"][step][ml][0]):
+                gap = fx["router_gap"][step][ml][0]
+                assert gap < TRAJ_NEAR_TIE, "step %d layer %d: routing differs (gap %.3g)" % (step, ml, gap)
+                log_near_tie("routing", "R=1 64-step run step %d layer %d" % (step, ml), gap)
+                ties += 1
+        assert_close(g_w, fx["topk_w"][step][:, 0], "step %d routing weights" % step, tol=TRAJ_TOL)
+        g_hid = hidden.cpu().numpy()[0].astype(np.float64)
+        ref = fx["hidden"][step][0]
+        worst = max(worst, assert_close(g_hid, ref, "step %d hidden" % step, tol=TRAJ_TOL))
+        medians.append(np.median(np.abs(g_hid - ref)) / np.sqrt(np.mean(ref ** 2.0)))
+        assert medians[-1] <= TRAJ_MEDIAN_TOL, "step %d hidden: median %.3g" % (step, medians[-1])
+        g_tok = int(tok_out.item())
+        if g_tok != fx["tok"][step][0]:
+            gap = fx["lm_top2"][step][0][0] - fx["lm_top2"][step][0][1]
+            assert gap < TRAJ_NEAR_TIE, "step %d: token %d vs %d (gap %.3g)" % (step, g_tok, fx["tok"][step][0], gap)
+            log_near_tie("token", "R=1 64-step run step %d" % step, gap)
+        if step in key_steps:
+            slot = d.prefix_cap + (t0 + step) % d.ring_cap
+            kc = ds.k_cache[-1, 0, :, slot].cpu().numpy().view(np.float16).astype(np.float64)
+            assert_close_f16(kc, fx["new_k_last"][key_steps.index(step)][0], "step %d last layer new k" % step,
+                             tol=TRAJ_TOL)
+    assert int(ds.gen_index.item()) == t0 + steps
+    assert ties <= 0.05 * steps * n_moe
+    print("[result] R=1 64 steps: worst hidden %.3g rms, worst median %.3g, routing near-ties %d" % (
+        worst, max(medians), ties))
 
 
 class _Lay:
@@ -232,9 +316,8 @@ def test_moe_prefill_2048_tokens(q):
     for t in ties:
         gap = O.topk_gap(logits[t], d.top_k, lay.router_bias)
         assert gap < NEAR_TIE, "token %d routing differs with gap %.3g" % (t, gap)
-    if ties:
-        print("[near-tie] tokens", ties)
-    else:
+        log_near_tie("routing", "prefill-shaped MoE token %d" % t, gap)
+    if not ties:
         c, o, p, _ = O.group(idx, d.n_experts)
         assert np.array_equal(counts.cpu().numpy(), c)
         assert np.array_equal(offsets.cpu().numpy(), o)

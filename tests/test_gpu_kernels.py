@@ -7,7 +7,7 @@ import pytest
 
 import oracle as O
 import synth
-from tests.gpu_util import NEAR_TIE, assert_close, assert_close_f16, f16_tensor, from_f16_tensor
+from tests.gpu_util import NEAR_TIE, assert_close, assert_close_f16, f16_tensor, from_f16_tensor, log_near_tie
 
 pytestmark = pytest.mark.gpu
 
@@ -319,10 +319,9 @@ def _moe_case(q, rows, seed, H=1280, E=64, K=6, S=2, F=896, fmt=synth.Q8_0, bias
         if not np.array_equal(g_idx[r], idx[r]):
             gap = O.topk_gap(logits[r], K, lay.router_bias)
             assert gap < NEAR_TIE, "row %d routing differs with oracle gap %.3g" % (r, gap)
+            log_near_tie("routing", "MoE layer rows=%d row %d" % (rows, r), gap)
             ties.append(r)
     keep_rows = [r for r in range(rows) if r not in ties]
-    if ties:
-        print("[near-tie] routing rows", ties)
     assert_close(cap_w.cpu().numpy()[keep_rows], wt[keep_rows], "topk weights")
     if not ties:
         c, o, p, _ = O.group(idx, E)

@@ -11,7 +11,7 @@ import pytest
 
 import oracle as O
 import synth
-from tests.gpu_util import NEAR_TIE, assert_close, assert_close_f16, f16_tensor
+from tests.gpu_util import NEAR_TIE, assert_close, assert_close_f16, f16_tensor, log_near_tie
 
 pytestmark = pytest.mark.gpu
 
@@ -115,8 +115,8 @@ def run_prefill(q, d, seed, P, row=0, rows=1, use_emb=False, forced=True, int8_k
         gap = res.lm_top2[0] - res.lm_top2[1]
         assert gap < tie, "token %d vs oracle %d, oracle gap %.3g" % (g_tok, res.tok, gap)
         ties.append(("token", gap))
-    if ties:
-        print("[near-tie]", ties, flush=True)
+    for t_ in ties:
+        log_near_tie(t_[0], "prompt pass " + " ".join(str(v) for v in t_[1:-1]), t_[-1])
     return res, dm, ds, model, st
 
 

@@ -10,7 +10,7 @@ import pytest
 
 import oracle as O
 import synth
-from tests.gpu_util import NEAR_TIE, f16_tensor
+from tests.gpu_util import NEAR_TIE, f16_tensor, log_near_tie
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ def _compare(got, ref, gaps, what, tie=NEAR_TIE):
     for i, (g, r) in enumerate(zip(got, ref)):
         if g != r:
             assert gaps[i] < tie, "%s token %d: %d vs oracle %d (oracle gap %.3g)" % (what, i, g, r, gaps[i])
-            print("[near-tie]", what, i, gaps[i], flush=True)
+            log_near_tie("token", "%s token %d" % (what, i), gaps[i])
             return False
     assert len(got) == len(ref), "%s: %d tokens vs oracle %d" % (what, len(got), len(ref))
     return True

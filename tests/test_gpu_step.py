@@ -13,7 +13,7 @@ import pytest
 
 import oracle as O
 import synth
-from tests.gpu_util import NEAR_TIE, assert_close, assert_close_f16, f16_tensor, from_f16_tensor
+from tests.gpu_util import NEAR_TIE, assert_close, assert_close_f16, f16_tensor, from_f16_tensor, log_near_tie
 
 pytestmark = pytest.mark.gpu
 
@@ -123,8 +123,8 @@ def run_steps(q, d, seed, prefix_len, gen_index, n_steps, forced=True, sample_ro
         nxt = tok.copy()
         nxt[rows] = res.tok
         tok = nxt
-    if ties:
-        print("[near-tie]", ties, flush=True)
+    for t_ in ties:
+        log_near_tie(t_[0], "step " + " ".join(str(v) for v in t_[1:-1]), t_[-1])
     return ties
 
 
@@ -144,10 +144,14 @@ def test_step_small_rows_32(q):
               n_steps=3)
 
 
-# Up to four rows the MoE combine runs inside the down projection and the
-# norms inside the consuming kernels; five rows take the separate kernels.
-# Shared-expert counts 0..2 and top-k 1..8 exercise the combine's slot lists.
-@pytest.mark.parametrize("R,ns,k", [(1, 0, 8), (1, 1, 1), (3, 2, 6), (4, 2, 6), (5, 2, 6)])
+# Launch paths by row count: up to 16 rows the norms are formed inside the
+# consuming kernels and the attention merge runs inside the O projection;
+# from 17 rows the separate merge, O projection and norm kernels run; up to
+# 32 rows the MoE down projection adds into the residual itself.  One row
+# takes the single-row grouping.  Shared-expert counts 0..2 and top-k 1..8
+# exercise the slot lists.
+@pytest.mark.parametrize("R,ns,k", [(1, 0, 8), (1, 1, 1), (3, 2, 6), (5, 2, 6), (16, 2, 6), (17, 2, 6),
+                                    (17, 1, 8)])
 def test_step_rows_around_folded_combine(q, R, ns, k):
     d = small_dims(n_shared=ns, top_k=k)
     run_steps(q, d, 530 + 16 * R + 4 * ns + k, prefix_len=[(11 * i + 5) % 41 for i in range(R)],
@@ -216,10 +220,14 @@ def test_step_single_moe_layer_q8(q):
     hidden = torch.from_numpy(h0.astype(np.float32)).cuda()
     cap_idx = torch.zeros((1, 1, d.top_k), dtype=torch.int32, device="cuda")
     cap = q.StepCapture(cap_idx.data_ptr(), None, None)
-    q.ocrdec_decode_step(dm.desc, ds.desc, None, hidden, None, None, cap, ws, wsb)
-    torch.cuda.synchronize()
+    # the oracle's routing is forced, so a near-tie (where both choices are
+    # correct) cannot part the two results; the GPU still reports its own
+    # choice, which must be the oracle's unless the oracle's gap is a near-tie
     res = O.decode_step(model, st.copy(), hidden_in=h0.astype(np.float64), with_lm=False)
+    forced = torch.from_numpy(np.array(res.topk_idx, np.int32).reshape(1, 1, d.top_k)).cuda()
+    q.ocrdec_decode_step(dm.desc, ds.desc, None, hidden, None, forced, cap, ws, wsb)
+    torch.cuda.synchronize()
     if not np.array_equal(cap_idx.cpu().numpy()[0, 0], res.topk_idx[0][0]):
         assert res.router_gap[0][0] < NEAR_TIE
-        pytest.skip("near-tie routing for this seed")
+        log_near_tie("routing", "single MoE layer (Q8_0)", res.router_gap[0][0])
     assert_close(hidden.cpu().numpy(), res.hidden, "moe layer hidden")
