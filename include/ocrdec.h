@@ -346,6 +346,22 @@ ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_state* st, 
                                  const ocrdec_step_capture* capture, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* ocrdec_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a static device array
+ * of 16 MiB that the library holds on every GPU it runs on until the process
+ * ends (enough for 32 rows with a cache of 4096 + 128 positions in the
+ * 12-layer decoder); the call allocates nothing.  All calls on one GPU share
+ * that array, so calls that overlap in time on one GPU (other streams, other
+ * threads) race and must not be made; consecutive calls on one stream are
+ * fine (nothing in it needs to start at zero).  Arguments and results as
+ * ocrdec_decode_step.  ocrdec_device_status cannot be used with it.
+ * Errors: as ocrdec_decode_step; WORKSPACE if the step needs more than the
+ * static array; DEVICE if the array's address cannot be obtained. */
+ocrdec_status ocrdec_decode_step_noalloc(const ocrdec_model* m, const ocrdec_state* st, const int32_t* tok_in,
+                                         float* hidden, int32_t* tok_out, const int32_t* forced_topk,
+                                         const ocrdec_step_capture* capture, void* stream);
+
 /* Device-side conditions of the most recent ocrdec_decode_step that used the
  * workspace `ws` (the Falcon-OCR card, "Two traps the host must avoid": a
  * wrong cache length or position does not fail, it yields fluent but

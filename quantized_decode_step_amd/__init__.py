@@ -113,6 +113,7 @@ _lib.ocrdec_prefill_batch.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _vp, _
                                       _P(StepCapture), _vp, _sz, _vp]
 _lib.ocrdec_round_workspace_bytes.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _P(_sz)]
 _lib.ocrdec_run_round.argtypes = [_P(ModelDesc), _P(StateDesc), _vp, _i32, _vp, _i32, _i32, _vp, _sz, _vp]
+_lib.ocrdec_decode_step_noalloc.argtypes = [_P(ModelDesc), _P(StateDesc), _vp, _vp, _vp, _vp, _P(StepCapture), _vp]
 _lib.ocrdec_device_status.argtypes = [_vp, _sz, _vp, _P(ctypes.c_uint32)]
 _lib.ocrdec_prefill.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _P(StepCapture),
                                 _vp, _sz, _vp]
@@ -120,7 +121,8 @@ for _fn in ("ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack", "ocrdec_gemv_
             "ocrdec_lm_argmax", "ocrdec_attn_workspace_bytes",
             "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes", "ocrdec_moe_layer", "ocrdec_step_workspace_bytes",
             "ocrdec_decode_step", "ocrdec_prefill_workspace_bytes", "ocrdec_prefill", "ocrdec_round_workspace_bytes",
-            "ocrdec_run_round", "ocrdec_prefill_batch_workspace_bytes", "ocrdec_prefill_batch", "ocrdec_device_status"):
+            "ocrdec_run_round", "ocrdec_prefill_batch_workspace_bytes", "ocrdec_prefill_batch", "ocrdec_device_status",
+            "ocrdec_decode_step_noalloc"):
     getattr(_lib, _fn).restype = ctypes.c_int
 
 EXPORTED = ["ocrdec_last_error", "ocrdec_version", "ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack",
@@ -128,7 +130,7 @@ EXPORTED = ["ocrdec_last_error", "ocrdec_version", "ocrdec_packed_bytes", "ocrde
             "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes",
             "ocrdec_moe_layer", "ocrdec_step_workspace_bytes", "ocrdec_decode_step",
             "ocrdec_prefill_workspace_bytes", "ocrdec_prefill", "ocrdec_round_workspace_bytes", "ocrdec_run_round",
-            "ocrdec_prefill_batch_workspace_bytes", "ocrdec_prefill_batch", "ocrdec_device_status"]
+            "ocrdec_prefill_batch_workspace_bytes", "ocrdec_prefill_batch", "ocrdec_device_status", "ocrdec_decode_step_noalloc"]
 
 
 def _ptr(t) -> int | None:
@@ -230,6 +232,13 @@ def ocrdec_decode_step(m: ModelDesc, st: StateDesc, tok_in=None, hidden=None, to
     _check(_lib.ocrdec_decode_step(ctypes.byref(m), ctypes.byref(st), _ptr(tok_in), _ptr(hidden), _ptr(tok_out),
                                    _ptr(forced_topk), ctypes.byref(capture) if capture is not None else None,
                                    _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def ocrdec_decode_step_noalloc(m: ModelDesc, st: StateDesc, tok_in=None, hidden=None, tok_out=None, forced_topk=None,
+                               capture: StepCapture | None = None, stream=None):
+    _check(_lib.ocrdec_decode_step_noalloc(ctypes.byref(m), ctypes.byref(st), _ptr(tok_in), _ptr(hidden),
+                                           _ptr(tok_out), _ptr(forced_topk),
+                                           ctypes.byref(capture) if capture is not None else None, _stream(stream)))
 
 
 def ocrdec_device_status(ws, ws_bytes: int, stream=None) -> int:

@@ -5,8 +5,18 @@
 // enqueued on the caller's stream with no host synchronisation, so the token
 // of one step can feed the next on the device ("How it is meant to be run",
 // Falcon-OCR card: rows of a round share one read of the weights).
+#include <mutex>
+
 #include "attn.hpp"
 #include "moe.hpp"
+
+// Scratch of ocrdec_decode_step_noalloc: the step's workspace for callers that
+// cannot allocate, in device memory that every GPU the library runs on holds
+// until the process ends.  Host code never passes this name to a kernel or a
+// copy (on the host it is only a stand-in for the symbol): it uses the device
+// address that hipGetSymbolAddress returns for the current device.
+static constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace ocrdec {
 
@@ -375,6 +385,52 @@ extern "C" ocrdec_status ocrdec_step_workspace_bytes(const ocrdec_model* m, cons
     OCR_CHECK_ARG(st->prefix_cap + st->ring_cap <= (1 << 16), "prefix_cap + ring_cap must be <= 65536");
     *bytes = carve_step(nullptr, m, st->rows, st->prefix_cap + st->ring_cap).bytes;
     return OCRDEC_OK;
+}
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept; NULL if the lookup fails.
+void* scratch_ptr(std::string* err) {
+    static std::mutex mu;
+    static void* ptrs[64] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) {
+        *err = std::string("hipGetDevice: ") + (e != hipSuccess ? hipGetErrorString(e) : "device index out of range");
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *err = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+            return nullptr;
+        }
+        ptrs[dev] = p;
+    }
+    return ptrs[dev];
+}
+
+}  // namespace
+
+extern "C" ocrdec_status ocrdec_decode_step_noalloc(const ocrdec_model* m, const ocrdec_state* st,
+                                                    const int32_t* tok_in, float* hidden, int32_t* tok_out,
+                                                    const int32_t* forced_topk, const ocrdec_step_capture* cap,
+                                                    void* stream) {
+    ocrdec_status s0 = check_step(m, st);
+    if (s0 != OCRDEC_OK) return s0;
+    OCR_CHECK_ARG(st->prefix_cap + st->ring_cap <= (1 << 16), "prefix_cap + ring_cap must be <= 65536");
+    const size_t need = carve_step(nullptr, m, st->rows, st->prefix_cap + st->ring_cap).bytes;
+    if (need > kScratchBytes)
+        return fail(OCRDEC_ERR_WORKSPACE, "ocrdec_decode_step_noalloc: this model and state need a " +
+                                              std::to_string(need) + "-byte workspace; the static scratch holds " +
+                                              std::to_string(kScratchBytes) + " bytes (use ocrdec_decode_step)");
+    std::string err;
+    void* ws = scratch_ptr(&err);
+    if (!ws) return fail(OCRDEC_ERR_DEVICE, err);
+    return ocrdec_decode_step(m, st, tok_in, hidden, tok_out, forced_topk, cap, ws, kScratchBytes, stream);
 }
 
 extern "C" ocrdec_status ocrdec_device_status(const void* ws, size_t ws_bytes, void* stream, uint32_t* flags) {
