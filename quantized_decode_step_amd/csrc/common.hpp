@@ -211,7 +211,7 @@ OCR_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
 // workgroups add their parts (atomic adds included), so the step is bitwise
 // reproducible.  The range is |h| < 2^30; a non-finite addend or one beyond
 // the range is replaced by 0 and reported through the status word.  Readers
-// convert to fp32 (correctly rounded through fp64).
+// convert to fp32.
 // ---------------------------------------------------------------------------
 
 typedef long long fix_t;
@@ -220,12 +220,22 @@ constexpr float kFixLimit = 1073741824.0f;  // 2^30
 // Status word bits (the decode step's workspace; ocrdec_device_status).
 constexpr uint32_t kStatTokenRange = 1u, kStatResidual = 2u, kStatLogit = 4u, kStatNoToken = 8u;
 
+// a = fl + f with fl = floor(a) (an integer below 2^30 in magnitude) and f in
+// [0, 1) exact in fp32; f * 2^32 is an integer whenever |a| >= 2^-9 and is
+// rounded to the nearest one below that, so the conversion is exact except
+// for the bits of tiny addends below 2^-32.  All in fp32/int32 arithmetic.
 OCR_DEV fix_t fix_from(float a, bool& bad) {
     const bool ok = fabsf(a) < kFixLimit;  // false for NaN
     bad |= !ok;
-    return ok ? (fix_t)__builtin_rint((double)a * 4294967296.0) : 0;
+    a = ok ? a : 0.f;
+    const float fl = floorf(a);
+    const uint32_t lo = (uint32_t)rintf((a - fl) * 4294967296.0f);  // <= 2^32 - 2^8
+    return (fix_t)(((uint64_t)(uint32_t)(int32_t)fl << 32) | lo);
 }
-OCR_DEV float fix_to(fix_t v) { return (float)((double)v * (1.0 / 4294967296.0)); }
+// hi + lo * 2^-32 with one fused rounding (hi exact below 2^24).
+OCR_DEV float fix_to(fix_t v) {
+    return fmaf((float)(uint32_t)v, 2.3283064365386963e-10f, (float)(int32_t)(v >> 32));
+}
 
 // Four consecutive residual values (fp32 or fixed point) at index 4*c4.
 OCR_DEV float4 ld_resid4(const float* h, int c4) { return ((const float4*)h)[c4]; }
@@ -233,10 +243,16 @@ OCR_DEV float4 ld_resid4(const fix_t* h, int c4) {
     const longlong2 a = ((const longlong2*)h)[2 * c4], b = ((const longlong2*)h)[2 * c4 + 1];
     return make_float4(fix_to(a.x), fix_to(a.y), fix_to(b.x), fix_to(b.y));
 }
-OCR_DEV void st_resid4(float* h, int c4, float4 v, bool&) { ((float4*)h)[c4] = v; }
-OCR_DEV void st_resid4(fix_t* h, int c4, float4 v, bool& bad) {
-    ((longlong2*)h)[2 * c4] = make_longlong2(fix_from(v.x, bad), fix_from(v.y, bad));
-    ((longlong2*)h)[2 * c4 + 1] = make_longlong2(fix_from(v.z, bad), fix_from(v.w, bad));
+// Stores four values at index 4*c4 and returns them as a reader will load them.
+OCR_DEV float4 st_resid4(float* h, int c4, float4 v, bool&) {
+    ((float4*)h)[c4] = v;
+    return v;
+}
+OCR_DEV float4 st_resid4(fix_t* h, int c4, float4 v, bool& bad) {
+    const fix_t a = fix_from(v.x, bad), b = fix_from(v.y, bad), c = fix_from(v.z, bad), d = fix_from(v.w, bad);
+    ((longlong2*)h)[2 * c4] = make_longlong2(a, b);
+    ((longlong2*)h)[2 * c4 + 1] = make_longlong2(c, d);
+    return make_float4(fix_to(a), fix_to(b), fix_to(c), fix_to(d));
 }
 
 // h[i] += a as an atomic integer add (any order gives the same sum).
@@ -251,23 +267,46 @@ OCR_DEV void report_status(uint32_t* status, bool flag, uint32_t bits) {
     if (status && m && (threadIdx.x & 63) == (unsigned)__builtin_ctzll(m)) atomicOr(status, bits);
 }
 
-// x = fp16(h / sqrt(mean(h^2) + eps) * gamma) for one residual row (fp32 or fixed point) of
-// H <= 256 * NV values (H % 4 == 0) by one wavefront: every load (row and
-// gain) is issued before the first use, so the row costs one memory round
-// trip.  The result goes to x and to xl (LDS), each if non-NULL.
-template <int NV = 16, class HT = float>
-OCR_DEV void wave_rmsnorm_row(const HT* h, const uint16_t* gamma, int H, float eps, uint16_t* x,
-                              uint16_t* xl = nullptr) {
+// The four-value groups c4 = lane + 64 i (i < NV) of one residual row of H
+// values (H % 4 == 0, n4 = H / 4 groups) as fp32, zero past the row.  Every
+// load is issued before the first use (addresses clamped into the row, no
+// branches), so the row costs one memory round trip in either form.
+template <int NV>
+OCR_DEV void load_resid_row(const float* h, int n4, float4 (&v)[NV]) {
     const int lane = threadIdx.x & 63;
-    const int n4 = H / 4;
-    float4 v[NV];
-    uint2 g[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = ((const float4*)h)[min(lane + 64 * i, n4 - 1)];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        if (lane + 64 * i >= n4) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+template <int NV>
+OCR_DEV void load_resid_row(const fix_t* h, int n4, float4 (&v)[NV]) {
+    const int lane = threadIdx.x & 63;
+    longlong2 a[NV], b[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int c4 = lane + 64 * i;
-        v[i] = c4 < n4 ? ld_resid4(h, c4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        g[i] = c4 < n4 ? ((const uint2*)gamma)[c4] : make_uint2(0, 0);
+        const int c = min(lane + 64 * i, n4 - 1);
+        a[i] = ((const longlong2*)h)[2 * c];
+        b[i] = ((const longlong2*)h)[2 * c + 1];
     }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        v[i] = lane + 64 * i < n4 ? make_float4(fix_to(a[i].x), fix_to(a[i].y), fix_to(b[i].x), fix_to(b[i].y))
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// x = fp16(v / sqrt(mean(v^2) + eps) * gamma) for one row held in registers
+// as load_resid_row leaves it (one wavefront).  The gains are requested first.
+// The result goes to x and to xl (LDS), each if non-NULL.
+template <int NV>
+OCR_DEV void rmsnorm_regs(const float4 (&v)[NV], const uint16_t* gamma, int H, float eps, uint16_t* x,
+                          uint16_t* xl) {
+    const int lane = threadIdx.x & 63;
+    const int n4 = H / 4;
+    uint2 g[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) g[i] = ((const uint2*)gamma)[min(lane + 64 * i, n4 - 1)];
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
@@ -285,4 +324,15 @@ OCR_DEV void wave_rmsnorm_row(const HT* h, const uint16_t* gamma, int H, float e
             if (xl) ((uint2*)xl)[c4] = make_uint2(lo, hi);
         }
     }
+}
+
+// x = fp16(h / sqrt(mean(h^2) + eps) * gamma) for one residual row (fp32 or
+// fixed point) of H <= 256 * NV values (H % 4 == 0) by one wavefront: one
+// memory round trip for the row and the gains.
+template <int NV = 16, class HT = float>
+OCR_DEV void wave_rmsnorm_row(const HT* h, const uint16_t* gamma, int H, float eps, uint16_t* x,
+                              uint16_t* xl = nullptr) {
+    float4 v[NV];
+    load_resid_row<NV>(h, H / 4, v);
+    rmsnorm_regs<NV>(v, gamma, H, eps, x, xl);
 }

@@ -41,9 +41,10 @@ OCR_DEV void status_begin(uint32_t* status, int r, int rows, bool tok_bad, bool 
     }
 }
 
-// h[r] = embed[tok[r]] (fp16 table) or src[r] (fp32); x[r] = norm(h[r]).
-// One wavefront per row.  HT: the residual's representation (the decode
-// step's fixed point, or fp32 for the prompt pass).
+// h[r] = embed[tok[r]] (fp16 table) or src[r] (fp32); x[r] = norm(h[r]),
+// formed from the values as stored.  One wavefront per row (H <= 4096).  HT:
+// the residual's representation (the decode step's fixed point, or fp32 for
+// the prompt pass).
 template <class HT>
 __global__ __launch_bounds__(64) void embed_norm_kernel(const int32_t* tok, const uint16_t* embed, int vocab,
                                                         const float* src, HT* h, const uint16_t* gamma, int H,
@@ -53,6 +54,7 @@ __global__ __launch_bounds__(64) void embed_norm_kernel(const int32_t* tok, cons
     HT* hr = h + (int64_t)r * H;
     const int n4 = H / 4;
     bool tok_bad = false, bad = false;
+    float4 v[16];
     if (tok || rows16) {
         // a row of the fp16 table, or row r of fp16 input features
         int t = tok ? tok[r] : 0;
@@ -61,36 +63,23 @@ __global__ __launch_bounds__(64) void embed_norm_kernel(const int32_t* tok, cons
         const uint2* from = (const uint2*)(tok ? embed + (int64_t)t * H : rows16 + (int64_t)r * H);
         uint2 e[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int c4 = lane + 64 * i;
-            e[i] = c4 < n4 ? from[c4] : make_uint2(0, 0);
-        }
+        for (int i = 0; i < 16; ++i) e[i] = from[min(lane + 64 * i, n4 - 1)];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int c4 = lane + 64 * i;
-            if (c4 < n4)
-                st_resid4(hr, c4,
-                          make_float4(h2f((uint16_t)(e[i].x & 0xFFFF)), h2f((uint16_t)(e[i].x >> 16)),
-                                      h2f((uint16_t)(e[i].y & 0xFFFF)), h2f((uint16_t)(e[i].y >> 16))),
-                          bad);
-        }
+        for (int i = 0; i < 16; ++i)
+            v[i] = make_float4(h2f((uint16_t)(e[i].x & 0xFFFF)), h2f((uint16_t)(e[i].x >> 16)),
+                               h2f((uint16_t)(e[i].y & 0xFFFF)), h2f((uint16_t)(e[i].y >> 16)));
     } else {
         const float4* from = (const float4*)(src + (int64_t)r * H);
-        float4 v[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int c4 = lane + 64 * i;
-            v[i] = c4 < n4 ? from[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        for (int i = 0; i < 16; ++i) v[i] = from[min(lane + 64 * i, n4 - 1)];
+    }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int c4 = lane + 64 * i;
-            if (c4 < n4) st_resid4(hr, c4, v[i], bad);
-        }
+    for (int i = 0; i < 16; ++i) {
+        const int c4 = lane + 64 * i;
+        v[i] = c4 < n4 ? st_resid4(hr, c4, v[i], bad) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     status_begin(status, r, rows, tok_bad, bad);
-    __threadfence_block();
-    wave_rmsnorm_row(hr, gamma, H, eps, x + (int64_t)r * H);
+    rmsnorm_regs<16>(v, gamma, H, eps, x + (int64_t)r * H, nullptr);
 }
 
 // h[r] = row tok[r] of a packed quantised table, dequantised; x[r] = norm(h[r]).
@@ -100,7 +89,7 @@ __global__ __launch_bounds__(64) void embed_norm_kernel(const int32_t* tok, cons
 // i < 8) and the row's block scales.  Lane l of the wavefront takes the
 // (chunk, group) pairs p = l, l+64, ...; each product d*q is exact in fp32
 // (q and (q-8) are integers of at most 8 bits, d has 11).
-template <int FMT, class HT>
+template <int FMT, class HT, int NV>
 __global__ __launch_bounds__(64) void embed_q_norm_kernel(const int32_t* tok, const uint8_t* table, int vocab,
                                                           int64_t nchunks, HT* h, const uint16_t* gamma, int H,
                                                           float eps, uint16_t* x, uint32_t* status, int rows) {
@@ -137,7 +126,7 @@ __global__ __launch_bounds__(64) void embed_q_norm_kernel(const int32_t* tok, co
     }
     status_begin(status, r, rows, tok_bad, bad);
     __threadfence_block();
-    wave_rmsnorm_row(hr, gamma, H, eps, x + (int64_t)r * H);
+    wave_rmsnorm_row<NV>(hr, gamma, H, eps, x + (int64_t)r * H);
 }
 
 // h[r] += y[r]; x[r] = fp16(RMSNorm(h[r]) * gamma): one wavefront per row.
@@ -174,11 +163,19 @@ __global__ __launch_bounds__(64) void gather_rows_kernel(const uint16_t* src, ui
 }
 
 // x[r] = fp16(RMSNorm(h[r]) * gamma) of the fixed-point residual: one
-// wavefront per row.
+// wavefront per row (H <= 256 * NV).
+template <int NV>
 __global__ __launch_bounds__(64) void norm_kernel(const fix_t* h, const uint16_t* gamma, int H, float eps,
                                                   uint16_t* x) {
     const int r = blockIdx.x;
-    wave_rmsnorm_row(h + (int64_t)r * H, gamma, H, eps, x + (int64_t)r * H);
+    wave_rmsnorm_row<NV>(h + (int64_t)r * H, gamma, H, eps, x + (int64_t)r * H);
+}
+
+// norm_kernel with the register count its row size needs
+void launch_norm(const fix_t* h, const uint16_t* gamma, int H, float eps, uint16_t* x, int rows, hipStream_t s) {
+    if (H <= 1280) hipLaunchKernelGGL(norm_kernel<5>, dim3(rows), dim3(64), 0, s, h, gamma, H, eps, x);
+    else if (H <= 2048) hipLaunchKernelGGL(norm_kernel<8>, dim3(rows), dim3(64), 0, s, h, gamma, H, eps, x);
+    else hipLaunchKernelGGL(norm_kernel<16>, dim3(rows), dim3(64), 0, s, h, gamma, H, eps, x);
 }
 
 __global__ void copy_rows_kernel(const float* src, float* dst, int64_t n) {
@@ -470,8 +467,12 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
         const int64_t nch = n_chunks(m->embed_q.fmt, H);
 #define OCR_EQ(F_)                                                                                                 \
     case F_:                                                                                                       \
-        hipLaunchKernelGGL((embed_q_norm_kernel<F_, fix_t>), dim3(R), dim3(64), 0, s, tok_in, tq, m->vocab, nch,   \
-                           w.h, m->layers[0].attn_norm, H, m->norm_eps, w.x, w.status, R);                         \
+        if (H <= 1280)                                                                                             \
+            hipLaunchKernelGGL((embed_q_norm_kernel<F_, fix_t, 5>), dim3(R), dim3(64), 0, s, tok_in, tq, m->vocab, \
+                               nch, w.h, m->layers[0].attn_norm, H, m->norm_eps, w.x, w.status, R);                \
+        else                                                                                                       \
+            hipLaunchKernelGGL((embed_q_norm_kernel<F_, fix_t, 16>), dim3(R), dim3(64), 0, s, tok_in, tq, m->vocab,\
+                               nch, w.h, m->layers[0].attn_norm, H, m->norm_eps, w.x, w.status, R);                \
         break;
         switch (m->embed_q.fmt) {
             OCR_EQ(OCRDEC_F16)
@@ -566,7 +567,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                        w.status);
             ++moe_l;
         } else {
-            if (!prolog) hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(64), 0, s, w.h, L.ffn_norm, H, m->norm_eps, w.x);
+            if (!prolog) launch_norm(w.h, L.ffn_norm, H, m->norm_eps, w.x, R, s);
             const int F = L.dense_ff;
             {
                 GemvPlan pl = plan_gemv(L.dense_gate_up.fmt, 2 * F, H, R, EPI_GLU);
@@ -600,7 +601,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                 launch_gemv(L.dense_down.fmt, EPI_RESID, pl, gp, s);
             }
             if (next_norm && !prolog)
-                hipLaunchKernelGGL(norm_kernel, dim3(R), dim3(64), 0, s, w.h, next_norm, H, m->norm_eps, w.x);
+                launch_norm(w.h, next_norm, H, m->norm_eps, w.x, R, s);
         }
     }
     if (hidden) {
@@ -694,8 +695,8 @@ extern "C" ocrdec_status ocrdec_prefill_batch(const ocrdec_model* m, const ocrde
         const int64_t nch = n_chunks(m->embed_q.fmt, H);
 #define OCR_EQ(F_)                                                                                                 \
     case F_:                                                                                                       \
-        hipLaunchKernelGGL((embed_q_norm_kernel<F_, float>), dim3(T), dim3(64), 0, s, tok, tq, m->vocab, nch, w.h, \
-                           m->layers[0].attn_norm, H, m->norm_eps, w.x, (uint32_t*)nullptr, T);                    \
+        hipLaunchKernelGGL((embed_q_norm_kernel<F_, float, 16>), dim3(T), dim3(64), 0, s, tok, tq, m->vocab, nch,  \
+                           w.h, m->layers[0].attn_norm, H, m->norm_eps, w.x, (uint32_t*)nullptr, T);               \
         break;
         switch (m->embed_q.fmt) {
             OCR_EQ(OCRDEC_F16)
