@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--no-round", action="store_true", help="skip the round-scheduler line")
     ap.add_argument("--prompt-iters", type=int, default=5)
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-call HBM GB/s of one layer's entry points")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing inside the step")
+    ap.add_argument("--no-layers", action="store_true", help="skip the single dense and MoE layer lines")
+    ap.add_argument("--no-sink", action="store_true", help="skip the sink-augmented block lines")
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--copy-mb", type=int, default=512, help="size of the calibration copy in --mode lm")
     return ap.parse_args()
@@ -109,6 +112,88 @@ def algorithmic_bytes(dm, d, rows: int, distinct_experts_per_layer: float, avg_k
     tot += nb(dm.src_lm) + 2 * H + rows * 2 * H
     tot += d.n_layers * rows * 2 * d.n_heads * d.head_dim * kv_bytes_per_value * avg_keys
     return tot
+
+
+def kernel_bytes(dm, d, R: int, distinct: float, avg_keys: float, kv_bytes_per_value: float = 2.0) -> dict:
+    """Algorithmic bytes of one launch of each kernel kind of the decode step
+    (the weight blocks it must stream, the KV window, the rows it reads)."""
+    def nb(m):
+        return {0: 2.0, 1: 34 / 32, 2: 18 / 32, 3: 36 / 32}[m.fmt] * m.n * m.k
+    lay = next(l for l in dm.src_layers if l.is_moe)
+    dense = next((l for l in dm.src_layers if not l.is_moe), None)
+    H, E = d.hidden, d.n_experts
+    glu_e, down_e = nb(lay.exp_gate_up) / E, nb(lay.exp_down) / E
+    glu_s, down_s = nb(lay.sh_gate_up) / d.n_shared, nb(lay.sh_down) / d.n_shared
+    kv = R * 2 * d.n_heads * d.head_dim * kv_bytes_per_value * avg_keys
+    out = {"qkv": nb(lay.wqkv) + R * H * 2, "attn": kv, "attn_merge_o": nb(lay.wo), "o_proj": nb(lay.wo),
+           "route": nb(lay.router), "expert_glu": distinct * glu_e + d.n_shared * glu_s,
+           "expert_down": distinct * down_e + d.n_shared * down_s, "lm_head": nb(dm.src_lm) + R * H * 2}
+    if dense is not None:
+        out["dense_glu"] = nb(dense.dense_gate_up)
+        out["dense_down"] = nb(dense.dense_down)
+    return out
+
+
+def profile_step(q, torch, stream, step_fn, reps: int = 10, capacity: int = 512):
+    """Per-kernel time inside the decode step: a HIP event before every kernel
+    the library enqueues (ocrdec_profile_set) and one after the last, direct
+    launches on the bench stream behind a short spin kernel (so that the whole
+    step is queued before the GPU reaches it and host enqueue time does not
+    show); the time between consecutive events is a kernel plus the gap
+    before it.  Returns ({kind: [us per launch, ...]} averaged over `reps`
+    steps, total us per step), or (None, None)."""
+    import ctypes
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+    for e in evs:  # creates the runtime events (torch creates them on first record)
+        e.record(stream)
+    torch.cuda.synchronize()
+    handles = (ctypes.c_void_p * capacity)(*[e.cuda_event for e in evs])
+    kinds = (ctypes.c_int32 * capacity)()
+    acc, names, tot = None, None, 0.0
+    try:
+        for _ in range(reps):
+            prof = q.Profile(ctypes.cast(handles, ctypes.POINTER(ctypes.c_void_p)), kinds, capacity, 0)
+            with torch.cuda.stream(stream):
+                torch.cuda._sleep(2_000_000)
+                q.ocrdec_profile_set(prof)
+                try:
+                    step_fn(stream)
+                    q.ocrdec_profile_mark(stream)
+                finally:
+                    q.ocrdec_profile_set(None)
+            torch.cuda.synchronize()
+            n = prof.count
+            t = np.array([evs[i].elapsed_time(evs[i + 1]) * 1000.0 for i in range(n - 1)])
+            if acc is None:
+                acc, names = t, [q.KERNEL_NAMES[kinds[i]] for i in range(n - 1)]
+            else:
+                acc += t
+            tot += evs[0].elapsed_time(evs[n - 1]) * 1000.0
+        acc /= reps
+        out = {}
+        for i, k in enumerate(names):
+            out.setdefault(k, []).append(float(acc[i]))
+        return out, tot / reps
+    except Exception as ex:  # reported, not fatal: the rest of the line stands
+        print("profile_step: %s" % ex, file=sys.stderr)
+        return None, None
+    finally:
+        torch.cuda.synchronize()
+
+
+def kernel_table(prof: dict, byts: dict, ms_step: float):
+    """Rows of {kernel, launches, avg_us, us_per_step, share, bytes_per_launch, GBps, frac} sorted by time."""
+    rows = []
+    for k, v in prof.items():
+        tot = float(np.sum(v))
+        r = {"kernel": k, "launches_per_step": len(v), "avg_us": round(tot / len(v), 2), "us_per_step": round(tot, 1),
+             "share_of_step": round(tot / (ms_step * 1000.0), 3)}
+        if k in byts:
+            gbs = byts[k] / (tot / len(v) * 1e-6) / 1e9
+            r.update({"bytes_per_launch": round(byts[k]), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)})
+        rows.append(r)
+    rows.sort(key=lambda r: -r["us_per_step"])
+    return rows
 
 
 def first_gen_index(steps: int, warmup: int, ring: int = 128) -> int:
@@ -206,13 +291,28 @@ def main():
         out["algorithmic_MB_per_step"] = byt / 1e6
         out["step_GBps"] = byt / (ms * 1e-3) / 1e9
         del graph
+        if want_sample and not args.no_profile:
+            prof, prof_us = profile_step(q, torch, stream, lambda s: q.ocrdec_decode_step(dm.desc, ds.desc, tok, None,
+                                                                                           tok, None, None, ws, wsb,
+                                                                                           stream=s))
+            if prof is not None:
+                out["profiled_us_per_step"] = round(prof_us, 1)
+                # each event and the direct launch add a roughly fixed time per
+                # kernel: (profiled step - graph step) / launches, subtracted
+                n_launch = sum(len(v) for v in prof.values())
+                ovh = max(0.0, (prof_us - ms * 1000.0) / n_launch)
+                out["event_overhead_us_per_launch"] = round(ovh, 2)
+                prof = {k: [max(t - ovh, 0.5 * t) for t in v] for k, v in prof.items()}
+                byk = kernel_bytes(dm, d, R, out["distinct_experts_per_moe_layer"] or d.top_k, avg_keys,
+                                   kv_bytes_per_value=(1.0 + 2.0 / d.head_dim) if int8_kv else 2.0)
+                out["kernels"] = kernel_table(prof, byk, ms)
         return out
 
     main_run = run_rows(args.rows, args.steps, args.warmup, True)
     sweep = []
     for r in [int(x) for x in args.sweep.split(",") if x.strip()]:
         if r != args.rows:
-            sweep.append(run_rows(r, args.steps, args.warmup, False))
+            sweep.append(run_rows(r, args.steps, args.warmup, True))
 
     # ---- the same step over an INT8 KV cache (codes + one fp16 scale per row, head and slot)
     int8_kv = None
@@ -276,6 +376,10 @@ def main():
     # ---- HBM GB/s of one decoder layer's entry points at one row
     kernels = None if args.no_kernels else per_call_bandwidth(q, torch, dev, stream, dm, d)
 
+    # ---- single decoder layers (dense fp16; Q8_0 MoE) and the sink-augmented block
+    layers1 = None if args.no_layers else single_layers(q, torch, dev, stream)
+    sink = None if args.no_sink else sink_blocks(q, torch, dev, stream)
+
     # ---- the prefill-shaped MoE layer (2048 tokens, MFMA path), reported beside the decode metric
     prefill = None if args.no_prefill else prefill_moe(args, q, torch, dev, stream)
 
@@ -315,17 +419,21 @@ def main():
                      "frac": round(main_run["step_GBps"] / HBM_PEAK_GBS, 4),
                      "distinct_experts_per_moe_layer": main_run["distinct_experts_per_moe_layer"]},
         "rows_sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in sweep],
-        "roofline": {"kernel": ("lm_argmax_kernel<F16, ring 10> (LM head %dx%d + fused argmax, %d row(s); "
-                                "one CU-balanced workgroup per CU, then the partial merge)" if R <= 16 else
-                                "gemv_kernel<F16,4,1,1,ARGMAX> (LM head %dx%d + fused argmax, %d row(s))")
-                               % (d.vocab, d.hidden, R),
-                     "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "traffic_note": traffic_note,
-                     "avg_us": round(lm_us, 2), "algorithmic_bytes": lm_bytes},
+        "roofline": dominant_roofline(main_run.get("kernels"), traffic if R == 1 else None),
+        "lm_head": {"kernel": ("lm_argmax_kernel<F16, ring 10> (LM head %dx%d + fused argmax, %d row(s); "
+                               "one CU-balanced workgroup per CU, then the partial merge)" if R <= 16 else
+                               "gemv_kernel<F16,4,1,1,ARGMAX> (LM head %dx%d + fused argmax, %d row(s))")
+                              % (d.vocab, d.hidden, R),
+                    "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_note": traffic_note,
+                    "avg_us": round(lm_us, 2), "algorithmic_bytes": lm_bytes,
+                    "timing": "ocrdec_lm_argmax alone, %d calls between HIP events on its stream" % args.lm_iters},
+        "step_kernels": main_run.get("kernels"),
         "cpu_baseline": cpu,
         "quantised_head": qhead,
         "kernels": kernels,
+        "single_layers": layers1,
+        "sink_block": sink,
         "prefill_moe": prefill,
         "prompt_pass": prompt,
         "int8_kv": int8_kv,
@@ -333,6 +441,25 @@ def main():
         "setup_s": round(t_build, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def dominant_roofline(kernels, lm_traffic):
+    """Roofline of the kernel kind that takes the most time per step (event
+    timing inside the step): algorithmic bytes per launch / average launch
+    time (kernel plus the gap before it)."""
+    if not kernels:
+        return None
+    k = next((r for r in kernels if "bytes_per_launch" in r), None)
+    if k is None:
+        return None
+    return {"kernel": k["kernel"], "bound": "hbm", "achieved": k["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": k["frac"], "traffic": lm_traffic if k["kernel"] == "lm_head" else None,
+            "avg_us": k["avg_us"], "launches_per_step": k["launches_per_step"], "share_of_step": k["share_of_step"],
+            "algorithmic_bytes": k["bytes_per_launch"],
+            "timing": "HIP events recorded on the bench stream before every kernel of the step (ocrdec_profile_set), "
+                      "direct launches queued behind a spin kernel, mean of 10 steps; a launch's time is the interval "
+                      "to the next event minus the mean per-launch cost of the events and direct launches "
+                      "((profiled step - graph step) / launches)"}
 
 
 def per_call_bandwidth(q, torch, dev, stream, dm, d, layer: int = 1, reps: int = 20, replays: int = 5):
@@ -402,6 +529,122 @@ def per_call_bandwidth(q, torch, dev, stream, dm, d, layer: int = 1, reps: int =
             del g
     return {"rows": 1, "layer": "MoE layer %d of the 12-layer decoder" % layer, "peak_GBps": HBM_PEAK_GBS,
             "calls": out}
+
+
+def _graph_time_us(torch, stream, fn, reps: int = 20, replays: int = 5) -> float:
+    """Microseconds per call of fn(stream): `reps` calls captured in a graph,
+    replayed `replays` times between HIP events on the stream."""
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            fn(stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(reps):
+                fn(torch.cuda.current_stream())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1000.0 / (reps * replays)
+
+
+def single_layers(q, torch, dev, stream):
+    """One decoder layer, one decode step at one row: the dense fp16 layer
+    (256 cached positions + the new token, SwiGLU 3584, seed 1001) and the Q8_0
+    MoE layer (prefix 1100 + a full 128-slot ring, seed 1002).  The hidden
+    state goes in and comes out (no embedding, no LM head).  Algorithmic bytes:
+    every weight block once (the MoE layer's 6 routed experts of the row and
+    the 2 shared ones) plus the KV window."""
+    import synth
+    out = []
+    for name, d, seed, pl, gi in (("dense fp16 layer: 1 row, 10x128 MHA over 256 cached + 1 new, SwiGLU 3584",
+                                   synth.dims_dense_layer(), 1001, 256, 0),
+                                  ("MoE Q8_0 layer: 1 row, prefix 1100 + full 128-slot ring, 64 routed top-6 + 2 "
+                                   "shared experts of 896", synth.dims_moe_layer(), 1002, 1100, 128)):
+        model = synth.make_model(d, seed, with_embed=False, with_lm=False)
+        st = synth.make_state(d, seed, [pl], [gi])
+        dm = q.DeviceModel(model)
+        ds = q.DeviceState(st, d.prefix_cap, d.ring_cap)
+        dm.bind_caches(ds.k_cache, ds.v_cache)
+        wsb = q.ocrdec_step_workspace_bytes(dm.desc, ds.desc)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        h0 = synth.normal_f16(synth.stream_id(seed, "h0"), (1, d.hidden))
+        hidden = torch.from_numpy(h0.astype(np.float32)).to(dev)
+        us = _graph_time_us(torch, stream, lambda s: q.ocrdec_decode_step(dm.desc, ds.desc, None, hidden, None, None,
+                                                                          None, ws, wsb, stream=s))
+
+        def nb(m):
+            return {0: 2.0, 1: 34 / 32, 2: 18 / 32, 3: 36 / 32}[m.fmt] * m.n * m.k
+        lay = model.layers[0]
+        byt = nb(lay.wqkv) + nb(lay.wo) + 4 * d.hidden
+        if lay.is_moe:
+            byt += nb(lay.router) + d.top_k * (nb(lay.exp_gate_up) + nb(lay.exp_down)) / d.n_experts
+            byt += nb(lay.sh_gate_up) + nb(lay.sh_down)
+            keys = pl + d.ring_cap
+        else:
+            byt += nb(lay.dense_gate_up) + nb(lay.dense_down)
+            keys = pl + 1
+        byt += 2 * d.n_heads * d.head_dim * 2 * keys
+        gbs = byt / (us * 1e-6) / 1e9
+        out.append({"workload": name, "us_per_step": round(us, 2), "rows_steps_per_s": round(1e6 / us, 1),
+                    "algorithmic_MB": round(byt / 1e6, 2), "GBps": round(gbs, 1),
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
+        del dm, ds, ws
+    return out
+
+
+def sink_blocks(q, torch, dev, stream, seed: int = 1004):
+    """The sink-augmented attention block with int8-asymmetric projections:
+    x [R][512] -> U8A_G32 QKV GEMV -> RoPE(64), new key at index L, attention
+    over the sink (index 0), the L cached and the new key (8 heads, q/k 65
+    lanes folded to 64 + a sink logit, v 64) -> U8A_G32 O GEMV.  Three C-ABI
+    calls per block.  Algorithmic bytes: the weights (0.885 + 0.295 MB) and
+    the KV of the L + 1 attended keys."""
+    import synth
+    H, NH, D = 512, 8, 64
+    wqkv = synth.random_qmat(synth.U8A_G32, synth.stream_id(seed, "wqkv"), 3 * H, H)
+    wo = synth.random_qmat(synth.U8A_G32, synth.stream_id(seed, "wo"), H, H)
+    dq, do = q.DeviceQMat(wqkv), q.DeviceQMat(wo)
+    sink = torch.from_numpy(synth.normal_f64(synth.stream_id(seed, "sink"), (NH,)).astype(np.float16)
+                            .astype(np.float32)).to(dev)
+    wbytes = (3 * H * H + H * H) * 36 / 32
+    out = []
+    for L in (350, 3000):
+        for R in (1, 6, 12, 24):
+            cap = L + 1
+            x = torch.from_numpy(synth.normal_f16(synth.stream_id(seed, "x", R), (R, H)).view(np.int16)).to(dev)
+            kc = torch.from_numpy(synth.normal_f16(synth.stream_id(seed, "kc", L), (R, NH, cap, D)).view(np.int16)).to(dev)
+            vc = torch.from_numpy(synth.normal_f16(synth.stream_id(seed, "vc", L), (R, NH, cap, D)).view(np.int16)).to(dev)
+            kc[:, :, 0] = 0
+            vc[:, :, 0] = 0
+            qkv = torch.zeros((R, 3 * H), dtype=torch.float32, device=dev)
+            o = torch.zeros((R, H), dtype=torch.int16, device=dev)
+            y = torch.zeros((R, H), dtype=torch.int16, device=dev)
+            pl = torch.full((R,), L, dtype=torch.int32, device=dev)
+            a = q.AttnArgs(R, NH, D, qkv.data_ptr(), 3 * H, kc.data_ptr(), vc.data_ptr(), cap, 0, pl.data_ptr(), None,
+                           sink.data_ptr(), 10000.0, 1.0 / 8.0, o.data_ptr(), H, None, None)
+            wsb = q.ocrdec_attn_workspace_bytes(a)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+            def block(s):
+                q.ocrdec_gemv_q(dq.desc, R, x, H, qkv, q.OCRDEC_OUT_F32, 3 * H, stream=s)
+                q.ocrdec_attn_decode(a, ws, wsb, stream=s)
+                q.ocrdec_gemv_q(do.desc, R, o, H, y, q.OCRDEC_OUT_F16, H, stream=s)
+            us = _graph_time_us(torch, stream, block)
+            byt = wbytes + R * NH * (L + 1) * D * 2 * 2.0
+            gbs = byt / (us * 1e-6) / 1e9
+            out.append({"rows": R, "cached": L, "us_per_block": round(us, 2),
+                        "rows_blocks_per_s": round(R * 1e6 / us, 1), "algorithmic_MB": round(byt / 1e6, 3),
+                        "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)})
+            del kc, vc, ws
+    return {"workload": "sink-augmented attention block: hidden 512, 8 heads (q/k 64 lanes + sink logit, v 64), "
+                        "U8A_G32 QKV and O projections, fp16 KV cache with the sink at index 0",
+            "runs": out}
 
 
 PREFILL_SEED = 1005

@@ -60,6 +60,54 @@ const char* ocrdec_last_error(void);
 const char* ocrdec_version(void);
 
 /* ------------------------------------------------------------------------ */
+/* Kernel timing                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Profiling of the kernels the library enqueues (Unlimited-OCR page, "Dall'ABI
+ * C all'API Python": the C interface reports memory and profiling).  While a
+ * profile is set on the calling thread, every kernel a call of this thread
+ * enqueues is preceded by a HIP event recorded on the call's stream, and the
+ * kind of that kernel is noted; ocrdec_profile_mark adds a final event.  The
+ * time between events i and i+1 (hipEventElapsedTime) is then kernel i's
+ * duration plus the gap before it.  Recording also works under stream
+ * capture (the events become graph nodes).  When `capacity` events have been
+ * recorded, later ones are dropped and `count` stays at capacity. */
+typedef enum {
+    OCRDEC_K_EMBED = 0,       /* embedding lookup + first norm */
+    OCRDEC_K_QKV = 1,         /* QKV projection (norm staged in it up to 16 rows) */
+    OCRDEC_K_ATTN = 2,        /* attention partials over 64-key splits (RoPE, cache write) */
+    OCRDEC_K_ATTN_MERGE = 3,  /* merge of the splits */
+    OCRDEC_K_ATTN_MERGE_O = 4,/* merge of the splits + O projection into the residual */
+    OCRDEC_K_O_PROJ = 5,      /* O projection into the residual */
+    OCRDEC_K_NORM = 6,        /* RMSNorm of the residual */
+    OCRDEC_K_ROUTE = 7,       /* router, top-k, grouping */
+    OCRDEC_K_EXPERT_GLU = 8,  /* grouped expert gate/up + SwiGLU */
+    OCRDEC_K_EXPERT_DOWN = 9, /* grouped expert down projection */
+    OCRDEC_K_COMBINE = 10,    /* weighted recombine */
+    OCRDEC_K_DENSE_GLU = 11,  /* dense gate/up + SwiGLU */
+    OCRDEC_K_DENSE_DOWN = 12, /* dense down projection into the residual */
+    OCRDEC_K_LM_HEAD = 13,    /* language head with fused argmax (partials) */
+    OCRDEC_K_ARGMAX = 14,     /* merge of the argmax partials */
+    OCRDEC_K_OTHER = 15       /* anything else (copies, generation index, prompt pass) */
+} ocrdec_kernel;
+
+typedef struct {
+    void** events;     /* host array [capacity] of hipEvent_t, created by the caller with timing enabled */
+    int32_t* kernels;  /* host array [capacity]: kernels[i] is the ocrdec_kernel enqueued after events[i]
+                          (-1 after the final mark) */
+    int32_t capacity;
+    int32_t count;     /* events recorded so far (the library advances it) */
+} ocrdec_profile;
+
+/* Sets the calling thread's profile (NULL: stop recording).  The struct and
+ * its arrays must stay valid while set.  Errors: INVALID_ARG for a non-NULL
+ * profile with NULL arrays or a negative capacity or count. */
+ocrdec_status ocrdec_profile_set(ocrdec_profile* prof);
+/* Records the final event of the profile on `stream` (no-op without one).
+ * Errors: DEVICE if the event cannot be recorded. */
+ocrdec_status ocrdec_profile_mark(void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Weight formats                                                            */
 /* ------------------------------------------------------------------------ */
 

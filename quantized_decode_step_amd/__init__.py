@@ -20,6 +20,9 @@ OCRDEC_OK, OCRDEC_ERR_INVALID_ARG, OCRDEC_ERR_UNSUPPORTED, OCRDEC_ERR_WORKSPACE,
 OCRDEC_F16, OCRDEC_Q8_0, OCRDEC_Q4_0, OCRDEC_U8A_G32 = range(4)
 OCRDEC_OUT_F32, OCRDEC_OUT_F16 = 0, 1
 OCRDEC_DEV_TOKEN_RANGE, OCRDEC_DEV_RESIDUAL, OCRDEC_DEV_LOGIT, OCRDEC_DEV_NO_TOKEN = 1, 2, 4, 8
+# ocrdec_kernel
+KERNEL_NAMES = ["embed", "qkv", "attn", "attn_merge", "attn_merge_o", "o_proj", "norm", "route", "expert_glu",
+                "expert_down", "combine", "dense_glu", "dense_down", "lm_head", "argmax", "other"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libocrdec.so is not built: run `python quantized_decode_step_amd/build.py` "
@@ -114,6 +117,13 @@ _lib.ocrdec_prefill_batch.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _vp, _
 _lib.ocrdec_round_workspace_bytes.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _P(_sz)]
 _lib.ocrdec_run_round.argtypes = [_P(ModelDesc), _P(StateDesc), _vp, _i32, _vp, _i32, _i32, _vp, _sz, _vp]
 _lib.ocrdec_decode_step_noalloc.argtypes = [_P(ModelDesc), _P(StateDesc), _vp, _vp, _vp, _vp, _P(StepCapture), _vp]
+class Profile(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(_vp)), ("kernels", ctypes.POINTER(_i32)), ("capacity", _i32),
+                ("count", _i32)]
+
+
+_lib.ocrdec_profile_set.argtypes = [ctypes.c_void_p]
+_lib.ocrdec_profile_mark.argtypes = [_vp]
 _lib.ocrdec_device_status.argtypes = [_vp, _sz, _vp, _P(ctypes.c_uint32)]
 _lib.ocrdec_prefill.argtypes = [_P(ModelDesc), _P(StateDesc), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _P(StepCapture),
                                 _vp, _sz, _vp]
@@ -122,7 +132,7 @@ for _fn in ("ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack", "ocrdec_gemv_
             "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes", "ocrdec_moe_layer", "ocrdec_step_workspace_bytes",
             "ocrdec_decode_step", "ocrdec_prefill_workspace_bytes", "ocrdec_prefill", "ocrdec_round_workspace_bytes",
             "ocrdec_run_round", "ocrdec_prefill_batch_workspace_bytes", "ocrdec_prefill_batch", "ocrdec_device_status",
-            "ocrdec_decode_step_noalloc"):
+            "ocrdec_decode_step_noalloc", "ocrdec_profile_set", "ocrdec_profile_mark"):
     getattr(_lib, _fn).restype = ctypes.c_int
 
 EXPORTED = ["ocrdec_last_error", "ocrdec_version", "ocrdec_packed_bytes", "ocrdec_pack", "ocrdec_unpack",
@@ -130,7 +140,8 @@ EXPORTED = ["ocrdec_last_error", "ocrdec_version", "ocrdec_packed_bytes", "ocrde
             "ocrdec_attn_decode", "ocrdec_moe_workspace_bytes",
             "ocrdec_moe_layer", "ocrdec_step_workspace_bytes", "ocrdec_decode_step",
             "ocrdec_prefill_workspace_bytes", "ocrdec_prefill", "ocrdec_round_workspace_bytes", "ocrdec_run_round",
-            "ocrdec_prefill_batch_workspace_bytes", "ocrdec_prefill_batch", "ocrdec_device_status", "ocrdec_decode_step_noalloc"]
+            "ocrdec_prefill_batch_workspace_bytes", "ocrdec_prefill_batch", "ocrdec_device_status", "ocrdec_decode_step_noalloc",
+            "ocrdec_profile_set", "ocrdec_profile_mark"]
 
 
 def _ptr(t) -> int | None:
@@ -239,6 +250,14 @@ def ocrdec_decode_step_noalloc(m: ModelDesc, st: StateDesc, tok_in=None, hidden=
     _check(_lib.ocrdec_decode_step_noalloc(ctypes.byref(m), ctypes.byref(st), _ptr(tok_in), _ptr(hidden),
                                            _ptr(tok_out), _ptr(forced_topk),
                                            ctypes.byref(capture) if capture is not None else None, _stream(stream)))
+
+
+def ocrdec_profile_set(prof: "Profile | None"):
+    _check(_lib.ocrdec_profile_set(ctypes.addressof(prof) if prof is not None else None))
+
+
+def ocrdec_profile_mark(stream=None):
+    _check(_lib.ocrdec_profile_mark(_stream(stream)))
 
 
 def ocrdec_device_status(ws, ws_bytes: int, stream=None) -> int:

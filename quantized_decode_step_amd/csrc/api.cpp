@@ -23,6 +23,16 @@ ocrdec_status launch_status(const char* what) {
     return OCRDEC_OK;
 }
 
+static thread_local ocrdec_profile* g_prof = nullptr;
+
+void prof_mark(hipStream_t s, int kernel) {
+    ocrdec_profile* p = g_prof;
+    if (!p || p->count >= p->capacity) return;
+    if (hipEventRecord((hipEvent_t)p->events[p->count], s) != hipSuccess) return;
+    p->kernels[p->count] = kernel;
+    p->count += 1;
+}
+
 ocrdec_status check_qmat(const ocrdec_qmat* w, const char* name) {
     if (!w) return fail(OCRDEC_ERR_INVALID_ARG, std::string(name) + ": NULL descriptor");
     PackGeom g;
@@ -107,6 +117,26 @@ ocrdec_status check_pack_args(int32_t fmt, int32_t n, int32_t k) {
 
 }  // namespace
 }  // namespace ocrdec
+
+extern "C" ocrdec_status ocrdec_profile_set(ocrdec_profile* prof) {
+    using namespace ocrdec;
+    if (prof) {
+        OCR_CHECK_ARG(prof->events && prof->kernels, "profile arrays must be non-NULL");
+        OCR_CHECK_ARG(prof->capacity >= 0 && prof->count >= 0, "capacity and count must be >= 0");
+    }
+    g_prof = prof;
+    return OCRDEC_OK;
+}
+
+extern "C" ocrdec_status ocrdec_profile_mark(void* stream) {
+    using namespace ocrdec;
+    ocrdec_profile* p = g_prof;
+    if (!p || p->count >= p->capacity) return OCRDEC_OK;
+    OCR_HIP(hipEventRecord((hipEvent_t)p->events[p->count], (hipStream_t)stream));
+    p->kernels[p->count] = -1;
+    p->count += 1;
+    return OCRDEC_OK;
+}
 
 using namespace ocrdec;
 

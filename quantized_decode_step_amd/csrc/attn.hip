@@ -490,8 +490,10 @@ void launch_attn_merge_o(const AttnParams& p0, int fmt, const uint8_t* wo, int n
     AttnParams p = p0;
     p.n_split = attn_n_split(p.cache_cap);
     dim3 g1(p.n_split, p.n_heads, p.rows);
+    prof_mark(s, OCRDEC_K_ATTN);
     if (p.k_scale) hipLaunchKernelGGL((attn_partial_kernel<128, true>), g1, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((attn_partial_kernel<128, false>), g1, dim3(256), 0, s, p);
+    prof_mark(s, OCRDEC_K_ATTN_MERGE_O);
     const int HD = p.n_heads * 128;
     const int64_t nch = n_chunks(fmt, HD);
     const size_t lds = (size_t)p.rows * (HD + 8) * 2;
@@ -870,8 +872,11 @@ void launch_attn_prefill(const PrefillAttnParams& p0, hipStream_t s) {
     const dim3 gr(p.P, p.n_heads), ga(p.n_qb * nch, p.n_heads, p.n_seq), gm(p.n_qb, p.n_heads, p.n_seq);
     const bool kv8 = p.k_scale != nullptr;
 #define OCR_PF(D_, K_)                                                                                   \
+    prof_mark(s, OCRDEC_K_OTHER);                                                                         \
     hipLaunchKernelGGL((prefill_rope_kernel<D_, K_>), gr, dim3(64), 0, s, p);                             \
+    prof_mark(s, OCRDEC_K_OTHER);                                                                         \
     hipLaunchKernelGGL((attn_prefill_kernel<D_, K_>), ga, dim3(256), 0, s, p);                            \
+    if (nch > 1) prof_mark(s, OCRDEC_K_OTHER);                                                            \
     if (nch > 1) hipLaunchKernelGGL(attn_prefill_merge_kernel<D_>, gm, dim3(256), 0, s, p, nch);
     if (p.head_dim == 128) {
         if (kv8) { OCR_PF(128, true) } else { OCR_PF(128, false) }
@@ -886,12 +891,16 @@ void launch_attn(const AttnParams& p, hipStream_t s) {
     dim3 g2(p.n_heads, p.rows);
     const bool kv8 = p.k_scale != nullptr;
     if (p.head_dim == 128) {
+        prof_mark(s, OCRDEC_K_ATTN);
         if (kv8) hipLaunchKernelGGL((attn_partial_kernel<128, true>), g1, dim3(256), 0, s, p);
         else hipLaunchKernelGGL((attn_partial_kernel<128, false>), g1, dim3(256), 0, s, p);
+        prof_mark(s, OCRDEC_K_ATTN_MERGE);
         hipLaunchKernelGGL(attn_combine_kernel<128>, g2, dim3(128), 0, s, p);
     } else {
+        prof_mark(s, OCRDEC_K_ATTN);
         if (kv8) hipLaunchKernelGGL((attn_partial_kernel<64, true>), g1, dim3(256), 0, s, p);
         else hipLaunchKernelGGL((attn_partial_kernel<64, false>), g1, dim3(256), 0, s, p);
+        prof_mark(s, OCRDEC_K_ATTN_MERGE);
         hipLaunchKernelGGL(attn_combine_kernel<64>, g2, dim3(64), 0, s, p);
     }
 }

@@ -35,6 +35,10 @@ ocrdec_status ok();
 // Checks the launch that was just enqueued.
 ocrdec_status launch_status(const char* what);
 
+// Records a profiling event before a kernel of kind `kernel` (ocrdec_kernel)
+// if the calling thread has a profile set (ocrdec_profile_set).
+void prof_mark(hipStream_t s, int kernel);
+
 // ---------------------------------------------------------------------------
 // Packed weight layout
 //

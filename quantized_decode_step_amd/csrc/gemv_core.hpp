@@ -287,40 +287,99 @@ OCR_DEV void stage_x(const XS& xs, int tok0, int ntok, int k, uint16_t* xl, int 
     }
 }
 
+// x = fp16(RMSNorm(h[r]) * gamma) for rows r0 .. r0+R-1 of the decode step's
+// fixed-point residual (row stride H), formed by all waves of the workgroup
+// into LDS (row r at xl + (r - r0) * ldl) and, if x_out is non-NULL, into
+// x_out + r * ldx.  A wave holds at most MAXG four-value groups of a row per
+// lane (8 * MAXG registers of raw residual), every load of them issued before
+// the first use.  With few rows a row is cut into G slices, one per wave (up
+// to four), whose partial sums of squares meet in LDS and are added in slice
+// order (the result does not depend on timing); a wave with one slice keeps
+// its values in registers, otherwise it reads its slices again (from cache)
+// to scale them.  With G = 1 every wave normalises whole rows on its own.
+// Every thread of the workgroup must call it (it may hold a barrier).
+template <int MAXG>
+OCR_DEV void block_rmsnorm_fix(const fix_t* h, const uint16_t* gamma, int H, float eps, int r0, int R,
+                               uint16_t* x_out, int64_t ldx, uint16_t* xl, int ldl) {
+    __shared__ float ss_lds[256];
+    const int nw = (int)blockDim.x >> 6, wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+    const int n4 = H / 4;
+    const int gmin = (n4 + 64 * MAXG - 1) / (64 * MAXG);
+    const int G = max(gmin, min(4, nw / max(R, 1)));
+    const int per = (n4 + G - 1) / G;
+    const int np = R * G;
+    const bool keep = np <= nw;
+    float4 v[MAXG];
+    uint2 g[MAXG];
+    auto load = [&](int pr) {
+        const int r = pr / G, s = pr % G;
+        const int g0 = s * per, g1 = min(g0 + per, n4);
+        const fix_t* hr = h + (int64_t)(r0 + r) * H;
+        longlong2 a[MAXG], b[MAXG];
+#pragma unroll
+        for (int i = 0; i < MAXG; ++i) {
+            const int c = min(g0 + lane + 64 * i, g1 - 1);
+            a[i] = ((const longlong2*)hr)[2 * c];
+            b[i] = ((const longlong2*)hr)[2 * c + 1];
+            g[i] = ((const uint2*)gamma)[c];
+        }
+#pragma unroll
+        for (int i = 0; i < MAXG; ++i)
+            v[i] = g0 + lane + 64 * i < g1
+                       ? make_float4(fix_to(a[i].x), fix_to(a[i].y), fix_to(b[i].x), fix_to(b[i].y))
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    auto sumsq = [&]() {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < MAXG; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+        return wave_sum(ss);
+    };
+    auto scale = [&](int pr, float tot) {
+        const int r = pr / G, s = pr % G;
+        const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+        const int g0 = s * per, g1 = min(g0 + per, n4);
+#pragma unroll
+        for (int i = 0; i < MAXG; ++i) {
+            const int c4 = g0 + lane + 64 * i;
+            if (c4 < g1) {
+                const uint32_t lo = (uint32_t)f2h(v[i].x * inv * h2f((uint16_t)(g[i].x & 0xFFFF))) |
+                                    ((uint32_t)f2h(v[i].y * inv * h2f((uint16_t)(g[i].x >> 16))) << 16);
+                const uint32_t hi = (uint32_t)f2h(v[i].z * inv * h2f((uint16_t)(g[i].y & 0xFFFF))) |
+                                    ((uint32_t)f2h(v[i].w * inv * h2f((uint16_t)(g[i].y >> 16))) << 16);
+                ((uint2*)(xl + r * ldl))[c4] = make_uint2(lo, hi);
+                if (x_out) ((uint2*)(x_out + (int64_t)(r0 + r) * ldx))[c4] = make_uint2(lo, hi);
+            }
+        }
+    };
+    if (G == 1) {  // whole rows per wave: no exchange
+        for (int pr = wave; pr < np; pr += nw) {
+            load(pr);
+            scale(pr, sumsq());
+        }
+        return;
+    }
+    for (int pr = wave; pr < np; pr += nw) {
+        load(pr);
+        const float ss = sumsq();
+        if (lane == 0) ss_lds[pr] = ss;
+    }
+    __syncthreads();
+    for (int pr = wave; pr < np; pr += nw) {
+        if (!keep) load(pr);
+        const int r = pr / G;
+        float tot = 0.f;
+        for (int j = 0; j < G; ++j) tot += ss_lds[r * G + j];
+        scale(pr, tot);
+    }
+}
+
 // x = fp16(RMSNorm(h[tok]) * gamma) for tokens tok0 .. tok0+15 of rows into
-// LDS (row stride ldl), one wavefront per token, from the decode step's
-// fixed-point residual; tokens past the row count are not written (their
-// fragments read as zero).  Rows of up to 1280 values are held in registers
-// (one memory round trip); longer rows take a second pass over the row (from
-// cache), so that the staging adds few registers to the kernel around it.
+// LDS (row stride ldl); tokens past the row count are not written (their
+// fragments read as zero).  All threads of the workgroup call it.
 OCR_DEV void stage_norm(const fix_t* h, const uint16_t* gamma, float eps, int rows, int tok0, int H, uint16_t* xl,
                         int ldl) {
-    const int nw = (int)blockDim.x >> 6, wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
-    const int nt = min(16, rows - tok0);
-    for (int t = wave; t < nt; t += nw) {
-        const fix_t* hr = h + (int64_t)(tok0 + t) * H;
-        if (H <= 1280) {
-            wave_rmsnorm_row<5>(hr, gamma, H, eps, nullptr, xl + t * ldl);
-            continue;
-        }
-        const int n4 = H / 4;
-        float ss = 0.f;
-        for (int c4 = lane; c4 < n4; c4 += 64) {
-            const float4 v = ld_resid4(hr, c4);
-            ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-        }
-        ss = wave_sum(ss);
-        const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-        for (int c4 = lane; c4 < n4; c4 += 64) {
-            const float4 v = ld_resid4(hr, c4);
-            const uint2 g = ((const uint2*)gamma)[c4];
-            const uint32_t lo = (uint32_t)f2h(v.x * inv * h2f((uint16_t)(g.x & 0xFFFF))) |
-                                ((uint32_t)f2h(v.y * inv * h2f((uint16_t)(g.x >> 16))) << 16);
-            const uint32_t hi = (uint32_t)f2h(v.z * inv * h2f((uint16_t)(g.y & 0xFFFF))) |
-                                ((uint32_t)f2h(v.w * inv * h2f((uint16_t)(g.y >> 16))) << 16);
-            ((uint2*)(xl + t * ldl))[c4] = make_uint2(lo, hi);
-        }
-    }
+    block_rmsnorm_fix<5>(h, gamma, H, eps, tok0, min(16, rows - tok0), nullptr, 0, xl, ldl);
 }
 
 template <int FMT, int XT>

@@ -772,9 +772,8 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
         if (staged) return;
         staged = 1;
         if (norm_w) {
-            for (int r = wave; r < R; r += 16)
-                wave_rmsnorm_row<NV>(h_in + (int64_t)r * H, norm_w, H, eps, x_out + (int64_t)r * ldx,
-                                     xl_dyn + r * ldl);
+            // three groups per lane: the 16-wave workgroup has 128 registers per lane
+            block_rmsnorm_fix<3>(h_in, norm_w, H, eps, 0, R, x_out, ldx, xl_dyn, ldl);
         } else {
             stage_x(XDirect{x, ldx, R}, 0, R, H, xl_dyn, ldl);
         }
@@ -1239,9 +1238,11 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     if (fused) p.sw = m.sw;
     if (norm_in && !small) {
         // the MoE input is the normalised residual: form it first
+        prof_mark(s, OCRDEC_K_NORM);
         hipLaunchKernelGGL(moe_norm_kernel, dim3(rows), dim3(256), 0, s, h_norm, norm_in, H, eps_in, (uint16_t*)x,
                            ldx);
     }
+    prof_mark(s, OCRDEC_K_ROUTE);
     if (small) {
         // router GEMV, top-k and grouping in one workgroup
         const uint8_t* rw = (const uint8_t*)w->router.data;
@@ -1297,7 +1298,9 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.lslices = rp.kslices;
         p.lslice = rp.ly_slice;
         launch_expert_gemm(w->router.fmt, false, rp, (rows + EG_TM - 1) / EG_TM, s);
+        prof_mark(s, OCRDEC_K_ROUTE);
         hipLaunchKernelGGL(topk_kernel, dim3((rows + 15) / 16), dim3(1024), 0, s, p);
+        prof_mark(s, OCRDEC_K_ROUTE);
         hipLaunchKernelGGL(group_large_kernel, dim3(1), dim3(1024), 0, s, p, EG_TM);
     } else {
         GemvPlan pl = plan_gemv(w->router.fmt, E, H, rows, EPI_F32);
@@ -1310,6 +1313,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         gp.y = m.logits;
         gp.ldy = E;
         launch_gemv(w->router.fmt, EPI_F32, pl, gp, s);
+        prof_mark(s, OCRDEC_K_ROUTE);
         hipLaunchKernelGGL(route_group_kernel, dim3(1), dim3(1024), 0, s, p);
     }
     const int max_virt = moe_max_virt(rows, w);
@@ -1334,6 +1338,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.y = m.a;
         p.ldy = F;
         p.out_tiles = F / 16;
+        prof_mark(s, OCRDEC_K_EXPERT_GLU);
         if (gemm) launch_expert_gemm(w->gate_up.fmt, true, p, max_virt, s);
         else launch_grouped(w->gate_up.fmt, true, p, rows, s);
     }
@@ -1364,11 +1369,13 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
             p.ldh = ldh;
             p.status = status;
         }
+        prof_mark(s, OCRDEC_K_EXPERT_DOWN);
         if (gemm) launch_expert_gemm(w->down.fmt, false, p, max_virt, s);
         else launch_grouped(w->down.fmt, false, p, rows, s);
     }
     // combine, or (down projection added into the residual) the next norm
     if (fused) {
+        if (norm_w) prof_mark(s, OCRDEC_K_NORM);
         if (norm_w)
             hipLaunchKernelGGL(moe_norm_kernel, dim3(rows), dim3(256), 0, s, (const fix_t*)h, norm_w, H, eps, x_out,
                                ldxo);
@@ -1391,6 +1398,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.eps = eps;
         p.x_out = x_out;
         p.ldx = ldxo;
+        prof_mark(s, OCRDEC_K_COMBINE);
         hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(rows <= 64 ? 1024 : 256), 0, s, p);
     }
 }

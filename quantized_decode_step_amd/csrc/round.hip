@@ -189,6 +189,7 @@ extern "C" ocrdec_status ocrdec_run_round(const ocrdec_model* m, const ocrdec_st
                                          kind == 0 ? nullptr : W.pemb, nullptr, W.first, nullptr, nullptr, inner,
                                          inner_bytes, stream);
                 if (s != OCRDEC_OK) return s;
+                prof_mark(hs, OCRDEC_K_OTHER);
                 hipLaunchKernelGGL(admit_rows_kernel, dim3(1), dim3(64), 0, hs, (int32_t*)st->prefix_len,
                                    st->gen_index, tok, W.first, a);
             }

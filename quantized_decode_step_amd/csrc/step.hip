@@ -462,6 +462,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     hipStream_t s = (hipStream_t)stream;
     StepWs w = carve_step(ws, m, R, cache_cap);
 
+    prof_mark(s, OCRDEC_K_EMBED);
     if (tok_in && !m->embed) {
         const uint8_t* tq = (const uint8_t*)m->embed_q.data;
         const int64_t nch = n_chunks(m->embed_q.fmt, H);
@@ -531,6 +532,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                 gp.gamma = L.attn_norm;
                 gp.eps = m->norm_eps;
             }
+            prof_mark(s, OCRDEC_K_QKV);
             launch_gemv(L.wqkv.fmt, EPI_F32, pl, gp, s);
         }
         // attention, and the O projection + residual (up to 16 rows: the
@@ -554,6 +556,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             gp.y = w.h;
             gp.ldy = H;
             gp.status = w.status;
+            prof_mark(s, OCRDEC_K_O_PROJ);
             launch_gemv(L.wo.fmt, EPI_RESID, pl, gp, s);
         }
         if (L.is_moe) {
@@ -567,7 +570,10 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                        w.status);
             ++moe_l;
         } else {
-            if (!prolog) launch_norm(w.h, L.ffn_norm, H, m->norm_eps, w.x, R, s);
+            if (!prolog) {
+                prof_mark(s, OCRDEC_K_NORM);
+                launch_norm(w.h, L.ffn_norm, H, m->norm_eps, w.x, R, s);
+            }
             const int F = L.dense_ff;
             {
                 GemvPlan pl = plan_gemv(L.dense_gate_up.fmt, 2 * F, H, R, EPI_GLU);
@@ -585,6 +591,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                     gp.gamma = L.ffn_norm;
                     gp.eps = m->norm_eps;
                 }
+                prof_mark(s, OCRDEC_K_DENSE_GLU);
                 launch_gemv(L.dense_gate_up.fmt, EPI_GLU, pl, gp, s);
             }
             {
@@ -598,14 +605,18 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                 gp.y = w.h;
                 gp.ldy = H;
                 gp.status = w.status;
+                prof_mark(s, OCRDEC_K_DENSE_DOWN);
                 launch_gemv(L.dense_down.fmt, EPI_RESID, pl, gp, s);
             }
-            if (next_norm && !prolog)
+            if (next_norm && !prolog) {
+                prof_mark(s, OCRDEC_K_NORM);
                 launch_norm(w.h, next_norm, H, m->norm_eps, w.x, R, s);
+            }
         }
     }
     if (hidden) {
         const int64_t n = (int64_t)R * H;
+        prof_mark(s, OCRDEC_K_OTHER);
         hipLaunchKernelGGL(fix_rows_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 1024)), dim3(256), 0, s,
                            w.h, hidden, n);
     }
@@ -623,9 +634,12 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             gp.gamma = m->final_norm;
             gp.eps = m->norm_eps;
         }
+        prof_mark(s, OCRDEC_K_LM_HEAD);
         launch_lm_argmax(m->lm_head.fmt, lp, gp, s);
+        prof_mark(s, OCRDEC_K_ARGMAX);
         launch_argmax_final(w.lm_part, lp.grid, R, tok_out, cap ? cap->lm_top2 : nullptr, st->gen_index, w.status, s);
     } else {
+        prof_mark(s, OCRDEC_K_OTHER);
         hipLaunchKernelGGL(bump_kernel, dim3(1), dim3(64), 0, s, st->gen_index, R);
     }
     return launch_status("ocrdec_decode_step");
@@ -689,6 +703,7 @@ extern "C" ocrdec_status ocrdec_prefill_batch(const ocrdec_model* m, const ocrde
                                               std::to_string(ws ? ws_bytes : 0));
     hipStream_t s = (hipStream_t)stream;
     PrefillWs w = carve_prefill(ws, m, T, n, max_len);
+    prof_mark(s, OCRDEC_K_EMBED);
     // h = the input rows, x = fp16(RMSNorm(h) * attn_norm of layer 0)
     if (tok && !m->embed) {
         const uint8_t* tq = (const uint8_t*)m->embed_q.data;
@@ -736,13 +751,16 @@ extern "C" ocrdec_status ocrdec_prefill_batch(const ocrdec_model* m, const ocrde
         const ocrdec_layer& L = m->layers[l];
         const uint16_t* next_norm = (l + 1 < m->n_layers) ? m->layers[l + 1].attn_norm : m->final_norm;
         if (!next_norm) next_norm = L.attn_norm;  // no LM head: the last norm is not used
+        prof_mark(s, OCRDEC_K_QKV);
         prefill_gemm(L.wqkv, false, T, w.x, H, w.qkv, 3 * HD, s);
         ap.k_cache = L.k_cache;
         ap.v_cache = L.v_cache;
         ap.k_scale = L.k_scale;
         ap.v_scale = L.v_scale;
         launch_attn_prefill(ap, s);
+        prof_mark(s, OCRDEC_K_O_PROJ);
         prefill_gemm(L.wo, false, T, w.o, HD, w.y, H, s);
+        prof_mark(s, OCRDEC_K_NORM);
         hipLaunchKernelGGL(resid_norm_kernel, dim3(T), dim3(64), 0, s, w.h, w.y, L.ffn_norm, H, m->norm_eps, w.x);
         if (L.is_moe) {
             const int K = L.moe.top_k;
@@ -755,18 +773,23 @@ extern "C" ocrdec_status ocrdec_prefill_batch(const ocrdec_model* m, const ocrde
             ++moe_l;
         } else {
             const int F = L.dense_ff;
+            prof_mark(s, OCRDEC_K_DENSE_GLU);
             prefill_gemm(L.dense_gate_up, true, T, w.x, H, w.a, F, s);
+            prof_mark(s, OCRDEC_K_DENSE_DOWN);
             prefill_gemm(L.dense_down, false, T, w.a, F, w.y, H, s);
+            prof_mark(s, OCRDEC_K_NORM);
             hipLaunchKernelGGL(resid_norm_kernel, dim3(T), dim3(64), 0, s, w.h, w.y, next_norm, H, m->norm_eps, w.x);
         }
     }
     if (hidden) {
         const int64_t cnt = (int64_t)T * H;
+        prof_mark(s, OCRDEC_K_OTHER);
         hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)std::min<int64_t>((cnt + 255) / 256, 1024)), dim3(256), 0,
                            s, w.h, hidden, cnt);
     }
     if (m->lm_head.data && tok_out) {
         // the last position of every sequence, normalised with final_norm by the last layer
+        prof_mark(s, OCRDEC_K_OTHER);
         hipLaunchKernelGGL(gather_rows_kernel, dim3(n), dim3(64), 0, s, w.x, w.x_last, H, last);
         const LmPlan lp = plan_lm(m->lm_head.fmt, m->vocab, H, n);
         GemvParams gp{};
@@ -776,7 +799,9 @@ extern "C" ocrdec_status ocrdec_prefill_batch(const ocrdec_model* m, const ocrde
         gp.nchunks = n_chunks(m->lm_head.fmt, H);
         gp.xs = XDirect{w.x_last, H, n};
         gp.part = w.lm_part;
+        prof_mark(s, OCRDEC_K_LM_HEAD);
         launch_lm_argmax(m->lm_head.fmt, lp, gp, s);
+        prof_mark(s, OCRDEC_K_ARGMAX);
         launch_argmax_final(w.lm_part, lp.grid, n, tok_out, cap ? cap->lm_top2 : nullptr, nullptr, nullptr, s);
     }
     return launch_status("ocrdec_prefill_batch");
