@@ -264,24 +264,32 @@ OCR_DEV void kloop(const uint8_t* const (&tile)[NT], int c0, int c1, const XS& x
 
 OCR_DEV int xlds_stride(int k) { return k + 8; }
 
-template <class XS>
+// Copies the activations of tokens tok0 .. tok0+ntok-1 (those that exist)
+// into LDS.  The 16-byte pieces of all rows are spread over the workgroup's
+// threads, and each thread issues up to B loads before it stores any: the
+// copy takes one memory round trip per B pieces per thread instead of one
+// per token row (for gathered rows, the row list is read first, in the same
+// pass).  Fragments of the tokens not copied read as zero.
+template <int B = 8, class XS>
 OCR_DEV void stage_x(const XS& xs, int tok0, int ntok, int k, uint16_t* xl, int ldl) {
-    // only the tokens that exist are copied; fragments of the others read as zero
     const int nt = min(ntok, max(xs.rows - tok0, 0));
     const int n16 = k >> 3;  // 16-byte pieces per row
-    for (int t = 0; t < nt; ++t) {
-        const uint16_t* p = xs.row(tok0 + t);
-        for (int c0 = 0; c0 < n16; c0 += 4 * (int)blockDim.x) {
-            uint4 v[4];
+    const int total = nt * n16;
+    const int nth = (int)blockDim.x, tid = (int)threadIdx.x;
+    for (int b0 = 0; b0 < total; b0 += B * nth) {
+        uint4 v[B];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = c0 + u * (int)blockDim.x + (int)threadIdx.x;
-                v[u] = c < n16 ? *(const uint4*)(p + c * 8) : make_uint4(0, 0, 0, 0);
-            }
+        for (int j = 0; j < B; ++j) {
+            const int i = min(b0 + j * nth + tid, max(total - 1, 0));
+            const int t = i / n16, c = i - t * n16;
+            v[j] = total > 0 ? *(const uint4*)(xs.rowc(tok0 + t) + c * 8) : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = c0 + u * (int)blockDim.x + (int)threadIdx.x;
-                if (c < n16) *(uint4*)(xl + t * ldl + c * 8) = v[u];
+        for (int j = 0; j < B; ++j) {
+            const int i = b0 + j * nth + tid;
+            if (i < total) {
+                const int t = i / n16, c = i - t * n16;
+                *(uint4*)(xl + t * ldl + c * 8) = v[j];
             }
         }
     }

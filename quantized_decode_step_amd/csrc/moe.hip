@@ -775,7 +775,7 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
             // three groups per lane: the 16-wave workgroup has 128 registers per lane
             block_rmsnorm_fix<3>(h_in, norm_w, H, eps, 0, R, x_out, ldx, xl_dyn, ldl);
         } else {
-            stage_x(XDirect{x, ldx, R}, 0, R, H, xl_dyn, ldl);
+            stage_x<4>(XDirect{x, ldx, R}, 0, R, H, xl_dyn, ldl);
         }
     };
     // XT = 2: 17-32 rows in one pass over the router weights
@@ -872,7 +872,7 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
 #pragma unroll
                 for (int vv = 0; vv < 4; ++vv) {
                     const int s_ = off + min(16 * xt + 4 * (lane >> 4) + vv, max(cnt - 1, 0));
-                    hrow[xt][vv] = p.vrows[s_];
+                    hrow[xt][vv] = p.one_row ? 0 : p.vrows[s_];
                     swt[xt][vv] = p.sw[s_];
                 }
         }
@@ -897,12 +897,18 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
             auto stage = [&]() {
                 if constexpr (GLU)
                     stage_x(XGather{p.x, p.ldx, p.vrows + off, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
-                else stage_x(XDirect{p.x + (int64_t)off * p.ldx, p.ldx, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
+                else stage_x<4>(XDirect{p.x + (int64_t)off * p.ldx, p.ldx, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
             };
             kloop_lds<FMT, NT, XT>(tile, c0, cc1, stage, xl_dyn, ldl, cnt - tok0, nblk, lane, acc);
         } else if constexpr (GLU) {
-            XGather xs{p.x, p.ldx, p.vrows + off, cnt};
-            kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
+            if (p.one_row) {
+                // every slot reads row 0: no row-list load before the activations
+                XDirect xs{p.x, p.ldx, 1};
+                kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
+            } else {
+                XGather xs{p.x, p.ldx, p.vrows + off, cnt};
+                kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
+            }
         } else {
             XDirect xs{p.x + (int64_t)off * p.ldx, p.ldx, cnt};
             kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
@@ -937,6 +943,106 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
         if constexpr (HADD) report_status(p.status, bad, kStatResidual);
         __syncthreads();
     }
+}
+
+// Streamed grouped expert GEMV for decode batches (work entries of at most
+// 16 tokens, activations staged in LDS).  A workgroup of four waves owns
+// 4 * IPW consecutive work items of one entry (GLU: gate/up tile pairs; down:
+// output tiles), so the waves share one staging of the entry's token rows.
+// Each wave streams its IPW items as one sequence of (item, chunk) through a
+// register ring of PF chunks that runs on from one item into the next, so the
+// weight stream does not drain between items and a workgroup's start-up
+// (work-list read, staging) is paid once for IPW items.  Epilogues as in
+// grouped_kernel (SwiGLU into a; down: y, or weight x output added into the
+// fixed-point residual).
+template <int FMT, bool GLU, bool HADD, int IPW, int PF>
+__global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p) {
+    constexpr int CB = Geom<FMT>::CB, SB = Geom<FMT>::SB;
+    constexpr int NT = GLU ? 2 : 1;
+    extern __shared__ __align__(16) uint16_t xl_dyn[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wpe = p.groups_per_expert / (4 * IPW);  // workgroups per entry
+    const int v = blockIdx.x / wpe;
+    const int g0 = (blockIdx.x % wpe) * 4 * IPW + wave * IPW;
+    const int vc = min(v, p.max_virt - 1);
+    const int n_virt = p.n_virt[0];
+    const int4 ent = p.virt[vc];
+    if (!(v < n_virt && v < p.max_virt)) return;  // uniform over the workgroup
+    const int e = ent.x, off = ent.y, cnt = min(ent.z, 16);
+    const uint8_t* base = (e < p.n_experts) ? p.w_routed + (int64_t)e * p.expert_bytes
+                                            : p.w_shared + (int64_t)(e - p.n_experts) * p.expert_bytes;
+    const int nc = (int)p.nchunks;
+    const int total = IPW * nc;
+    const int nblk = p.k / 32;
+    auto tile_of = [&](int i, int t) { return (GLU && t == 1) ? g0 + i + p.half_tiles : g0 + i; };
+    auto chunk_ptr = [&](int q, int t) {
+        const int qc = min(q, total - 1);
+        return base + ((int64_t)tile_of(qc / nc, t) * nc + (qc % nc)) * CB;
+    };
+    WRegs wb[PF][NT];
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) load_wchunk<FMT>(chunk_ptr(u, t), lane, wb[u][t]);
+    // residual-adding down projection: rows and weights of this lane's slots
+    int hrow[4];
+    float swt[4];
+    if constexpr (HADD) {
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+            const int s_ = off + min(4 * (lane >> 4) + vv, max(cnt - 1, 0));
+            hrow[vv] = p.one_row ? 0 : p.vrows[s_];
+            swt[vv] = p.sw[s_];
+        }
+    }
+    const int ldl = xlds_stride(p.k);
+    if constexpr (GLU) stage_x(XGather{p.x, p.ldx, p.vrows + off, cnt}, 0, 16, p.k, xl_dyn, ldl);
+    else stage_x(XDirect{p.x + (int64_t)off * p.ldx, p.ldx, cnt}, 0, 16, p.k, xl_dyn, ldl);
+    __syncthreads();
+    float4v acc[NT][1];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t][0] = float4v{0.f, 0.f, 0.f, 0.f};
+    bool bad = false;
+    for (int q0 = 0; q0 < total; q0 += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int q = q0 + u;
+            if (q < total) {
+                const int c = q % nc;
+                half8v xa[SB][1];
+                float4v xs[SB][1];
+                lds_xfrags<FMT, 1>(xl_dyn, ldl, cnt, c, nblk, lane, xa);
+                xsums<FMT, 1>(xa, xs);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) chunk_mac<FMT, 1>(wb[u][t], xa, xs, acc[t]);
+                if (q + PF < total) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) load_wchunk<FMT>(chunk_ptr(q + PF, t), lane, wb[u][t]);
+                }
+                if (c == nc - 1) {  // item q / nc complete
+                    const int i = q / nc;
+#pragma unroll
+                    for (int vv = 0; vv < 4; ++vv) {
+                        const int tok = 4 * (lane >> 4) + vv;
+                        if (tok >= cnt) continue;
+                        const int64_t slot = off + tok;
+                        if constexpr (GLU) {
+                            const int col = tile_of(i, 0) * 16 + (lane & 15);
+                            ((uint16_t*)p.y)[slot * p.ldy + col] = f2h(silu(acc[0][0][vv]) * acc[1][0][vv]);
+                        } else {
+                            const int row = tile_of(i, 0) * 16 + (lane & 15);
+                            if constexpr (HADD)
+                                fix_atomic_add(p.h + (int64_t)hrow[vv] * p.ldh + row, swt[vv] * acc[0][0][vv], bad);
+                            else ((float*)p.y)[slot * p.ldy + row] = acc[0][0][vv];
+                        }
+                    }
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) acc[t][0] = float4v{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+    }
+    if constexpr (HADD) report_status(p.status, bad, kStatResidual);
 }
 
 // x = fp16(RMSNorm(h) * gamma) of one fixed-point residual row per workgroup.
@@ -1125,9 +1231,35 @@ void launch_grouped_fmt(const GroupedParams& p, int xt, int ks, bool lds, int gr
 #undef OCR_G
 }
 
+// Streamed form (grouped_stream_kernel): two items per wave, entries of at
+// most 16 tokens staged in LDS.
+constexpr int STREAM_IPW = 2;
+template <int FMT, bool GLU>
+void launch_stream_t(const GroupedParams& p, hipStream_t s) {
+    constexpr int PF = GLU ? 6 : 7;
+    const int grid = p.max_virt * (p.groups_per_expert / (4 * STREAM_IPW));
+    const size_t lb = lds_x_bytes(p.k, 1);
+    if (!GLU && p.sw) hipLaunchKernelGGL((grouped_stream_kernel<FMT, GLU, true, STREAM_IPW, PF>), dim3(grid), dim3(256), lb, s, p);
+    else hipLaunchKernelGGL((grouped_stream_kernel<FMT, GLU, false, STREAM_IPW, PF>), dim3(grid), dim3(256), lb, s, p);
+}
+
 void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream_t s) {
     const int64_t items = (int64_t)p.max_virt * p.groups_per_expert;
     const int ks = items >= 2048 ? 1 : 4;
+    // gate/up of large decode batches: the streamed form (entries of at most 16
+    // tokens, staged in LDS).  It halves the workgroups, which pays only when
+    // they exceed the CUs' workgroup slots: measured at 24 rows (gate/up 31.9
+    // -> 28.0 us) but slower at 6 and 12 rows (17.5 -> 19.6 us at 6) and for
+    // the down projection at every row count.
+    if (glu && rows_hint >= 20 && p.entries16 && ks == 1 && p.groups_per_expert % (4 * STREAM_IPW) == 0 &&
+        lds_x_bytes(p.k, 1) <= 65536 && use_lds_x(p.k, 1, rows_hint)) {
+        switch (fmt) {
+        case OCRDEC_F16: launch_stream_t<OCRDEC_F16, true>(p, s); return;
+        case OCRDEC_Q8_0: launch_stream_t<OCRDEC_Q8_0, true>(p, s); return;
+        case OCRDEC_Q4_0: launch_stream_t<OCRDEC_Q4_0, true>(p, s); return;
+        case OCRDEC_U8A_G32: launch_stream_t<OCRDEC_U8A_G32, true>(p, s); return;
+        }
+    }
     // LDS staging needs every wave of a workgroup on the same expert; it uses
     // 16-token passes (routed experts usually get far fewer tokens than rows)
     const bool same_expert = (p.groups_per_expert % (4 / ks)) == 0;
@@ -1338,6 +1470,8 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.y = m.a;
         p.ldy = F;
         p.out_tiles = F / 16;
+        p.one_row = rows == 1;
+        p.entries16 = small;
         prof_mark(s, OCRDEC_K_EXPERT_GLU);
         if (gemm) launch_expert_gemm(w->gate_up.fmt, true, p, max_virt, s);
         else launch_grouped(w->gate_up.fmt, true, p, rows, s);
@@ -1363,6 +1497,8 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.y = m.y;
         p.ldy = H;
         p.out_tiles = H / 16;
+        p.one_row = rows == 1;
+        p.entries16 = small;
         if (fused) {
             p.sw = m.sw;
             p.h = (fix_t*)h;

@@ -69,6 +69,8 @@ struct GroupedParams {
     int64_t ldh;
     const float* sw;
     uint32_t* status;
+    int one_row;       // one token row in all (decode of one row): every slot's row is 0
+    int entries16;     // every work entry holds at most 16 tokens (decode-sized grouping)
 };
 
 struct CombineParams {
