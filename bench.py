@@ -29,35 +29,39 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 SEED = 1003
 ROOT = os.path.dirname(os.path.abspath(__file__))
-# Counter-measured HBM traffic of the LM-head kernel (rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE runs of `bench.py --mode lm`, calibrated on a copy of known size).  It
-# applies only while the kernel sources hash to the value recorded with it.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_argmax_traffic.md")
-KERNEL_SOURCES = ["common.hpp", "gemv_core.hpp", "gemv.hpp", "gemv.hip"]
+# Counter-measured HBM traffic per launch of each kernel kind of the decode
+# step (rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs, calibrated on a copy
+# of known size), at 1 and 24 rows.  It applies only while the kernel sources
+# hash to the value recorded with it.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_traffic.md")
+CSRC = os.path.join(ROOT, "quantized_decode_step_amd", "csrc")
 
 
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "quantized_decode_step_amd", "csrc", f), "rb") as fh:
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """(bytes per launch, note) from the counter summary if it matches the
-    current kernel sources, else (None, reason)."""
+def recorded_traffic(rows: int):
+    """({kind: bytes per launch}, note) from the counter summary if it was
+    taken at this row count and matches the current kernel sources."""
     if not os.path.exists(TRAFFIC_FILE):
         return None, "no counter summary"
     vals = {}
     for line in open(TRAFFIC_FILE):
-        if ":" in line and line.strip().startswith(("source-hash", "traffic-bytes-per-launch")):
+        if ":" in line and line.strip().startswith(("source-hash", "traffic-r")):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
     if vals.get("source-hash") != kernel_source_hash():
-        return None, "kernel changed since the counters were taken"
-    return float(vals["traffic-bytes-per-launch"]), "rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0 (calibrated)"
+        return None, "kernel sources changed since the counters were taken"
+    key = "traffic-r%d" % rows
+    if key not in vals:
+        return None, "counters taken at 1 and 24 rows only"
+    return json.loads(vals[key]), "rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0 per launch (calibrated on a 512 MiB copy)"
 
 
 def parse():
@@ -337,7 +341,8 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
     lm_us = e0.elapsed_time(e1) * 1000.0 / args.lm_iters
-    traffic, traffic_note = recorded_traffic() if R == 1 else (None, "counters taken at 1 row")
+    traffic_all, traffic_note = recorded_traffic(R)
+    traffic = traffic_all.get("lm_head") if traffic_all else None
     lm_bytes = d.vocab * d.hidden * 2.0 + R * d.hidden * 2.0
     lm_gbs = lm_bytes / (lm_us * 1e-6) / 1e9
 
@@ -419,7 +424,7 @@ def main():
                      "frac": round(main_run["step_GBps"] / HBM_PEAK_GBS, 4),
                      "distinct_experts_per_moe_layer": main_run["distinct_experts_per_moe_layer"]},
         "rows_sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in sweep],
-        "roofline": dominant_roofline(main_run.get("kernels"), traffic if R == 1 else None),
+        "roofline": dominant_roofline(main_run.get("kernels"), traffic_all, traffic_note),
         "lm_head": {"kernel": ("lm_argmax_kernel<F16, ring 10> (LM head %dx%d + fused argmax, %d row(s); "
                                "one CU-balanced workgroup per CU, then the partial merge)" if R <= 16 else
                                "gemv_kernel<F16,4,1,1,ARGMAX> (LM head %dx%d + fused argmax, %d row(s))")
@@ -443,7 +448,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def dominant_roofline(kernels, lm_traffic):
+def dominant_roofline(kernels, traffic, traffic_note):
     """Roofline of the kernel kind that takes the most time per step (event
     timing inside the step): algorithmic bytes per launch / average launch
     time (kernel plus the gap before it)."""
@@ -453,7 +458,7 @@ def dominant_roofline(kernels, lm_traffic):
     if k is None:
         return None
     return {"kernel": k["kernel"], "bound": "hbm", "achieved": k["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": k["frac"], "traffic": lm_traffic if k["kernel"] == "lm_head" else None,
+            "frac": k["frac"], "traffic": (traffic or {}).get(k["kernel"]), "traffic_note": traffic_note,
             "avg_us": k["avg_us"], "launches_per_step": k["launches_per_step"], "share_of_step": k["share_of_step"],
             "algorithmic_bytes": k["bytes_per_launch"],
             "timing": "HIP events recorded on the bench stream before every kernel of the step (ocrdec_profile_set), "
