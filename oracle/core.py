@@ -10,13 +10,11 @@ Numeric conventions (shared by every function below):
   and v are what the cache holds); the attention output; the SwiGLU
   intermediate.  [UOCR] "Il decoder e il Mixture of Experts": the decode loop
   keeps activations in fp16.
-* The residual stream ``h`` is not rounded to fp16 (the GPU keeps it in fp32).
-  Reading: the fp16 activations are the tensors the projections and the cache
-  consume; the running sum between blocks is kept wide, as [NCNN] 3.1 does
-  with its FP32 residual between blocks to avoid the error that repeated
-  low-precision round trips accumulate.  With an fp16 residual every layer
-  adds one-ulp rounding disagreements that no implementation can keep under
-  the comparison tolerance.
+* The residual stream ``h`` is not rounded to fp16.  Reading: the pages do
+  not say which tensors "activations" covers; the fp16 ones are taken to be
+  the tensors the projections and the cache consume, and the running sum
+  between blocks is kept wide, the precision [NCNN] 3.1 gives the residual
+  between the blocks of its decoder (the only page that states one).
 * Expert outputs, the MoE combine, router logits and LM-head logits are not
   rounded to fp16.  Where floating point decides an integer (top-k routing,
   the LM-head argmax) the decision is taken on logits rounded to float32, the
