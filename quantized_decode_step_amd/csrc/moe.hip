@@ -20,21 +20,50 @@ namespace ocrdec {
 // Routing and grouping (one workgroup of 1024 threads = 16 wavefronts)
 // ---------------------------------------------------------------------------
 
+// The end of row r's top-k in one wavefront, once lane k < K holds the k-th
+// choice `own`: the experts used (forced ones if given) go to idx_out
+// [rows][K], their renormalised weights (softmax over the used experts'
+// logits) to p.w and w_out, and the captures.  logit(e): the row's logit of
+// expert e (bias added separately if non-NULL).
+template <class LOGIT>
+OCR_DEV void topk_finish(const MoeParams& p, int r, int own, LOGIT logit, const float* bias, int* idx_out,
+                         float* w_out) {
+    const int lane = threadIdx.x & 63;
+    const int E = p.n_experts, K = p.top_k;
+    int use = own;
+    const bool forced = p.forced && p.forced[(int64_t)r * K] >= 0;
+    if (forced && lane < K) use = p.forced[(int64_t)r * K + lane];
+    use = min(max(use, 0), E - 1);  // device data: keep every index in range
+    float lk = -INFINITY;
+    if (lane < K) lk = logit(use) + (bias ? bias[use] : 0.f);
+    const float m = wave_max(lk);
+    const float ex = lane < K ? __expf(lk - m) : 0.f;
+    const float den = wave_sum(ex);
+    if (lane < K) {
+        const float w = ex / den;
+        idx_out[r * K + lane] = use;
+        p.w[(int64_t)r * K + lane] = w;
+        if (w_out) w_out[r * K + lane] = w;
+        if (p.cap_idx) p.cap_idx[(int64_t)r * K + lane] = own;
+        if (p.cap_w) p.cap_w[(int64_t)r * K + lane] = w;
+    }
+}
+
 // Top-k of the rows of `lg` ([rows][E], fp32, row stride ldl; global memory
 // or LDS; `bias` [E] added if non-NULL), one wavefront per row: lane l holds
 // experts l, l+64, ...; each of the K rounds takes the wave-wide maximum (a
 // DPP reduction) and the lowest expert holding it (a ballot), so ties go to
 // the lower index; a NaN logit counts as -inf and a taken expert drops out.
 // Writes the experts used (forced ones if given) to idx_out [rows][K], their
-// renormalised weights and the captures.
+// renormalised weights and the captures.  Row r's logits are row r - lr0 of lg.
 OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl, const float* bias, int* idx_out, int r0 = 0,
-                       int r1 = -1, int nsl = 1, int64_t lsl = 0, float* w_out = nullptr) {
+                       int r1 = -1, int nsl = 1, int64_t lsl = 0, float* w_out = nullptr, int lr0 = 0) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int E = p.n_experts, K = p.top_k;
     const float taken = __builtin_nanf("");
     if (r1 < 0) r1 = p.rows;
     for (int r = r0 + wave; r < r1; r += nw) {
-        const float* l = lg + (int64_t)r * ldl;
+        const float* l = lg + (int64_t)(r - lr0) * ldl;
         // logit e: the sum of the k-slices' partial products, in slice order
         auto logit = [&](int e) {
             float x = l[e];
@@ -67,23 +96,46 @@ OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl, const float
             if ((e & 63) == lane) v[e >> 6] = taken;
             if (lane == k) own = e;
         }
-        int use = own;
-        const bool forced = p.forced && p.forced[(int64_t)r * K] >= 0;
-        if (forced && lane < K) use = p.forced[(int64_t)r * K + lane];
-        use = min(max(use, 0), E - 1);  // device data: keep every index in range
-        float lk = -INFINITY;
-        if (lane < K) lk = logit(use) + (bias ? bias[use] : 0.f);
-        const float m = wave_max(lk);
-        const float ex = lane < K ? __expf(lk - m) : 0.f;
-        const float den = wave_sum(ex);
-        if (lane < K) {
-            const float w = ex / den;
-            idx_out[r * K + lane] = use;
-            p.w[(int64_t)r * K + lane] = w;
-            if (w_out) w_out[r * K + lane] = w;
-            if (p.cap_idx) p.cap_idx[(int64_t)r * K + lane] = own;
-            if (p.cap_w) p.cap_w[(int64_t)r * K + lane] = w;
-        }
+        topk_finish(p, r, own, logit, bias, idx_out, w_out);
+    }
+}
+
+// Top-k of one row whose E <= 64 logits l (bias included) sit in LDS, by
+// rank: expert e's rank is the number of experts before it in the order
+// (logit descending, then index ascending; NaN as -inf), which is the order
+// in which topk_rows' rounds take them, so the result is the same.  Every
+// wave counts, for all experts at once (lane e), the experts of its own
+// share of the row that come before; the partial counts meet in LDS (part_s:
+// 64 * waves ints) and wave 0 sums them in wave order, finds the K experts of
+// rank < K and finishes as topk_rows.  Every thread of the workgroup must call
+// it (it holds a barrier).
+OCR_DEV void topk_one_row_ranked(const MoeParams& p, const float* l, int r, int* idx_out, float* w_out, int* part_s) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int E = p.n_experts, K = p.top_k;
+    auto val = [&](int e) {
+        const float x = l[e];
+        return (x == x) ? x : -INFINITY;
+    };
+    const float ve = val(min(lane, E - 1));
+    const int per = (E + nw - 1) / nw, j0 = wave * per, j1 = min(E, j0 + per);
+    int cnt = 0;
+    for (int j = j0; j < j1; ++j) {
+        const float vj = val(j);
+        cnt += (vj > ve || (vj == ve && j < lane)) ? 1 : 0;
+    }
+    part_s[wave * 64 + lane] = cnt;
+    __syncthreads();
+    if (wave == 0) {
+        int rank = 0;
+        for (int w = 0; w < nw; ++w) rank += part_s[w * 64 + lane];
+        // lane k < K learns the expert of rank k (one writer per rank)
+        int* sel_s = part_s + 64 * nw;
+        if (lane < E && rank < K) sel_s[rank] = lane;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int own = lane < K ? sel_s[lane] : 0;
+        topk_finish(p, r, own, [&](int e) { return l[e]; }, nullptr, idx_out, w_out);
     }
 }
 
@@ -742,7 +794,15 @@ __global__ __launch_bounds__(64 * EG_NW, 2) void expert_gemm_kernel(GroupedParam
 // written out for the expert kernels), or copied from x.  The k-splits are
 // summed in a fixed order in LDS; top-k reads the logits from LDS; the
 // grouping works in LDS.  Dynamic LDS: rows * (H + 8) halves.
-template <int FMT, int NV, bool BIAS, int XT>
+// MODE: ROUTE_ALL, all rows (<= 32) in the one workgroup, as above;
+// ROUTE_ONE, a batch of one row (its grouping is a few lane operations of
+// wave 0); ROUTE_ROW, one workgroup per row (row = workgroup id) forms that
+// row's input, logits and choice and writes them to p.idx / p.w, with no
+// grouping (the expert kernels of the expert-indexed decode MoE find their
+// tokens from p.idx).  A single row's top-k (E <= 64) is taken by rank over
+// all waves.
+enum { ROUTE_ALL = 0, ROUTE_ONE = 1, ROUTE_ROW = 2 };
+template <int FMT, int NV, bool BIAS, int XT, int MODE = ROUTE_ALL>
 __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const uint8_t* router, int H,
                                                             const uint16_t* x, int64_t ldx, const fix_t* h_in,
                                                             const uint16_t* norm_w, float eps, uint16_t* x_out) {
@@ -754,7 +814,9 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
     __shared__ float wsel_s[256];
     __shared__ unsigned long long mask_s[4 * 256];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int E = p.n_experts, T = E / 16, R = p.rows;
+    const int E = p.n_experts, T = E / 16;
+    constexpr bool ROW = MODE == ROUTE_ROW;
+    const int r0 = ROW ? (int)blockIdx.x : 0, R = MODE == ROUTE_ALL ? p.rows : 1;
     // The arguments the serial tail (top-k, grouping) reads are requested
     // now: a scalar-cache miss there stalls the only workgroup for a memory
     // round trip.
@@ -773,9 +835,9 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
         staged = 1;
         if (norm_w) {
             // three groups per lane: the 16-wave workgroup has 128 registers per lane
-            block_rmsnorm_fix<3>(h_in, norm_w, H, eps, 0, R, x_out, ldx, xl_dyn, ldl);
+            block_rmsnorm_fix<3>(h_in, norm_w, H, eps, r0, R, x_out, ldx, xl_dyn, ldl);
         } else {
-            stage_x<4>(XDirect{x, ldx, R}, 0, R, H, xl_dyn, ldl);
+            stage_x<4>(XDirect{x + (int64_t)r0 * ldx, ldx, R}, 0, R, H, xl_dyn, ldl);
         }
     };
     // XT = 2: 17-32 rows in one pass over the router weights
@@ -783,7 +845,8 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
         float4v acc[1][XT];
 #pragma unroll
         for (int xt = 0; xt < XT; ++xt) acc[0][xt] = float4v{0.f, 0.f, 0.f, 0.f};
-        kloop_lds<FMT, 1, XT, decltype(stage), 4>(tp, c0, c1, stage, xl_dyn + tok0 * ldl, ldl, R - tok0, H / 32, lane,
+        // (a one-row workgroup has the registers for one more chunk in flight)
+        kloop_lds<FMT, 1, XT, decltype(stage), MODE == ROUTE_ALL ? 4 : 5>(tp, c0, c1, stage, xl_dyn + tok0 * ldl, ldl, R - tok0, H / 32, lane,
                                                   acc);
 #pragma unroll
         for (int xt = 0; xt < XT; ++xt) red[(xt * 16 + wave) * 64 + lane] = acc[0][xt];
@@ -806,14 +869,27 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
         }
         __syncthreads();
     }
-    topk_rows(p, lg_s, E, nullptr, use_s, 0, -1, 1, 0, p.sw ? wsel_s : nullptr);
-    if (R == 1) {
-        // wavefront 0 chose the row's experts and groups them itself
-        if (wave == 0) group_one_row(p, use_s, wsel_s);
-        return;
+    // (the k-split partials in red are consumed: its LDS holds the rank counts)
+    if (R == 1 && E <= 64) {
+        if constexpr (ROW) topk_one_row_ranked(p, lg_s, r0, p.idx, nullptr, (int*)red);
+        else topk_one_row_ranked(p, lg_s, 0, use_s, p.sw ? wsel_s : nullptr, (int*)red);
+    } else {
+        if constexpr (ROW) topk_rows(p, lg_s, E, nullptr, p.idx, r0, r0 + 1, 1, 0, nullptr, r0);
+        else topk_rows(p, lg_s, E, nullptr, use_s, 0, -1, 1, 0, p.sw ? wsel_s : nullptr);
     }
-    __syncthreads();
-    group_pairs_small(p, use_s, mask_s, counts_s, offsets_s, wsel_s);
+    if constexpr (ROW) {
+        return;
+    } else {
+        if (R == 1) {
+            // wavefront 0 chose the row's experts and groups them itself
+            if (wave == 0) group_one_row(p, use_s, wsel_s);
+            return;
+        }
+        if constexpr (MODE == ROUTE_ALL) {
+            __syncthreads();
+            group_pairs_small(p, use_s, mask_s, counts_s, offsets_s, wsel_s);
+        }
+    }
 }
 
 // Dynamic LDS of route_fused_kernel.
@@ -828,26 +904,123 @@ inline size_t route_lds_bytes(int rows, int H) { return (size_t)rows * (H + 8) *
 // the expert's slots of a, fp32 y[slot][row].
 // ---------------------------------------------------------------------------
 
-template <int FMT, int XT, int KS, bool GLU, bool LDSX, bool HADD = false>
+// Expert-indexed decode MoE: the tokens of work entry v, found from the chosen
+// experts pidx [rows][top_k] (pair i = r * top_k + j, rows * top_k <= 256).
+// Entries: shared expert s, 16-token block b at v = s * nb16 + b; then the
+// routed experts that hold at least one token, in expert order (the A-th of
+// them at v = S * nb16 + A, its second block, if any, at S * nb16 + n_active
+// + A).  Entries past those hold nothing.  A routed expert's tokens are its
+// pairs in pair order (row, then rank: the order a stable grouping gives).
+// Writes the entry's expert to e and LDS lists of its tokens (at most 16):
+// row, slot of a (a routed pair's slot is its pair index, shared expert s's
+// slot of row r is rows * top_k + s * rows + r) and, if w_s is non-NULL, the
+// combine weight (pw[pair]; shared: 1).  Every wave computes the expert and
+// count from the same ballots, so both are uniform over the workgroup; wave 0
+// writes the lists.  Returns the count.
+OCR_DEV int expert_entry(const GroupedParams& p, int v, int& e, int* row_s, int* slot_s, float* w_s) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int R = p.rows, K = p.top_k, NP = R * K, E = p.n_experts;
+    const int sv = p.n_shared * p.nb16;
+    if (v < sv) {
+        const int s = v / p.nb16, b = v % p.nb16, cnt = max(0, min(16, R - 16 * b));
+        e = E + s;
+        if (wave == 0 && lane < cnt) {
+            const int r = 16 * b + lane;
+            row_s[lane] = r;
+            slot_s[lane] = NP + s * R + r;
+            if (w_s) w_s[lane] = 1.f;
+        }
+        return cnt;
+    }
+    int id[4];
+    float wt[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = min(64 * j + lane, NP - 1);
+        id[j] = p.pidx[i];
+        wt[j] = w_s ? p.pw[i] : 0.f;
+    }
+    // the active experts as an E-bit mask (E <= 256), OR-reduced over the wave
+    unsigned long long act[4] = {0ull, 0ull, 0ull, 0ull};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const unsigned long long bit = 64 * j + lane < NP ? 1ull << (id[j] & 63) : 0ull;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) act[w] |= (id[j] >> 6) == w ? bit : 0ull;
+    }
+    const int nwd = (E + 63) >> 6;
+    int nact = 0;
+    for (int w = 0; w < nwd; ++w) {  // uniform
+        for (int o = 32; o > 0; o >>= 1) act[w] |= __shfl_xor(act[w], o, 64);
+        nact += __popcll(act[w]);
+    }
+    const int u = v - sv;
+    const int b = u < nact ? 0 : 1, a = u - b * nact;
+    if (b >= p.nb16 || a >= nact) return 0;
+    // the a-th set bit of the mask
+    e = 0;
+    int before = 0;
+    for (int w = 0; w < nwd; ++w) {
+        const int c = __popcll(act[w]);
+        if (a < before + c) {
+            const bool hit = ((act[w] >> lane) & 1ull) && __popcll(act[w] & ((1ull << lane) - 1ull)) == a - before;
+            e = min(max(64 * w + __ffsll((long long)__ballot(hit)) - 1, 0), E - 1);  // (exactly one lane hits)
+            break;
+        }
+        before += c;
+    }
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bool m = 64 * j + lane < NP && id[j] == e;
+        const unsigned long long bal = __ballot(m);
+        const int t = base + __popcll(bal & ((1ull << lane) - 1ull)) - 16 * b;
+        if (wave == 0 && m && t >= 0 && t < 16) {
+            row_s[t] = (64 * j + lane) / K;
+            slot_s[t] = 64 * j + lane;
+            if (w_s) w_s[t] = wt[j];
+        }
+        base += __popcll(bal);
+    }
+    return max(0, min(16, base - 16 * b));
+}
+
+template <int FMT, int XT, int KS, bool GLU, bool LDSX, bool HADD = false, bool BYEXP = false>
 __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(GroupedParams p) {
     constexpr int CB = Geom<FMT>::CB;
     constexpr int NT = GLU ? 2 : 1;
     extern __shared__ __align__(16) uint16_t xl_dyn[];
     __shared__ float4v red[(KS > 1) ? 4 * NT * XT * 64 : 1];
+    static_assert(!BYEXP || (XT == 1 && KS == 1), "expert-indexed entries: 16 tokens, one wave per item");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int item = blockIdx.x * (4 / KS) + wave / KS;
     const int ks = wave % KS;
     const int v = item / p.groups_per_expert;
     const int g = item % p.groups_per_expert;
-    // the list entry is read unconditionally (in bounds: v is clamped) so that
-    // it travels with the count in one round trip
-    const int vc = min(v, p.max_virt - 1);
-    const int n_virt = p.n_virt[0];
-    const int4 ent = p.virt[vc];
-    const bool valid = v < n_virt && v < p.max_virt;
-    const int e = valid ? ent.x : 0;
-    const int off = valid ? ent.y : 0;
-    const int cnt = valid ? ent.z : 0;
+    // expert-indexed entries: token lists in LDS (row, slot, weight)
+    __shared__ int tr_s[BYEXP ? 16 : 1], ts_s[BYEXP ? 16 : 1];
+    __shared__ float tw_s[BYEXP ? 16 : 1];
+    bool valid;
+    int e, off, cnt;
+    if constexpr (BYEXP) {
+        // every wave of the workgroup works on entry v (KS = 1, whole tile
+        // groups per expert): the count is uniform
+        cnt = expert_entry(p, v, e, tr_s, ts_s, HADD ? tw_s : nullptr);
+        __syncthreads();
+        if (cnt == 0) return;
+        valid = true;
+        off = 0;
+    } else {
+        // the list entry is read unconditionally (in bounds: v is clamped) so
+        // that it travels with the count in one round trip
+        const int vc = min(v, p.max_virt - 1);
+        const int n_virt = p.n_virt[0];
+        const int4 ent = p.virt[vc];
+        valid = v < n_virt && v < p.max_virt;
+        e = valid ? ent.x : 0;
+        off = valid ? ent.y : 0;
+        cnt = valid ? ent.z : 0;
+    }
     const uint8_t* base = (e < p.n_experts) ? p.w_routed + (int64_t)e * p.expert_bytes
                                             : p.w_shared + (int64_t)(e - p.n_experts) * p.expert_bytes;
     const uint8_t* tile[NT];
@@ -871,9 +1044,15 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
             for (int xt = 0; xt < XT; ++xt)
 #pragma unroll
                 for (int vv = 0; vv < 4; ++vv) {
-                    const int s_ = off + min(16 * xt + 4 * (lane >> 4) + vv, max(cnt - 1, 0));
-                    hrow[xt][vv] = p.one_row ? 0 : p.vrows[s_];
-                    swt[xt][vv] = p.sw[s_];
+                    const int t_ = min(16 * xt + 4 * (lane >> 4) + vv, max(cnt - 1, 0));
+                    if constexpr (BYEXP) {
+                        hrow[xt][vv] = tr_s[t_];
+                        swt[xt][vv] = tw_s[t_];
+                    } else {
+                        const int s_ = off + t_;
+                        hrow[xt][vv] = p.one_row ? 0 : p.vrows[s_];
+                        swt[xt][vv] = p.sw[s_];
+                    }
                 }
         }
     }
@@ -896,19 +1075,24 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
             const int ldl = xlds_stride(p.k);
             auto stage = [&]() {
                 if constexpr (GLU)
-                    stage_x(XGather{p.x, p.ldx, p.vrows + off, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
+                    stage_x(XGather{p.x, p.ldx, BYEXP ? tr_s : p.vrows + off, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
+                else if constexpr (BYEXP)
+                    stage_x<4>(XGather{p.x, p.ldx, ts_s, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
                 else stage_x<4>(XDirect{p.x + (int64_t)off * p.ldx, p.ldx, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
             };
             kloop_lds<FMT, NT, XT>(tile, c0, cc1, stage, xl_dyn, ldl, cnt - tok0, nblk, lane, acc);
         } else if constexpr (GLU) {
-            if (p.one_row) {
+            if (!BYEXP && p.one_row) {
                 // every slot reads row 0: no row-list load before the activations
                 XDirect xs{p.x, p.ldx, 1};
                 kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
             } else {
-                XGather xs{p.x, p.ldx, p.vrows + off, cnt};
+                XGather xs{p.x, p.ldx, BYEXP ? tr_s : p.vrows + off, cnt};
                 kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
             }
+        } else if constexpr (BYEXP) {
+            XGather xs{p.x, p.ldx, ts_s, cnt};
+            kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
         } else {
             XDirect xs{p.x + (int64_t)off * p.ldx, p.ldx, cnt};
             kloop<FMT, NT, XT>(tile, c0, cc1, xs, tok0, nblk, lane, acc);
@@ -922,7 +1106,7 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
                 for (int vv = 0; vv < 4; ++vv) {
                     const int tok = tok0 + 16 * xt + 4 * (lane >> 4) + vv;
                     if (tok >= cnt) continue;
-                    const int64_t slot = off + tok;
+                    const int64_t slot = BYEXP ? ts_s[tok] : off + tok;
                     if constexpr (GLU) {
                         const int col = tidx[0] * 16 + (lane & 15);
                         const float gv = acc[0][xt][vv], uv = acc[1][xt][vv];
@@ -955,7 +1139,7 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
 // (work-list read, staging) is paid once for IPW items.  Epilogues as in
 // grouped_kernel (SwiGLU into a; down: y, or weight x output added into the
 // fixed-point residual).
-template <int FMT, bool GLU, bool HADD, int IPW, int PF>
+template <int FMT, bool GLU, bool HADD, int IPW, int PF, bool BYEXP = false>
 __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p) {
     constexpr int CB = Geom<FMT>::CB, SB = Geom<FMT>::SB;
     constexpr int NT = GLU ? 2 : 1;
@@ -964,11 +1148,23 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
     const int wpe = p.groups_per_expert / (4 * IPW);  // workgroups per entry
     const int v = blockIdx.x / wpe;
     const int g0 = (blockIdx.x % wpe) * 4 * IPW + wave * IPW;
-    const int vc = min(v, p.max_virt - 1);
-    const int n_virt = p.n_virt[0];
-    const int4 ent = p.virt[vc];
-    if (!(v < n_virt && v < p.max_virt)) return;  // uniform over the workgroup
-    const int e = ent.x, off = ent.y, cnt = min(ent.z, 16);
+    __shared__ int tr_s[BYEXP ? 16 : 1], ts_s[BYEXP ? 16 : 1];
+    __shared__ float tw_s[BYEXP ? 16 : 1];
+    int e, off, cnt;
+    if constexpr (BYEXP) {
+        cnt = expert_entry(p, v, e, tr_s, ts_s, HADD ? tw_s : nullptr);
+        __syncthreads();
+        if (cnt == 0) return;  // uniform over the workgroup
+        off = 0;
+    } else {
+        const int vc = min(v, p.max_virt - 1);
+        const int n_virt = p.n_virt[0];
+        const int4 ent = p.virt[vc];
+        if (!(v < n_virt && v < p.max_virt)) return;  // uniform over the workgroup
+        e = ent.x;
+        off = ent.y;
+        cnt = min(ent.z, 16);
+    }
     const uint8_t* base = (e < p.n_experts) ? p.w_routed + (int64_t)e * p.expert_bytes
                                             : p.w_shared + (int64_t)(e - p.n_experts) * p.expert_bytes;
     const int nc = (int)p.nchunks;
@@ -990,13 +1186,19 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
     if constexpr (HADD) {
 #pragma unroll
         for (int vv = 0; vv < 4; ++vv) {
-            const int s_ = off + min(4 * (lane >> 4) + vv, max(cnt - 1, 0));
-            hrow[vv] = p.one_row ? 0 : p.vrows[s_];
-            swt[vv] = p.sw[s_];
+            const int t_ = min(4 * (lane >> 4) + vv, max(cnt - 1, 0));
+            if constexpr (BYEXP) {
+                hrow[vv] = tr_s[t_];
+                swt[vv] = tw_s[t_];
+            } else {
+                hrow[vv] = p.one_row ? 0 : p.vrows[off + t_];
+                swt[vv] = p.sw[off + t_];
+            }
         }
     }
     const int ldl = xlds_stride(p.k);
-    if constexpr (GLU) stage_x(XGather{p.x, p.ldx, p.vrows + off, cnt}, 0, 16, p.k, xl_dyn, ldl);
+    if constexpr (GLU) stage_x(XGather{p.x, p.ldx, BYEXP ? tr_s : p.vrows + off, cnt}, 0, 16, p.k, xl_dyn, ldl);
+    else if constexpr (BYEXP) stage_x(XGather{p.x, p.ldx, ts_s, cnt}, 0, 16, p.k, xl_dyn, ldl);
     else stage_x(XDirect{p.x + (int64_t)off * p.ldx, p.ldx, cnt}, 0, 16, p.k, xl_dyn, ldl);
     __syncthreads();
     float4v acc[NT][1];
@@ -1025,7 +1227,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
                     for (int vv = 0; vv < 4; ++vv) {
                         const int tok = 4 * (lane >> 4) + vv;
                         if (tok >= cnt) continue;
-                        const int64_t slot = off + tok;
+                        const int64_t slot = BYEXP ? ts_s[tok] : off + tok;
                         if constexpr (GLU) {
                             const int col = tile_of(i, 0) * 16 + (lane & 15);
                             ((uint16_t*)p.y)[slot * p.ldy + col] = f2h(silu(acc[0][0][vv]) * acc[1][0][vv]);
@@ -1215,6 +1417,13 @@ namespace {
 template <int FMT, bool GLU>
 void launch_grouped_fmt(const GroupedParams& p, int xt, int ks, bool lds, int grid, hipStream_t s) {
     const size_t lb = lds ? lds_x_bytes(p.k, xt) : 0;
+    if (p.pidx) {
+        // expert-indexed entries (16 tokens, one wave per item); the down
+        // projection adds into the residual
+        if (lds) hipLaunchKernelGGL((grouped_kernel<FMT, 1, 1, GLU, true, !GLU, true>), dim3(grid), dim3(256), lb, s, p);
+        else hipLaunchKernelGGL((grouped_kernel<FMT, 1, 1, GLU, false, !GLU, true>), dim3(grid), dim3(256), 0, s, p);
+        return;
+    }
 #define OCR_G(XT_, KS_)                                                                                          \
     if (xt == XT_ && ks == KS_) {                                                                               \
         if (!GLU && p.sw) {                                                                                     \
@@ -1239,13 +1448,17 @@ void launch_stream_t(const GroupedParams& p, hipStream_t s) {
     constexpr int PF = GLU ? 6 : 7;
     const int grid = p.max_virt * (p.groups_per_expert / (4 * STREAM_IPW));
     const size_t lb = lds_x_bytes(p.k, 1);
-    if (!GLU && p.sw) hipLaunchKernelGGL((grouped_stream_kernel<FMT, GLU, true, STREAM_IPW, PF>), dim3(grid), dim3(256), lb, s, p);
+    if (p.pidx) {
+        if (GLU) hipLaunchKernelGGL((grouped_stream_kernel<FMT, GLU, false, STREAM_IPW, PF, true>), dim3(grid), dim3(256), lb, s, p);
+        else hipLaunchKernelGGL((grouped_stream_kernel<FMT, GLU, true, STREAM_IPW, PF, true>), dim3(grid), dim3(256), lb, s, p);
+    } else if (!GLU && p.sw) hipLaunchKernelGGL((grouped_stream_kernel<FMT, GLU, true, STREAM_IPW, PF>), dim3(grid), dim3(256), lb, s, p);
     else hipLaunchKernelGGL((grouped_stream_kernel<FMT, GLU, false, STREAM_IPW, PF>), dim3(grid), dim3(256), lb, s, p);
 }
 
 void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream_t s) {
     const int64_t items = (int64_t)p.max_virt * p.groups_per_expert;
-    const int ks = items >= 2048 ? 1 : 4;
+    // (expert-indexed entries: one wave per item)
+    const int ks = (items >= 2048 || p.pidx) ? 1 : 4;
     // gate/up of large decode batches: the streamed form (entries of at most 16
     // tokens, staged in LDS).  It halves the workgroups, which pays only when
     // they exceed the CUs' workgroup slots: measured at 24 rows (gate/up 31.9
@@ -1266,7 +1479,7 @@ void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream
     // the down projection reads its activations contiguously: LDS staging pays
     // for any row count there (and keeps three workgroups per CU)
     const bool lds = (glu ? use_lds_x(p.k, 1, rows_hint) : lds_x_bytes(p.k, 1) <= 65536) && same_expert;
-    const int xt = lds ? 1 : (rows_hint <= 16 ? 1 : 2);
+    const int xt = (lds || p.pidx) ? 1 : (rows_hint <= 16 ? 1 : 2);
     const int grid = (int)((items + (4 / ks) - 1) / (4 / ks));
 #define OCR_F(F_)                                                                          \
     case F_:                                                                               \
@@ -1326,6 +1539,18 @@ void launch_dense_gemm(int fmt, bool glu, const uint8_t* w, int n, int k, int ro
     launch_expert_gemm(fmt, glu, p, (rows + EG_TM - 1) / EG_TM, s);
 }
 
+// Work entries of the expert-indexed decode MoE: (shared experts, then
+// routed ones) x 16-token blocks, tokens found from the chosen experts.
+static void set_byexp(GroupedParams& p, const MoeWs& m, int rows, int K, int S) {
+    p.pidx = m.idx;
+    p.pw = m.w;
+    p.rows = rows;
+    p.top_k = K;
+    p.nb16 = (rows + 15) / 16;
+    p.n_shared = S;
+    p.max_virt = (p.n_experts + S) * p.nb16;
+}
+
 void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_t ldx, void* h, int h_mode, int64_t ldh,
                 int add_residual, const int32_t* forced, const ocrdec_moe_capture* cap, int32_t* cap_idx,
                 float* cap_w, const MoeWs& m, const uint16_t* norm_w, float eps, uint16_t* x_out, int64_t ldxo,
@@ -1365,9 +1590,16 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
     // adds its weighted outputs into the residual itself (atomic integer adds),
     // no combine kernel
     const bool fused = fuse_combine && small && h_mode == RESID_FIX && add_residual;
+    // 2-32 rows of the decode step: the expert-indexed form.  One routing
+    // workgroup per row (norm, router GEMV, top-k), no grouping pass; each
+    // expert kernel workgroup owns a fixed (expert, 16-token block) and finds
+    // its tokens in the chosen experts itself.  (One row keeps the single
+    // routing workgroup, whose grouping of one row is a few lane operations.)
+    const bool byexp = fused && rows >= 2 && !p.cap_counts && !p.cap_offsets && !p.cap_perm &&
+                       (F / 16) % (4 * 2) == 0 && (H / 16) % 4 == 0;
     // the grouping also lists every slot's combine weight: the down projection
     // adds its outputs into the residual itself
-    if (fused) p.sw = m.sw;
+    if (fused && !byexp) p.sw = m.sw;
     if (norm_in && !small) {
         // the MoE input is the normalised residual: form it first
         prof_mark(s, OCRDEC_K_NORM);
@@ -1380,10 +1612,16 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         const uint8_t* rw = (const uint8_t*)w->router.data;
         // 17-32 rows: one 32-token pass over the router weights where the LDS
         // allows (fp16 and Q8_0 routers; the other formats' variants spill)
-        const bool xt2 = rows > 16 && route_lds_bytes(rows, H) <= 84 * 1024 &&
+        const bool xt2 = !byexp && rows > 16 && route_lds_bytes(rows, H) <= 84 * 1024 &&
                          (w->router.fmt == OCRDEC_F16 || w->router.fmt == OCRDEC_Q8_0);
 #define OCR_RLB(F_, NV_, B_)                                                                                   \
-    if (xt2)                                                                                                   \
+    if (byexp)                                                                                                 \
+        hipLaunchKernelGGL((route_fused_kernel<F_, NV_, B_, 1, ROUTE_ROW>), dim3(rows), dim3(1024), route_lds_bytes(1, H), \
+                           s, p, rw, H, x, ldx, h_norm, norm_in, eps_in, (uint16_t*)x);                        \
+    else if (rows == 1)                                                                                        \
+        hipLaunchKernelGGL((route_fused_kernel<F_, NV_, B_, 1, ROUTE_ONE>), dim3(1), dim3(1024), route_lds_bytes(1, H), \
+                           s, p, rw, H, x, ldx, h_norm, norm_in, eps_in, (uint16_t*)x);                        \
+    else if (xt2)                                                                                              \
         hipLaunchKernelGGL((route_fused_kernel<F_, NV_, B_, 2>), dim3(1), dim3(1024), route_lds_bytes(rows, H), s, p, \
                            rw, H, x, ldx, h_norm, norm_in, eps_in, (uint16_t*)x);                              \
     else                                                                                                       \
@@ -1472,6 +1710,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
         p.out_tiles = F / 16;
         p.one_row = rows == 1;
         p.entries16 = small;
+        if (byexp) set_byexp(p, m, rows, K, S);
         prof_mark(s, OCRDEC_K_EXPERT_GLU);
         if (gemm) launch_expert_gemm(w->gate_up.fmt, true, p, max_virt, s);
         else launch_grouped(w->gate_up.fmt, true, p, rows, s);
@@ -1505,6 +1744,7 @@ void launch_moe(const ocrdec_moe_weights* w, int rows, const uint16_t* x, int64_
             p.ldh = ldh;
             p.status = status;
         }
+        if (byexp) set_byexp(p, m, rows, K, S);
         prof_mark(s, OCRDEC_K_EXPERT_DOWN);
         if (gemm) launch_expert_gemm(w->down.fmt, false, p, max_virt, s);
         else launch_grouped(w->down.fmt, false, p, rows, s);

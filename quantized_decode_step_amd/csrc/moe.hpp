@@ -71,6 +71,16 @@ struct GroupedParams {
     uint32_t* status;
     int one_row;       // one token row in all (decode of one row): every slot's row is 0
     int entries16;     // every work entry holds at most 16 tokens (decode-sized grouping)
+    // Expert-indexed decode MoE (no grouping pass, pidx non-NULL): a
+    // workgroup finds its entry's expert and tokens in pidx [rows][top_k] (the
+    // chosen experts, row-major: pair i = r * top_k + j) itself: shared
+    // experts' 16-token blocks first, then the routed experts holding tokens
+    // (expert_entry).  A routed pair's slot of a is its pair index, shared
+    // expert s's slot of row r is rows*top_k + s*rows + r; the combine weight
+    // is pw[pair] (shared: 1).  max_virt = (n_experts + n_shared) * nb16.
+    const int32_t* pidx;
+    const float* pw;
+    int rows, top_k, nb16, n_shared;
 };
 
 struct CombineParams {
