@@ -74,6 +74,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch kernels directly instead of replaying a graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-cpu-sweep", action="store_true", help="time the oracle at one row only")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-shaped MoE layer line")
     ap.add_argument("--no-qhead", action="store_true", help="skip the Q4_0 LM-head and embedding variant")
     ap.add_argument("--lm-iters", type=int, default=50)
@@ -398,6 +399,10 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(model, d, args.cpu_seconds, T0)
+        # the oracle at every swept row count: one whole step of R rows each
+        if not args.no_cpu_sweep:
+            for s_ in sweep:
+                s_["cpu_baseline"] = cpu_baseline(model, d, 0.0, T0, rows=s_["rows"])
 
     line = {
         "metric": "decode rows\u00b7steps/s (12-layer MoE step) + achieved HBM GB/s vs peak",
@@ -833,9 +838,9 @@ def lm_only(args, dm, d, q, torch, dev, stream):
                       "copy_bytes": n, "copy_launches": 3}), flush=True)
 
 
-def cpu_baseline(model, d, budget_s: float, T0: int):
-    """The oracle, as it stands, on one row of the same workload: as many whole
-    steps as fit in the budget (at least one)."""
+def cpu_baseline(model, d, budget_s: float, T0: int, rows: int = 1):
+    """The oracle, as it stands, on `rows` rows of the same workload: as many
+    whole steps as fit in the budget (at least one)."""
     import synth
     import oracle as O
     try:
@@ -843,8 +848,8 @@ def cpu_baseline(model, d, budget_s: float, T0: int):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = 1
-    st = synth.make_state(d, SEED, [d.prefix_cap], [T0])
-    tok = synth.first_tokens(d, SEED, 1)
+    st = synth.make_state(d, SEED, [d.prefix_cap] * rows, [T0] * rows)
+    tok = synth.first_tokens(d, SEED, rows)
     steps = 0
     t0 = time.time()
     while True:
@@ -854,9 +859,9 @@ def cpu_baseline(model, d, budget_s: float, T0: int):
         if time.time() - t0 >= budget_s:
             break
     el = time.time() - t0
-    return {"value": round(steps / el, 4), "unit": "rows\u00b7steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": "%d step(s) of 1 row of the same 12-layer workload (prefix 1100, ring from t=%d), "
-                      "numpy float64, %.1f s" % (steps, T0, el)}
+    return {"value": round(rows * steps / el, 4), "unit": "rows\u00b7steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": "%d step(s) of %d row(s) of the same 12-layer workload (prefix 1100, ring from t=%d), "
+                      "numpy float64, %.1f s" % (steps, rows, T0, el)}
 
 
 if __name__ == "__main__":

@@ -1459,18 +1459,31 @@ void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream
     const int64_t items = (int64_t)p.max_virt * p.groups_per_expert;
     // (expert-indexed entries: one wave per item)
     const int ks = (items >= 2048 || p.pidx) ? 1 : 4;
-    // gate/up of large decode batches: the streamed form (entries of at most 16
-    // tokens, staged in LDS).  It halves the workgroups, which pays only when
-    // they exceed the CUs' workgroup slots: measured at 24 rows (gate/up 31.9
-    // -> 28.0 us) but slower at 6 and 12 rows (17.5 -> 19.6 us at 6) and for
-    // the down projection at every row count.
-    if (glu && rows_hint >= 20 && p.entries16 && ks == 1 && p.groups_per_expert % (4 * STREAM_IPW) == 0 &&
+    // gate/up of decode batches from 10 rows: the streamed form (entries of at
+    // most 16 tokens, staged in LDS).  It halves the workgroups, which pays
+    // once they exceed the CUs' workgroup slots (two per CU for the one-item
+    // form): measured at 12, 16 and 24 rows (step 1.110 -> 1.100, 1.258 ->
+    // 1.237 ms; gate/up 31.9 -> 28.0 us at 24), even at 8 rows, slower at 6
+    // (0.851 -> 0.869 ms).
+    if (glu && rows_hint >= 10 && p.entries16 && ks == 1 && p.groups_per_expert % (4 * STREAM_IPW) == 0 &&
         lds_x_bytes(p.k, 1) <= 65536 && use_lds_x(p.k, 1, rows_hint)) {
         switch (fmt) {
         case OCRDEC_F16: launch_stream_t<OCRDEC_F16, true>(p, s); return;
         case OCRDEC_Q8_0: launch_stream_t<OCRDEC_Q8_0, true>(p, s); return;
         case OCRDEC_Q4_0: launch_stream_t<OCRDEC_Q4_0, true>(p, s); return;
         case OCRDEC_U8A_G32: launch_stream_t<OCRDEC_U8A_G32, true>(p, s); return;
+        }
+    }
+    // the expert-indexed down projection of 20 or more rows: the streamed form
+    // too (24 rows: 20.0 -> 19.0 us; slower at 6 and 12 rows, 12.1 -> 14.6 and
+    // 14.1 -> 15.3 us)
+    if (!glu && p.pidx && rows_hint >= 20 && p.groups_per_expert % (4 * STREAM_IPW) == 0 &&
+        lds_x_bytes(p.k, 1) <= 65536) {
+        switch (fmt) {
+        case OCRDEC_F16: launch_stream_t<OCRDEC_F16, false>(p, s); return;
+        case OCRDEC_Q8_0: launch_stream_t<OCRDEC_Q8_0, false>(p, s); return;
+        case OCRDEC_Q4_0: launch_stream_t<OCRDEC_Q4_0, false>(p, s); return;
+        case OCRDEC_U8A_G32: launch_stream_t<OCRDEC_U8A_G32, false>(p, s); return;
         }
     }
     // LDS staging needs every wave of a workgroup on the same expert; it uses
