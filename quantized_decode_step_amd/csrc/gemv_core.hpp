@@ -12,6 +12,8 @@
 // token 16*xt + 4*(l >> 4) + v and weight row 16*tile + (l & 15).
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace ocrdec {
@@ -295,6 +297,38 @@ OCR_DEV void stage_x(const XS& xs, int tok0, int ntok, int k, uint16_t* xl, int 
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their
+// maxima, i.e. not waited for).
+template <int N>
+OCR_DEV void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Copies nt activation rows into LDS (row t at xl + t * ldl) with
+// buffer loads that write LDS directly, no registers: wave w of the
+// workgroup copies rows w, w + waves, ..., one instruction per 64 pieces of
+// 16 bytes of a row.  row_of(t) gives row t's address (the same in every
+// lane).  The caller waits for them (vmcnt) and then for the workgroup: issued
+// ahead of the weights, they let the activations arrive first, as loads
+// return in issue order.
+template <class ROWF>
+OCR_DEV void stage_rows_direct(ROWF row_of, int nt, int k, uint16_t* xl, int ldl) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int n16 = k >> 3;
+    for (int t = wave; t < nt; t += nw) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)row_of(t), 0, 0x7fffffff, 0x00020000);
+        for (int i = 0; 64 * i < n16; ++i)
+            if (64 * i + lane < n16)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(xl + t * ldl + 512 * i), 16, lane * 16,
+                                                         1024 * i, 0, 0);
+    }
+}
+
 // x = fp16(RMSNorm(h[r]) * gamma) for rows r0 .. r0+R-1 of the decode step's
 // fixed-point residual (row stride H), formed by all waves of the workgroup
 // into LDS (row r at xl + (r - r0) * ldl) and, if x_out is non-NULL, into
@@ -415,18 +449,41 @@ constexpr int kloop_lds_depth() {
 // them into LDS; the barrier follows), so both travel in the same round trip;
 // afterwards the A fragments come from LDS and only weights stream from
 // memory.
-template <int FMT, int NT, int XT, class STAGE, int PF = kloop_lds_depth<FMT, NT>()>
+struct NoIssue {
+    OCR_DEV void operator()() const {}
+};
+
+// Weight load instructions of a kloop_lds prologue (its PF chunks of NT tiles).
+template <int FMT, int NT, int PF>
+constexpr int kloop_prologue_loads() { return PF * NT * (FMT == OCRDEC_F16 ? 1 : 2); }
+
+// pre(), if given: runs before the first weight chunks are requested
+// (activation loads issued there travel ahead of the weights); stage() after
+// them.  With pre() the first PF chunks are requested unconditionally (a
+// short range repeats its last chunk; an empty one reads a chunk of the tile
+// in range: c0 <= nchunks and c1 <= nchunks), so that exactly
+// kloop_prologue_loads() loads follow pre().
+template <int FMT, int NT, int XT, class STAGE, int PF = kloop_lds_depth<FMT, NT>(), class PRE = NoIssue>
 OCR_DEV void kloop_lds(const uint8_t* const (&tile)[NT], int c0, int c1, STAGE stage, const uint16_t* xl, int ldl,
-                       int ntok, int nblk, int lane, float4v (&acc)[NT][XT]) {
+                       int ntok, int nblk, int lane, float4v (&acc)[NT][XT], PRE pre = PRE{}) {
     constexpr int CB = Geom<FMT>::CB;
     constexpr int SB = Geom<FMT>::SB;
+    constexpr bool PRE_ISSUES = !std::is_same<PRE, NoIssue>::value;
+    pre();
+    if constexpr (PRE_ISSUES) __builtin_amdgcn_sched_barrier(0);
     WRegs wb[PF][NT];
 #pragma unroll
-    for (int u = 0; u < PF; ++u)
-        if (c0 + u < c1) {
+    for (int u = 0; u < PF; ++u) {
+        if constexpr (PRE_ISSUES) {
+            const int cu = max(min(c0 + u, c1 - 1), 0);
+#pragma unroll
+            for (int i = 0; i < NT; ++i) load_wchunk<FMT>(tile[i] + (int64_t)cu * CB, lane, wb[u][i]);
+        } else if (c0 + u < c1) {
 #pragma unroll
             for (int i = 0; i < NT; ++i) load_wchunk<FMT>(tile[i] + (int64_t)(c0 + u) * CB, lane, wb[u][i]);
         }
+    }
+    if constexpr (PRE_ISSUES) __builtin_amdgcn_sched_barrier(0);
     stage();
     __syncthreads();
     for (int c = c0; c < c1; c += PF) {

@@ -560,17 +560,6 @@ constexpr int EG_NBUF = 2;   // LDS stage buffers: stage s+1 in flight while s i
 constexpr int EG_LDS = EG_NBUF * EG_TM * EG_KS * 2;
 constexpr int EG_NDMA = EG_TM * EG_KS * 2 / 1024 / EG_NW;  // 1 KiB stage loads per wave and stage
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their
-// maxima, i.e. not waited for).
-template <int N>
-OCR_DEV void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 template <int FMT, bool GLU>
 __global__ __launch_bounds__(64 * EG_NW, 2) void expert_gemm_kernel(GroupedParams p, int n_cg) {
     constexpr int SB = Geom<FMT>::SB, CB = Geom<FMT>::CB, KC = 32 * SB;
@@ -825,7 +814,7 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
     const int tile = wave % T, ks = wave / T;
     const int64_t nch = n_chunks_dev<FMT>(H);
     const int cper = (int)((nch + nks - 1) / nks);
-    const int c0 = ks * cper;
+    const int c0 = (int)min((int64_t)ks * cper, nch);  // (a chunk index in range even when empty)
     const int c1 = ks < nks ? (int)min((int64_t)(c0 + cper), nch) : c0;
     const uint8_t* tp[1] = {router + (int64_t)tile * nch * CB};
     const int ldl = xlds_stride(H);
@@ -1031,7 +1020,7 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
         tile[i] = base + (int64_t)tidx[i] * p.nchunks * CB;
     }
     const int cper = (int)((p.nchunks + KS - 1) / KS);
-    const int c0 = ks * cper;
+    const int c0 = (int)min((int64_t)ks * cper, p.nchunks);  // (a chunk index in range even when empty)
     const int c1 = valid ? (int)min((int64_t)(c0 + cper), p.nchunks) : c0;
     const int nblk = p.k / 32;
     // residual-adding down projection: the rows and weights of this lane's
@@ -1073,14 +1062,24 @@ __global__ __launch_bounds__(256, (GLU || !LDSX) ? 2 : 3) void grouped_kernel(Gr
             // the workgroup's waves share one expert (groups_per_expert is a
             // multiple of the waves per workgroup), hence one token set
             const int ldl = xlds_stride(p.k);
-            auto stage = [&]() {
-                if constexpr (GLU)
-                    stage_x(XGather{p.x, p.ldx, BYEXP ? tr_s : p.vrows + off, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
-                else if constexpr (BYEXP)
-                    stage_x<4>(XGather{p.x, p.ldx, ts_s, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
-                else stage_x<4>(XDirect{p.x + (int64_t)off * p.ldx, p.ldx, cnt}, tok0, 16 * XT, p.k, xl_dyn, ldl);
+            // the pass's token rows go into LDS by direct buffer loads issued
+            // ahead of the weight ring (pre); stage() waits for all but the
+            // ring's loads
+            constexpr int PFL = kloop_lds_depth<FMT, NT>();
+            auto pre = [&]() {
+                stage_rows_direct(
+                    [&](int t) {
+                        int row;
+                        if constexpr (GLU) row = BYEXP ? tr_s[tok0 + t] : p.vrows[off + tok0 + t];
+                        else if constexpr (BYEXP) row = ts_s[tok0 + t];
+                        else row = off + tok0 + t;
+                        return p.x + (int64_t)__builtin_amdgcn_readfirstlane(row) * p.ldx;
+                    },
+                    min(16 * XT, cnt - tok0), p.k, xl_dyn, ldl);
             };
-            kloop_lds<FMT, NT, XT>(tile, c0, cc1, stage, xl_dyn, ldl, cnt - tok0, nblk, lane, acc);
+            auto stage = [&]() { wait_vmcnt<kloop_prologue_loads<FMT, NT, PFL>()>(); };
+            kloop_lds<FMT, NT, XT, decltype(stage), PFL, decltype(pre)>(tile, c0, cc1, stage, xl_dyn, ldl, cnt - tok0,
+                                                                       nblk, lane, acc, pre);
         } else if constexpr (GLU) {
             if (!BYEXP && p.one_row) {
                 // every slot reads row 0: no row-list load before the activations
@@ -1175,11 +1174,6 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
         const int qc = min(q, total - 1);
         return base + ((int64_t)tile_of(qc / nc, t) * nc + (qc % nc)) * CB;
     };
-    WRegs wb[PF][NT];
-#pragma unroll
-    for (int u = 0; u < PF; ++u)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) load_wchunk<FMT>(chunk_ptr(u, t), lane, wb[u][t]);
     // residual-adding down projection: rows and weights of this lane's slots
     int hrow[4];
     float swt[4];
@@ -1196,10 +1190,28 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
             }
         }
     }
+    // The entry's token rows go into LDS by buffer loads that write LDS
+    // directly (wave w copies rows w, w+4, ...; one instruction per 64 pieces
+    // of 16 bytes of a row), issued ahead of the weight ring: loads return in
+    // issue order, so the rows are in once all but the ring's loads are.
     const int ldl = xlds_stride(p.k);
-    if constexpr (GLU) stage_x(XGather{p.x, p.ldx, BYEXP ? tr_s : p.vrows + off, cnt}, 0, 16, p.k, xl_dyn, ldl);
-    else if constexpr (BYEXP) stage_x(XGather{p.x, p.ldx, ts_s, cnt}, 0, 16, p.k, xl_dyn, ldl);
-    else stage_x(XDirect{p.x + (int64_t)off * p.ldx, p.ldx, cnt}, 0, 16, p.k, xl_dyn, ldl);
+    stage_rows_direct(
+        [&](int t) {
+            int row;
+            if constexpr (GLU) row = BYEXP ? tr_s[t] : p.vrows[off + t];
+            else if constexpr (BYEXP) row = ts_s[t];
+            else row = off + t;
+            return p.x + (int64_t)__builtin_amdgcn_readfirstlane(row) * p.ldx;
+        },
+        cnt, p.k, xl_dyn, ldl);
+    __builtin_amdgcn_sched_barrier(0);
+    WRegs wb[PF][NT];
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) load_wchunk<FMT>(chunk_ptr(u, t), lane, wb[u][t]);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<PF * NT * (FMT == OCRDEC_F16 ? 1 : 2)>();  // everything but the ring: the rows are in LDS
     __syncthreads();
     float4v acc[NT][1];
 #pragma unroll

@@ -456,3 +456,47 @@ def test_lm_argmax_ties_go_to_lowest_index(q, n, k):
     q.ocrdec_lm_argmax(dm.desc, rows, f16_tensor(x), tok, None, ws, wsb)
     torch.cuda.synchronize()
     assert tok.cpu().numpy().tolist() == [17, 17, 17]
+
+
+def _planted_block_rows(fmt, n, k, vals):
+    """Canonical Q8_0 / Q4_0 rows whose only nonzero weight is column 0 of
+    the rows in `vals` (value d * q, written exactly)."""
+    nb = k // 32
+    if fmt == synth.Q8_0:
+        blk = np.zeros((n, nb, 34), np.uint8)
+        for v, (d, qv) in vals.items():
+            blk[v, 0, 0:2] = np.frombuffer(np.float16(d).tobytes(), np.uint8)
+            blk[v, 0, 2] = np.uint8(np.int8(qv).view(np.uint8))
+    else:
+        blk = np.zeros((n, nb, 18), np.uint8)
+        blk[:, :, 2:] = 0x88  # every code 8: value 0
+        for v, (d, qv) in vals.items():
+            blk[v, 0, 0:2] = np.frombuffer(np.float16(d).tobytes(), np.uint8)
+            blk[v, 0, 2] = 0x80 | (qv + 8)  # element 0 in the low nibble of byte 0
+    return synth.QMat(fmt, n, k, blk.reshape(-1).copy())
+
+
+# block formats: five chunks per row against the ring of four, so tiles end
+# inside a pass of the ring
+@pytest.mark.parametrize("fmt,k", [(synth.Q8_0, 320), (synth.Q4_0, 640)])
+def test_lm_argmax_block_ties_go_to_lowest_index(q, fmt, k):
+    import torch
+    n, rows = 40000, 3
+    _say("lm_argmax planted ties", synth.FMT_NAMES[fmt], n, k)
+    # four rows at 2.0 (d = 1, q = 2), one at 1.5 (d = 0.5, q = 3)
+    vals = {v: (1.0, 2) for v in (17, 900, 4000, n - 5)}
+    vals[3000] = (0.5, 3)
+    m = _planted_block_rows(fmt, n, k, vals)
+    x = np.zeros((rows, k), np.float16)
+    x[:, 0] = 1
+    z = O.gemv_qmat(m, x.astype(np.float64))
+    assert z[0, 17] == 2.0 and z[0, 3000] == 1.5 and np.count_nonzero(z[0]) == 5
+    dm = q.DeviceQMat(m)
+    tok = torch.full((rows,), -1, dtype=torch.int32, device="cuda")
+    top2 = torch.zeros((rows, 2), dtype=torch.float32, device="cuda")
+    wsb = q.ocrdec_lm_argmax_workspace_bytes(dm.desc, rows)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    q.ocrdec_lm_argmax(dm.desc, rows, f16_tensor(x), tok, top2, ws, wsb)
+    torch.cuda.synchronize()
+    assert tok.cpu().numpy().tolist() == [17, 17, 17]
+    assert top2.cpu().numpy().tolist() == [[2.0, 2.0]] * rows
