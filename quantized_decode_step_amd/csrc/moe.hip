@@ -1217,11 +1217,15 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t][0] = float4v{0.f, 0.f, 0.f, 0.f};
     bool bad = false;
+    // (PF divides the stream's length, checked by the host: every pass of the
+    // ring is whole and the refills are unconditional, past the end they
+    // repeat the last chunk, from cache; with no branch around them the
+    // ring's registers stay in place across the loop's back edge)
     for (int q0 = 0; q0 < total; q0 += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
             const int q = q0 + u;
-            if (q < total) {
+            {
                 const int c = q % nc;
                 half8v xa[SB][1];
                 float4v xs[SB][1];
@@ -1229,10 +1233,8 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
                 xsums<FMT, 1>(xa, xs);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) chunk_mac<FMT, 1>(wb[u][t], xa, xs, acc[t]);
-                if (q + PF < total) {
 #pragma unroll
-                    for (int t = 0; t < NT; ++t) load_wchunk<FMT>(chunk_ptr(q + PF, t), lane, wb[u][t]);
-                }
+                for (int t = 0; t < NT; ++t) load_wchunk<FMT>(chunk_ptr(q + PF, t), lane, wb[u][t]);
                 if (c == nc - 1) {  // item q / nc complete
                     const int i = q / nc;
 #pragma unroll
@@ -1453,11 +1455,16 @@ void launch_grouped_fmt(const GroupedParams& p, int xt, int ks, bool lds, int gr
 }
 
 // Streamed form (grouped_stream_kernel): two items per wave, entries of at
-// most 16 tokens staged in LDS.
+// most 16 tokens staged in LDS; the ring depth must divide the stream.
 constexpr int STREAM_IPW = 2;
+inline int stream_pf(bool glu) { return glu ? 5 : 7; }
+inline bool stream_ok(const GroupedParams& p, bool glu) {
+    return p.groups_per_expert % (4 * STREAM_IPW) == 0 && lds_x_bytes(p.k, 1) <= 65536 &&
+           (STREAM_IPW * p.nchunks) % stream_pf(glu) == 0;
+}
 template <int FMT, bool GLU>
 void launch_stream_t(const GroupedParams& p, hipStream_t s) {
-    constexpr int PF = GLU ? 6 : 7;
+    constexpr int PF = GLU ? 5 : 7;  // = stream_pf(GLU)
     const int grid = p.max_virt * (p.groups_per_expert / (4 * STREAM_IPW));
     const size_t lb = lds_x_bytes(p.k, 1);
     if (p.pidx) {
@@ -1477,8 +1484,7 @@ void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream
     // form): measured at 12, 16 and 24 rows (step 1.110 -> 1.100, 1.258 ->
     // 1.237 ms; gate/up 31.9 -> 28.0 us at 24), even at 8 rows, slower at 6
     // (0.851 -> 0.869 ms).
-    if (glu && rows_hint >= 10 && p.entries16 && ks == 1 && p.groups_per_expert % (4 * STREAM_IPW) == 0 &&
-        lds_x_bytes(p.k, 1) <= 65536 && use_lds_x(p.k, 1, rows_hint)) {
+    if (glu && rows_hint >= 10 && p.entries16 && ks == 1 && stream_ok(p, true) && use_lds_x(p.k, 1, rows_hint)) {
         switch (fmt) {
         case OCRDEC_F16: launch_stream_t<OCRDEC_F16, true>(p, s); return;
         case OCRDEC_Q8_0: launch_stream_t<OCRDEC_Q8_0, true>(p, s); return;
@@ -1489,8 +1495,7 @@ void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream
     // the expert-indexed down projection of 20 or more rows: the streamed form
     // too (24 rows: 20.0 -> 19.0 us; slower at 6 and 12 rows, 12.1 -> 14.6 and
     // 14.1 -> 15.3 us)
-    if (!glu && p.pidx && rows_hint >= 20 && p.groups_per_expert % (4 * STREAM_IPW) == 0 &&
-        lds_x_bytes(p.k, 1) <= 65536) {
+    if (!glu && p.pidx && rows_hint >= 20 && stream_ok(p, false)) {
         switch (fmt) {
         case OCRDEC_F16: launch_stream_t<OCRDEC_F16, false>(p, s); return;
         case OCRDEC_Q8_0: launch_stream_t<OCRDEC_Q8_0, false>(p, s); return;
