@@ -106,9 +106,10 @@ OCR_DEV void topk_rows(const MoeParams& p, const float* lg, int ldl, const float
 // in which topk_rows' rounds take them, so the result is the same.  Every
 // wave counts, for all experts at once (lane e), the experts of its own
 // share of the row that come before; the partial counts meet in LDS (part_s:
-// 64 * waves ints) and wave 0 sums them in wave order, finds the K experts of
-// rank < K and finishes as topk_rows.  Every thread of the workgroup must call
-// it (it holds a barrier).
+// 64 * 16 + 64 ints, expert e's counts at 16 * e, read with four 16-byte loads)
+// and wave 0 sums them in wave order, finds the K experts of rank < K and
+// finishes as topk_rows.  Every thread of the workgroup must call it (it holds
+// a barrier); at most 16 waves.
 OCR_DEV void topk_one_row_ranked(const MoeParams& p, const float* l, int r, int* idx_out, float* w_out, int* part_s) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int E = p.n_experts, K = p.top_k;
@@ -123,13 +124,19 @@ OCR_DEV void topk_one_row_ranked(const MoeParams& p, const float* l, int r, int*
         const float vj = val(j);
         cnt += (vj > ve || (vj == ve && j < lane)) ? 1 : 0;
     }
-    part_s[wave * 64 + lane] = cnt;
+    if (wave == 0)
+        for (int w = nw; w < 16; ++w) part_s[16 * lane + w] = 0;
+    part_s[16 * lane + wave] = cnt;
     __syncthreads();
     if (wave == 0) {
         int rank = 0;
-        for (int w = 0; w < nw; ++w) rank += part_s[w * 64 + lane];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int4 c4 = *(const int4*)(part_s + 16 * lane + 4 * q);
+            rank += c4.x + c4.y + c4.z + c4.w;
+        }
         // lane k < K learns the expert of rank k (one writer per rank)
-        int* sel_s = part_s + 64 * nw;
+        int* sel_s = part_s + 64 * 16;
         if (lane < E && rank < K) sel_s[rank] = lane;
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -240,9 +247,12 @@ OCR_DEV void group_one_row(const MoeParams& p, const int* idx_s, const float* w_
     const int e = lane < K ? idx_s[lane] : 0x7fffffff;
     // (a forced choice may repeat an expert: equal ids rank by choice, one
     // entry per token, which the expert kernels treat like one of two tokens)
+    // Every lane reads the K choices from LDS (independent reads, no chain of
+    // lane exchanges).
     int rank = 0;
+#pragma unroll 8
     for (int j = 0; j < K; ++j) {
-        const int ej = __shfl(e, j, 64);
+        const int ej = idx_s[j];
         rank += (ej < e || (ej == e && j < lane)) ? 1 : 0;
     }
     if (lane < K) {
