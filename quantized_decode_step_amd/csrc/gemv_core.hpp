@@ -416,6 +416,72 @@ OCR_DEV void block_rmsnorm_fix(const fix_t* h, const uint16_t* gamma, int H, flo
     }
 }
 
+// block_rmsnorm_fix for one row, in two phases for a kernel that also
+// requests weights: issue() requests row r0's slices (wave w < G takes slice
+// w of G) as raw fixed-point values and gains in registers, finish() forms
+// the norm (partial sums of squares added in slice order in LDS, as
+// block_rmsnorm_fix does) into LDS row 0 and x_out row r0.  The workgroup
+// must have at least G wavefronts; every thread calls both.
+template <int MAXG>
+struct RowNormFix {
+    longlong2 a[MAXG], b[MAXG];
+    uint2 g[MAXG];
+    int G, per, n4, g0, g1;
+    OCR_DEV void issue(const fix_t* h, const uint16_t* gamma, int H, int r0) {
+        const int nw = (int)blockDim.x >> 6, wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+        n4 = H / 4;
+        const int gmin = (n4 + 64 * MAXG - 1) / (64 * MAXG);
+        G = max(gmin, min(4, nw));
+        per = (n4 + G - 1) / G;
+        const int sl = min(wave, G - 1);
+        g0 = sl * per;
+        g1 = min(g0 + per, n4);
+        const fix_t* hr = h + (int64_t)r0 * H;
+        if (wave < G) {
+#pragma unroll
+            for (int i = 0; i < MAXG; ++i) {
+                const int c = min(g0 + lane + 64 * i, g1 - 1);
+                a[i] = ((const longlong2*)hr)[2 * c];
+                b[i] = ((const longlong2*)hr)[2 * c + 1];
+                g[i] = ((const uint2*)gamma)[c];
+            }
+        }
+    }
+    OCR_DEV void finish(int H, float eps, int r0, uint16_t* x_out, int64_t ldx, uint16_t* xl) {
+        __shared__ float ss_lds[16];
+        const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+        float4 v[MAXG];
+#pragma unroll
+        for (int i = 0; i < MAXG; ++i)
+            v[i] = wave < G && g0 + lane + 64 * i < g1
+                       ? make_float4(fix_to(a[i].x), fix_to(a[i].y), fix_to(b[i].x), fix_to(b[i].y))
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < MAXG; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+        ss = wave_sum(ss);
+        if (lane == 0 && wave < G) ss_lds[wave] = ss;
+        __syncthreads();
+        if (wave < G) {
+            float tot = 0.f;
+            for (int j = 0; j < G; ++j) tot += ss_lds[j];
+            const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+            for (int i = 0; i < MAXG; ++i) {
+                const int c4 = g0 + lane + 64 * i;
+                if (c4 < g1) {
+                    const uint32_t lo = (uint32_t)f2h(v[i].x * inv * h2f((uint16_t)(g[i].x & 0xFFFF))) |
+                                        ((uint32_t)f2h(v[i].y * inv * h2f((uint16_t)(g[i].x >> 16))) << 16);
+                    const uint32_t hi = (uint32_t)f2h(v[i].z * inv * h2f((uint16_t)(g[i].y & 0xFFFF))) |
+                                        ((uint32_t)f2h(v[i].w * inv * h2f((uint16_t)(g[i].y >> 16))) << 16);
+                    ((uint2*)xl)[c4] = make_uint2(lo, hi);
+                    if (x_out) ((uint2*)(x_out + (int64_t)r0 * ldx))[c4] = make_uint2(lo, hi);
+                }
+            }
+        }
+    }
+};
+
 // x = fp16(RMSNorm(h[tok]) * gamma) for tokens tok0 .. tok0+15 of rows into
 // LDS (row stride ldl); tokens past the row count are not written (their
 // fragments read as zero).  All threads of the workgroup call it.

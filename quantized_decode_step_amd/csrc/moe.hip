@@ -844,9 +844,24 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(MoeParams p, const ui
         float4v acc[1][XT];
 #pragma unroll
         for (int xt = 0; xt < XT; ++xt) acc[0][xt] = float4v{0.f, 0.f, 0.f, 0.f};
-        // (a one-row workgroup has the registers for one more chunk in flight)
-        kloop_lds<FMT, 1, XT, decltype(stage), MODE == ROUTE_ALL ? 4 : 5>(tp, c0, c1, stage, xl_dyn + tok0 * ldl, ldl, R - tok0, H / 32, lane,
-                                                  acc);
+        if constexpr (MODE != ROUTE_ALL) {
+            if (norm_w) {
+                // one row: its residual slices are requested ahead of the router
+                // weights (they arrive first, and the norm is ready when the
+                // weights are); a one-row workgroup has the registers for one
+                // more chunk in flight
+                RowNormFix<3> rn;
+                auto pre = [&]() { rn.issue(h_in, norm_w, H, r0); };
+                auto fin = [&]() { rn.finish(H, eps, r0, x_out, ldx, xl_dyn); };
+                kloop_lds<FMT, 1, XT, decltype(fin), 5, decltype(pre)>(tp, c0, c1, fin, xl_dyn, ldl, 1, H / 32, lane,
+                                                                       acc, pre);
+            } else {
+                kloop_lds<FMT, 1, XT, decltype(stage), 5>(tp, c0, c1, stage, xl_dyn, ldl, 1, H / 32, lane, acc);
+            }
+        } else {
+            kloop_lds<FMT, 1, XT, decltype(stage), 4>(tp, c0, c1, stage, xl_dyn + tok0 * ldl, ldl, R - tok0, H / 32,
+                                                      lane, acc);
+        }
 #pragma unroll
         for (int xt = 0; xt < XT; ++xt) red[(xt * 16 + wave) * 64 + lane] = acc[0][xt];
         __syncthreads();
