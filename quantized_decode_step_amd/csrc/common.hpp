@@ -170,12 +170,20 @@ OCR_DEV half2v u32_to_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 OCR_DEV uint32_t h2_to_u32(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 
 // Eight Q4_0 codes (one packed dword) -> the eight fp16 values q - 8 (exact).
+// (x & m) | (y & ~m) in one VALU operation: the compiler emits a separate
+// and + or for a mask and a constant that are both literals.
+OCR_DEV uint32_t bit_select(uint32_t m, uint32_t x, uint32_t y) {
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(m), "v"(x), "v"(y));
+    return r;
+}
 OCR_DEV half8v deq_q4(uint32_t dw) {
     const half2v off = {(f16_t)1032.0f, (f16_t)1032.0f};
-    half2v p0 = u32_to_h2((dw & 0x000F000Fu) | 0x64006400u) - off;
-    half2v p1 = u32_to_h2(((dw >> 4) & 0x000F000Fu) | 0x64006400u) - off;
-    half2v p2 = u32_to_h2(((dw >> 8) & 0x000F000Fu) | 0x64006400u) - off;
-    half2v p3 = u32_to_h2(((dw >> 12) & 0x000F000Fu) | 0x64006400u) - off;
+    constexpr uint32_t M = 0x000F000Fu, E = 0x64006400u;
+    half2v p0 = u32_to_h2(bit_select(M, dw, E)) - off;
+    half2v p1 = u32_to_h2(bit_select(M, dw >> 4, E)) - off;
+    half2v p2 = u32_to_h2(bit_select(M, dw >> 8, E)) - off;
+    half2v p3 = u32_to_h2(bit_select(M, dw >> 12, E)) - off;
     uint4 r = {h2_to_u32(p0), h2_to_u32(p1), h2_to_u32(p2), h2_to_u32(p3)};
     return bits_to_half8(r);
 }

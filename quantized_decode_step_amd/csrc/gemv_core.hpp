@@ -126,6 +126,34 @@ OCR_DEV void chunk_mac(const WRegs& w, const half8v (&xa)[Geom<FMT>::SB][XT],
     }
 }
 
+// chunk_mac for the NT tiles of one chunk and one x-tile, block-scaled
+// formats: every tile's block products are issued before any of them is
+// scaled, so the scaling does not wait on the matrix pipe's latency.
+template <int FMT, int NT>
+OCR_DEV void chunk_mac_tiles(const WRegs (&w)[NT], const half8v (&xa)[Geom<FMT>::SB][1],
+                             const float4v (&xs)[Geom<FMT>::SB][1], float4v (&acc)[NT][1]) {
+    constexpr int SB = Geom<FMT>::SB;
+    if constexpr (FMT == OCRDEC_Q4_0 || FMT == OCRDEC_Q8_0) {
+        const float4v zero = {0.f, 0.f, 0.f, 0.f};
+        float4v t[NT][SB];
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int j = 0; j < SB; ++j) t[i][j] = mfma16(xa[j][0], wfrag<FMT>(w[i], j), zero);
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const float d = wscale<FMT>(w[i], j);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[i][0][v] = fmaf(d, t[i][j][v], acc[i][0][v]);
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) chunk_mac<FMT, 1>(w[i], xa, xs, acc[i]);
+    }
+}
+
 // Activation source: token i of the current x-tile set -> fp16 row pointer
 // (row: NULL past the last token; rowc: clamped to the last token, rows >= 1).
 struct XDirect {
@@ -503,6 +531,18 @@ OCR_DEV void lds_xfrags(const uint16_t* xl, int ldl, int ntok, int c, int nblk, 
             if (blk < nblk && tok < ntok) v = *(const uint4*)(xl + tok * ldl + blk * 32 + 8 * (lane >> 4));
             xa[j][xt] = bits_to_half8(v);
         }
+}
+
+// lds_xfrags without range checks, for a k of whole chunks: the LDS rows past
+// the token count hold stale values, which reach only those tokens' outputs
+// (an MFMA output row depends on its own A row alone), and those are never
+// stored.
+template <int FMT>
+OCR_DEV void lds_xfrags_all(const uint16_t* xl, int ldl, int c, int lane, half8v (&xa)[Geom<FMT>::SB][1]) {
+#pragma unroll
+    for (int j = 0; j < Geom<FMT>::SB; ++j)
+        xa[j][0] = bits_to_half8(
+            *(const uint4*)(xl + (lane & 15) * ldl + (c * Geom<FMT>::SB + j) * 32 + 8 * (lane >> 4)));
 }
 
 template <int FMT, int NT>

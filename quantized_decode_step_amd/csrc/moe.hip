@@ -1193,7 +1193,6 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
                                             : p.w_shared + (int64_t)(e - p.n_experts) * p.expert_bytes;
     const int nc = (int)p.nchunks;
     const int total = IPW * nc;
-    const int nblk = p.k / 32;
     auto tile_of = [&](int i, int t) { return (GLU && t == 1) ? g0 + i + p.half_tiles : g0 + i; };
     auto chunk_ptr = [&](int q, int t) {
         const int qc = min(q, total - 1);
@@ -1254,10 +1253,9 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
                 const int c = q % nc;
                 half8v xa[SB][1];
                 float4v xs[SB][1];
-                lds_xfrags<FMT, 1>(xl_dyn, ldl, cnt, c, nblk, lane, xa);
+                lds_xfrags_all<FMT>(xl_dyn, ldl, c, lane, xa);
                 xsums<FMT, 1>(xa, xs);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) chunk_mac<FMT, 1>(wb[u][t], xa, xs, acc[t]);
+                chunk_mac_tiles<FMT, NT>(wb[u], xa, xs, acc);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) load_wchunk<FMT>(chunk_ptr(q + PF, t), lane, wb[u][t]);
                 if (c == nc - 1) {  // item q / nc complete
@@ -1484,7 +1482,7 @@ void launch_grouped_fmt(const GroupedParams& p, int xt, int ks, bool lds, int gr
 constexpr int STREAM_IPW = 2;
 inline int stream_pf(bool glu) { return glu ? 5 : 7; }
 inline bool stream_ok(const GroupedParams& p, bool glu) {
-    return p.groups_per_expert % (4 * STREAM_IPW) == 0 && lds_x_bytes(p.k, 1) <= 65536 &&
+    return p.groups_per_expert % (4 * STREAM_IPW) == 0 && lds_x_bytes(p.k, 1) <= 65536 && p.k % 128 == 0 &&
            (STREAM_IPW * p.nchunks) % stream_pf(glu) == 0;
 }
 template <int FMT, bool GLU>
