@@ -169,22 +169,38 @@ OCR_DEV half8v bits_to_half8(uint4 q) { return __builtin_bit_cast(half8v, q); }
 OCR_DEV half2v u32_to_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 OCR_DEV uint32_t h2_to_u32(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 
-// Eight Q4_0 codes (one packed dword) -> the eight fp16 values q - 8 (exact).
-// (x & m) | (y & ~m) in one VALU operation: the compiler emits a separate
-// and + or for a mask and a constant that are both literals.
-OCR_DEV uint32_t bit_select(uint32_t m, uint32_t x, uint32_t y) {
-    uint32_t r;
-    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(m), "v"(x), "v"(y));
-    return r;
+// (x & m) | c for a constant c with no bits in m, in one VALU operation
+// (v_and_or_b32).  With both m and c literals the compiler emits a separate
+// and + or; an empty asm statement hides c's value, so it is kept in a
+// register and the three-operand form applies.  The asm emits no instruction:
+// the hardware's register-dependency rules stay with the compiler.
+OCR_DEV uint32_t mask_or(uint32_t x, uint32_t m, uint32_t c) {
+    asm("" : "+v"(c));
+    return (x & m) | c;
 }
+
+// Eight Q4_0 codes (one packed dword) -> the eight fp16 values q - 8 (exact).
 OCR_DEV half8v deq_q4(uint32_t dw) {
     const half2v off = {(f16_t)1032.0f, (f16_t)1032.0f};
     constexpr uint32_t M = 0x000F000Fu, E = 0x64006400u;
-    half2v p0 = u32_to_h2(bit_select(M, dw, E)) - off;
-    half2v p1 = u32_to_h2(bit_select(M, dw >> 4, E)) - off;
-    half2v p2 = u32_to_h2(bit_select(M, dw >> 8, E)) - off;
-    half2v p3 = u32_to_h2(bit_select(M, dw >> 12, E)) - off;
+    half2v p0 = u32_to_h2(mask_or(dw, M, E)) - off;
+    half2v p1 = u32_to_h2(mask_or(dw >> 4, M, E)) - off;
+    half2v p2 = u32_to_h2(mask_or(dw >> 8, M, E)) - off;
+    half2v p3 = u32_to_h2(mask_or(dw >> 12, M, E)) - off;
     uint4 r = {h2_to_u32(p0), h2_to_u32(p1), h2_to_u32(p2), h2_to_u32(p3)};
+    return bits_to_half8(r);
+}
+
+// Eight Q4_0 codes (one packed dword) -> the exact fp16 values c_i + n_i of
+// the raw nibbles n_i (q_i + 8), c = {1024, 1024, 64, 64, 1024, 1024, 64, 64}
+// for the eight k positions: a nibble is placed in the mantissa of 1024 (bits
+// 0-3) or, unshifted at bits 4-7, in the mantissa of 64 (whose mantissa step is
+// 1/16), so one shift serves four values.  The bias c_i + 8 is removed through
+// the accumulator input of the block's product (q4_bias_table).
+OCR_DEV half8v deq_q4_biased(uint32_t dw) {
+    constexpr uint32_t M0 = 0x000F000Fu, M1 = 0x00F000F0u, E0 = 0x64006400u, E1 = 0x54005400u;
+    const uint32_t h = dw >> 8;
+    uint4 r = {mask_or(dw, M0, E0), mask_or(dw, M1, E1), mask_or(h, M0, E0), mask_or(h, M1, E1)};
     return bits_to_half8(r);
 }
 

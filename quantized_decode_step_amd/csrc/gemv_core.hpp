@@ -44,12 +44,30 @@ struct WRegs {
 template <int FMT>
 OCR_DEV void load_wchunk(const uint8_t* chunk, int lane, WRegs& r) {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(chunk + lane * 16));
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(chunk + (uint32_t)lane * 16u));
     r.q = make_uint4(v.x, v.y, v.z, v.w);
     if constexpr (FMT == OCRDEC_Q4_0 || FMT == OCRDEC_U8A_G32) {
-        r.s = *(const uint2*)(chunk + 1024 + (lane & 15) * 8);
+        r.s = *(const uint2*)(chunk + 1024u + ((uint32_t)lane & 15u) * 8u);
     } else if constexpr (FMT == OCRDEC_Q8_0) {
-        r.s.x = *(const uint32_t*)(chunk + 1024 + (lane & 15) * 4);
+        r.s.x = *(const uint32_t*)(chunk + 1024u + ((uint32_t)lane & 15u) * 4u);
+        r.s.y = 0;
+    } else {
+        r.s = make_uint2(0, 0);
+    }
+}
+
+// load_wchunk through a buffer resource over the weights (base address in
+// scalar registers) at byte offset soff of the chunk: the lane offsets are
+// fixed, so a load needs no per-lane address arithmetic.
+template <int FMT>
+OCR_DEV void load_wchunk_rs(__amdgpu_buffer_rsrc_t rs, uint32_t soff, int lane, WRegs& r) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, (int)soff, 2 /* nt */);
+    r.q = make_uint4(v[0], v[1], v[2], v[3]);
+    if constexpr (FMT == OCRDEC_Q4_0 || FMT == OCRDEC_U8A_G32) {
+        const auto sv = __builtin_amdgcn_raw_buffer_load_b64(rs, 1024 + (lane & 15) * 8, (int)soff, 0);
+        r.s = make_uint2(sv[0], sv[1]);
+    } else if constexpr (FMT == OCRDEC_Q8_0) {
+        r.s.x = __builtin_amdgcn_raw_buffer_load_b32(rs, 1024 + (lane & 15) * 4, (int)soff, 0);
         r.s.y = 0;
     } else {
         r.s = make_uint2(0, 0);
@@ -151,6 +169,51 @@ OCR_DEV void chunk_mac_tiles(const WRegs (&w)[NT], const half8v (&xa)[Geom<FMT>:
     } else {
 #pragma unroll
         for (int i = 0; i < NT; ++i) chunk_mac<FMT, 1>(w[i], xa, xs, acc[i]);
+    }
+}
+
+// Q4_0 through biased codes (deq_q4_biased): the MFMA of block j forms
+// sum_k x_k (c_k + n_k) starting from the accumulator input -sum_k x_k (c_k + 8),
+// which leaves sum_k x_k q_k; products and the bias sums are exact in fp32, the
+// sums carry the rounding of terms up to 1032 |x|.  nb[j]: that input for the
+// chunk's block j (q4_bias_table); four VALU operations per eight weights
+// fewer than deq_q4 and no separate correction.
+template <int NT>
+OCR_DEV void chunk_mac_q4b(const WRegs (&w)[NT], const half8v (&xa)[4][1], const float4v (&nb)[4],
+                           float4v (&acc)[NT][1]) {
+    float4v t[NT][4];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const uint32_t dw[4] = {w[i].q.x, w[i].q.y, w[i].q.z, w[i].q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[i][j] = mfma16(xa[j][0], deq_q4_biased(dw[j]), nb[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float d = wscale<OCRDEC_Q4_0>(w[i], j);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][0][v] = fmaf(d, t[i][j][v], acc[i][0][v]);
+        }
+}
+
+// The accumulator inputs of chunk_mac_q4b for LDS-staged activations: for
+// every 32-column block j of the k range and token t, tab[16 j + t] =
+// -sum_k x[t][k] (c_k + 8) (an MFMA of the block's activations against that
+// coefficient vector; every column of its result holds the token's sum).
+// Wave w of the workgroup takes blocks w, w + waves, ...; rows past the token
+// count give values that only those tokens' outputs see.  The caller waits for
+// the workgroup afterwards.
+OCR_DEV void q4_bias_table(const uint16_t* xl, int ldl, int nblk, float* tab) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const half8v cv = {(f16_t)-1032.0f, (f16_t)-1032.0f, (f16_t)-72.0f, (f16_t)-72.0f,
+                       (f16_t)-1032.0f, (f16_t)-1032.0f, (f16_t)-72.0f, (f16_t)-72.0f};
+    const float4v zero = {0.f, 0.f, 0.f, 0.f};
+    for (int j = wave; j < nblk; j += nw) {
+        const half8v xa = bits_to_half8(*(const uint4*)(xl + (lane & 15) * ldl + j * 32 + 8 * (lane >> 4)));
+        const float4v u = mfma16(xa, cv, zero);
+        if ((lane & 15) == 0) *(float4v*)(tab + 16 * j + 4 * (lane >> 4)) = u;
     }
 }
 

@@ -1168,7 +1168,9 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
     constexpr int CB = Geom<FMT>::CB, SB = Geom<FMT>::SB;
     constexpr int NT = GLU ? 2 : 1;
     extern __shared__ __align__(16) uint16_t xl_dyn[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // (the wave index read as a scalar: chunk addresses are then scalar bases
+    // plus the lane's fixed offset, with no per-lane 64-bit address math)
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpe = p.groups_per_expert / (4 * IPW);  // workgroups per entry
     const int v = blockIdx.x / wpe;
     const int g0 = (blockIdx.x % wpe) * 4 * IPW + wave * IPW;
@@ -1189,14 +1191,16 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
         off = ent.y;
         cnt = min(ent.z, 16);
     }
+    e = __builtin_amdgcn_readfirstlane(e);  // (uniform: weight addresses stay scalar)
     const uint8_t* base = (e < p.n_experts) ? p.w_routed + (int64_t)e * p.expert_bytes
                                             : p.w_shared + (int64_t)(e - p.n_experts) * p.expert_bytes;
     const int nc = (int)p.nchunks;
     const int total = IPW * nc;
     auto tile_of = [&](int i, int t) { return (GLU && t == 1) ? g0 + i + p.half_tiles : g0 + i; };
-    auto chunk_ptr = [&](int q, int t) {
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7fffffff, 0x00020000);
+    auto chunk_off = [&](int q, int t) {  // byte offset of the wave's chunk q of tile stream t
         const int qc = min(q, total - 1);
-        return base + ((int64_t)tile_of(qc / nc, t) * nc + (qc % nc)) * CB;
+        return (uint32_t)(tile_of(qc / nc, t) * nc + (qc % nc)) * (uint32_t)CB;
     };
     // residual-adding down projection: rows and weights of this lane's slots
     int hrow[4];
@@ -1233,10 +1237,15 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
 #pragma unroll
     for (int u = 0; u < PF; ++u)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) load_wchunk<FMT>(chunk_ptr(u, t), lane, wb[u][t]);
+        for (int t = 0; t < NT; ++t) load_wchunk_rs<FMT>(wrs, chunk_off(u, t), lane, wb[u][t]);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<PF * NT * (FMT == OCRDEC_F16 ? 1 : 2)>();  // everything but the ring: the rows are in LDS
     __syncthreads();
+    float* btab = (float*)(xl_dyn + 16 * ldl);  // Q4_0: the blocks' accumulator inputs, after the rows
+    if constexpr (FMT == OCRDEC_Q4_0) {
+        q4_bias_table(xl_dyn, ldl, p.k / 32, btab);
+        __syncthreads();
+    }
     float4v acc[NT][1];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t][0] = float4v{0.f, 0.f, 0.f, 0.f};
@@ -1254,10 +1263,17 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
                 half8v xa[SB][1];
                 float4v xs[SB][1];
                 lds_xfrags_all<FMT>(xl_dyn, ldl, c, lane, xa);
-                xsums<FMT, 1>(xa, xs);
-                chunk_mac_tiles<FMT, NT>(wb[u], xa, xs, acc);
+                if constexpr (FMT == OCRDEC_Q4_0) {
+                    float4v nb[4];
 #pragma unroll
-                for (int t = 0; t < NT; ++t) load_wchunk<FMT>(chunk_ptr(q + PF, t), lane, wb[u][t]);
+                    for (int j = 0; j < 4; ++j) nb[j] = *(const float4v*)(btab + 16 * (4 * c + j) + 4 * (lane >> 4));
+                    chunk_mac_q4b<NT>(wb[u], xa, nb, acc);
+                } else {
+                    xsums<FMT, 1>(xa, xs);
+                    chunk_mac_tiles<FMT, NT>(wb[u], xa, xs, acc);
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t) load_wchunk_rs<FMT>(wrs, chunk_off(q + PF, t), lane, wb[u][t]);
                 if (c == nc - 1) {  // item q / nc complete
                     const int i = q / nc;
 #pragma unroll
@@ -1481,15 +1497,18 @@ void launch_grouped_fmt(const GroupedParams& p, int xt, int ks, bool lds, int gr
 // most 16 tokens staged in LDS; the ring depth must divide the stream.
 constexpr int STREAM_IPW = 2;
 inline int stream_pf(bool glu) { return glu ? 5 : 7; }
+// LDS of the streamed kernels: 16 staged rows, then (Q4_0) 16 floats per
+// 32-column block
+inline size_t stream_lds_bytes(int k) { return lds_x_bytes(k, 1) + (size_t)(k / 32) * 64; }
 inline bool stream_ok(const GroupedParams& p, bool glu) {
-    return p.groups_per_expert % (4 * STREAM_IPW) == 0 && lds_x_bytes(p.k, 1) <= 65536 && p.k % 128 == 0 &&
+    return p.groups_per_expert % (4 * STREAM_IPW) == 0 && stream_lds_bytes(p.k) <= 65536 && p.k % 128 == 0 &&
            (STREAM_IPW * p.nchunks) % stream_pf(glu) == 0;
 }
 template <int FMT, bool GLU>
 void launch_stream_t(const GroupedParams& p, hipStream_t s) {
     constexpr int PF = GLU ? 5 : 7;  // = stream_pf(GLU)
     const int grid = p.max_virt * (p.groups_per_expert / (4 * STREAM_IPW));
-    const size_t lb = lds_x_bytes(p.k, 1);
+    const size_t lb = stream_lds_bytes(p.k);
     if (p.pidx) {
         if (GLU) hipLaunchKernelGGL((grouped_stream_kernel<FMT, GLU, false, STREAM_IPW, PF, true>), dim3(grid), dim3(256), lb, s, p);
         else hipLaunchKernelGGL((grouped_stream_kernel<FMT, GLU, true, STREAM_IPW, PF, true>), dim3(grid), dim3(256), lb, s, p);
@@ -1501,13 +1520,12 @@ void launch_grouped(int fmt, bool glu, GroupedParams p, int rows_hint, hipStream
     const int64_t items = (int64_t)p.max_virt * p.groups_per_expert;
     // (expert-indexed entries: one wave per item)
     const int ks = (items >= 2048 || p.pidx) ? 1 : 4;
-    // gate/up of decode batches from 10 rows: the streamed form (entries of at
+    // gate/up of decode batches from 6 rows: the streamed form (entries of at
     // most 16 tokens, staged in LDS).  It halves the workgroups, which pays
     // once they exceed the CUs' workgroup slots (two per CU for the one-item
-    // form): measured at 12, 16 and 24 rows (step 1.110 -> 1.100, 1.258 ->
-    // 1.237 ms; gate/up 31.9 -> 28.0 us at 24), even at 8 rows, slower at 6
-    // (0.851 -> 0.869 ms).
-    if (glu && rows_hint >= 10 && p.entries16 && ks == 1 && stream_ok(p, true) && use_lds_x(p.k, 1, rows_hint)) {
+    // form), and its Q4_0 loop (biased codes) has the fewest VALU operations
+    // per weight: gate/up 15.3 -> 13.5 us at 6 rows, 17.4 -> 15.7 at 8.
+    if (glu && rows_hint >= 6 && p.entries16 && ks == 1 && stream_ok(p, true) && use_lds_x(p.k, 1, rows_hint)) {
         switch (fmt) {
         case OCRDEC_F16: launch_stream_t<OCRDEC_F16, true>(p, s); return;
         case OCRDEC_Q8_0: launch_stream_t<OCRDEC_Q8_0, true>(p, s); return;
