@@ -191,16 +191,26 @@ OCR_DEV half8v deq_q4(uint32_t dw) {
     return bits_to_half8(r);
 }
 
-// Eight Q4_0 codes (one packed dword) -> the exact fp16 values c_i + n_i of
-// the raw nibbles n_i (q_i + 8), c = {1024, 1024, 64, 64, 1024, 1024, 64, 64}
-// for the eight k positions: a nibble is placed in the mantissa of 1024 (bits
-// 0-3) or, unshifted at bits 4-7, in the mantissa of 64 (whose mantissa step is
-// 1/16), so one shift serves four values.  The bias c_i + 8 is removed through
-// the accumulator input of the block's product (q4_bias_table).
-OCR_DEV half8v deq_q4_biased(uint32_t dw) {
-    constexpr uint32_t M0 = 0x000F000Fu, M1 = 0x00F000F0u, E0 = 0x64006400u, E1 = 0x54005400u;
+// Eight Q4_0 codes (one packed dword) -> their raw nibbles n_i = q_i + 8 as
+// fp16 subnormals, n_i * 2^-24 exactly (the matrix cores take subnormal fp16
+// operands at their value): four masks and three shifts, no conversion.  The
+// products with fp16 activations are exact in fp32; the offset 8 and the
+// factor 2^-24 are taken out through the accumulator (q4_bias, Q4_RAW_SCALE).
+OCR_DEV half8v deq_q4_raw(uint32_t dw) {
+    constexpr uint32_t M = 0x000F000Fu;
+    uint4 r = {dw & M, (dw >> 4) & M, (dw >> 8) & M, (dw >> 12) & M};
+    return bits_to_half8(r);
+}
+constexpr float Q4_RAW_SCALE = 16777216.0f;  // 2^24
+
+// The same codes with one shift per dword: positions 0, 1, 4, 5 hold
+// n * 2^-24 and positions 2, 3, 6, 7 (nibbles left at bits 4-7) hold
+// 16 n * 2^-24, for activations whose positions 2, 3, 6, 7 were divided by 16
+// (q4_split_prepare), which makes every product x n 2^-24 again.
+OCR_DEV half8v deq_q4_split(uint32_t dw) {
+    constexpr uint32_t M0 = 0x000F000Fu, M1 = 0x00F000F0u;
     const uint32_t h = dw >> 8;
-    uint4 r = {mask_or(dw, M0, E0), mask_or(dw, M1, E1), mask_or(h, M0, E0), mask_or(h, M1, E1)};
+    uint4 r = {dw & M0, dw & M1, h & M0, h & M1};
     return bits_to_half8(r);
 }
 

@@ -311,6 +311,11 @@ __global__ __launch_bounds__(64 * LM_WAVES, 1) void lm_argmax_kernel(GemvParams 
     if (p.hn) stage_norm(p.hn, p.gamma, p.eps, R, 0, p.k, xl_dyn, ldl);
     else stage_x(p.xs, 0, 16, p.k, xl_dyn, ldl);
     __syncthreads();
+    float* btab = (float*)(xl_dyn + 16 * ldl);  // Q4_0: the blocks' accumulator inputs, after the rows
+    if constexpr (FMT == OCRDEC_Q4_0) {
+        q4_split_prepare(xl_dyn, ldl, R, nblk, nc * 4, btab);
+        __syncthreads();
+    }
     auto grab = [&]() {
         int u = 0;
         if (lane == 0) u = atomicAdd(&next_s, 1);
@@ -338,14 +343,22 @@ __global__ __launch_bounds__(64 * LM_WAVES, 1) void lm_argmax_kernel(GemvParams 
                 half8v xa[SB][1];
                 float4v xs[SB][1];
                 lds_xfrags<FMT, 1>(xl_dyn, ldl, R, c, nblk, lane, xa);
-                xsums<FMT, 1>(xa, xs);
-                chunk_mac<FMT, 1>(ring[s], xa, xs, acc[0]);
+                if constexpr (FMT == OCRDEC_Q4_0) {
+                    float4v nb[4][1];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) nb[j][0] = *(const float4v*)(btab + 16 * (4 * c + j) + 4 * (lane >> 4));
+                    chunk_mac_q4b<1, 1, true>(&ring[s], xa, nb, acc);
+                } else {
+                    xsums<FMT, 1>(xa, xs);
+                    chunk_mac<FMT, 1>(ring[s], xa, xs, acc[0]);
+                }
                 // refill the slot with the chunk PF further on in the stream
                 // (the next tile's, past this one's end; nc % PF == 0)
                 const int cf = c + PF;
                 load_wchunk<FMT>(cf < nc ? tc + (int64_t)cf * CB : tn + (int64_t)(cf - nc) * CB, lane, ring[s]);
             }
         }
+        if constexpr (FMT == OCRDEC_Q4_0) scale_acc<1, 1>(acc, Q4_RAW_SCALE);  // (raw codes)
         const int row = (t0 + ucur) * 16 + (lane & 15);
         if (row < p.n) {
 #pragma unroll
@@ -424,7 +437,9 @@ LmPlan plan_lm(int fmt, int n, int k, int rows) {
     LmPlan lp;
     const int pf = lm_pf(fmt, k);
     const int ntiles = (n + 15) / 16;
-    const size_t xb = (size_t)16 * (k + 8) * 2;  // the staged activations (row stride k + 8)
+    // the staged activations (row stride k + 8), then for Q4_0 16 floats per
+    // 32-column block of the padded k range
+    const size_t xb = (size_t)16 * (k + 8) * 2 + (fmt == OCRDEC_Q4_0 ? (size_t)n_chunks(fmt, k) * 4 * 64 : 0);
     lp.dyn = rows <= 16 && pf > 0 && xb <= LM_LDS && ntiles >= 8 * device_cus();
     lp.grid = lp.dyn ? device_cus() : plan_gemv(fmt, n, k, rows, EPI_ARGMAX).grid;
     return lp;

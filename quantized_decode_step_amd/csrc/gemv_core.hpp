@@ -172,47 +172,129 @@ OCR_DEV void chunk_mac_tiles(const WRegs (&w)[NT], const half8v (&xa)[Geom<FMT>:
     }
 }
 
-// Q4_0 through biased codes (deq_q4_biased): the MFMA of block j forms
-// sum_k x_k (c_k + n_k) starting from the accumulator input -sum_k x_k (c_k + 8),
-// which leaves sum_k x_k q_k; products and the bias sums are exact in fp32, the
-// sums carry the rounding of terms up to 1032 |x|.  nb[j]: that input for the
-// chunk's block j (q4_bias_table); four VALU operations per eight weights
-// fewer than deq_q4 and no separate correction.
-template <int NT>
-OCR_DEV void chunk_mac_q4b(const WRegs (&w)[NT], const half8v (&xa)[4][1], const float4v (&nb)[4],
-                           float4v (&acc)[NT][1]) {
-    float4v t[NT][4];
+// Q4_0 through raw codes (deq_q4_raw): the MFMA of block j forms
+// 2^-24 sum_k x_k n_k starting from the accumulator input -2^-24 * 8 sum_k x_k,
+// which leaves 2^-24 sum_k x_k q_k; the block scale is applied as for the
+// other formats and the accumulators carry the factor 2^-24 until the k-loop
+// ends (q4_unscale).  nb[j][xt]: that input for the chunk's block j and
+// x-tile xt.  Seven VALU operations per eight weights, against eleven with
+// deq_q4.
+// SPLIT: the codes of deq_q4_split, for activations prepared by
+// q4_split_prepare (five VALU operations per eight weights).
+template <int NT, int XT, bool SPLIT = false>
+OCR_DEV void chunk_mac_q4b(const WRegs* w, const half8v (&xa)[4][XT], const float4v (&nb)[4][XT],
+                           float4v (&acc)[NT][XT]) {
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         const uint32_t dw[4] = {w[i].q.x, w[i].q.y, w[i].q.z, w[i].q.w};
+        float4v t[4][XT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) t[i][j] = mfma16(xa[j][0], deq_q4_biased(dw[j]), nb[j]);
-    }
+        for (int j = 0; j < 4; ++j) {
+            const half8v b = SPLIT ? deq_q4_split(dw[j]) : deq_q4_raw(dw[j]);
 #pragma unroll
-    for (int i = 0; i < NT; ++i)
+            for (int xt = 0; xt < XT; ++xt) t[j][xt] = mfma16(xa[j][xt], b, nb[j][xt]);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float d = wscale<OCRDEC_Q4_0>(w[i], j);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[i][0][v] = fmaf(d, t[i][j][v], acc[i][0][v]);
+            for (int xt = 0; xt < XT; ++xt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[i][xt][v] = fmaf(d, t[j][xt][v], acc[i][xt][v]);
         }
+    }
 }
 
-// The accumulator inputs of chunk_mac_q4b for LDS-staged activations: for
-// every 32-column block j of the k range and token t, tab[16 j + t] =
-// -sum_k x[t][k] (c_k + 8) (an MFMA of the block's activations against that
-// coefficient vector; every column of its result holds the token's sum).
-// Wave w of the workgroup takes blocks w, w + waves, ...; rows past the token
-// count give values that only those tokens' outputs see.  The caller waits for
-// the workgroup afterwards.
-OCR_DEV void q4_bias_table(const uint16_t* xl, int ldl, int nblk, float* tab) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    const half8v cv = {(f16_t)-1032.0f, (f16_t)-1032.0f, (f16_t)-72.0f, (f16_t)-72.0f,
-                       (f16_t)-1032.0f, (f16_t)-1032.0f, (f16_t)-72.0f, (f16_t)-72.0f};
+// Multiplies accumulators by s (a power of two: exact).
+template <int NT, int XT>
+OCR_DEV void scale_acc(float4v (&acc)[NT][XT], float s) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int xt = 0; xt < XT; ++xt) acc[i][xt] *= s;
+}
+
+// -2^-24 * 8 * sum_k x[t][k] for one block's A fragment: an MFMA against the
+// constant -2^-21 (an exact fp16 subnormal); every column of the result holds
+// the token's sum.
+OCR_DEV float4v q4_bias(const half8v& xa) {
+    const uint4 c = {0x80088008u, 0x80088008u, 0x80088008u, 0x80088008u};
     const float4v zero = {0.f, 0.f, 0.f, 0.f};
-    for (int j = wave; j < nblk; j += nw) {
-        const half8v xa = bits_to_half8(*(const uint4*)(xl + (lane & 15) * ldl + j * 32 + 8 * (lane >> 4)));
-        const float4v u = mfma16(xa, cv, zero);
+    return mfma16(xa, bits_to_half8(c), zero);
+}
+
+// chunk_mac for the NT tiles of one chunk.  Q4_0 with one x-tile takes the
+// raw codes, with the bias of each block formed once for all tiles (the
+// accumulators then carry the factor 2^-24: the k-loop brackets its chunks
+// with q4_scale / q4_unscale); the rest run chunk_mac per tile.
+template <int FMT, int XT>
+constexpr bool q4_raw_path() { return FMT == OCRDEC_Q4_0 && XT == 1; }
+template <int FMT, int NT, int XT>
+OCR_DEV void q4_scale(float4v (&acc)[NT][XT]) {
+    if constexpr (q4_raw_path<FMT, XT>()) scale_acc<NT, XT>(acc, 1.0f / Q4_RAW_SCALE);
+}
+template <int FMT, int NT, int XT>
+OCR_DEV void q4_unscale(float4v (&acc)[NT][XT]) {
+    if constexpr (q4_raw_path<FMT, XT>()) scale_acc<NT, XT>(acc, Q4_RAW_SCALE);
+}
+template <int FMT, int NT, int XT>
+OCR_DEV void chunk_mac_nt(const WRegs* w, const half8v (&xa)[Geom<FMT>::SB][XT],
+                          const float4v (&xs)[Geom<FMT>::SB][XT], float4v (&acc)[NT][XT]) {
+    if constexpr (q4_raw_path<FMT, XT>()) {
+        // block by block (all products of a chunk at once would not fit the
+        // k-loops' register budgets; with two x-tiles neither does the
+        // bias, and deq_q4 serves).  The caller's loop ends with q4_unscale.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float4v nb[XT];
+#pragma unroll
+            for (int xt = 0; xt < XT; ++xt) nb[xt] = q4_bias(xa[j][xt]);
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const uint32_t dw = j == 0 ? w[i].q.x : j == 1 ? w[i].q.y : j == 2 ? w[i].q.z : w[i].q.w;
+                const half8v b = deq_q4_raw(dw);
+                const float d = wscale<OCRDEC_Q4_0>(w[i], j);
+#pragma unroll
+                for (int xt = 0; xt < XT; ++xt) {
+                    const float4v t = mfma16(xa[j][xt], b, nb[xt]);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[i][xt][v] = fmaf(d, t[v], acc[i][xt][v]);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) chunk_mac<FMT, XT>(w[i], xa, xs, acc[i]);
+    }
+}
+
+// For chunk_mac_q4b<.., SPLIT> over LDS-staged activations, once per
+// workgroup: divides positions 2, 3, 6, 7 of every 8-column group of the
+// staged rows by 16 in place (exact for normal results; a value below 2^-10
+// keeps its subnormal quotient's 2^-25 absolute rounding) and writes
+// tab[16 j + t] = -2^-24 * 8 * sum_k x[t][k] of block j and token t over the
+// values as stored (an MFMA against -2^-21 at positions 0, 1, 4, 5 and -2^-17
+// at the divided ones), for blocks j < nblk_pad; blocks from nblk on and
+// tokens from ntok on give 0.  Each lane rewrites exactly the piece it then
+// reads; wave w takes blocks w, w + waves, ...  The caller waits for the
+// workgroup afterwards.
+OCR_DEV void q4_split_prepare(uint16_t* xl, int ldl, int ntok, int nblk, int nblk_pad, float* tab) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const uint4 cu = {0x80088008u, 0x80808080u, 0x80088008u, 0x80808080u};
+    const half8v coef = bits_to_half8(cu);
+    const half2v sixteenth = {(f16_t)0.0625f, (f16_t)0.0625f};
+    const float4v zero = {0.f, 0.f, 0.f, 0.f};
+    for (int j = wave; j < nblk_pad; j += nw) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (j < nblk) {
+            uint4* pc = (uint4*)(xl + (lane & 15) * ldl + j * 32 + 8 * (lane >> 4));
+            v = *pc;
+            v.y = h2_to_u32(u32_to_h2(v.y) * sixteenth);
+            v.w = h2_to_u32(u32_to_h2(v.w) * sixteenth);
+            *pc = v;
+            if ((lane & 15) >= ntok) v = make_uint4(0, 0, 0, 0);
+        }
+        const float4v u = mfma16(bits_to_half8(v), coef, zero);
         if ((lane & 15) == 0) *(float4v*)(tab + 16 * j + 4 * (lane >> 4)) = u;
     }
 }
@@ -307,6 +389,7 @@ OCR_DEV void kloop(const uint8_t* const (&tile)[NT], int c0, int c1, const XS& x
     const int n = __builtin_amdgcn_readfirstlane(c1 - c0);
     const int cb = __builtin_amdgcn_readfirstlane(c0);
     if (n <= 0) return;
+    q4_scale<FMT, NT, XT>(acc);
     WRegs wb[PF][NT];
     half8v xb[PF][SB][XT];
     auto fetch = [&](int u, int c) {
@@ -318,8 +401,7 @@ OCR_DEV void kloop(const uint8_t* const (&tile)[NT], int c0, int c1, const XS& x
         mask_xfrags<FMT, XT>(xs, tok0, cb + c, nblk, lane, xb[u]);
         float4v xsum[SB][XT];
         xsums<FMT, XT>(xb[u], xsum);
-#pragma unroll
-        for (int i = 0; i < NT; ++i) chunk_mac<FMT, XT>(wb[u][i], xb[u], xsum, acc[i]);
+        chunk_mac_nt<FMT, NT, XT>(wb[u], xb[u], xsum, acc);
     };
 #pragma unroll
     for (int u = 0; u < PF; ++u) fetch(u, min(u, n - 1));
@@ -343,6 +425,7 @@ OCR_DEV void kloop(const uint8_t* const (&tile)[NT], int c0, int c1, const XS& x
 #pragma unroll
     for (int u = 0; u < PF; ++u)
         if (it + PF + u < n) use(u, it + PF + u);
+    q4_unscale<FMT, NT, XT>(acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -655,6 +738,7 @@ OCR_DEV void kloop_lds(const uint8_t* const (&tile)[NT], int c0, int c1, STAGE s
     if constexpr (PRE_ISSUES) __builtin_amdgcn_sched_barrier(0);
     stage();
     __syncthreads();
+    q4_scale<FMT, NT, XT>(acc);
     for (int c = c0; c < c1; c += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
@@ -664,8 +748,7 @@ OCR_DEV void kloop_lds(const uint8_t* const (&tile)[NT], int c0, int c1, STAGE s
                 float4v xsum[SB][XT];
                 lds_xfrags<FMT, XT>(xl, ldl, ntok, cc, nblk, lane, xa);
                 xsums<FMT, XT>(xa, xsum);
-#pragma unroll
-                for (int i = 0; i < NT; ++i) chunk_mac<FMT, XT>(wb[u][i], xa, xsum, acc[i]);
+                chunk_mac_nt<FMT, NT, XT>(wb[u], xa, xsum, acc);
                 if (cc + PF < c1) {
 #pragma unroll
                     for (int i = 0; i < NT; ++i)
@@ -674,6 +757,7 @@ OCR_DEV void kloop_lds(const uint8_t* const (&tile)[NT], int c0, int c1, STAGE s
             }
         }
     }
+    q4_unscale<FMT, NT, XT>(acc);
 }
 
 // LDS bytes for 16*xt tokens of k activations.  The LDS path is used when it

@@ -1243,7 +1243,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
     __syncthreads();
     float* btab = (float*)(xl_dyn + 16 * ldl);  // Q4_0: the blocks' accumulator inputs, after the rows
     if constexpr (FMT == OCRDEC_Q4_0) {
-        q4_bias_table(xl_dyn, ldl, p.k / 32, btab);
+        q4_split_prepare(xl_dyn, ldl, cnt, p.k / 32, p.k / 32, btab);
         __syncthreads();
     }
     float4v acc[NT][1];
@@ -1264,10 +1264,10 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
                 float4v xs[SB][1];
                 lds_xfrags_all<FMT>(xl_dyn, ldl, c, lane, xa);
                 if constexpr (FMT == OCRDEC_Q4_0) {
-                    float4v nb[4];
+                    float4v nb[4][1];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) nb[j] = *(const float4v*)(btab + 16 * (4 * c + j) + 4 * (lane >> 4));
-                    chunk_mac_q4b<NT>(wb[u], xa, nb, acc);
+                    for (int j = 0; j < 4; ++j) nb[j][0] = *(const float4v*)(btab + 16 * (4 * c + j) + 4 * (lane >> 4));
+                    chunk_mac_q4b<NT, 1, true>(wb[u], xa, nb, acc);
                 } else {
                     xsums<FMT, 1>(xa, xs);
                     chunk_mac_tiles<FMT, NT>(wb[u], xa, xs, acc);
@@ -1276,6 +1276,7 @@ __global__ __launch_bounds__(256, 2) void grouped_stream_kernel(GroupedParams p)
                 for (int t = 0; t < NT; ++t) load_wchunk_rs<FMT>(wrs, chunk_off(q + PF, t), lane, wb[u][t]);
                 if (c == nc - 1) {  // item q / nc complete
                     const int i = q / nc;
+                    if constexpr (FMT == OCRDEC_Q4_0) scale_acc<NT, 1>(acc, Q4_RAW_SCALE);  // (raw codes)
 #pragma unroll
                     for (int vv = 0; vv < 4; ++vv) {
                         const int tok = 4 * (lane >> 4) + vv;
