@@ -399,6 +399,12 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(model, d, args.cpu_seconds, T0)
+        # the same on one host thread: one whole step
+        try:
+            one = cpu_baseline(model, d, 0.0, T0, threads=1)
+            cpu["single_thread"] = {k_: one[k_] for k_ in ("value", "cores", "sample")}
+        except ImportError:
+            pass
         # the oracle at every swept row count: one whole step of R rows each
         if not args.no_cpu_sweep:
             for s_ in sweep:
@@ -838,9 +844,14 @@ def lm_only(args, dm, d, q, torch, dev, stream):
                       "copy_bytes": n, "copy_launches": 3}), flush=True)
 
 
-def cpu_baseline(model, d, budget_s: float, T0: int, rows: int = 1):
+def cpu_baseline(model, d, budget_s: float, T0: int, rows: int = 1, threads: int = 0):
     """The oracle, as it stands, on `rows` rows of the same workload: as many
-    whole steps as fit in the budget (at least one)."""
+    whole steps as fit in the budget (at least one); with `threads`, its BLAS
+    limited to that many threads."""
+    if threads:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=threads):
+            return cpu_baseline(model, d, budget_s, T0, rows)
     import synth
     import oracle as O
     try:

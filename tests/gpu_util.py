@@ -1,6 +1,6 @@
 """Helpers shared by the GPU parity tests (comparison rules, device uploads).
 
-Comparison rule for floating point (derived in the design doc):
+Comparison rule for floating point:
   * fp32 outputs: max |gpu - oracle| <= 2e-3 * rms(oracle).
   * fp16-stored outputs: every element within 2e-3 * rms(oracle) + one fp16
     ulp of the oracle's value.  Both sides compute the same real number up to
@@ -74,12 +74,17 @@ def from_f16_tensor(t) -> np.ndarray:
     return t.cpu().numpy().view(np.float16).astype(np.float64)
 
 
+# near-ties accepted in this session (the parity report lists them)
+NEAR_TIES = []
+
+
 def log_near_tie(kind: str, what: str, gap: float):
     """Records an accepted near-tie (a routing or argmax decision that differs
     from the oracle's where the oracle's own gap is below the threshold) in
     the JSONL log named by OCRDEC_NEAR_TIE_LOG (default
     gpurun_out/near_ties.jsonl) and on stdout."""
     rec = {"kind": kind, "case": what, "oracle_gap": float(gap)}
+    NEAR_TIES.append(rec)
     print("[near-tie]", json.dumps(rec), flush=True)
     path = os.environ.get("OCRDEC_NEAR_TIE_LOG", os.path.join("gpurun_out", "near_ties.jsonl"))
     try:
