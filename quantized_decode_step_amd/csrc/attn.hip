@@ -389,17 +389,20 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnParams p) {
     p.out[(int64_t)r * p.ld_out + h * D + tid] = f2h(o / red[1]);
 }
 
-// Decode of up to 16 rows with head_dim 128: the merge of each head's
+// Decode of up to 24 rows with head_dim 128: the merge of each head's
 // splits and that head's share of the O projection in one launch, in place
 // of the merge kernel, a launch gap and the O projection's GEMV.  Workgroup
-// (g, hd) merges head hd of every row (thread group r takes rows r, r + 4, ..., as
-// attn_combine_kernel: the partials requested before the window is known)
-// into LDS; its eight wavefronts then multiply the merged row with the
-// head's D columns of W_o for the 16-row tiles 8g .. 8g+7 (one tile each;
-// the weights were requested before the merge) and add the products into
-// the fixed-point residual with atomic integer adds: the residual receives one
-// addend per head in the order the workgroups finish, and the integer sum is
-// the same in any order.
+// (g, hd, z) takes rows 4z .. 4z+3: thread group rg (128 threads) merges
+// head hd of row 4z + rg (as attn_combine_kernel: the partials requested
+// before the window is known) into LDS; its eight wavefronts then multiply
+// the merged rows with the head's D columns of W_o for the 16-row tiles
+// 8g .. 8g+7 (one tile each; the weights were requested before the merge) and
+// add the products into the fixed-point residual with atomic integer adds:
+// the residual receives one addend per head in the order the workgroups
+// finish, and the integer sum is the same in any order.  Rows in groups of
+// four over the grid (rather than passes of four in one workgroup) keep every
+// merge to one round of dependent loads; each group reads the head's W_o
+// columns again, from cache.
 template <int FMT>
 __global__ __launch_bounds__(512) void attn_merge_o_kernel(AttnParams p, const uint8_t* wo, int n_out, int64_t nchunks,
                                                            fix_t* h, int64_t ldh, uint32_t* status) {
@@ -408,13 +411,14 @@ __global__ __launch_bounds__(512) void attn_merge_o_kernel(AttnParams p, const u
     __shared__ float f_s[4][1024 + 1];
     __shared__ float red[4], l2[4][2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = blockIdx.x, hd = blockIdx.y;
+    const int g = blockIdx.x, hd = blockIdx.y, rbase = 4 * blockIdx.z;
+    const int nr = min(4, p.rows - rbase);  // rows of this workgroup (>= 1)
     const int rg = tid >> 7, t = tid & 127;
     const int ldl = p.n_heads * D + 8;
-    // thread group rg merges rows rg, rg + 4, ... (passes of four rows)
+    // thread group rg merges row rbase + rg into LDS row rg
     auto merge_row = [&](int rr) {
-        const bool act = rr < p.rows;
-        const int r = act ? rr : 0;
+        const bool act = rr < nr;
+        const int r = act ? rbase + rr : rbase;
         const int ns = p.n_split;
         const float* part0 = p.part + ((int64_t)r * p.n_heads + hd) * ns * (D + 2);
         const float mv = (act && t < ns) ? part0[t * (D + 2) + D] : -INFINITY;
@@ -457,31 +461,27 @@ __global__ __launch_bounds__(512) void attn_merge_o_kernel(AttnParams p, const u
         for (int i = PRE; i < n_used; ++i) o = fmaf(part0[i * (D + 2) + t], fs[i], o);
         if (act) xl[rr * ldl + hd * D + t] = f2h(o / (l2[rg][0] + l2[rg][1]));
     };
-    auto merge = [&]() {
-        merge_row(rg);
-        for (int r0 = 4; r0 < p.rows; r0 += 4) {
-            __syncthreads();  // this group's LDS scratch is reused
-            merge_row(r0 + rg);
-        }
-    };
+    auto merge = [&]() { merge_row(rg); };
     const int tile = g * 8 + wave;
     const bool on = tile * 16 < n_out;
     const uint8_t* tp[1] = {wo + (int64_t)(on ? tile : 0) * nchunks * Geom<FMT>::CB};
     const int c0 = hd * CPH, c1 = on ? c0 + CPH : c0;
     float4v acc[1][1] = {{float4v{0.f, 0.f, 0.f, 0.f}}};
-    kloop_lds<FMT, 1, 1, decltype(merge), CPH>(tp, c0, c1, merge, xl, ldl, p.rows, p.n_heads * D / 32, lane, acc);
+    kloop_lds<FMT, 1, 1, decltype(merge), CPH>(tp, c0, c1, merge, xl, ldl, nr, p.n_heads * D / 32, lane, acc);
     if (!on) return;
     bool bad = false;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int tok = 4 * (lane >> 4) + v, row = tile * 16 + (lane & 15);
-        if (tok < p.rows && row < n_out) fix_atomic_add(h + (int64_t)tok * ldh + row, acc[0][0][v], bad);
+        if (tok < nr && row < n_out) fix_atomic_add(h + (int64_t)(rbase + tok) * ldh + row, acc[0][0][v], bad);
     }
     report_status(status, bad, kStatResidual);
 }
 
 bool attn_merge_o_ok(const AttnParams& p, int fmt, int n_out) {
-    if (p.rows < 1 || p.rows > 16 || p.head_dim != 128 || n_out % 16 != 0) return false;
+    // up to 24 rows (600 workgroups of 512 threads at 24; with 32 rows the
+    // grid needs a second round and the merge kernel + O GEMV is as fast)
+    if (p.rows < 1 || p.rows > 24 || p.head_dim != 128 || n_out % 16 != 0) return false;
     return fmt == OCRDEC_F16 || fmt == OCRDEC_Q8_0 || fmt == OCRDEC_Q4_0 || fmt == OCRDEC_U8A_G32;
 }
 
@@ -496,8 +496,8 @@ void launch_attn_merge_o(const AttnParams& p0, int fmt, const uint8_t* wo, int n
     prof_mark(s, OCRDEC_K_ATTN_MERGE_O);
     const int HD = p.n_heads * 128;
     const int64_t nch = n_chunks(fmt, HD);
-    const size_t lds = (size_t)p.rows * (HD + 8) * 2;
-    dim3 g2((n_out / 16 + 7) / 8, p.n_heads);
+    const size_t lds = (size_t)std::min(p.rows, 4) * (HD + 8) * 2;
+    dim3 g2((n_out / 16 + 7) / 8, p.n_heads, (p.rows + 3) / 4);
 #define OCR_MO(F_) \
     case F_: hipLaunchKernelGGL(attn_merge_o_kernel<F_>, g2, dim3(512), lds, s, p, wo, n_out, nch, h, ldh, status); break;
     switch (fmt) {

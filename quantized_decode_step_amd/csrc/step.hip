@@ -506,11 +506,11 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     ap0.part = w.attn_part;
     attn_set_rope(ap0, m->rope_theta);
     // Up to 16 rows: the kernels that consume a normalised residual (QKV,
-    // the dense MLP, the language head) form RMSNorm(h) in their LDS staging,
-    // the attention merge runs inside the O projection and the MoE down
-    // projection adds its weighted outputs into the residual, so no separate
-    // norm, merge or combine kernel runs.  (With more rows the per-consumer
-    // norms cost more than the kernels they replace.)
+    // the dense MLP, the language head) form RMSNorm(h) in their LDS staging
+    // and the MoE down projection adds its weighted outputs into the residual,
+    // so no separate norm or combine kernel runs.  (With more rows the
+    // per-consumer norms cost more than the kernels they replace.)  Up to 24
+    // rows the attention merge runs inside the O projection.
     const bool prolog = R <= 16 && lds_x_bytes(H, 1) <= 65536;
     int moe_l = 0;
     for (int l = 0; l < m->n_layers; ++l) {
@@ -535,7 +535,7 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
             prof_mark(s, OCRDEC_K_QKV);
             launch_gemv(L.wqkv.fmt, EPI_F32, pl, gp, s);
         }
-        // attention, and the O projection + residual (up to 16 rows: the
+        // attention, and the O projection + residual (up to 24 rows: the
         // merge of the splits and the projection are one launch)
         AttnParams ap = ap0;
         ap.k_cache = L.k_cache;

@@ -161,13 +161,14 @@ def test_step_small_rows_32(q):
 
 
 # Launch paths by row count: up to 16 rows the norms are formed inside the
-# consuming kernels and the attention merge runs inside the O projection;
-# from 17 rows the separate merge, O projection and norm kernels run; up to
-# 32 rows the MoE down projection adds into the residual itself.  One row
+# consuming kernels, from 17 rows the separate norm kernels run; up to 24
+# rows the attention merge runs inside the O projection (in workgroups of four
+# rows), from 25 rows the separate merge and O projection run; up to 32 rows
+# the MoE down projection adds into the residual itself.  One row
 # takes the single-row grouping.  Shared-expert counts 0..2 and top-k 1..8
 # exercise the slot lists.
 @pytest.mark.parametrize("R,ns,k", [(1, 0, 8), (1, 1, 1), (3, 2, 6), (5, 2, 6), (16, 2, 6), (17, 2, 6),
-                                    (17, 1, 8)])
+                                    (17, 1, 8), (24, 2, 6), (25, 2, 6)])
 def test_step_rows_around_folded_combine(q, R, ns, k):
     d = small_dims(n_shared=ns, top_k=k)
     run_steps(q, d, 530 + 16 * R + 4 * ns + k, prefix_len=[(11 * i + 5) % 41 for i in range(R)],
