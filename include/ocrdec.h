@@ -73,7 +73,8 @@ const char* ocrdec_version(void);
  * capture (the events become graph nodes).  When `capacity` events have been
  * recorded, later ones are dropped and `count` stays at capacity. */
 typedef enum {
-    OCRDEC_K_EMBED = 0,       /* embedding lookup + first norm */
+    OCRDEC_K_EMBED = 0,       /* embedding lookup + first norm (up to 16 rows with an fp16 table it runs
+                                 inside the first QKV projection and has no event of its own) */
     OCRDEC_K_QKV = 1,         /* QKV projection (norm staged in it up to 16 rows) */
     OCRDEC_K_ATTN = 2,        /* attention partials over 64-key splits (RoPE, cache write) */
     OCRDEC_K_ATTN_MERGE = 3,  /* merge of the splits */

@@ -293,6 +293,23 @@ OCR_DEV float4 st_resid4(fix_t* h, int c4, float4 v, bool& bad) {
     return make_float4(fix_to(a), fix_to(b), fix_to(c), fix_to(d));
 }
 
+// The status area of the decode step's workspace: word 0 collects the bits
+// the step's kernels raise with atomic ORs; word 1 + r holds row r's input
+// bits, written by the first kernel, which also clears word 0 and the words
+// of rows past the batch (up to kStatusRows).  Later kernels run after it in
+// stream order, so nothing is lost to the clearing.
+constexpr int kStatusRows = 32;
+OCR_DEV void status_begin(uint32_t* status, int r, int rows, bool tok_bad, bool resid_bad) {
+    if (!status) return;
+    const int lane = threadIdx.x & 63;
+    const bool rb = __ballot(resid_bad) != 0;
+    if (lane == 0) status[1 + r] = (tok_bad ? kStatTokenRange : 0u) | (rb ? kStatResidual : 0u);
+    if (r == 0) {
+        if (lane == 0) status[0] = 0;
+        if (lane >= rows && lane < kStatusRows) status[1 + lane] = 0;
+    }
+}
+
 // h[i] += a as an atomic integer add (any order gives the same sum).
 OCR_DEV void fix_atomic_add(fix_t* h, float a, bool& bad) {
     atomicAdd((unsigned long long*)h, (unsigned long long)fix_from(a, bad));

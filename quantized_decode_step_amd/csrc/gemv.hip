@@ -8,8 +8,9 @@ namespace ocrdec {
 // XT = 1, 2: 16 or 32 tokens per pass.  XSRC: where the activations come
 // from: X_GLOBAL, their fragments are loaded from global memory alongside the
 // weights (for k too large to stage); X_LDS, they are staged in LDS;
-// X_NORM (XT = 1), formed in LDS as RMSNorm(hn) * gamma.
-constexpr int X_GLOBAL = 0, X_LDS = 1, X_NORM = 2;
+// X_NORM (XT = 1), formed in LDS as RMSNorm(hn) * gamma; X_EMBED (XT = 1,
+// one pass), the same from embedding rows (GemvParams::er).
+constexpr int X_GLOBAL = 0, X_LDS = 1, X_NORM = 2, X_EMBED = 3;
 template <int FMT, int NT, int XT, int KS, int EPI, int XSRC>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
     constexpr int CB = Geom<FMT>::CB;
@@ -64,6 +65,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
         if constexpr (XSRC != X_GLOBAL) {
             auto stage = [&]() {
                 if constexpr (XSRC == X_NORM) stage_norm(p.hn, p.gamma, p.eps, p.xs.rows, tok0, p.k, xl_dyn, ldl);
+                else if constexpr (XSRC == X_EMBED)
+                    stage_embed_norm(p.er, p.gamma, p.eps, p.xs.rows, tok0, p.k, xl_dyn, ldl);
                 else stage_x(p.xs, tok0, 16 * XT, p.k, xl_dyn, ldl);
             };
             kloop_lds<FMT, NT, XT>(tile, c0, c1, stage, xl_dyn, ldl, p.xs.rows - tok0, nblk, lane, acc);
@@ -188,6 +191,31 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
         }
         __syncthreads();
     }
+    if constexpr (XSRC == X_EMBED) {
+        // workgroup b stores embedding rows b, b + grid, ... into the
+        // residual (a non-finite value is stored as 0 and flagged) and opens
+        // their status words
+        __shared__ int bad_s;
+        for (int r = blockIdx.x; r < p.xs.rows; r += gridDim.x) {
+            if (threadIdx.x == 0) bad_s = 0;
+            __syncthreads();
+            const int t0 = p.er.tok[r];
+            const bool tok_bad = t0 < 0 || t0 >= p.er.vocab;
+            const uint2* er_row = (const uint2*)(p.er.table + (int64_t)clamp_tok(t0, p.er.vocab) * p.k);
+            fix_t* hr = p.eh + (int64_t)r * p.k;
+            bool bad = false;
+            for (int c4 = threadIdx.x; c4 < p.k / 4; c4 += blockDim.x) {
+                const uint2 e = er_row[c4];
+                st_resid4(hr, c4,
+                          make_float4(h2f((uint16_t)(e.x & 0xFFFF)), h2f((uint16_t)(e.x >> 16)),
+                                      h2f((uint16_t)(e.y & 0xFFFF)), h2f((uint16_t)(e.y >> 16))),
+                          bad);
+            }
+            if (__ballot(bad) != 0 && lane == 0) atomicOr(&bad_s, 1);
+            __syncthreads();
+            if (wave == 0) status_begin(p.status, r, p.xs.rows, tok_bad, bad_s != 0);
+        }
+    }
 }
 
 namespace {
@@ -206,6 +234,8 @@ void launch_fmt(const GemvParams& p, int nt, int ks, int xt, int xsrc, hipStream
     if (nt == NT_ && ks == KS_ && xt == XT_) {                                               \
         if constexpr (XT_ == 1)                                                              \
             if (xsrc == X_NORM) return launch_t<FMT, NT_, XT_, KS_, EPI, X_NORM>(p, s);       \
+        if constexpr (XT_ == 1 && EPI == EPI_F32)                                            \
+            if (xsrc == X_EMBED) return launch_t<FMT, NT_, XT_, KS_, EPI, X_EMBED>(p, s);     \
         if (xsrc == X_LDS) launch_t<FMT, NT_, XT_, KS_, EPI, X_LDS>(p, s);                   \
         else launch_t<FMT, NT_, XT_, KS_, EPI, X_GLOBAL>(p, s);                              \
         return;                                                                              \
@@ -249,7 +279,7 @@ void launch_gemv(int fmt, int epi, const GemvPlan& plan, GemvParams p, hipStream
     // 16-token passes
     GemvPlan pl = plan;
     if (p.hn) pl.xt = 1;
-    const int xsrc = p.hn ? X_NORM : (pl.lds ? X_LDS : X_GLOBAL);
+    const int xsrc = p.hn ? (p.er.table ? X_EMBED : X_NORM) : (pl.lds ? X_LDS : X_GLOBAL);
     p.n_groups = pl.groups;
 #define OCR_E(E_)                                                                          \
     case E_:                                                                               \

@@ -24,6 +24,13 @@ struct GemvParams {
     const uint16_t* gamma;
     float eps;
     uint32_t* status;  // status word (kStat* bits) or NULL
+    // With er.table non-NULL as well (one 16-token pass): the rows are the
+    // fp16 embedding rows er.table[er.tok[r]] instead of hn, and workgroup 0
+    // also stores them as the residual eh [rows][k] (fixed point) and opens
+    // the status words (the embedding step of the decode step, folded into
+    // the first consumer).
+    EmbedRows er;
+    fix_t* eh;
 };
 
 struct GemvPlan {

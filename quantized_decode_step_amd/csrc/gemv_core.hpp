@@ -514,9 +514,24 @@ OCR_DEV void stage_rows_direct(ROWF row_of, int nt, int k, uint16_t* xl, int ldl
 // its values in registers, otherwise it reads its slices again (from cache)
 // to scale them.  With G = 1 every wave normalises whole rows on its own.
 // Every thread of the workgroup must call it (it may hold a barrier).
-template <int MAXG>
+// Rows of fp16 embedding-table values, row r = table row tok[r] (clamped to
+// [0, vocab)), read as the decode step's residual stores them: a non-finite
+// value becomes 0 (the fixed-point residual holds every finite fp16 value
+// exactly).  ETAB = nullptr: the rows are fixed-point residual rows.
+struct EmbedRows {
+    const uint16_t* table;
+    const int32_t* tok;
+    int vocab;
+};
+OCR_DEV int clamp_tok(int t, int vocab) { return t < 0 ? 0 : (t >= vocab ? vocab - 1 : t); }
+OCR_DEV float embed_val(uint16_t b) {
+    const float f = h2f(b);
+    return fabsf(f) <= 65504.0f ? f : 0.0f;
+}
+
+template <int MAXG, bool EMB = false>
 OCR_DEV void block_rmsnorm_fix(const fix_t* h, const uint16_t* gamma, int H, float eps, int r0, int R,
-                               uint16_t* x_out, int64_t ldx, uint16_t* xl, int ldl) {
+                               uint16_t* x_out, int64_t ldx, uint16_t* xl, int ldl, EmbedRows er = EmbedRows{}) {
     __shared__ float ss_lds[256];
     const int nw = (int)blockDim.x >> 6, wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
     const int n4 = H / 4;
@@ -530,20 +545,38 @@ OCR_DEV void block_rmsnorm_fix(const fix_t* h, const uint16_t* gamma, int H, flo
     auto load = [&](int pr) {
         const int r = pr / G, s = pr % G;
         const int g0 = s * per, g1 = min(g0 + per, n4);
-        const fix_t* hr = h + (int64_t)(r0 + r) * H;
-        longlong2 a[MAXG], b[MAXG];
+        if constexpr (EMB) {
+            const int t = clamp_tok(er.tok[r0 + r], er.vocab);
+            const uint2* er_row = (const uint2*)(er.table + (int64_t)t * H);
+            uint2 e[MAXG];
 #pragma unroll
-        for (int i = 0; i < MAXG; ++i) {
-            const int c = min(g0 + lane + 64 * i, g1 - 1);
-            a[i] = ((const longlong2*)hr)[2 * c];
-            b[i] = ((const longlong2*)hr)[2 * c + 1];
-            g[i] = ((const uint2*)gamma)[c];
+            for (int i = 0; i < MAXG; ++i) {
+                const int c = min(g0 + lane + 64 * i, g1 - 1);
+                e[i] = er_row[c];
+                g[i] = ((const uint2*)gamma)[c];
+            }
+#pragma unroll
+            for (int i = 0; i < MAXG; ++i)
+                v[i] = g0 + lane + 64 * i < g1
+                           ? make_float4(embed_val((uint16_t)(e[i].x & 0xFFFF)), embed_val((uint16_t)(e[i].x >> 16)),
+                                         embed_val((uint16_t)(e[i].y & 0xFFFF)), embed_val((uint16_t)(e[i].y >> 16)))
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
+            const fix_t* hr = h + (int64_t)(r0 + r) * H;
+            longlong2 a[MAXG], b[MAXG];
+#pragma unroll
+            for (int i = 0; i < MAXG; ++i) {
+                const int c = min(g0 + lane + 64 * i, g1 - 1);
+                a[i] = ((const longlong2*)hr)[2 * c];
+                b[i] = ((const longlong2*)hr)[2 * c + 1];
+                g[i] = ((const uint2*)gamma)[c];
+            }
+#pragma unroll
+            for (int i = 0; i < MAXG; ++i)
+                v[i] = g0 + lane + 64 * i < g1
+                           ? make_float4(fix_to(a[i].x), fix_to(a[i].y), fix_to(b[i].x), fix_to(b[i].y))
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-#pragma unroll
-        for (int i = 0; i < MAXG; ++i)
-            v[i] = g0 + lane + 64 * i < g1
-                       ? make_float4(fix_to(a[i].x), fix_to(a[i].y), fix_to(b[i].x), fix_to(b[i].y))
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
     };
     auto sumsq = [&]() {
         float ss = 0.f;
@@ -662,6 +695,11 @@ struct RowNormFix {
 OCR_DEV void stage_norm(const fix_t* h, const uint16_t* gamma, float eps, int rows, int tok0, int H, uint16_t* xl,
                         int ldl) {
     block_rmsnorm_fix<5>(h, gamma, H, eps, tok0, min(16, rows - tok0), nullptr, 0, xl, ldl);
+}
+// The same from embedding rows (first layer of the decode step).
+OCR_DEV void stage_embed_norm(EmbedRows er, const uint16_t* gamma, float eps, int rows, int tok0, int H,
+                              uint16_t* xl, int ldl) {
+    block_rmsnorm_fix<5, true>(nullptr, gamma, H, eps, tok0, min(16, rows - tok0), nullptr, 0, xl, ldl, er);
 }
 
 template <int FMT, int XT>

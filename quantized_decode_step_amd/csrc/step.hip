@@ -24,23 +24,6 @@ namespace {
 
 constexpr int kMaxRows = 32;
 
-// The status area of the decode step's workspace: word 0 collects the bits
-// the step's kernels raise with atomic ORs; word 1 + r holds row r's input
-// bits, written by the first kernel, which also clears word 0 and the words
-// of rows past the batch (up to kStatusRows).  Later kernels run after it in
-// stream order, so nothing is lost to the clearing.
-constexpr int kStatusRows = 32;
-OCR_DEV void status_begin(uint32_t* status, int r, int rows, bool tok_bad, bool resid_bad) {
-    if (!status) return;
-    const int lane = threadIdx.x & 63;
-    const bool rb = __ballot(resid_bad) != 0;
-    if (lane == 0) status[1 + r] = (tok_bad ? kStatTokenRange : 0u) | (rb ? kStatResidual : 0u);
-    if (r == 0) {
-        if (lane == 0) status[0] = 0;
-        if (lane >= rows && lane < kStatusRows) status[1 + lane] = 0;
-    }
-}
-
 // h[r] = embed[tok[r]] (fp16 table) or src[r] (fp32); x[r] = norm(h[r]),
 // formed from the values as stored.  One wavefront per row (H <= 4096).  HT:
 // the residual's representation (the decode step's fixed point, or fp32 for
@@ -462,8 +445,20 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     hipStream_t s = (hipStream_t)stream;
     StepWs w = carve_step(ws, m, R, cache_cap);
 
-    prof_mark(s, OCRDEC_K_EMBED);
-    if (tok_in && !m->embed) {
+    // Up to 16 rows: the kernels that consume a normalised residual (QKV,
+    // the dense MLP, the language head) form RMSNorm(h) in their LDS staging
+    // and the MoE down projection adds its weighted outputs into the residual,
+    // so no separate norm or combine kernel runs.  (With more rows the
+    // per-consumer norms cost more than the kernels they replace.)  Up to 24
+    // rows the attention merge runs inside the O projection.  With an fp16
+    // embedding table the first QKV projection also reads the embedding rows
+    // itself and stores the residual (no embedding kernel).
+    const bool prolog = R <= 16 && lds_x_bytes(H, 1) <= 65536;
+    const bool fold_embed = prolog && tok_in && m->embed;
+    if (!fold_embed) prof_mark(s, OCRDEC_K_EMBED);
+    if (fold_embed) {
+        // (in the first QKV projection below)
+    } else if (tok_in && !m->embed) {
         const uint8_t* tq = (const uint8_t*)m->embed_q.data;
         const int64_t nch = n_chunks(m->embed_q.fmt, H);
 #define OCR_EQ(F_)                                                                                                 \
@@ -505,13 +500,6 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
     ap0.n_split = attn_n_split(cache_cap);
     ap0.part = w.attn_part;
     attn_set_rope(ap0, m->rope_theta);
-    // Up to 16 rows: the kernels that consume a normalised residual (QKV,
-    // the dense MLP, the language head) form RMSNorm(h) in their LDS staging
-    // and the MoE down projection adds its weighted outputs into the residual,
-    // so no separate norm or combine kernel runs.  (With more rows the
-    // per-consumer norms cost more than the kernels they replace.)  Up to 24
-    // rows the attention merge runs inside the O projection.
-    const bool prolog = R <= 16 && lds_x_bytes(H, 1) <= 65536;
     int moe_l = 0;
     for (int l = 0; l < m->n_layers; ++l) {
         const ocrdec_layer& L = m->layers[l];
@@ -531,6 +519,11 @@ extern "C" ocrdec_status ocrdec_decode_step(const ocrdec_model* m, const ocrdec_
                 gp.hn = w.h;
                 gp.gamma = L.attn_norm;
                 gp.eps = m->norm_eps;
+            }
+            if (l == 0 && fold_embed) {
+                gp.er = EmbedRows{m->embed, tok_in, m->vocab};
+                gp.eh = w.h;
+                gp.status = w.status;
             }
             prof_mark(s, OCRDEC_K_QKV);
             launch_gemv(L.wqkv.fmt, EPI_F32, pl, gp, s);
