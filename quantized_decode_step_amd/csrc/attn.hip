@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
     __shared__ __align__(16) int8_t vnew8_s[KV8 ? D : 1];
     __shared__ float snew_s[2];
     __shared__ float sc_s[KPS];
-    __shared__ float o_s[4][D];
+    __shared__ float o_s[4 * (64 / LPK)][D];  // p.V of every (wave, key group)
     __shared__ float red_s[8];
 
     const int s = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
@@ -193,6 +193,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
         vnew_s[tid - 64] = f2h(xv);
     }
     __syncthreads();
+    // the new token's codes (KV8, waves 0 and 1), stored to the cache at the end
+    int8_t q8keep[KV8 ? D / 64 : 1];
+    uint16_t s16keep = 0;
     if constexpr (KV8) {
         // wave 0 quantises the new key, wave 1 the new value (D / 64 values per lane)
         if (has_new && wave < 2) {
@@ -208,22 +211,16 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
             const uint16_t s16 = f2h(__fdiv_rn(am, 127.0f));
             const float sf = h2f(s16);
             int8_t* dst = wave == 0 ? knew8_s : vnew8_s;
-            int8_t* gdst = (int8_t*)(wave == 0 ? p.k_cache : p.v_cache) + (head_off + w.new_idx) * D;
 #pragma unroll
             for (int j = 0; j < PER; ++j) {
                 const float qv = sf > 0.f ? fminf(fmaxf(roundf(__fdiv_rn(x[j], sf)), -127.f), 127.f) : 0.f;
                 dst[lane * PER + j] = (int8_t)qv;
-                gdst[lane * PER + j] = (int8_t)qv;
+                q8keep[j] = (int8_t)qv;
             }
-            if (lane == 0) {
-                snew_s[wave] = sf;
-                (wave == 0 ? p.k_scale : p.v_scale)[head_off + w.new_idx] = s16;
-            }
+            s16keep = s16;
+            if (lane == 0) snew_s[wave] = sf;
         }
         __syncthreads();
-    } else if (has_new && tid < D) {
-        p.k_cache[(head_off + w.new_idx) * D + tid] = knew_s[tid];
-        p.v_cache[(head_off + w.new_idx) * D + tid] = vnew_s[tid];
     }
 
     // ---- scores
@@ -250,8 +247,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
                 for (int i = 0; i < 8; ++i) dot = fmaf(qf[i], (float)kh[i], dot);
             }
         }
-#pragma unroll
-        for (int off = LPK / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+        dot = group_sum<LPK>(dot);  // the key's LPK lanes
         if (o < o1 && (lane % LPK) == 0) {
             float sc = dot * p.scale;
             if (p.sink && ord_to_idx(p, w, o) == 0) sc += p.sink[h];
@@ -298,17 +294,32 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnParams p) {
             }
         }
     }
-    // reduce over the key groups of the wavefront (lanes sharing dsub)
+    // sum over the key groups of all wavefronts through LDS (independent
+    // reads instead of chains of cross-lane permutes), in a fixed order
 #pragma unroll
-    for (int off = LPK; off < 64; off <<= 1)
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) acc[i] += __shfl_xor(acc[i], off, 64);
-    if (lane < LPK) {
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) o_s[wave][dsub + i] = acc[i];
-    }
+    for (int i = 0; i < VPL; ++i) o_s[wave * (64 / LPK) + lane / LPK][dsub + i] = acc[i];
     __syncthreads();
-    if (tid < D) part[tid] = o_s[0][tid] + o_s[1][tid] + o_s[2][tid] + o_s[3][tid];
+    if (tid < D) {
+        float o = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4 * (64 / LPK); ++j) o += o_s[j][tid];
+        part[tid] = o;
+    }
+    // The new token into the cache, last: nothing in this kernel reads it from
+    // there (its split takes it from LDS), and a store issued earlier would
+    // make every later barrier wait for it.
+    if constexpr (KV8) {
+        if (has_new && wave < 2) {
+            constexpr int PER = D / 64;
+            int8_t* gdst = (int8_t*)(wave == 0 ? p.k_cache : p.v_cache) + (head_off + w.new_idx) * D;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) gdst[lane * PER + j] = q8keep[j];
+            if (lane == 0) (wave == 0 ? p.k_scale : p.v_scale)[head_off + w.new_idx] = s16keep;
+        }
+    } else if (has_new && tid < D) {
+        p.k_cache[(head_off + w.new_idx) * D + tid] = knew_s[tid];
+        p.v_cache[(head_off + w.new_idx) * D + tid] = vnew_s[tid];
+    }
     if (tid == 0) {
         part[D] = red_s[0];
         part[D + 1] = red_s[1];

@@ -154,6 +154,17 @@ OCR_DEV float wave_sum(float v) {
     v += dpp_move<0x143, 0xC>(v, 0.f);  // row_bcast:31
     return lane63(v);
 }
+// Sum over each aligned group of W lanes (W = 4, 8 or 16), in every lane of
+// the group: the first steps of wave_sum (DPP moves, no LDS permutes).
+template <int W>
+OCR_DEV float group_sum(float v) {
+    static_assert(W == 4 || W == 8 || W == 16, "group width");
+    v += dpp_move<0xB1>(v, 0.f);                          // quad_perm [1,0,3,2]
+    v += dpp_move<0x4E>(v, 0.f);                          // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) v += dpp_move<0x141>(v, 0.f);   // row_half_mirror
+    if constexpr (W == 16) v += dpp_move<0x140>(v, 0.f);  // row_mirror
+    return v;
+}
 OCR_DEV float wave_max(float v) {
     v = fmaxf(v, dpp_move<0xB1>(v, v));
     v = fmaxf(v, dpp_move<0x4E>(v, v));
