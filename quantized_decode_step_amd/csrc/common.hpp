@@ -165,6 +165,24 @@ OCR_DEV float group_sum(float v) {
     if constexpr (W == 16) v += dpp_move<0x140>(v, 0.f);  // row_mirror
     return v;
 }
+// Bitwise OR over all 64 lanes (result in every lane), by the same DPP steps
+// as wave_sum.
+template <int CTRL, int ROW_MASK = 0xF>
+OCR_DEV uint32_t dpp_move_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+OCR_DEV uint32_t wave_or(uint32_t v) {
+    v |= dpp_move_u32<0xB1>(v);
+    v |= dpp_move_u32<0x4E>(v);
+    v |= dpp_move_u32<0x141>(v);
+    v |= dpp_move_u32<0x140>(v);
+    v |= dpp_move_u32<0x142, 0xA>(v);
+    v |= dpp_move_u32<0x143, 0xC>(v);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+OCR_DEV unsigned long long wave_or(unsigned long long v) {
+    return (unsigned long long)wave_or((uint32_t)v) | ((unsigned long long)wave_or((uint32_t)(v >> 32)) << 32);
+}
 OCR_DEV float wave_max(float v) {
     v = fmaxf(v, dpp_move<0xB1>(v, v));
     v = fmaxf(v, dpp_move<0x4E>(v, v));

@@ -965,7 +965,7 @@ OCR_DEV int expert_entry(const GroupedParams& p, int v, int& e, int* row_s, int*
     const int nwd = (E + 63) >> 6;
     int nact = 0;
     for (int w = 0; w < nwd; ++w) {  // uniform
-        for (int o = 32; o > 0; o >>= 1) act[w] |= __shfl_xor(act[w], o, 64);
+        act[w] = wave_or(act[w]);
         nact += __popcll(act[w]);
     }
     const int u = v - sv;
