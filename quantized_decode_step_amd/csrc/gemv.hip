@@ -320,11 +320,17 @@ size_t argmax_ws_bytes(int grid, int rows) { return align256((size_t)grid * rows
 constexpr int LM_WAVES = 8;
 constexpr size_t LM_LDS = 96 * 1024;  // > half the CU's LDS: one workgroup per CU
 
+// Wavefronts per workgroup: eight, twelve for Q4_0 (its ring of five chunks
+// holds a sixth of an fp16 ring's bytes; three waves per SIMD fit its registers)
+template <int FMT>
+constexpr int lm_waves() { return FMT == OCRDEC_Q4_0 ? 12 : LM_WAVES; }
+
 template <int FMT, int PF>
-__global__ __launch_bounds__(64 * LM_WAVES, 1) void lm_argmax_kernel(GemvParams p) {
+__global__ __launch_bounds__(64 * lm_waves<FMT>(), 1) void lm_argmax_kernel(GemvParams p) {
     constexpr int SB = Geom<FMT>::SB, CB = Geom<FMT>::CB;
+    constexpr int NWV = lm_waves<FMT>();
     extern __shared__ __align__(16) uint16_t xl_dyn[];
-    __shared__ float amx[LM_WAVES * 16 * 3];
+    __shared__ float amx[NWV * 16 * 3];
     __shared__ int next_s;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ntiles = (p.n + 15) / 16;
@@ -332,7 +338,7 @@ __global__ __launch_bounds__(64 * LM_WAVES, 1) void lm_argmax_kernel(GemvParams 
     const int nt = (int)((int64_t)ntiles * (blockIdx.x + 1) / gridDim.x) - t0;
     const int nc = (int)p.nchunks, nblk = p.k / 32, ldl = xlds_stride(p.k), R = p.xs.rows;
     // tiles of the slice: wave w starts with tile w, then asks the counter
-    if (threadIdx.x == 0) next_s = LM_WAVES;
+    if (threadIdx.x == 0) next_s = NWV;
     auto tptr = [&](int u) { return p.w + (int64_t)(t0 + min(u, max(nt - 1, 0))) * nc * CB; };
     WRegs ring[PF];
     int ucur = wave;
@@ -430,7 +436,7 @@ __global__ __launch_bounds__(64 * LM_WAVES, 1) void lm_argmax_kernel(GemvParams 
         const int tok = threadIdx.x;
         float b = -INFINITY, s2 = -INFINITY;
         int bi = 0x7fffffff;
-        for (int w = 0; w < LM_WAVES; ++w) {
+        for (int w = 0; w < NWV; ++w) {
             const float* e = amx + (w * 16 + tok) * 3;
             argmax_merge(b, bi, s2, e[0], __float_as_int(e[1]), e[2]);
         }
@@ -485,9 +491,9 @@ void launch_lm_argmax(int fmt, const LmPlan& lp, GemvParams p, hipStream_t s) {
 #define OCR_LM(F_, A_, B_)                                                                                      \
     case F_:                                                                                                    \
         if (pf == A_)                                                                                           \
-            hipLaunchKernelGGL((lm_argmax_kernel<F_, A_>), dim3(lp.grid), dim3(64 * LM_WAVES), LM_LDS, s, p);    \
+            hipLaunchKernelGGL((lm_argmax_kernel<F_, A_>), dim3(lp.grid), dim3(64 * lm_waves<F_>()), LM_LDS, s, p);    \
         else                                                                                                    \
-            hipLaunchKernelGGL((lm_argmax_kernel<F_, B_>), dim3(lp.grid), dim3(64 * LM_WAVES), LM_LDS, s, p);    \
+            hipLaunchKernelGGL((lm_argmax_kernel<F_, B_>), dim3(lp.grid), dim3(64 * lm_waves<F_>()), LM_LDS, s, p);    \
         break;
     switch (fmt) {
         OCR_LM(OCRDEC_F16, 10, 8)
