@@ -305,8 +305,9 @@ size_t argmax_ws_bytes(int grid, int rows) { return align256((size_t)grid * rows
 // ---------------------------------------------------------------------------
 // LM head with fused argmax for up to 16 rows, balanced within each CU
 //
-// One workgroup of eight wavefronts per CU (its LDS request leaves room for
-// no second one) owns an equal slice of the 16-row tiles.  Its wavefronts
+// One workgroup of eight wavefronts (twelve for Q4_0) per CU (its LDS
+// request leaves room for no second one) owns an equal slice of the 16-row
+// tiles.  Its wavefronts
 // take tiles one at a time from an LDS counter, so a wavefront the CU favours
 // (the issue arbiter prefers older waves) simply takes more tiles, and all of
 // a CU's wavefronts finish within about one tile of each other.  Each
