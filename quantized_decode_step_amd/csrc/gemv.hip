@@ -305,7 +305,7 @@ size_t argmax_ws_bytes(int grid, int rows) { return align256((size_t)grid * rows
 // ---------------------------------------------------------------------------
 // LM head with fused argmax for up to 16 rows, balanced within each CU
 //
-// One workgroup of eight wavefronts (twelve for Q4_0) per CU (its LDS
+// One workgroup of eight wavefronts (twelve for Q4_0, U8A) per CU (its LDS
 // request leaves room for no second one) owns an equal slice of the 16-row
 // tiles.  Its wavefronts
 // take tiles one at a time from an LDS counter, so a wavefront the CU favours
@@ -321,10 +321,11 @@ size_t argmax_ws_bytes(int grid, int rows) { return align256((size_t)grid * rows
 constexpr int LM_WAVES = 8;
 constexpr size_t LM_LDS = 96 * 1024;  // > half the CU's LDS: one workgroup per CU
 
-// Wavefronts per workgroup: eight, twelve for Q4_0 (its ring of five chunks
-// holds a sixth of an fp16 ring's bytes; three waves per SIMD fit its registers)
+// Wavefronts per workgroup: eight, twelve for Q4_0 and U8A (their rings of
+// five chunks hold a sixth of an fp16 ring's bytes, and three waves per SIMD
+// fit their registers; sixteen Q8_0 wavefronts measured no faster than eight)
 template <int FMT>
-constexpr int lm_waves() { return FMT == OCRDEC_Q4_0 ? 12 : LM_WAVES; }
+constexpr int lm_waves() { return FMT == OCRDEC_Q4_0 || FMT == OCRDEC_U8A_G32 ? 12 : LM_WAVES; }
 
 template <int FMT, int PF>
 __global__ __launch_bounds__(64 * lm_waves<FMT>(), 1) void lm_argmax_kernel(GemvParams p) {
