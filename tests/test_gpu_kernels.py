@@ -403,12 +403,14 @@ def test_moe_prefill_formats(q, rows, fmt, F):
 
 # full-vocabulary heads with up to 16 rows take the CU-balanced kernel, the
 # others the general GEMV with the argmax epilogue.  Q4_0 heads of 33000 and
-# 36864 rows give each of 256 CUs 8-9 tiles: fewer than the twelve wavefronts
-# of the Q4_0 form, so some start with no tile (one head ends mid-tile).
+# 36864 rows and a U8A head of 36864 give each of 256 CUs 8-9 tiles: fewer
+# than the twelve wavefronts of those forms, so some start with no tile (one
+# head ends mid-tile).
 @pytest.mark.parametrize("fmt,n,rows", [(synth.F16, 129280, 1), (synth.F16, 129280, 24), (synth.Q8_0, 5000, 7),
                                         (synth.Q4_0, 999, 32), (synth.Q4_0, 129280, 24), (synth.Q8_0, 129280, 1),
                                         (synth.F16, 129280, 16), (synth.Q4_0, 129280, 3),
-                                        (synth.U8A_G32, 100000, 2), (synth.Q4_0, 36864, 1), (synth.Q4_0, 33000, 5)])
+                                        (synth.U8A_G32, 100000, 2), (synth.Q4_0, 36864, 1), (synth.Q4_0, 33000, 5),
+                                        (synth.U8A_G32, 36864, 3)])
 def test_lm_argmax_parity(q, fmt, n, rows):
     import torch
     seed = 77 + n + rows
