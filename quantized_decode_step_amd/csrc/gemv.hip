@@ -380,7 +380,11 @@ __global__ __launch_bounds__(64 * lm_waves<FMT>(), 1) void lm_argmax_kernel(Gemv
                 const int c = c0 + s;
                 half8v xa[SB][1];
                 float4v xs[SB][1];
-                lds_xfrags<FMT, 1>(xl_dyn, ldl, R, c, nblk, lane, xa);
+                // Q4_0 (whole chunks only): unchecked reads; the LDS rows past
+                // the token count hold stale values that reach only those
+                // tokens' outputs, which are never reported
+                if constexpr (FMT == OCRDEC_Q4_0) lds_xfrags_all<FMT>(xl_dyn, ldl, c, lane, xa);
+                else lds_xfrags<FMT, 1>(xl_dyn, ldl, R, c, nblk, lane, xa);
                 if constexpr (FMT == OCRDEC_Q4_0) {
                     float4v nb[4][1];
 #pragma unroll
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(64 * lm_waves<FMT>(), 1) void lm_argmax_kernel(Gemv
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const float val = acc[0][0][v];
-                nonfin |= !(fabsf(val) < INFINITY);
+                nonfin |= 4 * (lane >> 4) + v < R && !(fabsf(val) < INFINITY);
                 if (val > best[v]) {
                     second[v] = best[v];
                     best[v] = val;
@@ -467,6 +471,7 @@ int device_cus() {
 int lm_pf(int fmt, int k) {
     const int64_t nc = n_chunks(fmt, k);
     if (fmt == OCRDEC_F16) return nc % 10 == 0 ? 10 : nc % 8 == 0 ? 8 : 0;
+    if (fmt == OCRDEC_Q4_0 && k % 128 != 0) return 0;  // its unchecked operand reads need whole chunks
     return nc % 5 == 0 ? 5 : nc % 4 == 0 ? 4 : 0;
 }
 }  // namespace
